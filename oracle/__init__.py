@@ -1,0 +1,144 @@
+"""fp64 CPU oracle for exact single-query attention decoding.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product library
+(``long_context_attention_split_amd``) never imports, links or runs it, and this
+package imports nothing from the product.
+
+- ``decode_f64``: the plain definition softmax(q K^T d^-1/2 + bias) V, evaluated
+  row by row in double precision by ``decode_f64.c`` (see its header for the
+  formula and the pages it follows).
+- ``alibi_bias``: the bias term that definition adds ("ALiBi with causal=True
+  unexpected bias?", causal bias vector example).
+- ``tree``: numpy fp64 split-and-merge decoding in the steps of the tree-attention
+  gist, used to pin the definition by chunk-count and merge-order invariance and to
+  check per-chunk partials.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "decode_f64.c")
+_LIB = os.path.join(_HERE, "liboracle_f64.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile decode_f64.c with gcc into liboracle_f64.so (host code only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+                               "-pthread", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_decode_f64.restype = i32
+        lib.oracle_decode_f64.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i64, i64, i64, i64, i64,
+                                          i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32]
+        lib.oracle_alibi_bias.restype = ctypes.c_double
+        lib.oracle_alibi_bias.argtypes = [i64, i64, ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+def _as_np(x):
+    """numpy view of a CPU tensor/array; bf16 tensors become their uint16 bit patterns."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy().view(np.uint16), BF16
+            if x.dtype == torch.float32:
+                return x.numpy(), F32
+            raise TypeError("oracle inputs must be fp32 or bf16, got %s" % x.dtype)
+    except ImportError:
+        pass
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16:
+        return x, BF16
+    raise TypeError("oracle inputs must be float32 or bf16 bits (uint16), got %s" % x.dtype)
+
+
+def _strides(a: np.ndarray):
+    es = a.itemsize
+    if a.strides[-1] != es:
+        raise ValueError("innermost dimension must be contiguous")
+    return [s // es for s in a.strides]
+
+
+def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]] = None,
+               n_threads: Optional[int] = None) -> np.ndarray:
+    """Oracle output (float64).
+
+    q [B, Hq, d]; k, v [B, Hkv, Lmax, d] (fp32 or bf16 torch tensors, or numpy float32 /
+    uint16 bf16 bits); seq_lens int32 [B] or None; slopes fp32 [Hq] or None.
+    ``rows``: flat b*Hq+h indices to compute (result [len(rows), d]); None for all
+    (result [B, Hq, d]).
+    """
+    lib = _load()
+    qn, qt = _as_np(q)
+    kn, kt = _as_np(k)
+    vn, vt = _as_np(v)
+    if kt != vt:
+        raise TypeError("k and v must share a dtype")
+    B, Hq, d = qn.shape
+    Bk, Hkv, Lmax, dk = kn.shape
+    if Bk != B or dk != d or vn.shape != kn.shape:
+        raise ValueError("shape mismatch")
+    sq, sk, sv = _strides(qn), _strides(kn), _strides(vn)
+    sl = None
+    if seq_lens is not None:
+        sl = np.ascontiguousarray(np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens,
+                                             dtype=np.int32))
+    sp = None
+    if slopes is not None:
+        sp = np.ascontiguousarray(np.asarray(slopes.cpu() if hasattr(slopes, "cpu") else slopes,
+                                             dtype=np.float32))
+    rw = None
+    n_rows = B * Hq
+    if rows is not None:
+        rw = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        n_rows = int(rw.size)
+    out = np.zeros((n_rows, d), dtype=np.float64)
+    if n_threads is None:
+        n_threads = len(os.sched_getaffinity(0))
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.oracle_decode_f64(ptr(qn), qt, sq[0], sq[1], ptr(kn), ptr(vn), kt,
+                               sk[0], sk[1], sk[2], sv[0], sv[1], sv[2],
+                               B, Hq, Hkv, Lmax, d, ptr(sl), ptr(sp), ptr(rw), n_rows,
+                               ptr(out), int(n_threads))
+    if rc != 0:
+        raise RuntimeError("oracle_decode_f64 failed (%d)" % rc)
+    return out if rows is not None else out.reshape(B, Hq, d)
+
+
+def alibi_bias(L: int, j: int, slope: float) -> float:
+    """The bias the oracle adds to key j's scaled score for a sequence of length L."""
+    return _load().oracle_alibi_bias(int(L), int(j), float(slope))
+
+
+def widen(x) -> np.ndarray:
+    """Exact fp64 copy of an fp32 / bf16 tensor (bf16: bits << 16)."""
+    a, t = _as_np(x)
+    if t == F32:
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

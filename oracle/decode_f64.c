@@ -1,0 +1,184 @@
+/*
+ * oracle/decode_f64.c -- plain fp64 CPU oracle for exact single-query attention decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously correct definition the GPU
+ * library is checked against.  Only the tests, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load it.  It includes no header of the product
+ * library and the product library never links, includes or calls it.
+ *
+ * What it computes, for every batch row b and query head h (one query token):
+ *
+ *   L    = seq_lens[b] clamped to [0, Lmax]           (Lmax when seq_lens is NULL)
+ *   kh   = floor(h / (Hq / Hkv))                      (contiguous query-head groups)
+ *   s_j  = d^(-1/2) * sum_i q[b,h,i] * k[b,kh,j,i] + beta_j,          0 <= j < L
+ *   beta_j = -slope_h * (L - 1 - j)   with ALiBi slopes, else 0
+ *   out[b,h,e] = sum_j exp(s_j - max_j s_j) * v[b,kh,j,e] / sum_j exp(s_j - max_j s_j)
+ *   L == 0  ->  out[b,h,:] = 0   (softmax over no keys is undefined; our convention)
+ *
+ * Sources:
+ *   - "Tree Attention Decoding" (tree_attn_decode.py gist), function regular_decode:
+ *     queries scaled by the inverse square root of the head dimension, dot products
+ *     with every key, softmax over the keys, weighted sum of the value rows.
+ *   - "ALiBi with causal=True unexpected bias?" (llm-foundry issue 186), the causal
+ *     bias vector example: for the last query the bias of key j is -(L-1-j) times a
+ *     per-head constant, added to the scaled scores.
+ *   - "Flash Aandacht: Revolutie in Transformer Efficientie", section on the
+ *     mathematics, softmax decomposition: subtracting the maximum score leaves the
+ *     softmax unchanged (it only keeps exp() in range).
+ *
+ * All arithmetic is double precision on exactly widened inputs (bf16 -> fp32 -> fp64
+ * are exact).  Rows are independent, so rows are spread over POSIX threads; each row
+ * is computed by one thread, in key order, with no blocking or reordering.
+ * Every function here is pinned by the CPU tests (closed forms, invariants, a library
+ * attention routine, the page's printed bias vector); nothing is "parity unpinned".
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+
+/* Widen one stored element to double.  bf16 is the upper half of an IEEE fp32. */
+static double widen(const void *base, int dtype, int64_t idx)
+{
+    if (dtype == OR_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ALiBi bias of key j for a query at position L-1 ("ALiBi with causal=True" issue:
+ * causal bias row arange(1-L, 1) times the head's slope). */
+double oracle_alibi_bias(int64_t L, int64_t j, double slope)
+{
+    return -slope * (double)(L - 1 - j);
+}
+
+typedef struct {
+    const void *q;
+    int q_dtype;
+    int64_t sqb, sqh;            /* q element strides for b, h (innermost stride 1) */
+    const void *k, *v;
+    int kv_dtype;
+    int64_t skb, skh, skj;       /* k element strides for b, kv-head, key */
+    int64_t svb, svh, svj;       /* v element strides */
+    int B, Hq, Hkv, Lmax, d;
+    const int32_t *seq_lens;     /* [B] or NULL */
+    const float *slopes;         /* [Hq] or NULL */
+    const int32_t *rows;         /* flat b*Hq+h indices to compute, or NULL for all */
+    int n_rows;
+    double *out;                 /* [n_rows, d] */
+    int n_threads;
+} oracle_job;
+
+/* One (b, h) row of the definition above; s is scratch of length >= Lmax. */
+static void decode_row(const oracle_job *J, int b, int h, double *s, double *out)
+{
+    const int d = J->d;
+    int64_t L = J->Lmax;
+    if (J->seq_lens) {
+        L = J->seq_lens[b];
+        if (L < 0) L = 0;
+        if (L > J->Lmax) L = J->Lmax;
+    }
+    for (int e = 0; e < d; ++e) out[e] = 0.0;
+    if (L == 0) return;
+
+    const int kh = h / (J->Hq / J->Hkv);
+    const double scale = 1.0 / sqrt((double)d);
+    const int64_t qoff = (int64_t)b * J->sqb + (int64_t)h * J->sqh;
+    const int64_t koff = (int64_t)b * J->skb + (int64_t)kh * J->skh;
+    const int64_t voff = (int64_t)b * J->svb + (int64_t)kh * J->svh;
+
+    /* scores s_j = (q . k_j) / sqrt(d) + beta_j */
+    for (int64_t j = 0; j < L; ++j) {
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i)
+            dot += widen(J->q, J->q_dtype, qoff + i) * widen(J->k, J->kv_dtype, koff + j * J->skj + i);
+        s[j] = dot * scale;
+        if (J->slopes) s[j] += oracle_alibi_bias(L, j, (double)J->slopes[h]);
+    }
+    /* softmax over the keys, with the maximum subtracted */
+    double m = s[0];
+    for (int64_t j = 1; j < L; ++j)
+        if (s[j] > m) m = s[j];
+    double z = 0.0;
+    for (int64_t j = 0; j < L; ++j) {
+        double w = exp(s[j] - m);
+        z += w;
+        for (int e = 0; e < d; ++e)
+            out[e] += w * widen(J->v, J->kv_dtype, voff + j * J->svj + e);
+    }
+    for (int e = 0; e < d; ++e) out[e] /= z;
+}
+
+typedef struct {
+    const oracle_job *J;
+    int tid;
+    int fail;
+} worker_arg;
+
+static void *worker(void *p)
+{
+    worker_arg *a = (worker_arg *)p;
+    const oracle_job *J = a->J;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(J->Lmax > 0 ? J->Lmax : 1));
+    if (!s) { a->fail = 1; return NULL; }
+    for (int r = a->tid; r < J->n_rows; r += J->n_threads) {
+        int flat = J->rows ? J->rows[r] : r;
+        int b = flat / J->Hq, h = flat % J->Hq;
+        decode_row(J, b, h, s, J->out + (int64_t)r * J->d);
+    }
+    free(s);
+    return NULL;
+}
+
+/*
+ * Compute the decode output for the requested rows.
+ *   q      : [B, Hq, d] with element strides (sqb, sqh, 1); dtype OR_F32 or OR_BF16
+ *   k, v   : [B, Hkv, Lmax, d] with element strides (s?b, s?h, s?j, 1); same dtype
+ *   rows   : flat indices b*Hq + h to compute (n_rows of them), or NULL for all B*Hq
+ *   out    : [n_rows, d] doubles, row r for rows[r]
+ *   n_threads: POSIX threads to use (>= 1)
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int oracle_decode_f64(const void *q, int q_dtype, int64_t sqb, int64_t sqh,
+                      const void *k, const void *v, int kv_dtype,
+                      int64_t skb, int64_t skh, int64_t skj,
+                      int64_t svb, int64_t svh, int64_t svj,
+                      int B, int Hq, int Hkv, int Lmax, int d,
+                      const int32_t *seq_lens, const float *slopes,
+                      const int32_t *rows, int n_rows, double *out, int n_threads)
+{
+    if (!q || !k || !v || !out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lmax < 0 || d <= 0)
+        return -1;
+    if ((q_dtype != OR_F32 && q_dtype != OR_BF16) || (kv_dtype != OR_F32 && kv_dtype != OR_BF16))
+        return -1;
+    oracle_job J = {q, q_dtype, sqb, sqh, k, v, kv_dtype, skb, skh, skj, svb, svh, svj,
+                    B, Hq, Hkv, Lmax, d, seq_lens, slopes, rows, rows ? n_rows : B * Hq, out,
+                    n_threads < 1 ? 1 : n_threads};
+    for (int r = 0; rows && r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= B * Hq) return -1;
+    if (J.n_threads > J.n_rows) J.n_threads = J.n_rows > 0 ? J.n_rows : 1;
+
+    pthread_t th[256];
+    worker_arg args[256];
+    if (J.n_threads > 256) J.n_threads = 256;
+    int rc = 0;
+    int started[256];
+    for (int t = 0; t < J.n_threads; ++t) {
+        args[t].J = &J; args[t].tid = t; args[t].fail = 0;
+        started[t] = pthread_create(&th[t], NULL, worker, &args[t]) == 0;
+        if (!started[t]) worker(&args[t]);   /* no thread: do this share here */
+    }
+    for (int t = 0; t < J.n_threads; ++t) {
+        if (started[t]) pthread_join(th[t], NULL);
+        if (args[t].fail) rc = -1;
+    }
+    return rc;
+}
