@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark: split-KV exact decode on one MI355X, 128k-token MHA workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S]
+
+One step = one full decode (split kernel + combine kernel) over the workload's
+inputs, already resident in HBM.  W untimed steps, then K timed steps between two
+device synchronisations.  Rank 0 prints one JSON line with:
+
+- value: KV-read throughput in GB/s (algorithmic K+V bytes / step time),
+- ms_per_step and decode_step_us,
+- roofline: the split kernel's algorithmic bytes per launch / its mean duration,
+  timed with events recorded on the launch stream around every timed launch,
+  against the 8 TB/s HBM peak; traffic = HBM bytes per launch measured by
+  rocprofv3 counters when the committed measurement matches the current kernel
+  source (else null),
+- cpu_baseline: the fp64 oracle timed on this host's cores over the same workload.
+
+Only one GPU is used: the decode of one sequence is split across the compute units
+of a single device, so --gpus above 1 is refused.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-step µs and KV-read HBM GB/s (% of peak) at 128k ctx, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+SPLIT_SOURCES = ("split_valu.hip", "split_mfma.hip", "device_util.h", "tad_internal.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SPLIT_SOURCES:
+        p = os.path.join(ROOT, "long_context_attention_split_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: int):
+    """HBM bytes per split-kernel launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "split_kernel_workload%d_traffic.txt" % workload)
+    if not os.path.exists(p):
+        return None
+    vals = {}
+    for ln in open(p):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["fetch_bytes_per_launch"]) + int(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(c, seconds_target: float = 10.0):
+    """Time the fp64 oracle over the workload's rows on this host's cores."""
+    import oracle
+    n_rows = c["q"].shape[0] * c["q"].shape[1]
+    threads = min(len(os.sched_getaffinity(0)), n_rows)
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    out = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            n_threads=threads)
+    dt = time.perf_counter() - t0
+    return out, dt, threads, n_rows
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--splits", type=int, default=0, help="chunks per head (0: automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode splits one sequence across the compute "
+              "units of a single MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import long_context_attention_split_amd as tad
+    import workloads as W
+
+    tad.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    c = W.make_workload(args.workload)
+    print("[bench] workload %d generated in %.1fs" % (args.workload, time.perf_counter() - t_gen),
+          file=sys.stderr, flush=True)
+    q = c["q"].to(dev)
+    k = c["k"].to(dev)
+    v = c["v"].to(dev)
+    sl = c["seq_lens"].to(dev) if c["seq_lens"] is not None else None
+    sp = c["slopes"].to(dev) if c["slopes"] is not None else None
+    S = args.splits if args.splits > 0 else tad.resolve_splits(q, k, c["n_splits"])
+    B, Hq, Hkv, Lmax, d = tad.shape_of(q, k)
+    ws = tad.workspace(q, k, S)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    kv_bytes = w.kv_bytes(c["seq_lens"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tad.tad_split(q, k, v, sl, sp, S, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        tad.tad_combine(ws, B, Hq, S, d, out, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    split_avg = sum(split_ms) / len(split_ms)
+    comb_avg = sum(comb_ms) / len(comb_ms)
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    split_gbs = kv_bytes / (split_avg * 1e-3) / 1e9
+    print("[bench] step %.1f us (split %.1f us, combine %.1f us), %.0f GB/s" %
+          (ms_per_step * 1e3, split_avg * 1e3, comb_avg * 1e3, gbs), file=sys.stderr, flush=True)
+
+    traffic = read_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "decode_step_us": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax,
+            "n_splits": S, "kv_bytes_per_step": kv_bytes,
+        },
+        "split_kernel_us": round(split_avg * 1e3, 2),
+        "combine_kernel_us": round(comb_avg * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(split_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "split (tad_split)",
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        gpu_out = out.cpu().double().numpy()
+        del q, k, v
+        torch.cuda.empty_cache()
+        ref, dt, threads, n_rows = cpu_baseline(c)
+        import numpy as np
+        err = float(np.abs(gpu_out - ref).max())
+        result["cpu_baseline"] = {
+            "value": round(kv_bytes / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole workload: all %d (b, head) rows, one pass, fp64 C oracle, %.2f s" % (n_rows, dt),
+            "seconds": round(dt, 3),
+        }
+        result["parity_max_abs_vs_oracle"] = err
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

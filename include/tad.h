@@ -1,0 +1,144 @@
+/*
+ * tad.h -- C ABI of libtad: exact single-query attention decoding over a long KV
+ * sequence, split into chunks that run on different compute units of one GPU, with
+ * the chunks' partial results merged by the log-sum-exp rescaling rule.
+ *
+ * What the library computes (per batch row b and query head h, one query token):
+ *
+ *   out[b,h,:] = softmax_j( q[b,h,:] . k[b,kh,j,:] / sqrt(d) + beta_j ) v[b,kh,j,:]
+ *
+ * over the keys j < L_b, with kh = floor(h / (Hq / Hkv)) and beta_j the optional
+ * ALiBi bias -slope_h * (L_b - 1 - j).  Sources: "Tree Attention Decoding"
+ * (tree_attn_decode.py gist), functions regular_decode (the definition) and
+ * tree_attn_decode (chunk the keys, keep a local max, a sum of exponentials and an
+ * exponential-weighted value sum per chunk, then take the global max, rescale and
+ * sum); "ALiBi with causal=True unexpected bias?" (llm-foundry issue 186: the causal
+ * bias row and passing a per-head vector instead of a full bias matrix);
+ * "Flash Aandacht: Revolutie in Transformer Efficientie", section on the mathematics
+ * (softmax decomposition and fusion).
+ *
+ * The split step is tad_split, the merge step tad_combine; tad_decode and
+ * tad_decode_ws run both.  All device work is asynchronous on the given stream.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are described by tad_tensor: a DEVICE pointer, a dtype, and shape and
+ *    strides in ELEMENTS.  The innermost stride must be 1; every row start must be
+ *    16-byte aligned (data pointer and outer strides in bytes multiples of 16).
+ *  - q   : [B, Hq, d] or [B, Hq, 1, d], TAD_F32 or TAD_BF16.
+ *  - k, v: [B, Hkv, Lmax, d] or [B, Lmax, d] (then Hkv = 1); same dtype (TAD_F32 or
+ *          TAD_BF16) and shape; any outer strides (e.g. a [B, Lmax, Hkv, d] cache
+ *          viewed as [B, Hkv, Lmax, d]).  Hq must be a multiple of Hkv.
+ *  - out : [B, Hq, d] or [B, Hq, 1, d], TAD_F32.
+ *  - d (head dimension) must be 64, 128, 256 or 512.
+ *  - seq_lens: DEVICE int32 [B] or NULL (every row uses Lmax).  Values are clamped
+ *    to [0, Lmax] on the device; keys at or beyond L_b are never read.  A row with
+ *    L_b = 0 produces out = 0.
+ *  - alibi_slopes: DEVICE fp32 [Hq] or NULL (no bias).
+ *  - n_splits: chunks per (b, head); <= 0 selects tad_auto_splits().  Chunking
+ *    follows torch.chunk: chunk length ceil(L_b / n_splits), the last one shorter,
+ *    trailing chunks possibly empty (an empty chunk contributes nothing).
+ *  - stream: HIP stream (0 = default stream).  All tensors are owned by the caller
+ *    and must stay valid until the stream work completes.  The library never frees
+ *    caller memory and keeps no state besides a per-device compute-unit count.
+ *  - Errors: 0 on success, a negative TAD_E* code otherwise; nothing is launched when
+ *    validation fails.  tad_last_error() gives a message (per calling thread).  No
+ *    C++ exception crosses the ABI and the library never aborts.  Faults inside a
+ *    kernel surface at the caller's next synchronisation, as for any HIP launch.
+ */
+#ifndef TAD_H
+#define TAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TAD_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1 };
+
+enum tad_status {
+    TAD_OK = 0,
+    TAD_EINVAL = -1,       /* null pointer, bad rank, shape mismatch, bad n_splits */
+    TAD_EDTYPE = -2,       /* dtype not allowed for this argument */
+    TAD_ELAYOUT = -3,      /* innermost stride != 1 or a row not 16-byte aligned */
+    TAD_EUNSUPPORTED = -4, /* head dimension or size outside what the kernels handle */
+    TAD_EWORKSPACE = -5,   /* workspace missing or too small */
+    TAD_EHIP = -6          /* a HIP runtime call or launch failed (message has the reason) */
+};
+
+typedef struct tad_tensor {
+    void *data;        /* device pointer */
+    int32_t dtype;     /* enum tad_dtype */
+    int32_t ndim;      /* 3 or 4 */
+    int64_t shape[4];
+    int64_t stride[4]; /* elements */
+} tad_tensor;
+
+/* Library version, TAD_VERSION of the build. */
+int tad_version(void);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+const char *tad_last_error(void);
+
+/*
+ * Chunks per (b, head) chosen when n_splits <= 0: enough work-groups to give every
+ * compute unit of `device` (-1: the current device) four, i.e.
+ * ceil(4 * CUs / (B * Hkv)), but no chunk shorter than 256 keys and at least one.
+ * Returns the count (>= 1) or a negative TAD_E* code.
+ */
+int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device);
+
+/*
+ * Bytes of device workspace tad_decode_ws / tad_split / tad_combine need for
+ * B * Hq rows, n_splits chunks and head dimension d (0 if an argument is < 1).
+ * Layout (all fp32, each array starting at a 256-byte boundary), with
+ * r = (b * Hq + h) * n_splits + s:
+ *     m[r]        chunk maximum of the scores, in base-2 units (score * log2 e);
+ *                 -inf for an empty chunk
+ *     l[r]        sum over the chunk of 2^(score*log2 e - m[r])
+ *     o[r * d + e] sum over the chunk of 2^(score*log2 e - m[r]) * v[., e]
+ * i.e. the per-chunk (local max, denominator, numerator) of tree_attn_decode, with
+ * the maximum kept in base 2.
+ */
+size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t n_splits, int32_t d);
+
+/*
+ * Split step: every (b, query head, chunk) partial (m, l, o) into `ws` (layout above).
+ * n_splits must be >= 1 here (use tad_auto_splits to pick one).  `ws` is a device
+ * buffer of at least tad_workspace_bytes(B, Hq, n_splits, d) bytes, 256-byte aligned.
+ */
+int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+              const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Merge step: for each (b, h), M = max_s m, w_s = 2^(m_s - M), L = sum_s w_s l_s,
+ * out = sum_s w_s o_s / L, summed in a fixed order (bit-reproducible).  Rows whose
+ * chunks are all empty get out = 0.  `out` is fp32 [B, Hq, d] (or [B, Hq, 1, d]).
+ */
+int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t n_splits,
+                int32_t d, tad_tensor *out, hipStream_t stream);
+
+/* Split + merge with a caller-provided workspace (no allocation). */
+int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+                  const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
+                  tad_tensor *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Split + merge; the workspace is taken with hipMallocAsync and released with
+ * hipFreeAsync on `stream` (stream-ordered, so concurrent calls on different
+ * streams do not share it).
+ */
+int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+               const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
+               tad_tensor *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAD_H */

@@ -1,0 +1,226 @@
+"""Python binding of libtad (split-KV exact attention decoding for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in ``include/tad.h``.  PyTorch supplies device memory and
+streams.  The functions carry the C names:
+
+- ``tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits, out, stream=None)``
+- ``tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits, out, ws, stream=None)``
+- ``tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream=None)``
+- ``tad_combine(ws, B, Hq, n_splits, d, out, stream=None)``
+- ``tad_auto_splits(B, Hkv, Lmax, device=-1)``, ``tad_workspace_bytes(B, Hq, n_splits, d)``
+- ``tad_version()``, ``tad_last_error()``
+
+and ``decode(...)`` allocates ``out`` and the workspace with torch and calls
+``tad_decode_ws``.  Tensors: q [B, Hq, d] fp32/bf16; k, v [B, Hkv, Lmax, d]
+fp32/bf16 (innermost dim contiguous); seq_lens int32 [B] or None; alibi_slopes fp32
+[Hq] or None; out fp32 [B, Hq, d].  All must live on the GPU.
+
+There is no fallback: if ``libtad.so`` has not been built, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtad.so")
+
+TAD_F32, TAD_BF16 = 0, 1
+TAD_OK, TAD_EINVAL, TAD_EDTYPE, TAD_ELAYOUT, TAD_EUNSUPPORTED, TAD_EWORKSPACE, TAD_EHIP = 0, -1, -2, -3, -4, -5, -6
+
+EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_bytes",
+           "tad_split", "tad_combine", "tad_decode_ws", "tad_decode")
+
+
+class TadTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class TadError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("libtad error %d: %s" % (code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Load libtad.so (raises if it is missing: there is no CPU path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtad.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m long_context_attention_split_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(TadTensor)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.tad_version.restype = ctypes.c_int
+    lib.tad_version.argtypes = []
+    lib.tad_last_error.restype = ctypes.c_char_p
+    lib.tad_last_error.argtypes = []
+    lib.tad_auto_splits.restype = i32
+    lib.tad_auto_splits.argtypes = [i32, i32, i64, i32]
+    lib.tad_workspace_bytes.restype = sz
+    lib.tad_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.tad_split.restype = ctypes.c_int
+    lib.tad_split.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
+    lib.tad_combine.restype = ctypes.c_int
+    lib.tad_combine.argtypes = [vp, sz, i32, i32, i32, i32, P, vp]
+    lib.tad_decode_ws.restype = ctypes.c_int
+    lib.tad_decode_ws.argtypes = [P, P, P, vp, vp, i32, P, vp, sz, vp]
+    lib.tad_decode.restype = ctypes.c_int
+    lib.tad_decode.argtypes = [P, P, P, vp, vp, i32, P, vp]
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def describe(t) -> TadTensor:
+    """tad_tensor for a torch tensor (no copy; the tensor must outlive the call's work)."""
+    torch = _torch()
+    if t.dtype == torch.float32:
+        dt = TAD_F32
+    elif t.dtype == torch.bfloat16:
+        dt = TAD_BF16
+    else:
+        dt = -1
+    if t.dim() > 4:
+        raise ValueError("tensors have at most 4 dims")
+    d = TadTensor()
+    d.data = t.data_ptr() if t.numel() > 0 or t.data_ptr() else None
+    d.dtype = dt
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> int:
+    if rc != TAD_OK:
+        raise TadError(rc, load().tad_last_error().decode())
+    return rc
+
+
+def tad_version() -> int:
+    return load().tad_version()
+
+
+def tad_last_error() -> str:
+    return load().tad_last_error().decode()
+
+
+def tad_auto_splits(B: int, Hkv: int, Lmax: int, device: int = -1) -> int:
+    r = load().tad_auto_splits(B, Hkv, Lmax, device)
+    if r < 0:
+        _check(r)
+    return r
+
+
+def tad_workspace_bytes(B: int, Hq: int, n_splits: int, d: int) -> int:
+    return load().tad_workspace_bytes(B, Hq, n_splits, d)
+
+
+def tad_split(q, k, v, seq_lens, alibi_slopes, n_splits: int, ws, stream=None) -> int:
+    lib = load()
+    dq, dk, dv = describe(q), describe(k), describe(v)
+    return _check(lib.tad_split(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
+                                _ptr(alibi_slopes), n_splits, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def tad_combine(ws, B: int, Hq: int, n_splits: int, d: int, out, stream=None) -> int:
+    lib = load()
+    do = describe(out)
+    return _check(lib.tad_combine(ws.data_ptr(), ws.numel() * ws.element_size(), B, Hq, n_splits, d,
+                                  ctypes.byref(do), _stream(stream)))
+
+
+def tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, ws, stream=None) -> int:
+    lib = load()
+    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    return _check(lib.tad_decode_ws(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
+                                    _ptr(alibi_slopes), n_splits, ctypes.byref(do), ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None) -> int:
+    lib = load()
+    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    return _check(lib.tad_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
+                                 _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
+
+
+def shape_of(q, k):
+    """(B, Hq, Hkv, Lmax, d) of a call's q and k."""
+    B, Hq, d = q.shape[0], q.shape[1], q.shape[-1]
+    if k.dim() == 4:
+        Hkv, Lmax = k.shape[1], k.shape[2]
+    else:
+        Hkv, Lmax = 1, k.shape[1]
+    return B, Hq, Hkv, Lmax, d
+
+
+def resolve_splits(q, k, n_splits: int = 0) -> int:
+    B, Hq, Hkv, Lmax, d = shape_of(q, k)
+    return n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, q.device.index or 0)
+
+
+def workspace(q, k, n_splits: int):
+    """A torch-allocated workspace for (q, k) with n_splits chunks (uint8, 256-aligned)."""
+    torch = _torch()
+    B, Hq, Hkv, Lmax, d = shape_of(q, k)
+    nbytes = tad_workspace_bytes(B, Hq, n_splits, d)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+
+
+def decode(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 0, stream=None):
+    """out = tad_decode_ws(...) with torch-allocated out [B, Hq, d] fp32 and workspace."""
+    torch = _torch()
+    S = resolve_splits(q, k, n_splits)
+    ws = workspace(q, k, S)
+    B, Hq, Hkv, Lmax, d = shape_of(q, k)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    tad_decode_ws(q, k, v, seq_lens, alibi_slopes, S, out, ws, stream)
+    return out
+
+
+def split_partials(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 1, stream=None):
+    """Run tad_split only; returns (m, l, o) views of the workspace:
+    m, l [B, Hq, S] (m in base-2 units), o [B, Hq, S, d]."""
+    torch = _torch()
+    ws = workspace(q, k, n_splits)
+    tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream)
+    B, Hq, Hkv, Lmax, d = shape_of(q, k)
+    n = B * Hq * n_splits
+    al = lambda x: (x + 255) // 256 * 256
+    off_l = al(4 * n)
+    off_o = off_l + al(4 * n)
+    m = ws[0:4 * n].view(torch.float32).view(B, Hq, n_splits)
+    l = ws[off_l:off_l + 4 * n].view(torch.float32).view(B, Hq, n_splits)
+    o = ws[off_o:off_o + 4 * n * d].view(torch.float32).view(B, Hq, n_splits, d)
+    return m, l, o

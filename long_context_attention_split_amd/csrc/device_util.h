@@ -1,0 +1,88 @@
+// device_util.h -- small gfx950 building blocks used by the decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tad {
+
+constexpr float kNegInf = -__builtin_inff();
+
+// Buffer resource over [base, base + bytes): loads past `bytes` return zero, which is
+// how chunk tails and ragged sequence ends are kept from reading out of range.
+// Word 3 = 0x00020000 is the raw (untyped, 32-bit data format) setting for gfx9 parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16-byte load through a buffer resource; `off` is a byte offset from the base.
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// bf16 pair in one dword -> two fp32 (bf16 is the upper half of an fp32).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 consecutive elements of a row as fp32: one 16-byte load of bf16, or two of fp32.
+template <bool BF16>
+struct Row8 {
+    static constexpr int kLoads = BF16 ? 1 : 2;
+    uint4 raw[kLoads];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) raw[i] = load16(r, off + 16u * i);
+    }
+    __device__ __forceinline__ float operator[](int e) const {
+        if constexpr (BF16) {
+            const uint32_t w = (&raw[0].x)[e >> 1];
+            return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+        } else {
+            return __uint_as_float((&raw[e >> 2].x)[e & 3]);
+        }
+    }
+};
+
+// DPP controls (gfx9): quad permutations, and mirrors inside 8- and 16-lane rows.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8, 16, 32 or 64); every lane of a group
+// ends with the same value (each butterfly step is symmetric).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group size");
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppRowHalfMirror>(x);
+    if constexpr (G >= 16) x += dpp<kDppRowMirror>(x);
+    if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace tad

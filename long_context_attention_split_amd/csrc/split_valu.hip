@@ -1,0 +1,219 @@
+// split_valu.hip -- split step of split-KV decoding on the vector ALUs (gfx950).
+//
+// One work-group (4 waves) owns one (batch row b, query head h, chunk s).  The chunk
+// is the s-th torch.chunk piece of the row's L_b keys.  It produces the chunk's
+// partial (m, l, o): the local maximum of the scores, the sum of exponentials
+// relative to it, and the exponential-weighted sum of value rows -- the
+// (local_max, den, num) triple of tree_attn_decode in "Tree Attention Decoding",
+// with the maximum and the exponentials in base 2 (the query is pre-scaled by
+// d^-1/2 * log2 e so that exp(x) becomes 2^x on the transcendental unit).
+//
+// Inside the chunk the keys stream through registers in tiles; each tile updates a
+// running maximum and sum in the manner of the block loop in "Flash Aandacht"
+// (section "Implementatiedetails"), but the output accumulator is kept
+// un-normalised -- rescaled by 2^(m_old - m_new) only -- and divided once, in the
+// merge step.  (The page's listing divides by the new running sum every block
+// without first multiplying the old output back by the old sum, which is only right
+// when the whole sequence fits in one block.)
+//
+// Lane layout: a key row of d elements is spread over G = d/8 lanes, each holding 8
+// consecutive elements (one 16-byte load for bf16, two for fp32).  A wave therefore
+// covers 64/G keys per load instruction; the q.k dot product is 8 FMAs per lane
+// followed by a log2(G)-step DPP butterfly inside the lane group.  Each lane group
+// runs its own online softmax over the keys it sees (no cross-group traffic in the
+// loop); the 4*64/G group states of a work-group are merged through LDS at the end.
+//
+// HBM traffic: every K and V byte of the chunk is read exactly once with 16-byte
+// coalesced buffer loads; loads past the chunk end return zero (buffer range), so
+// ragged tails and neighbouring chunks are never fetched.
+
+#include "device_util.h"
+#include "tad_internal.h"
+
+namespace tad {
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
+    constexpr int EPL = 8;                       // elements per lane per key
+    constexpr int G = D / EPL;                   // lanes per key row
+    constexpr int KPW = 64 / G;                  // keys per wave load instruction
+    constexpr int ELEM = BF16 ? 2 : 4;
+    constexpr int U = 16 / ELEM;                 // keys per lane group per tile
+    constexpr int T = KPW * U;                   // keys per wave tile
+    constexpr int NW = kSplitThreads / 64;       // waves per work-group
+    constexpr int SLOTS = NW * KPW;              // lane-group states to merge
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane / G;
+    const int sub = lane % G;
+
+    // ---- work-group -> (b, h, s).  With query-head groups (GQA handled here), the g
+    // work-groups that read the same KV chunk get ids that are equal modulo 8, so they
+    // land on the same XCD and share its L2.
+    int b, h, s;
+    const int S = a.S;
+    if (a.group == 1) {
+        const int id = blockIdx.x;
+        s = id % S;
+        const int row = id / S;
+        b = row / a.Hq;
+        h = row % a.Hq;
+    } else {
+        const int id = blockIdx.x;
+        const int xcd = id & 7;
+        const int slot = id >> 3;
+        const int r = slot % a.group;
+        const int u = (slot / a.group) * 8 + xcd;          // (b, kvh, s) unit
+        if (u >= a.B * a.Hkv * S) return;
+        s = u % S;
+        const int bk = u / S;
+        b = bk / a.Hkv;
+        h = (bk % a.Hkv) * a.group + r;
+    }
+    const int kvh = h / a.group;
+
+    int L = a.Lmax;
+    if (a.seq_lens) L = min(max(a.seq_lens[b], 0), a.Lmax);
+    const int c = (L + S - 1) / S;                       // torch.chunk length
+    const int j0 = (int)min((int64_t)s * c, (int64_t)L);
+    const int j1 = min(j0 + c, L);
+    const int n = j1 - j0;
+
+    // ---- per-chunk buffer resources: [chunk start, chunk end) of this head's K and V.
+    const uint32_t krow = (uint32_t)(a.skj * ELEM), vrow = (uint32_t)(a.svj * ELEM);
+    const char *kbase = (const char *)a.k + ((int64_t)b * a.skb + (int64_t)kvh * a.skh + (int64_t)j0 * a.skj) * ELEM;
+    const char *vbase = (const char *)a.v + ((int64_t)b * a.svb + (int64_t)kvh * a.svh + (int64_t)j0 * a.svj) * ELEM;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)n * krow);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)n * vrow);
+
+    // ---- this lane's 8 query elements, pre-scaled into base-2 units.
+    float qv[EPL];
+    {
+        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + sub * EPL;
+        if (a.q_bf16) {
+            const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qv[2 * i] = bf16_lo(ws[i]) * a.qscale;
+                qv[2 * i + 1] = bf16_hi(ws[i]) * a.qscale;
+            }
+        } else {
+            const float4 *qp = (const float4 *)((const float *)a.q + qoff);
+            const float4 x0 = qp[0], x1 = qp[1];
+            qv[0] = x0.x * a.qscale; qv[1] = x0.y * a.qscale; qv[2] = x0.z * a.qscale; qv[3] = x0.w * a.qscale;
+            qv[4] = x1.x * a.qscale; qv[5] = x1.y * a.qscale; qv[6] = x1.z * a.qscale; qv[7] = x1.w * a.qscale;
+        }
+    }
+    // ALiBi in base-2 units: bias of key j is slope*log2e*(j - (L-1)); j - (L-1) is an
+    // exact integer in fp32 for L < 2^24.
+    const float slope2 = a.slopes ? a.slopes[h] * 1.4426950408889634f : 0.f;
+    const bool alibi = a.slopes != nullptr;
+
+    float m = kNegInf, l = 0.f;
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+
+    const uint32_t lane_off = (uint32_t)(sub * EPL * ELEM);
+    for (int t0 = wave * T; t0 < n; t0 += NW * T) {
+        Row8<BF16> kk[U], vv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) kk[u].load(kr, (uint32_t)(t0 + u * KPW + grp) * krow + lane_off);
+#pragma unroll
+        for (int u = 0; u < U; ++u) vv[u].load(vr, (uint32_t)(t0 + u * KPW + grp) * vrow + lane_off);
+
+        float sc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc = fmaf(qv[e], kk[u][e], acc);
+            sc[u] = group_sum<G>(acc);
+        }
+        if (alibi) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                sc[u] = fmaf(slope2, (float)(j0 + t0 + u * KPW + grp - (L - 1)), sc[u]);
+        }
+        if (t0 + T > n) {                                   // tail tile: mask keys past the chunk
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (t0 + u * KPW + grp >= n) sc[u] = kNegInf;
+        }
+        float mt = sc[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mt = fmaxf(mt, sc[u]);
+        const float m_new = fmaxf(m, mt);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // all masked so far: no NaN
+        const float alpha = exp2_fast(m - m_use);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float p = exp2_fast(sc[u] - m_use);
+            l += p;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vv[u][e], o[e]);
+        }
+        m = m_new;
+    }
+
+    // ---- merge the SLOTS lane-group states of this work-group (fixed order).
+    __shared__ float lds_o[SLOTS][D];
+    __shared__ float lds_m[SLOTS], lds_l[SLOTS];
+    const int slot = wave * KPW + grp;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) lds_o[slot][sub * EPL + e] = o[e];
+    if (sub == 0) {
+        lds_m[slot] = m;
+        lds_l[slot] = l;
+    }
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) M = fmaxf(M, lds_m[i]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    const int64_t r = ((int64_t)b * a.Hq + h) * S + s;
+    for (int e = threadIdx.x; e < D; e += kSplitThreads) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_o[i][e], acc);
+        a.ws_o[r * D + e] = acc;
+    }
+    if (threadIdx.x == 0) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_l[i], acc);
+        a.ws_m[r] = M;
+        a.ws_l[r] = acc;
+    }
+}
+
+template <int D, bool BF16>
+static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
+    int64_t grid;
+    if (a.group == 1) {
+        grid = (int64_t)a.B * a.Hq * a.S;
+    } else {
+        const int64_t units = (int64_t)a.B * a.Hkv * a.S;
+        grid = (units + 7) / 8 * 8 * a.group;
+    }
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((split_valu_kernel<D, BF16>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_valu(const SplitArgs &a, int d, bool kv_bf16, hipStream_t st) {
+    switch (d) {
+        case 64: return kv_bf16 ? launch_t<64, true>(a, st) : launch_t<64, false>(a, st);
+        case 128: return kv_bf16 ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
+        case 256: return kv_bf16 ? launch_t<256, true>(a, st) : launch_t<256, false>(a, st);
+        case 512: return kv_bf16 ? launch_t<512, true>(a, st) : launch_t<512, false>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tad

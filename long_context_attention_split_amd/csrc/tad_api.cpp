@@ -1,0 +1,330 @@
+// tad_api.cpp -- the C ABI of libtad (declared in include/tad.h): argument
+// validation, chunk-count choice, workspace carving and the two kernel launches.
+// Every check that can fail runs before anything is launched.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "tad.h"
+#include "tad_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return TAD_OK;
+}
+
+int elem_size(int32_t dtype) { return dtype == TAD_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shapes and strides of one decode call, normalised to 4-D [B, H, L, d] views.
+struct Problem {
+    int64_t B = 0, Hq = 0, Hkv = 0, Lmax = 0, d = 0;
+    int32_t q_dtype = 0, kv_dtype = 0;
+    int64_t sqb = 0, sqh = 0;
+    int64_t skb = 0, skh = 0, skj = 0;
+    int64_t svb = 0, svh = 0, svj = 0;
+};
+
+// q or out: [B, H, d] or [B, H, 1, d].
+int parse_query_like(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int64_t *d,
+                     int64_t *sb, int64_t *sh) {
+    if (!t) return fail(TAD_EINVAL, "%s: null tensor descriptor", name);
+    if (!t->data) return fail(TAD_EINVAL, "%s: null data pointer", name);
+    if (t->ndim == 3) {
+        *B = t->shape[0]; *H = t->shape[1]; *d = t->shape[2];
+        *sb = t->stride[0]; *sh = t->stride[1];
+        if (t->stride[2] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
+    } else if (t->ndim == 4) {
+        if (t->shape[2] != 1) return fail(TAD_EINVAL, "%s: 4-D form must be [B, H, 1, d]", name);
+        *B = t->shape[0]; *H = t->shape[1]; *d = t->shape[3];
+        *sb = t->stride[0]; *sh = t->stride[1];
+        if (t->stride[3] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
+    } else {
+        return fail(TAD_EINVAL, "%s: ndim must be 3 or 4 (got %d)", name, t->ndim);
+    }
+    if (*B < 0 || *H < 1 || *d < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
+    return TAD_OK;
+}
+
+// k or v: [B, Hkv, L, d] or [B, L, d].
+int parse_kv(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int64_t *L, int64_t *d,
+             int64_t *sb, int64_t *sh, int64_t *sj) {
+    if (!t) return fail(TAD_EINVAL, "%s: null tensor descriptor", name);
+    if (!t->data) return fail(TAD_EINVAL, "%s: null data pointer", name);
+    if (t->ndim == 4) {
+        *B = t->shape[0]; *H = t->shape[1]; *L = t->shape[2]; *d = t->shape[3];
+        *sb = t->stride[0]; *sh = t->stride[1]; *sj = t->stride[2];
+        if (t->stride[3] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
+    } else if (t->ndim == 3) {
+        *B = t->shape[0]; *H = 1; *L = t->shape[1]; *d = t->shape[2];
+        *sb = t->stride[0]; *sh = 0; *sj = t->stride[1];
+        if (t->stride[2] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
+    } else {
+        return fail(TAD_EINVAL, "%s: ndim must be 3 or 4 (got %d)", name, t->ndim);
+    }
+    if (*B < 0 || *H < 1 || *L < 0 || *d < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
+    if (t->dtype != TAD_F32 && t->dtype != TAD_BF16)
+        return fail(TAD_EDTYPE, "%s: dtype must be TAD_F32 or TAD_BF16", name);
+    const int64_t es = elem_size(t->dtype);
+    if (!aligned16(t->data) || (*sb * es) % 16 || (*sh * es) % 16 || (*sj * es) % 16)
+        return fail(TAD_ELAYOUT, "%s: rows must start on 16-byte boundaries", name);
+    if (*L > 1 && *sj < *d) return fail(TAD_ELAYOUT, "%s: key stride smaller than d (rows overlap)", name);
+    return TAD_OK;
+}
+
+int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, Problem *P) {
+    int rc;
+    int64_t Bq, Hq, dq;
+    if ((rc = parse_query_like(q, "q", &Bq, &Hq, &dq, &P->sqb, &P->sqh))) return rc;
+    if (q->dtype != TAD_F32 && q->dtype != TAD_BF16) return fail(TAD_EDTYPE, "q: dtype must be TAD_F32 or TAD_BF16");
+    const int64_t qes = elem_size(q->dtype);
+    if (!aligned16(q->data) || (P->sqb * qes) % 16 || (P->sqh * qes) % 16)
+        return fail(TAD_ELAYOUT, "q: rows must start on 16-byte boundaries");
+    int64_t Bk, Hk, Lk, dk, Bv, Hv, Lv, dv;
+    if ((rc = parse_kv(k, "k", &Bk, &Hk, &Lk, &dk, &P->skb, &P->skh, &P->skj))) return rc;
+    if ((rc = parse_kv(v, "v", &Bv, &Hv, &Lv, &dv, &P->svb, &P->svh, &P->svj))) return rc;
+    if (k->dtype != v->dtype) return fail(TAD_EDTYPE, "k and v must share a dtype");
+    if (Bk != Bv || Hk != Hv || Lk != Lv || dk != dv) return fail(TAD_EINVAL, "k and v shapes differ");
+    if (Bk != Bq) return fail(TAD_EINVAL, "batch of q (%lld) and k (%lld) differ", (long long)Bq, (long long)Bk);
+    if (dk != dq) return fail(TAD_EINVAL, "head dim of q (%lld) and k (%lld) differ", (long long)dq, (long long)dk);
+    if (Hq % Hk) return fail(TAD_EINVAL, "query heads (%lld) not a multiple of KV heads (%lld)", (long long)Hq, (long long)Hk);
+    if (dq != 64 && dq != 128 && dq != 256 && dq != 512)
+        return fail(TAD_EUNSUPPORTED, "head dim %lld not supported (64, 128, 256, 512)", (long long)dq);
+    if (Bq > 0x7fffffff || Hq > 0x7fffffff || Lk > 0x3fffffff)
+        return fail(TAD_EUNSUPPORTED, "sizes too large");
+    P->B = Bq; P->Hq = Hq; P->Hkv = Hk; P->Lmax = Lk; P->d = dq;
+    P->q_dtype = q->dtype; P->kv_dtype = k->dtype;
+    return TAD_OK;
+}
+
+int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *soh) {
+    int rc;
+    int64_t B, H, d;
+    if ((rc = parse_query_like(out, "out", &B, &H, &d, sob, soh))) return rc;
+    if (out->dtype != TAD_F32) return fail(TAD_EDTYPE, "out: dtype must be TAD_F32");
+    if (B != P.B || H != P.Hq || d != P.d) return fail(TAD_EINVAL, "out: shape must be [B, Hq, d] of the inputs");
+    return TAD_OK;
+}
+
+// 32-bit buffer offsets: one chunk plus a tile of overrun must span < 4 GiB.
+int check_offsets(const Problem &P, int64_t S) {
+    const int64_t es = elem_size(P.kv_dtype);
+    const int64_t c = (P.Lmax + S - 1) / S;
+    const int64_t span_k = (c + 64) * P.skj * es, span_v = (c + 64) * P.svj * es;
+    if (span_k >= (int64_t(1) << 32) || span_v >= (int64_t(1) << 32))
+        return fail(TAD_EUNSUPPORTED, "chunk spans >= 4 GiB; use more splits");
+    return TAD_OK;
+}
+
+std::mutex g_cu_mu;
+int g_cu_count[64] = {0};
+
+int device_cus(int32_t device, int *cus) {
+    int dev = device;
+    if (dev < 0) {
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(TAD_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    if (dev >= 64) return fail(TAD_EINVAL, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_cu_mu);
+    if (!g_cu_count[dev]) {
+        int n = 0;
+        hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail(TAD_EHIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+        g_cu_count[dev] = n > 0 ? n : 1;
+    }
+    *cus = g_cu_count[dev];
+    return TAD_OK;
+}
+
+int32_t auto_splits_for(int64_t B, int64_t Hkv, int64_t Lmax, int cus) {
+    const int64_t units = B * Hkv > 0 ? B * Hkv : 1;
+    int64_t S = (4 * (int64_t)cus + units - 1) / units;
+    const int64_t by_len = Lmax / 256;                 // no chunk shorter than 256 keys
+    if (S > by_len) S = by_len;
+    if (S > tad::kMaxSplits) S = tad::kMaxSplits;
+    if (S < 1) S = 1;
+    return (int32_t)S;
+}
+
+struct WsPtrs {
+    float *m, *l, *o;
+};
+
+int carve_ws(void *ws, size_t ws_bytes, int64_t rows, int64_t S, int64_t d, WsPtrs *p) {
+    const tad::WsLayout L = tad::ws_layout(rows, S, d);
+    if (!ws) return fail(TAD_EWORKSPACE, "workspace pointer is null");
+    if ((uintptr_t)ws & 255u) return fail(TAD_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < L.total)
+        return fail(TAD_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+    p->m = (float *)((char *)ws + L.off_m);
+    p->l = (float *)((char *)ws + L.off_l);
+    p->o = (float *)((char *)ws + L.off_o);
+    return TAD_OK;
+}
+
+int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+                 const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
+                 hipStream_t stream) {
+    tad::SplitArgs a;
+    a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.q_bf16 = P.q_dtype == TAD_BF16;
+    a.k = k->data; a.v = v->data;
+    a.skb = P.skb; a.skh = P.skh; a.skj = P.skj;
+    a.svb = P.svb; a.svh = P.svh; a.svj = P.svj;
+    a.seq_lens = seq_lens; a.slopes = slopes;
+    a.B = (int32_t)P.B; a.Hq = (int32_t)P.Hq; a.Hkv = (int32_t)P.Hkv; a.Lmax = (int32_t)P.Lmax;
+    a.S = S; a.group = (int32_t)(P.Hq / P.Hkv);
+    a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
+    a.ws_m = w.m; a.ws_l = w.l; a.ws_o = w.o;
+    hipError_t e = tad::launch_split_valu(a, (int)P.d, P.kv_dtype == TAD_BF16, stream);
+    if (e != hipSuccess) return fail(TAD_EHIP, "split kernel launch: %s", hipGetErrorString(e));
+    return TAD_OK;
+}
+
+int launch_merge(int64_t B, int64_t Hq, int32_t S, int64_t d, const WsPtrs &w, const tad_tensor *out,
+                 int64_t sob, int64_t soh, hipStream_t stream) {
+    tad::CombineArgs c;
+    c.ws_m = w.m; c.ws_l = w.l; c.ws_o = w.o;
+    c.out = (float *)out->data; c.sob = sob; c.soh = soh;
+    c.B = (int32_t)B; c.Hq = (int32_t)Hq; c.S = S;
+    hipError_t e = tad::launch_combine(c, (int)d, stream);
+    if (e != hipSuccess) return fail(TAD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));
+    return TAD_OK;
+}
+
+int check_splits(int32_t S) {
+    if (S < 1 || S > tad::kMaxSplits)
+        return fail(TAD_EINVAL, "n_splits must be in [1, %d] (got %d)", tad::kMaxSplits, S);
+    return TAD_OK;
+}
+
+// Validation shared by tad_decode and tad_decode_ws; resolves automatic n_splits.
+int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, int32_t n_splits,
+                   const tad_tensor *out, Problem *P, int32_t *S, int64_t *sob, int64_t *soh) {
+    int rc;
+    if ((rc = parse_problem(q, k, v, P))) return rc;
+    if ((rc = check_out(out, *P, sob, soh))) return rc;
+    if (n_splits <= 0) {
+        int cus = 0;
+        if ((rc = device_cus(-1, &cus))) return rc;
+        *S = auto_splits_for(P->B, P->Hkv, P->Lmax, cus);
+    } else {
+        *S = n_splits;
+    }
+    if ((rc = check_splits(*S))) return rc;
+    return check_offsets(*P, *S);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tad_version(void) { return TAD_VERSION; }
+
+const char *tad_last_error(void) { return g_last_error.c_str(); }
+
+int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device) {
+    if (B < 1 || Hkv < 1 || Lmax < 0) return fail(TAD_EINVAL, "tad_auto_splits: bad sizes");
+    int cus = 0;
+    int rc = device_cus(device, &cus);
+    if (rc) return rc;
+    ok();
+    return auto_splits_for(B, Hkv, Lmax, cus);
+}
+
+size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t n_splits, int32_t d) {
+    if (B < 1 || Hq < 1 || n_splits < 1 || d < 1) return 0;
+    return tad::ws_layout((int64_t)B * Hq, n_splits, d).total;
+}
+
+int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
+              const float *alibi_slopes, int32_t n_splits, void *ws, size_t ws_bytes, hipStream_t stream) {
+    Problem P;
+    int rc;
+    if ((rc = parse_problem(q, k, v, &P))) return rc;
+    if ((rc = check_splits(n_splits))) return rc;
+    if ((rc = check_offsets(P, n_splits))) return rc;
+    WsPtrs w;
+    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq, n_splits, P.d, &w))) return rc;
+    if (P.B == 0) return ok();
+    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, stream))) return rc;
+    return ok();
+}
+
+int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t n_splits, int32_t d,
+                tad_tensor *out, hipStream_t stream) {
+    int rc;
+    if (B < 0 || Hq < 1) return fail(TAD_EINVAL, "tad_combine: bad B or Hq");
+    if (d != 64 && d != 128 && d != 256 && d != 512)
+        return fail(TAD_EUNSUPPORTED, "head dim %d not supported (64, 128, 256, 512)", d);
+    if ((rc = check_splits(n_splits))) return rc;
+    Problem P;
+    P.B = B; P.Hq = Hq; P.d = d;
+    int64_t sob, soh;
+    if ((rc = check_out(out, P, &sob, &soh))) return rc;
+    WsPtrs w;
+    if ((rc = carve_ws(const_cast<void *>(ws), ws_bytes, (int64_t)B * Hq, n_splits, d, &w))) return rc;
+    if (B == 0) return ok();
+    if ((rc = launch_merge(B, Hq, n_splits, d, w, out, sob, soh, stream))) return rc;
+    return ok();
+}
+
+int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
+                  const float *alibi_slopes, int32_t n_splits, tad_tensor *out, void *ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    Problem P;
+    int32_t S;
+    int64_t sob, soh;
+    int rc;
+    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &sob, &soh))) return rc;
+    WsPtrs w;
+    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq, S, P.d, &w))) return rc;
+    if (P.B == 0) return ok();
+    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, S, w, stream))) return rc;
+    if ((rc = launch_merge(P.B, P.Hq, S, P.d, w, out, sob, soh, stream))) return rc;
+    return ok();
+}
+
+int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
+               const float *alibi_slopes, int32_t n_splits, tad_tensor *out, hipStream_t stream) {
+    Problem P;
+    int32_t S;
+    int64_t sob, soh;
+    int rc;
+    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &sob, &soh))) return rc;
+    if (P.B == 0) return ok();
+    const size_t bytes = tad::ws_layout(P.B * P.Hq, S, P.d).total;
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) return fail(TAD_EHIP, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
+    WsPtrs w;
+    rc = carve_ws(ws, bytes, P.B * P.Hq, S, P.d, &w);
+    if (!rc) rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, S, w, stream);
+    if (!rc) rc = launch_merge(P.B, P.Hq, S, P.d, w, out, sob, soh, stream);
+    e = hipFreeAsync(ws, stream);
+    if (rc) return rc;
+    if (e != hipSuccess) return fail(TAD_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

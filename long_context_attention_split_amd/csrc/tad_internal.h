@@ -1,0 +1,58 @@
+// tad_internal.h -- argument blocks shared by the host library and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace tad {
+
+// Everything the split kernels need, by value (lives in the kernel argument segment).
+struct SplitArgs {
+    const void *q;          // [B, Hq, d], innermost contiguous
+    int64_t sqb, sqh;       // q element strides
+    int32_t q_bf16;         // q dtype: 1 = bf16, 0 = fp32
+    const void *k, *v;      // [B, Hkv, Lmax, d], innermost contiguous
+    int64_t skb, skh, skj;  // k element strides
+    int64_t svb, svh, svj;  // v element strides
+    const int32_t *seq_lens;  // [B] or null
+    const float *slopes;      // [Hq] or null
+    int32_t B, Hq, Hkv, Lmax, S, group;
+    float qscale;           // d^-1/2 * log2(e): scores come out in base-2 units
+    float *ws_m, *ws_l, *ws_o;  // partial arrays (see tad.h)
+};
+
+struct CombineArgs {
+    const float *ws_m, *ws_l, *ws_o;
+    float *out;             // [B, Hq, d] fp32
+    int64_t sob, soh;       // out element strides
+    int32_t B, Hq, S;
+};
+
+// Workspace carving (same arithmetic as tad_workspace_bytes).
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+    size_t off_m, off_l, off_o, total;
+};
+
+inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
+    WsLayout w;
+    size_t n = size_t(rows) * size_t(S);
+    w.off_m = 0;
+    w.off_l = align256(n * sizeof(float));
+    w.off_o = w.off_l + align256(n * sizeof(float));
+    w.total = w.off_o + align256(n * size_t(d) * sizeof(float));
+    return w;
+}
+
+// Launchers (defined next to their kernels).  Return the hipError_t of the launch.
+hipError_t launch_split_valu(const SplitArgs &a, int d, bool kv_bf16, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
+
+// Keys per work-group tile of the VALU split kernel (for tests of the host logic).
+constexpr int kSplitThreads = 256;
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 4096;
+
+}  // namespace tad

@@ -1,0 +1,184 @@
+"""Host-side checks of libtad's C ABI that need no GPU.
+
+The library must load, export every function include/tad.h declares, and reject
+bad arguments with the documented error codes before anything reaches the device.
+Descriptors here carry fake (but aligned) device addresses: validation never
+dereferences them, and every call below fails or returns before a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_split_amd as tad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tad.h")
+
+FAKE = 0x10000000   # 256-byte aligned stand-in address, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tad_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert set(declared) == set(tad.EXPORTS)
+    so = lib.load()
+    for name in declared:
+        assert hasattr(so, name), name
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define TAD_VERSION (\d+)", open(HEADER).read())
+    assert lib.tad_version() == int(m.group(1))
+
+
+def test_workspace_bytes_layout(lib):
+    # m and l: rows*S floats each, 256-aligned; o: rows*S*d floats
+    assert lib.tad_workspace_bytes(1, 32, 32, 128) == 2 * 4096 + 1024 * 128 * 4
+    assert lib.tad_workspace_bytes(8, 32, 16, 128) == 2 * 16384 + 4096 * 128 * 4
+    assert lib.tad_workspace_bytes(1, 1, 8, 512) == 2 * 256 + 8 * 512 * 4
+    assert lib.tad_workspace_bytes(0, 1, 1, 64) == 0
+    assert lib.tad_workspace_bytes(1, 1, 0, 64) == 0
+
+
+def desc(shape, dtype=tad.TAD_BF16, strides=None, addr=FAKE):
+    t = tad.TadTensor()
+    t.data = addr
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        t.shape[i] = s
+        t.stride[i] = st
+    return t
+
+
+def good(B=2, Hq=8, Hkv=2, L=100, d=128):
+    return dict(q=desc([B, Hq, d], tad.TAD_F32), k=desc([B, Hkv, L, d]), v=desc([B, Hkv, L, d]),
+                out=desc([B, Hq, d], tad.TAD_F32))
+
+
+def call_split(so, a, n_splits=4, ws=FAKE, ws_bytes=1 << 30):
+    return so.tad_split(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]), None, None,
+                        n_splits, ws, ws_bytes, None)
+
+
+def call_decode_ws(so, a, n_splits=4, ws=FAKE, ws_bytes=1 << 30):
+    return so.tad_decode_ws(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]), None, None,
+                            n_splits, ctypes.byref(a["out"]), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: a.update(q=desc([2, 8, 96], tad.TAD_F32), k=desc([2, 2, 100, 96]), v=desc([2, 2, 100, 96]),
+                        out=desc([2, 8, 96], tad.TAD_F32)), tad.TAD_EUNSUPPORTED),
+    (lambda a: a.update(q=desc([2, 6, 128], tad.TAD_F32), out=desc([2, 6, 128], tad.TAD_F32),
+                        k=desc([2, 4, 100, 128]), v=desc([2, 4, 100, 128])), tad.TAD_EINVAL),   # 6 % 4
+    (lambda a: a.update(k=desc([2, 2, 100, 128], tad.TAD_F32)), tad.TAD_EDTYPE),               # k f32, v bf16
+    (lambda a: a.update(k=desc([2, 2, 100, 128], 7), v=desc([2, 2, 100, 128], 7)), tad.TAD_EDTYPE),
+    (lambda a: a.update(q=desc([2, 8, 128], 5)), tad.TAD_EDTYPE),
+    (lambda a: a.update(k=desc([2, 2, 100, 128], addr=FAKE + 8)), tad.TAD_ELAYOUT),            # misaligned
+    (lambda a: a.update(k=desc([2, 2, 100, 128], strides=[25600, 12800, 128, 2])), tad.TAD_ELAYOUT),
+    (lambda a: a.update(k=desc([2, 2, 100, 128], strides=[25604, 12800, 128, 1])), tad.TAD_ELAYOUT),
+    (lambda a: a.update(q=desc([3, 8, 128], tad.TAD_F32)), tad.TAD_EINVAL),                    # batch
+    (lambda a: a.update(v=desc([2, 2, 99, 128])), tad.TAD_EINVAL),                             # k/v shape
+    (lambda a: a.update(q=desc([2, 8, 64], tad.TAD_F32)), tad.TAD_EINVAL),                     # head dim
+    (lambda a: a.update(q=desc([2, 8, 2, 128], tad.TAD_F32)), tad.TAD_EINVAL),                 # 4-D q, i != 1
+    (lambda a: a.update(k=desc([2, 2, 100, 128], addr=0)), tad.TAD_EINVAL),                    # null data
+    (lambda a: a.update(k=desc([200, 128])), tad.TAD_EINVAL),                                  # 2-D k
+])
+def test_split_rejects_bad_arguments(lib, mutate, code):
+    so = lib.load()
+    a = good()
+    mutate(a)
+    assert call_split(so, a) == code
+    assert lib.tad_last_error() != ""
+
+
+def test_split_rejects_bad_splits_and_workspace(lib):
+    so = lib.load()
+    a = good()
+    assert call_split(so, a, n_splits=0) == tad.TAD_EINVAL
+    assert call_split(so, a, n_splits=4097) == tad.TAD_EINVAL
+    need = lib.tad_workspace_bytes(2, 8, 4, 128)
+    assert call_split(so, a, ws_bytes=need - 1) == tad.TAD_EWORKSPACE
+    assert call_split(so, a, ws=FAKE + 16) == tad.TAD_EWORKSPACE
+    assert call_split(so, a, ws=0) == tad.TAD_EWORKSPACE
+    assert "workspace" in lib.tad_last_error()
+
+
+def test_null_descriptors(lib):
+    so = lib.load()
+    a = good()
+    rc = so.tad_split(None, ctypes.byref(a["k"]), ctypes.byref(a["v"]), None, None, 4, FAKE, 1 << 30, None)
+    assert rc == tad.TAD_EINVAL
+    rc = so.tad_decode_ws(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]), None, None, 4,
+                          None, FAKE, 1 << 30, None)
+    assert rc == tad.TAD_EINVAL
+
+
+def test_decode_ws_checks_out(lib):
+    so = lib.load()
+    a = good()
+    a["out"] = desc([2, 8, 128], tad.TAD_BF16)
+    assert call_decode_ws(so, a) == tad.TAD_EDTYPE
+    a["out"] = desc([2, 7, 128], tad.TAD_F32)
+    assert call_decode_ws(so, a) == tad.TAD_EINVAL
+    a["out"] = desc([2, 8, 128], tad.TAD_F32, strides=[1024, 128, 2])
+    assert call_decode_ws(so, a) == tad.TAD_ELAYOUT
+
+
+def test_combine_validation(lib):
+    so = lib.load()
+    out = desc([2, 8, 128], tad.TAD_F32)
+    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 4, 96, ctypes.byref(out), None) == tad.TAD_EUNSUPPORTED
+    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 0, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
+    assert so.tad_combine(FAKE, 10, 2, 8, 4, 128, ctypes.byref(out), None) == tad.TAD_EWORKSPACE
+    assert so.tad_combine(FAKE, 1 << 30, 2, 9, 4, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
+
+
+def test_empty_batch_is_a_no_op(lib):
+    """B = 0 validates and returns success without touching the device."""
+    so = lib.load()
+    a = good(B=0)
+    assert call_split(so, a) == tad.TAD_OK
+    assert call_decode_ws(so, a) == tad.TAD_OK
+    assert lib.tad_last_error() == ""
+
+
+def test_chunk_span_limit(lib):
+    """Chunks whose K rows would span >= 4 GiB are refused (32-bit buffer offsets)."""
+    so = lib.load()
+    L = 1 << 20
+    a = good(B=1, Hq=1, Hkv=1, L=L)
+    a["k"] = desc([1, 1, L, 128], strides=[L * 4096, L * 4096, 4096, 1])   # 8 KiB rows
+    a["v"] = desc([1, 1, L, 128], strides=[L * 4096, L * 4096, 4096, 1])
+    assert call_split(so, a, n_splits=1) == tad.TAD_EUNSUPPORTED
+    assert call_split(so, a, n_splits=4, ws_bytes=0) == tad.TAD_EWORKSPACE   # passes the span check
+
+
+def test_auto_splits_without_device_reports_hip_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.load().tad_auto_splits(1, 32, 131072, -1) == tad.TAD_EHIP
+    assert lib.load().tad_auto_splits(0, 32, 131072, -1) == tad.TAD_EINVAL
+
+
+def test_product_does_not_reach_the_oracle():
+    """The binding and the HIP sources never import, include or load the oracle."""
+    pkg = os.path.join(ROOT, "long_context_attention_split_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,227 @@
+"""GPU parity: libtad (through its C ABI) against the fp64 oracle.
+
+Bars (the acceptance tolerances of the method): fp32 K/V -> max-abs error <= 1e-5;
+bf16 K/V (fp32 accumulation) -> max-abs error <= 2e-3 * max|V| over the valid keys.
+A stricter diagnostic also holds every case to a relative L2 error <= 1e-4, so that a
+subtly wrong kernel cannot hide under the loose bf16 bar (long-context outputs are
+averages of many rows and are small).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import tree
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REL_L2_DIAG = 1e-4
+
+
+def note(msg):
+    print("[case] " + msg, flush=True)
+
+
+def vmax_valid(v, seq_lens):
+    vv = v.float()
+    if seq_lens is None:
+        return float(vv.abs().max())
+    return max(float(vv[b, :, :max(0, int(L))].abs().max()) if int(L) > 0 else 0.0
+               for b, L in enumerate(seq_lens))
+
+
+def assert_parity(out, ref, kv_dtype, vmax, what=""):
+    out = np.asarray(out, dtype=np.float64)
+    err = np.abs(out - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    bar = 1e-5 if kv_dtype == torch.float32 else 2e-3 * vmax
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(out - ref)) / nref if nref > 0 else float(np.linalg.norm(out))
+    note("%s max_abs=%.3e bar=%.3e rel_l2=%.3e" % (what, max_abs, bar, rel))
+    assert np.isfinite(out).all(), what
+    assert max_abs <= bar, (what, max_abs, bar)
+    assert rel <= REL_L2_DIAG, (what, rel)
+
+
+def to_dev(c):
+    g = dict(c)
+    for key in ("q", "k", "v", "seq_lens", "slopes"):
+        if g.get(key) is not None:
+            g[key] = g[key].to(DEV)
+    return g
+
+
+def gpu_decode(lib, c, n_splits):
+    g = to_dev(c)
+    out = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], n_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def run_case(lib, seed, B, Hq, Hkv, L, d, kv=torch.bfloat16, q_dtype=torch.float32, seq_lens=None,
+             alibi=False, n_splits=0, k_scale=1.0):
+    note("seed=%d B=%d Hq=%d Hkv=%d L=%d d=%d kv=%s q=%s lens=%s alibi=%s S=%d" %
+         (seed, B, Hq, Hkv, L, d, kv, q_dtype, seq_lens, alibi, n_splits))
+    c = W.random_case(seed, B, Hq, Hkv, L, d, q_dtype=q_dtype, kv_dtype=kv, seq_lens=seq_lens,
+                      alibi=alibi, k_scale=k_scale)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"])
+    out = gpu_decode(lib, c, n_splits)
+    assert_parity(out, ref, kv, vmax_valid(c["v"], c["seq_lens"]), "seed=%d" % seed)
+    return out, ref, c
+
+
+# ----------------------------------------------------------------------------- small shapes
+
+def test_gist_shape_31_keys_8_chunks(lib):
+    """The gist's test: 31 keys, width 512, fp32, 8 chunks (seven of 4 keys, one of 3)."""
+    run_case(lib, 100, 1, 1, 1, 31, 512, kv=torch.float32, n_splits=8)
+
+
+@pytest.mark.parametrize("L,S", [(9, 8), (3, 8), (1, 4), (1, 1), (64, 64), (65, 64)])
+def test_empty_and_tiny_chunks(lib, L, S):
+    run_case(lib, 110 + L + S, 2, 4, 4, L, 128, n_splits=S)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("kv", [torch.float32, torch.bfloat16])
+def test_head_dims_and_dtypes(lib, d, kv):
+    """Several tiles per wave and a ragged last tile in every chunk (L=1000, S=3)."""
+    run_case(lib, 120 + d, 2, 2, 2, 1000, d, kv=kv, n_splits=3)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 8, 31, 64, 255, 1024])
+def test_split_count_sweep(lib, S):
+    run_case(lib, 130, 1, 4, 4, 4099, 128, n_splits=S)
+
+
+def test_ragged_lengths_with_poisoned_tail(lib):
+    """Keys past each length are NaN; lengths include 0, 1, an odd size and the maximum."""
+    lens = [0, 1, 777, 2048, 1500, 3]
+    out, ref, c = run_case(lib, 140, 6, 8, 8, 2048, 128, seq_lens=lens, n_splits=5)
+    assert (out[0] == 0).all()
+
+
+@pytest.mark.parametrize("g", [2, 4, 8])
+def test_grouped_query_heads(lib, g):
+    run_case(lib, 150 + g, 2, 4 * g, 4, 1500, 128, seq_lens=[1500, 913], n_splits=6)
+
+
+def test_alibi_bias(lib):
+    run_case(lib, 160, 2, 16, 16, 3000, 128, seq_lens=[3000, 1234], alibi=True, n_splits=4)
+
+
+def test_alibi_fp32_tight(lib):
+    run_case(lib, 161, 1, 8, 8, 1000, 64, kv=torch.float32, alibi=True, n_splits=3)
+
+
+def test_bf16_query(lib):
+    run_case(lib, 170, 2, 4, 4, 700, 128, q_dtype=torch.bfloat16, n_splits=3)
+
+
+def test_large_logits(lib):
+    """K scaled by 6: logits span tens of units; the online max must keep exp() in range."""
+    run_case(lib, 180, 1, 4, 4, 5000, 128, n_splits=7, k_scale=6.0)
+
+
+def test_strided_and_3d_layouts(lib):
+    """A [B, L, H, d] cache viewed as [B, H, L, d], and the 3-D [B, L, d] form."""
+    c = W.random_case(190, 2, 4, 4, 600, 128)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"])
+    kt = c["k"].transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    vt = c["v"].transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    out = lib.decode(c["q"].to(DEV), kt, vt, None, None, 5)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), ref, torch.bfloat16, vmax_valid(c["v"], None), "strided")
+    c1 = W.random_case(191, 3, 1, 1, 500, 64)
+    ref1 = oracle.decode_f64(c1["q"], c1["k"], c1["v"])
+    out1 = lib.decode(c1["q"].to(DEV), c1["k"][:, 0].to(DEV), c1["v"][:, 0].to(DEV), None, None, 2)
+    torch.cuda.synchronize()
+    assert_parity(out1.cpu().numpy(), ref1, torch.bfloat16, vmax_valid(c1["v"], None), "3d")
+
+
+def test_entry_points_agree(lib):
+    """tad_decode (stream-ordered allocation), tad_decode_ws and tad_split + tad_combine
+    give bit-identical outputs; repeated calls are bit-identical (fixed-order sums)."""
+    c = to_dev(W.random_case(200, 2, 8, 2, 3333, 128, seq_lens=[3333, 2000], alibi=True))
+    S = 6
+    a = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S)
+    out_b = torch.empty_like(a)
+    lib.tad_decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S, out_b)
+    ws = lib.workspace(c["q"], c["k"], S)
+    lib.tad_split(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S, ws)
+    out_c = torch.empty_like(a)
+    lib.tad_combine(ws, 2, 8, S, 128, out_c)
+    again = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S)
+    torch.cuda.synchronize()
+    assert torch.equal(a, out_b) and torch.equal(a, out_c) and torch.equal(a, again)
+
+
+# ----------------------------------------------------------------------------- partials
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_split_partials_match_chunk_statistics(lib, alibi):
+    """tad_split's (m, l, o) equal the per-chunk (local_max, den, num) of the tree
+    decoding steps, with m in base 2 (m * ln 2 = local_max)."""
+    B, H, L, d, S = 1, 3, 2000, 128, 7
+    c = W.random_case(210 + alibi, B, H, H, L, d, alibi=alibi)
+    g = to_dev(c)
+    m, l, o = lib.split_partials(g["q"], g["k"], g["v"], None, g["slopes"], S)
+    torch.cuda.synchronize()
+    m, l, o = m.cpu().double().numpy(), l.cpu().double().numpy(), o.cpu().double().numpy()
+    for h in range(H):
+        bias = None
+        if alibi:
+            bias = np.array([oracle.alibi_bias(L, j, float(c["slopes"][h])) for j in range(L)])
+        parts = tree.chunk_partials(oracle.widen(c["q"])[0, h], oracle.widen(c["k"])[0, h],
+                                    oracle.widen(c["v"])[0, h], S, bias)
+        for s, (lm, den, num) in enumerate(parts):
+            assert m[0, h, s] * math.log(2) == pytest.approx(lm, rel=1e-5, abs=1e-5)
+            # rescale the GPU's l, o to the oracle's exact local max before comparing
+            fix = math.exp(m[0, h, s] * math.log(2) - lm)
+            assert l[0, h, s] * fix == pytest.approx(den, rel=1e-4)
+            np.testing.assert_allclose(o[0, h, s] * fix, num, rtol=1e-4, atol=1e-4 * np.abs(num).max())
+
+
+def test_empty_chunk_partials(lib):
+    """Chunks past the sequence end are the merge identity: m = -inf, l = 0, o = 0."""
+    c = to_dev(W.random_case(220, 1, 2, 2, 9, 64))
+    m, l, o = lib.split_partials(c["q"], c["k"], c["v"], None, None, 8)
+    torch.cuda.synchronize()
+    # 9 keys over 8 chunks: length 2, chunks 5..7 empty
+    assert torch.isinf(m[:, :, 5:]).all() and (m[:, :, 5:] < 0).all()
+    assert (l[:, :, 5:] == 0).all() and (o[:, :, 5:] == 0).all()
+    assert torch.isfinite(m[:, :, :5]).all()
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def test_zero_query_is_mean(lib):
+    c = W.random_case(230, 1, 4, 4, 10000, 128)
+    c["q"].zero_()
+    out = gpu_decode(lib, c, 9)
+    mean = oracle.widen(c["v"]).mean(axis=2)
+    assert np.abs(out - mean).max() <= 2e-6
+
+
+def test_dominant_key_and_value_shift(lib):
+    """O(1)-magnitude pins at long context: a planted key returns its V row; V + c
+    shifts the output by c."""
+    B, H, L, d = 1, 4, 50000, 128
+    q = W.draw_q(240, B, H, d)
+    k = W.draw_kv(241, B, H, L, d, torch.bfloat16)
+    v = W.draw_kv(242, B, H, L, d, torch.bfloat16)
+    pos = W.plant_dominant_keys(243, q, k, 60.0)
+    out = gpu_decode(lib, dict(q=q, k=k, v=v, seq_lens=None, slopes=None), 0)
+    for h in range(H):
+        np.testing.assert_allclose(out[0, h], oracle.widen(v)[0, h, int(pos[0, h])], atol=1e-5)
+    c = W.random_case(244, 1, 4, 4, 50000, 128)
+    base = gpu_decode(lib, c, 0)
+    c["v"] = (c["v"].float() + 2.0).to(torch.bfloat16)
+    ref2 = oracle.decode_f64(c["q"], c["k"], c["v"])
+    shifted = gpu_decode(lib, c, 0)
+    assert_parity(shifted, ref2, torch.bfloat16, vmax_valid(c["v"], None), "v+2")
+    assert np.abs(shifted.mean() - base.mean() - 2.0) < 1e-2
