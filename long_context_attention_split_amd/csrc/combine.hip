@@ -32,6 +32,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     __shared__ float red[NW];
     __shared__ float part[NT];
 
+    constexpr int R = D <= NT ? NT / D : 1;   // thread rows per output element
+    constexpr int PRE = 16;                   // o loads issued up front per thread
+    float ov[PRE];
+    if constexpr (D <= NT) {
+        const int e = tid % D, rr = tid / D;
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+            const int s = rr + i * R;
+            ov[i] = (s < S) ? o[(int64_t)s * D + e] : 0.f;
+        }
+    }
+
     // global max (tree: per-thread strided max, wave butterfly, then the NW waves)
     float mx = kNegInf;
     for (int s = tid; s < S; s += NT) mx = fmaxf(mx, m[s]);
@@ -59,12 +71,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     for (int i = 0; i < NW; ++i) Lsum += red[i];
     const float inv = (Lsum > 0.f) ? 1.f / Lsum : 0.f;
 
-    // numerator: R thread rows share the splits of each output element
+    // numerator: R thread rows share the splits of each output element.  The first
+    // PRE value loads of every thread were issued before the max reduction above (they
+    // do not depend on it), so their latency overlaps it.
     if constexpr (D <= NT) {
-        constexpr int R = NT / D;
         const int e = tid % D, rr = tid / D;
         float acc = 0.f;
-        for (int s = rr; s < S; s += R) acc = fmaf(w[s], o[(int64_t)s * D + e], acc);
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+            const int s = rr + i * R;
+            if (s < S) acc = fmaf(w[s], ov[i], acc);
+        }
+#pragma unroll 8
+        for (int s = rr + PRE * R; s < S; s += R) acc = fmaf(w[s], o[(int64_t)s * D + e], acc);
         part[tid] = acc;
         __syncthreads();
         if (tid < D) {
@@ -78,6 +97,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
         const int b = row / a.Hq, h = row % a.Hq;
         for (int e = tid; e < D; e += NT) {
             float acc = 0.f;
+#pragma unroll 8
             for (int s = 0; s < S; ++s) acc = fmaf(w[s], o[(int64_t)s * D + e], acc);
             a.out[(int64_t)b * a.sob + (int64_t)h * a.soh + e] = acc * inv;
         }

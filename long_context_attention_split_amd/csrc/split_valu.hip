@@ -32,7 +32,10 @@
 
 namespace tad {
 
-template <int D, bool BF16>
+// POLICY: kPolicyNT when every K/V byte is read by one work-group only (one query
+// head per KV head); the default policy when the g work-groups of a query-head group
+// re-read the same chunk and should find it in L2.
+template <int D, bool BF16, int POLICY>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
     constexpr int EPL = 8;                       // elements per lane per key
     constexpr int G = D / EPL;                   // lanes per key row
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
 
     const uint32_t lane_off = (uint32_t)(sub * EPL * ELEM);
     for (int t0 = wave * T; t0 < n; t0 += NW * T) {
-        Row8<BF16> kk[U], vv[U];
+        Row8<BF16, POLICY> kk[U], vv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) kk[u].load(kr, (uint32_t)(t0 + u * KPW + grp) * krow + lane_off);
 #pragma unroll
@@ -202,7 +205,10 @@ static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
         grid = (units + 7) / 8 * 8 * a.group;
     }
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((split_valu_kernel<D, BF16>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+    if (a.group == 1)
+        hipLaunchKernelGGL((split_valu_kernel<D, BF16, kPolicyNT>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((split_valu_kernel<D, BF16, kPolicyDefault>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
     return hipGetLastError();
 }
 
