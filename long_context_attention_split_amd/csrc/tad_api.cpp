@@ -196,7 +196,10 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     a.S = S; a.group = (int32_t)(P.Hq / P.Hkv);
     a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
     a.ws_m = w.m; a.ws_l = w.l; a.ws_o = w.o;
-    hipError_t e = tad::launch_split_valu(a, (int)P.d, P.kv_dtype == TAD_BF16, stream);
+    const bool bf16 = P.kv_dtype == TAD_BF16;
+    hipError_t e = tad::split_mfma_supported((int)P.d, bf16, a.group)
+                       ? tad::launch_split_mfma(a, (int)P.d, stream)
+                       : tad::launch_split_valu(a, (int)P.d, bf16, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "split kernel launch: %s", hipGetErrorString(e));
     return TAD_OK;
 }

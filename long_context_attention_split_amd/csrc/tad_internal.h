@@ -48,6 +48,8 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
 
 // Launchers (defined next to their kernels).  Return the hipError_t of the launch.
 hipError_t launch_split_valu(const SplitArgs &a, int d, bool kv_bf16, hipStream_t s);
+bool split_mfma_supported(int d, bool kv_bf16, int group);
+hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
 
 // Keys per work-group tile of the VALU split kernel (for tests of the host logic).
