@@ -34,9 +34,13 @@
  *    to [0, Lmax] on the device; keys at or beyond L_b are never read.  A row with
  *    L_b = 0 produces out = 0.
  *  - alibi_slopes: DEVICE fp32 [Hq] or NULL (no bias).
- *  - n_splits: chunks per (b, head); <= 0 selects tad_auto_splits().  Chunking
- *    follows torch.chunk: chunk length ceil(L_b / n_splits), the last one shorter,
- *    trailing chunks possibly empty (an empty chunk contributes nothing).
+ *  - n_splits: chunks per (b, head); <= 0 selects tad_auto_splits().  Every row is
+ *    cut into contiguous chunks of one length c = ceil(Lref / n_splits), where Lref
+ *    is the longest (clamped) sequence length in the batch (Lmax without seq_lens):
+ *    torch.chunk(n_splits) when all rows have the same length.  The last chunk of a
+ *    row may be shorter; shorter rows end with empty chunks, which contribute
+ *    nothing.  (The result does not depend on the chunking; with one chunk length
+ *    every non-empty work-group of a ragged batch has the same amount of work.)
  *  - stream: HIP stream (0 = default stream).  All tensors are owned by the caller
  *    and must stay valid until the stream work completes.  The library never frees
  *    caller memory and keeps no state besides a per-device compute-unit count.
@@ -85,10 +89,10 @@ int tad_version(void);
 const char *tad_last_error(void);
 
 /*
- * Chunks per (b, head) chosen when n_splits <= 0: enough work-groups to give every
- * compute unit of `device` (-1: the current device) four, i.e.
- * ceil(4 * CUs / (B * Hkv)), but no chunk shorter than 256 keys and at least one.
- * Returns the count (>= 1) or a negative TAD_E* code.
+ * Chunks per (b, head) chosen when n_splits <= 0, for a batch of B rows with Hkv KV
+ * heads and Lmax keys on `device` (-1: the current device): ceil(4 * CUs / (B * Hkv)),
+ * i.e. four work-groups per compute unit, all resident at once, but no chunk shorter
+ * than 256 keys and at least one.  Returns the count (>= 1) or a negative TAD_E* code.
  */
 int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device);
 

@@ -186,6 +186,7 @@ def shape_of(q, k):
 
 
 def resolve_splits(q, k, n_splits: int = 0) -> int:
+    """n_splits if positive, else the library's automatic choice."""
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
     return n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, q.device.index or 0)
 

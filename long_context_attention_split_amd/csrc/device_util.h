@@ -89,6 +89,12 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -4,35 +4,38 @@
 // dense product S^T[key][head] = K_tile . Q^T, and so does the value update
 // O^T[e][head] += V_tile^T . P^T.  One work-group (4 waves) owns one (b, kv head,
 // chunk) and all g query heads of the group, so every K and V byte of the chunk is
-// read from HBM once (with the non-temporal policy) however many heads share it.
-// The per-head partials (m, l, o) it writes are the same as the vector-ALU kernel's
-// (see split_valu.hip): chunk maximum in base 2, sum of 2^(s - m), and the
-// 2^(s - m)-weighted sum of value rows, i.e. the per-chunk local max, denominator
-// and numerator of tree_attn_decode ("Tree Attention Decoding").
+// read from HBM once however many heads share it.  The per-head partials (m, l, o)
+// it writes are the same as the vector-ALU kernel's (see split_valu.hip): chunk
+// maximum in base 2, sum of 2^(s - m), and the 2^(s - m)-weighted sum of value
+// rows, i.e. the per-chunk local max, denominator and numerator of tree_attn_decode
+// ("Tree Attention Decoding").
 //
-// MFMA used: v_mfma_f32_16x16x32_bf16.  Lane l holds A[i][k] for i = l%16 and
-// B[k][j] for j = l%16, with k in the 8-wide block l/16, and C[i][j] for
-// j = l%16, i = 4*(l/16) + r, r = 0..3.  The reduction index only has to be laid out
-// the same way in A and B, which the code below does by construction.
+// Data path: each wave streams 16-key tiles of K and V straight from HBM into its
+// own LDS buffers with buffer_load_dwordx4 ... lds (non-temporal).  Every load
+// instruction covers whole consecutive rows -- the pattern that streams at full HBM
+// rate -- and the 16 lanes of a row fetch its 16-byte chunks in an XOR-swizzled
+// order, so that the matrix-core operand reads from LDS (16 rows, one chunk each)
+// hit 16 distinct bank groups.
 //
-//  * scores: A = 16 keys x 32 dims of K (lane: key l%16, dims 32kk + 8(l/16) .. +7,
-//    one 16-byte load), B = Q^T with heads on the 16 columns (zero past g).  fp32 q
-//    is split into bf16 hi + lo and both are multiplied (two MFMAs), which keeps the
-//    scores at ~16 significant bits of q; K is exactly bf16.  Result: lane l holds
-//    the scores of keys 4(l/16)+r of the subtile for head l%16.
-//  * transpose: multiplying the same K-style A operand of V by a 0/1 selector
-//    B[k][j] = (k == j + 16h) gives C[key][j] = V[key][32kk + 16h + j]: lane l then
-//    holds 4 keys of one value column -- the transposed layout the value product
-//    needs.  The values are exact bf16 and the product is exact.
-//  * value update: A = V^T (16 value columns x 32 keys: the 4 keys of each of two
-//    subtiles), B = P^T (32 keys x heads), with the probabilities split into bf16
-//    hi + lo (two MFMAs, ~16-bit weights).  The key order inside the 32-wide
-//    reduction is the same permutation on both sides, so it needs no shuffle.
+// Matrix instructions: v_mfma_f32_16x16x32_bf16 (lane l: A[i][k] with i = l%16,
+// B[k][j] with j = l%16, k in the 8-wide block l/16; C[i][j] with j = l%16,
+// i = 4(l/16) + r) and v_mfma_f32_16x16x16_bf16 (same, 4-wide k blocks).  The
+// reduction index only has to be laid out the same way in A and B.
+//  * scores: A = 16 keys x 32 dims of K from LDS, B = Q^T with heads on the 16
+//    columns (zero past g).  fp32 q is split into bf16 hi + lo and both are
+//    multiplied (two MFMAs), keeping ~16 significant bits of q; K is exactly bf16.
+//    Lane l gets the scores of keys 4(l/16)+r for head l%16.
+//  * transpose: the same A operand of V times a 0/1 selector B[k][j] = (k == j+16h)
+//    gives C[key][j] = V[key][32kk + 16h + j], i.e. lane l holds keys 4(l/16)+r of
+//    one value column: the operand layout of the value product.  Exact.
+//  * value update (16x16x16): A = V^T (16 value columns x the tile's 16 keys),
+//    B = P^T (16 keys x heads), the probabilities split into bf16 hi + lo.
 //
-// Softmax per head: lane l owns head l%16 and 8 of the tile's 32 keys; the four
-// lanes l, l^16, l^32, l^48 together hold the tile and exchange their max and sum.
-// The running (m, l) and the rescale of O by 2^(m_old - m_new) follow the online
-// softmax of the "Flash Aandacht" page's block loop, kept un-normalised.
+// Softmax per head: lane l owns head l%16 and 4 of the tile's 16 keys; the lanes
+// l, l^16, l^32, l^48 exchange their max and sum.  The running (m, l) and the
+// rescale of O by 2^(m_old - m_new) follow the online softmax of the "Flash
+// Aandacht" page's block loop, kept un-normalised; the rescale is skipped when no
+// head's maximum moved (the factor is then exactly 1).
 
 #include "device_util.h"
 #include "tad_internal.h"
@@ -49,7 +52,8 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
 
 // Two fp32 values that are exact bf16 numbers -> one packed dword (x in the low half).
 __device__ __forceinline__ uint32_t pack_exact_bf16(float x, float y) {
-    return (__float_as_uint(x) >> 16) | (__float_as_uint(y) & 0xffff0000u);
+    // v_perm_b32: bytes {x.2, x.3, y.2, y.3} = (x >> 16) | (y & 0xffff0000)
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
 }
 
 // x = hi + lo with hi, lo bf16 (truncations): |x - hi - lo| <= 2^-16 |x|.
@@ -60,18 +64,43 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) 
     lo = __float_as_uint(r) >> 16;
 }
 
-template <int D>
-__global__ __launch_bounds__(kSplitThreads) void split_mfma_kernel(SplitArgs a) {
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// WAVES: occupancy target (waves per SIMD) the register allocator must meet.
+// NBUF: LDS tile buffers per wave; with 2, the next tile's loads are in flight while
+// the current one is consumed.
+template <int D, int WAVES = 4, int NBUF = 1>
+__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
+void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int NKK = D / 32;          // 32-wide slices of d (score reduction)
     constexpr int NB = D / 16;           // 16-wide column blocks of the output
-    constexpr int TK = 32;               // keys per wave tile (two 16-key subtiles)
+    constexpr int TK = 16;               // keys per wave tile
+    constexpr int CH = D / 8;            // 16-byte chunks per bf16 row
+    constexpr int RPI = 64 / CH;         // rows per load instruction
+    constexpr int NLD = TK / RPI;        // load instructions per tile and tensor
+    constexpr int TILE = TK * CH;        // 16-byte LDS slots per tile
     constexpr int NW = kSplitThreads / 64;
     constexpr int MAXG = 16;
+    static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
+
+    // Per wave: a (K tile, V tile) pair in smem, and a second pair in smem2 when
+    // double-buffering (separate arrays, so the compiler can tell a read of one
+    // buffer from a load still landing in the other).  smem is reused for the merge.
+    __shared__ uint4 smem[NW * 2 * TILE];
+    __shared__ uint4 smem2[NBUF == 2 ? NW * 2 * TILE : 1];
+    __shared__ float lds_ml[2][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int c4 = lane >> 4;            // 8-wide reduction block of this lane
+    const int c4 = lane >> 4;            // 8-wide (4-wide) reduction block of this lane
     const int j16 = lane & 15;           // column (head) / row (key, value column)
 
     const int S = a.S, g = a.group;
@@ -81,11 +110,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_mfma_kernel(SplitArgs a) 
     const bool head_ok = j16 < g;
     const int h = kvh * g + (head_ok ? j16 : 0);
 
-    int L = a.Lmax;
-    if (a.seq_lens) L = min(max(a.seq_lens[b], 0), a.Lmax);
-    const int c = (L + S - 1) / S;
-    const int j0 = (int)min((int64_t)s * c, (int64_t)L);
-    const int j1 = min(j0 + c, L);
+    const ChunkRange cr = chunk_range(a, b, s);
+    const int L = cr.L, j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
 
     const uint32_t krow = (uint32_t)(a.skj * 2), vrow = (uint32_t)(a.svj * 2);
@@ -135,100 +161,134 @@ __global__ __launch_bounds__(kSplitThreads) void split_mfma_kernel(SplitArgs a) 
     const float slope2 = (a.slopes && head_ok) ? a.slopes[h] * 1.4426950408889634f : 0.f;
     const bool alibi = a.slopes != nullptr;
 
+    // LDS slot (row r, position p) holds chunk p ^ swz(r) of row r; with CH = 16 the
+    // 16 rows of an operand read land in 16 distinct 16-byte bank groups, and with
+    // CH = 8 the row parity plus swz(r) = r/2 does the same.
+    auto swz = [](int r) { return (r / (16 / CH)) % CH; };
+    uint4 *const bufA = smem + wave * 2 * TILE;
+    uint4 *const bufB = smem2 + (NBUF == 2 ? wave * 2 * TILE : 0);
+    const int ld_r = lane / CH, ld_p = lane % CH;
+    // HBM -> LDS, whole rows per instruction; rows past the chunk end read as zero.
+    auto issue_tile = [&](uint4 *tk, int t0) {
+        uint4 *tv = tk + TILE;
+#pragma unroll
+        for (int u = 0; u < NLD; ++u) {
+            const int r = u * RPI + ld_r;
+            const uint32_t col = 16u * (uint32_t)(ld_p ^ swz(r));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(tk + u * 64), 16,
+                                                     (uint32_t)(t0 + r) * krow + col, 0, 0, kPolicyNT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(tv + u * 64), 16,
+                                                     (uint32_t)(t0 + r) * vrow + col, 0, 0, kPolicyNT);
+        }
+    };
+
     float m = kNegInf, l = 0.f;
     f32x4_t O[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    for (int t0 = wave * TK; t0 < n; t0 += NW * TK) {
-        uint4 kraw[2][NKK], vraw[2][NKK];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                kraw[sub][kk] = load16<kPolicyNT>(kr, (uint32_t)(t0 + 16 * sub + j16) * krow + 64u * kk + 16u * c4);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                vraw[sub][kk] = load16<kPolicyNT>(vr, (uint32_t)(t0 + 16 * sub + j16) * vrow + 64u * kk + 16u * c4);
+    auto consume = [&](const uint4 *tk, int t0) {
+        const uint4 *tv = tk + TILE;
 
-        // scores: sc[sub][r] is key t0 + 16 sub + 4 c4 + r, head j16
-        f32x4_t sc[2];
+        // scores: sc[r] is key t0 + 4 c4 + r, head j16
+        f32x4_t sc = zero4;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            f32x4_t acc = zero4;
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                acc = mfma16x16x32(kraw[sub][kk], qhi[kk], acc);
-                acc = mfma16x16x32(kraw[sub][kk], qlo[kk], acc);
-            }
-            sc[sub] = acc;
+        for (int kk = 0; kk < NKK; ++kk) {
+            const uint4 ka = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
+            sc = mfma16x16x32(ka, qhi[kk], sc);
+            sc = mfma16x16x32(ka, qlo[kk], sc);
         }
-        float p[8];
+        float p[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int key = t0 + 16 * (t >> 2) + 4 * c4 + (t & 3);
-            float x = sc[t >> 2][t & 3];
+        for (int r = 0; r < 4; ++r) {
+            const int key = t0 + 4 * c4 + r;
+            float x = sc[r];
             if (alibi) x = fmaf(slope2, (float)(j0 + key - (L - 1)), x);
-            p[t] = (key < n) ? x : kNegInf;
+            p[r] = (key < n) ? x : kNegInf;
         }
-        float mt = p[0];
-#pragma unroll
-        for (int t = 1; t < 8; ++t) mt = fmaxf(mt, p[t]);
+        float mt = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m, mt);
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = exp2_fast(m - m_use);
         float ps = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            p[t] = exp2_fast(p[t] - m_use);
-            ps += p[t];
+        for (int r = 0; r < 4; ++r) {
+            p[r] = exp2_fast(p[r] - m_use);
+            ps += p[r];
         }
         ps += __shfl_xor(ps, 16, 64);
         ps += __shfl_xor(ps, 32, 64);
-        l = fmaf(l, alpha, ps);
+        if (__any(m_new != m)) {               // some head's running max moved
+            const float alpha = exp2_fast(m - m_use);
+            l *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
+        }
+        l += ps;
         m = m_new;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
 
-        // P^T operands: reduction slot t of this lane is key t0 + 16 (t>>2) + 4 c4 + (t&3)
-        uint32_t ph[8], pl[8];
+        // P^T operands: reduction slot t of this lane is key t0 + 4 c4 + t
+        uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) split_bf16(p[t], ph[t], pl[t]);
-        const uint4 phi = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16, ph[4] | ph[5] << 16, ph[6] | ph[7] << 16);
-        const uint4 plo = make_uint4(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16, pl[4] | pl[5] << 16, pl[6] | pl[7] << 16);
+        for (int r = 0; r < 4; ++r) split_bf16(p[r], ph[r], pl[r]);
+        const uint2 phi = make_uint2(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16);
+        const uint2 plo = make_uint2(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16);
 
-        // V^T blocks (same key slots), then the value update
+        // V^T blocks by the selector product, then the value update
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
+            const uint4 va = tv[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const f32x4_t v0 = mfma16x16x32(vraw[0][kk], sel[half], zero4);
-                const f32x4_t v1 = mfma16x16x32(vraw[1][kk], sel[half], zero4);
-                const uint4 vt = make_uint4(pack_exact_bf16(v0[0], v0[1]), pack_exact_bf16(v0[2], v0[3]),
-                                            pack_exact_bf16(v1[0], v1[1]), pack_exact_bf16(v1[2], v1[3]));
+                const f32x4_t vt = mfma16x16x32(va, sel[half], zero4);
+                const uint2 vop = make_uint2(pack_exact_bf16(vt[0], vt[1]), pack_exact_bf16(vt[2], vt[3]));
                 const int nb = 2 * kk + half;
-                O[nb] = mfma16x16x32(vt, phi, O[nb]);
-                O[nb] = mfma16x16x32(vt, plo, O[nb]);
+                O[nb] = mfma16x16x16(vop, phi, O[nb]);
+                O[nb] = mfma16x16x16(vop, plo, O[nb]);
             }
+        }
+    };
+
+    constexpr int STRIDE = NW * TK;
+    constexpr int VM_ALL = 0x0F70;                 // s_waitcnt vmcnt(0)
+    constexpr int VM_NEXT = 0x0F70 | (2 * NLD);    // vmcnt(2*NLD): all but the next tile's loads
+    if constexpr (NBUF == 1) {
+        for (int t0 = wave * TK; t0 < n; t0 += STRIDE) {
+            issue_tile(bufA, t0);
+            __builtin_amdgcn_s_waitcnt(VM_ALL);
+            consume(bufA, t0);
+        }
+    } else {
+        // Two buffers, alternating; a buffer is refilled only after the tile read from
+        // it has been consumed (its LDS reads fed that tile's matrix products).
+        int t0 = wave * TK;
+        if (t0 < n) issue_tile(bufA, t0);
+        while (t0 < n) {
+            if (t0 + STRIDE < n) { issue_tile(bufB, t0 + STRIDE); __builtin_amdgcn_s_waitcnt(VM_NEXT); }
+            else __builtin_amdgcn_s_waitcnt(VM_ALL);
+            consume(bufA, t0);
+            t0 += STRIDE;
+            if (t0 >= n) break;
+            if (t0 + STRIDE < n) { issue_tile(bufA, t0 + STRIDE); __builtin_amdgcn_s_waitcnt(VM_NEXT); }
+            else __builtin_amdgcn_s_waitcnt(VM_ALL);
+            consume(bufB, t0);
+            t0 += STRIDE;
         }
     }
 
-    // ---- merge the NW wave states per head through LDS, then write the partials.
-    __shared__ float lds_o[NW][MAXG][D];
-    __shared__ float lds_m[NW][MAXG], lds_l[NW][MAXG];
+    // ---- merge the NW wave states per head through LDS (reusing the tile buffers).
+    __syncthreads();
+    float(*lds_o)[MAXG][D] = reinterpret_cast<float(*)[MAXG][D]>(smem);
     if (head_ok) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) lds_o[wave][j16][16 * nb + 4 * c4 + r] = O[nb][r];
         if (c4 == 0) {
-            lds_m[wave][j16] = m;
-            lds_l[wave][j16] = l;
+            lds_ml[0][wave][j16] = m;
+            lds_ml[1][wave][j16] = l;
         }
     }
     __syncthreads();
@@ -236,14 +296,14 @@ __global__ __launch_bounds__(kSplitThreads) void split_mfma_kernel(SplitArgs a) 
         const int hh = idx / D, e = idx % D;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_m[w][hh]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[0][w][hh]);
         const float Mu = (M == kNegInf) ? 0.f : M;
         float acc = 0.f, lsum = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float sw = exp2_fast(lds_m[w][hh] - Mu);
+            const float sw = exp2_fast(lds_ml[0][w][hh] - Mu);
             acc = fmaf(sw, lds_o[w][hh][e], acc);
-            lsum = fmaf(sw, lds_l[w][hh], lsum);
+            lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
         }
         const int64_t r = ((int64_t)b * a.Hq + kvh * g + hh) * S + s;
         a.ws_o[r * D + e] = acc;

@@ -1,7 +1,8 @@
 // split_valu.hip -- split step of split-KV decoding on the vector ALUs (gfx950).
 //
 // One work-group (4 waves) owns one (batch row b, query head h, chunk s).  The chunk
-// is the s-th torch.chunk piece of the row's L_b keys.  It produces the chunk's
+// is the s-th of the row's L_b keys cut into pieces of one batch-wide length (see
+// chunk_range in tad_internal.h; torch.chunk(S) for a single length).  It produces the chunk's
 // partial (m, l, o): the local maximum of the scores, the sum of exponentials
 // relative to it, and the exponential-weighted sum of value rows -- the
 // (local_max, den, num) triple of tree_attn_decode in "Tree Attention Decoding",
@@ -35,13 +36,16 @@ namespace tad {
 // POLICY: kPolicyNT when every K/V byte is read by one work-group only (one query
 // head per KV head); the default policy when the g work-groups of a query-head group
 // re-read the same chunk and should find it in L2.
-template <int D, bool BF16, int POLICY>
+// UK: keys per lane group per tile (K and V tiles of UK*16 bytes per lane for bf16).
+// PF: software pipelining -- the next tile's loads are issued before the current
+// tile is consumed (two register tiles, alternating).
+template <int D, bool BF16, int POLICY, int UK = 16 / (BF16 ? 2 : 4), bool PF = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
     constexpr int EPL = 8;                       // elements per lane per key
     constexpr int G = D / EPL;                   // lanes per key row
     constexpr int KPW = 64 / G;                  // keys per wave load instruction
     constexpr int ELEM = BF16 ? 2 : 4;
-    constexpr int U = 16 / ELEM;                 // keys per lane group per tile
+    constexpr int U = UK;                        // keys per lane group per tile
     constexpr int T = KPW * U;                   // keys per wave tile
     constexpr int NW = kSplitThreads / 64;       // waves per work-group
     constexpr int SLOTS = NW * KPW;              // lane-group states to merge
@@ -76,11 +80,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     }
     const int kvh = h / a.group;
 
-    int L = a.Lmax;
-    if (a.seq_lens) L = min(max(a.seq_lens[b], 0), a.Lmax);
-    const int c = (L + S - 1) / S;                       // torch.chunk length
-    const int j0 = (int)min((int64_t)s * c, (int64_t)L);
-    const int j1 = min(j0 + c, L);
+    const ChunkRange cr = chunk_range(a, b, s);
+    const int L = cr.L, j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
 
     // ---- per-chunk buffer resources: [chunk start, chunk end) of this head's K and V.
@@ -120,13 +121,15 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
     const uint32_t lane_off = (uint32_t)(sub * EPL * ELEM);
-    for (int t0 = wave * T; t0 < n; t0 += NW * T) {
-        Row8<BF16, POLICY> kk[U], vv[U];
+    using Tile = Row8<BF16, POLICY>[U];
+    auto load_tile = [&](Tile &kk, Tile &vv, int t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) kk[u].load(kr, (uint32_t)(t0 + u * KPW + grp) * krow + lane_off);
 #pragma unroll
         for (int u = 0; u < U; ++u) vv[u].load(vr, (uint32_t)(t0 + u * KPW + grp) * vrow + lane_off);
-
+    };
+    // One tile: scores, online max/sum update, value accumulation.
+    auto consume = [&](const Tile &kk, const Tile &vv, int t0) {
         float sc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -162,6 +165,28 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
             for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vv[u][e], o[e]);
         }
         m = m_new;
+    };
+
+    constexpr int STRIDE = NW * T;
+    if constexpr (!PF) {
+        for (int t0 = wave * T; t0 < n; t0 += STRIDE) {
+            Tile kk, vv;
+            load_tile(kk, vv, t0);
+            consume(kk, vv, t0);
+        }
+    } else {
+        Tile ka, va, kb, vb;
+        int t0 = wave * T;
+        if (t0 < n) load_tile(ka, va, t0);
+        while (t0 < n) {
+            if (t0 + STRIDE < n) load_tile(kb, vb, t0 + STRIDE);
+            consume(ka, va, t0);
+            t0 += STRIDE;
+            if (t0 >= n) break;
+            if (t0 + STRIDE < n) load_tile(ka, va, t0 + STRIDE);
+            consume(kb, vb, t0);
+            t0 += STRIDE;
+        }
     }
 
     // ---- merge the SLOTS lane-group states of this work-group (fixed order).

@@ -29,6 +29,34 @@ struct CombineArgs {
     int32_t B, Hq, S;
 };
 
+// Keys [j0, j1) of batch row b that chunk s covers, and the row's length L.
+// Every row of the batch is cut with one chunk length, c = ceil(Lref / S), where
+// Lref is the longest (clamped) length in the batch -- Lmax when no lengths are
+// given, which makes the chunks those of torch.chunk(S).  Rows shorter than Lref
+// end with empty chunks, and every non-empty work-group has the same amount of work.
+// Must be called by whole waves (it reduces the lengths across the wave).
+struct ChunkRange {
+    int L, j0, j1;
+};
+
+__device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int s) {
+    int L = a.Lmax, Lref = a.Lmax;
+    if (a.seq_lens) {
+        L = min(max(a.seq_lens[b], 0), a.Lmax);
+        int mx = 0;
+        for (int i = (int)(threadIdx.x & 63); i < a.B; i += 64) mx = max(mx, min(max(a.seq_lens[i], 0), a.Lmax));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+        Lref = mx;
+    }
+    const int c = (Lref + a.S - 1) / a.S;
+    ChunkRange r;
+    r.L = L;
+    r.j0 = (int)min((int64_t)s * c, (int64_t)L);
+    r.j1 = min(r.j0 + c, L);
+    return r;
+}
+
 // Workspace carving (same arithmetic as tad_workspace_bytes).
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

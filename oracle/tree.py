@@ -36,11 +36,15 @@ import numpy as np
 Partial = Tuple[float, float, np.ndarray]   # (local_max, den, num)
 
 
-def chunk_bounds(L: int, n_chunks: int) -> List[Tuple[int, int]]:
-    """[lo, hi) of each of n_chunks chunks, torch.chunk style; empty ones are (lo, lo)."""
+def chunk_bounds(L: int, n_chunks: int, chunk_len: Optional[int] = None) -> List[Tuple[int, int]]:
+    """[lo, hi) of each of n_chunks chunks; empty ones are (lo, lo).
+
+    By default torch.chunk style (length ceil(L / n_chunks)).  ``chunk_len`` fixes the
+    length instead -- the reading used when the rows of a batch with different lengths
+    share one chunk length (a row then ends with empty chunks)."""
     if L <= 0:
         return [(0, 0)] * n_chunks
-    c = -(-L // n_chunks)
+    c = chunk_len if chunk_len is not None else -(-L // n_chunks)
     out = []
     for r in range(n_chunks):
         lo = min(r * c, L)
@@ -50,10 +54,11 @@ def chunk_bounds(L: int, n_chunks: int) -> List[Tuple[int, int]]:
 
 
 def chunk_partials(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_chunks: int,
-                   bias: Optional[np.ndarray] = None) -> List[Partial]:
+                   bias: Optional[np.ndarray] = None, chunk_len: Optional[int] = None) -> List[Partial]:
     """Per-chunk (local_max, den, num) for one query row.
 
-    q [d], k [L, d], v [L, d] (any float dtype; computed in fp64), bias [L] or None.
+    q [d], k [L, d], v [L, d] (any float dtype; computed in fp64), bias [L] or None;
+    chunk_len as in ``chunk_bounds``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -62,7 +67,7 @@ def chunk_partials(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_chunks: int,
     scale = d ** -0.5
     q = q * scale
     parts: List[Partial] = []
-    for lo, hi in chunk_bounds(k.shape[0], n_chunks):
+    for lo, hi in chunk_bounds(k.shape[0], n_chunks, chunk_len):
         if hi <= lo:
             parts.append((-math.inf, 0.0, np.zeros(v.shape[-1])))
             continue
@@ -121,6 +126,6 @@ def merge_tree(parts: Sequence[Partial], arity_order: Optional[Sequence[int]] = 
     return o / l
 
 
-def tree_decode_row(q, k, v, n_chunks: int, bias=None) -> np.ndarray:
+def tree_decode_row(q, k, v, n_chunks: int, bias=None, chunk_len: Optional[int] = None) -> np.ndarray:
     """The whole tree decode for one query row (steps 1-5)."""
-    return merge_all(chunk_partials(q, k, v, n_chunks, bias))
+    return merge_all(chunk_partials(q, k, v, n_chunks, bias, chunk_len))

@@ -273,6 +273,19 @@ def test_tree_decode_matches_definition(n_chunks, alibi):
         np.testing.assert_allclose(got, out[0, h], rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("chunk_len", [1, 5, 13, 40, 100])
+def test_fixed_chunk_length_matches_definition(chunk_len):
+    """A batch-wide chunk length (rows ending in empty chunks) gives the same result."""
+    L, d = 77, 32
+    c = rand_case(18, L=L, d=d, alibi=True)
+    out = oracle.decode_f64(c["q"], c["k"], c["v"], slopes=c["slopes"])
+    bias = np.array([oracle.alibi_bias(L, j, float(c["slopes"][0])) for j in range(L)])
+    n = max(1, -(-100 // chunk_len))
+    got = tree.tree_decode_row(f64(c["q"])[0, 0], f64(c["k"])[0, 0], f64(c["v"])[0, 0], n, bias, chunk_len)
+    np.testing.assert_allclose(got, out[0, 0], rtol=1e-12, atol=1e-14)
+    assert tree.chunk_bounds(L, 3, 40) == [(0, 40), (40, 77), (77, 77)]
+
+
 def test_gist_chunk_sizes():
     """torch.chunk semantics: 31 keys over 8 -> seven chunks of 4 and one of 3;
     9 keys over 8 -> chunk length 2, five non-empty chunks and three empty ones."""

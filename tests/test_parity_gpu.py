@@ -186,6 +186,31 @@ def test_split_partials_match_chunk_statistics(lib, alibi):
             np.testing.assert_allclose(o[0, h, s] * fix, num, rtol=1e-4, atol=1e-4 * np.abs(num).max())
 
 
+def test_split_partials_ragged_batch(lib):
+    """With per-row lengths every row is cut with the batch-wide chunk length
+    ceil(max L / S); shorter rows end in empty chunks."""
+    lens = [2000, 700, 1333]
+    B, H, L, d, S = 3, 2, 2000, 64, 7
+    c = W.random_case(215, B, H, H, L, d, seq_lens=lens)
+    g = to_dev(c)
+    m, l, o = lib.split_partials(g["q"], g["k"], g["v"], g["seq_lens"], None, S)
+    torch.cuda.synchronize()
+    m, l, o = m.cpu().double().numpy(), l.cpu().double().numpy(), o.cpu().double().numpy()
+    clen = -(-max(lens) // S)
+    for b, Lb in enumerate(lens):
+        for h in range(H):
+            parts = tree.chunk_partials(oracle.widen(c["q"])[b, h], oracle.widen(c["k"])[b, h, :Lb],
+                                        oracle.widen(c["v"])[b, h, :Lb], S, None, clen)
+            for s, (lm, den, num) in enumerate(parts):
+                if den == 0.0:
+                    assert m[b, h, s] == -np.inf and l[b, h, s] == 0 and (o[b, h, s] == 0).all()
+                    continue
+                assert m[b, h, s] * math.log(2) == pytest.approx(lm, rel=1e-5, abs=1e-5)
+                fix = math.exp(m[b, h, s] * math.log(2) - lm)
+                assert l[b, h, s] * fix == pytest.approx(den, rel=1e-4)
+                np.testing.assert_allclose(o[b, h, s] * fix, num, rtol=1e-4, atol=1e-4 * np.abs(num).max())
+
+
 def test_empty_chunk_partials(lib):
     """Chunks past the sequence end are the merge identity: m = -inf, l = 0, o = 0."""
     c = to_dev(W.random_case(220, 1, 2, 2, 9, 64))
