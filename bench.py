@@ -48,9 +48,11 @@ def kernel_source_hash() -> str:
 def read_traffic(workload: int):
     """HBM bytes per split-kernel launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "split_kernel_workload%d_traffic.txt" % workload)
-    if not os.path.exists(p):
+    names = ["split_kernel_workload%d_traffic.txt" % workload, "split_mfma_workload%d_traffic.txt" % workload]
+    paths = [os.path.join(ROOT, "profiles", n) for n in names if os.path.exists(os.path.join(ROOT, "profiles", n))]
+    if not paths:
         return None
+    p = paths[0]
     vals = {}
     for ln in open(p):
         if "=" in ln and not ln.lstrip().startswith("#"):
