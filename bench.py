@@ -3,8 +3,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S]
 
-One step = one full decode (split kernel + combine kernel) over the workload's
-inputs, already resident in HBM.  W untimed steps, then K timed steps between two
+One step = one full decode over the workload's inputs, already resident in HBM:
+the split kernel then the combine kernel (tad_split + tad_combine, which is what
+tad_decode_ws runs at this size).  W untimed steps, then K timed steps between two
 device synchronisations.  Rank 0 prints one JSON line with:
 
 - value: KV-read throughput in GB/s (algorithmic K+V bytes / step time),
@@ -152,8 +153,8 @@ def main(argv=None) -> int:
     kv_bytes = w.kv_bytes(c["seq_lens"])
     stream = torch.cuda.current_stream()
 
-    # Events bracket only the split launch (the dominant kernel): every event record
-    # costs a few microseconds of queue time, and the step time includes it.
+    # One step = tad_split then tad_combine (what tad_decode_ws runs at this size);
+    # events bracket the split launch, the dominant kernel.
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -175,11 +176,11 @@ def main(argv=None) -> int:
     split_ms = [e[0].elapsed_time(e[1]) for e in evs]
     ms_per_step = wall * 1e3 / args.steps
     split_avg = sum(split_ms) / len(split_ms)
-    # the combine's share of the step: everything outside the split brackets
+    # outside the split brackets: the combine kernel and launch gaps
     comb_avg = ms_per_step - split_avg
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     split_gbs = kv_bytes / (split_avg * 1e-3) / 1e9
-    print("[bench] step %.1f us (split %.1f us, rest %.1f us), %.0f GB/s" %
+    print("[bench] step %.1f us (split kernel %.1f us, combine + gaps %.1f us), %.0f GB/s" %
           (ms_per_step * 1e3, split_avg * 1e3, comb_avg * 1e3, gbs), file=sys.stderr, flush=True)
 
     traffic = read_traffic(args.workload)

@@ -99,16 +99,23 @@ int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device);
 /*
  * Bytes of device workspace tad_decode_ws / tad_split / tad_combine need for
  * B * Hq rows, n_splits chunks and head dimension d (0 if an argument is < 1).
- * Layout (all fp32, each array starting at a 256-byte boundary), with
- * r = (b * Hq + h) * n_splits + s:
- *     m[r]        chunk maximum of the scores, in base-2 units (score * log2 e);
+ * Layout (each array starting at a 256-byte boundary), with r = (b * Hq + h) *
+ * n_splits + s:
+ *     m[r]        fp32: chunk maximum of the scores, in base-2 units (score * log2 e);
  *                 -inf for an empty chunk
- *     l[r]        sum over the chunk of 2^(score*log2 e - m[r])
- *     o[r * d + e] sum over the chunk of 2^(score*log2 e - m[r]) * v[., e]
- * i.e. the per-chunk (local max, denominator, numerator) of tree_attn_decode, with
- * the maximum kept in base 2.
+ *     l[r]        fp32: sum over the chunk of 2^(score*log2 e - m[r])
+ *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e]
+ *     cnt[b*Hq+h] int32: arrival counters of the fused merge (see tad_decode_ws)
+ * m, l, o are the per-chunk (local max, denominator, numerator) of tree_attn_decode,
+ * with the maximum kept in base 2.
  */
 size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t n_splits, int32_t d);
+
+/*
+ * Zero a workspace (all ws_bytes of it) with a small kernel on `stream` (no memset, so
+ * it may be captured in a graph).  A zeroed workspace is ready for tad_decode_ws.
+ */
+int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Split step: every (b, query head, chunk) partial (m, l, o) into `ws` (layout above).
@@ -127,15 +134,26 @@ int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
 int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t n_splits,
                 int32_t d, tad_tensor *out, hipStream_t stream);
 
-/* Split + merge with a caller-provided workspace (no allocation). */
+/*
+ * Split + merge with a caller-provided workspace (no allocation).  Small problems
+ * (B * Hq * n_splits below the device's compute-unit count, n_splits <= 1024) run
+ * as ONE launch: each split work-group writes its partial, and the last one of a
+ * row to finish (counted in the workspace's cnt array) merges the row, then returns
+ * its counter to zero.  Larger problems run the split and combine kernels back to
+ * back (the counters are then unused).  Either way the output is bit-identical to
+ * tad_split followed by tad_combine.  The counters must be zero the first time a
+ * workspace is used (tad_workspace_clear, or memory allocated zeroed); every call
+ * that runs to completion leaves them zero, so a workspace can be reused call after
+ * call.  Calls that share one workspace must not overlap.
+ */
 int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                   const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
                   tad_tensor *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Split + merge; the workspace is taken with hipMallocAsync and released with
- * hipFreeAsync on `stream` (stream-ordered, so concurrent calls on different
- * streams do not share it).
+ * Split + merge; the workspace is taken with hipMallocAsync, its counters cleared by
+ * a kernel, and it is released with hipFreeAsync on `stream` (stream-ordered, so
+ * concurrent calls on different streams do not share it).
  */
 int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,

@@ -9,7 +9,7 @@ streams.  The functions carry the C names:
 - ``tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream=None)``
 - ``tad_combine(ws, B, Hq, n_splits, d, out, stream=None)``
 - ``tad_auto_splits(B, Hkv, Lmax, device=-1)``, ``tad_workspace_bytes(B, Hq, n_splits, d)``
-- ``tad_version()``, ``tad_last_error()``
+- ``tad_workspace_clear(ws, stream=None)``, ``tad_version()``, ``tad_last_error()``
 
 and ``decode(...)`` allocates ``out`` and the workspace with torch and calls
 ``tad_decode_ws``.  Tensors: q [B, Hq, d] fp32/bf16; k, v [B, Hkv, Lmax, d]
@@ -31,7 +31,7 @@ TAD_F32, TAD_BF16 = 0, 1
 TAD_OK, TAD_EINVAL, TAD_EDTYPE, TAD_ELAYOUT, TAD_EUNSUPPORTED, TAD_EWORKSPACE, TAD_EHIP = 0, -1, -2, -3, -4, -5, -6
 
 EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_bytes",
-           "tad_split", "tad_combine", "tad_decode_ws", "tad_decode")
+           "tad_workspace_clear", "tad_split", "tad_combine", "tad_decode_ws", "tad_decode")
 
 
 class TadTensor(ctypes.Structure):
@@ -67,6 +67,8 @@ def load():
     lib.tad_auto_splits.argtypes = [i32, i32, i64, i32]
     lib.tad_workspace_bytes.restype = sz
     lib.tad_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.tad_workspace_clear.restype = ctypes.c_int
+    lib.tad_workspace_clear.argtypes = [vp, sz, vp]
     lib.tad_split.restype = ctypes.c_int
     lib.tad_split.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
     lib.tad_combine.restype = ctypes.c_int
@@ -145,6 +147,10 @@ def tad_workspace_bytes(B: int, Hq: int, n_splits: int, d: int) -> int:
     return load().tad_workspace_bytes(B, Hq, n_splits, d)
 
 
+def tad_workspace_clear(ws, stream=None) -> int:
+    return _check(load().tad_workspace_clear(ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def tad_split(q, k, v, seq_lens, alibi_slopes, n_splits: int, ws, stream=None) -> int:
     lib = load()
     dq, dk, dv = describe(q), describe(k), describe(v)
@@ -192,11 +198,12 @@ def resolve_splits(q, k, n_splits: int = 0) -> int:
 
 
 def workspace(q, k, n_splits: int):
-    """A torch-allocated workspace for (q, k) with n_splits chunks (uint8, 256-aligned)."""
+    """A zeroed torch-allocated workspace for (q, k) with n_splits chunks (uint8,
+    256-aligned), ready for tad_decode_ws and reusable across calls."""
     torch = _torch()
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
     nbytes = tad_workspace_bytes(B, Hq, n_splits, d)
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
 
 
 def decode(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 0, stream=None):

@@ -38,6 +38,7 @@
 // head's maximum moved (the factor is then exactly 1).
 
 #include "device_util.h"
+#include "merge.h"
 #include "tad_internal.h"
 
 namespace tad {
@@ -306,10 +307,38 @@ void split_mfma_kernel(SplitArgs a) {
             lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
         }
         const int64_t r = ((int64_t)b * a.Hq + kvh * g + hh) * S + s;
-        a.ws_o[r * D + e] = acc;
-        if (e == 0) {
-            a.ws_m[r] = M;
-            a.ws_l[r] = lsum;
+        if (a.fused) {                       // written through for the merging work-group
+            store_partial(&a.ws_o[r * D + e], acc);
+            if (e == 0) {
+                store_partial(&a.ws_m[r], M);
+                store_partial(&a.ws_l[r], lsum);
+            }
+        } else {
+            a.ws_o[r * D + e] = acc;
+            if (e == 0) {
+                a.ws_m[r] = M;
+                a.ws_l[r] = lsum;
+            }
+        }
+    }
+
+    // ---- fused merge: the last of the S work-groups of this (b, kv head) merges its g rows.
+    if (a.fused) {
+        static_assert(NW * 2 * TILE * 4 >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in smem");
+        __shared__ int last;
+        const int64_t row0 = (int64_t)b * a.Hq + kvh * g;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
+        __syncthreads();
+        if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row0], 1) == S - 1;
+        __syncthreads();
+        if (last) {
+            for (int hh = 0; hh < g; ++hh) {
+                const int64_t row = row0 + hh;
+                merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
+                             a.out + (int64_t)b * a.sob + (int64_t)(kvh * g + hh) * a.soh,
+                             reinterpret_cast<float *>(smem));
+            }
+            if (threadIdx.x == 0) a.cnt[row0] = 0;
         }
     }
 }

@@ -29,6 +29,7 @@
 // ragged tails and neighbouring chunks are never fetched.
 
 #include "device_util.h"
+#include "merge.h"
 #include "tad_internal.h"
 
 namespace tad {
@@ -205,18 +206,42 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     for (int i = 0; i < SLOTS; ++i) M = fmaxf(M, lds_m[i]);
     const float Mu = (M == kNegInf) ? 0.f : M;
     const int64_t r = ((int64_t)b * a.Hq + h) * S + s;
+    // Partials are written through to the device coherence point when this kernel also
+    // merges (fused), so the merging work-group can read them without cache maintenance.
     for (int e = threadIdx.x; e < D; e += kSplitThreads) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_o[i][e], acc);
-        a.ws_o[r * D + e] = acc;
+        if (a.fused) store_partial(&a.ws_o[r * D + e], acc);
+        else a.ws_o[r * D + e] = acc;
     }
     if (threadIdx.x == 0) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_l[i], acc);
-        a.ws_m[r] = M;
-        a.ws_l[r] = acc;
+        if (a.fused) {
+            store_partial(&a.ws_m[r], M);
+            store_partial(&a.ws_l[r], acc);
+        } else {
+            a.ws_m[r] = M;
+            a.ws_l[r] = acc;
+        }
+    }
+
+    // ---- fused merge: the last of the row's S work-groups to arrive merges the row.
+    if (a.fused) {
+        static_assert(SLOTS * D >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in lds_o");
+        __shared__ int last;
+        const int64_t row = (int64_t)b * a.Hq + h;
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
+        __syncthreads();
+        if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row], 1) == S - 1;
+        __syncthreads();
+        if (last) {
+            merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
+                         a.out + (int64_t)b * a.sob + (int64_t)h * a.soh, &lds_o[0][0]);
+            if (threadIdx.x == 0) a.cnt[row] = 0;
+        }
     }
 }
 

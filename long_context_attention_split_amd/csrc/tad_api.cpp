@@ -169,6 +169,7 @@ int32_t auto_splits_for(int64_t B, int64_t Hkv, int64_t Lmax, int cus) {
 
 struct WsPtrs {
     float *m, *l, *o;
+    int32_t *cnt;
 };
 
 int carve_ws(void *ws, size_t ws_bytes, int64_t rows, int64_t S, int64_t d, WsPtrs *p) {
@@ -180,12 +181,15 @@ int carve_ws(void *ws, size_t ws_bytes, int64_t rows, int64_t S, int64_t d, WsPt
     p->m = (float *)((char *)ws + L.off_m);
     p->l = (float *)((char *)ws + L.off_l);
     p->o = (float *)((char *)ws + L.off_o);
+    p->cnt = (int32_t *)((char *)ws + L.off_cnt);
     return TAD_OK;
 }
 
+// Launch the split kernel.  With `out` non-null the kernel also merges (fused: the
+// last work-group of each row merges it, using the workspace's arrival counters).
 int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                  const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
-                 hipStream_t stream) {
+                 const tad_tensor *out, int64_t sob, int64_t soh, hipStream_t stream) {
     tad::SplitArgs a;
     a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.q_bf16 = P.q_dtype == TAD_BF16;
     a.k = k->data; a.v = v->data;
@@ -196,6 +200,10 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     a.S = S; a.group = (int32_t)(P.Hq / P.Hkv);
     a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
     a.ws_m = w.m; a.ws_l = w.l; a.ws_o = w.o;
+    a.fused = out != nullptr;
+    a.cnt = w.cnt;
+    a.out = out ? (float *)out->data : nullptr;
+    a.sob = sob; a.soh = soh;
     const bool bf16 = P.kv_dtype == TAD_BF16;
     hipError_t e = tad::split_mfma_supported((int)P.d, bf16, a.group)
                        ? tad::launch_split_mfma(a, (int)P.d, stream)
@@ -219,6 +227,24 @@ int check_splits(int32_t S) {
     if (S < 1 || S > tad::kMaxSplits)
         return fail(TAD_EINVAL, "n_splits must be in [1, %d] (got %d)", tad::kMaxSplits, S);
     return TAD_OK;
+}
+
+// Split + merge.  Small grids (fewer (row, chunk) pairs than compute units) are
+// launch-bound, and there one launch with the merge fused into the split kernel's
+// last work-group per row wins; on larger grids the fused merge lands on the
+// kernel's tail and costs more than a second, short kernel, so split and combine
+// run back to back.  Both give bit-identical outputs (the same merge routine).
+int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+               const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
+               const tad_tensor *out, int64_t sob, int64_t soh, hipStream_t stream) {
+    int cus = 0;
+    int rc0 = device_cus(-1, &cus);
+    if (rc0) return rc0;
+    if (S <= tad::kMaxFusedSplits && P.B * P.Hq * (int64_t)S < cus)
+        return launch_split(P, q, k, v, seq_lens, slopes, S, w, out, sob, soh, stream);
+    int rc = launch_split(P, q, k, v, seq_lens, slopes, S, w, nullptr, 0, 0, stream);
+    if (rc) return rc;
+    return launch_merge(P.B, P.Hq, S, P.d, w, out, sob, soh, stream);
 }
 
 // Validation shared by tad_decode and tad_decode_ws; resolves automatic n_splits.
@@ -260,6 +286,14 @@ size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t n_splits, int32_t d) {
     return tad::ws_layout((int64_t)B * Hq, n_splits, d).total;
 }
 
+int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws) return fail(TAD_EWORKSPACE, "workspace pointer is null");
+    if ((uintptr_t)ws & 255u) return fail(TAD_EWORKSPACE, "workspace must be 256-byte aligned");
+    hipError_t e = tad::launch_fill_zero((int32_t *)ws, (int64_t)(ws_bytes / sizeof(int32_t)), stream);
+    if (e != hipSuccess) return fail(TAD_EHIP, "workspace clear launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
               const float *alibi_slopes, int32_t n_splits, void *ws, size_t ws_bytes, hipStream_t stream) {
     Problem P;
@@ -270,7 +304,7 @@ int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, con
     WsPtrs w;
     if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq, n_splits, P.d, &w))) return rc;
     if (P.B == 0) return ok();
-    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, stream))) return rc;
+    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, nullptr, 0, 0, stream))) return rc;
     return ok();
 }
 
@@ -303,8 +337,7 @@ int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
     WsPtrs w;
     if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq, S, P.d, &w))) return rc;
     if (P.B == 0) return ok();
-    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, S, w, stream))) return rc;
-    if ((rc = launch_merge(P.B, P.Hq, S, P.d, w, out, sob, soh, stream))) return rc;
+    if ((rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, out, sob, soh, stream))) return rc;
     return ok();
 }
 
@@ -322,8 +355,11 @@ int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, co
     if (e != hipSuccess) return fail(TAD_EHIP, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
     WsPtrs w;
     rc = carve_ws(ws, bytes, P.B * P.Hq, S, P.d, &w);
-    if (!rc) rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, S, w, stream);
-    if (!rc) rc = launch_merge(P.B, P.Hq, S, P.d, w, out, sob, soh, stream);
+    if (!rc) {
+        hipError_t ez = tad::launch_fill_zero(w.cnt, P.B * P.Hq, stream);
+        if (ez != hipSuccess) rc = fail(TAD_EHIP, "counter clear launch: %s", hipGetErrorString(ez));
+    }
+    if (!rc) rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, out, sob, soh, stream);
     e = hipFreeAsync(ws, stream);
     if (rc) return rc;
     if (e != hipSuccess) return fail(TAD_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));

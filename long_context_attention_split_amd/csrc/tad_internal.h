@@ -20,6 +20,12 @@ struct SplitArgs {
     int32_t B, Hq, Hkv, Lmax, S, group;
     float qscale;           // d^-1/2 * log2(e): scores come out in base-2 units
     float *ws_m, *ws_l, *ws_o;  // partial arrays (see tad.h)
+    // Fused merge: when set, the last work-group to finish a row (counted in cnt)
+    // merges the row's partials into out.  cnt must be zero on entry and is left zero.
+    int32_t fused;
+    int32_t *cnt;           // [B * Hq] arrival counters
+    float *out;             // [B, Hq, d] fp32
+    int64_t sob, soh;       // out element strides
 };
 
 struct CombineArgs {
@@ -61,7 +67,7 @@ __device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-    size_t off_m, off_l, off_o, total;
+    size_t off_m, off_l, off_o, off_cnt, total;
 };
 
 inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
@@ -70,7 +76,8 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
     w.off_m = 0;
     w.off_l = align256(n * sizeof(float));
     w.off_o = w.off_l + align256(n * sizeof(float));
-    w.total = w.off_o + align256(n * size_t(d) * sizeof(float));
+    w.off_cnt = w.off_o + align256(n * size_t(d) * sizeof(float));
+    w.total = w.off_cnt + align256(size_t(rows) * sizeof(int32_t));
     return w;
 }
 
@@ -79,10 +86,12 @@ hipError_t launch_split_valu(const SplitArgs &a, int d, bool kv_bf16, hipStream_
 bool split_mfma_supported(int d, bool kv_bf16, int group);
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
+hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);
 
 // Keys per work-group tile of the VALU split kernel (for tests of the host logic).
 constexpr int kSplitThreads = 256;
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSplits = 4096;
+constexpr int kMaxFusedSplits = 1024;   // the fused merge keeps S weights in the kernel's LDS
 
 }  // namespace tad

@@ -39,10 +39,10 @@ def test_version_matches_header(lib):
 
 
 def test_workspace_bytes_layout(lib):
-    # m and l: rows*S floats each, 256-aligned; o: rows*S*d floats
-    assert lib.tad_workspace_bytes(1, 32, 32, 128) == 2 * 4096 + 1024 * 128 * 4
-    assert lib.tad_workspace_bytes(8, 32, 16, 128) == 2 * 16384 + 4096 * 128 * 4
-    assert lib.tad_workspace_bytes(1, 1, 8, 512) == 2 * 256 + 8 * 512 * 4
+    # m and l: rows*S floats each, 256-aligned; o: rows*S*d floats; cnt: rows int32
+    assert lib.tad_workspace_bytes(1, 32, 32, 128) == 2 * 4096 + 1024 * 128 * 4 + 256
+    assert lib.tad_workspace_bytes(8, 32, 16, 128) == 2 * 16384 + 4096 * 128 * 4 + 1024
+    assert lib.tad_workspace_bytes(1, 1, 8, 512) == 2 * 256 + 8 * 512 * 4 + 256
     assert lib.tad_workspace_bytes(0, 1, 1, 64) == 0
     assert lib.tad_workspace_bytes(1, 1, 0, 64) == 0
 

@@ -93,7 +93,7 @@ def test_head_dims_and_dtypes(lib, d, kv):
     run_case(lib, 120 + d, 2, 2, 2, 1000, d, kv=kv, n_splits=3)
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 7, 8, 31, 64, 255, 1024])
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 8, 31, 64, 255, 1024, 1025, 2000])
 def test_split_count_sweep(lib, S):
     run_case(lib, 130, 1, 4, 4, 4099, 128, n_splits=S)
 
@@ -158,6 +158,38 @@ def test_entry_points_agree(lib):
     again = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S)
     torch.cuda.synchronize()
     assert torch.equal(a, out_b) and torch.equal(a, out_c) and torch.equal(a, again)
+
+
+def test_workspace_reuse_and_clear(lib):
+    """tad_decode_ws merges in the split kernel's last work-group per row; its arrival
+    counters return to zero, so one workspace serves call after call (and after
+    tad_workspace_clear of a dirty buffer)."""
+    c = to_dev(W.random_case(205, 2, 8, 2, 2500, 128, seq_lens=[2500, 1700]))
+    c2 = to_dev(W.random_case(206, 2, 8, 8, 2500, 64))
+    S = 5
+    ref = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], None, S)
+    ws = lib.workspace(c["q"], c["k"], S)
+    outs = []
+    for _ in range(4):
+        out = torch.empty_like(ref)
+        lib.tad_decode_ws(c["q"], c["k"], c["v"], c["seq_lens"], None, S, out, ws)
+        outs.append(out)
+    ws.fill_(0x5A)                                   # a dirty buffer, then an explicit clear
+    lib.tad_workspace_clear(ws)
+    out = torch.empty_like(ref)
+    lib.tad_decode_ws(c["q"], c["k"], c["v"], c["seq_lens"], None, S, out, ws)
+    outs.append(out)
+    # a different problem (MHA, d 64) through a workspace of its own, twice
+    ws2 = lib.workspace(c2["q"], c2["k"], 3)
+    o2 = [torch.empty((2, 8, 64), device=DEV) for _ in range(2)]
+    for o in o2:
+        lib.tad_decode_ws(c2["q"], c2["k"], c2["v"], None, None, 3, o, ws2)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+    assert torch.equal(o2[0], o2[1])
+    ref2 = oracle.decode_f64(c2["q"].cpu(), c2["k"].cpu(), c2["v"].cpu())
+    assert_parity(o2[0].cpu().numpy(), ref2, torch.bfloat16, vmax_valid(c2["v"].cpu(), None), "reuse d64")
 
 
 # ----------------------------------------------------------------------------- partials
