@@ -7,7 +7,8 @@ package imports nothing from the product.
 
 - ``decode_f64``: the plain definition softmax(q K^T d^-1/2 + bias) V, evaluated
   row by row in double precision by ``decode_f64.c`` (see its header for the
-  formula and the pages it follows).
+  formula and the pages it follows); fp32, bf16 and OCP fp8 (E4M3, E5M2) keys and
+  values, fp8 with per-(batch, KV head) dequantisation scales.
 - ``alibi_bias``: the bias term that definition adds ("ALiBi with causal=True
   unexpected bias?", causal bias vector example).
 - ``tree``: numpy fp64 split-and-merge decoding in the steps of the tree-attention
@@ -28,7 +29,7 @@ _SRC = os.path.join(_HERE, "decode_f64.c")
 _LIB = os.path.join(_HERE, "liboracle_f64.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:
@@ -50,9 +51,13 @@ def _load():
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_decode_f64.restype = i32
         lib.oracle_decode_f64.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i64, i64, i64, i64, i64,
-                                          i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, i32]
+                                          i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32]
         lib.oracle_alibi_bias.restype = ctypes.c_double
         lib.oracle_alibi_bias.argtypes = [i64, i64, ctypes.c_double]
+        lib.oracle_fp8_e4m3.restype = ctypes.c_double
+        lib.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_e5m2.restype = ctypes.c_double
+        lib.oracle_fp8_e5m2.argtypes = [ctypes.c_uint8]
         _lib = lib
     return _lib
 
@@ -67,7 +72,11 @@ def _as_np(x):
                 return x.view(torch.int16).numpy().view(np.uint16), BF16
             if x.dtype == torch.float32:
                 return x.numpy(), F32
-            raise TypeError("oracle inputs must be fp32 or bf16, got %s" % x.dtype)
+            if x.dtype == torch.float8_e4m3fn:
+                return x.view(torch.uint8).numpy(), FP8_E4M3
+            if x.dtype == torch.float8_e5m2:
+                return x.view(torch.uint8).numpy(), FP8_E5M2
+            raise TypeError("oracle inputs must be fp32, bf16 or fp8, got %s" % x.dtype)
     except ImportError:
         pass
     x = np.asarray(x)
@@ -86,11 +95,12 @@ def _strides(a: np.ndarray):
 
 
 def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]] = None,
-               n_threads: Optional[int] = None) -> np.ndarray:
+               n_threads: Optional[int] = None, k_scale=None, v_scale=None) -> np.ndarray:
     """Oracle output (float64).
 
-    q [B, Hq, d]; k, v [B, Hkv, Lmax, d] (fp32 or bf16 torch tensors, or numpy float32 /
-    uint16 bf16 bits); seq_lens int32 [B] or None; slopes fp32 [Hq] or None.
+    q [B, Hq, d]; k, v [B, Hkv, Lmax, d] (fp32, bf16 or fp8 torch tensors, or numpy
+    float32 / uint16 bf16 bits); seq_lens int32 [B] or None; slopes fp32 [Hq] or None;
+    k_scale, v_scale fp32 [B, Hkv] dequantisation scales (real = stored * scale) or None.
     ``rows``: flat b*Hq+h indices to compute (result [len(rows), d]); None for all
     (result [B, Hq, d]).
     """
@@ -113,6 +123,13 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
     if slopes is not None:
         sp = np.ascontiguousarray(np.asarray(slopes.cpu() if hasattr(slopes, "cpu") else slopes,
                                              dtype=np.float32))
+    ksc = vsc = None
+    if k_scale is not None:
+        ksc = np.ascontiguousarray(np.asarray(k_scale.cpu() if hasattr(k_scale, "cpu") else k_scale,
+                                              dtype=np.float32)).reshape(-1)
+    if v_scale is not None:
+        vsc = np.ascontiguousarray(np.asarray(v_scale.cpu() if hasattr(v_scale, "cpu") else v_scale,
+                                              dtype=np.float32)).reshape(-1)
     rw = None
     n_rows = B * Hq
     if rows is not None:
@@ -124,7 +141,7 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
     rc = lib.oracle_decode_f64(ptr(qn), qt, sq[0], sq[1], ptr(kn), ptr(vn), kt,
                                sk[0], sk[1], sk[2], sv[0], sv[1], sv[2],
-                               B, Hq, Hkv, Lmax, d, ptr(sl), ptr(sp), ptr(rw), n_rows,
+                               B, Hq, Hkv, Lmax, d, ptr(sl), ptr(sp), ptr(ksc), ptr(vsc), ptr(rw), n_rows,
                                ptr(out), int(n_threads))
     if rc != 0:
         raise RuntimeError("oracle_decode_f64 failed (%d)" % rc)
@@ -136,9 +153,19 @@ def alibi_bias(L: int, j: int, slope: float) -> float:
     return _load().oracle_alibi_bias(int(L), int(j), float(slope))
 
 
+def fp8_value(bits: int, fmt: int) -> float:
+    """The oracle's decoding of one FP8 byte (fmt FP8_E4M3 or FP8_E5M2)."""
+    lib = _load()
+    return lib.oracle_fp8_e4m3(bits) if fmt == FP8_E4M3 else lib.oracle_fp8_e5m2(bits)
+
+
 def widen(x) -> np.ndarray:
-    """Exact fp64 copy of an fp32 / bf16 tensor (bf16: bits << 16)."""
+    """Exact fp64 copy of an fp32 / bf16 / fp8 tensor (bf16: bits << 16; fp8: the
+    oracle's own decoding table)."""
     a, t = _as_np(x)
     if t == F32:
         return a.astype(np.float64)
+    if t in (FP8_E4M3, FP8_E5M2):
+        table = np.array([fp8_value(i, t) for i in range(256)], dtype=np.float64)
+        return table[a]
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

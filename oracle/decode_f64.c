@@ -26,8 +26,13 @@
  *     mathematics, softmax decomposition: subtracting the maximum score leaves the
  *     softmax unchanged (it only keeps exp() in range).
  *
+ * FP8 keys and values (OCP E4M3 "fn" and E5M2 formats) carry a dequantisation scale per
+ * (batch row, KV head): the stored value times the scale is the real value; the scores
+ * and the weighted sum use those real values.  (The pages name FP8 attention only; the
+ * scale granularity is our reading.)
+ *
  * All arithmetic is double precision on exactly widened inputs (bf16 -> fp32 -> fp64
- * are exact).  Rows are independent, so rows are spread over POSIX threads; each row
+ * and fp8 -> fp64 are exact).  Rows are independent, so rows are spread over POSIX threads; each row
  * is computed by one thread, in key order, with no blocking or reordering.
  * Every function here is pinned by the CPU tests (closed forms, invariants, a library
  * attention routine, the page's printed bias vector); nothing is "parity unpinned".
@@ -40,12 +45,40 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_FP8_E4M3 2
+#define OR_FP8_E5M2 3
+
+/* OCP FP8 E4M3 ("fn": no infinities, S.1111.111 is NaN): bias 7, 3 mantissa bits. */
+double oracle_fp8_e4m3(uint8_t x)
+{
+    const int sign = x >> 7, e = (x >> 3) & 15, m = x & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);                 /* (m / 8) * 2^(1 - 7) */
+    else v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* OCP FP8 E5M2: bias 15, 2 mantissa bits, IEEE-style infinities and NaNs. */
+double oracle_fp8_e5m2(uint8_t x)
+{
+    const int sign = x >> 7, e = (x >> 2) & 31, m = x & 3;
+    double v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -16);           /* (m / 4) * 2^(1 - 15) */
+    else v = ldexp(1.0 + m / 4.0, e - 15);
+    return sign ? -v : v;
+}
 
 /* Widen one stored element to double.  bf16 is the upper half of an IEEE fp32. */
 static double widen(const void *base, int dtype, int64_t idx)
 {
     if (dtype == OR_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == OR_FP8_E4M3)
+        return oracle_fp8_e4m3(((const uint8_t *)base)[idx]);
+    if (dtype == OR_FP8_E5M2)
+        return oracle_fp8_e5m2(((const uint8_t *)base)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -70,6 +103,7 @@ typedef struct {
     int B, Hq, Hkv, Lmax, d;
     const int32_t *seq_lens;     /* [B] or NULL */
     const float *slopes;         /* [Hq] or NULL */
+    const float *k_scale, *v_scale; /* [B * Hkv] dequantisation scales, or NULL (= 1) */
     const int32_t *rows;         /* flat b*Hq+h indices to compute, or NULL for all */
     int n_rows;
     double *out;                 /* [n_rows, d] */
@@ -91,6 +125,8 @@ static void decode_row(const oracle_job *J, int b, int h, double *s, double *out
 
     const int kh = h / (J->Hq / J->Hkv);
     const double scale = 1.0 / sqrt((double)d);
+    const double ks = J->k_scale ? (double)J->k_scale[b * J->Hkv + kh] : 1.0;
+    const double vs = J->v_scale ? (double)J->v_scale[b * J->Hkv + kh] : 1.0;
     const int64_t qoff = (int64_t)b * J->sqb + (int64_t)h * J->sqh;
     const int64_t koff = (int64_t)b * J->skb + (int64_t)kh * J->skh;
     const int64_t voff = (int64_t)b * J->svb + (int64_t)kh * J->svh;
@@ -99,7 +135,7 @@ static void decode_row(const oracle_job *J, int b, int h, double *s, double *out
     for (int64_t j = 0; j < L; ++j) {
         double dot = 0.0;
         for (int i = 0; i < d; ++i)
-            dot += widen(J->q, J->q_dtype, qoff + i) * widen(J->k, J->kv_dtype, koff + j * J->skj + i);
+            dot += widen(J->q, J->q_dtype, qoff + i) * (ks * widen(J->k, J->kv_dtype, koff + j * J->skj + i));
         s[j] = dot * scale;
         if (J->slopes) s[j] += oracle_alibi_bias(L, j, (double)J->slopes[h]);
     }
@@ -112,7 +148,7 @@ static void decode_row(const oracle_job *J, int b, int h, double *s, double *out
         double w = exp(s[j] - m);
         z += w;
         for (int e = 0; e < d; ++e)
-            out[e] += w * widen(J->v, J->kv_dtype, voff + j * J->svj + e);
+            out[e] += w * (vs * widen(J->v, J->kv_dtype, voff + j * J->svj + e));
     }
     for (int e = 0; e < d; ++e) out[e] /= z;
 }
@@ -142,6 +178,8 @@ static void *worker(void *p)
  * Compute the decode output for the requested rows.
  *   q      : [B, Hq, d] with element strides (sqb, sqh, 1); dtype OR_F32 or OR_BF16
  *   k, v   : [B, Hkv, Lmax, d] with element strides (s?b, s?h, s?j, 1); same dtype
+ *            (OR_F32, OR_BF16, OR_FP8_E4M3, OR_FP8_E5M2)
+ *   k_scale, v_scale: [B * Hkv] scales (real = stored * scale), or NULL
  *   rows   : flat indices b*Hq + h to compute (n_rows of them), or NULL for all B*Hq
  *   out    : [n_rows, d] doubles, row r for rows[r]
  *   n_threads: POSIX threads to use (>= 1)
@@ -153,15 +191,16 @@ int oracle_decode_f64(const void *q, int q_dtype, int64_t sqb, int64_t sqh,
                       int64_t svb, int64_t svh, int64_t svj,
                       int B, int Hq, int Hkv, int Lmax, int d,
                       const int32_t *seq_lens, const float *slopes,
+                      const float *k_scale, const float *v_scale,
                       const int32_t *rows, int n_rows, double *out, int n_threads)
 {
     if (!q || !k || !v || !out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lmax < 0 || d <= 0)
         return -1;
-    if ((q_dtype != OR_F32 && q_dtype != OR_BF16) || (kv_dtype != OR_F32 && kv_dtype != OR_BF16))
+    if ((q_dtype != OR_F32 && q_dtype != OR_BF16) || kv_dtype < OR_F32 || kv_dtype > OR_FP8_E5M2)
         return -1;
     oracle_job J = {q, q_dtype, sqb, sqh, k, v, kv_dtype, skb, skh, skj, svb, svh, svj,
-                    B, Hq, Hkv, Lmax, d, seq_lens, slopes, rows, rows ? n_rows : B * Hq, out,
-                    n_threads < 1 ? 1 : n_threads};
+                    B, Hq, Hkv, Lmax, d, seq_lens, slopes, k_scale, v_scale,
+                    rows, rows ? n_rows : B * Hq, out, n_threads < 1 ? 1 : n_threads};
     for (int r = 0; rows && r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= B * Hq) return -1;
     if (J.n_threads > J.n_rows) J.n_threads = J.n_rows > 0 ? J.n_rows : 1;

@@ -346,3 +346,40 @@ def test_workload_recipes_shapes():
     s = W.alibi_slopes(16)
     assert s[0] == 2 ** -0.5 and s[15] == 2 ** -8
     assert W.WORKLOADS[2].kv_bytes() == 2 * 1024 ** 3
+
+
+# ----------------------------------------------------------------------------- fp8
+
+@pytest.mark.parametrize("fmt,tdt", [(oracle.FP8_E4M3, torch.float8_e4m3fn), (oracle.FP8_E5M2, torch.float8_e5m2)])
+def test_fp8_decoding_matches_torch(fmt, tdt):
+    """The oracle's OCP FP8 decoding equals torch's float8 types for all 256 patterns."""
+    ref = torch.arange(256, dtype=torch.uint8).view(tdt).to(torch.float64).numpy()
+    got = np.array([oracle.fp8_value(i, fmt) for i in range(256)])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_fp8_known_values():
+    e4 = lambda b: oracle.fp8_value(b, oracle.FP8_E4M3)
+    e5 = lambda b: oracle.fp8_value(b, oracle.FP8_E5M2)
+    assert e4(0x7E) == 448.0 and e4(0x01) == 2.0 ** -9 and e4(0x38) == 1.0 and e4(0xB8) == -1.0
+    assert math.isnan(e4(0x7F)) and math.isnan(e4(0xFF))
+    assert e5(0x7B) == 57344.0 and e5(0x01) == 2.0 ** -16 and e5(0x3C) == 1.0
+    assert e5(0x7C) == math.inf and math.isnan(e5(0x7E))
+
+
+@pytest.mark.parametrize("tdt", [torch.float8_e4m3fn, torch.float8_e5m2])
+def test_fp8_scaled_equals_dequantised_fp32(tdt):
+    """FP8 K/V with per-(b, head) scales give the output of the dequantised values
+    (stored * scale, exact in fp32 for these scales' products)."""
+    c = W.random_case(19, B=2, Hq=4, Hkv=2, L=60, d=32, kv_dtype=tdt)
+    out = oracle.decode_f64(c["q"], c["k"], c["v"], k_scale=c["k_scale"], v_scale=c["v_scale"])
+    kd = torch.from_numpy(oracle.widen(c["k"]) * c["k_scale"].double().numpy()[:, :, None, None])
+    vd = torch.from_numpy(oracle.widen(c["v"]) * c["v_scale"].double().numpy()[:, :, None, None])
+    q = torch.from_numpy(f64(c["q"])).unsqueeze(2)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q, kd.repeat_interleave(2, dim=1), vd.repeat_interleave(2, dim=1)).squeeze(2)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # the scales matter: without them the output differs
+    assert not np.allclose(oracle.decode_f64(c["q"], c["k"], c["v"]), out)

@@ -28,6 +28,8 @@ id     description
 5      1M-key stress: batch 1, 8 heads, d 128, 1048576 keys, K/V bf16; K is
        bf16(6 N(0,1)); one key per head, at a seeded position, is replaced by
        bf16(c q_h) with c = 60 sqrt(d) / |q_h|^2 so that its logit is about +60.
+6      workload 2 with FP8 (OCP E4M3) K and V: each (b, kv-head) slab of N(0,1)
+       draws is divided by its amax/448 and rounded to E4M3; the scale is kept.
 =====  =========================================================================
 """
 from __future__ import annotations
@@ -66,7 +68,7 @@ class Workload:
 
     def kv_bytes(self, seq_lens: Optional[torch.Tensor] = None) -> int:
         """Algorithmic K+V bytes one decode reads: 2 * d * elem * keys per KV head."""
-        elem = 4 if self.kv_dtype == F32 else 2
+        elem = 4 if self.kv_dtype == F32 else (1 if self.kv_dtype in FP8_MAX else 2)
         if seq_lens is None:
             keys = self.B * self.Lmax
         else:
@@ -82,6 +84,8 @@ WORKLOADS = {
     4: Workload(4, "ALiBi B4 H16 d128 L65536 bf16", 4, 16, 16, 128, 65536, F32, BF16, alibi=True),
     5: Workload(5, "1M-key stress B1 H8 d128 L1048576 bf16, planted key", 1, 8, 8, 128, 1 << 20,
                 F32, BF16, k_scale=6.0, planted_logit=60.0),
+    6: Workload(6, "MHA B1 H32 d128 L131072 fp8-e4m3 K/V, per-head scales", 1, 32, 32, 128, 131072,
+                F32, torch.float8_e4m3fn),
 }
 
 
@@ -115,6 +119,27 @@ def draw_kv(seed: int, B: int, Hkv: int, L: int, d: int, dtype=BF16, scale: floa
     return out
 
 
+FP8_MAX = {torch.float8_e4m3fn: 448.0, torch.float8_e5m2: 57344.0}
+
+
+def draw_kv_fp8(seed: int, B: int, Hkv: int, L: int, d: int, dtype=torch.float8_e4m3fn):
+    """N(0,1) K or V quantised to FP8 with one scale per (b, kv-head) slab.
+
+    The slab's scale is amax / (largest finite value of the format); the stored value is
+    the N(0,1) draw divided by the scale, rounded by Tensor.to.  Returns (stored
+    [B, Hkv, L, d] fp8, scales [B, Hkv] fp32) -- real value = stored * scale."""
+    g = _gen(seed)
+    out = torch.empty((B, Hkv, L, d), dtype=dtype)
+    scale = torch.empty((B, Hkv), dtype=F32)
+    for b in range(B):
+        for h in range(Hkv):
+            slab = torch.randn((L, d), generator=g, dtype=F32)
+            s = float(slab.abs().max()) / FP8_MAX[dtype]
+            scale[b, h] = s
+            out[b, h].copy_((slab / scale[b, h]).to(dtype))
+    return out, scale
+
+
 def draw_seq_lens(seed: int, B: int, lo: int, hi: int) -> torch.Tensor:
     """Integers uniform on [lo, hi] inclusive, int32."""
     return torch.randint(lo, hi + 1, (B,), generator=_gen(seed), dtype=torch.int64).to(torch.int32)
@@ -129,8 +154,13 @@ def make_workload(wid: int):
     w = WORKLOADS[wid]
     base = 1000 * wid
     q = draw_q(base + 0, w.B, w.Hq, w.d, w.q_dtype)
-    k = draw_kv(base + 1, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype, w.k_scale)
-    v = draw_kv(base + 2, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype)
+    ks = vs = None
+    if w.kv_dtype in FP8_MAX:
+        k, ks = draw_kv_fp8(base + 1, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype)
+        v, vs = draw_kv_fp8(base + 2, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype)
+    else:
+        k = draw_kv(base + 1, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype, w.k_scale)
+        v = draw_kv(base + 2, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype)
     seq_lens = None
     if w.ragged:
         seq_lens = draw_seq_lens(base + 3, w.B, w.ragged_lo, w.Lmax)
@@ -143,7 +173,7 @@ def make_workload(wid: int):
     if w.planted_logit is not None:
         planted = plant_dominant_keys(base + 4, q, k, w.planted_logit)
     return dict(workload=w, q=q, k=k, v=v, seq_lens=seq_lens, slopes=slopes,
-                n_splits=w.n_splits, planted=planted)
+                n_splits=w.n_splits, planted=planted, k_scale=ks, v_scale=vs)
 
 
 def plant_dominant_keys(seed: int, q: torch.Tensor, k: torch.Tensor, logit: float) -> torch.Tensor:
@@ -166,17 +196,32 @@ def plant_dominant_keys(seed: int, q: torch.Tensor, k: torch.Tensor, logit: floa
 
 def random_case(seed: int, B: int, Hq: int, Hkv: int, L: int, d: int, q_dtype=F32, kv_dtype=BF16,
                 seq_lens=None, alibi: bool = False, k_scale: float = 1.0, poison_tail: bool = True):
-    """A small seeded case of arbitrary shape for parity tests (same recipe as the workloads)."""
+    """A small seeded case of arbitrary shape for parity tests (same recipe as the workloads).
+
+    FP8 K/V (kv_dtype float8_e4m3fn / float8_e5m2) come with per-(b, kv-head) scales in
+    the returned k_scale / v_scale (None otherwise)."""
     q = draw_q(seed, B, Hq, d, q_dtype)
-    k = draw_kv(seed + 1, B, Hkv, L, d, kv_dtype, k_scale)
-    v = draw_kv(seed + 2, B, Hkv, L, d, kv_dtype)
+    ks = vs = None
+    if kv_dtype in FP8_MAX:
+        k, ks = draw_kv_fp8(seed + 1, B, Hkv, L, d, kv_dtype)
+        v, vs = draw_kv_fp8(seed + 2, B, Hkv, L, d, kv_dtype)
+        if k_scale != 1.0:
+            ks = ks * k_scale
+    else:
+        k = draw_kv(seed + 1, B, Hkv, L, d, kv_dtype, k_scale)
+        v = draw_kv(seed + 2, B, Hkv, L, d, kv_dtype)
     sl = None
     if seq_lens is not None:
         sl = torch.as_tensor(seq_lens, dtype=torch.int32)
         if poison_tail:
             for b in range(B):
                 Lb = max(0, min(int(sl[b]), L))
-                k[b, :, Lb:, :] = float("nan")
-                v[b, :, Lb:, :] = float("nan")
+                if kv_dtype in FP8_MAX:       # NaN bit patterns (E4M3: 0x7F, E5M2: 0x7E)
+                    nan_bits = 0x7F if kv_dtype == torch.float8_e4m3fn else 0x7E
+                    k.view(torch.uint8)[b, :, Lb:, :] = nan_bits
+                    v.view(torch.uint8)[b, :, Lb:, :] = nan_bits
+                else:
+                    k[b, :, Lb:, :] = float("nan")
+                    v[b, :, Lb:, :] = float("nan")
     slopes = alibi_slopes(Hq) if alibi else None
-    return dict(q=q, k=k, v=v, seq_lens=sl, slopes=slopes)
+    return dict(q=q, k=k, v=v, seq_lens=sl, slopes=slopes, k_scale=ks, v_scale=vs)
