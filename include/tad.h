@@ -25,9 +25,13 @@
  *    strides in ELEMENTS.  The innermost stride must be 1; every row start must be
  *    16-byte aligned (data pointer and outer strides in bytes multiples of 16).
  *  - q   : [B, Hq, d] or [B, Hq, 1, d], TAD_F32 or TAD_BF16.
- *  - k, v: [B, Hkv, Lmax, d] or [B, Lmax, d] (then Hkv = 1); same dtype (TAD_F32 or
- *          TAD_BF16) and shape; any outer strides (e.g. a [B, Lmax, Hkv, d] cache
- *          viewed as [B, Hkv, Lmax, d]).  Hq must be a multiple of Hkv.
+ *  - k, v: [B, Hkv, Lmax, d] or [B, Lmax, d] (then Hkv = 1); same dtype (TAD_F32,
+ *          TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2) and shape; any outer strides (e.g.
+ *          a [B, Lmax, Hkv, d] cache viewed as [B, Hkv, Lmax, d]).  Hq must be a
+ *          multiple of Hkv.  FP8 tensors may carry a dequantisation scale (the
+ *          tensor's `scale`: device fp32 [B * Hkv], index b * Hkv + kv_head; the real
+ *          value is stored * scale; NULL means 1).  `scale` must be NULL for every
+ *          other tensor.
  *  - out : [B, Hq, d] or [B, Hq, 1, d], TAD_F32.
  *  - d (head dimension) must be 64, 128, 256 or 512.
  *  - seq_lens: DEVICE int32 [B] or NULL (every row uses Lmax).  Values are clamped
@@ -60,9 +64,10 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10100 /* major*10000 + minor*100 + patch */
 
-enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1 };
+/* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
+enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
 
 enum tad_status {
     TAD_OK = 0,
@@ -75,11 +80,12 @@ enum tad_status {
 };
 
 typedef struct tad_tensor {
-    void *data;        /* device pointer */
-    int32_t dtype;     /* enum tad_dtype */
-    int32_t ndim;      /* 3 or 4 */
+    void *data;         /* device pointer */
+    int32_t dtype;      /* enum tad_dtype */
+    int32_t ndim;       /* 3 or 4 */
     int64_t shape[4];
-    int64_t stride[4]; /* elements */
+    int64_t stride[4];  /* elements */
+    const float *scale; /* FP8 k/v only: device fp32 [B * Hkv] dequantisation scales, or NULL */
 } tad_tensor;
 
 /* Library version, TAD_VERSION of the build. */

@@ -13,7 +13,8 @@ streams.  The functions carry the C names:
 
 and ``decode(...)`` allocates ``out`` and the workspace with torch and calls
 ``tad_decode_ws``.  Tensors: q [B, Hq, d] fp32/bf16; k, v [B, Hkv, Lmax, d]
-fp32/bf16 (innermost dim contiguous); seq_lens int32 [B] or None; alibi_slopes fp32
+fp32/bf16/float8_e4m3fn/float8_e5m2 (innermost dim contiguous; FP8 with optional
+k_scale / v_scale fp32 [B, Hkv]); seq_lens int32 [B] or None; alibi_slopes fp32
 [Hq] or None; out fp32 [B, Hq, d].  All must live on the GPU.
 
 There is no fallback: if ``libtad.so`` has not been built, ``load()`` raises.
@@ -27,7 +28,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtad.so")
 
-TAD_F32, TAD_BF16 = 0, 1
+TAD_F32, TAD_BF16, TAD_FP8_E4M3, TAD_FP8_E5M2 = 0, 1, 2, 3
 TAD_OK, TAD_EINVAL, TAD_EDTYPE, TAD_ELAYOUT, TAD_EUNSUPPORTED, TAD_EWORKSPACE, TAD_EHIP = 0, -1, -2, -3, -4, -5, -6
 
 EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_bytes",
@@ -36,7 +37,7 @@ EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_by
 
 class TadTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
-                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4), ("scale", ctypes.c_void_p)]
 
 
 class TadError(RuntimeError):
@@ -88,13 +89,18 @@ def _torch():
     return torch
 
 
-def describe(t) -> TadTensor:
-    """tad_tensor for a torch tensor (no copy; the tensor must outlive the call's work)."""
+def describe(t, scale=None) -> TadTensor:
+    """tad_tensor for a torch tensor (no copy; the tensor must outlive the call's work).
+    ``scale``: fp32 [B, Hkv] dequantisation scales of an FP8 k or v, or None."""
     torch = _torch()
     if t.dtype == torch.float32:
         dt = TAD_F32
     elif t.dtype == torch.bfloat16:
         dt = TAD_BF16
+    elif t.dtype == torch.float8_e4m3fn:
+        dt = TAD_FP8_E4M3
+    elif t.dtype == torch.float8_e5m2:
+        dt = TAD_FP8_E5M2
     else:
         dt = -1
     if t.dim() > 4:
@@ -106,6 +112,7 @@ def describe(t) -> TadTensor:
     for i in range(t.dim()):
         d.shape[i] = t.shape[i]
         d.stride[i] = t.stride(i)
+    d.scale = None if scale is None else scale.data_ptr()
     return d
 
 
@@ -151,9 +158,10 @@ def tad_workspace_clear(ws, stream=None) -> int:
     return _check(load().tad_workspace_clear(ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def tad_split(q, k, v, seq_lens, alibi_slopes, n_splits: int, ws, stream=None) -> int:
+def tad_split(q, k, v, seq_lens, alibi_slopes, n_splits: int, ws, stream=None, k_scale=None,
+              v_scale=None) -> int:
     lib = load()
-    dq, dk, dv = describe(q), describe(k), describe(v)
+    dq, dk, dv = describe(q), describe(k, k_scale), describe(v, v_scale)
     return _check(lib.tad_split(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                 _ptr(alibi_slopes), n_splits, ws.data_ptr(), ws.numel() * ws.element_size(),
                                 _stream(stream)))
@@ -166,17 +174,19 @@ def tad_combine(ws, B: int, Hq: int, n_splits: int, d: int, out, stream=None) ->
                                   ctypes.byref(do), _stream(stream)))
 
 
-def tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, ws, stream=None) -> int:
+def tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, ws, stream=None, k_scale=None,
+                  v_scale=None) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
     return _check(lib.tad_decode_ws(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                     _ptr(alibi_slopes), n_splits, ctypes.byref(do), ws.data_ptr(),
                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None) -> int:
+def tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None, k_scale=None,
+               v_scale=None) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
     return _check(lib.tad_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                  _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
 
@@ -206,23 +216,25 @@ def workspace(q, k, n_splits: int):
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
 
 
-def decode(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 0, stream=None):
+def decode(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 0, stream=None, k_scale=None,
+           v_scale=None):
     """out = tad_decode_ws(...) with torch-allocated out [B, Hq, d] fp32 and workspace."""
     torch = _torch()
     S = resolve_splits(q, k, n_splits)
     ws = workspace(q, k, S)
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
-    tad_decode_ws(q, k, v, seq_lens, alibi_slopes, S, out, ws, stream)
+    tad_decode_ws(q, k, v, seq_lens, alibi_slopes, S, out, ws, stream, k_scale, v_scale)
     return out
 
 
-def split_partials(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 1, stream=None):
+def split_partials(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 1, stream=None,
+                   k_scale=None, v_scale=None):
     """Run tad_split only; returns (m, l, o) views of the workspace:
     m, l [B, Hq, S] (m in base-2 units), o [B, Hq, S, d]."""
     torch = _torch()
     ws = workspace(q, k, n_splits)
-    tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream)
+    tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream, k_scale, v_scale)
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
     n = B * Hq * n_splits
     al = lambda x: (x + 255) // 256 * 256

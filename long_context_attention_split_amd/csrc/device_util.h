@@ -32,21 +32,49 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// 8 consecutive elements of a row as fp32: one 16-byte load of bf16, or two of fp32.
-template <bool BF16, int POLICY>
-struct Row8 {
-    static constexpr int kLoads = BF16 ? 1 : 2;
+// Element types of K and V (values of SplitArgs::kv_type).
+constexpr int kKvF32 = 0, kKvBF16 = 1, kKvE4M3 = 2, kKvE5M2 = 3;
+
+// The slice of one key row a lane holds: EPL consecutive elements, loaded with one
+// 16-byte load (bf16: 8 elements, FP8: 16) or two (fp32: 8), then widened to fp32.
+// FP8 uses the hardware OCP E4M3 / E5M2 conversions (v_cvt_pk_f32_fp8 / _bf8, two
+// elements per instruction; exact).
+template <int KVT, int POLICY>
+struct RowChunk {
+    static constexpr int kLoads = KVT == kKvF32 ? 2 : 1;
+    static constexpr int EPL = (KVT == kKvE4M3 || KVT == kKvE5M2) ? 16 : 8;
+    static constexpr int kBytes = 16 * kLoads;        // bytes per lane per key
     uint4 raw[kLoads];
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) raw[i] = load16<POLICY>(r, off + 16u * i);
     }
-    __device__ __forceinline__ float operator[](int e) const {
-        if constexpr (BF16) {
-            const uint32_t w = (&raw[0].x)[e >> 1];
-            return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    __device__ __forceinline__ void widen(float (&f)[EPL]) const {
+        if constexpr (KVT == kKvF32) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = __uint_as_float((&raw[e >> 2].x)[e & 3]);
+        } else if constexpr (KVT == kKvBF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = (&raw[0].x)[i];
+                f[2 * i] = bf16_lo(w);
+                f[2 * i + 1] = bf16_hi(w);
+            }
         } else {
-            return __uint_as_float((&raw[e >> 2].x)[e & 3]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int w = (int)(&raw[0].x)[i];
+                typedef float f2_t __attribute__((ext_vector_type(2)));
+                f2_t lo, hi;
+                if constexpr (KVT == kKvE4M3) {
+                    lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+                    hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+                } else {
+                    lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+                    hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+                }
+                f[4 * i] = lo.x; f[4 * i + 1] = lo.y; f[4 * i + 2] = hi.x; f[4 * i + 3] = hi.y;
+            }
         }
     }
 };
@@ -63,14 +91,14 @@ __device__ __forceinline__ float dpp(float x) {
                                          0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of G lanes (G = 8, 16, 32 or 64); every lane of a group
+// Sum over aligned groups of G lanes (G = 4, 8, 16, 32 or 64); every lane of a group
 // ends with the same value (each butterfly step is symmetric).
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-    static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group size");
+    static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
     x += dpp<kDppQuadXor1>(x);
     x += dpp<kDppQuadXor2>(x);
-    x += dpp<kDppRowHalfMirror>(x);
+    if constexpr (G >= 8) x += dpp<kDppRowHalfMirror>(x);
     if constexpr (G >= 16) x += dpp<kDppRowMirror>(x);
     if constexpr (G >= 32) x += __shfl_xor(x, 16, 64);
     if constexpr (G >= 64) x += __shfl_xor(x, 32, 64);

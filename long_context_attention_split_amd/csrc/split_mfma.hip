@@ -343,8 +343,8 @@ void split_mfma_kernel(SplitArgs a) {
     }
 }
 
-bool split_mfma_supported(int d, bool kv_bf16, int group) {
-    return kv_bf16 && group >= 2 && group <= 16 && (d == 64 || d == 128);
+bool split_mfma_supported(int d, int kv_type, int group) {
+    return kv_type == kKvBF16 && group >= 2 && group <= 16 && (d == 64 || d == 128);
 }
 
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {

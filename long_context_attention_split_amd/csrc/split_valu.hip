@@ -17,10 +17,12 @@
 // without first multiplying the old output back by the old sum, which is only right
 // when the whole sequence fits in one block.)
 //
-// Lane layout: a key row of d elements is spread over G = d/8 lanes, each holding 8
-// consecutive elements (one 16-byte load for bf16, two for fp32).  A wave therefore
-// covers 64/G keys per load instruction; the q.k dot product is 8 FMAs per lane
-// followed by a log2(G)-step DPP butterfly inside the lane group.  Each lane group
+// Lane layout: a key row of d elements is spread over G = d/EPL lanes, each holding
+// EPL consecutive elements (8 for fp32 and bf16, 16 for FP8: one 16-byte load, two
+// for fp32).  A wave therefore covers 64/G keys per load instruction; the q.k dot
+// product is EPL FMAs per lane followed by a log2(G)-step DPP butterfly inside the
+// lane group.  FP8 K/V carry a dequantisation scale per (b, kv head): the K scale
+// is folded into q, the V scale into the chunk's output.  Each lane group
 // runs its own online softmax over the keys it sees (no cross-group traffic in the
 // loop); the 4*64/G group states of a work-group are merged through LDS at the end.
 //
@@ -40,12 +42,14 @@ namespace tad {
 // UK: keys per lane group per tile (K and V tiles of UK*16 bytes per lane for bf16).
 // PF: software pipelining -- the next tile's loads are issued before the current
 // tile is consumed (two register tiles, alternating).
-template <int D, bool BF16, int POLICY, int UK = 16 / (BF16 ? 2 : 4), bool PF = false>
+// KVT: element type of K and V (kKvF32, kKvBF16, kKvE4M3, kKvE5M2).
+template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PF = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
-    constexpr int EPL = 8;                       // elements per lane per key
+    using Row = RowChunk<KVT, POLICY>;
+    constexpr int EPL = Row::EPL;                // elements per lane per key
     constexpr int G = D / EPL;                   // lanes per key row
     constexpr int KPW = 64 / G;                  // keys per wave load instruction
-    constexpr int ELEM = BF16 ? 2 : 4;
+    constexpr int ELEM = KVT == kKvF32 ? 4 : (KVT == kKvBF16 ? 2 : 1);
     constexpr int U = UK;                        // keys per lane group per tile
     constexpr int T = KPW * U;                   // keys per wave tile
     constexpr int NW = kSplitThreads / 64;       // waves per work-group
@@ -92,23 +96,30 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)n * krow);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)n * vrow);
 
-    // ---- this lane's 8 query elements, pre-scaled into base-2 units.
+    // ---- this lane's EPL query elements, pre-scaled into base-2 units (and by the
+    // K dequantisation scale, which multiplies every score of this KV head).
     float qv[EPL];
     {
+        const float qs = a.qscale * (a.k_scale ? a.k_scale[b * a.Hkv + kvh] : 1.f);
         const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + sub * EPL;
-        if (a.q_bf16) {
-            const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qv[2 * i] = bf16_lo(ws[i]) * a.qscale;
-                qv[2 * i + 1] = bf16_hi(ws[i]) * a.qscale;
+        for (int c8 = 0; c8 < EPL / 8; ++c8) {
+            if (a.q_bf16) {
+                const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff + 8 * c8);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qv[8 * c8 + 2 * i] = bf16_lo(ws[i]) * qs;
+                    qv[8 * c8 + 2 * i + 1] = bf16_hi(ws[i]) * qs;
+                }
+            } else {
+                const float4 *qp = (const float4 *)((const float *)a.q + qoff + 8 * c8);
+                const float4 x0 = qp[0], x1 = qp[1];
+                qv[8 * c8 + 0] = x0.x * qs; qv[8 * c8 + 1] = x0.y * qs;
+                qv[8 * c8 + 2] = x0.z * qs; qv[8 * c8 + 3] = x0.w * qs;
+                qv[8 * c8 + 4] = x1.x * qs; qv[8 * c8 + 5] = x1.y * qs;
+                qv[8 * c8 + 6] = x1.z * qs; qv[8 * c8 + 7] = x1.w * qs;
             }
-        } else {
-            const float4 *qp = (const float4 *)((const float *)a.q + qoff);
-            const float4 x0 = qp[0], x1 = qp[1];
-            qv[0] = x0.x * a.qscale; qv[1] = x0.y * a.qscale; qv[2] = x0.z * a.qscale; qv[3] = x0.w * a.qscale;
-            qv[4] = x1.x * a.qscale; qv[5] = x1.y * a.qscale; qv[6] = x1.z * a.qscale; qv[7] = x1.w * a.qscale;
         }
     }
     // ALiBi in base-2 units: bias of key j is slope*log2e*(j - (L-1)); j - (L-1) is an
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
     const uint32_t lane_off = (uint32_t)(sub * EPL * ELEM);
-    using Tile = Row8<BF16, POLICY>[U];
+    using Tile = Row[U];
     auto load_tile = [&](Tile &kk, Tile &vv, int t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) kk[u].load(kr, (uint32_t)(t0 + u * KPW + grp) * krow + lane_off);
@@ -134,9 +145,11 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
         float sc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            float kf[EPL];
+            kk[u].widen(kf);
             float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc = fmaf(qv[e], kk[u][e], acc);
+            for (int e = 0; e < EPL; ++e) acc = fmaf(qv[e], kf[e], acc);
             sc[u] = group_sum<G>(acc);
         }
         if (alibi) {
@@ -162,8 +175,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
         for (int u = 0; u < U; ++u) {
             const float p = exp2_fast(sc[u] - m_use);
             l += p;
+            float vf[EPL];
+            vv[u].widen(vf);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vv[u][e], o[e]);
+            for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
         }
         m = m_new;
     };
@@ -206,12 +221,14 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     for (int i = 0; i < SLOTS; ++i) M = fmaxf(M, lds_m[i]);
     const float Mu = (M == kNegInf) ? 0.f : M;
     const int64_t r = ((int64_t)b * a.Hq + h) * S + s;
+    const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // V dequantisation
     // Partials are written through to the device coherence point when this kernel also
     // merges (fused), so the merging work-group can read them without cache maintenance.
     for (int e = threadIdx.x; e < D; e += kSplitThreads) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_o[i][e], acc);
+        acc *= vsc;
         if (a.fused) store_partial(&a.ws_o[r * D + e], acc);
         else a.ws_o[r * D + e] = acc;
     }
@@ -245,7 +262,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     }
 }
 
-template <int D, bool BF16>
+template <int D, int KVT>
 static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
     int64_t grid;
     if (a.group == 1) {
@@ -256,18 +273,29 @@ static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
     }
     if (grid <= 0) return hipSuccess;
     if (a.group == 1)
-        hipLaunchKernelGGL((split_valu_kernel<D, BF16, kPolicyNT>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((split_valu_kernel<D, BF16, kPolicyDefault>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_split_valu(const SplitArgs &a, int d, bool kv_bf16, hipStream_t st) {
+template <int D>
+static hipError_t launch_d(const SplitArgs &a, hipStream_t st) {
+    switch (a.kv_type) {
+        case kKvF32: return launch_t<D, kKvF32>(a, st);
+        case kKvBF16: return launch_t<D, kKvBF16>(a, st);
+        case kKvE4M3: return launch_t<D, kKvE4M3>(a, st);
+        case kKvE5M2: return launch_t<D, kKvE5M2>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t st) {
     switch (d) {
-        case 64: return kv_bf16 ? launch_t<64, true>(a, st) : launch_t<64, false>(a, st);
-        case 128: return kv_bf16 ? launch_t<128, true>(a, st) : launch_t<128, false>(a, st);
-        case 256: return kv_bf16 ? launch_t<256, true>(a, st) : launch_t<256, false>(a, st);
-        case 512: return kv_bf16 ? launch_t<512, true>(a, st) : launch_t<512, false>(a, st);
+        case 64: return launch_d<64>(a, st);
+        case 128: return launch_d<128>(a, st);
+        case 256: return launch_d<256>(a, st);
+        case 512: return launch_d<512>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -11,6 +11,7 @@
 #include <string>
 
 #include "tad.h"
+#include "device_util.h"
 #include "tad_internal.h"
 
 namespace {
@@ -32,7 +33,11 @@ int ok() {
     return TAD_OK;
 }
 
-int elem_size(int32_t dtype) { return dtype == TAD_BF16 ? 2 : 4; }
+int elem_size(int32_t dtype) {
+    return dtype == TAD_F32 ? 4 : (dtype == TAD_BF16 ? 2 : 1);
+}
+
+bool is_fp8(int32_t dtype) { return dtype == TAD_FP8_E4M3 || dtype == TAD_FP8_E5M2; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -43,6 +48,7 @@ struct Problem {
     int64_t sqb = 0, sqh = 0;
     int64_t skb = 0, skh = 0, skj = 0;
     int64_t svb = 0, svh = 0, svj = 0;
+    const float *k_scale = nullptr, *v_scale = nullptr;
 };
 
 // q or out: [B, H, d] or [B, H, 1, d].
@@ -83,8 +89,10 @@ int parse_kv(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int6
         return fail(TAD_EINVAL, "%s: ndim must be 3 or 4 (got %d)", name, t->ndim);
     }
     if (*B < 0 || *H < 1 || *L < 0 || *d < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
-    if (t->dtype != TAD_F32 && t->dtype != TAD_BF16)
-        return fail(TAD_EDTYPE, "%s: dtype must be TAD_F32 or TAD_BF16", name);
+    if (t->dtype != TAD_F32 && t->dtype != TAD_BF16 && !is_fp8(t->dtype))
+        return fail(TAD_EDTYPE, "%s: dtype must be TAD_F32, TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2", name);
+    if (t->scale && !is_fp8(t->dtype))
+        return fail(TAD_EINVAL, "%s: a dequantisation scale is only allowed for FP8 tensors", name);
     const int64_t es = elem_size(t->dtype);
     if (!aligned16(t->data) || (*sb * es) % 16 || (*sh * es) % 16 || (*sj * es) % 16)
         return fail(TAD_ELAYOUT, "%s: rows must start on 16-byte boundaries", name);
@@ -97,6 +105,7 @@ int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
     int64_t Bq, Hq, dq;
     if ((rc = parse_query_like(q, "q", &Bq, &Hq, &dq, &P->sqb, &P->sqh))) return rc;
     if (q->dtype != TAD_F32 && q->dtype != TAD_BF16) return fail(TAD_EDTYPE, "q: dtype must be TAD_F32 or TAD_BF16");
+    if (q->scale) return fail(TAD_EINVAL, "q: scale must be NULL");
     const int64_t qes = elem_size(q->dtype);
     if (!aligned16(q->data) || (P->sqb * qes) % 16 || (P->sqh * qes) % 16)
         return fail(TAD_ELAYOUT, "q: rows must start on 16-byte boundaries");
@@ -114,6 +123,7 @@ int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
         return fail(TAD_EUNSUPPORTED, "sizes too large");
     P->B = Bq; P->Hq = Hq; P->Hkv = Hk; P->Lmax = Lk; P->d = dq;
     P->q_dtype = q->dtype; P->kv_dtype = k->dtype;
+    P->k_scale = k->scale; P->v_scale = v->scale;
     return TAD_OK;
 }
 
@@ -122,6 +132,7 @@ int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *so
     int64_t B, H, d;
     if ((rc = parse_query_like(out, "out", &B, &H, &d, sob, soh))) return rc;
     if (out->dtype != TAD_F32) return fail(TAD_EDTYPE, "out: dtype must be TAD_F32");
+    if (out->scale) return fail(TAD_EINVAL, "out: scale must be NULL");
     if (B != P.B || H != P.Hq || d != P.d) return fail(TAD_EINVAL, "out: shape must be [B, Hq, d] of the inputs");
     return TAD_OK;
 }
@@ -193,6 +204,10 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     tad::SplitArgs a;
     a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.q_bf16 = P.q_dtype == TAD_BF16;
     a.k = k->data; a.v = v->data;
+    a.kv_type = P.kv_dtype == TAD_F32 ? tad::kKvF32
+              : P.kv_dtype == TAD_BF16 ? tad::kKvBF16
+              : P.kv_dtype == TAD_FP8_E4M3 ? tad::kKvE4M3 : tad::kKvE5M2;
+    a.k_scale = P.k_scale; a.v_scale = P.v_scale;
     a.skb = P.skb; a.skh = P.skh; a.skj = P.skj;
     a.svb = P.svb; a.svh = P.svh; a.svj = P.svj;
     a.seq_lens = seq_lens; a.slopes = slopes;
@@ -204,10 +219,9 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     a.cnt = w.cnt;
     a.out = out ? (float *)out->data : nullptr;
     a.sob = sob; a.soh = soh;
-    const bool bf16 = P.kv_dtype == TAD_BF16;
-    hipError_t e = tad::split_mfma_supported((int)P.d, bf16, a.group)
+    hipError_t e = tad::split_mfma_supported((int)P.d, a.kv_type, a.group)
                        ? tad::launch_split_mfma(a, (int)P.d, stream)
-                       : tad::launch_split_valu(a, (int)P.d, bf16, stream);
+                       : tad::launch_split_valu(a, (int)P.d, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "split kernel launch: %s", hipGetErrorString(e));
     return TAD_OK;
 }

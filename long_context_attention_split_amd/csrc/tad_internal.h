@@ -13,6 +13,8 @@ struct SplitArgs {
     int64_t sqb, sqh;       // q element strides
     int32_t q_bf16;         // q dtype: 1 = bf16, 0 = fp32
     const void *k, *v;      // [B, Hkv, Lmax, d], innermost contiguous
+    int32_t kv_type;        // kKvF32, kKvBF16, kKvE4M3, kKvE5M2 (device_util.h)
+    const float *k_scale, *v_scale;  // [B * Hkv] dequantisation scales, or null (1)
     int64_t skb, skh, skj;  // k element strides
     int64_t svb, svh, svj;  // v element strides
     const int32_t *seq_lens;  // [B] or null
@@ -82,8 +84,8 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
 }
 
 // Launchers (defined next to their kernels).  Return the hipError_t of the launch.
-hipError_t launch_split_valu(const SplitArgs &a, int d, bool kv_bf16, hipStream_t s);
-bool split_mfma_supported(int d, bool kv_bf16, int group);
+hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t s);
+bool split_mfma_supported(int d, int kv_type, int group);
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);

@@ -104,6 +104,35 @@ def test_split_rejects_bad_arguments(lib, mutate, code):
     assert lib.tad_last_error() != ""
 
 
+def test_fp8_and_scale_rules(lib):
+    """FP8 is accepted for k/v (with or without scales), not for q or out; a scale on a
+    non-FP8 tensor is refused."""
+    so = lib.load()
+    a = good()
+    a["k"] = desc([2, 2, 100, 128], tad.TAD_FP8_E4M3)
+    a["v"] = desc([2, 2, 100, 128], tad.TAD_FP8_E4M3)
+    a["k"].scale = FAKE
+    a["v"].scale = FAKE
+    assert call_split(so, a, ws_bytes=0) == tad.TAD_EWORKSPACE        # validated up to the workspace
+    a["v"] = desc([2, 2, 100, 128], tad.TAD_FP8_E5M2)
+    assert call_split(so, a) == tad.TAD_EDTYPE                        # k and v formats differ
+    b = good()
+    b["q"] = desc([2, 8, 128], tad.TAD_FP8_E4M3)
+    assert call_split(so, b) == tad.TAD_EDTYPE
+    c = good()
+    c["k"].scale = FAKE
+    assert call_split(so, c) == tad.TAD_EINVAL
+    d = good()
+    d["out"] = desc([2, 8, 128], tad.TAD_FP8_E4M3)
+    assert call_decode_ws(so, d) == tad.TAD_EDTYPE
+    # FP8 rows of 64 elements are 64 bytes: still 16-byte aligned
+    e = good(d=64)
+    e["k"] = desc([2, 2, 100, 64], tad.TAD_FP8_E5M2)
+    e["v"] = desc([2, 2, 100, 64], tad.TAD_FP8_E5M2)
+    e["q"] = desc([2, 8, 64], tad.TAD_F32)
+    assert call_split(so, e, ws_bytes=0) == tad.TAD_EWORKSPACE
+
+
 def test_split_rejects_bad_splits_and_workspace(lib):
     so = lib.load()
     a = good()

@@ -49,7 +49,7 @@ def assert_parity(out, ref, kv_dtype, vmax, what=""):
 
 def to_dev(c):
     g = dict(c)
-    for key in ("q", "k", "v", "seq_lens", "slopes"):
+    for key in ("q", "k", "v", "seq_lens", "slopes", "k_scale", "v_scale"):
         if g.get(key) is not None:
             g[key] = g[key].to(DEV)
     return g
@@ -57,9 +57,19 @@ def to_dev(c):
 
 def gpu_decode(lib, c, n_splits):
     g = to_dev(c)
-    out = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], n_splits)
+    out = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], n_splits,
+                     k_scale=g.get("k_scale"), v_scale=g.get("v_scale"))
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def vmax_real(c):
+    """max |V| over valid keys, in real (dequantised) units."""
+    v = torch.from_numpy(oracle.widen(c["v"]))
+    if c.get("v_scale") is not None:
+        v = v * c["v_scale"].double()[:, :, None, None]
+    v = torch.nan_to_num(v, nan=0.0)
+    return vmax_valid(v, c["seq_lens"])
 
 
 def run_case(lib, seed, B, Hq, Hkv, L, d, kv=torch.bfloat16, q_dtype=torch.float32, seq_lens=None,
@@ -68,9 +78,10 @@ def run_case(lib, seed, B, Hq, Hkv, L, d, kv=torch.bfloat16, q_dtype=torch.float
          (seed, B, Hq, Hkv, L, d, kv, q_dtype, seq_lens, alibi, n_splits))
     c = W.random_case(seed, B, Hq, Hkv, L, d, q_dtype=q_dtype, kv_dtype=kv, seq_lens=seq_lens,
                       alibi=alibi, k_scale=k_scale)
-    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"])
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
     out = gpu_decode(lib, c, n_splits)
-    assert_parity(out, ref, kv, vmax_valid(c["v"], c["seq_lens"]), "seed=%d" % seed)
+    assert_parity(out, ref, kv, vmax_real(c), "seed=%d" % seed)
     return out, ref, c
 
 
@@ -158,6 +169,27 @@ def test_entry_points_agree(lib):
     again = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S)
     torch.cuda.synchronize()
     assert torch.equal(a, out_b) and torch.equal(a, out_c) and torch.equal(a, again)
+
+
+FP8 = [torch.float8_e4m3fn, torch.float8_e5m2]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("kv", FP8)
+def test_fp8_head_dims(lib, d, kv):
+    """OCP FP8 K/V with per-(b, head) dequantisation scales; several tiles and a ragged
+    tail per chunk."""
+    run_case(lib, 300 + d, 2, 2, 2, 1000, d, kv=kv, n_splits=3)
+
+
+@pytest.mark.parametrize("kv", FP8)
+def test_fp8_ragged_gqa_alibi(lib, kv):
+    """FP8 with NaN bit patterns past each length, grouped heads and ALiBi."""
+    run_case(lib, 310, 3, 8, 2, 3000, 128, kv=kv, seq_lens=[3000, 1, 2222], alibi=True, n_splits=4)
+
+
+def test_fp8_long_context(lib):
+    run_case(lib, 320, 1, 8, 8, 65536, 128, kv=torch.float8_e4m3fn, n_splits=0, k_scale=4.0)
 
 
 def test_workspace_reuse_and_clear(lib):

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from test_parity_gpu import assert_parity, note, vmax_valid
+from test_parity_gpu import assert_parity, note, vmax_real
 
 pytestmark = pytest.mark.gpu
 
@@ -28,15 +28,18 @@ def run_workload(lib, wid):
     v = c["v"].to(DEV)
     sl = c["seq_lens"].to(DEV) if c["seq_lens"] is not None else None
     sp = c["slopes"].to(DEV) if c["slopes"] is not None else None
+    ks = c["k_scale"].to(DEV) if c["k_scale"] is not None else None
+    vs = c["v_scale"].to(DEV) if c["v_scale"] is not None else None
     S = lib.resolve_splits(q, k, c["n_splits"])
     note("workload %d: n_splits=%d" % (wid, S))
-    out = lib.decode(q, k, v, sl, sp, S)
+    out = lib.decode(q, k, v, sl, sp, S, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     del q, k, v
     torch.cuda.empty_cache()
-    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"])
-    assert_parity(out, ref, w.kv_dtype, vmax_valid(c["v"], c["seq_lens"]), "workload %d" % wid)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
+    assert_parity(out, ref, w.kv_dtype, vmax_real(c), "workload %d" % wid)
     return out, ref, c
 
 
@@ -55,6 +58,10 @@ def test_workload3_gqa_ragged(lib):
 
 def test_workload4_alibi(lib):
     run_workload(lib, 4)
+
+
+def test_workload6_fp8_mha(lib):
+    run_workload(lib, 6)
 
 
 def test_workload5_million_keys(lib):
