@@ -50,8 +50,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_decode_f64.restype = i32
-        lib.oracle_decode_f64.argtypes = [vp, i32, i64, i64, vp, vp, i32, i64, i64, i64, i64, i64, i64,
-                                          i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32]
+        lib.oracle_decode_f64.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, i64, i64, i64, i64, i64,
+                                          i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32]
         lib.oracle_alibi_bias.restype = ctypes.c_double
         lib.oracle_alibi_bias.argtypes = [i64, i64, ctypes.c_double]
         lib.oracle_fp8_e4m3.restype = ctypes.c_double
@@ -98,11 +98,12 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
                n_threads: Optional[int] = None, k_scale=None, v_scale=None) -> np.ndarray:
     """Oracle output (float64).
 
-    q [B, Hq, d]; k, v [B, Hkv, Lmax, d] (fp32, bf16 or fp8 torch tensors, or numpy
-    float32 / uint16 bf16 bits); seq_lens int32 [B] or None; slopes fp32 [Hq] or None;
-    k_scale, v_scale fp32 [B, Hkv] dequantisation scales (real = stored * scale) or None.
-    ``rows``: flat b*Hq+h indices to compute (result [len(rows), d]); None for all
-    (result [B, Hq, d]).
+    q [B, Hq, d] or [B, Hq, nq, d] (nq query tokens, the last nq positions of each row,
+    causal among themselves); k, v [B, Hkv, Lmax, d] (fp32, bf16 or fp8 torch tensors,
+    or numpy float32 / uint16 bf16 bits); seq_lens int32 [B] or None; slopes fp32 [Hq]
+    or None; k_scale, v_scale fp32 [B, Hkv] dequantisation scales (real = stored *
+    scale) or None.  ``rows``: flat (b*Hq+h)*nq+t indices to compute (result
+    [len(rows), d]); None for all (result shaped like q).
     """
     lib = _load()
     qn, qt = _as_np(q)
@@ -110,7 +111,10 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
     vn, vt = _as_np(v)
     if kt != vt:
         raise TypeError("k and v must share a dtype")
-    B, Hq, d = qn.shape
+    multi = qn.ndim == 4
+    if not multi:
+        qn = qn[:, :, None, :]
+    B, Hq, nq, d = qn.shape
     Bk, Hkv, Lmax, dk = kn.shape
     if Bk != B or dk != d or vn.shape != kn.shape:
         raise ValueError("shape mismatch")
@@ -131,7 +135,7 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
         vsc = np.ascontiguousarray(np.asarray(v_scale.cpu() if hasattr(v_scale, "cpu") else v_scale,
                                               dtype=np.float32)).reshape(-1)
     rw = None
-    n_rows = B * Hq
+    n_rows = B * Hq * nq
     if rows is not None:
         rw = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
         n_rows = int(rw.size)
@@ -139,13 +143,15 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
     if n_threads is None:
         n_threads = len(os.sched_getaffinity(0))
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
-    rc = lib.oracle_decode_f64(ptr(qn), qt, sq[0], sq[1], ptr(kn), ptr(vn), kt,
+    rc = lib.oracle_decode_f64(ptr(qn), qt, sq[0], sq[1], sq[2], nq, ptr(kn), ptr(vn), kt,
                                sk[0], sk[1], sk[2], sv[0], sv[1], sv[2],
                                B, Hq, Hkv, Lmax, d, ptr(sl), ptr(sp), ptr(ksc), ptr(vsc), ptr(rw), n_rows,
                                ptr(out), int(n_threads))
     if rc != 0:
         raise RuntimeError("oracle_decode_f64 failed (%d)" % rc)
-    return out if rows is not None else out.reshape(B, Hq, d)
+    if rows is not None:
+        return out
+    return out.reshape(B, Hq, nq, d) if multi else out.reshape(B, Hq, d)
 
 
 def alibi_bias(L: int, j: int, slope: float) -> float:

@@ -6,14 +6,18 @@
  * cpu_baseline leg of bench.py may load it.  It includes no header of the product
  * library and the product library never links, includes or calls it.
  *
- * What it computes, for every batch row b and query head h (one query token):
+ * What it computes, for every batch row b, query head h and query token t of nq
+ * (nq = 1 is single-token decode):
  *
  *   L    = seq_lens[b] clamped to [0, Lmax]           (Lmax when seq_lens is NULL)
+ *   the nq query tokens are the row's last nq positions; token t sits at position
+ *   L - nq + t and sees the keys up to it (causal among the new tokens), i.e. it is
+ *   single-token decode over the first Lt = clamp(L - nq + t + 1, 0, L) keys:
  *   kh   = floor(h / (Hq / Hkv))                      (contiguous query-head groups)
- *   s_j  = d^(-1/2) * sum_i q[b,h,i] * k[b,kh,j,i] + beta_j,          0 <= j < L
- *   beta_j = -slope_h * (L - 1 - j)   with ALiBi slopes, else 0
- *   out[b,h,e] = sum_j exp(s_j - max_j s_j) * v[b,kh,j,e] / sum_j exp(s_j - max_j s_j)
- *   L == 0  ->  out[b,h,:] = 0   (softmax over no keys is undefined; our convention)
+ *   s_j  = d^(-1/2) * sum_i q[b,h,t,i] * k[b,kh,j,i] + beta_j,        0 <= j < Lt
+ *   beta_j = -slope_h * (Lt - 1 - j)  with ALiBi slopes, else 0 (query position minus j)
+ *   out[b,h,t,e] = sum_j exp(s_j - max_j s_j) v[b,kh,j,e] / sum_j exp(s_j - max_j s_j)
+ *   Lt == 0 ->  out[b,h,t,:] = 0  (softmax over no keys is undefined; our convention)
  *
  * Sources:
  *   - "Tree Attention Decoding" (tree_attn_decode.py gist), function regular_decode:
@@ -25,6 +29,9 @@
  *   - "Flash Aandacht: Revolutie in Transformer Efficientie", section on the
  *     mathematics, softmax decomposition: subtracting the maximum score leaves the
  *     softmax unchanged (it only keeps exp() in range).
+ *   - Several query tokens: the gist's einsum allows more than one query row (index i);
+ *     the causal reading (each new token sees the cache up to its own position) is ours,
+ *     the usual one for verifying several drafted tokens at once.
  *
  * FP8 keys and values (OCP E4M3 "fn" and E5M2 formats) carry a dequantisation scale per
  * (batch row, KV head): the stored value times the scale is the real value; the scores
@@ -95,7 +102,8 @@ double oracle_alibi_bias(int64_t L, int64_t j, double slope)
 typedef struct {
     const void *q;
     int q_dtype;
-    int64_t sqb, sqh;            /* q element strides for b, h (innermost stride 1) */
+    int64_t sqb, sqh, sqt;       /* q element strides for b, h, token (innermost stride 1) */
+    int nq;                      /* query tokens per (b, h) */
     const void *k, *v;
     int kv_dtype;
     int64_t skb, skh, skj;       /* k element strides for b, kv-head, key */
@@ -104,14 +112,14 @@ typedef struct {
     const int32_t *seq_lens;     /* [B] or NULL */
     const float *slopes;         /* [Hq] or NULL */
     const float *k_scale, *v_scale; /* [B * Hkv] dequantisation scales, or NULL (= 1) */
-    const int32_t *rows;         /* flat b*Hq+h indices to compute, or NULL for all */
+    const int32_t *rows;         /* flat (b*Hq+h)*nq+t indices to compute, or NULL for all */
     int n_rows;
     double *out;                 /* [n_rows, d] */
     int n_threads;
 } oracle_job;
 
-/* One (b, h) row of the definition above; s is scratch of length >= Lmax. */
-static void decode_row(const oracle_job *J, int b, int h, double *s, double *out)
+/* One (b, h, t) row of the definition above; s is scratch of length >= Lmax. */
+static void decode_row(const oracle_job *J, int b, int h, int t, double *s, double *out)
 {
     const int d = J->d;
     int64_t L = J->Lmax;
@@ -120,6 +128,8 @@ static void decode_row(const oracle_job *J, int b, int h, double *s, double *out
         if (L < 0) L = 0;
         if (L > J->Lmax) L = J->Lmax;
     }
+    L = L - J->nq + t + 1;               /* keys up to this token's own position */
+    if (L < 0) L = 0;
     for (int e = 0; e < d; ++e) out[e] = 0.0;
     if (L == 0) return;
 
@@ -127,7 +137,7 @@ static void decode_row(const oracle_job *J, int b, int h, double *s, double *out
     const double scale = 1.0 / sqrt((double)d);
     const double ks = J->k_scale ? (double)J->k_scale[b * J->Hkv + kh] : 1.0;
     const double vs = J->v_scale ? (double)J->v_scale[b * J->Hkv + kh] : 1.0;
-    const int64_t qoff = (int64_t)b * J->sqb + (int64_t)h * J->sqh;
+    const int64_t qoff = (int64_t)b * J->sqb + (int64_t)h * J->sqh + (int64_t)t * J->sqt;
     const int64_t koff = (int64_t)b * J->skb + (int64_t)kh * J->skh;
     const int64_t voff = (int64_t)b * J->svb + (int64_t)kh * J->svh;
 
@@ -167,8 +177,9 @@ static void *worker(void *p)
     if (!s) { a->fail = 1; return NULL; }
     for (int r = a->tid; r < J->n_rows; r += J->n_threads) {
         int flat = J->rows ? J->rows[r] : r;
-        int b = flat / J->Hq, h = flat % J->Hq;
-        decode_row(J, b, h, s, J->out + (int64_t)r * J->d);
+        int t = flat % J->nq, bh = flat / J->nq;
+        int b = bh / J->Hq, h = bh % J->Hq;
+        decode_row(J, b, h, t, s, J->out + (int64_t)r * J->d);
     }
     free(s);
     return NULL;
@@ -176,16 +187,16 @@ static void *worker(void *p)
 
 /*
  * Compute the decode output for the requested rows.
- *   q      : [B, Hq, d] with element strides (sqb, sqh, 1); dtype OR_F32 or OR_BF16
+ *   q      : [B, Hq, nq, d] with element strides (sqb, sqh, sqt, 1); dtype OR_F32 or OR_BF16
  *   k, v   : [B, Hkv, Lmax, d] with element strides (s?b, s?h, s?j, 1); same dtype
  *            (OR_F32, OR_BF16, OR_FP8_E4M3, OR_FP8_E5M2)
  *   k_scale, v_scale: [B * Hkv] scales (real = stored * scale), or NULL
- *   rows   : flat indices b*Hq + h to compute (n_rows of them), or NULL for all B*Hq
+ *   rows   : flat indices (b*Hq + h)*nq + t to compute (n_rows of them), or NULL for all
  *   out    : [n_rows, d] doubles, row r for rows[r]
  *   n_threads: POSIX threads to use (>= 1)
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int oracle_decode_f64(const void *q, int q_dtype, int64_t sqb, int64_t sqh,
+int oracle_decode_f64(const void *q, int q_dtype, int64_t sqb, int64_t sqh, int64_t sqt, int nq,
                       const void *k, const void *v, int kv_dtype,
                       int64_t skb, int64_t skh, int64_t skj,
                       int64_t svb, int64_t svh, int64_t svj,
@@ -194,15 +205,15 @@ int oracle_decode_f64(const void *q, int q_dtype, int64_t sqb, int64_t sqh,
                       const float *k_scale, const float *v_scale,
                       const int32_t *rows, int n_rows, double *out, int n_threads)
 {
-    if (!q || !k || !v || !out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lmax < 0 || d <= 0)
+    if (!q || !k || !v || !out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lmax < 0 || d <= 0 || nq < 1)
         return -1;
     if ((q_dtype != OR_F32 && q_dtype != OR_BF16) || kv_dtype < OR_F32 || kv_dtype > OR_FP8_E5M2)
         return -1;
-    oracle_job J = {q, q_dtype, sqb, sqh, k, v, kv_dtype, skb, skh, skj, svb, svh, svj,
+    oracle_job J = {q, q_dtype, sqb, sqh, sqt, nq, k, v, kv_dtype, skb, skh, skj, svb, svh, svj,
                     B, Hq, Hkv, Lmax, d, seq_lens, slopes, k_scale, v_scale,
-                    rows, rows ? n_rows : B * Hq, out, n_threads < 1 ? 1 : n_threads};
+                    rows, rows ? n_rows : B * Hq * nq, out, n_threads < 1 ? 1 : n_threads};
     for (int r = 0; rows && r < n_rows; ++r)
-        if (rows[r] < 0 || rows[r] >= B * Hq) return -1;
+        if (rows[r] < 0 || rows[r] >= B * Hq * nq) return -1;
     if (J.n_threads > J.n_rows) J.n_threads = J.n_rows > 0 ? J.n_rows : 1;
 
     pthread_t th[256];

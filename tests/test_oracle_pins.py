@@ -383,3 +383,57 @@ def test_fp8_scaled_equals_dequantised_fp32(tdt):
     np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
     # the scales matter: without them the output differs
     assert not np.allclose(oracle.decode_f64(c["q"], c["k"], c["v"]), out)
+
+
+# ----------------------------------------------------------------------------- several query tokens
+
+def multi_case(seed, B, Hq, Hkv, nq, L, d, lens=None, alibi=False):
+    c = W.random_case(seed, B, Hq, Hkv, L, d, seq_lens=lens, alibi=alibi)
+    c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(seed + 9))
+    return c
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+def test_multi_token_matches_sdpa_with_causal_mask(alibi):
+    """nq new tokens at the last nq positions, each seeing the keys up to its own
+    position: torch SDPA (fp64) with an explicit causal mask (and the ALiBi term
+    -slope * (position - j)) over those query positions."""
+    B, Hq, Hkv, nq, L, d = 2, 4, 2, 5, 40, 16
+    lens = [40, 23]
+    c = multi_case(21, B, Hq, Hkv, nq, L, d, lens, alibi)
+    out = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"])
+    assert out.shape == (B, Hq, nq, d)
+    q = torch.from_numpy(f64(c["q"]))
+    k = torch.from_numpy(np.nan_to_num(f64(c["k"]))).repeat_interleave(Hq // Hkv, dim=1)
+    v = torch.from_numpy(np.nan_to_num(f64(c["v"]))).repeat_interleave(Hq // Hkv, dim=1)
+    mask = torch.full((B, Hq, nq, L), -math.inf, dtype=torch.float64)
+    for b, Lb in enumerate(lens):
+        for t in range(nq):
+            pos = Lb - nq + t
+            j = torch.arange(pos + 1, dtype=torch.float64)
+            bias = torch.zeros(Hq, pos + 1, dtype=torch.float64)
+            if alibi:
+                bias = -c["slopes"].double().view(Hq, 1) * (pos - j).view(1, -1)
+            mask[b, :, t, :pos + 1] = bias
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_multi_token_last_token_is_single_token_decode():
+    """The last of nq tokens sees every key: it equals single-token decode with that q;
+    a single token given in 4-D form equals the 3-D form."""
+    c = multi_case(22, 2, 4, 4, 3, 50, 32, [50, 31])
+    out = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"])
+    single = oracle.decode_f64(c["q"][:, :, -1].contiguous(), c["k"], c["v"], seq_lens=c["seq_lens"])
+    np.testing.assert_array_equal(out[:, :, -1], single)
+    one = oracle.decode_f64(c["q"][:, :, :1].contiguous(), c["k"], c["v"], seq_lens=c["seq_lens"])
+    np.testing.assert_array_equal(one[:, :, 0], oracle.decode_f64(c["q"][:, :, 0].contiguous(), c["k"], c["v"],
+                                                                    seq_lens=c["seq_lens"]))
+
+
+def test_multi_token_more_tokens_than_keys():
+    """Tokens whose position is before the first key see nothing: output 0."""
+    c = multi_case(23, 1, 2, 2, 6, 4, 16)
+    out = oracle.decode_f64(c["q"], c["k"], c["v"])
+    assert (out[:, :, :2] == 0).all()                    # positions -2, -1
+    assert np.isfinite(out).all() and (out[:, :, 2:] != 0).any()
