@@ -82,7 +82,7 @@ def cpu_baseline(c, cpu_seconds_target: float = 10.0):
     while passes == 0 or (total * threads < cpu_seconds_target and passes < 1000):
         t0 = time.perf_counter()
         o = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
-                              n_threads=threads)
+                              n_threads=threads, k_scale=c["k_scale"], v_scale=c["v_scale"])
         total += time.perf_counter() - t0
         passes += 1
         if out is None:
@@ -146,6 +146,8 @@ def main(argv=None) -> int:
     v = c["v"].to(dev)
     sl = c["seq_lens"].to(dev) if c["seq_lens"] is not None else None
     sp = c["slopes"].to(dev) if c["slopes"] is not None else None
+    ks = c["k_scale"].to(dev) if c["k_scale"] is not None else None
+    vs = c["v_scale"].to(dev) if c["v_scale"] is not None else None
     S = args.splits if args.splits > 0 else tad.resolve_splits(q, k, c["n_splits"])
     B, Hq, Hkv, Lmax, d = tad.shape_of(q, k)
     ws = tad.workspace(q, k, S)
@@ -158,10 +160,10 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        tad.tad_split(q, k, v, sl, sp, S, ws, stream)
+        tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
         if ev is not None:
             ev[1].record(stream)
-        tad.tad_combine(ws, B, Hq, S, d, out, stream)
+        tad.tad_combine(ws, B, Hq, 1, S, d, out, stream)
 
     for _ in range(args.warmup):
         step()

@@ -3,12 +3,15 @@
  * sequence, split into chunks that run on different compute units of one GPU, with
  * the chunks' partial results merged by the log-sum-exp rescaling rule.
  *
- * What the library computes (per batch row b and query head h, one query token):
+ * What the library computes (per batch row b, query head h and query token t):
  *
- *   out[b,h,:] = softmax_j( q[b,h,:] . k[b,kh,j,:] / sqrt(d) + beta_j ) v[b,kh,j,:]
+ *   out[b,h,t,:] = softmax_j( q[b,h,t,:] . k[b,kh,j,:] / sqrt(d) + beta_j ) v[b,kh,j,:]
  *
- * over the keys j < L_b, with kh = floor(h / (Hq / Hkv)) and beta_j the optional
- * ALiBi bias -slope_h * (L_b - 1 - j).  Sources: "Tree Attention Decoding"
+ * over the keys j < L_t, with kh = floor(h / (Hq / Hkv)) and beta_j the optional
+ * ALiBi bias -slope_h * (L_t - 1 - j).  With one query token (the usual decode
+ * step) L_t = L_b.  With nq tokens they are the row's last nq positions and token t
+ * sees the keys up to its own position: L_t = clamp(L_b - nq + t + 1, 0, L_b)
+ * (causal among the new tokens, as when several drafted tokens are verified).  Sources: "Tree Attention Decoding"
  * (tree_attn_decode.py gist), functions regular_decode (the definition) and
  * tree_attn_decode (chunk the keys, keep a local max, a sum of exponentials and an
  * exponential-weighted value sum per chunk, then take the global max, rescale and
@@ -24,7 +27,8 @@
  *  - Tensors are described by tad_tensor: a DEVICE pointer, a dtype, and shape and
  *    strides in ELEMENTS.  The innermost stride must be 1; every row start must be
  *    16-byte aligned (data pointer and outer strides in bytes multiples of 16).
- *  - q   : [B, Hq, d] or [B, Hq, 1, d], TAD_F32 or TAD_BF16.
+ *  - q   : [B, Hq, d] (one token) or [B, Hq, nq, d] (nq <= 256 tokens), TAD_F32 or
+ *          TAD_BF16.
  *  - k, v: [B, Hkv, Lmax, d] or [B, Lmax, d] (then Hkv = 1); same dtype (TAD_F32,
  *          TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2) and shape; any outer strides (e.g.
  *          a [B, Lmax, Hkv, d] cache viewed as [B, Hkv, Lmax, d]).  Hq must be a
@@ -32,11 +36,11 @@
  *          tensor's `scale`: device fp32 [B * Hkv], index b * Hkv + kv_head; the real
  *          value is stored * scale; NULL means 1).  `scale` must be NULL for every
  *          other tensor.
- *  - out : [B, Hq, d] or [B, Hq, 1, d], TAD_F32.
+ *  - out : like q ([B, Hq, d] or [B, Hq, nq, d]), TAD_F32.
  *  - d (head dimension) must be 64, 128, 256 or 512.
  *  - seq_lens: DEVICE int32 [B] or NULL (every row uses Lmax).  Values are clamped
  *    to [0, Lmax] on the device; keys at or beyond L_b are never read.  A row with
- *    L_b = 0 produces out = 0.
+ *    L_b = 0 produces out = 0 (so does a token whose position is before the first key).
  *  - alibi_slopes: DEVICE fp32 [Hq] or NULL (no bias).
  *  - n_splits: chunks per (b, head); <= 0 selects tad_auto_splits().  Every row is
  *    cut into contiguous chunks of one length c = ceil(Lref / n_splits), where Lref
@@ -64,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10200 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -104,18 +108,18 @@ int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device);
 
 /*
  * Bytes of device workspace tad_decode_ws / tad_split / tad_combine need for
- * B * Hq rows, n_splits chunks and head dimension d (0 if an argument is < 1).
- * Layout (each array starting at a 256-byte boundary), with r = (b * Hq + h) *
- * n_splits + s:
+ * B * Hq * nq rows, n_splits chunks and head dimension d (0 if an argument is < 1).
+ * Layout (each array starting at a 256-byte boundary), with row = (b * Hq + h) * nq
+ * + t and r = row * n_splits + s:
  *     m[r]        fp32: chunk maximum of the scores, in base-2 units (score * log2 e);
  *                 -inf for an empty chunk
  *     l[r]        fp32: sum over the chunk of 2^(score*log2 e - m[r])
  *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e]
- *     cnt[b*Hq+h] int32: arrival counters of the fused merge (see tad_decode_ws)
+ *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws)
  * m, l, o are the per-chunk (local max, denominator, numerator) of tree_attn_decode,
  * with the maximum kept in base 2.
  */
-size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t n_splits, int32_t d);
+size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t nq, int32_t n_splits, int32_t d);
 
 /*
  * Zero a workspace (all ws_bytes of it) with a small kernel on `stream` (no memset, so
@@ -133,16 +137,17 @@ int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
               void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Merge step: for each (b, h), M = max_s m, w_s = 2^(m_s - M), L = sum_s w_s l_s,
- * out = sum_s w_s o_s / L, summed in a fixed order (bit-reproducible).  Rows whose
- * chunks are all empty get out = 0.  `out` is fp32 [B, Hq, d] (or [B, Hq, 1, d]).
+ * Merge step: for each (b, h, t) row, M = max_s m, w_s = 2^(m_s - M), L = sum_s w_s
+ * l_s, out = sum_s w_s o_s / L, summed in a fixed order (bit-reproducible).  Rows
+ * whose chunks are all empty get out = 0.  `out` is fp32 [B, Hq, d] (nq = 1) or
+ * [B, Hq, nq, d].
  */
-int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t n_splits,
+int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t nq, int32_t n_splits,
                 int32_t d, tad_tensor *out, hipStream_t stream);
 
 /*
  * Split + merge with a caller-provided workspace (no allocation).  Small problems
- * (B * Hq * n_splits below the device's compute-unit count, n_splits <= 1024) run
+ * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 1024) run
  * as ONE launch: each split work-group writes its partial, and the last one of a
  * row to finish (counted in the workspace's cnt array) merges the row, then returns
  * its counter to zero.  Larger problems run the split and combine kernels back to

@@ -7,15 +7,16 @@ streams.  The functions carry the C names:
 - ``tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits, out, stream=None)``
 - ``tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits, out, ws, stream=None)``
 - ``tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream=None)``
-- ``tad_combine(ws, B, Hq, n_splits, d, out, stream=None)``
-- ``tad_auto_splits(B, Hkv, Lmax, device=-1)``, ``tad_workspace_bytes(B, Hq, n_splits, d)``
+- ``tad_combine(ws, B, Hq, nq, n_splits, d, out, stream=None)``
+- ``tad_auto_splits(B, Hkv, Lmax, device=-1)``, ``tad_workspace_bytes(B, Hq, nq, n_splits, d)``
 - ``tad_workspace_clear(ws, stream=None)``, ``tad_version()``, ``tad_last_error()``
 
 and ``decode(...)`` allocates ``out`` and the workspace with torch and calls
-``tad_decode_ws``.  Tensors: q [B, Hq, d] fp32/bf16; k, v [B, Hkv, Lmax, d]
+``tad_decode_ws``.  Tensors: q [B, Hq, d] or [B, Hq, nq, d] (nq new tokens, causal)
+fp32/bf16; k, v [B, Hkv, Lmax, d]
 fp32/bf16/float8_e4m3fn/float8_e5m2 (innermost dim contiguous; FP8 with optional
 k_scale / v_scale fp32 [B, Hkv]); seq_lens int32 [B] or None; alibi_slopes fp32
-[Hq] or None; out fp32 [B, Hq, d].  All must live on the GPU.
+[Hq] or None; out fp32 shaped like q.  All must live on the GPU.
 
 There is no fallback: if ``libtad.so`` has not been built, ``load()`` raises.
 """
@@ -67,13 +68,13 @@ def load():
     lib.tad_auto_splits.restype = i32
     lib.tad_auto_splits.argtypes = [i32, i32, i64, i32]
     lib.tad_workspace_bytes.restype = sz
-    lib.tad_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.tad_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.tad_workspace_clear.restype = ctypes.c_int
     lib.tad_workspace_clear.argtypes = [vp, sz, vp]
     lib.tad_split.restype = ctypes.c_int
     lib.tad_split.argtypes = [P, P, P, vp, vp, i32, vp, sz, vp]
     lib.tad_combine.restype = ctypes.c_int
-    lib.tad_combine.argtypes = [vp, sz, i32, i32, i32, i32, P, vp]
+    lib.tad_combine.argtypes = [vp, sz, i32, i32, i32, i32, i32, P, vp]
     lib.tad_decode_ws.restype = ctypes.c_int
     lib.tad_decode_ws.argtypes = [P, P, P, vp, vp, i32, P, vp, sz, vp]
     lib.tad_decode.restype = ctypes.c_int
@@ -150,8 +151,8 @@ def tad_auto_splits(B: int, Hkv: int, Lmax: int, device: int = -1) -> int:
     return r
 
 
-def tad_workspace_bytes(B: int, Hq: int, n_splits: int, d: int) -> int:
-    return load().tad_workspace_bytes(B, Hq, n_splits, d)
+def tad_workspace_bytes(B: int, Hq: int, nq: int, n_splits: int, d: int) -> int:
+    return load().tad_workspace_bytes(B, Hq, nq, n_splits, d)
 
 
 def tad_workspace_clear(ws, stream=None) -> int:
@@ -167,10 +168,10 @@ def tad_split(q, k, v, seq_lens, alibi_slopes, n_splits: int, ws, stream=None, k
                                 _stream(stream)))
 
 
-def tad_combine(ws, B: int, Hq: int, n_splits: int, d: int, out, stream=None) -> int:
+def tad_combine(ws, B: int, Hq: int, nq: int, n_splits: int, d: int, out, stream=None) -> int:
     lib = load()
     do = describe(out)
-    return _check(lib.tad_combine(ws.data_ptr(), ws.numel() * ws.element_size(), B, Hq, n_splits, d,
+    return _check(lib.tad_combine(ws.data_ptr(), ws.numel() * ws.element_size(), B, Hq, nq, n_splits, d,
                                   ctypes.byref(do), _stream(stream)))
 
 
@@ -207,12 +208,17 @@ def resolve_splits(q, k, n_splits: int = 0) -> int:
     return n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, q.device.index or 0)
 
 
+def tokens_of(q) -> int:
+    """Query tokens per (b, h): 1 for [B, Hq, d], nq for [B, Hq, nq, d]."""
+    return q.shape[2] if q.dim() == 4 else 1
+
+
 def workspace(q, k, n_splits: int):
     """A zeroed torch-allocated workspace for (q, k) with n_splits chunks (uint8,
     256-aligned), ready for tad_decode_ws and reusable across calls."""
     torch = _torch()
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
-    nbytes = tad_workspace_bytes(B, Hq, n_splits, d)
+    nbytes = tad_workspace_bytes(B, Hq, tokens_of(q), n_splits, d)
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
 
 
@@ -222,8 +228,7 @@ def decode(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 0, stream=
     torch = _torch()
     S = resolve_splits(q, k, n_splits)
     ws = workspace(q, k, S)
-    B, Hq, Hkv, Lmax, d = shape_of(q, k)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     tad_decode_ws(q, k, v, seq_lens, alibi_slopes, S, out, ws, stream, k_scale, v_scale)
     return out
 
@@ -236,11 +241,13 @@ def split_partials(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 1,
     ws = workspace(q, k, n_splits)
     tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream, k_scale, v_scale)
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
-    n = B * Hq * n_splits
+    nq = tokens_of(q)
+    n = B * Hq * nq * n_splits
     al = lambda x: (x + 255) // 256 * 256
     off_l = al(4 * n)
     off_o = off_l + al(4 * n)
-    m = ws[0:4 * n].view(torch.float32).view(B, Hq, n_splits)
-    l = ws[off_l:off_l + 4 * n].view(torch.float32).view(B, Hq, n_splits)
-    o = ws[off_o:off_o + 4 * n * d].view(torch.float32).view(B, Hq, n_splits, d)
+    lead = (B, Hq, nq) if q.dim() == 4 else (B, Hq)
+    m = ws[0:4 * n].view(torch.float32).view(*lead, n_splits)
+    l = ws[off_l:off_l + 4 * n].view(torch.float32).view(*lead, n_splits)
+    o = ws[off_o:off_o + 4 * n * d].view(torch.float32).view(*lead, n_splits, d)
     return m, l, o

@@ -1,6 +1,6 @@
 // combine.hip -- merge step of split-KV decoding as its own kernel.
 //
-// One work-group per (b, h) row merges that row's S chunk partials with merge_row
+// One work-group per (b, h, query token) row merges that row's S chunk partials with merge_row
 // (merge.h): a max tree, weights 2^(m_s - M), a fixed-order sum tree, one divide.
 // This is the global max / renormalise / sum / divide sequence that tree_attn_decode
 // ("Tree Attention Decoding") performs with one max all-reduce and two sum
@@ -17,15 +17,16 @@ template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
     static_assert(kCombineThreads == kMergeThreads, "merge_row runs on the whole work-group");
     __shared__ float lds[kMaxSplits + kMergeThreads];
-    const int row = blockIdx.x;
+    const int row = blockIdx.x;                  // (b * Hq + h) * nq + t
     const int S = a.S;
-    const int b = row / a.Hq, h = row % a.Hq;
+    const int t = row % a.nq, bh = row / a.nq;
+    const int b = bh / a.Hq, h = bh % a.Hq;
     merge_row<D>(a.ws_m + (int64_t)row * S, a.ws_l + (int64_t)row * S, a.ws_o + (int64_t)row * S * D, S,
-                 a.out + (int64_t)b * a.sob + (int64_t)h * a.soh, lds);
+                 a.out + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)t * a.sot, lds);
 }
 
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t st) {
-    const int64_t rows = (int64_t)a.B * a.Hq;
+    const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
     if (rows <= 0) return hipSuccess;
     switch (d) {
         case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)rows), dim3(kCombineThreads), 0, st, a); break;

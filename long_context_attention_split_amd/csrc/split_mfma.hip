@@ -1,10 +1,11 @@
 // split_mfma.hip -- split step for grouped-query attention on the matrix cores (gfx950).
 //
-// With g query heads sharing one KV head, the scores of a key tile form a real
-// dense product S^T[key][head] = K_tile . Q^T, and so does the value update
-// O^T[e][head] += V_tile^T . P^T.  One work-group (4 waves) owns one (b, kv head,
-// chunk) and all g query heads of the group, so every K and V byte of the chunk is
-// read from HBM once however many heads share it.  The per-head partials (m, l, o)
+// With g query heads sharing one KV head (and/or nq query tokens per head), the
+// scores of a key tile form a real dense product S^T[key][column] = K_tile . Q^T over
+// the g*nq (head, token) columns, and so does the value update O^T[e][column] +=
+// V_tile^T . P^T.  One work-group (4 waves) owns one (b, kv head, chunk) and all its
+// columns, so every K and V byte of the chunk is read from HBM once however many
+// heads and tokens share it.  Each column masks the keys past its token's position.  The per-head partials (m, l, o)
 // it writes are the same as the vector-ALU kernel's (see split_valu.hip): chunk
 // maximum in base 2, sum of 2^(s - m), and the 2^(s - m)-weighted sum of value
 // rows, i.e. the per-chunk local max, denominator and numerator of tree_attn_decode
@@ -104,16 +105,23 @@ void split_mfma_kernel(SplitArgs a) {
     const int c4 = lane >> 4;            // 8-wide (4-wide) reduction block of this lane
     const int j16 = lane & 15;           // column (head) / row (key, value column)
 
-    const int S = a.S, g = a.group;
+    // Columns of the products are (query head, query token) pairs: column j16 < g*nq is
+    // head kvh*g + j16/nq, token j16%nq; with one token this is one head per column.
+    const int S = a.S, g = a.group, nq = a.nq;
+    const int gq = g * nq;
     const int s = blockIdx.x % S;
     const int bk = blockIdx.x / S;
     const int b = bk / a.Hkv, kvh = bk % a.Hkv;
-    const bool head_ok = j16 < g;
-    const int h = kvh * g + (head_ok ? j16 : 0);
+    const bool head_ok = j16 < gq;
+    const int tok = head_ok ? j16 % nq : 0;
+    const int h = kvh * g + (head_ok ? j16 / nq : 0);
 
     const ChunkRange cr = chunk_range(a, b, s);
-    const int L = cr.L, j0 = cr.j0, j1 = cr.j1;
+    const int j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
+    // keys this column's token sees, and that limit relative to the chunk start
+    const int Lc = visible_keys(cr.L, nq, tok);
+    const int lim = min(n, Lc - j0);
 
     const uint32_t krow = (uint32_t)(a.skj * 2), vrow = (uint32_t)(a.svj * 2);
     const char *kbase = (const char *)a.k + ((int64_t)b * a.skb + (int64_t)kvh * a.skh + (int64_t)j0 * a.skj) * 2;
@@ -126,7 +134,7 @@ void split_mfma_kernel(SplitArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         float x[8];
-        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + 32 * kk + 8 * c4;
+        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)tok * a.sqt + 32 * kk + 8 * c4;
         if (a.q_bf16) {
             const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -205,8 +213,8 @@ void split_mfma_kernel(SplitArgs a) {
         for (int r = 0; r < 4; ++r) {
             const int key = t0 + 4 * c4 + r;
             float x = sc[r];
-            if (alibi) x = fmaf(slope2, (float)(j0 + key - (L - 1)), x);
-            p[r] = (key < n) ? x : kNegInf;
+            if (alibi) x = fmaf(slope2, (float)(j0 + key - (Lc - 1)), x);
+            p[r] = (key < lim) ? x : kNegInf;
         }
         float mt = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -293,7 +301,7 @@ void split_mfma_kernel(SplitArgs a) {
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < g * D; idx += kSplitThreads) {
+    for (int idx = threadIdx.x; idx < gq * D; idx += kSplitThreads) {
         const int hh = idx / D, e = idx % D;
         float M = kNegInf;
 #pragma unroll
@@ -306,7 +314,7 @@ void split_mfma_kernel(SplitArgs a) {
             acc = fmaf(sw, lds_o[w][hh][e], acc);
             lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
         }
-        const int64_t r = ((int64_t)b * a.Hq + kvh * g + hh) * S + s;
+        const int64_t r = (((int64_t)b * a.Hq + kvh * g) * nq + hh) * S + s;   // hh: column
         if (a.fused) {                       // written through for the merging work-group
             store_partial(&a.ws_o[r * D + e], acc);
             if (e == 0) {
@@ -322,29 +330,30 @@ void split_mfma_kernel(SplitArgs a) {
         }
     }
 
-    // ---- fused merge: the last of the S work-groups of this (b, kv head) merges its g rows.
+    // ---- fused merge: the last of the S work-groups of this (b, kv head) merges its g*nq rows.
     if (a.fused) {
         static_assert(NW * 2 * TILE * 4 >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in smem");
         __shared__ int last;
-        const int64_t row0 = (int64_t)b * a.Hq + kvh * g;
+        const int64_t row0 = ((int64_t)b * a.Hq + kvh * g) * nq;
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
         __syncthreads();
         if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row0], 1) == S - 1;
         __syncthreads();
         if (last) {
-            for (int hh = 0; hh < g; ++hh) {
-                const int64_t row = row0 + hh;
+            for (int cc = 0; cc < gq; ++cc) {
+                const int64_t row = row0 + cc;
                 merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
-                             a.out + (int64_t)b * a.sob + (int64_t)(kvh * g + hh) * a.soh,
-                             reinterpret_cast<float *>(smem));
+                                   a.out + (int64_t)b * a.sob + (int64_t)(kvh * g + cc / nq) * a.soh +
+                                       (int64_t)(cc % nq) * a.sot,
+                                   reinterpret_cast<float *>(smem));
             }
             if (threadIdx.x == 0) a.cnt[row0] = 0;
         }
     }
 }
 
-bool split_mfma_supported(int d, int kv_type, int group) {
-    return kv_type == kKvBF16 && group >= 2 && group <= 16 && (d == 64 || d == 128);
+bool split_mfma_supported(int d, int kv_type, int group, int nq) {
+    return kv_type == kKvBF16 && group * nq >= 2 && group * nq <= 16 && (d == 64 || d == 128);
 }
 
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {

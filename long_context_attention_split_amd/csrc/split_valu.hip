@@ -60,33 +60,40 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const int grp = lane / G;
     const int sub = lane % G;
 
-    // ---- work-group -> (b, h, s).  With query-head groups (GQA handled here), the g
-    // work-groups that read the same KV chunk get ids that are equal modulo 8, so they
-    // land on the same XCD and share its L2.
-    int b, h, s;
+    // ---- work-group -> (b, h, t, s): query head h, query token t, chunk s.  When
+    // several (head, token) rows read the same KV chunk (query-head groups, several
+    // tokens), their gq work-groups get ids that are equal modulo 8, so they land on
+    // the same XCD and share its L2.
+    int b, h, t, s;
     const int S = a.S;
-    if (a.group == 1) {
+    const int gq = a.group * a.nq;                        // rows per KV head
+    if (gq == 1) {
         const int id = blockIdx.x;
         s = id % S;
         const int row = id / S;
         b = row / a.Hq;
         h = row % a.Hq;
+        t = 0;
     } else {
         const int id = blockIdx.x;
         const int xcd = id & 7;
         const int slot = id >> 3;
-        const int r = slot % a.group;
-        const int u = (slot / a.group) * 8 + xcd;          // (b, kvh, s) unit
+        const int r = slot % gq;
+        const int u = (slot / gq) * 8 + xcd;              // (b, kvh, s) unit
         if (u >= a.B * a.Hkv * S) return;
         s = u % S;
         const int bk = u / S;
         b = bk / a.Hkv;
-        h = (bk % a.Hkv) * a.group + r;
+        h = (bk % a.Hkv) * a.group + r / a.nq;
+        t = r % a.nq;
     }
     const int kvh = h / a.group;
 
+    // The chunk of the KV row, clipped to the keys this token sees; from here on the
+    // row is single-token decode over its first L keys.
     const ChunkRange cr = chunk_range(a, b, s);
-    const int L = cr.L, j0 = cr.j0, j1 = cr.j1;
+    const int L = visible_keys(cr.L, a.nq, t);
+    const int j1 = min(cr.j1, L), j0 = min(cr.j0, j1);
     const int n = j1 - j0;
 
     // ---- per-chunk buffer resources: [chunk start, chunk end) of this head's K and V.
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     float qv[EPL];
     {
         const float qs = a.qscale * (a.k_scale ? a.k_scale[b * a.Hkv + kvh] : 1.f);
-        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + sub * EPL;
+        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)t * a.sqt + sub * EPL;
 #pragma unroll
         for (int c8 = 0; c8 < EPL / 8; ++c8) {
             if (a.q_bf16) {
@@ -220,7 +227,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
 #pragma unroll
     for (int i = 0; i < SLOTS; ++i) M = fmaxf(M, lds_m[i]);
     const float Mu = (M == kNegInf) ? 0.f : M;
-    const int64_t r = ((int64_t)b * a.Hq + h) * S + s;
+    const int64_t row = ((int64_t)b * a.Hq + h) * a.nq + t;
+    const int64_t r = row * S + s;
     const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // V dequantisation
     // Partials are written through to the device coherence point when this kernel also
     // merges (fused), so the merging work-group can read them without cache maintenance.
@@ -249,14 +257,14 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     if (a.fused) {
         static_assert(SLOTS * D >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in lds_o");
         __shared__ int last;
-        const int64_t row = (int64_t)b * a.Hq + h;
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
         __syncthreads();
         if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row], 1) == S - 1;
         __syncthreads();
         if (last) {
             merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
-                         a.out + (int64_t)b * a.sob + (int64_t)h * a.soh, &lds_o[0][0]);
+                               a.out + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)t * a.sot,
+                               &lds_o[0][0]);
             if (threadIdx.x == 0) a.cnt[row] = 0;
         }
     }
@@ -265,14 +273,15 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
 template <int D, int KVT>
 static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
     int64_t grid;
-    if (a.group == 1) {
+    const int gq = a.group * a.nq;
+    if (gq == 1) {
         grid = (int64_t)a.B * a.Hq * a.S;
     } else {
         const int64_t units = (int64_t)a.B * a.Hkv * a.S;
-        grid = (units + 7) / 8 * 8 * a.group;
+        grid = (units + 7) / 8 * 8 * gq;
     }
     if (grid <= 0) return hipSuccess;
-    if (a.group == 1)
+    if (gq == 1)
         hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
     else
         hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);

@@ -43,32 +43,32 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Shapes and strides of one decode call, normalised to 4-D [B, H, L, d] views.
 struct Problem {
-    int64_t B = 0, Hq = 0, Hkv = 0, Lmax = 0, d = 0;
+    int64_t B = 0, Hq = 0, Hkv = 0, Lmax = 0, d = 0, nq = 1;
     int32_t q_dtype = 0, kv_dtype = 0;
-    int64_t sqb = 0, sqh = 0;
+    int64_t sqb = 0, sqh = 0, sqt = 0;
     int64_t skb = 0, skh = 0, skj = 0;
     int64_t svb = 0, svh = 0, svj = 0;
     const float *k_scale = nullptr, *v_scale = nullptr;
 };
 
-// q or out: [B, H, d] or [B, H, 1, d].
-int parse_query_like(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int64_t *d,
-                     int64_t *sb, int64_t *sh) {
+// q or out: [B, H, d] (one token) or [B, H, nq, d].
+int parse_query_like(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int64_t *nq,
+                     int64_t *d, int64_t *sb, int64_t *sh, int64_t *st) {
     if (!t) return fail(TAD_EINVAL, "%s: null tensor descriptor", name);
     if (!t->data) return fail(TAD_EINVAL, "%s: null data pointer", name);
     if (t->ndim == 3) {
-        *B = t->shape[0]; *H = t->shape[1]; *d = t->shape[2];
-        *sb = t->stride[0]; *sh = t->stride[1];
+        *B = t->shape[0]; *H = t->shape[1]; *nq = 1; *d = t->shape[2];
+        *sb = t->stride[0]; *sh = t->stride[1]; *st = 0;
         if (t->stride[2] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
     } else if (t->ndim == 4) {
-        if (t->shape[2] != 1) return fail(TAD_EINVAL, "%s: 4-D form must be [B, H, 1, d]", name);
-        *B = t->shape[0]; *H = t->shape[1]; *d = t->shape[3];
-        *sb = t->stride[0]; *sh = t->stride[1];
+        *B = t->shape[0]; *H = t->shape[1]; *nq = t->shape[2]; *d = t->shape[3];
+        *sb = t->stride[0]; *sh = t->stride[1]; *st = t->stride[2];
         if (t->stride[3] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
     } else {
         return fail(TAD_EINVAL, "%s: ndim must be 3 or 4 (got %d)", name, t->ndim);
     }
-    if (*B < 0 || *H < 1 || *d < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
+    if (*B < 0 || *H < 1 || *d < 1 || *nq < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
+    if (*nq > 256) return fail(TAD_EUNSUPPORTED, "%s: at most 256 query tokens per row", name);
     return TAD_OK;
 }
 
@@ -102,12 +102,12 @@ int parse_kv(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int6
 
 int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, Problem *P) {
     int rc;
-    int64_t Bq, Hq, dq;
-    if ((rc = parse_query_like(q, "q", &Bq, &Hq, &dq, &P->sqb, &P->sqh))) return rc;
+    int64_t Bq, Hq, dq, nq;
+    if ((rc = parse_query_like(q, "q", &Bq, &Hq, &nq, &dq, &P->sqb, &P->sqh, &P->sqt))) return rc;
     if (q->dtype != TAD_F32 && q->dtype != TAD_BF16) return fail(TAD_EDTYPE, "q: dtype must be TAD_F32 or TAD_BF16");
     if (q->scale) return fail(TAD_EINVAL, "q: scale must be NULL");
     const int64_t qes = elem_size(q->dtype);
-    if (!aligned16(q->data) || (P->sqb * qes) % 16 || (P->sqh * qes) % 16)
+    if (!aligned16(q->data) || (P->sqb * qes) % 16 || (P->sqh * qes) % 16 || (P->sqt * qes) % 16)
         return fail(TAD_ELAYOUT, "q: rows must start on 16-byte boundaries");
     int64_t Bk, Hk, Lk, dk, Bv, Hv, Lv, dv;
     if ((rc = parse_kv(k, "k", &Bk, &Hk, &Lk, &dk, &P->skb, &P->skh, &P->skj))) return rc;
@@ -121,19 +121,21 @@ int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
         return fail(TAD_EUNSUPPORTED, "head dim %lld not supported (64, 128, 256, 512)", (long long)dq);
     if (Bq > 0x7fffffff || Hq > 0x7fffffff || Lk > 0x3fffffff)
         return fail(TAD_EUNSUPPORTED, "sizes too large");
-    P->B = Bq; P->Hq = Hq; P->Hkv = Hk; P->Lmax = Lk; P->d = dq;
+    if (Bq * Hq * nq > 0x7fffffff) return fail(TAD_EUNSUPPORTED, "sizes too large");
+    P->B = Bq; P->Hq = Hq; P->Hkv = Hk; P->Lmax = Lk; P->d = dq; P->nq = nq;
     P->q_dtype = q->dtype; P->kv_dtype = k->dtype;
     P->k_scale = k->scale; P->v_scale = v->scale;
     return TAD_OK;
 }
 
-int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *soh) {
+int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *soh, int64_t *sot) {
     int rc;
-    int64_t B, H, d;
-    if ((rc = parse_query_like(out, "out", &B, &H, &d, sob, soh))) return rc;
+    int64_t B, H, d, nq;
+    if ((rc = parse_query_like(out, "out", &B, &H, &nq, &d, sob, soh, sot))) return rc;
     if (out->dtype != TAD_F32) return fail(TAD_EDTYPE, "out: dtype must be TAD_F32");
     if (out->scale) return fail(TAD_EINVAL, "out: scale must be NULL");
-    if (B != P.B || H != P.Hq || d != P.d) return fail(TAD_EINVAL, "out: shape must be [B, Hq, d] of the inputs");
+    if (B != P.B || H != P.Hq || d != P.d || nq != P.nq)
+        return fail(TAD_EINVAL, "out: shape must be [B, Hq, (nq,) d] of the inputs");
     return TAD_OK;
 }
 
@@ -196,13 +198,20 @@ int carve_ws(void *ws, size_t ws_bytes, int64_t rows, int64_t S, int64_t d, WsPt
     return TAD_OK;
 }
 
-// Launch the split kernel.  With `out` non-null the kernel also merges (fused: the
+// Output of a decode: fp32 [B, Hq, nq, d] with element strides.
+struct OutDesc {
+    float *data = nullptr;
+    int64_t sob = 0, soh = 0, sot = 0;
+};
+
+// Launch the split kernel.  With out.data non-null the kernel also merges (fused: the
 // last work-group of each row merges it, using the workspace's arrival counters).
 int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                  const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
-                 const tad_tensor *out, int64_t sob, int64_t soh, hipStream_t stream) {
+                 const OutDesc &out, hipStream_t stream) {
     tad::SplitArgs a;
-    a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.q_bf16 = P.q_dtype == TAD_BF16;
+    a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.sqt = P.sqt; a.q_bf16 = P.q_dtype == TAD_BF16;
+    a.nq = (int32_t)P.nq;
     a.k = k->data; a.v = v->data;
     a.kv_type = P.kv_dtype == TAD_F32 ? tad::kKvF32
               : P.kv_dtype == TAD_BF16 ? tad::kKvBF16
@@ -215,23 +224,23 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     a.S = S; a.group = (int32_t)(P.Hq / P.Hkv);
     a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
     a.ws_m = w.m; a.ws_l = w.l; a.ws_o = w.o;
-    a.fused = out != nullptr;
+    a.fused = out.data != nullptr;
     a.cnt = w.cnt;
-    a.out = out ? (float *)out->data : nullptr;
-    a.sob = sob; a.soh = soh;
-    hipError_t e = tad::split_mfma_supported((int)P.d, a.kv_type, a.group)
+    a.out = out.data;
+    a.sob = out.sob; a.soh = out.soh; a.sot = out.sot;
+    hipError_t e = tad::split_mfma_supported((int)P.d, a.kv_type, a.group, a.nq)
                        ? tad::launch_split_mfma(a, (int)P.d, stream)
                        : tad::launch_split_valu(a, (int)P.d, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "split kernel launch: %s", hipGetErrorString(e));
     return TAD_OK;
 }
 
-int launch_merge(int64_t B, int64_t Hq, int32_t S, int64_t d, const WsPtrs &w, const tad_tensor *out,
-                 int64_t sob, int64_t soh, hipStream_t stream) {
+int launch_merge(int64_t B, int64_t Hq, int64_t nq, int32_t S, int64_t d, const WsPtrs &w, const OutDesc &out,
+                 hipStream_t stream) {
     tad::CombineArgs c;
     c.ws_m = w.m; c.ws_l = w.l; c.ws_o = w.o;
-    c.out = (float *)out->data; c.sob = sob; c.soh = soh;
-    c.B = (int32_t)B; c.Hq = (int32_t)Hq; c.S = S;
+    c.out = out.data; c.sob = out.sob; c.soh = out.soh; c.sot = out.sot;
+    c.B = (int32_t)B; c.Hq = (int32_t)Hq; c.nq = (int32_t)nq; c.S = S;
     hipError_t e = tad::launch_combine(c, (int)d, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));
     return TAD_OK;
@@ -250,23 +259,23 @@ int check_splits(int32_t S) {
 // run back to back.  Both give bit-identical outputs (the same merge routine).
 int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
-               const tad_tensor *out, int64_t sob, int64_t soh, hipStream_t stream) {
+               const OutDesc &out, hipStream_t stream) {
     int cus = 0;
-    int rc0 = device_cus(-1, &cus);
-    if (rc0) return rc0;
-    if (S <= tad::kMaxFusedSplits && P.B * P.Hq * (int64_t)S < cus)
-        return launch_split(P, q, k, v, seq_lens, slopes, S, w, out, sob, soh, stream);
-    int rc = launch_split(P, q, k, v, seq_lens, slopes, S, w, nullptr, 0, 0, stream);
+    int rc = device_cus(-1, &cus);
     if (rc) return rc;
-    return launch_merge(P.B, P.Hq, S, P.d, w, out, sob, soh, stream);
+    if (S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus)
+        return launch_split(P, q, k, v, seq_lens, slopes, S, w, out, stream);
+    if ((rc = launch_split(P, q, k, v, seq_lens, slopes, S, w, OutDesc(), stream))) return rc;
+    return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);
 }
 
 // Validation shared by tad_decode and tad_decode_ws; resolves automatic n_splits.
 int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, int32_t n_splits,
-                   const tad_tensor *out, Problem *P, int32_t *S, int64_t *sob, int64_t *soh) {
+                   const tad_tensor *out, Problem *P, int32_t *S, OutDesc *od) {
     int rc;
     if ((rc = parse_problem(q, k, v, P))) return rc;
-    if ((rc = check_out(out, *P, sob, soh))) return rc;
+    if ((rc = check_out(out, *P, &od->sob, &od->soh, &od->sot))) return rc;
+    od->data = (float *)out->data;
     if (n_splits <= 0) {
         int cus = 0;
         if ((rc = device_cus(-1, &cus))) return rc;
@@ -295,9 +304,9 @@ int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device) {
     return auto_splits_for(B, Hkv, Lmax, cus);
 }
 
-size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t n_splits, int32_t d) {
-    if (B < 1 || Hq < 1 || n_splits < 1 || d < 1) return 0;
-    return tad::ws_layout((int64_t)B * Hq, n_splits, d).total;
+size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t nq, int32_t n_splits, int32_t d) {
+    if (B < 1 || Hq < 1 || nq < 1 || n_splits < 1 || d < 1) return 0;
+    return tad::ws_layout((int64_t)B * Hq * nq, n_splits, d).total;
 }
 
 int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream) {
@@ -316,27 +325,28 @@ int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, con
     if ((rc = check_splits(n_splits))) return rc;
     if ((rc = check_offsets(P, n_splits))) return rc;
     WsPtrs w;
-    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq, n_splits, P.d, &w))) return rc;
+    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, n_splits, P.d, &w))) return rc;
     if (P.B == 0) return ok();
-    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, nullptr, 0, 0, stream))) return rc;
+    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, OutDesc(), stream))) return rc;
     return ok();
 }
 
-int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t n_splits, int32_t d,
-                tad_tensor *out, hipStream_t stream) {
+int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t nq, int32_t n_splits,
+                int32_t d, tad_tensor *out, hipStream_t stream) {
     int rc;
-    if (B < 0 || Hq < 1) return fail(TAD_EINVAL, "tad_combine: bad B or Hq");
+    if (B < 0 || Hq < 1 || nq < 1) return fail(TAD_EINVAL, "tad_combine: bad B, Hq or nq");
     if (d != 64 && d != 128 && d != 256 && d != 512)
         return fail(TAD_EUNSUPPORTED, "head dim %d not supported (64, 128, 256, 512)", d);
     if ((rc = check_splits(n_splits))) return rc;
     Problem P;
-    P.B = B; P.Hq = Hq; P.d = d;
-    int64_t sob, soh;
-    if ((rc = check_out(out, P, &sob, &soh))) return rc;
+    P.B = B; P.Hq = Hq; P.d = d; P.nq = nq;
+    OutDesc od;
+    if ((rc = check_out(out, P, &od.sob, &od.soh, &od.sot))) return rc;
+    od.data = (float *)out->data;
     WsPtrs w;
-    if ((rc = carve_ws(const_cast<void *>(ws), ws_bytes, (int64_t)B * Hq, n_splits, d, &w))) return rc;
+    if ((rc = carve_ws(const_cast<void *>(ws), ws_bytes, (int64_t)B * Hq * nq, n_splits, d, &w))) return rc;
     if (B == 0) return ok();
-    if ((rc = launch_merge(B, Hq, n_splits, d, w, out, sob, soh, stream))) return rc;
+    if ((rc = launch_merge(B, Hq, nq, n_splits, d, w, od, stream))) return rc;
     return ok();
 }
 
@@ -345,13 +355,13 @@ int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                   hipStream_t stream) {
     Problem P;
     int32_t S;
-    int64_t sob, soh;
+    OutDesc od;
     int rc;
-    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &sob, &soh))) return rc;
+    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &od))) return rc;
     WsPtrs w;
-    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq, S, P.d, &w))) return rc;
+    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, S, P.d, &w))) return rc;
     if (P.B == 0) return ok();
-    if ((rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, out, sob, soh, stream))) return rc;
+    if ((rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream))) return rc;
     return ok();
 }
 
@@ -359,21 +369,22 @@ int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, co
                const float *alibi_slopes, int32_t n_splits, tad_tensor *out, hipStream_t stream) {
     Problem P;
     int32_t S;
-    int64_t sob, soh;
+    OutDesc od;
     int rc;
-    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &sob, &soh))) return rc;
+    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &od))) return rc;
     if (P.B == 0) return ok();
-    const size_t bytes = tad::ws_layout(P.B * P.Hq, S, P.d).total;
+    const int64_t rows = P.B * P.Hq * P.nq;
+    const size_t bytes = tad::ws_layout(rows, S, P.d).total;
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, bytes, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
     WsPtrs w;
-    rc = carve_ws(ws, bytes, P.B * P.Hq, S, P.d, &w);
+    rc = carve_ws(ws, bytes, rows, S, P.d, &w);
     if (!rc) {
-        hipError_t ez = tad::launch_fill_zero(w.cnt, P.B * P.Hq, stream);
+        hipError_t ez = tad::launch_fill_zero(w.cnt, rows, stream);
         if (ez != hipSuccess) rc = fail(TAD_EHIP, "counter clear launch: %s", hipGetErrorString(ez));
     }
-    if (!rc) rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, out, sob, soh, stream);
+    if (!rc) rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream);
     e = hipFreeAsync(ws, stream);
     if (rc) return rc;
     if (e != hipSuccess) return fail(TAD_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));

@@ -9,9 +9,10 @@ namespace tad {
 
 // Everything the split kernels need, by value (lives in the kernel argument segment).
 struct SplitArgs {
-    const void *q;          // [B, Hq, d], innermost contiguous
-    int64_t sqb, sqh;       // q element strides
+    const void *q;          // [B, Hq, nq, d], innermost contiguous
+    int64_t sqb, sqh, sqt;  // q element strides
     int32_t q_bf16;         // q dtype: 1 = bf16, 0 = fp32
+    int32_t nq;             // query tokens per (b, h): the row's last nq positions, causal
     const void *k, *v;      // [B, Hkv, Lmax, d], innermost contiguous
     int32_t kv_type;        // kKvF32, kKvBF16, kKvE4M3, kKvE5M2 (device_util.h)
     const float *k_scale, *v_scale;  // [B * Hkv] dequantisation scales, or null (1)
@@ -25,17 +26,23 @@ struct SplitArgs {
     // Fused merge: when set, the last work-group to finish a row (counted in cnt)
     // merges the row's partials into out.  cnt must be zero on entry and is left zero.
     int32_t fused;
-    int32_t *cnt;           // [B * Hq] arrival counters
-    float *out;             // [B, Hq, d] fp32
-    int64_t sob, soh;       // out element strides
+    int32_t *cnt;           // [B * Hq * nq] arrival counters
+    float *out;             // [B, Hq, nq, d] fp32
+    int64_t sob, soh, sot;  // out element strides
 };
 
 struct CombineArgs {
     const float *ws_m, *ws_l, *ws_o;
-    float *out;             // [B, Hq, d] fp32
-    int64_t sob, soh;       // out element strides
-    int32_t B, Hq, S;
+    float *out;             // [B, Hq, nq, d] fp32
+    int64_t sob, soh, sot;  // out element strides
+    int32_t B, Hq, nq, S;
 };
+
+// Keys a query token sees: token t of nq sits at position L - nq + t and sees the keys
+// up to it, i.e. the first clamp(L - nq + t + 1, 0, L) keys.
+__device__ __forceinline__ int visible_keys(int L, int nq, int t) {
+    return min(max(L - nq + t + 1, 0), L);
+}
 
 // Keys [j0, j1) of batch row b that chunk s covers, and the row's length L.
 // Every row of the batch is cut with one chunk length, c = ceil(Lref / S), where
@@ -85,7 +92,7 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
 
 // Launchers (defined next to their kernels).  Return the hipError_t of the launch.
 hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t s);
-bool split_mfma_supported(int d, int kv_type, int group);
+bool split_mfma_supported(int d, int kv_type, int group, int nq);
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);

@@ -40,11 +40,13 @@ def test_version_matches_header(lib):
 
 def test_workspace_bytes_layout(lib):
     # m and l: rows*S floats each, 256-aligned; o: rows*S*d floats; cnt: rows int32
-    assert lib.tad_workspace_bytes(1, 32, 32, 128) == 2 * 4096 + 1024 * 128 * 4 + 256
-    assert lib.tad_workspace_bytes(8, 32, 16, 128) == 2 * 16384 + 4096 * 128 * 4 + 1024
-    assert lib.tad_workspace_bytes(1, 1, 8, 512) == 2 * 256 + 8 * 512 * 4 + 256
-    assert lib.tad_workspace_bytes(0, 1, 1, 64) == 0
-    assert lib.tad_workspace_bytes(1, 1, 0, 64) == 0
+    assert lib.tad_workspace_bytes(1, 32, 1, 32, 128) == 2 * 4096 + 1024 * 128 * 4 + 256
+    assert lib.tad_workspace_bytes(8, 32, 1, 16, 128) == 2 * 16384 + 4096 * 128 * 4 + 1024
+    assert lib.tad_workspace_bytes(1, 1, 1, 8, 512) == 2 * 256 + 8 * 512 * 4 + 256
+    assert lib.tad_workspace_bytes(1, 32, 4, 32, 128) == 2 * 16384 + 4096 * 128 * 4 + 512   # 4 tokens
+    assert lib.tad_workspace_bytes(0, 1, 1, 1, 64) == 0
+    assert lib.tad_workspace_bytes(1, 1, 1, 0, 64) == 0
+    assert lib.tad_workspace_bytes(1, 1, 0, 1, 64) == 0
 
 
 def desc(shape, dtype=tad.TAD_BF16, strides=None, addr=FAKE):
@@ -92,7 +94,8 @@ def call_decode_ws(so, a, n_splits=4, ws=FAKE, ws_bytes=1 << 30):
     (lambda a: a.update(q=desc([3, 8, 128], tad.TAD_F32)), tad.TAD_EINVAL),                    # batch
     (lambda a: a.update(v=desc([2, 2, 99, 128])), tad.TAD_EINVAL),                             # k/v shape
     (lambda a: a.update(q=desc([2, 8, 64], tad.TAD_F32)), tad.TAD_EINVAL),                     # head dim
-    (lambda a: a.update(q=desc([2, 8, 2, 128], tad.TAD_F32)), tad.TAD_EINVAL),                 # 4-D q, i != 1
+    (lambda a: a.update(q=desc([2, 8, 0, 128], tad.TAD_F32)), tad.TAD_EINVAL),                 # no tokens
+    (lambda a: a.update(q=desc([2, 8, 257, 128], tad.TAD_F32)), tad.TAD_EUNSUPPORTED),         # > 256 tokens
     (lambda a: a.update(k=desc([2, 2, 100, 128], addr=0)), tad.TAD_EINVAL),                    # null data
     (lambda a: a.update(k=desc([200, 128])), tad.TAD_EINVAL),                                  # 2-D k
 ])
@@ -138,7 +141,7 @@ def test_split_rejects_bad_splits_and_workspace(lib):
     a = good()
     assert call_split(so, a, n_splits=0) == tad.TAD_EINVAL
     assert call_split(so, a, n_splits=4097) == tad.TAD_EINVAL
-    need = lib.tad_workspace_bytes(2, 8, 4, 128)
+    need = lib.tad_workspace_bytes(2, 8, 1, 4, 128)
     assert call_split(so, a, ws_bytes=need - 1) == tad.TAD_EWORKSPACE
     assert call_split(so, a, ws=FAKE + 16) == tad.TAD_EWORKSPACE
     assert call_split(so, a, ws=0) == tad.TAD_EWORKSPACE
@@ -164,15 +167,24 @@ def test_decode_ws_checks_out(lib):
     assert call_decode_ws(so, a) == tad.TAD_EINVAL
     a["out"] = desc([2, 8, 128], tad.TAD_F32, strides=[1024, 128, 2])
     assert call_decode_ws(so, a) == tad.TAD_ELAYOUT
+    # several query tokens: out must carry the same token count
+    a["q"] = desc([2, 8, 3, 128], tad.TAD_F32)
+    a["out"] = desc([2, 8, 128], tad.TAD_F32)
+    assert call_decode_ws(so, a) == tad.TAD_EINVAL
+    a["out"] = desc([2, 8, 3, 128], tad.TAD_F32)
+    need = lib.tad_workspace_bytes(2, 8, 3, 4, 128)
+    assert call_decode_ws(so, a, ws_bytes=need - 1) == tad.TAD_EWORKSPACE
 
 
 def test_combine_validation(lib):
     so = lib.load()
     out = desc([2, 8, 128], tad.TAD_F32)
-    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 4, 96, ctypes.byref(out), None) == tad.TAD_EUNSUPPORTED
-    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 0, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
-    assert so.tad_combine(FAKE, 10, 2, 8, 4, 128, ctypes.byref(out), None) == tad.TAD_EWORKSPACE
-    assert so.tad_combine(FAKE, 1 << 30, 2, 9, 4, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
+    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 1, 4, 96, ctypes.byref(out), None) == tad.TAD_EUNSUPPORTED
+    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 1, 0, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
+    assert so.tad_combine(FAKE, 10, 2, 8, 1, 4, 128, ctypes.byref(out), None) == tad.TAD_EWORKSPACE
+    assert so.tad_combine(FAKE, 1 << 30, 2, 9, 1, 4, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
+    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 2, 4, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
+    assert so.tad_combine(FAKE, 1 << 30, 2, 8, 0, 4, 128, ctypes.byref(out), None) == tad.TAD_EINVAL
 
 
 def test_empty_batch_is_a_no_op(lib):

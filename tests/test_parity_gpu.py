@@ -165,7 +165,7 @@ def test_entry_points_agree(lib):
     ws = lib.workspace(c["q"], c["k"], S)
     lib.tad_split(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S, ws)
     out_c = torch.empty_like(a)
-    lib.tad_combine(ws, 2, 8, S, 128, out_c)
+    lib.tad_combine(ws, 2, 8, 1, S, 128, out_c)
     again = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S)
     torch.cuda.synchronize()
     assert torch.equal(a, out_b) and torch.equal(a, out_c) and torch.equal(a, again)
@@ -190,6 +190,52 @@ def test_fp8_ragged_gqa_alibi(lib, kv):
 
 def test_fp8_long_context(lib):
     run_case(lib, 320, 1, 8, 8, 65536, 128, kv=torch.float8_e4m3fn, n_splits=0, k_scale=4.0)
+
+
+def multi_case(seed, B, Hq, Hkv, nq, L, d, kv=torch.bfloat16, lens=None, alibi=False):
+    c = W.random_case(seed, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi)
+    c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(seed + 9))
+    return c
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,nq,kv,d", [
+    (2, 4, 4, 2, torch.bfloat16, 128),      # matrix-core path: 2 tokens per head
+    (1, 8, 8, 16, torch.bfloat16, 128),     # 16 tokens fill the 16 columns
+    (2, 8, 2, 4, torch.bfloat16, 64),       # 4 heads x 4 tokens
+    (2, 4, 4, 17, torch.bfloat16, 128),     # more columns than 16: vector path
+    (2, 8, 2, 5, torch.bfloat16, 128),      # 4 heads x 5 tokens: vector path
+    (2, 4, 4, 3, torch.float32, 128),       # fp32: vector path
+    (2, 4, 2, 3, torch.float8_e4m3fn, 256),
+])
+@pytest.mark.parametrize("alibi", [False, True])
+def test_several_query_tokens(lib, B, Hq, Hkv, nq, kv, d, alibi):
+    """nq new tokens per row, each seeing the keys up to its own position (causal among
+    the new tokens); ragged lengths including one shorter than nq."""
+    lens = [700, nq - 2][:B] if B > 1 else [1000]
+    L = max(lens)
+    note("tokens B=%d Hq=%d Hkv=%d nq=%d kv=%s d=%d alibi=%s lens=%s" % (B, Hq, Hkv, nq, kv, d, alibi, lens))
+    c = multi_case(400 + nq + d, B, Hq, Hkv, nq, L, d, kv, lens, alibi)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
+    for S in (3, 40):
+        out = gpu_decode(lib, c, S)
+        assert out.shape == (B, Hq, nq, d)
+        assert_parity(out, ref, kv, vmax_real(c), "tokens S=%d" % S)
+    if B > 1:
+        assert (out[1, :, :2] == 0).all()          # positions before the first key
+
+
+def test_several_tokens_entry_points_agree(lib):
+    """Fused (small) and split + combine give identical multi-token outputs."""
+    c = to_dev(multi_case(450, 2, 8, 2, 3, 900, 128, lens=[900, 500]))
+    S = 4
+    a = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], None, S)
+    ws = lib.workspace(c["q"], c["k"], S)
+    lib.tad_split(c["q"], c["k"], c["v"], c["seq_lens"], None, S, ws)
+    b = torch.empty_like(a)
+    lib.tad_combine(ws, 2, 8, 3, S, 128, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 def test_workspace_reuse_and_clear(lib):
