@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10300 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -169,6 +169,45 @@ int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
 int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
                tad_tensor *out, hipStream_t stream);
+
+/*
+ * Paged K/V cache.  The pages leave the K/V cache to the caller (SwitchHead README,
+ * forward signature: the caller keeps the cache and hands it back each step); a
+ * paged cache is the layout serving engines use for it: a shared pool of
+ * fixed-size pages, each sequence owning a list of pages in a block table.  This
+ * layout is not on the pages; it only changes where key j of row b is read:
+ * page block_table[b * max_pages + j / page_size], row j % page_size of that page.
+ *  - k_cache, v_cache: 4-D [num_pages, page_size, Hkv, d], same dtype and shape,
+ *    TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2 (FP8 with the per-(b, kv head) `scale`
+ *    described above); innermost stride 1, any outer strides, rows 16-byte aligned;
+ *    page_size a multiple of 16; d 64, 128 or 256.
+ *  - pages->block_table: DEVICE int32 [B, max_pages], row-major, pages->max_pages
+ *    >= 1.  The logical length is Lmax = max_pages * page_size; only the entries
+ *    covering the first L_b keys of row b are read.  An entry outside [0, num_pages)
+ *    is not checked on the host (the table lives on the device): its keys and
+ *    values read as zeros, and no memory outside the cache is touched.
+ *  - The chunk length c = ceil(Lref / n_splits) is rounded up to whole pages.
+ * q, out, seq_lens, alibi_slopes, n_splits, the workspace and the error codes are
+ * as for tad_split / tad_decode_ws / tad_decode; the result equals theirs on the
+ * gathered [B, Hkv, Lmax, d] K and V up to rounding (the chunk boundaries, and so
+ * the summation order, may differ).
+ */
+typedef struct tad_paged_kv {
+    const int32_t *block_table; /* device int32 [B, max_pages] */
+    int32_t max_pages;          /* block-table entries per batch row */
+} tad_paged_kv;
+
+int tad_split_paged(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,
+                    const tad_paged_kv *pages, const int32_t *seq_lens, const float *alibi_slopes,
+                    int32_t n_splits, void *ws, size_t ws_bytes, hipStream_t stream);
+
+int tad_decode_paged_ws(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,
+                        const tad_paged_kv *pages, const int32_t *seq_lens, const float *alibi_slopes,
+                        int32_t n_splits, tad_tensor *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+int tad_decode_paged(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,
+                     const tad_paged_kv *pages, const int32_t *seq_lens, const float *alibi_slopes,
+                     int32_t n_splits, tad_tensor *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

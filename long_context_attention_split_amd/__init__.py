@@ -10,6 +10,9 @@ streams.  The functions carry the C names:
 - ``tad_combine(ws, B, Hq, nq, n_splits, d, out, stream=None)``
 - ``tad_auto_splits(B, Hkv, Lmax, device=-1)``, ``tad_workspace_bytes(B, Hq, nq, n_splits, d)``
 - ``tad_workspace_clear(ws, stream=None)``, ``tad_version()``, ``tad_last_error()``
+- ``tad_split_paged``, ``tad_decode_paged_ws``, ``tad_decode_paged``: the same with a
+  paged K/V cache (k_cache, v_cache [num_pages, page_size, Hkv, d] and an int32
+  block table [B, max_pages] in place of k and v)
 
 and ``decode(...)`` allocates ``out`` and the workspace with torch and calls
 ``tad_decode_ws``.  Tensors: q [B, Hq, d] or [B, Hq, nq, d] (nq new tokens, causal)
@@ -33,12 +36,17 @@ TAD_F32, TAD_BF16, TAD_FP8_E4M3, TAD_FP8_E5M2 = 0, 1, 2, 3
 TAD_OK, TAD_EINVAL, TAD_EDTYPE, TAD_ELAYOUT, TAD_EUNSUPPORTED, TAD_EWORKSPACE, TAD_EHIP = 0, -1, -2, -3, -4, -5, -6
 
 EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_bytes",
-           "tad_workspace_clear", "tad_split", "tad_combine", "tad_decode_ws", "tad_decode")
+           "tad_workspace_clear", "tad_split", "tad_combine", "tad_decode_ws", "tad_decode",
+           "tad_split_paged", "tad_decode_paged_ws", "tad_decode_paged")
 
 
 class TadTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4), ("scale", ctypes.c_void_p)]
+
+
+class TadPagedKv(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32)]
 
 
 class TadError(RuntimeError):
@@ -79,6 +87,13 @@ def load():
     lib.tad_decode_ws.argtypes = [P, P, P, vp, vp, i32, P, vp, sz, vp]
     lib.tad_decode.restype = ctypes.c_int
     lib.tad_decode.argtypes = [P, P, P, vp, vp, i32, P, vp]
+    PG = ctypes.POINTER(TadPagedKv)
+    lib.tad_split_paged.restype = ctypes.c_int
+    lib.tad_split_paged.argtypes = [P, P, P, PG, vp, vp, i32, vp, sz, vp]
+    lib.tad_decode_paged_ws.restype = ctypes.c_int
+    lib.tad_decode_paged_ws.argtypes = [P, P, P, PG, vp, vp, i32, P, vp, sz, vp]
+    lib.tad_decode_paged.restype = ctypes.c_int
+    lib.tad_decode_paged.argtypes = [P, P, P, PG, vp, vp, i32, P, vp]
     _lib = lib
     return lib
 
@@ -190,6 +205,61 @@ def tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None,
     dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
     return _check(lib.tad_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                  _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
+
+
+def paged(block_table) -> TadPagedKv:
+    """tad_paged_kv for an int32 [B, max_pages] device block table."""
+    torch = _torch()
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor")
+    p = TadPagedKv()
+    p.block_table = block_table.data_ptr() if block_table.numel() else None
+    p.max_pages = block_table.shape[1]
+    return p
+
+
+def tad_split_paged(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n_splits: int, ws, stream=None,
+                    k_scale=None, v_scale=None) -> int:
+    lib = load()
+    dq, dk, dv, pg = describe(q), describe(k_cache, k_scale), describe(v_cache, v_scale), paged(block_table)
+    return _check(lib.tad_split_paged(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(pg),
+                                      _ptr(seq_lens), _ptr(alibi_slopes), n_splits, ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tad_decode_paged_ws(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n_splits: int, out, ws,
+                        stream=None, k_scale=None, v_scale=None) -> int:
+    lib = load()
+    dq, dk, dv, do = describe(q), describe(k_cache, k_scale), describe(v_cache, v_scale), describe(out)
+    pg = paged(block_table)
+    return _check(lib.tad_decode_paged_ws(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(pg),
+                                          _ptr(seq_lens), _ptr(alibi_slopes), n_splits, ctypes.byref(do),
+                                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tad_decode_paged(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n_splits: int, out, stream=None,
+                     k_scale=None, v_scale=None) -> int:
+    lib = load()
+    dq, dk, dv, do = describe(q), describe(k_cache, k_scale), describe(v_cache, v_scale), describe(out)
+    pg = paged(block_table)
+    return _check(lib.tad_decode_paged(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(pg),
+                                       _ptr(seq_lens), _ptr(alibi_slopes), n_splits, ctypes.byref(do),
+                                       _stream(stream)))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens=None, alibi_slopes=None, n_splits: int = 0,
+                 stream=None, k_scale=None, v_scale=None):
+    """out = tad_decode_paged_ws(...) with torch-allocated out and workspace."""
+    torch = _torch()
+    B, Hq, d = q.shape[0], q.shape[1], q.shape[-1]
+    Hkv, Lmax = k_cache.shape[2], block_table.shape[1] * k_cache.shape[1]
+    S = n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, q.device.index or 0)
+    nbytes = tad_workspace_bytes(B, Hq, tokens_of(q), S, d)
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    tad_decode_paged_ws(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, S, out, ws, stream,
+                        k_scale, v_scale)
+    return out
 
 
 def shape_of(q, k):

@@ -78,7 +78,9 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // WAVES: occupancy target (waves per SIMD) the register allocator must meet.
 // NBUF: LDS tile buffers per wave; with 2, the next tile's loads are in flight while
 // the current one is consumed.
-template <int D, int WAVES = 4, int NBUF = 1>
+// PAGED: K/V rows come from a paged cache; each 16-key tile lies inside one page
+// (page sizes are multiples of 16) and gets its own buffer resources.
+template <int D, int WAVES = 4, int NBUF = 1, bool PAGED = false>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
@@ -123,11 +125,11 @@ void split_mfma_kernel(SplitArgs a) {
     const int Lc = visible_keys(cr.L, nq, tok);
     const int lim = min(n, Lc - j0);
 
-    const uint32_t krow = (uint32_t)(a.skj * 2), vrow = (uint32_t)(a.svj * 2);
-    const char *kbase = (const char *)a.k + ((int64_t)b * a.skb + (int64_t)kvh * a.skh + (int64_t)j0 * a.skj) * 2;
-    const char *vbase = (const char *)a.v + ((int64_t)b * a.svb + (int64_t)kvh * a.svh + (int64_t)j0 * a.svj) * 2;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)n * krow);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)n * vrow);
+    const KvRows kvk(a.k, 2, a.skb, a.skh, a.skj, a.skp, a, b, kvh);
+    const KvRows kvv(a.v, 2, a.svb, a.svh, a.svj, a.svp, a, b, kvh);
+    const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
+    const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
+    const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
 
     // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo.
     uint4 qhi[NKK], qlo[NKK];
@@ -180,14 +182,22 @@ void split_mfma_kernel(SplitArgs a) {
     // HBM -> LDS, whole rows per instruction; rows past the chunk end read as zero.
     auto issue_tile = [&](uint4 *tk, int t0) {
         uint4 *tv = tk + TILE;
+        __amdgpu_buffer_rsrc_t krs = kr, vrs = vr;
+        int tb = t0;                                       // first row, relative to the resource
+        if constexpr (PAGED) {
+            const int nt = min(TK, n - t0);
+            krs = kvk.rows(j0 + t0, nt);
+            vrs = kvv.rows(j0 + t0, nt);
+            tb = 0;
+        }
 #pragma unroll
         for (int u = 0; u < NLD; ++u) {
             const int r = u * RPI + ld_r;
             const uint32_t col = 16u * (uint32_t)(ld_p ^ swz(r));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_ptr_t)(tk + u * 64), 16,
-                                                     (uint32_t)(t0 + r) * krow + col, 0, 0, kPolicyNT);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(tv + u * 64), 16,
-                                                     (uint32_t)(t0 + r) * vrow + col, 0, 0, kPolicyNT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(tk + u * 64), 16,
+                                                     (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(tv + u * 64), 16,
+                                                     (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
         }
     };
 
@@ -359,9 +369,16 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {
     const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
     if (grid <= 0) return hipSuccess;
+    const bool paged = a.block_table != nullptr;
     switch (d) {
-        case 64: hipLaunchKernelGGL(split_mfma_kernel<64>, dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(split_mfma_kernel<128>, dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a); break;
+        case 64:
+            if (paged) hipLaunchKernelGGL((split_mfma_kernel<64, 4, 1, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+            else hipLaunchKernelGGL((split_mfma_kernel<64>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+            break;
+        case 128:
+            if (paged) hipLaunchKernelGGL((split_mfma_kernel<128, 4, 1, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+            else hipLaunchKernelGGL((split_mfma_kernel<128>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

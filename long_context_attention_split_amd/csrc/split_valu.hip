@@ -43,7 +43,11 @@ namespace tad {
 // PF: software pipelining -- the next tile's loads are issued before the current
 // tile is consumed (two register tiles, alternating).
 // KVT: element type of K and V (kKvF32, kKvBF16, kKvE4M3, kKvE5M2).
-template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PF = false>
+// PAGED: K/V rows come from a paged cache through the block table; every wave tile
+// then lies inside one page (tile length divides the page size) and gets its own
+// buffer resource.
+template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PF = false,
+          bool PAGED = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
     using Row = RowChunk<KVT, POLICY>;
     constexpr int EPL = Row::EPL;                // elements per lane per key
@@ -54,6 +58,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     constexpr int T = KPW * U;                   // keys per wave tile
     constexpr int NW = kSplitThreads / 64;       // waves per work-group
     constexpr int SLOTS = NW * KPW;              // lane-group states to merge
+    static_assert(!PAGED || T == 16, "paged tiles are 16 keys: page sizes are multiples of 16");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -96,12 +101,13 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const int j1 = min(cr.j1, L), j0 = min(cr.j0, j1);
     const int n = j1 - j0;
 
-    // ---- per-chunk buffer resources: [chunk start, chunk end) of this head's K and V.
-    const uint32_t krow = (uint32_t)(a.skj * ELEM), vrow = (uint32_t)(a.svj * ELEM);
-    const char *kbase = (const char *)a.k + ((int64_t)b * a.skb + (int64_t)kvh * a.skh + (int64_t)j0 * a.skj) * ELEM;
-    const char *vbase = (const char *)a.v + ((int64_t)b * a.svb + (int64_t)kvh * a.svh + (int64_t)j0 * a.svj) * ELEM;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase, (uint32_t)n * krow);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase, (uint32_t)n * vrow);
+    // ---- buffer resources: one per chunk ([chunk start, chunk end) of this head's K
+    // and V), or, for a paged cache, one per tile (built in load_tile).
+    const KvRows kvk(a.k, ELEM, a.skb, a.skh, a.skj, a.skp, a, b, kvh);
+    const KvRows kvv(a.v, ELEM, a.svb, a.svh, a.svj, a.svp, a, b, kvh);
+    const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
+    const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
+    const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
 
     // ---- this lane's EPL query elements, pre-scaled into base-2 units (and by the
     // K dequantisation scale, which multiplies every score of this KV head).
@@ -142,10 +148,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const uint32_t lane_off = (uint32_t)(sub * EPL * ELEM);
     using Tile = Row[U];
     auto load_tile = [&](Tile &kk, Tile &vv, int t0) {
+        __amdgpu_buffer_rsrc_t krs = kr, vrs = vr;
+        int tb = t0;                                       // first row, relative to the resource
+        if constexpr (PAGED) {
+            const int nt = min(T, n - t0);
+            krs = kvk.rows(j0 + t0, nt);
+            vrs = kvv.rows(j0 + t0, nt);
+            tb = 0;
+        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) kk[u].load(kr, (uint32_t)(t0 + u * KPW + grp) * krow + lane_off);
+        for (int u = 0; u < U; ++u) kk[u].load(krs, (uint32_t)(tb + u * KPW + grp) * krow + lane_off);
 #pragma unroll
-        for (int u = 0; u < U; ++u) vv[u].load(vr, (uint32_t)(t0 + u * KPW + grp) * vrow + lane_off);
+        for (int u = 0; u < U; ++u) vv[u].load(vrs, (uint32_t)(tb + u * KPW + grp) * vrow + lane_off);
     };
     // One tile: scores, online max/sum update, value accumulation.
     auto consume = [&](const Tile &kk, const Tile &vv, int t0) {
@@ -272,6 +286,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
 
 template <int D, int KVT>
 static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
+    // paged caches: 16-key wave tiles (page sizes are multiples of 16)
+    constexpr int KPW = 64 * RowChunk<KVT, kPolicyNT>::EPL / D;
+    constexpr int UP = 16 / KPW > 0 ? 16 / KPW : 1;
     int64_t grid;
     const int gq = a.group * a.nq;
     if (gq == 1) {
@@ -281,10 +298,21 @@ static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
         grid = (units + 7) / 8 * 8 * gq;
     }
     if (grid <= 0) return hipSuccess;
-    if (gq == 1)
+    if (a.block_table) {
+        if constexpr (KVT == kKvF32 || D > 256) {
+            return hipErrorInvalidValue;                  // not offered for paged caches
+        } else if (gq == 1) {
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, false, true>), dim3((unsigned)grid),
+                               dim3(kSplitThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, false, true>), dim3((unsigned)grid),
+                               dim3(kSplitThreads), 0, st, a);
+        }
+    } else if (gq == 1) {
         hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-    else
+    } else {
         hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+    }
     return hipGetLastError();
 }
 

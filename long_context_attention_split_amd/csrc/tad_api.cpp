@@ -49,6 +49,9 @@ struct Problem {
     int64_t skb = 0, skh = 0, skj = 0;
     int64_t svb = 0, svh = 0, svj = 0;
     const float *k_scale = nullptr, *v_scale = nullptr;
+    // paged cache (block_table non-null): skh/skj are the head/row strides inside a page
+    const int32_t *block_table = nullptr;
+    int64_t max_pages = 0, page_size = 0, num_pages = 0, skp = 0, svp = 0;
 };
 
 // q or out: [B, H, d] (one token) or [B, H, nq, d].
@@ -128,6 +131,65 @@ int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
     return TAD_OK;
 }
 
+// k_cache or v_cache of a paged cache: [num_pages, page_size, Hkv, d].
+int parse_paged_kv(const tad_tensor *t, const char *name, int64_t *NP, int64_t *PS, int64_t *H, int64_t *d,
+                   int64_t *sp, int64_t *sj, int64_t *sh) {
+    if (!t) return fail(TAD_EINVAL, "%s: null tensor descriptor", name);
+    if (!t->data) return fail(TAD_EINVAL, "%s: null data pointer", name);
+    if (t->ndim != 4) return fail(TAD_EINVAL, "%s: a paged cache is 4-D [num_pages, page_size, Hkv, d]", name);
+    *NP = t->shape[0]; *PS = t->shape[1]; *H = t->shape[2]; *d = t->shape[3];
+    *sp = t->stride[0]; *sj = t->stride[1]; *sh = t->stride[2];
+    if (t->stride[3] != 1) return fail(TAD_ELAYOUT, "%s: innermost stride must be 1", name);
+    if (*NP < 1 || *PS < 1 || *H < 1 || *d < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
+    if (*PS % 16) return fail(TAD_EUNSUPPORTED, "%s: page_size must be a multiple of 16 (got %lld)", name,
+                              (long long)*PS);
+    if (t->dtype != TAD_BF16 && !is_fp8(t->dtype))
+        return fail(TAD_EDTYPE, "%s: a paged cache must be TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2", name);
+    if (t->scale && !is_fp8(t->dtype))
+        return fail(TAD_EINVAL, "%s: a dequantisation scale is only allowed for FP8 tensors", name);
+    const int64_t es = elem_size(t->dtype);
+    if (!aligned16(t->data) || (*sp * es) % 16 || (*sj * es) % 16 || (*sh * es) % 16)
+        return fail(TAD_ELAYOUT, "%s: rows must start on 16-byte boundaries", name);
+    if (*sj < *d) return fail(TAD_ELAYOUT, "%s: row stride smaller than d (rows overlap)", name);
+    if (*NP > 0x7fffffff || 16 * *sj * es >= (int64_t(1) << 32))
+        return fail(TAD_EUNSUPPORTED, "%s: sizes too large", name);
+    return TAD_OK;
+}
+
+int parse_paged_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const tad_paged_kv *pages,
+                        Problem *P) {
+    int rc;
+    if (!pages) return fail(TAD_EINVAL, "pages: null descriptor");
+    if (!pages->block_table) return fail(TAD_EINVAL, "pages: null block table");
+    if (pages->max_pages < 1) return fail(TAD_EINVAL, "pages: max_pages must be >= 1 (got %d)", pages->max_pages);
+    int64_t Bq, Hq, dq, nq;
+    if ((rc = parse_query_like(q, "q", &Bq, &Hq, &nq, &dq, &P->sqb, &P->sqh, &P->sqt))) return rc;
+    if (q->dtype != TAD_F32 && q->dtype != TAD_BF16) return fail(TAD_EDTYPE, "q: dtype must be TAD_F32 or TAD_BF16");
+    if (q->scale) return fail(TAD_EINVAL, "q: scale must be NULL");
+    const int64_t qes = elem_size(q->dtype);
+    if (!aligned16(q->data) || (P->sqb * qes) % 16 || (P->sqh * qes) % 16 || (P->sqt * qes) % 16)
+        return fail(TAD_ELAYOUT, "q: rows must start on 16-byte boundaries");
+    int64_t NPk, PSk, Hk, dk, NPv, PSv, Hv, dv;
+    if ((rc = parse_paged_kv(k, "k_cache", &NPk, &PSk, &Hk, &dk, &P->skp, &P->skj, &P->skh))) return rc;
+    if ((rc = parse_paged_kv(v, "v_cache", &NPv, &PSv, &Hv, &dv, &P->svp, &P->svj, &P->svh))) return rc;
+    if (k->dtype != v->dtype) return fail(TAD_EDTYPE, "k_cache and v_cache must share a dtype");
+    if (NPk != NPv || PSk != PSv || Hk != Hv || dk != dv) return fail(TAD_EINVAL, "k_cache and v_cache shapes differ");
+    if (dk != dq) return fail(TAD_EINVAL, "head dim of q (%lld) and k_cache (%lld) differ", (long long)dq, (long long)dk);
+    if (Hq % Hk) return fail(TAD_EINVAL, "query heads (%lld) not a multiple of KV heads (%lld)", (long long)Hq, (long long)Hk);
+    if (dq != 64 && dq != 128 && dq != 256)
+        return fail(TAD_EUNSUPPORTED, "head dim %lld not supported with a paged cache (64, 128, 256)", (long long)dq);
+    const int64_t Lmax = (int64_t)pages->max_pages * PSk;
+    if (Bq > 0x7fffffff || Hq > 0x7fffffff || Lmax > 0x3fffffff || Bq * Hq * nq > 0x7fffffff)
+        return fail(TAD_EUNSUPPORTED, "sizes too large");
+    P->B = Bq; P->Hq = Hq; P->Hkv = Hk; P->Lmax = Lmax; P->d = dq; P->nq = nq;
+    P->skb = P->svb = 0;
+    P->q_dtype = q->dtype; P->kv_dtype = k->dtype;
+    P->k_scale = k->scale; P->v_scale = v->scale;
+    P->block_table = pages->block_table;
+    P->max_pages = pages->max_pages; P->page_size = PSk; P->num_pages = NPk;
+    return TAD_OK;
+}
+
 int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *soh, int64_t *sot) {
     int rc;
     int64_t B, H, d, nq;
@@ -141,6 +203,7 @@ int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *so
 
 // 32-bit buffer offsets: one chunk plus a tile of overrun must span < 4 GiB.
 int check_offsets(const Problem &P, int64_t S) {
+    if (P.block_table) return TAD_OK;    // paged: one resource per 16-key tile (checked in parse_paged_kv)
     const int64_t es = elem_size(P.kv_dtype);
     const int64_t c = (P.Lmax + S - 1) / S;
     const int64_t span_k = (c + 64) * P.skj * es, span_v = (c + 64) * P.svj * es;
@@ -220,6 +283,9 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     a.skb = P.skb; a.skh = P.skh; a.skj = P.skj;
     a.svb = P.svb; a.svh = P.svh; a.svj = P.svj;
     a.seq_lens = seq_lens; a.slopes = slopes;
+    a.block_table = P.block_table;
+    a.max_pages = (int32_t)P.max_pages; a.page_size = (int32_t)P.page_size; a.num_pages = (int32_t)P.num_pages;
+    a.skp = P.skp; a.svp = P.svp;
     a.B = (int32_t)P.B; a.Hq = (int32_t)P.Hq; a.Hkv = (int32_t)P.Hkv; a.Lmax = (int32_t)P.Lmax;
     a.S = S; a.group = (int32_t)(P.Hq / P.Hkv);
     a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
@@ -269,11 +335,12 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);
 }
 
-// Validation shared by tad_decode and tad_decode_ws; resolves automatic n_splits.
-int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, int32_t n_splits,
-                   const tad_tensor *out, Problem *P, int32_t *S, OutDesc *od) {
+// Validation shared by the decode entry points (pages non-null: paged cache);
+// resolves automatic n_splits.
+int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const tad_paged_kv *pages,
+                   int32_t n_splits, const tad_tensor *out, Problem *P, int32_t *S, OutDesc *od) {
     int rc;
-    if ((rc = parse_problem(q, k, v, P))) return rc;
+    if ((rc = pages ? parse_paged_problem(q, k, v, pages, P) : parse_problem(q, k, v, P))) return rc;
     if ((rc = check_out(out, *P, &od->sob, &od->soh, &od->sot))) return rc;
     od->data = (float *)out->data;
     if (n_splits <= 0) {
@@ -285,6 +352,63 @@ int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v
     }
     if ((rc = check_splits(*S))) return rc;
     return check_offsets(*P, *S);
+}
+
+int split_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const tad_paged_kv *pages,
+               const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits, void *ws, size_t ws_bytes,
+               hipStream_t stream) {
+    Problem P;
+    int rc;
+    if ((rc = pages ? parse_paged_problem(q, k, v, pages, &P) : parse_problem(q, k, v, &P))) return rc;
+    if ((rc = check_splits(n_splits))) return rc;
+    if ((rc = check_offsets(P, n_splits))) return rc;
+    WsPtrs w;
+    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, n_splits, P.d, &w))) return rc;
+    if (P.B == 0) return ok();
+    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, OutDesc(), stream))) return rc;
+    return ok();
+}
+
+int decode_ws_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const tad_paged_kv *pages,
+                   const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits, tad_tensor *out, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+    Problem P;
+    int32_t S;
+    OutDesc od;
+    int rc;
+    if ((rc = prepare_decode(q, k, v, pages, n_splits, out, &P, &S, &od))) return rc;
+    WsPtrs w;
+    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, S, P.d, &w))) return rc;
+    if (P.B == 0) return ok();
+    if ((rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream))) return rc;
+    return ok();
+}
+
+int decode_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const tad_paged_kv *pages,
+                const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits, tad_tensor *out,
+                hipStream_t stream) {
+    Problem P;
+    int32_t S;
+    OutDesc od;
+    int rc;
+    if ((rc = prepare_decode(q, k, v, pages, n_splits, out, &P, &S, &od))) return rc;
+    if (P.B == 0) return ok();
+    const int64_t rows = P.B * P.Hq * P.nq;
+    const size_t bytes = tad::ws_layout(rows, S, P.d).total;
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, bytes, stream);
+    if (e != hipSuccess) return fail(TAD_EHIP, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
+    WsPtrs w;
+    rc = carve_ws(ws, bytes, rows, S, P.d, &w);
+    if (!rc) {
+        hipError_t ez = tad::launch_fill_zero(w.cnt, rows, stream);
+        if (ez != hipSuccess) rc = fail(TAD_EHIP, "counter clear launch: %s", hipGetErrorString(ez));
+    }
+    if (!rc) rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream);
+    e = hipFreeAsync(ws, stream);
+    if (rc) return rc;
+    if (e != hipSuccess) return fail(TAD_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // namespace
@@ -319,16 +443,14 @@ int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream) {
 
 int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
               const float *alibi_slopes, int32_t n_splits, void *ws, size_t ws_bytes, hipStream_t stream) {
-    Problem P;
-    int rc;
-    if ((rc = parse_problem(q, k, v, &P))) return rc;
-    if ((rc = check_splits(n_splits))) return rc;
-    if ((rc = check_offsets(P, n_splits))) return rc;
-    WsPtrs w;
-    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, n_splits, P.d, &w))) return rc;
-    if (P.B == 0) return ok();
-    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, OutDesc(), stream))) return rc;
-    return ok();
+    return split_impl(q, k, v, nullptr, seq_lens, alibi_slopes, n_splits, ws, ws_bytes, stream);
+}
+
+int tad_split_paged(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,
+                    const tad_paged_kv *pages, const int32_t *seq_lens, const float *alibi_slopes,
+                    int32_t n_splits, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!pages) return fail(TAD_EINVAL, "pages: null descriptor");
+    return split_impl(q, k_cache, v_cache, pages, seq_lens, alibi_slopes, n_splits, ws, ws_bytes, stream);
 }
 
 int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t nq, int32_t n_splits,
@@ -353,42 +475,26 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
 int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
                   const float *alibi_slopes, int32_t n_splits, tad_tensor *out, void *ws, size_t ws_bytes,
                   hipStream_t stream) {
-    Problem P;
-    int32_t S;
-    OutDesc od;
-    int rc;
-    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &od))) return rc;
-    WsPtrs w;
-    if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, S, P.d, &w))) return rc;
-    if (P.B == 0) return ok();
-    if ((rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream))) return rc;
-    return ok();
+    return decode_ws_impl(q, k, v, nullptr, seq_lens, alibi_slopes, n_splits, out, ws, ws_bytes, stream);
 }
 
 int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
                const float *alibi_slopes, int32_t n_splits, tad_tensor *out, hipStream_t stream) {
-    Problem P;
-    int32_t S;
-    OutDesc od;
-    int rc;
-    if ((rc = prepare_decode(q, k, v, n_splits, out, &P, &S, &od))) return rc;
-    if (P.B == 0) return ok();
-    const int64_t rows = P.B * P.Hq * P.nq;
-    const size_t bytes = tad::ws_layout(rows, S, P.d).total;
-    void *ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, bytes, stream);
-    if (e != hipSuccess) return fail(TAD_EHIP, "hipMallocAsync(%zu): %s", bytes, hipGetErrorString(e));
-    WsPtrs w;
-    rc = carve_ws(ws, bytes, rows, S, P.d, &w);
-    if (!rc) {
-        hipError_t ez = tad::launch_fill_zero(w.cnt, rows, stream);
-        if (ez != hipSuccess) rc = fail(TAD_EHIP, "counter clear launch: %s", hipGetErrorString(ez));
-    }
-    if (!rc) rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream);
-    e = hipFreeAsync(ws, stream);
-    if (rc) return rc;
-    if (e != hipSuccess) return fail(TAD_EHIP, "hipFreeAsync: %s", hipGetErrorString(e));
-    return ok();
+    return decode_impl(q, k, v, nullptr, seq_lens, alibi_slopes, n_splits, out, stream);
+}
+
+int tad_decode_paged_ws(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,
+                        const tad_paged_kv *pages, const int32_t *seq_lens, const float *alibi_slopes,
+                        int32_t n_splits, tad_tensor *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!pages) return fail(TAD_EINVAL, "pages: null descriptor");
+    return decode_ws_impl(q, k_cache, v_cache, pages, seq_lens, alibi_slopes, n_splits, out, ws, ws_bytes, stream);
+}
+
+int tad_decode_paged(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,
+                     const tad_paged_kv *pages, const int32_t *seq_lens, const float *alibi_slopes,
+                     int32_t n_splits, tad_tensor *out, hipStream_t stream) {
+    if (!pages) return fail(TAD_EINVAL, "pages: null descriptor");
+    return decode_impl(q, k_cache, v_cache, pages, seq_lens, alibi_slopes, n_splits, out, stream);
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 
+#include "device_util.h"
+
 namespace tad {
 
 // Everything the split kernels need, by value (lives in the kernel argument segment).
@@ -20,6 +22,12 @@ struct SplitArgs {
     int64_t svb, svh, svj;  // v element strides
     const int32_t *seq_lens;  // [B] or null
     const float *slopes;      // [Hq] or null
+    // Paged K/V cache (block_table non-null): k and v are [num_pages, page_size, Hkv, d]
+    // with page strides skp / svp, row strides skj / svj and head strides skh / svh;
+    // key j of row b lives in page block_table[b * max_pages + j / page_size].
+    const int32_t *block_table;
+    int32_t max_pages, page_size, num_pages;
+    int64_t skp, svp;
     int32_t B, Hq, Hkv, Lmax, S, group;
     float qscale;           // d^-1/2 * log2(e): scores come out in base-2 units
     float *ws_m, *ws_l, *ws_o;  // partial arrays (see tad.h)
@@ -64,13 +72,50 @@ __device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int
         for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
         Lref = mx;
     }
-    const int c = (Lref + a.S - 1) / a.S;
+    int c = (Lref + a.S - 1) / a.S;
+    if (a.block_table) c = (c + a.page_size - 1) / a.page_size * a.page_size;   // whole pages
     ChunkRange r;
     r.L = L;
     r.j0 = (int)min((int64_t)s * c, (int64_t)L);
     r.j1 = min(r.j0 + c, L);
     return r;
 }
+
+// Rows of one (b, kv head) of K or V: a strided slab, or pages of a paged cache.
+struct KvRows {
+    const char *base;       // slab: row 0 of the (b, kv head); paged: cache + kv-head offset
+    uint32_t row_bytes;
+    const int32_t *table;   // paged: this batch row's block-table row, else null
+    int page_size, num_pages;
+    int64_t page_bytes;
+
+    __device__ __forceinline__ KvRows(const void *t, int elem, int64_t sb, int64_t sh, int64_t sj, int64_t sp,
+                                      const SplitArgs &a, int b, int kvh) {
+        row_bytes = (uint32_t)(sj * elem);
+        if (a.block_table) {
+            base = (const char *)t + (int64_t)kvh * sh * elem;
+            table = a.block_table + (int64_t)b * a.max_pages;
+            page_size = a.page_size;
+            num_pages = a.num_pages;
+            page_bytes = sp * elem;
+        } else {
+            base = (const char *)t + ((int64_t)b * sb + (int64_t)kvh * sh) * elem;
+            table = nullptr;
+            page_size = num_pages = 0;
+            page_bytes = 0;
+        }
+    }
+    // Buffer resource over rows [j, j + rows).  Paged: [j, j + rows) must lie in one
+    // page; a block-table entry outside [0, num_pages) gives an empty range, so those
+    // keys and values read as zero instead of touching memory outside the cache.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows(int j, int n) const {
+        if (!table) return make_rsrc(base + (int64_t)j * row_bytes, (uint32_t)n * row_bytes);
+        const int page = table[j / page_size];
+        if (page < 0 || page >= num_pages) return make_rsrc(base, 0u);
+        return make_rsrc(base + (int64_t)page * page_bytes + (int64_t)(j % page_size) * row_bytes,
+                         (uint32_t)n * row_bytes);
+    }
+};
 
 // Workspace carving (same arithmetic as tad_workspace_bytes).
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }

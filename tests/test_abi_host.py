@@ -207,6 +207,89 @@ def test_chunk_span_limit(lib):
     assert call_split(so, a, n_splits=4, ws_bytes=0) == tad.TAD_EWORKSPACE   # passes the span check
 
 
+def paged_good(B=2, Hq=8, Hkv=2, NP=20, PS=16, d=128, max_pages=7):
+    return dict(q=desc([B, Hq, d], tad.TAD_F32), k=desc([NP, PS, Hkv, d]), v=desc([NP, PS, Hkv, d]),
+                out=desc([B, Hq, d], tad.TAD_F32), pages=tad.TadPagedKv(FAKE, max_pages))
+
+
+def call_split_paged(so, a, n_splits=4, ws=FAKE, ws_bytes=1 << 30, pages=True):
+    pg = ctypes.byref(a["pages"]) if pages else None
+    return so.tad_split_paged(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]), pg, None, None,
+                              n_splits, ws, ws_bytes, None)
+
+
+def call_decode_paged_ws(so, a, n_splits=4, ws=FAKE, ws_bytes=1 << 30):
+    return so.tad_decode_paged_ws(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                                  ctypes.byref(a["pages"]), None, None, n_splits, ctypes.byref(a["out"]), ws,
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: a.update(k=desc([20, 16, 2, 128], tad.TAD_F32), v=desc([20, 16, 2, 128], tad.TAD_F32)),
+     tad.TAD_EDTYPE),                                                                        # fp32 cache
+    (lambda a: a.update(k=desc([20, 24, 2, 128]), v=desc([20, 24, 2, 128])), tad.TAD_EUNSUPPORTED),  # page 24
+    (lambda a: a.update(q=desc([2, 8, 512], tad.TAD_F32), k=desc([20, 16, 2, 512]), v=desc([20, 16, 2, 512]),
+                        out=desc([2, 8, 512], tad.TAD_F32)), tad.TAD_EUNSUPPORTED),          # d 512
+    (lambda a: a.update(k=desc([320, 2, 128])), tad.TAD_EINVAL),                             # 3-D cache
+    (lambda a: a.update(v=desc([20, 16, 4, 128])), tad.TAD_EINVAL),                          # k/v heads differ
+    (lambda a: a.update(v=desc([21, 16, 2, 128])), tad.TAD_EINVAL),                          # k/v pages differ
+    (lambda a: a.update(k=desc([20, 16, 2, 128], strides=[4096, 256, 128, 2])), tad.TAD_ELAYOUT),
+    (lambda a: a.update(k=desc([20, 16, 2, 128], strides=[4096, 256, 132, 1])), tad.TAD_ELAYOUT),  # 264 B
+    (lambda a: a.update(k=desc([20, 16, 2, 128], strides=[4096, 100, 128, 1])), tad.TAD_ELAYOUT),  # overlap
+    (lambda a: a.update(k=desc([20, 16, 2, 128], addr=FAKE + 8)), tad.TAD_ELAYOUT),
+    (lambda a: a.update(pages=tad.TadPagedKv(FAKE, 0)), tad.TAD_EINVAL),                     # no pages
+    (lambda a: a.update(pages=tad.TadPagedKv(None, 7)), tad.TAD_EINVAL),                     # null table
+    (lambda a: a.update(pages=tad.TadPagedKv(FAKE, 1 << 27)), tad.TAD_EUNSUPPORTED),         # Lmax 2^31
+    (lambda a: a.update(q=desc([2, 6, 128], tad.TAD_F32), k=desc([20, 16, 4, 128]), v=desc([20, 16, 4, 128])),
+     tad.TAD_EINVAL),                                                                        # 6 % 4 heads
+    (lambda a: a.update(q=desc([2, 8, 64], tad.TAD_F32)), tad.TAD_EINVAL),                   # head dim
+])
+def test_split_paged_rejects_bad_arguments(lib, mutate, code):
+    so = lib.load()
+    a = paged_good()
+    mutate(a)
+    rc = call_split_paged(so, a)
+    assert rc == code, lib.tad_last_error()
+    assert lib.tad_last_error() != ""
+
+
+def test_paged_entry_points_validate_like_the_contiguous_ones(lib):
+    so = lib.load()
+    a = paged_good()
+    assert call_split_paged(so, a, pages=False) == tad.TAD_EINVAL               # null pages descriptor
+    assert call_split_paged(so, a, ws_bytes=0) == tad.TAD_EWORKSPACE           # all else valid
+    assert call_split_paged(so, a, n_splits=0) == tad.TAD_EINVAL
+    need = lib.tad_workspace_bytes(2, 8, 1, 4, 128)
+    assert call_split_paged(so, a, ws_bytes=need - 1) == tad.TAD_EWORKSPACE
+    # FP8 caches with scales are accepted; a scale on a bf16 cache is not
+    f = paged_good()
+    f["k"] = desc([20, 16, 2, 128], tad.TAD_FP8_E4M3)
+    f["v"] = desc([20, 16, 2, 128], tad.TAD_FP8_E4M3)
+    f["k"].scale = FAKE
+    assert call_split_paged(so, f, ws_bytes=0) == tad.TAD_EWORKSPACE
+    g = paged_good()
+    g["k"].scale = FAKE
+    assert call_split_paged(so, g) == tad.TAD_EINVAL
+    # out is checked, several query tokens are accepted
+    o = paged_good()
+    o["out"] = desc([2, 8, 64], tad.TAD_F32)
+    assert call_decode_paged_ws(so, o) == tad.TAD_EINVAL
+    o["q"] = desc([2, 8, 5, 128], tad.TAD_F32)
+    o["out"] = desc([2, 8, 5, 128], tad.TAD_F32)
+    assert call_decode_paged_ws(so, o, ws_bytes=0) == tad.TAD_EWORKSPACE
+    # a [num_pages, Hkv, page_size, d] cache seen through strides is a legal layout
+    t = paged_good()
+    t["k"] = desc([20, 16, 2, 128], strides=[4096, 128, 2048, 1])
+    assert call_split_paged(so, t, ws_bytes=0) == tad.TAD_EWORKSPACE
+    # empty batch: no-op success
+    e = paged_good(B=0)
+    assert call_split_paged(so, e) == tad.TAD_OK
+    assert call_decode_paged_ws(so, e) == tad.TAD_OK
+    rc = so.tad_decode_paged(ctypes.byref(e["q"]), ctypes.byref(e["k"]), ctypes.byref(e["v"]), None, None, None,
+                             4, ctypes.byref(e["out"]), None)
+    assert rc == tad.TAD_EINVAL
+
+
 def test_auto_splits_without_device_reports_hip_error(lib):
     import torch
     if torch.cuda.is_available():

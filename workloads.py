@@ -31,6 +31,10 @@ id     description
 6      workload 2 with FP8 (OCP E4M3) K and V: each (b, kv-head) slab of N(0,1)
        draws is divided by its amax/448 and rounded to E4M3; the scale is kept.
 =====  =========================================================================
+
+``page_kv`` lays any of these K/V tensors out as a paged cache: pages of
+``page_size`` rows in a pool with a few spare pages, assigned to (b, logical page)
+by a seeded random permutation (seed + 5), every unused row poisoned with NaN.
 """
 from __future__ import annotations
 
@@ -225,3 +229,52 @@ def random_case(seed: int, B: int, Hq: int, Hkv: int, L: int, d: int, q_dtype=F3
                     v[b, :, Lb:, :] = float("nan")
     slopes = alibi_slopes(Hq) if alibi else None
     return dict(q=q, k=k, v=v, seq_lens=sl, slopes=slopes, k_scale=ks, v_scale=vs)
+
+
+def _raw(t: torch.Tensor) -> torch.Tensor:
+    """Bit view (int16 for 2-byte, uint8 for 1-byte, int32 for 4-byte elements)."""
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()])
+
+
+def _nan_bits(dtype) -> int:
+    if dtype == torch.float8_e4m3fn:
+        return 0x7F
+    if dtype == torch.float8_e5m2:
+        return 0x7E
+    return int(torch.tensor(float("nan"), dtype=dtype).view({2: torch.int16, 4: torch.int32}[
+        torch.tensor(0, dtype=dtype).element_size()]))
+
+
+def page_kv(k: torch.Tensor, v: torch.Tensor, page_size: int, seed: int, spare: int = 3,
+            head_major: bool = False):
+    """Copy [B, Hkv, L, d] K and V into a paged cache.
+
+    Returns (k_cache, v_cache, block_table): caches shaped [num_pages, page_size, Hkv, d]
+    with num_pages = B * ceil(L / page_size) + spare, and block_table int32
+    [B, ceil(L / page_size)] whose entry [b, p] is the page holding logical rows
+    [p * page_size, (p + 1) * page_size) of batch row b.  Pages are handed out by a
+    seeded random permutation of the pool; rows no logical key maps to (spare pages,
+    the tail of the last page) hold NaN.  head_major stores each page as
+    [Hkv, page_size, d] (the returned caches are then strided views of that storage).
+    Pure data movement, on bit views: values are copied exactly."""
+    B, Hkv, L, d = k.shape
+    mp = max(1, -(-L // page_size))
+    n_pages = B * mp + spare
+    perm = torch.randperm(n_pages, generator=_gen(seed + 5))
+    table = perm[:B * mp].view(B, mp).to(torch.int32)
+    caches = []
+    for x in (k, v):
+        fill = _nan_bits(x.dtype)
+        padded = torch.full((B, Hkv, mp * page_size, d), fill, dtype=_raw(x).dtype)
+        padded[:, :, :L] = _raw(x)
+        pages = padded.view(B, Hkv, mp, page_size, d)
+        if head_major:
+            store = torch.full((n_pages, Hkv, page_size, d), fill, dtype=padded.dtype)
+            store[table.view(-1).long()] = pages.permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, page_size, d)
+            cache = store.view(x.dtype).permute(0, 2, 1, 3)
+        else:
+            store = torch.full((n_pages, page_size, Hkv, d), fill, dtype=padded.dtype)
+            store[table.view(-1).long()] = pages.permute(0, 2, 3, 1, 4).reshape(B * mp, page_size, Hkv, d)
+            cache = store.view(x.dtype)
+        caches.append(cache)
+    return caches[0], caches[1], table
