@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark: split-KV exact decode on one MI355X, 128k-token MHA workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S] [--page-size P]
 
 One step = one full decode over the workload's inputs, already resident in HBM:
 the split kernel then the combine kernel (tad_split + tad_combine, which is what
-tad_decode_ws runs at this size).  W untimed steps, then K timed steps between two
+tad_decode_ws runs at this size); with --page-size the K/V are first copied into
+a paged cache (a permuted page pool, workloads.page_kv) and the split step is
+tad_split_paged.  W untimed steps, then K timed steps between two
 device synchronisations.  Rank 0 prints one JSON line with:
 
 - value: KV-read throughput in GB/s (algorithmic K+V bytes / step time),
@@ -46,10 +48,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: int):
+def read_traffic(workload: int, page_size: int = 0):
     """HBM bytes per split-kernel launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    names = ["split_kernel_workload%d_traffic.txt" % workload, "split_mfma_workload%d_traffic.txt" % workload]
+    if page_size:
+        names = ["split_paged%d_workload%d_traffic.txt" % (page_size, workload)]
+    else:
+        names = ["split_kernel_workload%d_traffic.txt" % workload, "split_mfma_workload%d_traffic.txt" % workload]
     paths = [os.path.join(ROOT, "profiles", n) for n in names if os.path.exists(os.path.join(ROOT, "profiles", n))]
     if not paths:
         return None
@@ -117,6 +122,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--splits", type=int, default=0, help="chunks per head (0: automatic)")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="read K/V from a paged cache with pages of this many rows (0: contiguous)")
+    ap.add_argument("--head-major-pages", action="store_true",
+                    help="store each page as [Hkv, page_size, d] instead of [page_size, Hkv, d]")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for HBM byte counters)")
@@ -142,15 +151,21 @@ def main(argv=None) -> int:
     print("[bench] workload %d generated in %.1fs" % (args.workload, time.perf_counter() - t_gen),
           file=sys.stderr, flush=True)
     q = c["q"].to(dev)
-    k = c["k"].to(dev)
-    v = c["v"].to(dev)
+    if args.page_size:
+        kc, vc, table = W.page_kv(c["k"], c["v"], args.page_size, 1000 * args.workload,
+                                  head_major=args.head_major_pages)
+        k, v, table = kc.to(dev), vc.to(dev), table.to(dev)
+        del kc, vc
+    else:
+        k = c["k"].to(dev)
+        v = c["v"].to(dev)
     sl = c["seq_lens"].to(dev) if c["seq_lens"] is not None else None
     sp = c["slopes"].to(dev) if c["slopes"] is not None else None
     ks = c["k_scale"].to(dev) if c["k_scale"] is not None else None
     vs = c["v_scale"].to(dev) if c["v_scale"] is not None else None
-    S = args.splits if args.splits > 0 else tad.resolve_splits(q, k, c["n_splits"])
-    B, Hq, Hkv, Lmax, d = tad.shape_of(q, k)
-    ws = tad.workspace(q, k, S)
+    B, Hq, Hkv, Lmax, d = tad.shape_of(c["q"], c["k"])
+    S = args.splits if args.splits > 0 else (c["n_splits"] if c["n_splits"] > 0 else tad.tad_auto_splits(B, Hkv, Lmax))
+    ws = tad.workspace(q, c["k"], S)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     kv_bytes = w.kv_bytes(c["seq_lens"])
     stream = torch.cuda.current_stream()
@@ -160,7 +175,10 @@ def main(argv=None) -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
+        if args.page_size:
+            tad.tad_split_paged(q, k, v, table, sl, sp, S, ws, stream, ks, vs)
+        else:
+            tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
         if ev is not None:
             ev[1].record(stream)
         tad.tad_combine(ws, B, Hq, 1, S, d, out, stream)
@@ -185,7 +203,9 @@ def main(argv=None) -> int:
     print("[bench] step %.1f us (split kernel %.1f us, combine + gaps %.1f us), %.0f GB/s" %
           (ms_per_step * 1e3, split_avg * 1e3, comb_avg * 1e3, gbs), file=sys.stderr, flush=True)
 
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload, args.page_size)
+    kv_name = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8-e4m3",
+               torch.float8_e5m2: "fp8-e5m2"}[w.kv_dtype]
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -200,11 +220,13 @@ def main(argv=None) -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
+        "kv_dtype": kv_name,
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax,
             "n_splits": S, "kv_bytes_per_step": kv_bytes,
+            "kv_layout": ("paged, %d-row pages%s" % (args.page_size, ", head-major" if args.head_major_pages else ""))
+                         if args.page_size else "contiguous",
         },
         "split_kernel_us": round(split_avg * 1e3, 2),
         "combine_and_gaps_us": round(comb_avg * 1e3, 2),
@@ -215,7 +237,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(split_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "split (tad_split)",
+            "kernel": "split (tad_split_paged)" if args.page_size else "split (tad_split)",
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtad.so")
 
-SOURCES = ["tad_api.cpp", "split_valu.hip", "split_mfma.hip", "combine.hip"]
+SOURCES = ["tad_api.cpp", "split_valu.hip", "split_mfma.hip", "split_heads.hip", "combine.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

@@ -130,6 +130,7 @@ void split_mfma_kernel(SplitArgs a) {
     const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
     const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
+    TilePages pages;                                       // paged: this wave's tile pages
 
     // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo.
     uint4 qhi[NKK], qlo[NKK];
@@ -186,8 +187,9 @@ void split_mfma_kernel(SplitArgs a) {
         int tb = t0;                                       // first row, relative to the resource
         if constexpr (PAGED) {
             const int nt = min(TK, n - t0);
-            krs = kvk.rows(j0 + t0, nt);
-            vrs = kvv.rows(j0 + t0, nt);
+            const int page = pages.get(kvk, j0, n, wave * TK, NW * TK, (t0 - wave * TK) / (NW * TK));
+            krs = kvk.page_rows(page, j0 + t0, nt);
+            vrs = kvv.page_rows(page, j0 + t0, nt);
             tb = 0;
         }
 #pragma unroll

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
     const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
+    TilePages pages;                                       // paged: this wave's tile pages
 
     // ---- this lane's EPL query elements, pre-scaled into base-2 units (and by the
     // K dequantisation scale, which multiplies every score of this KV head).
@@ -152,8 +153,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
         int tb = t0;                                       // first row, relative to the resource
         if constexpr (PAGED) {
             const int nt = min(T, n - t0);
-            krs = kvk.rows(j0 + t0, nt);
-            vrs = kvv.rows(j0 + t0, nt);
+            const int page = pages.get(kvk, j0, n, wave * T, NW * T, (t0 - wave * T) / (NW * T));
+            krs = kvk.page_rows(page, j0 + t0, nt);
+            vrs = kvv.page_rows(page, j0 + t0, nt);
             tb = 0;
         }
 #pragma unroll

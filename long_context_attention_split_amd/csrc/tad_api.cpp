@@ -267,11 +267,12 @@ struct OutDesc {
     int64_t sob = 0, soh = 0, sot = 0;
 };
 
-// Launch the split kernel.  With out.data non-null the kernel also merges (fused: the
-// last work-group of each row merges it, using the workspace's arrival counters).
-int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
-                 const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
-                 const OutDesc &out, hipStream_t stream) {
+// Kernel arguments of a split launch.  With out.data non-null the kernel also merges
+// (fused: the last work-group of each row merges it, using the workspace's arrival
+// counters).
+tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+                          const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
+                          const OutDesc &out) {
     tad::SplitArgs a;
     a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.sqt = P.sqt; a.q_bf16 = P.q_dtype == TAD_BF16;
     a.nq = (int32_t)P.nq;
@@ -294,9 +295,21 @@ int launch_split(const Problem &P, const tad_tensor *q, const tad_tensor *k, con
     a.cnt = w.cnt;
     a.out = out.data;
     a.sob = out.sob; a.soh = out.soh; a.sot = out.sot;
-    hipError_t e = tad::split_mfma_supported((int)P.d, a.kv_type, a.group, a.nq)
-                       ? tad::launch_split_mfma(a, (int)P.d, stream)
-                       : tad::launch_split_valu(a, (int)P.d, stream);
+    return a;
+}
+
+// Launch the split kernel.  Kernel choice: query-head groups and several tokens on the
+// matrix cores; caches whose heads are interleaved per key (one query head per KV
+// head, unfused) on the head-packed vector kernel; everything else on the vector
+// kernel.
+int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream) {
+    hipError_t e;
+    if (tad::split_mfma_supported((int)d, a.kv_type, a.group, a.nq))
+        e = tad::launch_split_mfma(a, (int)d, stream);
+    else if (tad::split_heads_supported(a, (int)d))
+        e = tad::launch_split_heads(a, (int)d, stream);
+    else
+        e = tad::launch_split_valu(a, (int)d, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "split kernel launch: %s", hipGetErrorString(e));
     return TAD_OK;
 }
@@ -329,9 +342,13 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
     int cus = 0;
     int rc = device_cus(-1, &cus);
     if (rc) return rc;
-    if (S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus)
-        return launch_split(P, q, k, v, seq_lens, slopes, S, w, out, stream);
-    if ((rc = launch_split(P, q, k, v, seq_lens, slopes, S, w, OutDesc(), stream))) return rc;
+    const tad::SplitArgs unfused = split_args(P, q, k, v, seq_lens, slopes, S, w, OutDesc());
+    // (the head-packed kernel has no fused form; its layouts always take two launches,
+    // so that the result never depends on the grid size)
+    if (S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus &&
+        !tad::split_heads_supported(unfused, (int)P.d))
+        return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
+    if ((rc = launch_split(unfused, P.d, stream))) return rc;
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);
 }
 
@@ -365,7 +382,8 @@ int split_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, co
     WsPtrs w;
     if ((rc = carve_ws(ws, ws_bytes, P.B * P.Hq * P.nq, n_splits, P.d, &w))) return rc;
     if (P.B == 0) return ok();
-    if ((rc = launch_split(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, OutDesc(), stream))) return rc;
+    if ((rc = launch_split(split_args(P, q, k, v, seq_lens, alibi_slopes, n_splits, w, OutDesc()), P.d, stream)))
+        return rc;
     return ok();
 }
 

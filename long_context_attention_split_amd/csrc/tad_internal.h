@@ -110,10 +110,31 @@ struct KvRows {
     // keys and values read as zero instead of touching memory outside the cache.
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows(int j, int n) const {
         if (!table) return make_rsrc(base + (int64_t)j * row_bytes, (uint32_t)n * row_bytes);
-        const int page = table[j / page_size];
+        return page_rows(page_id(j), j, n);
+    }
+    // Paged: the block-table entry of the page holding row j (j < Lmax).
+    __device__ __forceinline__ int page_id(int j) const { return table[j / page_size]; }
+    // Paged: resource over rows [j, j + n) of the page with block-table entry `page`.
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rows(int page, int j, int n) const {
         if (page < 0 || page >= num_pages) return make_rsrc(base, 0u);
         return make_rsrc(base + (int64_t)page * page_bytes + (int64_t)(j % page_size) * row_bytes,
                          (uint32_t)n * row_bytes);
+    }
+};
+
+// Block-table entries of one wave's tiles, fetched 64 at a time with one vector load:
+// lane i holds the page of the wave's tile 64 q + i, so a tile's page is a register
+// read instead of a dependent memory load in front of its K/V loads.  Tile k of the
+// wave starts at row first + k * stride of a chunk of n rows starting at key j0;
+// get() must be called for k = 0, 1, 2, ... in order, by the whole wave.
+struct TilePages {
+    int lane_page = -1;
+    __device__ __forceinline__ int get(const KvRows &kv, int j0, int n, int first, int stride, int k) {
+        if ((k & 63) == 0) {
+            const int t = first + (k + (int)(threadIdx.x & 63)) * stride;
+            lane_page = t < n ? kv.page_id(j0 + t) : -1;
+        }
+        return __builtin_amdgcn_readlane(lane_page, k & 63);
     }
 };
 
@@ -139,6 +160,8 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
 hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t s);
 bool split_mfma_supported(int d, int kv_type, int group, int nq);
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
+bool split_heads_supported(const SplitArgs &a, int d);
+hipError_t launch_split_heads(const SplitArgs &a, int d, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);
 

@@ -1,0 +1,118 @@
+"""GPU parity for K/V caches whose heads are interleaved per key.
+
+A [B, L, Hkv, d] cache described as [B, Hkv, L, d] through strides (and paged caches
+with [page_size, Hkv, d] pages) store the heads of one key next to each other; with
+one query head per KV head the library reads them with the head-packed split kernel.
+Checked against the fp64 oracle on the same values, at the usual bars, across
+dtypes, head dims, chunk counts, ragged lengths and ALiBi; plus the fallbacks (head
+counts the kernel cannot pack) and the agreement of the entry points.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from test_parity_gpu import DEV, assert_parity, note, vmax_real
+
+pytestmark = pytest.mark.gpu
+
+
+def interleave(x):
+    """[B, H, L, d] -> the same values stored [B, L, H, d], viewed as [B, H, L, d] on the GPU."""
+    return x.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+
+
+def run_interleaved(lib, c, S):
+    g = lambda key: None if c.get(key) is None else c[key].to(DEV)
+    k, v = interleave(c["k"]), interleave(c["v"])
+    assert k.stride(1) == k.shape[-1]
+    out = lib.decode(c["q"].to(DEV), k, v, g("seq_lens"), g("slopes"), S, k_scale=g("k_scale"),
+                     v_scale=g("v_scale"))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_of(c):
+    return oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                             k_scale=c["k_scale"], v_scale=c["v_scale"])
+
+
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float32, torch.float8_e4m3fn, torch.float8_e5m2])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_interleaved_heads_dtypes_and_dims(lib, kv, d):
+    """16 heads (packed by 4), ragged lengths, several chunks."""
+    note("interleaved kv=%s d=%d" % (kv, d))
+    c = W.random_case(800 + d, 2, 16, 16, 1000, d, kv_dtype=kv, seq_lens=[1000, 613])
+    ref = oracle_of(c)
+    for S in (1, 7):
+        assert_parity(run_interleaved(lib, c, S), ref, kv, vmax_real(c), "interleaved S=%d" % S)
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 33, 300])
+def test_interleaved_split_counts_alibi(lib, S):
+    """Chunk counts from one to more chunks than keys per chunk tile; ALiBi; a zero
+    length and a length of one."""
+    c = W.random_case(820, 4, 8, 8, 1500, 128, seq_lens=[1500, 0, 1, 999], alibi=True)
+    note("interleaved alibi S=%d" % S)
+    out = run_interleaved(lib, c, S)
+    assert_parity(out, oracle_of(c), torch.bfloat16, vmax_real(c), "interleaved alibi S=%d" % S)
+    assert (out[1] == 0).all()
+
+
+def test_interleaved_bf16_query_and_large_logits(lib):
+    c = W.random_case(830, 2, 8, 8, 3000, 128, q_dtype=torch.bfloat16, k_scale=6.0)
+    assert_parity(run_interleaved(lib, c, 6), oracle_of(c), torch.bfloat16, vmax_real(c), "bf16 q")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(6, 6), (2, 2), (8, 2)])
+def test_interleaved_fallbacks(lib, Hq, Hkv):
+    """Head counts the kernel cannot pack (6 and 2 heads: it packs heads by 4)
+    and query-head groups take the other kernels; results are the same."""
+    c = W.random_case(840 + Hq, 2, Hq, Hkv, 900, 128, seq_lens=[900, 450])
+    assert_parity(run_interleaved(lib, c, 4), oracle_of(c), torch.bfloat16, vmax_real(c), "fallback")
+
+
+def test_interleaved_entry_points_agree(lib):
+    """For interleaved caches tad_decode_ws never fuses: tad_decode_ws, tad_decode and
+    tad_split + tad_combine are bit-identical on small and large grids."""
+    for B, H, S in ((1, 4, 2), (2, 32, 16)):
+        c = W.random_case(850 + B, B, H, H, 2000, 128, seq_lens=[2000, 1234][:B])
+        q, sl = c["q"].to(DEV), c["seq_lens"].to(DEV)
+        k, v = interleave(c["k"]), interleave(c["v"])
+        a = lib.decode(q, k, v, sl, None, S)
+        b = torch.empty_like(a)
+        lib.tad_decode(q, k, v, sl, None, S, b)
+        ws = lib.workspace(q, k, S)
+        lib.tad_split(q, k, v, sl, None, S, ws)
+        cc = torch.empty_like(a)
+        lib.tad_combine(ws, B, H, 1, S, 128, cc)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(a, cc)
+
+
+def test_interleaved_partials_match_contiguous(lib):
+    """The per-chunk partials of the head-packed kernel describe the same chunk
+    statistics as those of the contiguous layout (m equal up to rounding, l and o
+    close), chunk by chunk."""
+    c = W.random_case(860, 1, 8, 8, 2048, 128)
+    q = c["q"].to(DEV)
+    S = 4
+    m1, l1, o1 = lib.split_partials(q, c["k"].to(DEV), c["v"].to(DEV), None, None, S)
+    m2, l2, o2 = lib.split_partials(q, interleave(c["k"]), interleave(c["v"]), None, None, S)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(m2.cpu().numpy(), m1.cpu().numpy(), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(l2.cpu().numpy(), l1.cpu().numpy(), rtol=1e-5, atol=0)
+    np.testing.assert_allclose(o2.cpu().numpy(), o1.cpu().numpy(), rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("kv,d", [(torch.bfloat16, 128), (torch.float8_e4m3fn, 128), (torch.bfloat16, 64),
+                                  (torch.float8_e5m2, 256)])
+def test_paged_interleaved_heads(lib, kv, d):
+    """Paged caches with [page_size, Hkv, d] pages and enough heads to pack."""
+    from test_paged_gpu import paged_case, run_paged
+    note("paged interleaved kv=%s d=%d" % (kv, d))
+    c = paged_case(870 + d, 2, 16, 16, 1100, d, 16, kv, lens=[1100, 555])
+    ref = oracle_of(c)
+    for S in (3, 12):
+        assert_parity(run_paged(lib, c, S), ref, kv, vmax_real(c), "paged interleaved S=%d" % S)
