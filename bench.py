@@ -36,12 +36,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-step µs and KV-read HBM GB/s (% of peak) at 128k ctx, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-SPLIT_SOURCES = ("split_valu.hip", "split_mfma.hip", "device_util.h", "tad_internal.h")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files) -> str:
+    """Short sha256 over the named kernel sources (under the package's csrc/)."""
     h = hashlib.sha256()
-    for f in SPLIT_SOURCES:
+    for f in files:
         p = os.path.join(ROOT, "long_context_attention_split_amd", "csrc", f)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
@@ -64,7 +64,8 @@ def read_traffic(workload: int, page_size: int = 0):
         if "=" in ln and not ln.lstrip().startswith("#"):
             k, v = ln.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_hash():
+    files = [f.strip() for f in vals.get("kernel_sources", "").split(",") if f.strip()]
+    if not files or vals.get("kernel_source_sha") != kernel_source_hash(files):
         return None
     try:
         return int(vals["fetch_bytes_per_launch"]) + int(vals["write_bytes_per_launch"])

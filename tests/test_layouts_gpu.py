@@ -60,6 +60,15 @@ def test_interleaved_split_counts_alibi(lib, S):
     assert (out[1] == 0).all()
 
 
+def test_interleaved_many_ragged_rows(lib):
+    """80 rows (more than a wave has lanes) with lengths from 0 up, interleaved heads."""
+    g = torch.Generator().manual_seed(7)
+    lens = torch.randint(0, 257, (80,), generator=g).tolist()
+    lens[3] = 0
+    c = W.random_case(825, 80, 4, 4, 256, 128, seq_lens=lens)
+    assert_parity(run_interleaved(lib, c, 3), oracle_of(c), torch.bfloat16, vmax_real(c), "80 rows")
+
+
 def test_interleaved_bf16_query_and_large_logits(lib):
     c = W.random_case(830, 2, 8, 8, 3000, 128, q_dtype=torch.bfloat16, k_scale=6.0)
     assert_parity(run_interleaved(lib, c, 6), oracle_of(c), torch.bfloat16, vmax_real(c), "bf16 q")

@@ -116,6 +116,17 @@ def test_ragged_lengths_with_poisoned_tail(lib):
     assert (out[0] == 0).all()
 
 
+@pytest.mark.parametrize("B,Hq,Hkv", [(100, 2, 2), (70, 8, 2), (130, 4, 4)])
+def test_many_ragged_rows(lib, B, Hq, Hkv):
+    """More batch rows than a wave has lanes, lengths from 0 to the maximum: the
+    work-group -> (row, chunk) assignment that puts non-empty chunks first must still
+    give every (row, head, chunk) partial exactly once."""
+    g = torch.Generator().manual_seed(B + Hq)
+    lens = torch.randint(0, 301, (B,), generator=g).tolist()
+    lens[0], lens[-1], lens[B // 2] = 0, 300, 1
+    run_case(lib, 145 + B, B, Hq, Hkv, 300, 64, seq_lens=lens, n_splits=5)
+
+
 @pytest.mark.parametrize("g", [2, 4, 8])
 def test_grouped_query_heads(lib, g):
     run_case(lib, 150 + g, 2, 4 * g, 4, 1500, 128, seq_lens=[1500, 913], n_splits=6)
