@@ -26,11 +26,10 @@
 //    columns (zero past g).  fp32 q is split into bf16 hi + lo and both are
 //    multiplied (two MFMAs), keeping ~16 significant bits of q; K is exactly bf16.
 //    Lane l gets the scores of keys 4(l/16)+r for head l%16.
-//  * transpose: the same A operand of V times a 0/1 selector B[k][j] = (k == j+16h)
-//    gives C[key][j] = V[key][32kk + 16h + j], i.e. lane l holds keys 4(l/16)+r of
-//    one value column: the operand layout of the value product.  Exact.
 //  * value update (16x16x16): A = V^T (16 value columns x the tile's 16 keys),
-//    B = P^T (16 keys x heads), the probabilities split into bf16 hi + lo.
+//    B = P^T (16 keys x heads), the probabilities split into bf16 hi + lo.  The V^T
+//    operand comes straight from the row-major V tile in LDS through gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16), one read per 16 value columns.
 //
 // Softmax per head: lane l owns head l%16 and 4 of the tile's 16 keys; the lanes
 // l, l^16, l^32, l^48 exchange their max and sum.  The running (m, l) and the
@@ -52,12 +51,6 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Two fp32 values that are exact bf16 numbers -> one packed dword (x in the low half).
-__device__ __forceinline__ uint32_t pack_exact_bf16(float x, float y) {
-    // v_perm_b32: bytes {x.2, x.3, y.2, y.3} = (x >> 16) | (y & 0xffff0000)
-    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
-}
-
 // x = hi + lo with hi, lo bf16 (truncations): |x - hi - lo| <= 2^-16 |x|.
 __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
     const uint32_t h = __float_as_uint(x) & 0xffff0000u;
@@ -67,6 +60,7 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) 
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
@@ -155,21 +149,6 @@ void split_mfma_kernel(SplitArgs a) {
         qhi[kk] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
         qlo[kk] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
     }
-    // ---- selector B operands for the transpose: element t is 1 where 8*c4 + t == j16 + 16*half.
-    uint4 sel[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t0 = 8 * c4 + 2 * i - 16 * half;
-            const uint32_t lo16 = (t0 == j16) ? 0x3F80u : 0u;       // bf16 1.0
-            const uint32_t hi16 = (t0 + 1 == j16) ? 0x3F80u : 0u;
-            w[i] = lo16 | (hi16 << 16);
-        }
-        sel[half] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-
     const float slope2 = (a.slopes && head_ok) ? a.slopes[h] * 1.4426950408889634f : 0.f;
     const bool alibi = a.slopes != nullptr;
 
@@ -180,6 +159,18 @@ void split_mfma_kernel(SplitArgs a) {
     uint4 *const bufA = smem + wave * 2 * TILE;
     uint4 *const bufB = smem2 + (NBUF == 2 ? wave * 2 * TILE : 0);
     const int ld_r = lane / CH, ld_p = lane % CH;
+    // A operand of the value product for value columns [16 nb, 16 nb + 16): lane l needs
+    // V[4(l/16) + t][16 nb + l%16], t = 0..3.  ds_read_b64_tr_b16 hands lane i of a
+    // 16-lane group element i%4 of the 4-element pieces addressed by lanes i/4 + 4t of
+    // the group, so lane l addresses row 4(l/16) + (l%16)/4, elements 16 nb + 4(l%4) ..
+    // +3 (8 bytes inside one swizzled 16-byte chunk).
+    const int tr_row = 4 * c4 + (j16 >> 2);
+    auto read_vt = [&](const uint4 *tv, int nb) -> uint2 {
+        const int e = 16 * nb + 4 * (lane & 3);
+        const uint16_t *p = (const uint16_t *)(tv + tr_row * CH + ((e >> 3) ^ swz(tr_row))) + (e & 7);
+        const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p);
+        return __builtin_bit_cast(uint2, v);
+    };
     // HBM -> LDS, whole rows per instruction; rows past the chunk end read as zero.
     auto issue_tile = [&](uint4 *tk, int t0) {
         uint4 *tv = tk + TILE;
@@ -257,18 +248,12 @@ void split_mfma_kernel(SplitArgs a) {
         const uint2 phi = make_uint2(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16);
         const uint2 plo = make_uint2(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16);
 
-        // V^T blocks by the selector product, then the value update
+        // V^T blocks straight from LDS with the transposing read, then the value update
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const uint4 va = tv[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f32x4_t vt = mfma16x16x32(va, sel[half], zero4);
-                const uint2 vop = make_uint2(pack_exact_bf16(vt[0], vt[1]), pack_exact_bf16(vt[2], vt[3]));
-                const int nb = 2 * kk + half;
-                O[nb] = mfma16x16x16(vop, phi, O[nb]);
-                O[nb] = mfma16x16x16(vop, plo, O[nb]);
-            }
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint2 vop = read_vt(tv, nb);
+            O[nb] = mfma16x16x16(vop, phi, O[nb]);
+            O[nb] = mfma16x16x16(vop, plo, O[nb]);
         }
     };
 
