@@ -16,7 +16,9 @@
 // instruction covers whole consecutive rows -- the pattern that streams at full HBM
 // rate -- and the 16 lanes of a row fetch its 16-byte chunks in an XOR-swizzled
 // order, so that the matrix-core operand reads from LDS (16 rows, one chunk each)
-// hit 16 distinct bank groups.
+// hit 16 distinct bank groups.  A wave reads a landed tile's operands into registers,
+// issues the next tile's loads into the same buffer, and then computes, so the
+// next tile is in flight while the current one is consumed.
 //
 // Matrix instructions: v_mfma_f32_16x16x32_bf16 (lane l: A[i][k] with i = l%16,
 // B[k][j] with j = l%16, k in the 8-wide block l/16; C[i][j] with j = l%16,
@@ -70,11 +72,12 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // WAVES: occupancy target (waves per SIMD) the register allocator must meet.
-// NBUF: LDS tile buffers per wave; with 2, the next tile's loads are in flight while
-// the current one is consumed.
+// OVL: overlap loads with compute -- a tile's operands are read from LDS into
+// registers, the next tile's loads into the same LDS buffer are issued, and only then
+// is the tile consumed, so a wave always has a tile in flight.
 // PAGED: K/V rows come from a paged cache; each 16-key tile lies inside one page
 // (page sizes are multiples of 16) and gets its own buffer resources.
-template <int D, int WAVES = 4, int NBUF = 1, bool PAGED = false>
+template <int D, int WAVES = 4, bool OVL = false, bool PAGED = false>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
@@ -89,11 +92,8 @@ void split_mfma_kernel(SplitArgs a) {
     constexpr int MAXG = 16;
     static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
 
-    // Per wave: a (K tile, V tile) pair in smem, and a second pair in smem2 when
-    // double-buffering (separate arrays, so the compiler can tell a read of one
-    // buffer from a load still landing in the other).  smem is reused for the merge.
+    // Per wave: a (K tile, V tile) pair in smem.  smem is reused for the merge.
     __shared__ uint4 smem[NW * 2 * TILE];
-    __shared__ uint4 smem2[NBUF == 2 ? NW * 2 * TILE : 1];
     __shared__ float lds_ml[2][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
@@ -157,7 +157,6 @@ void split_mfma_kernel(SplitArgs a) {
     // CH = 8 the row parity plus swz(r) = r/2 does the same.
     auto swz = [](int r) { return (r / (16 / CH)) % CH; };
     uint4 *const bufA = smem + wave * 2 * TILE;
-    uint4 *const bufB = smem2 + (NBUF == 2 ? wave * 2 * TILE : 0);
     const int ld_r = lane / CH, ld_p = lane % CH;
     // A operand of the value product for value columns [16 nb, 16 nb + 16): lane l needs
     // V[4(l/16) + t][16 nb + l%16], t = 0..3.  ds_read_b64_tr_b16 hands lane i of a
@@ -200,16 +199,26 @@ void split_mfma_kernel(SplitArgs a) {
     for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    auto consume = [&](const uint4 *tk, int t0) {
-        const uint4 *tv = tk + TILE;
+    // The matrix operands of one tile, as each lane holds them: K rows for the score
+    // product, V^T blocks for the value product.
+    struct TileOps {
+        uint4 k[NKK];
+        uint2 v[NB];
+    };
+    auto read_tile = [&](const uint4 *tk, TileOps &ops) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) ops.k[kk] = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ops.v[nb] = read_vt(tk + TILE, nb);
+    };
 
+    auto consume = [&](const TileOps &ops, int t0) {
         // scores: sc[r] is key t0 + 4 c4 + r, head j16
         f32x4_t sc = zero4;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            const uint4 ka = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
-            sc = mfma16x16x32(ka, qhi[kk], sc);
-            sc = mfma16x16x32(ka, qlo[kk], sc);
+            sc = mfma16x16x32(ops.k[kk], qhi[kk], sc);
+            sc = mfma16x16x32(ops.k[kk], qlo[kk], sc);
         }
         float p[4];
 #pragma unroll
@@ -251,36 +260,36 @@ void split_mfma_kernel(SplitArgs a) {
         // V^T blocks straight from LDS with the transposing read, then the value update
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const uint2 vop = read_vt(tv, nb);
-            O[nb] = mfma16x16x16(vop, phi, O[nb]);
-            O[nb] = mfma16x16x16(vop, plo, O[nb]);
+            O[nb] = mfma16x16x16(ops.v[nb], phi, O[nb]);
+            O[nb] = mfma16x16x16(ops.v[nb], plo, O[nb]);
         }
     };
 
     constexpr int STRIDE = NW * TK;
     constexpr int VM_ALL = 0x0F70;                 // s_waitcnt vmcnt(0)
-    constexpr int VM_NEXT = 0x0F70 | (2 * NLD);    // vmcnt(2*NLD): all but the next tile's loads
-    if constexpr (NBUF == 1) {
+    constexpr int LGKM_ALL = 0xC07F;               // s_waitcnt lgkmcnt(0)
+    if constexpr (!OVL) {
         for (int t0 = wave * TK; t0 < n; t0 += STRIDE) {
             issue_tile(bufA, t0);
             __builtin_amdgcn_s_waitcnt(VM_ALL);
-            consume(bufA, t0);
+            TileOps ops;
+            read_tile(bufA, ops);
+            consume(ops, t0);
         }
     } else {
-        // Two buffers, alternating; a buffer is refilled only after the tile read from
-        // it has been consumed (its LDS reads fed that tile's matrix products).
+        // The buffer is refilled as soon as the tile's operands are in registers (the
+        // LDS reads have returned), and the tile is consumed while the next one loads.
         int t0 = wave * TK;
         if (t0 < n) issue_tile(bufA, t0);
         while (t0 < n) {
-            if (t0 + STRIDE < n) { issue_tile(bufB, t0 + STRIDE); __builtin_amdgcn_s_waitcnt(VM_NEXT); }
-            else __builtin_amdgcn_s_waitcnt(VM_ALL);
-            consume(bufA, t0);
-            t0 += STRIDE;
-            if (t0 >= n) break;
-            if (t0 + STRIDE < n) { issue_tile(bufA, t0 + STRIDE); __builtin_amdgcn_s_waitcnt(VM_NEXT); }
-            else __builtin_amdgcn_s_waitcnt(VM_ALL);
-            consume(bufB, t0);
-            t0 += STRIDE;
+            __builtin_amdgcn_s_waitcnt(VM_ALL);
+            TileOps ops;
+            read_tile(bufA, ops);
+            __builtin_amdgcn_s_waitcnt(LGKM_ALL);
+            const int tn = t0 + STRIDE;
+            if (tn < n) issue_tile(bufA, tn);
+            consume(ops, t0);
+            t0 = tn;
         }
     }
 
@@ -353,19 +362,27 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
     return kv_type == kKvBF16 && group * nq >= 2 && group * nq <= 16 && (d == 64 || d == 128);
 }
 
+// Launched variants: loads overlapped with compute.  The tile held in registers
+// costs d/4 + 8 VGPRs per lane; at d = 128 that needs 3 waves per SIMD (152 VGPRs;
+// 4 waves would spill), which measured faster than 4 waves without the overlap
+// (grouped-query decode, 8 KV heads, 131072 keys: 87.0 vs 93.8 us).  d = 64 keeps 4.
+template <int D>
+static void launch_mfma_d(const SplitArgs &a, int64_t grid, hipStream_t st) {
+    constexpr int WAVES = D == 128 ? 3 : 4;
+    if (a.block_table)
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
+                           st, a);
+    else
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, false>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
+                           st, a);
+}
+
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {
     const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
     if (grid <= 0) return hipSuccess;
-    const bool paged = a.block_table != nullptr;
     switch (d) {
-        case 64:
-            if (paged) hipLaunchKernelGGL((split_mfma_kernel<64, 4, 1, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-            else hipLaunchKernelGGL((split_mfma_kernel<64>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-            break;
-        case 128:
-            if (paged) hipLaunchKernelGGL((split_mfma_kernel<128, 4, 1, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-            else hipLaunchKernelGGL((split_mfma_kernel<128>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-            break;
+        case 64: launch_mfma_d<64>(a, grid, st); break;
+        case 128: launch_mfma_d<128>(a, grid, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
