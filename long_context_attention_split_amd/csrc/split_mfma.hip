@@ -72,12 +72,9 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // WAVES: occupancy target (waves per SIMD) the register allocator must meet.
-// OVL: overlap loads with compute -- a tile's operands are read from LDS into
-// registers, the next tile's loads into the same LDS buffer are issued, and only then
-// is the tile consumed, so a wave always has a tile in flight.
 // PAGED: K/V rows come from a paged cache; each 16-key tile lies inside one page
 // (page sizes are multiples of 16) and gets its own buffer resources.
-template <int D, int WAVES = 4, bool OVL = false, bool PAGED = false>
+template <int D, int WAVES, bool PAGED>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
@@ -268,29 +265,19 @@ void split_mfma_kernel(SplitArgs a) {
     constexpr int STRIDE = NW * TK;
     constexpr int VM_ALL = 0x0F70;                 // s_waitcnt vmcnt(0)
     constexpr int LGKM_ALL = 0xC07F;               // s_waitcnt lgkmcnt(0)
-    if constexpr (!OVL) {
-        for (int t0 = wave * TK; t0 < n; t0 += STRIDE) {
-            issue_tile(bufA, t0);
-            __builtin_amdgcn_s_waitcnt(VM_ALL);
-            TileOps ops;
-            read_tile(bufA, ops);
-            consume(ops, t0);
-        }
-    } else {
-        // The buffer is refilled as soon as the tile's operands are in registers (the
-        // LDS reads have returned), and the tile is consumed while the next one loads.
-        int t0 = wave * TK;
-        if (t0 < n) issue_tile(bufA, t0);
-        while (t0 < n) {
-            __builtin_amdgcn_s_waitcnt(VM_ALL);
-            TileOps ops;
-            read_tile(bufA, ops);
-            __builtin_amdgcn_s_waitcnt(LGKM_ALL);
-            const int tn = t0 + STRIDE;
-            if (tn < n) issue_tile(bufA, tn);
-            consume(ops, t0);
-            t0 = tn;
-        }
+    // The buffer is refilled as soon as the tile's operands are in registers (the LDS
+    // reads have returned), and the tile is consumed while the next one loads.
+    int t0 = wave * TK;
+    if (t0 < n) issue_tile(bufA, t0);
+    while (t0 < n) {
+        __builtin_amdgcn_s_waitcnt(VM_ALL);
+        TileOps ops;
+        read_tile(bufA, ops);
+        __builtin_amdgcn_s_waitcnt(LGKM_ALL);
+        const int tn = t0 + STRIDE;
+        if (tn < n) issue_tile(bufA, tn);
+        consume(ops, t0);
+        t0 = tn;
     }
 
     // ---- merge the NW wave states per head through LDS (reusing the tile buffers).
@@ -370,10 +357,10 @@ template <int D>
 static void launch_mfma_d(const SplitArgs &a, int64_t grid, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
     if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
                            st, a);
     else
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, false>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
                            st, a);
 }
 

@@ -40,14 +40,11 @@ namespace tad {
 // head per KV head); the default policy when the g work-groups of a query-head group
 // re-read the same chunk and should find it in L2.
 // UK: keys per lane group per tile (K and V tiles of UK*16 bytes per lane for bf16).
-// PF: software pipelining -- the next tile's loads are issued before the current
-// tile is consumed (two register tiles, alternating).
 // KVT: element type of K and V (kKvF32, kKvBF16, kKvE4M3, kKvE5M2).
 // PAGED: K/V rows come from a paged cache through the block table; every wave tile
 // then lies inside one page (tile length divides the page size) and gets its own
 // buffer resource.
-template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PF = false,
-          bool PAGED = false>
+template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PAGED = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
     using Row = RowChunk<KVT, POLICY>;
     constexpr int EPL = Row::EPL;                // elements per lane per key
@@ -207,25 +204,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     };
 
     constexpr int STRIDE = NW * T;
-    if constexpr (!PF) {
-        for (int t0 = wave * T; t0 < n; t0 += STRIDE) {
-            Tile kk, vv;
-            load_tile(kk, vv, t0);
-            consume(kk, vv, t0);
-        }
-    } else {
-        Tile ka, va, kb, vb;
-        int t0 = wave * T;
-        if (t0 < n) load_tile(ka, va, t0);
-        while (t0 < n) {
-            if (t0 + STRIDE < n) load_tile(kb, vb, t0 + STRIDE);
-            consume(ka, va, t0);
-            t0 += STRIDE;
-            if (t0 >= n) break;
-            if (t0 + STRIDE < n) load_tile(ka, va, t0 + STRIDE);
-            consume(kb, vb, t0);
-            t0 += STRIDE;
-        }
+    for (int t0 = wave * T; t0 < n; t0 += STRIDE) {
+        Tile kk, vv;
+        load_tile(kk, vv, t0);
+        consume(kk, vv, t0);
     }
 
     // ---- merge the SLOTS lane-group states of this work-group (fixed order).
@@ -304,10 +286,10 @@ static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
         if constexpr (KVT == kKvF32 || D > 256) {
             return hipErrorInvalidValue;                  // not offered for paged caches
         } else if (gq == 1) {
-            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, false, true>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, true>), dim3((unsigned)grid),
                                dim3(kSplitThreads), 0, st, a);
         } else {
-            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, false, true>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, true>), dim3((unsigned)grid),
                                dim3(kSplitThreads), 0, st, a);
         }
     } else if (gq == 1) {
