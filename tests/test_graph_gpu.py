@@ -1,0 +1,75 @@
+"""The allocation-free entry points inside a captured HIP graph.
+
+tad_decode_ws and tad_decode_paged_ws launch only kernels (no allocation, no memset),
+so a caller may capture them.  Each case captures one call, then replays the graph
+several times with eager work (and a new query written into the captured buffer)
+between replays; every replay must equal the eager call bit for bit.
+"""
+import pytest
+import torch
+
+import workloads as W
+from test_parity_gpu import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(x):
+    return None if x is None else x.to(DEV)
+
+
+@pytest.mark.parametrize("case", ["fused-gqa", "split-combine-mha", "paged-interleaved", "tokens"])
+def test_decode_ws_replays_in_a_graph(lib, case):
+    print("[case] graph %s" % case, flush=True)
+    paged = case == "paged-interleaved"
+    if case == "fused-gqa":           # small grid: one launch, merge in the last work-group
+        c, S = W.random_case(900, 2, 8, 2, 2500, 128, seq_lens=[2500, 1700]), 5
+    elif case == "split-combine-mha":  # large grid: split then combine
+        c, S = W.random_case(901, 2, 32, 32, 4000, 128, seq_lens=[4000, 3333]), 16
+    elif case == "tokens":
+        c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
+        c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
+    else:
+        c, S = W.random_case(904, 2, 16, 16, 2000, 128, seq_lens=[2000, 1111]), 8
+    q, k, v, sl = dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["seq_lens"])
+    if paged:
+        kc, vc, tb = W.page_kv(c["k"], c["v"], 16, 904)
+        kc, vc, tb = dev(kc), dev(vc), dev(tb)
+
+    def call(out, ws):
+        if paged:
+            lib.tad_decode_paged_ws(q, kc, vc, tb, sl, None, S, out, ws)
+        else:
+            lib.tad_decode_ws(q, k, v, sl, None, S, out, ws)
+
+    def eager():
+        out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+        ws = lib.workspace(q, k, S)
+        call(out, ws)
+        torch.cuda.synchronize()
+        return out
+
+    ref = eager()
+    out = torch.empty_like(ref)
+    ws = lib.workspace(q, k, S)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                     # warm-up call off the capture
+        call(out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, ws)
+    for i in range(3):
+        out.fill_(float("nan"))                       # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d" % i
+    # a new query written into the captured buffer: the replay decodes it
+    q.copy_(torch.randn(q.shape, generator=torch.Generator().manual_seed(905)).to(DEV))
+    ref2 = eager()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref2)
+    assert not torch.equal(ref, ref2)
