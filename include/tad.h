@@ -150,8 +150,10 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 1024) run
  * as ONE launch: each split work-group writes its partial, and the last one of a
  * row to finish (counted in the workspace's cnt array) merges the row, then returns
- * its counter to zero.  Larger problems run the split and combine kernels back to
- * back (the counters are then unused).  Either way the output is bit-identical to
+ * its counter to zero.  Larger problems, and caches whose KV heads are interleaved
+ * per key with one query head per KV head (read by a kernel without the fused form),
+ * run the split and combine kernels back to back (the counters are then unused).
+ * Either way the output is bit-identical to
  * tad_split followed by tad_combine.  The counters must be zero the first time a
  * workspace is used (tad_workspace_clear, or memory allocated zeroed); every call
  * that runs to completion leaves them zero, so a workspace can be reused call after
