@@ -127,6 +127,8 @@ def main(argv=None) -> int:
                     help="read K/V from a paged cache with pages of this many rows (0: contiguous)")
     ap.add_argument("--head-major-pages", action="store_true",
                     help="store each page as [Hkv, page_size, d] instead of [page_size, Hkv, d]")
+    ap.add_argument("--token-major", action="store_true",
+                    help="contiguous K/V stored [B, L, Hkv, d] (described as [B, Hkv, L, d] by strides)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for HBM byte counters)")
@@ -157,6 +159,9 @@ def main(argv=None) -> int:
                                   head_major=args.head_major_pages)
         k, v, table = kc.to(dev), vc.to(dev), table.to(dev)
         del kc, vc
+    elif args.token_major:
+        k = c["k"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+        v = c["v"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
     else:
         k = c["k"].to(dev)
         v = c["v"].to(dev)
@@ -227,7 +232,8 @@ def main(argv=None) -> int:
             "workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax,
             "n_splits": S, "kv_bytes_per_step": kv_bytes,
             "kv_layout": ("paged, %d-row pages%s" % (args.page_size, ", head-major" if args.head_major_pages else ""))
-                         if args.page_size else "contiguous",
+                         if args.page_size else ("contiguous [B, L, H, d]" if args.token_major
+                                                 else "contiguous [B, H, L, d]"),
         },
         "split_kernel_us": round(split_avg * 1e3, 2),
         "combine_and_gaps_us": round(comb_avg * 1e3, 2),

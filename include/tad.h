@@ -130,7 +130,7 @@ int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
 /*
  * Split step: every (b, query head, chunk) partial (m, l, o) into `ws` (layout above).
  * n_splits must be >= 1 here (use tad_auto_splits to pick one).  `ws` is a device
- * buffer of at least tad_workspace_bytes(B, Hq, n_splits, d) bytes, 256-byte aligned.
+ * buffer of at least tad_workspace_bytes(B, Hq, nq, n_splits, d) bytes, 256-byte aligned.
  */
 int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
               const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,

@@ -74,8 +74,13 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // WAVES: occupancy target (waves per SIMD) the register allocator must meet.
 // PAGED: K/V rows come from a paged cache; each 16-key tile lies inside one page
 // (page sizes are multiples of 16) and gets its own buffer resources.
-template <int D, int WAVES, bool PAGED>
-__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
+// HG, NWH: a work-group serves HG adjacent KV heads of one chunk with NWH waves each
+// (HG = 1: the 4 waves share one KV head).  HG = 4 is for caches that store the KV
+// heads of a key next to each other: the waves of the 4 heads then read the 4
+// adjacent rows of each key at about the same time, where one head's waves alone
+// would read short runs spread over the cache.
+template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4>
+__global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr int NKK = D / 32;          // 32-wide slices of d (score reduction)
@@ -85,7 +90,8 @@ void split_mfma_kernel(SplitArgs a) {
     constexpr int RPI = 64 / CH;         // rows per load instruction
     constexpr int NLD = TK / RPI;        // load instructions per tile and tensor
     constexpr int TILE = TK * CH;        // 16-byte LDS slots per tile
-    constexpr int NW = kSplitThreads / 64;
+    constexpr int NW = HG * NWH;         // waves per work-group
+    constexpr int THREADS = 64 * NW;
     constexpr int MAXG = 16;
     static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
 
@@ -94,7 +100,7 @@ void split_mfma_kernel(SplitArgs a) {
     __shared__ float lds_ml[2][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int c4 = lane >> 4;            // 8-wide (4-wide) reduction block of this lane
     const int j16 = lane & 15;           // column (head) / row (key, value column)
 
@@ -104,7 +110,10 @@ void split_mfma_kernel(SplitArgs a) {
     const int gq = g * nq;
     const int s = blockIdx.x % S;
     const int bk = blockIdx.x / S;
-    const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+    const int b = bk / (a.Hkv / HG);
+    const int kvh0 = (bk % (a.Hkv / HG)) * HG;             // first KV head of the work-group
+    const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
+    const int kvh = kvh0 + hx;
     const bool head_ok = j16 < gq;
     const int tok = head_ok ? j16 % nq : 0;
     const int h = kvh * g + (head_ok ? j16 / nq : 0);
@@ -122,6 +131,7 @@ void split_mfma_kernel(SplitArgs a) {
     const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
     TilePages pages;                                       // paged: this wave's tile pages
+    int ktile = 0;                                         // paged: tiles issued so far
 
     // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo.
     uint4 qhi[NKK], qlo[NKK];
@@ -174,7 +184,7 @@ void split_mfma_kernel(SplitArgs a) {
         int tb = t0;                                       // first row, relative to the resource
         if constexpr (PAGED) {
             const int nt = min(TK, n - t0);
-            const int page = pages.get(kvk, j0, n, wave * TK, NW * TK, (t0 - wave * TK) / (NW * TK));
+            const int page = pages.get(kvk, j0, n, wr * TK, NWH * TK, ktile++);
             krs = kvk.page_rows(page, j0 + t0, nt);
             vrs = kvv.page_rows(page, j0 + t0, nt);
             tb = 0;
@@ -262,12 +272,12 @@ void split_mfma_kernel(SplitArgs a) {
         }
     };
 
-    constexpr int STRIDE = NW * TK;
+    constexpr int STRIDE = NWH * TK;
     constexpr int VM_ALL = 0x0F70;                 // s_waitcnt vmcnt(0)
     constexpr int LGKM_ALL = 0xC07F;               // s_waitcnt lgkmcnt(0)
     // The buffer is refilled as soon as the tile's operands are in registers (the LDS
     // reads have returned), and the tile is consumed while the next one loads.
-    int t0 = wave * TK;
+    int t0 = wr * TK;
     if (t0 < n) issue_tile(bufA, t0);
     while (t0 < n) {
         __builtin_amdgcn_s_waitcnt(VM_ALL);
@@ -294,20 +304,20 @@ void split_mfma_kernel(SplitArgs a) {
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < gq * D; idx += kSplitThreads) {
-        const int hh = idx / D, e = idx % D;
+    for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
+        const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
         float M = kNegInf;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[0][w][hh]);
+        for (int w = x * NWH; w < x * NWH + NWH; ++w) M = fmaxf(M, lds_ml[0][w][hh]);
         const float Mu = (M == kNegInf) ? 0.f : M;
         float acc = 0.f, lsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
+        for (int w = x * NWH; w < x * NWH + NWH; ++w) {
             const float sw = exp2_fast(lds_ml[0][w][hh] - Mu);
             acc = fmaf(sw, lds_o[w][hh][e], acc);
             lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
         }
-        const int64_t r = (((int64_t)b * a.Hq + kvh * g) * nq + hh) * S + s;   // hh: column
+        const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;   // hh: column
         if (a.fused) {                       // written through for the merging work-group
             store_partial(&a.ws_o[r * D + e], acc);
             if (e == 0) {
@@ -324,7 +334,7 @@ void split_mfma_kernel(SplitArgs a) {
     }
 
     // ---- fused merge: the last of the S work-groups of this (b, kv head) merges its g*nq rows.
-    if (a.fused) {
+    if constexpr (HG == 1) if (a.fused) {
         static_assert(NW * 2 * TILE * 4 >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in smem");
         __shared__ int last;
         const int64_t row0 = ((int64_t)b * a.Hq + kvh * g) * nq;
@@ -349,27 +359,46 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
     return kv_type == kKvBF16 && group * nq >= 2 && group * nq <= 16 && (d == 64 || d == 128);
 }
 
+// The 4-KV-heads-per-work-group variant: d = 128 caches with the KV heads of a key
+// adjacent, a head count divisible by 4, and no fused merge (it has none).
+bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
+    return d == 128 && !a.fused && a.Hkv % 4 == 0 && a.skh == d && a.svh == d &&
+           split_mfma_supported(d, a.kv_type, a.group, a.nq);
+}
+
 // Launched variants: loads overlapped with compute.  The tile held in registers
 // costs d/4 + 8 VGPRs per lane; at d = 128 that needs 3 waves per SIMD (152 VGPRs;
 // 4 waves would spill), which measured faster than 4 waves without the overlap
 // (grouped-query decode, 8 KV heads, 131072 keys: 87.0 vs 93.8 us).  d = 64 keeps 4.
+// Interleaved-head caches at d = 128 run 4 KV heads x 3 waves per work-group (one
+// work-group of 12 waves per CU at the usual chunk count).
 template <int D>
-static void launch_mfma_d(const SplitArgs &a, int64_t grid, hipStream_t st) {
+static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
+    if constexpr (D == 128) {
+        if (split_mfma_grouped_heads(a, D)) {
+            const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
+            if (a.block_table)
+                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 4, 3>), dim3((unsigned)grid), dim3(64 * 12), 0,
+                                   st, a);
+            else
+                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 4, 3>), dim3((unsigned)grid), dim3(64 * 12), 0,
+                                   st, a);
+            return;
+        }
+    }
+    const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
     if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
-                           st, a);
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false>), dim3((unsigned)grid), dim3(kSplitThreads), 0,
-                           st, a);
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
 }
 
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {
-    const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
-    if (grid <= 0) return hipSuccess;
+    if ((int64_t)a.B * a.Hkv * a.S <= 0) return hipSuccess;
     switch (d) {
-        case 64: launch_mfma_d<64>(a, grid, st); break;
-        case 128: launch_mfma_d<128>(a, grid, st); break;
+        case 64: launch_mfma_d<64>(a, st); break;
+        case 128: launch_mfma_d<128>(a, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -159,6 +159,7 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
 // Launchers (defined next to their kernels).  Return the hipError_t of the launch.
 hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t s);
 bool split_mfma_supported(int d, int kv_type, int group, int nq);
+bool split_mfma_grouped_heads(const SplitArgs &a, int d);
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 bool split_heads_supported(const SplitArgs &a, int d);
 hipError_t launch_split_heads(const SplitArgs &a, int d, hipStream_t s);

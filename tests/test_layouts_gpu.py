@@ -74,6 +74,21 @@ def test_interleaved_bf16_query_and_large_logits(lib):
     assert_parity(run_interleaved(lib, c, 6), oracle_of(c), torch.bfloat16, vmax_real(c), "bf16 q")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,nq,S", [(2, 32, 8, 1, 5), (3, 16, 4, 1, 1), (2, 32, 8, 2, 7), (1, 8, 8, 1, 33),
+                                          (2, 64, 16, 1, 4)])
+@pytest.mark.parametrize("alibi", [False, True])
+def test_interleaved_grouped_query_heads(lib, B, Hq, Hkv, nq, S, alibi):
+    """Grouped-query heads over a [B, L, Hkv, d] cache with a KV-head count divisible by
+    4: the matrix-core kernel serves 4 adjacent KV heads per work-group."""
+    note("interleaved gqa B=%d Hq=%d Hkv=%d nq=%d S=%d alibi=%s" % (B, Hq, Hkv, nq, S, alibi))
+    lens = [1300, 777, 5][:B]
+    c = W.random_case(880 + Hkv + nq + S, B, Hq, Hkv, 1300, 128, seq_lens=lens, alibi=alibi)
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, 128), generator=torch.Generator().manual_seed(881))
+    out = run_interleaved(lib, c, S)
+    assert_parity(out, oracle_of(c), torch.bfloat16, vmax_real(c), "interleaved gqa S=%d" % S)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(6, 6), (2, 2), (8, 2)])
 def test_interleaved_fallbacks(lib, Hq, Hkv):
     """Head counts the kernel cannot pack (6 and 2 heads: it packs heads by 4)

@@ -109,9 +109,9 @@ def test_paged_entry_points_agree(lib):
 
 def test_paged_equals_contiguous_when_chunks_coincide(lib):
     """With a chunk length that is already a whole number of pages, the matrix-core
-    kernel reads the same 16-key tiles in the same order from either layout, so the
-    paged and contiguous results are bit-identical."""
-    c = paged_case(690, 2, 16, 4, 1024, 128, 16, lens=[1024, 1024])
+    kernel reads the same 16-key tiles in the same order from head-major pages as from
+    the contiguous layout, so the paged and contiguous results are bit-identical."""
+    c = paged_case(690, 2, 16, 4, 1024, 128, 16, lens=[1024, 1024], head_major=True)
     S = 4                                              # c = 256 keys = 16 pages
     a = run_paged(lib, c, S)
     g = {k: dev(c[k]) for k in ("q", "k", "v", "seq_lens")}
