@@ -14,7 +14,6 @@
 
 namespace tad {
 
-// Called by all kMergeThreads threads of a work-group.  `lds` must hold S + 256 floats.
 // Loads of the partials are per-lane (vector) loads.  COHERENT: read them at the
 // device coherence point (agent-scope atomic loads), for partials that other
 // work-groups of the same kernel wrote with agent-scope atomic stores.
@@ -35,13 +34,18 @@ __device__ __forceinline__ void store_partial(float *p, float x) {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, bool COHERENT = false>
+// Merge of one row, called by all NT threads of a work-group (NT a multiple of 64, at
+// least kMergeThreads).  The arithmetic runs on the first kMergeThreads threads in a
+// fixed order, so the result does not depend on the work-group size; the others only
+// join the barriers.  `lds` must hold S + kMergeThreads floats.
+template <int D, bool COHERENT = false, int NT = kMergeThreads>
 __device__ __forceinline__ void merge_row(const float *m, const float *l, const float *o, int S,
                                           float *out_row, float *lds) {
-    constexpr int NT = kMergeThreads;
+    constexpr int NC = kMergeThreads;           // threads that compute
+    static_assert(NT % 64 == 0 && NT >= NC && (D > NC || NC % D == 0), "work-group shape");
     const int tid = threadIdx.x, lane = tid & 63;
     float *w = lds;           // [S] weights
-    float *part = lds + S;    // [NT] partial sums
+    float *part = lds + S;    // [NC] partial sums
 
     // global max: every wave reduces all S (lane-strided, then a butterfly), so every
     // wave holds the same value without a barrier
@@ -61,13 +65,15 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
     const float inv = (ls > 0.f) ? 1.f / ls : 0.f;
     __syncthreads();
 
-    if constexpr (D <= NT) {
-        constexpr int R = NT / D;              // thread rows sharing each output element
-        const int e = tid % D, rr = tid / D;
-        float acc = 0.f;
+    if constexpr (D <= NC) {
+        constexpr int R = NC / D;              // thread rows sharing each output element
+        if (tid < NC) {
+            const int e = tid % D, rr = tid / D;
+            float acc = 0.f;
 #pragma unroll 8
-        for (int s = rr; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);
-        part[tid] = acc;
+            for (int s = rr; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);
+            part[tid] = acc;
+        }
         __syncthreads();
         if (tid < D) {
             float sum = 0.f;
@@ -75,8 +81,8 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
             for (int i = 0; i < R; ++i) sum += part[i * D + tid];
             out_row[tid] = sum * inv;
         }
-    } else {
-        for (int e = tid; e < D; e += NT) {
+    } else if (tid < NC) {
+        for (int e = tid; e < D; e += NC) {
             float acc = 0.f;
 #pragma unroll 8
             for (int s = 0; s < S; ++s) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);

@@ -75,10 +75,10 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // PAGED: K/V rows come from a paged cache; each 16-key tile lies inside one page
 // (page sizes are multiples of 16) and gets its own buffer resources.
 // HG, NWH: a work-group serves HG adjacent KV heads of one chunk with NWH waves each
-// (HG = 1: the 4 waves share one KV head).  HG = 4 is for caches that store the KV
-// heads of a key next to each other: the waves of the 4 heads then read the 4
-// adjacent rows of each key at about the same time, where one head's waves alone
-// would read short runs spread over the cache.
+// (HG = 1: the 4 waves share one KV head).  With HG = 4 and caches that store the KV
+// heads of a key next to each other, the waves of the 4 heads read the 4 adjacent
+// rows of each key at about the same time, where one head's waves alone would read
+// short runs spread over the cache.
 template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
@@ -333,22 +333,24 @@ void split_mfma_kernel(SplitArgs a) {
         }
     }
 
-    // ---- fused merge: the last of the S work-groups of this (b, kv head) merges its g*nq rows.
-    if constexpr (HG == 1) if (a.fused) {
+    // ---- fused merge: the last of the S work-groups of this (b, KV head group) merges
+    // its HG*g*nq rows (consecutive: query heads kvh0*g .. (kvh0+HG)*g - 1); the group's
+    // arrivals are counted in the counter of its first row.
+    if (a.fused) {
         static_assert(NW * 2 * TILE * 4 >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in smem");
         __shared__ int last;
-        const int64_t row0 = ((int64_t)b * a.Hq + kvh * g) * nq;
+        const int64_t row0 = ((int64_t)b * a.Hq + kvh0 * g) * nq;
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
         __syncthreads();
         if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row0], 1) == S - 1;
         __syncthreads();
         if (last) {
-            for (int cc = 0; cc < gq; ++cc) {
+            for (int cc = 0; cc < HG * gq; ++cc) {
                 const int64_t row = row0 + cc;
-                merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
-                                   a.out + (int64_t)b * a.sob + (int64_t)(kvh * g + cc / nq) * a.soh +
-                                       (int64_t)(cc % nq) * a.sot,
-                                   reinterpret_cast<float *>(smem));
+                merge_row<D, true, THREADS>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
+                                            a.out + (int64_t)b * a.sob + (int64_t)(kvh0 * g + cc / nq) * a.soh +
+                                                (int64_t)(cc % nq) * a.sot,
+                                            reinterpret_cast<float *>(smem));
             }
             if (threadIdx.x == 0) a.cnt[row0] = 0;
         }
@@ -359,19 +361,20 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
     return kv_type == kKvBF16 && group * nq >= 2 && group * nq <= 16 && (d == 64 || d == 128);
 }
 
-// The 4-KV-heads-per-work-group variant: d = 128 caches with the KV heads of a key
-// adjacent, a head count divisible by 4, and no fused merge (it has none).
+// The 4-KV-heads-per-work-group variant: d = 128 and a KV head count divisible by 4.
 bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
-    return d == 128 && !a.fused && a.Hkv % 4 == 0 && a.skh == d && a.svh == d &&
-           split_mfma_supported(d, a.kv_type, a.group, a.nq);
+    return d == 128 && a.Hkv % 4 == 0 && split_mfma_supported(d, a.kv_type, a.group, a.nq);
 }
 
 // Launched variants: loads overlapped with compute.  The tile held in registers
 // costs d/4 + 8 VGPRs per lane; at d = 128 that needs 3 waves per SIMD (152 VGPRs;
 // 4 waves would spill), which measured faster than 4 waves without the overlap
 // (grouped-query decode, 8 KV heads, 131072 keys: 87.0 vs 93.8 us).  d = 64 keeps 4.
-// Interleaved-head caches at d = 128 run 4 KV heads x 3 waves per work-group (one
-// work-group of 12 waves per CU at the usual chunk count).
+// With a KV head count divisible by 4, d = 128 runs 4 KV heads x 3 waves per
+// work-group: one 12-wave work-group per CU at the usual chunk count, all resident
+// at once, and for caches with the heads of a key adjacent the 4 heads' waves read
+// each key's adjacent rows together (ragged grouped-query workload: 126.6 -> 119.5 us
+// on [B, Hkv, L, d] K/V, 154.5 -> 120.9 us on [B, L, Hkv, d]).
 template <int D>
 static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;

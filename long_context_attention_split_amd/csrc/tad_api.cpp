@@ -343,10 +343,10 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
     int rc = device_cus(-1, &cus);
     if (rc) return rc;
     const tad::SplitArgs unfused = split_args(P, q, k, v, seq_lens, slopes, S, w, OutDesc());
-    // (the kernels for caches with interleaved heads have no fused form; those layouts
-    // always take two launches, so that the result never depends on the grid size)
+    // (the head-packed kernel has no fused form; its layouts always take two launches,
+    // so that the result never depends on the grid size)
     if (S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus &&
-        !tad::split_heads_supported(unfused, (int)P.d) && !tad::split_mfma_grouped_heads(unfused, (int)P.d))
+        !tad::split_heads_supported(unfused, (int)P.d))
         return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
     if ((rc = launch_split(unfused, P.d, stream))) return rc;
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);
