@@ -53,6 +53,12 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Two fp32 values that are exact bf16 numbers -> one packed dword (x in the low half).
+__device__ __forceinline__ uint32_t pack_exact_bf16(float x, float y) {
+    // v_perm_b32: bytes {x.2, x.3, y.2, y.3} = (x >> 16) | (y & 0xffff0000)
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+}
+
 // x = hi + lo with hi, lo bf16 (truncations): |x - hi - lo| <= 2^-16 |x|.
 __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
     const uint32_t h = __float_as_uint(x) & 0xffff0000u;
@@ -79,7 +85,10 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // heads of a key next to each other, the waves of the 4 heads read the 4 adjacent
 // rows of each key at about the same time, where one head's waves alone would read
 // short runs spread over the cache.
-template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4>
+// KVT: kKvBF16, or an FP8 format (kKvE4M3, kKvE5M2): FP8 tiles land in their own LDS
+// buffer and each wave widens its tile to bf16 in the bf16 tile buffer (exact: every
+// E4M3 and E5M2 value is a bf16 number), after which the bf16 path runs unchanged.
+template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
@@ -94,9 +103,16 @@ void split_mfma_kernel(SplitArgs a) {
     constexpr int THREADS = 64 * NW;
     constexpr int MAXG = 16;
     static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
+    constexpr bool F8 = KVT != kKvBF16;
+    constexpr int ELEM = F8 ? 1 : 2;
+    constexpr int CHF = D / 16;          // 16-byte chunks per FP8 row
+    constexpr int RPIF = 64 / CHF;       // FP8 rows per load instruction
+    constexpr int NLDF = TK / RPIF;      // FP8 load instructions per tile and tensor
+    constexpr int TILEF = F8 ? TK * CHF : 0;   // 16-byte LDS slots per FP8 tile
 
-    // Per wave: a (K tile, V tile) pair in smem.  smem is reused for the merge.
-    __shared__ uint4 smem[NW * 2 * TILE];
+    // Per wave: a bf16 (K tile, V tile) pair in smem, then (FP8) the FP8 pair the loads
+    // land in.  The bf16 tiles are reused for the merge.
+    __shared__ uint4 smem[NW * 2 * (TILE + TILEF)];
     __shared__ float lds_ml[2][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
@@ -125,15 +141,17 @@ void split_mfma_kernel(SplitArgs a) {
     const int Lc = visible_keys(cr.L, nq, tok);
     const int lim = min(n, Lc - j0);
 
-    const KvRows kvk(a.k, 2, a.skb, a.skh, a.skj, a.skp, a, b, kvh);
-    const KvRows kvv(a.v, 2, a.svb, a.svh, a.svj, a.svp, a, b, kvh);
+    const KvRows kvk(a.k, ELEM, a.skb, a.skh, a.skj, a.skp, a, b, kvh);
+    const KvRows kvv(a.v, ELEM, a.svb, a.svh, a.svj, a.svp, a, b, kvh);
     const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
     const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
     TilePages pages;                                       // paged: this wave's tile pages
     int ktile = 0;                                         // paged: tiles issued so far
 
-    // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo.
+    // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo,
+    // scaled into base-2 units and by the K dequantisation scale of the KV head (FP8).
+    const float qs = a.qscale * ((F8 && a.k_scale) ? a.k_scale[b * a.Hkv + kvh] : 1.f);
     uint4 qhi[NKK], qlo[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -152,7 +170,7 @@ void split_mfma_kernel(SplitArgs a) {
         }
         uint32_t hw[8], lw[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) split_bf16(head_ok ? x[t] * a.qscale : 0.f, hw[t], lw[t]);
+        for (int t = 0; t < 8; ++t) split_bf16(head_ok ? x[t] * qs : 0.f, hw[t], lw[t]);
         qhi[kk] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
         qlo[kk] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
     }
@@ -164,6 +182,7 @@ void split_mfma_kernel(SplitArgs a) {
     // CH = 8 the row parity plus swz(r) = r/2 does the same.
     auto swz = [](int r) { return (r / (16 / CH)) % CH; };
     uint4 *const bufA = smem + wave * 2 * TILE;
+    uint4 *const bufF = smem + NW * 2 * TILE + wave * 2 * TILEF;   // FP8 only
     const int ld_r = lane / CH, ld_p = lane % CH;
     // A operand of the value product for value columns [16 nb, 16 nb + 16): lane l needs
     // V[4(l/16) + t][16 nb + l%16], t = 0..3.  ds_read_b64_tr_b16 hands lane i of a
@@ -189,14 +208,54 @@ void split_mfma_kernel(SplitArgs a) {
             vrs = kvv.page_rows(page, j0 + t0, nt);
             tb = 0;
         }
+        if constexpr (F8) {
+            // FP8 rows land unswizzled in bufF (row r at slot r * CHF)
 #pragma unroll
-        for (int u = 0; u < NLD; ++u) {
-            const int r = u * RPI + ld_r;
-            const uint32_t col = 16u * (uint32_t)(ld_p ^ swz(r));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(tk + u * 64), 16,
-                                                     (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(tv + u * 64), 16,
-                                                     (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
+            for (int u = 0; u < NLDF; ++u) {
+                const int r = u * RPIF + lane / CHF;
+                const uint32_t col = 16u * (uint32_t)(lane % CHF);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(bufF + u * 64), 16,
+                                                         (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(bufF + TILEF + u * 64), 16,
+                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < NLD; ++u) {
+                const int r = u * RPI + ld_r;
+                const uint32_t col = 16u * (uint32_t)(ld_p ^ swz(r));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(tk + u * 64), 16,
+                                                         (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(tv + u * 64), 16,
+                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
+            }
+        }
+    };
+    // FP8: widen one landed tile (bufF, K or V) into the swizzled bf16 tile layout.  An
+    // FP8 chunk holds dims 16 fc .. 16 fc + 15 of its row, i.e. bf16 chunks 2 fc, 2 fc + 1.
+    auto widen_tile = [&](const uint4 *src, uint4 *dst) {
+#pragma unroll
+        for (int i = 0; i < TK * CHF / 64; ++i) {
+            const int idx = lane + 64 * i, r = idx / CHF, fc = idx % CHF;
+            const uint4 w = src[idx];
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            uint32_t o8[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                typedef float f2_t __attribute__((ext_vector_type(2)));
+                f2_t lo, hi;
+                if constexpr (KVT == kKvE4M3) {
+                    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
+                    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
+                } else {
+                    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], false);
+                    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], true);
+                }
+                o8[2 * j] = pack_exact_bf16(lo.x, lo.y);
+                o8[2 * j + 1] = pack_exact_bf16(hi.x, hi.y);
+            }
+            dst[r * CH + ((2 * fc) ^ swz(r))] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
+            dst[r * CH + ((2 * fc + 1) ^ swz(r))] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
         }
     };
 
@@ -281,6 +340,10 @@ void split_mfma_kernel(SplitArgs a) {
     if (t0 < n) issue_tile(bufA, t0);
     while (t0 < n) {
         __builtin_amdgcn_s_waitcnt(VM_ALL);
+        if constexpr (F8) {
+            widen_tile(bufF, bufA);
+            widen_tile(bufF + TILEF, bufA + TILE);
+        }
         TileOps ops;
         read_tile(bufA, ops);
         __builtin_amdgcn_s_waitcnt(LGKM_ALL);
@@ -316,6 +379,9 @@ void split_mfma_kernel(SplitArgs a) {
             const float sw = exp2_fast(lds_ml[0][w][hh] - Mu);
             acc = fmaf(sw, lds_o[w][hh][e], acc);
             lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
+        }
+        if constexpr (F8) {
+            if (a.v_scale) acc *= a.v_scale[b * a.Hkv + kvh0 + x];       // V dequantisation
         }
         const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;   // hh: column
         if (a.fused) {                       // written through for the merging work-group
@@ -358,7 +424,8 @@ void split_mfma_kernel(SplitArgs a) {
 }
 
 bool split_mfma_supported(int d, int kv_type, int group, int nq) {
-    return kv_type == kKvBF16 && group * nq >= 2 && group * nq <= 16 && (d == 64 || d == 128);
+    return (kv_type == kKvBF16 || kv_type == kKvE4M3 || kv_type == kKvE5M2) && group * nq >= 2 &&
+           group * nq <= 16 && (d == 64 || d == 128);
 }
 
 // The 4-KV-heads-per-work-group variant: d = 128 and a KV head count divisible by 4.
@@ -375,26 +442,37 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
 // at once, and for caches with the heads of a key adjacent the 4 heads' waves read
 // each key's adjacent rows together (ragged grouped-query workload: 126.6 -> 119.5 us
 // on [B, Hkv, L, d] K/V, 154.5 -> 120.9 us on [B, L, Hkv, d]).
-template <int D>
-static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
+template <int D, int KVT>
+static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
     if constexpr (D == 128) {
         if (split_mfma_grouped_heads(a, D)) {
             const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
             if (a.block_table)
-                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 4, 3>), dim3((unsigned)grid), dim3(64 * 12), 0,
-                                   st, a);
+                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 4, 3, KVT>), dim3((unsigned)grid),
+                                   dim3(64 * 12), 0, st, a);
             else
-                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 4, 3>), dim3((unsigned)grid), dim3(64 * 12), 0,
-                                   st, a);
+                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 4, 3, KVT>), dim3((unsigned)grid),
+                                   dim3(64 * 12), 0, st, a);
             return;
         }
     }
     const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
     if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 1, 4, KVT>), dim3((unsigned)grid), dim3(kSplitThreads),
+                           0, st, a);
     else
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
+        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 1, 4, KVT>), dim3((unsigned)grid), dim3(kSplitThreads),
+                           0, st, a);
+}
+
+template <int D>
+static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
+    switch (a.kv_type) {
+        case kKvE4M3: launch_mfma_t<D, kKvE4M3>(a, st); break;
+        case kKvE5M2: launch_mfma_t<D, kKvE5M2>(a, st); break;
+        default: launch_mfma_t<D, kKvBF16>(a, st); break;
+    }
 }
 
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {

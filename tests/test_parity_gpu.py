@@ -199,6 +199,29 @@ def test_fp8_ragged_gqa_alibi(lib, kv):
     run_case(lib, 310, 3, 8, 2, 3000, 128, kv=kv, seq_lens=[3000, 1, 2222], alibi=True, n_splits=4)
 
 
+@pytest.mark.parametrize("kv", FP8)
+@pytest.mark.parametrize("B,Hq,Hkv,d,nq,S", [
+    (2, 8, 2, 128, 1, 5),        # 4 heads per KV head, one KV head per work-group
+    (2, 32, 8, 128, 1, 3),       # 4 KV heads per work-group (fused: small grid)
+    (3, 32, 8, 128, 1, 16),      # 4 KV heads per work-group, split + combine
+    (2, 16, 4, 64, 1, 7),        # d 64
+    (2, 8, 8, 128, 2, 6),        # several tokens, 4 KV heads per work-group
+])
+def test_fp8_matrix_core_path(lib, kv, B, Hq, Hkv, d, nq, S):
+    """FP8 K/V with query-head groups or several tokens take the matrix-core kernel: FP8
+    tiles widened to bf16 in LDS, K scale folded into q, V scale into the partials."""
+    note("fp8 mfma kv=%s B=%d Hq=%d Hkv=%d d=%d nq=%d S=%d" % (kv, B, Hq, Hkv, d, nq, S))
+    lens = [1700, 1, 999][:B]
+    c = W.random_case(330 + Hkv + d + nq, B, Hq, Hkv, 1700, d, kv_dtype=kv, seq_lens=lens, alibi=True,
+                      k_scale=3.0)
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(331))
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
+    out = gpu_decode(lib, c, S)
+    assert_parity(out, ref, kv, vmax_real(c), "fp8 mfma")
+
+
 def test_fp8_long_context(lib):
     run_case(lib, 320, 1, 8, 8, 65536, 128, kv=torch.float8_e4m3fn, n_splits=0, k_scale=4.0)
 
