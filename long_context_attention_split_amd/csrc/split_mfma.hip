@@ -110,9 +110,10 @@ void split_mfma_kernel(SplitArgs a) {
     constexpr int NLDF = TK / RPIF;      // FP8 load instructions per tile and tensor
     constexpr int TILEF = F8 ? TK * CHF : 0;   // 16-byte LDS slots per FP8 tile
 
-    // Per wave: a bf16 (K tile, V tile) pair in smem, then (FP8) the FP8 pair the loads
-    // land in.  The bf16 tiles are reused for the merge.
-    __shared__ uint4 smem[NW * 2 * (TILE + TILEF)];
+    // Per wave: a bf16 (K tile, V tile) pair in smem and (FP8) the FP8 pair the loads
+    // land in, in smemF.  The bf16 tiles are reused for the merge.
+    __shared__ uint4 smem[NW * 2 * TILE];
+    __shared__ uint4 smemF[F8 ? NW * 2 * TILEF : 1];
     __shared__ float lds_ml[2][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
@@ -182,7 +183,7 @@ void split_mfma_kernel(SplitArgs a) {
     // CH = 8 the row parity plus swz(r) = r/2 does the same.
     auto swz = [](int r) { return (r / (16 / CH)) % CH; };
     uint4 *const bufA = smem + wave * 2 * TILE;
-    uint4 *const bufF = smem + NW * 2 * TILE + wave * 2 * TILEF;   // FP8 only
+    uint4 *const bufF = smemF + wave * 2 * TILEF;                  // FP8 only
     const int ld_r = lane / CH, ld_p = lane % CH;
     // A operand of the value product for value columns [16 nb, 16 nb + 16): lane l needs
     // V[4(l/16) + t][16 nb + l%16], t = 0..3.  ds_read_b64_tr_b16 hands lane i of a
