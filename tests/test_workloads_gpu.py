@@ -1,4 +1,4 @@
-"""Full-size parity on the five seeded workloads, in the launch configuration the
+"""Full-size parity on the seeded workloads, in the launch configuration the
 benchmark times (automatic split count unless the workload fixes one).
 
 Every output row is checked against the fp64 oracle (the oracle is threaded over
@@ -62,6 +62,11 @@ def test_workload4_alibi(lib):
 
 def test_workload6_fp8_mha(lib):
     run_workload(lib, 6)
+
+
+def test_workload7_fp8_gqa_ragged(lib):
+    out, ref, c = run_workload(lib, 7)
+    assert c["seq_lens"].min() >= 1024
 
 
 def test_workload5_million_keys(lib):

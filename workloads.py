@@ -30,6 +30,8 @@ id     description
        bf16(c q_h) with c = 60 sqrt(d) / |q_h|^2 so that its logit is about +60.
 6      workload 2 with FP8 (OCP E4M3) K and V: each (b, kv-head) slab of N(0,1)
        draws is divided by its amax/448 and rounded to E4M3; the scale is kept.
+7      workload 3 with FP8 (OCP E4M3) K and V, quantised as in workload 6; keys
+       past each length hold the E4M3 NaN pattern.
 =====  =========================================================================
 
 ``page_kv`` lays any of these K/V tensors out as a paged cache: pages of
@@ -90,6 +92,8 @@ WORKLOADS = {
                 F32, BF16, k_scale=6.0, planted_logit=60.0),
     6: Workload(6, "MHA B1 H32 d128 L131072 fp8-e4m3 K/V, per-head scales", 1, 32, 32, 128, 131072,
                 F32, torch.float8_e4m3fn),
+    7: Workload(7, "GQA B8 Hq32 Hkv8 d128 ragged L<=32768 fp8-e4m3 K/V, per-head scales", 8, 32, 8, 128, 32768,
+                F32, torch.float8_e4m3fn, ragged=True),
 }
 
 
@@ -170,8 +174,12 @@ def make_workload(wid: int):
         seq_lens = draw_seq_lens(base + 3, w.B, w.ragged_lo, w.Lmax)
         for b in range(w.B):
             L = int(seq_lens[b])
-            k[b, :, L:, :] = float("nan")
-            v[b, :, L:, :] = float("nan")
+            if w.kv_dtype in FP8_MAX:                 # the format's NaN bit pattern
+                k.view(torch.uint8)[b, :, L:, :] = _nan_bits(w.kv_dtype)
+                v.view(torch.uint8)[b, :, L:, :] = _nan_bits(w.kv_dtype)
+            else:
+                k[b, :, L:, :] = float("nan")
+                v[b, :, L:, :] = float("nan")
     slopes = alibi_slopes(w.Hq) if w.alibi else None
     planted = None
     if w.planted_logit is not None:
