@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
     constexpr int STRIDE = NW * U;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int grp = lane / G;                    // head h0 + grp
     const int sub = lane % G;
 

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     static_assert(!PAGED || T == 16, "paged tiles are 16 keys: page sizes are multiples of 16");
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int grp = lane / G;
     const int sub = lane % G;
 

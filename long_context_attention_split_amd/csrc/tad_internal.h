@@ -70,7 +70,7 @@ __device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int
         for (int i = (int)(threadIdx.x & 63); i < a.B; i += 64) mx = max(mx, min(max(a.seq_lens[i], 0), a.Lmax));
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-        Lref = mx;
+        Lref = __builtin_amdgcn_readfirstlane(mx);   // equal in every lane: keep it scalar
     }
     int c = (Lref + a.S - 1) / a.S;
     if (a.block_table) c = (c + a.page_size - 1) / a.page_size * a.page_size;   // whole pages
