@@ -86,8 +86,9 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // rows of each key at about the same time, where one head's waves alone would read
 // short runs spread over the cache.
 // KVT: kKvBF16, or an FP8 format (kKvE4M3, kKvE5M2): FP8 tiles land in their own LDS
-// buffer and each wave widens its tile to bf16 in the bf16 tile buffer (exact: every
-// E4M3 and E5M2 value is a bf16 number), after which the bf16 path runs unchanged.
+// buffer; K operands are read from it and widened to bf16 in registers, and the V tile
+// is widened into the bf16 tile buffer for the transposing read (exact: every E4M3
+// and E5M2 value is a bf16 number).
 template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
@@ -182,6 +183,7 @@ void split_mfma_kernel(SplitArgs a) {
     // 16 rows of an operand read land in 16 distinct 16-byte bank groups, and with
     // CH = 8 the row parity plus swz(r) = r/2 does the same.
     auto swz = [](int r) { return (r / (16 / CH)) % CH; };
+    auto swzf = [](int r) { return (r / (16 / CHF)) % CHF; };   // the same for FP8 rows
     uint4 *const bufA = smem + wave * 2 * TILE;
     uint4 *const bufF = smemF + wave * 2 * TILEF;                  // FP8 only
     const int ld_r = lane / CH, ld_p = lane % CH;
@@ -210,11 +212,11 @@ void split_mfma_kernel(SplitArgs a) {
             tb = 0;
         }
         if constexpr (F8) {
-            // FP8 rows land unswizzled in bufF (row r at slot r * CHF)
+            // FP8 rows land in bufF with slot p of row r holding chunk p ^ swzf(r)
 #pragma unroll
             for (int u = 0; u < NLDF; ++u) {
                 const int r = u * RPIF + lane / CHF;
-                const uint32_t col = 16u * (uint32_t)(lane % CHF);
+                const uint32_t col = 16u * (uint32_t)((lane % CHF) ^ swzf(r));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(bufF + u * 64), 16,
                                                          (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(bufF + TILEF + u * 64), 16,
@@ -232,12 +234,12 @@ void split_mfma_kernel(SplitArgs a) {
             }
         }
     };
-    // FP8: widen one landed tile (bufF, K or V) into the swizzled bf16 tile layout.  An
-    // FP8 chunk holds dims 16 fc .. 16 fc + 15 of its row, i.e. bf16 chunks 2 fc, 2 fc + 1.
+    // FP8: widen the landed V tile (bufF) into the swizzled bf16 tile layout.  An FP8
+    // chunk holds dims 16 fc .. 16 fc + 15 of its row, i.e. bf16 chunks 2 fc, 2 fc + 1.
     auto widen_tile = [&](const uint4 *src, uint4 *dst) {
 #pragma unroll
         for (int i = 0; i < TK * CHF / 64; ++i) {
-            const int idx = lane + 64 * i, r = idx / CHF, fc = idx % CHF;
+            const int idx = lane + 64 * i, r = idx / CHF, fc = (idx % CHF) ^ swzf(r);
             const uint4 w = src[idx];
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
             uint32_t o8[8];
@@ -273,8 +275,36 @@ void split_mfma_kernel(SplitArgs a) {
         uint2 v[NB];
     };
     auto read_tile = [&](const uint4 *tk, TileOps &ops) {
+        if constexpr (F8) {
+            // K operands straight from the FP8 tile: dims 32 kk + 8 c4 .. + 7 of row j16
+            // are 8 bytes of chunk 2 kk + c4/2, widened to bf16 in registers (exact)
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) ops.k[kk] = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
+            for (int kk = 0; kk < NKK; ++kk) {
+                const uint2 w8 = *(const uint2 *)((const uint32_t *)(bufF + j16 * CHF +
+                                                                     ((2 * kk + (c4 >> 1)) ^ swzf(j16))) +
+                                                  2 * (c4 & 1));
+                const uint32_t ws[2] = {w8.x, w8.y};
+                uint32_t o4[4];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    typedef float f2_t __attribute__((ext_vector_type(2)));
+                    f2_t lo, hi;
+                    if constexpr (KVT == kKvE4M3) {
+                        lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
+                        hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
+                    } else {
+                        lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], false);
+                        hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], true);
+                    }
+                    o4[2 * j] = pack_exact_bf16(lo.x, lo.y);
+                    o4[2 * j + 1] = pack_exact_bf16(hi.x, hi.y);
+                }
+                ops.k[kk] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) ops.k[kk] = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) ops.v[nb] = read_vt(tk + TILE, nb);
     };
@@ -341,10 +371,7 @@ void split_mfma_kernel(SplitArgs a) {
     if (t0 < n) issue_tile(bufA, t0);
     while (t0 < n) {
         __builtin_amdgcn_s_waitcnt(VM_ALL);
-        if constexpr (F8) {
-            widen_tile(bufF, bufA);
-            widen_tile(bufF + TILEF, bufA + TILE);
-        }
+        if constexpr (F8) widen_tile(bufF + TILEF, bufA + TILE);
         TileOps ops;
         read_tile(bufA, ops);
         __builtin_amdgcn_s_waitcnt(LGKM_ALL);
