@@ -89,6 +89,15 @@ def test_interleaved_grouped_query_heads(lib, B, Hq, Hkv, nq, S, alibi):
     assert_parity(out, oracle_of(c), torch.bfloat16, vmax_real(c), "interleaved gqa S=%d" % S)
 
 
+@pytest.mark.parametrize("kv", [torch.float8_e4m3fn, torch.float8_e5m2])
+@pytest.mark.parametrize("S", [3, 16])
+def test_interleaved_fp8_grouped_query_heads(lib, kv, S):
+    """FP8 K/V in a [B, L, Hkv, d] cache with 4 adjacent KV heads per work-group."""
+    note("interleaved fp8 gqa kv=%s S=%d" % (kv, S))
+    c = W.random_case(890 + S, 2, 32, 8, 1400, 128, kv_dtype=kv, seq_lens=[1400, 611], alibi=True)
+    assert_parity(run_interleaved(lib, c, S), oracle_of(c), kv, vmax_real(c), "interleaved fp8 gqa S=%d" % S)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(6, 6), (2, 2), (8, 2)])
 def test_interleaved_fallbacks(lib, Hq, Hkv):
     """Head counts the kernel cannot pack (6 and 2 heads: it packs heads by 4)

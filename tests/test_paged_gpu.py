@@ -57,6 +57,8 @@ def oracle_of(c):
     (2, 8, 2, 1000, 128, 48, torch.float8_e5m2, 6),        # FP8 E5M2, GQA 4, 48-row pages
     (2, 4, 4, 600, 64, 16, torch.float8_e4m3fn, 3),        # FP8, d 64
     (1, 8, 8, 4096, 128, 256, torch.bfloat16, 0),          # 256-row pages, automatic splits
+    (2, 32, 8, 1200, 128, 16, torch.float8_e4m3fn, 5),     # FP8 GQA, 4 KV heads per work-group
+    (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 12),       # FP8 E5M2 GQA, 4 KV heads, split + combine
 ])
 def test_paged_matches_oracle(lib, B, Hq, Hkv, L, d, ps, kv, S):
     """Ragged lengths (one not a page multiple) over a permuted page pool."""
