@@ -3,10 +3,12 @@
 // With g query heads sharing one KV head (and/or nq query tokens per head), the
 // scores of a key tile form a real dense product S^T[key][column] = K_tile . Q^T over
 // the g*nq (head, token) columns, and so does the value update O^T[e][column] +=
-// V_tile^T . P^T.  One work-group (4 waves) owns one (b, kv head, chunk) and all its
-// columns, so every K and V byte of the chunk is read from HBM once however many
-// heads and tokens share it.  Each column masks the keys past its token's position.  The per-head partials (m, l, o)
-// it writes are the same as the vector-ALU kernel's (see split_valu.hip): chunk
+// V_tile^T . P^T.  Each wave serves all the columns of one KV head, and the waves of
+// a work-group share one (b, chunk) -- 4 waves on one KV head, or 3 waves on each of
+// 4 adjacent KV heads -- so every K and V byte of the chunk is read from HBM once
+// however many heads and tokens share it.  Each column masks the keys past its
+// token's position.  The per-head partials (m, l, o) it writes are the same as the
+// vector-ALU kernel's (see split_valu.hip): chunk
 // maximum in base 2, sum of 2^(s - m), and the 2^(s - m)-weighted sum of value
 // rows, i.e. the per-chunk local max, denominator and numerator of tree_attn_decode
 // ("Tree Attention Decoding").
