@@ -4,8 +4,9 @@
 // scores of a key tile form a real dense product S^T[key][column] = K_tile . Q^T over
 // the g*nq (head, token) columns, and so does the value update O^T[e][column] +=
 // V_tile^T . P^T.  Each wave serves all the columns of one KV head, and the waves of
-// a work-group share one (b, chunk) -- 4 waves on one KV head, or 3 waves on each of
-// 4 adjacent KV heads -- so every K and V byte of the chunk is read from HBM once
+// a work-group share one (b, chunk) -- 4 waves on one KV head, or 3 (d = 128) or 4
+// (d = 64) waves on each of 4 adjacent KV heads -- so every K and V byte of the chunk
+// is read from HBM once
 // however many heads and tokens share it.  Each column masks the keys past its
 // token's position.  The per-head partials (m, l, o) it writes are the same as the
 // vector-ALU kernel's (see split_valu.hip): chunk
@@ -458,34 +459,34 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
            group * nq <= 16 && (d == 64 || d == 128);
 }
 
-// The 4-KV-heads-per-work-group variant: d = 128 and a KV head count divisible by 4.
+// The 4-KV-heads-per-work-group variant: a KV head count divisible by 4.
 bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
-    return d == 128 && a.Hkv % 4 == 0 && split_mfma_supported(d, a.kv_type, a.group, a.nq);
+    return a.Hkv % 4 == 0 && split_mfma_supported(d, a.kv_type, a.group, a.nq);
 }
 
 // Launched variants: loads overlapped with compute.  The tile held in registers
 // costs d/4 + 8 VGPRs per lane; at d = 128 that needs 3 waves per SIMD (152 VGPRs;
 // 4 waves would spill), which measured faster than 4 waves without the overlap
 // (grouped-query decode, 8 KV heads, 131072 keys: 87.0 vs 93.8 us).  d = 64 keeps 4.
-// With a KV head count divisible by 4, d = 128 runs 4 KV heads x 3 waves per
-// work-group: one 12-wave work-group per CU at the usual chunk count, all resident
-// at once, and for caches with the heads of a key adjacent the 4 heads' waves read
-// each key's adjacent rows together (ragged grouped-query workload: 126.6 -> 119.5 us
-// on [B, Hkv, L, d] K/V, 154.5 -> 120.9 us on [B, L, Hkv, d]).
+// With a KV head count divisible by 4, a work-group runs 4 KV heads x WAVES waves
+// (12 waves at d = 128, 16 at d = 64): one work-group per CU at the usual chunk
+// count, all resident at once, and for caches with the heads of a key adjacent the 4
+// heads' waves read each key's adjacent rows together.  Ragged grouped-query
+// workload, 8 KV heads, 32768 keys: d = 128 126.6 -> 119.5 us on [B, Hkv, L, d] K/V
+// and 154.5 -> 120.9 us on [B, L, Hkv, d]; d = 64 57.6 -> 54.5 us and 78.8 -> 56.0 us.
 template <int D, int KVT>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
-    if constexpr (D == 128) {
-        if (split_mfma_grouped_heads(a, D)) {
-            const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
-            if (a.block_table)
-                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 4, 3, KVT>), dim3((unsigned)grid),
-                                   dim3(64 * 12), 0, st, a);
-            else
-                hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 4, 3, KVT>), dim3((unsigned)grid),
-                                   dim3(64 * 12), 0, st, a);
-            return;
-        }
+    if (split_mfma_grouped_heads(a, D)) {
+        constexpr int NWH = WAVES;                         // one work-group fills a CU
+        const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
+        if (a.block_table)
+            hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 4, NWH, KVT>), dim3((unsigned)grid),
+                               dim3(64 * 4 * NWH), 0, st, a);
+        else
+            hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 4, NWH, KVT>), dim3((unsigned)grid),
+                               dim3(64 * 4 * NWH), 0, st, a);
+        return;
     }
     const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
     if (a.block_table)

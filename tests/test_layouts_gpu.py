@@ -89,6 +89,19 @@ def test_interleaved_grouped_query_heads(lib, B, Hq, Hkv, nq, S, alibi):
     assert_parity(out, oracle_of(c), torch.bfloat16, vmax_real(c), "interleaved gqa S=%d" % S)
 
 
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
+@pytest.mark.parametrize("B,Hq,Hkv,nq,S", [(2, 32, 8, 1, 5), (3, 16, 4, 2, 9), (2, 16, 8, 1, 16)])
+def test_interleaved_grouped_query_heads_d64(lib, kv, B, Hq, Hkv, nq, S):
+    """d = 64 grouped-query heads over a [B, L, Hkv, d] cache: 4 adjacent KV heads x 4
+    waves per work-group, ragged lengths, ALiBi, one and several tokens."""
+    note("interleaved gqa d64 kv=%s B=%d Hq=%d Hkv=%d nq=%d S=%d" % (kv, B, Hq, Hkv, nq, S))
+    c = W.random_case(960 + Hkv + nq + S, B, Hq, Hkv, 1250, 64, kv_dtype=kv, seq_lens=[1250, 701, 3][:B],
+                      alibi=True)
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, 64), generator=torch.Generator().manual_seed(961))
+    assert_parity(run_interleaved(lib, c, S), oracle_of(c), kv, vmax_real(c), "interleaved gqa d64 S=%d" % S)
+
+
 @pytest.mark.parametrize("kv", [torch.float8_e4m3fn, torch.float8_e5m2])
 @pytest.mark.parametrize("S", [3, 16])
 def test_interleaved_fp8_grouped_query_heads(lib, kv, S):

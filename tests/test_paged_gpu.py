@@ -59,6 +59,8 @@ def oracle_of(c):
     (1, 8, 8, 4096, 128, 256, torch.bfloat16, 0),          # 256-row pages, automatic splits
     (2, 32, 8, 1200, 128, 16, torch.float8_e4m3fn, 5),     # FP8 GQA, 4 KV heads per work-group
     (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 12),       # FP8 E5M2 GQA, 4 KV heads, split + combine
+    (2, 32, 8, 1100, 64, 16, torch.bfloat16, 6),           # d 64 GQA, 4 KV heads per work-group
+    (3, 16, 8, 1000, 64, 32, torch.float8_e4m3fn, 11),     # d 64 FP8 GQA, 4 KV heads, split + combine
 ])
 def test_paged_matches_oracle(lib, B, Hq, Hkv, L, d, ps, kv, S):
     """Ragged lengths (one not a page multiple) over a permuted page pool."""

@@ -272,16 +272,16 @@ def test_several_tokens_entry_points_agree(lib):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,nq", [(16, 4, 1), (32, 8, 1), (8, 8, 2)])
-def test_grouped_kv_heads_fused_equals_split_combine(lib, Hq, Hkv, nq):
-    """d = 128 with a KV head count divisible by 4 runs 4 KV heads per work-group; on a
-    small grid tad_decode_ws merges in the last work-group of each 4-head group, and
-    the result is bit-identical to tad_split + tad_combine and within the bar of the
-    oracle."""
-    note("grouped kv heads Hq=%d Hkv=%d nq=%d" % (Hq, Hkv, nq))
-    c = W.random_case(460 + Hq + nq, 2, Hq, Hkv, 1800, 128, seq_lens=[1800, 1001])
+def test_grouped_kv_heads_fused_equals_split_combine(lib, Hq, Hkv, nq, d):
+    """A KV head count divisible by 4 runs 4 KV heads per work-group; on a small grid
+    tad_decode_ws merges in the last work-group of each 4-head group, and the result
+    is bit-identical to tad_split + tad_combine and within the bar of the oracle."""
+    note("grouped kv heads Hq=%d Hkv=%d nq=%d d=%d" % (Hq, Hkv, nq, d))
+    c = W.random_case(460 + Hq + nq + d, 2, Hq, Hkv, 1800, d, seq_lens=[1800, 1001])
     if nq > 1:
-        c["q"] = torch.randn((2, Hq, nq, 128), generator=torch.Generator().manual_seed(461))
+        c["q"] = torch.randn((2, Hq, nq, d), generator=torch.Generator().manual_seed(461))
     ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"])
     g = to_dev(c)
     S = 3                                              # 2 * Hq * nq * 3 < CU count: fused
@@ -290,7 +290,7 @@ def test_grouped_kv_heads_fused_equals_split_combine(lib, Hq, Hkv, nq):
     ws = lib.workspace(g["q"], g["k"], S)
     lib.tad_split(g["q"], g["k"], g["v"], g["seq_lens"], None, S, ws)
     b = torch.empty_like(a)
-    lib.tad_combine(ws, 2, Hq, nq, S, 128, b)
+    lib.tad_combine(ws, 2, Hq, nq, S, d, b)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, again)
     assert_parity(a.cpu().numpy(), ref, torch.bfloat16, vmax_real(c), "grouped kv heads")
