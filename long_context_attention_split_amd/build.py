@@ -53,6 +53,14 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.check_call(cmd)
+    # A kernel template the host pass could not instantiate leaves its launch stub
+    # undefined without any diagnostic; such a library would only fail when loaded.
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    undef = subprocess.run([nm, "-u", tmp], stdout=subprocess.PIPE, text=True, check=True).stdout
+    stubs = [ln.split()[-1] for ln in undef.splitlines() if "__device_stub__" in ln]
+    if stubs:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs left undefined by the host pass:\n  " + "\n  ".join(stubs))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -42,6 +42,8 @@
 // Aandacht" page's block loop, kept un-normalised; the rescale is skipped when no
 // head's maximum moved (the factor is then exactly 1).
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "merge.h"
 #include "tad_internal.h"
@@ -56,18 +58,30 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Two fp32 values that are exact bf16 numbers -> one packed dword (x in the low half).
-__device__ __forceinline__ uint32_t pack_exact_bf16(float x, float y) {
-    // v_perm_b32: bytes {x.2, x.3, y.2, y.3} = (x >> 16) | (y & 0xffff0000)
-    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
-}
-
 // x = hi + lo with hi, lo bf16 (truncations): |x - hi - lo| <= 2^-16 |x|.
 __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
     const uint32_t h = __float_as_uint(x) & 0xffff0000u;
     const float r = x - __uint_as_float(h);              // exact
     hi = h >> 16;
     lo = __float_as_uint(r) >> 16;
+}
+
+// Four FP8 codes (one dword) -> four bf16 in two dwords, codes 0, 1 in lo and 2, 3 in
+// hi (low half first).  gfx950's scaled conversion with scale 1 is exact: every E4M3
+// and E5M2 value is a bf16 number.
+template <int KVT>
+__device__ __forceinline__ void widen_fp8x4(uint32_t w, uint32_t &lo, uint32_t &hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t a, b;
+    if constexpr (KVT == kKvE4M3) {
+        a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);
+        b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);
+    } else {
+        a = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, false);
+        b = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, true);
+    }
+    lo = __builtin_bit_cast(uint32_t, a);
+    hi = __builtin_bit_cast(uint32_t, b);
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -81,44 +95,42 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // WAVES: occupancy target (waves per SIMD) the register allocator must meet.
-// PAGED: K/V rows come from a paged cache; each 16-key tile lies inside one page
-// (page sizes are multiples of 16) and gets its own buffer resources.
+// PAGED: K/V rows come from a paged cache; each 16-row piece of a tile lies inside one
+// page (page sizes are multiples of 16) and gets its own buffer resources.
 // HG, NWH: a work-group serves HG adjacent KV heads of one chunk with NWH waves each
 // (HG = 1: the 4 waves share one KV head).  With HG = 4 and caches that store the KV
 // heads of a key next to each other, the waves of the 4 heads read the 4 adjacent
 // rows of each key at about the same time, where one head's waves alone would read
 // short runs spread over the cache.
-// KVT: kKvBF16, or an FP8 format (kKvE4M3, kKvE5M2): FP8 tiles land in their own LDS
-// buffer; K operands are read from it and widened to bf16 in registers, and the V tile
-// is widened into the bf16 tile buffer for the transposing read (exact: every E4M3
-// and E5M2 value is a bf16 number).
+// KVT: kKvBF16, or an FP8 format (kKvE4M3, kKvE5M2).  FP8 tiles hold 32 keys (the
+// same bytes as a 16-key bf16 tile) and stay FP8 in LDS: the K operands are read
+// as they are, the V^T operands through gfx950's 8-bit transposing LDS read
+// (ds_read_b64_tr_b8), and both are widened to bf16 in registers (exact: every E4M3
+// and E5M2 value is a bf16 number).  The value product then runs on
+// v_mfma_f32_16x16x32_bf16 over the 32 keys.
 template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(D == 64 || D == 128, "head dim");
+    constexpr bool F8 = KVT != kKvBF16;
+    constexpr int ELEM = F8 ? 1 : 2;     // bytes per K/V element
     constexpr int NKK = D / 32;          // 32-wide slices of d (score reduction)
     constexpr int NB = D / 16;           // 16-wide column blocks of the output
-    constexpr int TK = 16;               // keys per wave tile
-    constexpr int CH = D / 8;            // 16-byte chunks per bf16 row
+    constexpr int TK = F8 ? 32 : 16;     // keys per wave tile
+    constexpr int NSB = TK / 16;         // 16-key score blocks per tile
+    constexpr int CH = D * ELEM / 16;    // 16-byte chunks per row
     constexpr int RPI = 64 / CH;         // rows per load instruction
     constexpr int NLD = TK / RPI;        // load instructions per tile and tensor
-    constexpr int TILE = TK * CH;        // 16-byte LDS slots per tile
+    constexpr int TILE = TK * CH;        // 16-byte LDS slots per tile and tensor
     constexpr int NW = HG * NWH;         // waves per work-group
     constexpr int THREADS = 64 * NW;
     constexpr int MAXG = 16;
+    static_assert(RPI <= 16 && NLD % NSB == 0, "a load instruction stays inside one 16-row piece of a tile");
     static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
-    constexpr bool F8 = KVT != kKvBF16;
-    constexpr int ELEM = F8 ? 1 : 2;
-    constexpr int CHF = D / 16;          // 16-byte chunks per FP8 row
-    constexpr int RPIF = 64 / CHF;       // FP8 rows per load instruction
-    constexpr int NLDF = TK / RPIF;      // FP8 load instructions per tile and tensor
-    constexpr int TILEF = F8 ? TK * CHF : 0;   // 16-byte LDS slots per FP8 tile
 
-    // Per wave: a bf16 (K tile, V tile) pair in smem and (FP8) the FP8 pair the loads
-    // land in, in smemF.  The bf16 tiles are reused for the merge.
+    // Per wave: a (K tile, V tile) pair, reused for the merge.
     __shared__ uint4 smem[NW * 2 * TILE];
-    __shared__ uint4 smemF[F8 ? NW * 2 * TILEF : 1];
-    __shared__ float lds_ml[2][NW][MAXG];
+    __shared__ float lds_ml[3][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -145,13 +157,15 @@ void split_mfma_kernel(SplitArgs a) {
     // keys this column's token sees, and that limit relative to the chunk start
     const int Lc = visible_keys(cr.L, nq, tok);
     const int lim = min(n, Lc - j0);
+    // tiles ending at or before lim_all are seen in full by every column
+    const int lim_all = __builtin_amdgcn_readfirstlane(min(n, visible_keys(cr.L, nq, 0) - j0));
 
     const KvRows kvk(a.k, ELEM, a.skb, a.skh, a.skj, a.skp, a, b, kvh);
     const KvRows kvv(a.v, ELEM, a.svb, a.svh, a.svj, a.svp, a, b, kvh);
     const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
     const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
-    TilePages pages;                                       // paged: this wave's tile pages
+    TilePages pages[NSB];                                  // paged: pages of the tiles' 16-row pieces
     int ktile = 0;                                         // paged: tiles issued so far
 
     // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo,
@@ -182,13 +196,14 @@ void split_mfma_kernel(SplitArgs a) {
     const float slope2 = (a.slopes && head_ok) ? a.slopes[h] * 1.4426950408889634f : 0.f;
     const bool alibi = a.slopes != nullptr;
 
-    // LDS slot (row r, position p) holds chunk p ^ swz(r) of row r; with CH = 16 the
-    // 16 rows of an operand read land in 16 distinct 16-byte bank groups, and with
-    // CH = 8 the row parity plus swz(r) = r/2 does the same.
-    auto swz = [](int r) { return (r / (16 / CH)) % CH; };
-    auto swzf = [](int r) { return (r / (16 / CHF)) % CHF; };   // the same for FP8 rows
+    // LDS slot (row r, position p) holds chunk p ^ swz(r) of row r.  Within a 16-row
+    // score block the 16 rows of an operand read land in distinct 16-byte bank groups
+    // (CH = 16: swz(r) = r; CH = 8: the row parity plus r/2; CH = 4: the row's place in
+    // the 256-byte bank space plus r/4).  Rows 16..31 of an FP8 tile are rotated by
+    // CH/2 more, so that the transposing V read, which takes rows from both halves,
+    // spreads too.
+    auto swz = [](int r) { return (r / (16 / CH) + (r / 16) * (CH / 2)) % CH; };
     uint4 *const bufA = smem + wave * 2 * TILE;
-    uint4 *const bufF = smemF + wave * 2 * TILEF;                  // FP8 only
     const int ld_r = lane / CH, ld_p = lane % CH;
     // A operand of the value product for value columns [16 nb, 16 nb + 16): lane l needs
     // V[4(l/16) + t][16 nb + l%16], t = 0..3.  ds_read_b64_tr_b16 hands lane i of a
@@ -202,32 +217,37 @@ void split_mfma_kernel(SplitArgs a) {
         const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p);
         return __builtin_bit_cast(uint2, v);
     };
+    // FP8: the A operand of the 16x16x32 value product for value columns [16 nb, +16):
+    // lane l needs V[key(8(l/16) + t)][16 nb + l%16], t = 0..7, with reduction slot
+    // 8 c + t holding key 4c + t (t < 4) or 16 + 4c + t - 4 (t >= 4) -- the keys whose
+    // probabilities the lane already holds.  ds_read_b64_tr_b8 hands lane i of a
+    // 16-lane group byte i%8 of the 8-byte pieces addressed by lanes i/8 + 2t, so lane
+    // l addresses the row of slot 8 c4 + j16/2, bytes 16 nb + 8 (j16 & 1) .. + 7.
+    const int tr8_t = j16 >> 1;
+    const int tr8_row = tr8_t < 4 ? 4 * c4 + tr8_t : 16 + 4 * c4 + tr8_t - 4;
+    auto read_vt8 = [&](const uint4 *tv, int nb) -> uint2 {
+        typedef int v2i_t __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
+        const char *p = (const char *)(tv + tr8_row * CH + (nb ^ swz(tr8_row))) + 8 * (j16 & 1);
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)p));
+    };
     // HBM -> LDS, whole rows per instruction; rows past the chunk end read as zero.
     auto issue_tile = [&](uint4 *tk, int t0) {
         uint4 *tv = tk + TILE;
-        __amdgpu_buffer_rsrc_t krs = kr, vrs = vr;
-        int tb = t0;                                       // first row, relative to the resource
-        if constexpr (PAGED) {
-            const int nt = min(TK, n - t0);
-            const int page = pages.get(kvk, j0, n, wr * TK, NWH * TK, ktile++);
-            krs = kvk.page_rows(page, j0 + t0, nt);
-            vrs = kvv.page_rows(page, j0 + t0, nt);
-            tb = 0;
-        }
-        if constexpr (F8) {
-            // FP8 rows land in bufF with slot p of row r holding chunk p ^ swzf(r)
 #pragma unroll
-            for (int u = 0; u < NLDF; ++u) {
-                const int r = u * RPIF + lane / CHF;
-                const uint32_t col = 16u * (uint32_t)((lane % CHF) ^ swzf(r));
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(bufF + u * 64), 16,
-                                                         (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(bufF + TILEF + u * 64), 16,
-                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
+        for (int h = 0; h < NSB; ++h) {                    // 16-row pieces of the tile
+            __amdgpu_buffer_rsrc_t krs = kr, vrs = vr;
+            int tb = t0;                                   // tile row 0, relative to the resource
+            if constexpr (PAGED) {
+                const int th = t0 + 16 * h;
+                const int nt = max(0, min(16, n - th));
+                const int page = pages[h].get(kvk, j0, n, wr * TK + 16 * h, NWH * TK, ktile);
+                krs = kvk.page_rows(page, j0 + th, nt);
+                vrs = kvv.page_rows(page, j0 + th, nt);
+                tb = -16 * h;
             }
-        } else {
 #pragma unroll
-            for (int u = 0; u < NLD; ++u) {
+            for (int u = h * (NLD / NSB); u < (h + 1) * (NLD / NSB); ++u) {
                 const int r = u * RPI + ld_r;
                 const uint32_t col = 16u * (uint32_t)(ld_p ^ swz(r));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(tk + u * 64), 16,
@@ -236,112 +256,101 @@ void split_mfma_kernel(SplitArgs a) {
                                                          (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
             }
         }
+        if constexpr (PAGED) ++ktile;
     };
-    // FP8: widen the landed V tile (bufF) into the swizzled bf16 tile layout.  An FP8
-    // chunk holds dims 16 fc .. 16 fc + 15 of its row, i.e. bf16 chunks 2 fc, 2 fc + 1.
-    auto widen_tile = [&](const uint4 *src, uint4 *dst) {
-#pragma unroll
-        for (int i = 0; i < TK * CHF / 64; ++i) {
-            const int idx = lane + 64 * i, r = idx / CHF, fc = (idx % CHF) ^ swzf(r);
-            const uint4 w = src[idx];
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-            uint32_t o8[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                typedef float f2_t __attribute__((ext_vector_type(2)));
-                f2_t lo, hi;
-                if constexpr (KVT == kKvE4M3) {
-                    lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
-                    hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
-                } else {
-                    lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], false);
-                    hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], true);
-                }
-                o8[2 * j] = pack_exact_bf16(lo.x, lo.y);
-                o8[2 * j + 1] = pack_exact_bf16(hi.x, hi.y);
-            }
-            dst[r * CH + ((2 * fc) ^ swz(r))] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-            dst[r * CH + ((2 * fc + 1) ^ swz(r))] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-        }
-    };
-
-    float m = kNegInf, l = 0.f;
+    // Column state: O and l are sums of 2^(s - m) for a reference m that is moved up to
+    // the running maximum mx only when mx passes it by more than kSlack (so a tile's
+    // weights are at most 2^kSlack and the rescale of O is rare); the epilogue
+    // re-expresses every wave's sums against the exact chunk maximum.
+    constexpr float kSlack = 8.f;
+    float m = kNegInf, mx = kNegInf, l = 0.f;
     f32x4_t O[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // The matrix operands of one tile, as each lane holds them: K rows for the score
-    // product, V^T blocks for the value product.
+    // product (bf16: 8 dims; FP8: 8 dims of each 16-key block, still FP8), V^T blocks
+    // for the value product (bf16: 4 keys; FP8: 8 keys, still FP8).
     struct TileOps {
-        uint4 k[NKK];
+        typename std::conditional<F8, uint2, uint4>::type k[NSB][NKK];
         uint2 v[NB];
     };
     auto read_tile = [&](const uint4 *tk, TileOps &ops) {
         if constexpr (F8) {
-            // K operands straight from the FP8 tile: dims 32 kk + 8 c4 .. + 7 of row j16
-            // are 8 bytes of chunk 2 kk + c4/2, widened to bf16 in registers (exact)
+            // dims 32 kk + 8 c4 .. + 7 of row 16 sb + j16: 8 bytes of chunk 2 kk + c4/2
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                const uint2 w8 = *(const uint2 *)((const uint32_t *)(bufF + j16 * CHF +
-                                                                     ((2 * kk + (c4 >> 1)) ^ swzf(j16))) +
-                                                  2 * (c4 & 1));
-                const uint32_t ws[2] = {w8.x, w8.y};
-                uint32_t o4[4];
+            for (int sb = 0; sb < NSB; ++sb) {
+                const int r = 16 * sb + j16;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    typedef float f2_t __attribute__((ext_vector_type(2)));
-                    f2_t lo, hi;
-                    if constexpr (KVT == kKvE4M3) {
-                        lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], false);
-                        hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[j], true);
-                    } else {
-                        lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], false);
-                        hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)ws[j], true);
-                    }
-                    o4[2 * j] = pack_exact_bf16(lo.x, lo.y);
-                    o4[2 * j + 1] = pack_exact_bf16(hi.x, hi.y);
-                }
-                ops.k[kk] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                for (int kk = 0; kk < NKK; ++kk)
+                    ops.k[sb][kk] = *(const uint2 *)((const uint32_t *)(tk + r * CH + ((2 * kk + (c4 >> 1)) ^ swz(r))) +
+                                                     2 * (c4 & 1));
             }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) ops.v[nb] = read_vt8(tk + TILE, nb);
         } else {
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) ops.k[kk] = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
-        }
+            for (int kk = 0; kk < NKK; ++kk) ops.k[0][kk] = tk[j16 * CH + ((4 * kk + c4) ^ swz(j16))];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) ops.v[nb] = read_vt(tk + TILE, nb);
+            for (int nb = 0; nb < NB; ++nb) ops.v[nb] = read_vt(tk + TILE, nb);
+        }
+    };
+    auto widen8 = [](uint2 w) -> uint4 {               // 8 FP8 codes -> 8 bf16, in order
+        uint4 o;
+        widen_fp8x4<KVT>(w.x, o.x, o.y);
+        widen_fp8x4<KVT>(w.y, o.z, o.w);
+        return o;
     };
 
-    auto consume = [&](const TileOps &ops, int t0) {
-        // scores: sc[r] is key t0 + 4 c4 + r, head j16
-        f32x4_t sc = zero4;
+    // ALIBI: add the per-head linear bias (wave-uniform: its own loop body).  Only tiles
+    // reaching past some column's visible limit run the masking.
+    auto consume = [&](const TileOps &ops, int t0, auto alibi_c) {
+        constexpr bool ALIBI = decltype(alibi_c)::value;
+        // scores: p[4 sb + r] is key t0 + 16 sb + 4 c4 + r, head j16
+        float p[4 * NSB];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            sc = mfma16x16x32(ops.k[kk], qhi[kk], sc);
-            sc = mfma16x16x32(ops.k[kk], qlo[kk], sc);
-        }
-        float p[4];
+        for (int sb = 0; sb < NSB; ++sb) {
+            f32x4_t sc = zero4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = t0 + 4 * c4 + r;
-            float x = sc[r];
-            if (alibi) x = fmaf(slope2, (float)(j0 + key - (Lc - 1)), x);
-            p[r] = (key < lim) ? x : kNegInf;
+            for (int kk = 0; kk < NKK; ++kk) {
+                uint4 kop;
+                if constexpr (F8) kop = widen8(ops.k[sb][kk]);
+                else kop = ops.k[sb][kk];
+                sc = mfma16x16x32(kop, qhi[kk], sc);
+                sc = mfma16x16x32(kop, qlo[kk], sc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = sc[r];
+                if constexpr (ALIBI) x = fmaf(slope2, (float)(j0 + t0 + 16 * sb + 4 * c4 + r - (Lc - 1)), x);
+                p[4 * sb + r] = x;
+            }
         }
-        float mt = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+        if (t0 + TK > lim_all) {
+#pragma unroll
+            for (int i = 0; i < 4 * NSB; ++i) p[i] = (t0 + 16 * (i / 4) + 4 * c4 + i % 4 < lim) ? p[i] : kNegInf;
+        }
+        float mt = p[0];
+#pragma unroll
+        for (int i = 1; i < 4 * NSB; ++i) mt = fmaxf(mt, p[i]);
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m, mt);
+        mx = fmaxf(mx, mt);
+        // some column's maximum passed its reference by more than the slack (or its
+        // first key arrived): every column's reference moves up to its running maximum
+        const bool up = __any(mt > m + kSlack);
+        const float m_new = up ? mx : m;
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
         float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p[r] = exp2_fast(p[r] - m_use);
-            ps += p[r];
+        for (int i = 0; i < 4 * NSB; ++i) {
+            p[i] = exp2_fast(p[i] - m_use);
+            ps += p[i];
         }
         ps += __shfl_xor(ps, 16, 64);
         ps += __shfl_xor(ps, 32, 64);
-        if (__any(m_new != m)) {               // some head's running max moved
+        if (up) {
             const float alpha = exp2_fast(m - m_use);
             l *= alpha;
 #pragma unroll
@@ -350,18 +359,30 @@ void split_mfma_kernel(SplitArgs a) {
         l += ps;
         m = m_new;
 
-        // P^T operands: reduction slot t of this lane is key t0 + 4 c4 + t
-        uint32_t ph[4], pl[4];
+        // P^T operands: reduction slot t of this lane holds p[t] -- bf16: key
+        // t0 + 4 c4 + t; FP8: the slot order of the V^T read above
+        uint32_t ph[4 * NSB], pl[4 * NSB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) split_bf16(p[r], ph[r], pl[r]);
-        const uint2 phi = make_uint2(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16);
-        const uint2 plo = make_uint2(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16);
-
-        // V^T blocks straight from LDS with the transposing read, then the value update
+        for (int i = 0; i < 4 * NSB; ++i) split_bf16(p[i], ph[i], pl[i]);
+        if constexpr (F8) {
+            const uint4 phi = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16, ph[4] | ph[5] << 16,
+                                         ph[6] | ph[7] << 16);
+            const uint4 plo = make_uint4(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16, pl[4] | pl[5] << 16,
+                                         pl[6] | pl[7] << 16);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            O[nb] = mfma16x16x16(ops.v[nb], phi, O[nb]);
-            O[nb] = mfma16x16x16(ops.v[nb], plo, O[nb]);
+            for (int nb = 0; nb < NB; ++nb) {
+                const uint4 vt = widen8(ops.v[nb]);
+                O[nb] = mfma16x16x32(vt, phi, O[nb]);
+                O[nb] = mfma16x16x32(vt, plo, O[nb]);
+            }
+        } else {
+            const uint2 phi = make_uint2(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16);
+            const uint2 plo = make_uint2(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                O[nb] = mfma16x16x16(ops.v[nb], phi, O[nb]);
+                O[nb] = mfma16x16x16(ops.v[nb], plo, O[nb]);
+            }
         }
     };
 
@@ -370,19 +391,22 @@ void split_mfma_kernel(SplitArgs a) {
     constexpr int LGKM_ALL = 0xC07F;               // s_waitcnt lgkmcnt(0)
     // The buffer is refilled as soon as the tile's operands are in registers (the LDS
     // reads have returned), and the tile is consumed while the next one loads.
-    int t0 = wr * TK;
-    if (t0 < n) issue_tile(bufA, t0);
-    while (t0 < n) {
-        __builtin_amdgcn_s_waitcnt(VM_ALL);
-        if constexpr (F8) widen_tile(bufF + TILEF, bufA + TILE);
-        TileOps ops;
-        read_tile(bufA, ops);
-        __builtin_amdgcn_s_waitcnt(LGKM_ALL);
-        const int tn = t0 + STRIDE;
-        if (tn < n) issue_tile(bufA, tn);
-        consume(ops, t0);
-        t0 = tn;
-    }
+    auto run = [&](auto alibi_c) {
+        int t0 = wr * TK;
+        if (t0 < n) issue_tile(bufA, t0);
+        while (t0 < n) {
+            __builtin_amdgcn_s_waitcnt(VM_ALL);
+            TileOps ops;
+            read_tile(bufA, ops);
+            __builtin_amdgcn_s_waitcnt(LGKM_ALL);
+            const int tn = t0 + STRIDE;
+            if (tn < n) issue_tile(bufA, tn);
+            consume(ops, t0, alibi_c);
+            t0 = tn;
+        }
+    };
+    if (alibi) run(std::true_type{});
+    else run(std::false_type{});
 
     // ---- merge the NW wave states per head through LDS (reusing the tile buffers).
     __syncthreads();
@@ -395,14 +419,15 @@ void split_mfma_kernel(SplitArgs a) {
         if (c4 == 0) {
             lds_ml[0][wave][j16] = m;
             lds_ml[1][wave][j16] = l;
+            lds_ml[2][wave][j16] = mx;
         }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
         const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
-        float M = kNegInf;
+        float M = kNegInf;                   // the exact chunk maximum of the column
 #pragma unroll
-        for (int w = x * NWH; w < x * NWH + NWH; ++w) M = fmaxf(M, lds_ml[0][w][hh]);
+        for (int w = x * NWH; w < x * NWH + NWH; ++w) M = fmaxf(M, lds_ml[2][w][hh]);
         const float Mu = (M == kNegInf) ? 0.f : M;
         float acc = 0.f, lsum = 0.f;
 #pragma unroll
