@@ -84,6 +84,23 @@ __device__ __forceinline__ void widen_fp8x4(uint32_t w, uint32_t &lo, uint32_t &
     hi = __builtin_bit_cast(uint32_t, b);
 }
 
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane rows) with gfx950's
+// row swaps, which stay in the VALU (no LDS round trip).  Each swap leaves a lane's own
+// value and its partner's in the two results in the same order in both rows of a
+// pair, so every lane computes the identical expression.
+__device__ __forceinline__ float rows_max(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -141,8 +158,12 @@ void split_mfma_kernel(SplitArgs a) {
     // head kvh*g + j16/nq, token j16%nq; with one token this is one head per column.
     const int S = a.S, g = a.group, nq = a.nq;
     const int gq = g * nq;
-    const int s = blockIdx.x % S;
+    // Work-group i runs on XCD i mod 8.  Chunk numbers are rotated by the unit index so
+    // that the first chunks of the units (the ones ragged rows have) start on different
+    // XCDs instead of piling onto the same ones (ragged grouped-query decode: 120 ->
+    // 116.5 us; paged: 123.5 -> 117.8 us).
     const int bk = blockIdx.x / S;
+    const int s = (int)((blockIdx.x + bk) % S);
     const int b = bk / (a.Hkv / HG);
     const int kvh0 = (bk % (a.Hkv / HG)) * HG;             // first KV head of the work-group
     const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
@@ -232,6 +253,10 @@ void split_mfma_kernel(SplitArgs a) {
         return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)p));
     };
     // HBM -> LDS, whole rows per instruction; rows past the chunk end read as zero.
+    // K is read non-temporal.  V too for bf16; FP8 V tiles use the default policy,
+    // which measured faster when part of the chip idles (ragged FP8 grouped-query
+    // decode: 49.3 -> 46.8 us) and made no difference or was slower elsewhere.
+    constexpr int VPOL = F8 ? kPolicyDefault : kPolicyNT;
     auto issue_tile = [&](uint4 *tk, int t0) {
         uint4 *tv = tk + TILE;
 #pragma unroll
@@ -253,7 +278,7 @@ void split_mfma_kernel(SplitArgs a) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(tk + u * 64), 16,
                                                          (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(tv + u * 64), 16,
-                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
+                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, VPOL);
             }
         }
         if constexpr (PAGED) ++ktile;
@@ -311,15 +336,16 @@ void split_mfma_kernel(SplitArgs a) {
         float p[4 * NSB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-            f32x4_t sc = zero4;
+            f32x4_t sh = zero4, sl = zero4;                // q hi and lo: two independent chains
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 uint4 kop;
                 if constexpr (F8) kop = widen8(ops.k[sb][kk]);
                 else kop = ops.k[sb][kk];
-                sc = mfma16x16x32(kop, qhi[kk], sc);
-                sc = mfma16x16x32(kop, qlo[kk], sc);
+                sh = mfma16x16x32(kop, qhi[kk], sh);
+                sl = mfma16x16x32(kop, qlo[kk], sl);
             }
+            const f32x4_t sc = sh + sl;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float x = sc[r];
@@ -334,8 +360,7 @@ void split_mfma_kernel(SplitArgs a) {
         float mt = p[0];
 #pragma unroll
         for (int i = 1; i < 4 * NSB; ++i) mt = fmaxf(mt, p[i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = rows_max(mt);
         mx = fmaxf(mx, mt);
         // some column's maximum passed its reference by more than the slack (or its
         // first key arrived): every column's reference moves up to its running maximum
@@ -348,8 +373,7 @@ void split_mfma_kernel(SplitArgs a) {
             p[i] = exp2_fast(p[i] - m_use);
             ps += p[i];
         }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
+        ps = rows_sum(ps);
         if (up) {
             const float alpha = exp2_fast(m - m_use);
             l *= alpha;
