@@ -158,23 +158,36 @@ void split_mfma_kernel(SplitArgs a) {
     // head kvh*g + j16/nq, token j16%nq; with one token this is one head per column.
     const int S = a.S, g = a.group, nq = a.nq;
     const int gq = g * nq;
-    // Work-group i runs on XCD i mod 8.  Chunk numbers are rotated by the unit index so
-    // that the first chunks of the units (the ones ragged rows have) start on different
-    // XCDs instead of piling onto the same ones (ragged grouped-query decode: 120 ->
-    // 116.5 us; paged: 123.5 -> 117.8 us).
-    const int bk = blockIdx.x / S;
-    const int s = (int)((blockIdx.x + bk) % S);
-    const int b = bk / (a.Hkv / HG);
-    const int kvh0 = (bk % (a.Hkv / HG)) * HG;             // first KV head of the work-group
+    // Work-group -> (row b, KV-head group, chunk s): every non-empty chunk of the batch
+    // first, so that a ragged batch's busy work-groups are dispatched together and
+    // spread over the XCDs in turn (work-group i runs on XCD i mod 8).
+    const int c = batch_chunk_len(a);
+    const WorkItem wi = busy_first_item(a, a.Hkv / HG, (int)blockIdx.x, c);
+    const int b = wi.b, s = wi.s;
+    const int kvh0 = wi.g * HG;                            // first KV head of the work-group
     const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
     const int kvh = kvh0 + hx;
     const bool head_ok = j16 < gq;
     const int tok = head_ok ? j16 % nq : 0;
     const int h = kvh * g + (head_ok ? j16 / nq : 0);
 
-    const ChunkRange cr = chunk_range(a, b, s);
+    const ChunkRange cr = chunk_range_c(a, b, s, c);
     const int j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
+    // An empty chunk writes the merge identity (m = -inf, l = 0, o = 0) and leaves,
+    // unless the work-group takes part in a fused merge.
+    if (n == 0 && !a.fused) {
+        for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
+            const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
+            const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
+            a.ws_o[r * D + e] = 0.f;
+            if (e == 0) {
+                a.ws_m[r] = kNegInf;
+                a.ws_l[r] = 0.f;
+            }
+        }
+        return;
+    }
     // keys this column's token sees, and that limit relative to the chunk start
     const int Lc = visible_keys(cr.L, nq, tok);
     const int lim = min(n, Lc - j0);

@@ -62,25 +62,87 @@ struct ChunkRange {
     int L, j0, j1;
 };
 
-__device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int s) {
-    int L = a.Lmax, Lref = a.Lmax;
+// Row b's length, clamped to [0, Lmax].
+__device__ __forceinline__ int row_len(const SplitArgs &a, int b) {
+    return a.seq_lens ? min(max(a.seq_lens[b], 0), a.Lmax) : a.Lmax;
+}
+
+// The batch chunk length c (wave-uniform).
+__device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
+    int Lref = a.Lmax;
     if (a.seq_lens) {
-        L = min(max(a.seq_lens[b], 0), a.Lmax);
         int mx = 0;
-        for (int i = (int)(threadIdx.x & 63); i < a.B; i += 64) mx = max(mx, min(max(a.seq_lens[i], 0), a.Lmax));
+        for (int i = (int)(threadIdx.x & 63); i < a.B; i += 64) mx = max(mx, row_len(a, i));
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
         Lref = __builtin_amdgcn_readfirstlane(mx);   // equal in every lane: keep it scalar
     }
     int c = (Lref + a.S - 1) / a.S;
     if (a.block_table) c = (c + a.page_size - 1) / a.page_size * a.page_size;   // whole pages
+    return c;
+}
+
+__device__ __forceinline__ ChunkRange chunk_range_c(const SplitArgs &a, int b, int s, int c) {
     ChunkRange r;
-    r.L = L;
-    r.j0 = (int)min((int64_t)s * c, (int64_t)L);
-    r.j1 = min(r.j0 + c, L);
+    r.L = row_len(a, b);
+    r.j0 = (int)min((int64_t)s * c, (int64_t)r.L);
+    r.j1 = min(r.j0 + c, r.L);
     return r;
 }
 
+__device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int s) {
+    return chunk_range_c(a, b, s, batch_chunk_len(a));
+}
+
+// Work-group k of a grid of B * G * S, G work-groups per (row, chunk): the (row b,
+// index g < G, chunk s) it serves, with every non-empty chunk of the batch ahead of
+// every empty one -- row by row, g by g, chunk by chunk among the non-empty ones, then
+// the same among the empty ones.  A ragged batch's busy work-groups are thus all
+// dispatched first (and spread over the XCDs in turn) instead of waiting behind
+// empty ones.  Wave-uniform; must be called by whole waves.
+struct WorkItem {
+    int b, g, s;
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ WorkItem busy_first_item(const SplitArgs &a, int G, int k, int c) {
+    const int lane = (int)(threadIdx.x & 63);
+    for (int pass = 0; pass < 2; ++pass) {       // 0: non-empty chunks, 1: empty ones
+        for (int b0 = 0; b0 < a.B; b0 += 64) {
+            const int bb = b0 + lane;
+            int cnt = 0;                         // this row's chunks of the pass
+            if (bb < a.B) {
+                const int L = row_len(a, bb);
+                const int busy = c > 0 ? min((L + c - 1) / c, a.S) : 0;
+                cnt = pass == 0 ? busy : a.S - busy;
+            }
+            const int incl = wave_incl_scan(cnt * G);
+            const int tot = __builtin_amdgcn_readlane(incl, 63);
+            if (k < tot) {
+                const uint64_t hit = __ballot(incl > k);
+                const int r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+                const int nr = __builtin_amdgcn_readlane(cnt, r);
+                const int off = k - (__builtin_amdgcn_readlane(incl, r) - nr * G);
+                WorkItem w;
+                w.b = b0 + r;
+                w.g = off / nr;
+                w.s = off % nr + (pass == 0 ? 0 : a.S - nr);
+                return w;
+            }
+            k -= tot;
+        }
+    }
+    return WorkItem{0, 0, 0};                    // not reached for k < B * G * S
+}
 // Rows of one (b, kv head) of K or V: a strided slab, or pages of a paged cache.
 struct KvRows {
     const char *base;       // slab: row 0 of the (b, kv head); paged: cache + kv-head offset

@@ -379,6 +379,51 @@ def test_split_partials_ragged_batch(lib):
                 np.testing.assert_allclose(o[b, h, s] * fix, num, rtol=1e-4, atol=1e-4 * np.abs(num).max())
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(80, 16, 4, 5), (70, 32, 8, 3), (3, 32, 8, 64), (2, 8, 4, 12)])
+def test_grouped_ragged_rows_busy_first(lib, B, Hq, Hkv, S):
+    """Matrix-core kernel with 4 KV heads per work-group: more rows than a wave has lanes,
+    zero lengths and many empty chunks.  Work-group k serves the k-th chunk in
+    busy-first order; every (row, head, chunk) partial must still be produced exactly
+    once.  (2, 8, 4, 12) is a small grid: the fused merge, where empty chunks stay in
+    the arrival count."""
+    g = torch.Generator().manual_seed(B + S)
+    L = 300 if B > 8 else 2000
+    lens = torch.randint(0, L + 1, (B,), generator=g).tolist()
+    lens[0], lens[-1], lens[B // 2] = 0, L, 1
+    run_case(lib, 470 + B + S, B, Hq, Hkv, L, 128, seq_lens=lens, n_splits=S)
+
+
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
+def test_grouped_split_partials_ragged(lib, kv):
+    """Per-chunk partials of the matrix-core kernel on a ragged batch: the chunk
+    statistics of the tree decoding steps, and the merge identity for empty chunks."""
+    lens = [1500, 0, 333, 1100]
+    B, Hq, Hkv, L, d, S = 4, 8, 4, 1500, 128, 9
+    c = W.random_case(225, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens)
+    g = to_dev(c)
+    m, l, o = lib.split_partials(g["q"], g["k"], g["v"], g["seq_lens"], None, S, k_scale=g["k_scale"],
+                                 v_scale=g["v_scale"])
+    torch.cuda.synchronize()
+    m, l, o = m.cpu().double().numpy(), l.cpu().double().numpy(), o.cpu().double().numpy()
+    clen = -(-max(lens) // S)
+    kw, vw = oracle.widen(c["k"]), oracle.widen(c["v"])
+    if c["k_scale"] is not None:
+        kw = kw * c["k_scale"].double().numpy()[:, :, None, None]
+        vw = vw * c["v_scale"].double().numpy()[:, :, None, None]
+    for b, Lb in enumerate(lens):
+        for h in range(Hq):
+            kh = h // (Hq // Hkv)
+            parts = tree.chunk_partials(oracle.widen(c["q"])[b, h], kw[b, kh, :Lb], vw[b, kh, :Lb], S, None, clen)
+            for s, (lm, den, num) in enumerate(parts):
+                if den == 0.0:
+                    assert m[b, h, s] == -np.inf and l[b, h, s] == 0 and (o[b, h, s] == 0).all()
+                    continue
+                assert m[b, h, s] * math.log(2) == pytest.approx(lm, rel=1e-4, abs=1e-4)
+                fix = math.exp(m[b, h, s] * math.log(2) - lm)
+                assert l[b, h, s] * fix == pytest.approx(den, rel=2e-3)
+                np.testing.assert_allclose(o[b, h, s] * fix, num, rtol=2e-3, atol=2e-3 * np.abs(num).max())
+
+
 def test_empty_chunk_partials(lib):
     """Chunks past the sequence end are the merge identity: m = -inf, l = 0, o = 0."""
     c = to_dev(W.random_case(220, 1, 2, 2, 9, 64))
