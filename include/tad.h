@@ -147,12 +147,15 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
 
 /*
  * Split + merge with a caller-provided workspace (no allocation).  Small problems
- * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 1024) run
- * as ONE launch: each split work-group writes its partial, and the last one of a
- * row to finish (counted in the workspace's cnt array) merges the row, then returns
- * its counter to zero.  Larger problems, and caches whose KV heads are interleaved
- * per key with one query head per KV head (read by a kernel without the fused form),
- * run the split and combine kernels back to back (the counters are then unused).
+ * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 1024)
+ * read by the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d]
+ * caches, and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512,
+ * more than 16 query rows per KV head) run as ONE launch: each split work-group
+ * writes its partial, and the last one of a row to finish (counted in the
+ * workspace's cnt array) merges the row, then returns its counter to zero.  Larger
+ * problems, grouped-query heads on the matrix cores and caches whose KV heads are
+ * interleaved per key with one query head per KV head run the split and combine
+ * kernels back to back (the counters are then unused).
  * Either way the output is bit-identical to
  * tad_split followed by tad_combine.  The counters must be zero the first time a
  * workspace is used (tad_workspace_clear, or memory allocated zeroed); every call

@@ -45,7 +45,6 @@
 #include <type_traits>
 
 #include "device_util.h"
-#include "merge.h"
 #include "tad_internal.h"
 
 namespace tad {
@@ -174,9 +173,8 @@ void split_mfma_kernel(SplitArgs a) {
     const ChunkRange cr = chunk_range_c(a, b, s, c);
     const int j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
-    // An empty chunk writes the merge identity (m = -inf, l = 0, o = 0) and leaves,
-    // unless the work-group takes part in a fused merge.
-    if (n == 0 && !a.fused) {
+    // An empty chunk writes the merge identity (m = -inf, l = 0, o = 0) and leaves.
+    if (n == 0) {
         for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
             const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
             const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
@@ -477,41 +475,10 @@ void split_mfma_kernel(SplitArgs a) {
             if (a.v_scale) acc *= a.v_scale[b * a.Hkv + kvh0 + x];       // V dequantisation
         }
         const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;   // hh: column
-        if (a.fused) {                       // written through for the merging work-group
-            store_partial(&a.ws_o[r * D + e], acc);
-            if (e == 0) {
-                store_partial(&a.ws_m[r], M);
-                store_partial(&a.ws_l[r], lsum);
-            }
-        } else {
-            a.ws_o[r * D + e] = acc;
-            if (e == 0) {
-                a.ws_m[r] = M;
-                a.ws_l[r] = lsum;
-            }
-        }
-    }
-
-    // ---- fused merge: the last of the S work-groups of this (b, KV head group) merges
-    // its HG*g*nq rows (consecutive: query heads kvh0*g .. (kvh0+HG)*g - 1); the group's
-    // arrivals are counted in the counter of its first row.
-    if (a.fused) {
-        static_assert(NW * 2 * TILE * 4 >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in smem");
-        __shared__ int last;
-        const int64_t row0 = ((int64_t)b * a.Hq + kvh0 * g) * nq;
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
-        __syncthreads();
-        if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row0], 1) == S - 1;
-        __syncthreads();
-        if (last) {
-            for (int cc = 0; cc < HG * gq; ++cc) {
-                const int64_t row = row0 + cc;
-                merge_row<D, true, THREADS>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
-                                            a.out + (int64_t)b * a.sob + (int64_t)(kvh0 * g + cc / nq) * a.soh +
-                                                (int64_t)(cc % nq) * a.sot,
-                                            reinterpret_cast<float *>(smem));
-            }
-            if (threadIdx.x == 0) a.cnt[row0] = 0;
+        a.ws_o[r * D + e] = acc;
+        if (e == 0) {
+            a.ws_m[r] = M;
+            a.ws_l[r] = lsum;
         }
     }
 }

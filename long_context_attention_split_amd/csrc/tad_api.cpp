@@ -332,10 +332,13 @@ int check_splits(int32_t S) {
 }
 
 // Split + merge.  Small grids (fewer (row, chunk) pairs than compute units) are
-// launch-bound, and there one launch with the merge fused into the split kernel's
-// last work-group per row wins; on larger grids the fused merge lands on the
-// kernel's tail and costs more than a second, short kernel, so split and combine
-// run back to back.  Both give bit-identical outputs (the same merge routine).
+// launch-bound, and there one launch with the merge fused into the vector kernel's
+// last work-group per row wins (one row each: 13.6 vs 15.5 us for 32 heads x 1024
+// keys).  The matrix-core kernel's work-groups serve up to 64 rows, which one work-
+// group would have to merge one after another (38 vs 15 us), and the head-packed
+// kernel serves 4 heads per wave; those always run split and combine, as do larger
+// grids, where the fused merge lands on the kernel's tail and costs more than a
+// second, short kernel.  Both give bit-identical outputs (the same merge routine).
 int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
                const OutDesc &out, hipStream_t stream) {
@@ -343,10 +346,9 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
     int rc = device_cus(-1, &cus);
     if (rc) return rc;
     const tad::SplitArgs unfused = split_args(P, q, k, v, seq_lens, slopes, S, w, OutDesc());
-    // (the head-packed kernel has no fused form; its layouts always take two launches,
-    // so that the result never depends on the grid size)
-    if (S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus &&
-        !tad::split_heads_supported(unfused, (int)P.d))
+    const bool vector_kernel = !tad::split_mfma_supported((int)P.d, unfused.kv_type, unfused.group, unfused.nq) &&
+                               !tad::split_heads_supported(unfused, (int)P.d);
+    if (vector_kernel && S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus)
         return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
     if ((rc = launch_split(unfused, P.d, stream))) return rc;
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);

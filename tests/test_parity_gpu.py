@@ -165,10 +165,13 @@ def test_strided_and_3d_layouts(lib):
     assert_parity(out1.cpu().numpy(), ref1, torch.bfloat16, vmax_valid(c1["v"], None), "3d")
 
 
-def test_entry_points_agree(lib):
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float32])
+def test_entry_points_agree(lib, kv):
     """tad_decode (stream-ordered allocation), tad_decode_ws and tad_split + tad_combine
-    give bit-identical outputs; repeated calls are bit-identical (fixed-order sums)."""
-    c = to_dev(W.random_case(200, 2, 8, 2, 3333, 128, seq_lens=[3333, 2000], alibi=True))
+    give bit-identical outputs; repeated calls are bit-identical (fixed-order sums).
+    bf16: grouped-query heads on the matrix cores (split + combine); fp32: the vector
+    kernel with its fused merge (a small grid)."""
+    c = to_dev(W.random_case(200, 2, 8, 2, 3333, 128, kv_dtype=kv, seq_lens=[3333, 2000], alibi=True))
     S = 6
     a = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], c["slopes"], S)
     out_b = torch.empty_like(a)
@@ -274,10 +277,10 @@ def test_several_tokens_entry_points_agree(lib):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,nq", [(16, 4, 1), (32, 8, 1), (8, 8, 2)])
-def test_grouped_kv_heads_fused_equals_split_combine(lib, Hq, Hkv, nq, d):
-    """A KV head count divisible by 4 runs 4 KV heads per work-group; on a small grid
-    tad_decode_ws merges in the last work-group of each 4-head group, and the result
-    is bit-identical to tad_split + tad_combine and within the bar of the oracle."""
+def test_grouped_kv_heads_decode_equals_split_combine(lib, Hq, Hkv, nq, d):
+    """Grouped-query heads (4 KV heads per work-group when the KV head count allows)
+    always run split + combine, also on small grids: tad_decode_ws equals tad_split +
+    tad_combine bit for bit, call after call, and is within the bar of the oracle."""
     note("grouped kv heads Hq=%d Hkv=%d nq=%d d=%d" % (Hq, Hkv, nq, d))
     c = W.random_case(460 + Hq + nq + d, 2, Hq, Hkv, 1800, d, seq_lens=[1800, 1001])
     if nq > 1:
@@ -297,10 +300,10 @@ def test_grouped_kv_heads_fused_equals_split_combine(lib, Hq, Hkv, nq, d):
 
 
 def test_workspace_reuse_and_clear(lib):
-    """tad_decode_ws merges in the split kernel's last work-group per row; its arrival
-    counters return to zero, so one workspace serves call after call (and after
-    tad_workspace_clear of a dirty buffer)."""
-    c = to_dev(W.random_case(205, 2, 8, 2, 2500, 128, seq_lens=[2500, 1700]))
+    """On small grids tad_decode_ws merges in the vector split kernel's last work-group
+    per row; its arrival counters return to zero, so one workspace serves call after
+    call (and after tad_workspace_clear of a dirty buffer)."""
+    c = to_dev(W.random_case(205, 2, 8, 8, 2500, 128, seq_lens=[2500, 1700]))
     c2 = to_dev(W.random_case(206, 2, 8, 8, 2500, 64))
     S = 5
     ref = lib.decode(c["q"], c["k"], c["v"], c["seq_lens"], None, S)
@@ -384,8 +387,7 @@ def test_grouped_ragged_rows_busy_first(lib, B, Hq, Hkv, S):
     """Matrix-core kernel with 4 KV heads per work-group: more rows than a wave has lanes,
     zero lengths and many empty chunks.  Work-group k serves the k-th chunk in
     busy-first order; every (row, head, chunk) partial must still be produced exactly
-    once.  (2, 8, 4, 12) is a small grid: the fused merge, where empty chunks stay in
-    the arrival count."""
+    once."""
     g = torch.Generator().manual_seed(B + S)
     L = 300 if B > 8 else 2000
     lens = torch.randint(0, L + 1, (B,), generator=g).tolist()
