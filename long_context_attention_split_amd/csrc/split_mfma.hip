@@ -160,8 +160,9 @@ void split_mfma_kernel(SplitArgs a) {
     // Work-group -> (row b, KV-head group, chunk s): every non-empty chunk of the batch
     // first, so that a ragged batch's busy work-groups are dispatched together and
     // spread over the XCDs in turn (work-group i runs on XCD i mod 8).
-    const int c = batch_chunk_len(a);
-    const WorkItem wi = busy_first_item(a, a.Hkv / HG, (int)blockIdx.x, c);
+    const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, used thrice
+    const int c = batch_chunk_len(a, len0);
+    const WorkItem wi = busy_first_item(a, a.Hkv / HG, (int)blockIdx.x, c, len0);
     const int b = wi.b, s = wi.s;
     const int kvh0 = wi.g * HG;                            // first KV head of the work-group
     const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
@@ -170,7 +171,10 @@ void split_mfma_kernel(SplitArgs a) {
     const int tok = head_ok ? j16 % nq : 0;
     const int h = kvh * g + (head_ok ? j16 / nq : 0);
 
-    const ChunkRange cr = chunk_range_c(a, b, s, c);
+    ChunkRange cr;
+    cr.L = b < 64 ? __builtin_amdgcn_readlane(len0, b) : row_len(a, b);
+    cr.j0 = (int)min((int64_t)s * c, (int64_t)cr.L);
+    cr.j1 = min(cr.j0 + c, cr.L);
     const int j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
     // An empty chunk writes the merge identity (m = -inf, l = 0, o = 0) and leaves.
@@ -200,33 +204,6 @@ void split_mfma_kernel(SplitArgs a) {
     TilePages pages[NSB];                                  // paged: pages of the tiles' 16-row pieces
     int ktile = 0;                                         // paged: tiles issued so far
 
-    // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo,
-    // scaled into base-2 units and by the K dequantisation scale of the KV head (FP8).
-    const float qs = a.qscale * ((F8 && a.k_scale) ? a.k_scale[b * a.Hkv + kvh] : 1.f);
-    uint4 qhi[NKK], qlo[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-        float x[8];
-        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)tok * a.sqt + 32 * kk + 8 * c4;
-        if (a.q_bf16) {
-            const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_lo(ws[i]); x[2 * i + 1] = bf16_hi(ws[i]); }
-        } else {
-            const float4 *qp = (const float4 *)((const float *)a.q + qoff);
-            const float4 x0 = qp[0], x1 = qp[1];
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-        }
-        uint32_t hw[8], lw[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) split_bf16(head_ok ? x[t] * qs : 0.f, hw[t], lw[t]);
-        qhi[kk] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
-        qlo[kk] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
-    }
-    const float slope2 = (a.slopes && head_ok) ? a.slopes[h] * 1.4426950408889634f : 0.f;
-    const bool alibi = a.slopes != nullptr;
 
     // LDS slot (row r, position p) holds chunk p ^ swz(r) of row r.  Within a 16-row
     // score block the 16 rows of an operand read land in distinct 16-byte bank groups
@@ -294,6 +271,37 @@ void split_mfma_kernel(SplitArgs a) {
         }
         if constexpr (PAGED) ++ktile;
     };
+    // The first tile's loads go out before q is read, so that their latencies overlap.
+    if (wr * TK < n) issue_tile(bufA, wr * TK);
+
+    // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo,
+    // scaled into base-2 units and by the K dequantisation scale of the KV head (FP8).
+    const float qs = a.qscale * ((F8 && a.k_scale) ? a.k_scale[b * a.Hkv + kvh] : 1.f);
+    uint4 qhi[NKK], qlo[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        float x[8];
+        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)tok * a.sqt + 32 * kk + 8 * c4;
+        if (a.q_bf16) {
+            const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_lo(ws[i]); x[2 * i + 1] = bf16_hi(ws[i]); }
+        } else {
+            const float4 *qp = (const float4 *)((const float *)a.q + qoff);
+            const float4 x0 = qp[0], x1 = qp[1];
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+        }
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) split_bf16(head_ok ? x[t] * qs : 0.f, hw[t], lw[t]);
+        qhi[kk] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
+        qlo[kk] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
+    }
+    const float slope2 = (a.slopes && head_ok) ? a.slopes[h] * 1.4426950408889634f : 0.f;
+    const bool alibi = a.slopes != nullptr;
+
     // Column state: O and l are sums of 2^(s - m) for a reference m that is moved up to
     // the running maximum mx only when mx passes it by more than kSlack (so a tile's
     // weights are at most 2^kSlack and the rescale of O is rare); the epilogue
@@ -427,8 +435,7 @@ void split_mfma_kernel(SplitArgs a) {
     // The buffer is refilled as soon as the tile's operands are in registers (the LDS
     // reads have returned), and the tile is consumed while the next one loads.
     auto run = [&](auto alibi_c) {
-        int t0 = wr * TK;
-        if (t0 < n) issue_tile(bufA, t0);
+        int t0 = wr * TK;                          // its loads were issued above
         while (t0 < n) {
             __builtin_amdgcn_s_waitcnt(VM_ALL);
             TileOps ops;

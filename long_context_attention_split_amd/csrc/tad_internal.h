@@ -67,12 +67,19 @@ __device__ __forceinline__ int row_len(const SplitArgs &a, int b) {
     return a.seq_lens ? min(max(a.seq_lens[b], 0), a.Lmax) : a.Lmax;
 }
 
-// The batch chunk length c (wave-uniform).
-__device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
+// Row (lane + 64 i)'s length in lane `lane`, for the rows of one 64-row block; 0 past B.
+__device__ __forceinline__ int lane_row_len(const SplitArgs &a, int b0) {
+    const int bb = b0 + (int)(threadIdx.x & 63);
+    return bb < a.B ? row_len(a, bb) : 0;
+}
+
+// The batch chunk length c (wave-uniform).  len0 = lane_row_len(a, 0), loaded once by
+// the caller and reused (the whole batch when B <= 64).
+__device__ __forceinline__ int batch_chunk_len(const SplitArgs &a, int len0) {
     int Lref = a.Lmax;
     if (a.seq_lens) {
-        int mx = 0;
-        for (int i = (int)(threadIdx.x & 63); i < a.B; i += 64) mx = max(mx, row_len(a, i));
+        int mx = len0;
+        for (int b0 = 64; b0 < a.B; b0 += 64) mx = max(mx, lane_row_len(a, b0));
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
         Lref = __builtin_amdgcn_readfirstlane(mx);   // equal in every lane: keep it scalar
@@ -80,6 +87,10 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
     int c = (Lref + a.S - 1) / a.S;
     if (a.block_table) c = (c + a.page_size - 1) / a.page_size * a.page_size;   // whole pages
     return c;
+}
+
+__device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
+    return batch_chunk_len(a, a.seq_lens ? lane_row_len(a, 0) : 0);
 }
 
 __device__ __forceinline__ ChunkRange chunk_range_c(const SplitArgs &a, int b, int s, int c) {
@@ -114,14 +125,14 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
-__device__ __forceinline__ WorkItem busy_first_item(const SplitArgs &a, int G, int k, int c) {
+__device__ __forceinline__ WorkItem busy_first_item(const SplitArgs &a, int G, int k, int c, int len0) {
     const int lane = (int)(threadIdx.x & 63);
     for (int pass = 0; pass < 2; ++pass) {       // 0: non-empty chunks, 1: empty ones
         for (int b0 = 0; b0 < a.B; b0 += 64) {
             const int bb = b0 + lane;
             int cnt = 0;                         // this row's chunks of the pass
             if (bb < a.B) {
-                const int L = row_len(a, bb);
+                const int L = b0 == 0 ? len0 : row_len(a, bb);
                 const int busy = c > 0 ? min((L + c - 1) / c, a.S) : 0;
                 cnt = pass == 0 ? busy : a.S - busy;
             }
