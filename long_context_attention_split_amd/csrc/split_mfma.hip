@@ -6,22 +6,21 @@
 // V_tile^T . P^T.  Each wave serves all the columns of one KV head, and the waves of
 // a work-group share one (b, chunk) -- 4 waves on one KV head, or 3 (d = 128) or 4
 // (d = 64) waves on each of 4 adjacent KV heads -- so every K and V byte of the chunk
-// is read from HBM once
-// however many heads and tokens share it.  Each column masks the keys past its
-// token's position.  The per-head partials (m, l, o) it writes are the same as the
-// vector-ALU kernel's (see split_valu.hip): chunk
-// maximum in base 2, sum of 2^(s - m), and the 2^(s - m)-weighted sum of value
-// rows, i.e. the per-chunk local max, denominator and numerator of tree_attn_decode
-// ("Tree Attention Decoding").
+// is read from HBM once however many heads and tokens share it.  Each column masks
+// the keys past its token's position.  The per-head partials (m, l, o) it writes are
+// the same as the vector-ALU kernel's (see split_valu.hip): chunk maximum in base 2,
+// sum of 2^(s - m), and the 2^(s - m)-weighted sum of value rows, i.e. the per-chunk
+// local max, denominator and numerator of tree_attn_decode ("Tree Attention
+// Decoding").
 //
-// Data path: each wave streams 16-key tiles of K and V straight from HBM into its
-// own LDS buffers with buffer_load_dwordx4 ... lds (non-temporal).  Every load
-// instruction covers whole consecutive rows -- the pattern that streams at full HBM
-// rate -- and the 16 lanes of a row fetch its 16-byte chunks in an XOR-swizzled
-// order, so that the matrix-core operand reads from LDS (16 rows, one chunk each)
-// hit 16 distinct bank groups.  A wave reads a landed tile's operands into registers,
-// issues the next tile's loads into the same buffer, and then computes, so the
-// next tile is in flight while the current one is consumed.
+// Data path: each wave streams tiles of K and V (16 keys for bf16, 32 keys for FP8:
+// 8 KiB at d = 128 either way) straight from HBM into its own LDS buffers with
+// buffer_load_dwordx4 ... lds.  Every load instruction covers whole consecutive rows
+// -- the pattern that streams at full HBM rate -- and the lanes of a row fetch its
+// 16-byte chunks in an XOR-swizzled order, so that the matrix-core operand reads
+// from LDS hit distinct bank groups.  A wave reads a landed tile's operands into
+// registers, issues the next tile's loads into the same buffer, and then computes,
+// so the next tile is in flight while the current one is consumed.
 //
 // Matrix instructions: v_mfma_f32_16x16x32_bf16 (lane l: A[i][k] with i = l%16,
 // B[k][j] with j = l%16, k in the 8-wide block l/16; C[i][j] with j = l%16,
@@ -29,18 +28,23 @@
 // reduction index only has to be laid out the same way in A and B.
 //  * scores: A = 16 keys x 32 dims of K from LDS, B = Q^T with heads on the 16
 //    columns (zero past g).  fp32 q is split into bf16 hi + lo and both are
-//    multiplied (two MFMAs), keeping ~16 significant bits of q; K is exactly bf16.
-//    Lane l gets the scores of keys 4(l/16)+r for head l%16.
-//  * value update (16x16x16): A = V^T (16 value columns x the tile's 16 keys),
+//    multiplied (two MFMAs), keeping ~16 significant bits of q; K is exactly bf16
+//    (FP8 K is widened to bf16 in registers, exactly).  Lane l gets the scores of
+//    keys 4(l/16)+r of each 16-key block for head l%16.
+//  * value update, bf16 (16x16x16): A = V^T (16 value columns x the tile's 16 keys),
 //    B = P^T (16 keys x heads), the probabilities split into bf16 hi + lo.  The V^T
 //    operand comes straight from the row-major V tile in LDS through gfx950's
 //    transposing LDS read (ds_read_b64_tr_b16), one read per 16 value columns.
+//  * value update, FP8 (16x16x32 over the 32-key tile): V^T comes from the FP8 tile
+//    through the 8-bit transposing read (ds_read_b64_tr_b8), addressed so that each
+//    lane's 8 reduction slots are the 8 keys whose probabilities it already holds;
+//    it is widened to bf16 in registers.
 //
-// Softmax per head: lane l owns head l%16 and 4 of the tile's 16 keys; the lanes
-// l, l^16, l^32, l^48 exchange their max and sum.  The running (m, l) and the
-// rescale of O by 2^(m_old - m_new) follow the online softmax of the "Flash
-// Aandacht" page's block loop, kept un-normalised; the rescale is skipped when no
-// head's maximum moved (the factor is then exactly 1).
+// Softmax per head: lane l owns head l%16 and 4 keys of each 16-key block; the lanes
+// l, l^16, l^32, l^48 exchange their max and sum (row swaps, no LDS).  The running
+// (m, l) and the rescale of O follow the online softmax of the "Flash Aandacht"
+// page's block loop, kept un-normalised, with the reference maximum moved only when
+// a column's maximum passes it by more than 2^8 (see below).
 
 #include <type_traits>
 
