@@ -205,14 +205,20 @@ def test_fp8_ragged_gqa_alibi(lib, kv):
 @pytest.mark.parametrize("kv", FP8)
 @pytest.mark.parametrize("B,Hq,Hkv,d,nq,S", [
     (2, 8, 2, 128, 1, 5),        # 4 heads per KV head, one KV head per work-group
-    (2, 32, 8, 128, 1, 3),       # 4 KV heads per work-group (fused: small grid)
-    (3, 32, 8, 128, 1, 16),      # 4 KV heads per work-group, split + combine
+    (2, 32, 8, 128, 1, 3),       # 4 KV heads per work-group, small grid
+    (3, 32, 8, 128, 1, 16),      # 4 KV heads per work-group, many chunks
     (2, 16, 4, 64, 1, 7),        # d 64
     (2, 8, 8, 128, 2, 6),        # several tokens, 4 KV heads per work-group
+    (3, 16, 4, 128, 3, 9),       # 4 heads x 3 tokens = 12 columns
+    (2, 4, 4, 128, 16, 4),       # 16 tokens fill the 16 columns
+    (3, 8, 4, 64, 4, 5),         # d 64, 2 heads x 4 tokens
+    (2, 4, 2, 64, 3, 11),        # d 64, one KV head per work-group, several tokens
 ])
 def test_fp8_matrix_core_path(lib, kv, B, Hq, Hkv, d, nq, S):
-    """FP8 K/V with query-head groups or several tokens take the matrix-core kernel: FP8
-    tiles widened to bf16 in LDS, K scale folded into q, V scale into the partials."""
+    """FP8 K/V with query-head groups or several tokens take the matrix-core kernel:
+    32-key FP8 tiles, K operands and V^T (8-bit transposing read) widened to bf16 in
+    registers, K scale folded into q, V scale into the partials.  Lengths include 1
+    (shorter than the tokens: columns with no visible key) and ALiBi is on."""
     note("fp8 mfma kv=%s B=%d Hq=%d Hkv=%d d=%d nq=%d S=%d" % (kv, B, Hq, Hkv, d, nq, S))
     lens = [1700, 1, 999][:B]
     c = W.random_case(330 + Hkv + d + nq, B, Hq, Hkv, 1700, d, kv_dtype=kv, seq_lens=lens, alibi=True,
