@@ -132,6 +132,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for HBM byte counters)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB of scratch between steps, outside the timed "
+                         "region, so that no K/V stays in L2 or the 256 MB memory-side cache; "
+                         "each step is then timed with events (default 0: steps back to back)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -170,7 +174,12 @@ def main(argv=None) -> int:
     ks = c["k_scale"].to(dev) if c["k_scale"] is not None else None
     vs = c["v_scale"].to(dev) if c["v_scale"] is not None else None
     B, Hq, Hkv, Lmax, d = tad.shape_of(c["q"], c["k"])
-    S = args.splits if args.splits > 0 else (c["n_splits"] if c["n_splits"] > 0 else tad.tad_auto_splits(B, Hkv, Lmax))
+    if args.splits > 0:
+        S = args.splits
+    elif c["n_splits"] > 0:
+        S = c["n_splits"]
+    else:                                  # what tad_decode_ws picks
+        S = tad.tad_auto_splits(B, Hkv, Lmax)
     ws = tad.workspace(q, c["k"], S)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     kv_bytes = w.kv_bytes(c["seq_lens"])
@@ -193,14 +202,27 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.flush_mib:
+        # flushed steps: each step bracketed by its own events, a scratch write between
+        scratch = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            scratch.fill_(float(i))
+            step(evs[i])
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = sum(evs[i][0].elapsed_time(ends[i]) for i in range(args.steps)) / args.steps
+        del scratch
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
     split_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    ms_per_step = wall * 1e3 / args.steps
     split_avg = sum(split_ms) / len(split_ms)
     # outside the split brackets: the combine kernel and launch gaps
     comb_avg = ms_per_step - split_avg
@@ -231,6 +253,8 @@ def main(argv=None) -> int:
         "config": {
             "workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax,
             "n_splits": S, "kv_bytes_per_step": kv_bytes,
+            "timing": ("per-step events, %d MiB scratch written between steps" % args.flush_mib
+                       if args.flush_mib else "steps back to back, wall clock"),
             "kv_layout": ("paged, %d-row pages%s" % (args.page_size, ", head-major" if args.head_major_pages else ""))
                          if args.page_size else ("contiguous [B, L, H, d]" if args.token_major
                                                  else "contiguous [B, H, L, d]"),

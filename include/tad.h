@@ -42,13 +42,18 @@
  *    to [0, Lmax] on the device; keys at or beyond L_b are never read.  A row with
  *    L_b = 0 produces out = 0 (so does a token whose position is before the first key).
  *  - alibi_slopes: DEVICE fp32 [Hq] or NULL (no bias).
- *  - n_splits: chunks per (b, head); <= 0 selects tad_auto_splits().  Every row is
- *    cut into contiguous chunks of one length c = ceil(Lref / n_splits), where Lref
- *    is the longest (clamped) sequence length in the batch (Lmax without seq_lens):
- *    torch.chunk(n_splits) when all rows have the same length.  The last chunk of a
- *    row may be shorter; shorter rows end with empty chunks, which contribute
- *    nothing.  (The result does not depend on the chunking; with one chunk length
- *    every non-empty work-group of a ragged batch has the same amount of work.)
+ *  - n_splits: chunks per (b, head); <= 0 selects tad_auto_splits().  Every row
+ *    is cut into contiguous chunks of one length c = ceil(Lref / n_splits), where
+ *    Lref is the longest (clamped) sequence length in the batch (Lmax without
+ *    seq_lens): torch.chunk(n_splits) when all rows have the same length.  The last
+ *    chunk of a row may be shorter; shorter rows end with empty chunks, which
+ *    contribute nothing.  The matrix-core kernel (query-head groups or several
+ *    tokens, bf16 or FP8 K/V, d 64 or 128) lengthens c when the batch's non-empty
+ *    chunks would need more work-groups than the device runs at once, to the shortest
+ *    length that fits (decided on the device from the row lengths); for it n_splits
+ *    is the finest chunking.  (The result does not depend on the chunking; with one
+ *    chunk length every non-empty work-group of a ragged batch has the same amount
+ *    of work.)
  *  - stream: HIP stream (0 = default stream).  All tensors are owned by the caller
  *    and must stay valid until the stream work completes.  The library never frees
  *    caller memory and keeps no state besides a per-device compute-unit count.
@@ -68,7 +73,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10300 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10400 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };

@@ -164,8 +164,8 @@ void split_mfma_kernel(SplitArgs a) {
     // Work-group -> (row b, KV-head group, chunk s): every non-empty chunk of the batch
     // first, so that a ragged batch's busy work-groups are dispatched together and
     // spread over the XCDs in turn (work-group i runs on XCD i mod 8).
-    const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, used thrice
-    const int c = batch_chunk_len(a, len0);
+    const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
+    const int c = fit_chunk_len(a, a.Hkv / HG, batch_chunk_len(a, len0), len0, a.wg_slots);
     const WorkItem wi = busy_first_item(a, a.Hkv / HG, (int)blockIdx.x, c, len0);
     const int b = wi.b, s = wi.s;
     const int kvh0 = wi.g * HG;                            // first KV head of the work-group
@@ -244,11 +244,8 @@ void split_mfma_kernel(SplitArgs a) {
         const char *p = (const char *)(tv + tr8_row * CH + (nb ^ swz(tr8_row))) + 8 * (j16 & 1);
         return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t *)p));
     };
-    // HBM -> LDS, whole rows per instruction; rows past the chunk end read as zero.
-    // K is read non-temporal.  V too for bf16; FP8 V tiles use the default policy,
-    // which measured faster when part of the chip idles (ragged FP8 grouped-query
-    // decode: 49.3 -> 46.8 us) and made no difference or was slower elsewhere.
-    constexpr int VPOL = F8 ? kPolicyDefault : kPolicyNT;
+    // HBM -> LDS, whole rows per instruction, non-temporal; rows past the chunk end
+    // read as zero.
     auto issue_tile = [&](uint4 *tk, int t0) {
         uint4 *tv = tk + TILE;
 #pragma unroll
@@ -270,7 +267,7 @@ void split_mfma_kernel(SplitArgs a) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(tk + u * 64), 16,
                                                          (uint32_t)(tb + r) * krow + col, 0, 0, kPolicyNT);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(tv + u * 64), 16,
-                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, VPOL);
+                                                         (uint32_t)(tb + r) * vrow + col, 0, 0, kPolicyNT);
             }
         }
         if constexpr (PAGED) ++ktile;
@@ -514,27 +511,37 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
 // heads' waves read each key's adjacent rows together.  Ragged grouped-query
 // workload, 8 KV heads, 32768 keys: d = 128 126.6 -> 119.5 us on [B, Hkv, L, d] K/V
 // and 154.5 -> 120.9 us on [B, L, Hkv, d]; d = 64 57.6 -> 54.5 us and 78.8 -> 56.0 us.
+// One launch, with wg_slots = the work-groups of this kernel the device runs at once
+// (its occupancy per CU, queried once, times the CU count).
+template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT>
+static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
+    constexpr int THREADS = 64 * HG * NWH;
+    static const int per_cu = [] {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT>), THREADS,
+                0) != hipSuccess || nb < 1)
+            nb = 1;
+        return nb;
+    }();
+    a.wg_slots = a.cus * per_cu;
+    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT>), dim3((unsigned)grid), dim3(THREADS), 0,
+                       st, a);
+}
+
 template <int D, int KVT>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
     if (split_mfma_grouped_heads(a, D)) {
         constexpr int NWH = WAVES;                         // one work-group fills a CU
         const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
-        if (a.block_table)
-            hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 4, NWH, KVT>), dim3((unsigned)grid),
-                               dim3(64 * 4 * NWH), 0, st, a);
-        else
-            hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 4, NWH, KVT>), dim3((unsigned)grid),
-                               dim3(64 * 4 * NWH), 0, st, a);
+        if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT>(a, grid, st);
+        else launch_k<D, WAVES, false, 4, NWH, KVT>(a, grid, st);
         return;
     }
     const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
-    if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, true, 1, 4, KVT>), dim3((unsigned)grid), dim3(kSplitThreads),
-                           0, st, a);
-    else
-        hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, false, 1, 4, KVT>), dim3((unsigned)grid), dim3(kSplitThreads),
-                           0, st, a);
+    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT>(a, grid, st);
+    else launch_k<D, WAVES, false, 1, 4, KVT>(a, grid, st);
 }
 
 template <int D>

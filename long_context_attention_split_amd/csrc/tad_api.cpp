@@ -289,6 +289,9 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
     a.skp = P.skp; a.svp = P.svp;
     a.B = (int32_t)P.B; a.Hq = (int32_t)P.Hq; a.Hkv = (int32_t)P.Hkv; a.Lmax = (int32_t)P.Lmax;
     a.S = S; a.group = (int32_t)(P.Hq / P.Hkv);
+    int cus = 0;
+    a.cus = device_cus(-1, &cus) == TAD_OK ? cus : 0;     // 0: the chunk-length fit is skipped
+    a.wg_slots = 0;
     a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
     a.ws_m = w.m; a.ws_l = w.l; a.ws_o = w.o;
     a.fused = out.data != nullptr;

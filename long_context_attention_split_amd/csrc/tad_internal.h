@@ -29,6 +29,8 @@ struct SplitArgs {
     int32_t max_pages, page_size, num_pages;
     int64_t skp, svp;
     int32_t B, Hq, Hkv, Lmax, S, group;
+    int32_t cus;            // compute units of the device
+    int32_t wg_slots;       // matrix-core kernel: work-groups the device runs at once (set by its launcher)
     float qscale;           // d^-1/2 * log2(e): scores come out in base-2 units
     float *ws_m, *ws_l, *ws_o;  // partial arrays (see tad.h)
     // Fused merge: when set, the last work-group to finish a row (counted in cnt)
@@ -91,6 +93,40 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a, int len0) {
 
 __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
     return batch_chunk_len(a, a.seq_lens ? lane_row_len(a, 0) : 0);
+}
+
+// The chunk length for a kernel whose work-groups each serve G (row, chunk) units of
+// work: the finest length the S slots per row allow (c = batch_chunk_len) when its
+// non-empty chunks fit in the `slots` work-groups the device runs at once, else the
+// shortest longer length that fits (when even one chunk per row does not fit, one
+// chunk per row).  Chunks then never wait for a second round of work-groups, and a
+// ragged batch still spreads over the whole device.  Wave-uniform.
+__device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, int len0, int slots) {
+    if (c <= 0 || slots <= 0) return c;
+    int Lref = 0;
+    auto busy_of = [&](int cc) {                 // G * sum_b ceil(L_b / cc)
+        int n = 0, mx = 0;
+        for (int b0 = 0; b0 < a.B; b0 += 64) {
+            const int L = b0 == 0 ? len0 : lane_row_len(a, b0);
+            n += (L + cc - 1) / cc;
+            mx = max(mx, L);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            n += __shfl_xor(n, off, 64);
+            mx = max(mx, __shfl_xor(mx, off, 64));
+        }
+        Lref = __builtin_amdgcn_readfirstlane(mx);
+        return __builtin_amdgcn_readfirstlane(n) * G;
+    };
+    int busy = busy_of(c);
+    for (int it = 0; it < 16 && busy > slots && c < Lref; ++it) {
+        int cn = (int)(((int64_t)c * busy + slots - 1) / slots);   // busy scales about as 1/c
+        if (a.block_table) cn = (cn + a.page_size - 1) / a.page_size * a.page_size;
+        c = max(min(cn, Lref), c + 1);
+        busy = busy_of(c);
+    }
+    return c;
 }
 
 __device__ __forceinline__ ChunkRange chunk_range_c(const SplitArgs &a, int b, int s, int c) {
