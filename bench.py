@@ -198,13 +198,15 @@ def main(argv=None) -> int:
             ev[1].record(stream)
         tad.tad_combine(ws, B, Hq, 1, S, d, out, stream)
 
-    for _ in range(args.warmup):
+    scratch = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) if args.flush_mib else None
+    for i in range(args.warmup):
+        if scratch is not None:
+            scratch.fill_(-1.0 - i)
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     if args.flush_mib:
         # flushed steps: each step bracketed by its own events, a scratch write between
-        scratch = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
@@ -213,7 +215,6 @@ def main(argv=None) -> int:
             ends[i].record(stream)
         torch.cuda.synchronize()
         ms_per_step = sum(evs[i][0].elapsed_time(ends[i]) for i in range(args.steps)) / args.steps
-        del scratch
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -222,6 +223,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_per_step = wall * 1e3 / args.steps
+    del scratch
     split_ms = [e[0].elapsed_time(e[1]) for e in evs]
     split_avg = sum(split_ms) / len(split_ms)
     # outside the split brackets: the combine kernel and launch gaps
