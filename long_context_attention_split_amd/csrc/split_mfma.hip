@@ -175,10 +175,7 @@ void split_mfma_kernel(SplitArgs a) {
     const int tok = head_ok ? j16 % nq : 0;
     const int h = kvh * g + (head_ok ? j16 / nq : 0);
 
-    ChunkRange cr;
-    cr.L = b < 64 ? __builtin_amdgcn_readlane(len0, b) : row_len(a, b);
-    cr.j0 = (int)min((int64_t)s * c, (int64_t)cr.L);
-    cr.j1 = min(cr.j0 + c, cr.L);
+    const ChunkRange cr = chunk_of(b < 64 ? __builtin_amdgcn_readlane(len0, b) : row_len(a, b), s, c);
     const int j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
     // An empty chunk writes the merge identity (m = -inf, l = 0, o = 0) and leaves.
@@ -207,7 +204,6 @@ void split_mfma_kernel(SplitArgs a) {
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
     TilePages pages[NSB];                                  // paged: pages of the tiles' 16-row pieces
     int ktile = 0;                                         // paged: tiles issued so far
-
 
     // LDS slot (row r, position p) holds chunk p ^ swz(r) of row r.  Within a 16-row
     // score block the 16 rows of an operand read land in distinct 16-byte bank groups

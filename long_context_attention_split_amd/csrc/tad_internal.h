@@ -129,16 +129,17 @@ __device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, i
     return c;
 }
 
-__device__ __forceinline__ ChunkRange chunk_range_c(const SplitArgs &a, int b, int s, int c) {
+// Chunk s of a row of L keys cut with chunk length c.
+__device__ __forceinline__ ChunkRange chunk_of(int L, int s, int c) {
     ChunkRange r;
-    r.L = row_len(a, b);
-    r.j0 = (int)min((int64_t)s * c, (int64_t)r.L);
-    r.j1 = min(r.j0 + c, r.L);
+    r.L = L;
+    r.j0 = (int)min((int64_t)s * c, (int64_t)L);
+    r.j1 = min(r.j0 + c, L);
     return r;
 }
 
 __device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int s) {
-    return chunk_range_c(a, b, s, batch_chunk_len(a));
+    return chunk_of(row_len(a, b), s, batch_chunk_len(a));
 }
 
 // Work-group k of a grid of B * G * S, G work-groups per (row, chunk): the (row b,
