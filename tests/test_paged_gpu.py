@@ -61,6 +61,8 @@ def oracle_of(c):
     (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 12),       # FP8 E5M2 GQA, 4 KV heads, split + combine
     (2, 32, 8, 1100, 64, 16, torch.bfloat16, 6),           # d 64 GQA, 4 KV heads per work-group
     (3, 16, 8, 1000, 64, 32, torch.float8_e4m3fn, 11),     # d 64 FP8 GQA, 4 KV heads, split + combine
+    (2, 16, 4, 900, 64, 16, torch.float8_e5m2, 7),         # d 64 FP8: 32-key tiles over two 16-row pages
+    (2, 8, 2, 777, 128, 16, torch.float8_e4m3fn, 9),       # FP8, one KV head per work-group, 16-row pages
 ])
 def test_paged_matches_oracle(lib, B, Hq, Hkv, L, d, ps, kv, S):
     """Ragged lengths (one not a page multiple) over a permuted page pool."""
@@ -71,16 +73,17 @@ def test_paged_matches_oracle(lib, B, Hq, Hkv, L, d, ps, kv, S):
     assert_parity(run_paged(lib, c, S), ref, kv, vmax_real(c), "paged")
 
 
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
 @pytest.mark.parametrize("nq,Hkv", [(3, 2), (16, 8), (5, 4)])
-def test_paged_several_tokens_alibi(lib, nq, Hkv):
+def test_paged_several_tokens_alibi(lib, nq, Hkv, kv):
     """Several query tokens (causal among themselves) and ALiBi over a paged cache."""
-    note("paged tokens nq=%d Hkv=%d" % (nq, Hkv))
-    c = paged_case(650 + nq, 2, 8, Hkv, 800, 128, 16, lens=[800, 333], alibi=True, nq=nq)
+    note("paged tokens nq=%d Hkv=%d kv=%s" % (nq, Hkv, kv))
+    c = paged_case(650 + nq, 2, 8, Hkv, 800, 128, 16, kv, lens=[800, 333], alibi=True, nq=nq)
     ref = oracle_of(c)
     for S in (2, 9):
         out = run_paged(lib, c, S)
         assert out.shape == (2, 8, nq, 128)
-        assert_parity(out, ref, torch.bfloat16, vmax_real(c), "paged tokens S=%d" % S)
+        assert_parity(out, ref, kv, vmax_real(c), "paged tokens S=%d" % S)
 
 
 @pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
