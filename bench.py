@@ -116,6 +116,43 @@ def copy_probe(dev, nbytes: int = 1 << 30, reps: int = 5):
             "rw_gbs": round(2 * nbytes / dt / 1e9, 1)}
 
 
+def read_stream_probe(k, v, stream, reps: int = 10):
+    """GB/s of a plain read stream over the K and V allocations (libtad_probe.so, built
+    beside libtad.so), timed with events on `stream`; None when the probe library is
+    missing."""
+    import ctypes
+    import torch
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_attention_split_amd",
+                        "libtad_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.tad_probe_read_stream.restype = ctypes.c_int
+    lib.tad_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(4096, dtype=torch.int32, device=k.device)
+    bufs = []
+    for t in (k, v):
+        base = t if t.is_contiguous() else t.transpose(1, 2)   # [B, L, H, d] storage seen through strides
+        if not base.is_contiguous():
+            return None
+        bufs.append((base.data_ptr(), base.numel() * base.element_size()))
+
+    def run():
+        for ptr, nbytes in bufs:
+            if lib.tad_probe_read_stream(ptr, nbytes, sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("read-stream probe launch failed")
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total = sum(nb for _, nb in bufs) * reps
+    return total / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +311,13 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    probe_gbs = read_stream_probe(k, v, stream)
+    if probe_gbs:
+        # a second denominator: what a plain read stream over the same K and V buffers
+        # achieves on this device in this run
+        result["read_probe"] = {"gbs": round(probe_gbs, 1), "frac_of_peak": round(probe_gbs / HBM_PEAK_GBS, 4),
+                                "kernel": "16-byte non-temporal loads, 1 KiB per load instruction, all CUs"}
+        result["roofline"]["frac_of_read_probe"] = round(split_gbs / probe_gbs, 4)
 
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()

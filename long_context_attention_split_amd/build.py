@@ -18,8 +18,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtad.so")
+# A plain HBM read stream that bench.py measures beside the split kernel; a
+# measurement aid kept out of the decode library.
+PROBE_LIB = os.path.join(HERE, "libtad_probe.so")
 
 SOURCES = ["tad_api.cpp", "split_valu.hip", "split_mfma.hip", "split_heads.hip", "combine.hip"]
+PROBE_SOURCES = ["stream_probe.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -48,8 +52,12 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(PROBE_SOURCES))) as ex:
         objs = list(ex.map(_compile, srcs))
+        probe_objs = list(ex.map(_compile, PROBE_SOURCES))
+    ptmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", ptmp] + probe_objs)
+    os.replace(ptmp, PROBE_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.check_call(cmd)
@@ -63,7 +71,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("kernel launch stubs left undefined by the host pass:\n  " + "\n  ".join(stubs))
     os.replace(tmp, LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -1,0 +1,52 @@
+// stream_probe.hip -- a plain HBM read stream, the measured ceiling the split kernels'
+// K/V streams are compared with (a measurement aid; not part of the decode library).
+//
+// Every work-group reads one contiguous slice of the buffer with 16-byte
+// non-temporal buffer loads, 4 waves x 8 loads in flight per wave, each load
+// instruction covering 1 KiB of consecutive bytes -- the access pattern of the split
+// kernels' K and V rows -- and folds the data into one word it writes to `sink`, so
+// that no load can be dropped.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+constexpr uint32_t kStep = kThreads * 16 * kUnroll;   // bytes per work-group iteration
+
+__global__ __launch_bounds__(kThreads) void stream_probe_kernel(const char *base, uint64_t slice,
+                                                                  uint64_t bytes, uint32_t *sink) {
+    const uint64_t start = (uint64_t)blockIdx.x * slice;
+    const uint64_t len = start < bytes ? (bytes - start < slice ? bytes - start : slice) : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base + start), (short)0, (int)len, 0x00020000);
+    const uint32_t lane_off = threadIdx.x * 16u;
+    uint32_t acc = 0;
+    for (uint32_t off = 0; off < (uint32_t)len; off += kStep) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  r, (int)(off + (uint32_t)u * kThreads * 16u + lane_off), 0, 2));
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;   // practically never taken; keeps the loads
+}
+
+}  // namespace
+
+// Read `bytes` bytes at `src` (device memory, 16-byte aligned) once, as fast as the
+// pattern above allows, on `stream`.  `sink`: device uint32 [4096], written at most.
+// Returns 0, or a hipError_t value if the launch failed.
+extern "C" int tad_probe_read_stream(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream) {
+    const int groups = 4096;                           // 16 per CU: every CU streams
+    uint64_t slice = (bytes + groups - 1) / groups;
+    slice = (slice + kStep - 1) / kStep * kStep;       // whole iterations per work-group
+    if (slice > 0x7fffffffull) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_probe_kernel, dim3(groups), dim3(kThreads), 0, stream, (const char *)src, slice, bytes,
+                       sink);
+    return (int)hipGetLastError();
+}
