@@ -30,7 +30,8 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtad.so")
+# TAD_LIB_PATH names another build of the same library (a host-sanitized one, say).
+LIB_PATH = os.environ.get("TAD_LIB_PATH") or os.path.join(_HERE, "libtad.so")
 
 TAD_F32, TAD_BF16, TAD_FP8_E4M3, TAD_FP8_E5M2 = 0, 1, 2, 3
 TAD_OK, TAD_EINVAL, TAD_EDTYPE, TAD_ELAYOUT, TAD_EUNSUPPORTED, TAD_EWORKSPACE, TAD_EHIP = 0, -1, -2, -3, -4, -5, -6

@@ -26,7 +26,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "decode_f64.c")
-_LIB = os.path.join(_HERE, "liboracle_f64.so")
+# ORACLE_LIB_PATH names another build of decode_f64.c (a host-sanitized one, say).
+_OVERRIDE = os.environ.get("ORACLE_LIB_PATH")
+_BUILT = os.path.join(_HERE, "liboracle_f64.so")
+_LIB = _OVERRIDE or _BUILT
 _lib = None
 
 F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
@@ -34,18 +37,18 @@ F32, BF16, FP8_E4M3, FP8_E5M2 = 0, 1, 2, 3
 
 def build(force: bool = True) -> str:
     """Compile decode_f64.c with gcc into liboracle_f64.so (host code only)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    if force or not os.path.exists(_BUILT) or os.path.getmtime(_BUILT) < os.path.getmtime(_SRC):
+        tmp = _BUILT + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
                                "-pthread", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _BUILT)
+    return _BUILT
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
