@@ -132,6 +132,38 @@ def test_grouped_query_heads(lib, g):
     run_case(lib, 150 + g, 2, 4 * g, 4, 1500, 128, seq_lens=[1500, 913], n_splits=6)
 
 
+def _repeat_heads(t, g):
+    """Each KV head repeated g times along dim 1 (byte-wise, so FP8 tensors work too)."""
+    if t is None:
+        return None
+    if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2):
+        return t.view(torch.uint8).repeat_interleave(g, dim=1).contiguous().view(t.dtype)
+    return t.repeat_interleave(g, dim=1).contiguous()
+
+
+@pytest.mark.parametrize("kv,d,nq", [(torch.bfloat16, 128, 1), (torch.bfloat16, 64, 2),
+                                     (torch.float8_e4m3fn, 128, 1)])
+def test_gqa_equals_repeated_kv_mha(lib, kv, d, nq):
+    """Grouped-query decoding equals multi-head decoding with every KV head repeated
+    for its query group (the grouped and the one-head-per-work-group kernels, run on
+    the same numbers)."""
+    g, B, Hq, L = 4, 2, 32, 20000
+    note("gqa vs repeated-kv mha kv=%s d=%d nq=%d" % (kv, d, nq))
+    c = W.random_case(470 + d + nq, B, Hq, Hq // g, L, d, kv_dtype=kv, seq_lens=[L, 13457])
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(471))
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], k_scale=c["k_scale"],
+                            v_scale=c["v_scale"])
+    gqa = gpu_decode(lib, c, 0)
+    mha_case = dict(c, k=_repeat_heads(c["k"], g), v=_repeat_heads(c["v"], g),
+                    k_scale=_repeat_heads(c["k_scale"], g), v_scale=_repeat_heads(c["v_scale"], g))
+    mha = gpu_decode(lib, mha_case, 0)
+    vmax = vmax_real(c)
+    assert_parity(gqa, ref, kv, vmax, "gqa")
+    assert_parity(mha, ref, kv, vmax, "repeated-kv mha")
+    assert np.abs(gqa - mha).max() <= 2e-3 * vmax
+
+
 def test_alibi_bias(lib):
     run_case(lib, 160, 2, 16, 16, 3000, 128, seq_lens=[3000, 1234], alibi=True, n_splits=4)
 
