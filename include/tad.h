@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10400 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10500 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -105,9 +105,11 @@ const char *tad_last_error(void);
 
 /*
  * Chunks per (b, head) chosen when n_splits <= 0, for a batch of B rows with Hkv KV
- * heads and Lmax keys on `device` (-1: the current device): ceil(4 * CUs / (B * Hkv)),
- * i.e. four work-groups per compute unit, all resident at once, but no chunk shorter
- * than 256 keys and at least one.  Returns the count (>= 1) or a negative TAD_E* code.
+ * heads and Lmax keys on `device` (-1: the current device): ceil(4 * CUs / (B * Hkv))
+ * for one row, i.e. four (row, KV head, chunk) units per compute unit, and
+ * ceil(6 * CUs / (B * Hkv)) for several rows, whose lengths may differ (seq_lens), so
+ * that a ragged batch's non-empty chunks still cover the device; no chunk shorter than
+ * 256 keys and at least one.  Returns the count (>= 1) or a negative TAD_E* code.
  */
 int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device);
 

@@ -59,7 +59,7 @@ def build(verbose: bool = False) -> str:
     subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", ptmp] + probe_objs)
     os.replace(ptmp, PROBE_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + objs
     subprocess.check_call(cmd)
     # A kernel template the host pass could not instantiate leaves its launch stub
     # undefined without any diagnostic; such a library would only fail when loaded.

@@ -114,7 +114,30 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// WAVES: occupancy target (waves per SIMD) the register allocator must meet.
+// The merge identity (m = -inf, l = 0, o = 0), written by one wave, for the query
+// columns of an empty item: row wi.b, KV heads wi.g * HG .. + HG - 1, chunk wi.s.
+// Those are the HG * g * nq (head, token) rows R0, R0 + 1, ... of the workspace
+// (at most 64).
+template <int D, int HG>
+__device__ __forceinline__ void wave_identity(const SplitArgs &a, const WorkItem wi) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int rows = HG * a.group * a.nq;
+    const int64_t R0 = ((int64_t)wi.b * a.Hq + (int64_t)wi.g * HG * a.group) * a.nq;
+    for (int i = 0; i < rows; ++i) {
+        float *o = a.ws_o + ((R0 + i) * a.S + wi.s) * D;
+#pragma unroll
+        for (int e = lane; e < D; e += 64) o[e] = 0.f;
+    }
+    if (lane < rows) {
+        const int64_t r = (R0 + lane) * a.S + wi.s;
+        a.ws_m[r] = kNegInf;
+        a.ws_l[r] = 0.f;
+    }
+}
+
+// One work item of the matrix-core split kernel: row wi.b, KV heads wi.g * HG ..
+// + HG - 1, chunk wi.s of the row's Lb keys cut with chunk length c.  smem and lds_ml
+// are the work-group's LDS.
 // PAGED: K/V rows come from a paged cache; each 16-row piece of a tile lies inside one
 // page (page sizes are multiples of 16) and gets its own buffer resources.
 // HG, NWH: a work-group serves HG adjacent KV heads of one chunk with NWH waves each
@@ -128,9 +151,9 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // (ds_read_b64_tr_b8), and both are widened to bf16 in registers (exact: every E4M3
 // and E5M2 value is a bf16 number).  The value product then runs on
 // v_mfma_f32_16x16x32_bf16 over the 32 keys.
-template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16>
-__global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
-void split_mfma_kernel(SplitArgs a) {
+template <int D, bool PAGED, int HG, int NWH, int KVT>
+__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int c, const int Lb,
+                                                uint4 *smem, float (*lds_ml)[HG * NWH][16]) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr bool F8 = KVT != kKvBF16;
     constexpr int ELEM = F8 ? 1 : 2;     // bytes per K/V element
@@ -148,9 +171,6 @@ void split_mfma_kernel(SplitArgs a) {
     static_assert(RPI <= 16 && NLD % NSB == 0, "a load instruction stays inside one 16-row piece of a tile");
     static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
 
-    // Per wave: a (K tile, V tile) pair, reused for the merge.
-    __shared__ uint4 smem[NW * 2 * TILE];
-    __shared__ float lds_ml[3][NW][MAXG];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -161,12 +181,6 @@ void split_mfma_kernel(SplitArgs a) {
     // head kvh*g + j16/nq, token j16%nq; with one token this is one head per column.
     const int S = a.S, g = a.group, nq = a.nq;
     const int gq = g * nq;
-    // Work-group -> (row b, KV-head group, chunk s): every non-empty chunk of the batch
-    // first, so that a ragged batch's busy work-groups are dispatched together and
-    // spread over the XCDs in turn (work-group i runs on XCD i mod 8).
-    const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
-    const int c = fit_chunk_len(a, a.Hkv / HG, batch_chunk_len(a, len0), len0, a.wg_slots);
-    const WorkItem wi = busy_first_item(a, a.Hkv / HG, (int)blockIdx.x, c, len0);
     const int b = wi.b, s = wi.s;
     const int kvh0 = wi.g * HG;                            // first KV head of the work-group
     const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
@@ -175,20 +189,11 @@ void split_mfma_kernel(SplitArgs a) {
     const int tok = head_ok ? j16 % nq : 0;
     const int h = kvh * g + (head_ok ? j16 / nq : 0);
 
-    const ChunkRange cr = chunk_of(b < 64 ? __builtin_amdgcn_readlane(len0, b) : row_len(a, b), s, c);
+    const ChunkRange cr = chunk_of(Lb, s, c);
     const int j0 = cr.j0, j1 = cr.j1;
     const int n = j1 - j0;
-    // An empty chunk writes the merge identity (m = -inf, l = 0, o = 0) and leaves.
-    if (n == 0) {
-        for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
-            const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
-            const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
-            a.ws_o[r * D + e] = 0.f;
-            if (e == 0) {
-                a.ws_m[r] = kNegInf;
-                a.ws_l[r] = 0.f;
-            }
-        }
+    if (n == 0) {                                          // an empty chunk
+        if (wave == 0) wave_identity<D, HG>(a, wi);
         return;
     }
     // keys this column's token sees, and that limit relative to the chunk start
@@ -487,6 +492,52 @@ void split_mfma_kernel(SplitArgs a) {
     }
 }
 
+// Items (row b, KV-head group, chunk s) in busy-first order: every non-empty chunk of
+// the batch first.  Work-group i < busy runs busy item i, so a ragged batch's busy
+// items go to the first work-groups, which the dispatcher spreads over the XCDs in
+// turn (work-group i runs on XCD i mod 8).  Empty item e's merge identity is written by
+// wave slot (busy * NW + e) mod (grid * NW) (slot = work-group * NW + wave): the waves
+// of the work-groups without a busy item first, then, after their busy item, those of
+// the others.  The grid holds at most one work-group per resident slot
+// when the batch's B * G (row, KV-head group) pairs fit in the slots -- the chunk-length
+// fit then leaves at most that many busy items -- and every item otherwise.  Launched
+// as work-groups of their own, empty chunks queued behind the busy ones (one 12-wave
+// work-group fills a CU's LDS) and each paid the prologue again.
+// WAVES: occupancy target (waves per SIMD) the register allocator must meet.
+template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16>
+__global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
+void split_mfma_kernel(SplitArgs a) {
+    constexpr bool F8 = KVT != kKvBF16;
+    constexpr int TILE = (F8 ? 32 : 16) * (D * (F8 ? 1 : 2) / 16);   // 16-byte slots per tile and tensor
+    constexpr int NW = HG * NWH;
+    // Per wave: a (K tile, V tile) pair, reused for the merge.
+    __shared__ uint4 smem[NW * 2 * TILE];
+    __shared__ float lds_ml[3][NW][16];
+
+    const int G = a.Hkv / HG;
+    const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
+    const int c = fit_chunk_len(a, G, batch_chunk_len(a, len0), len0, a.wg_slots);
+    const int busy = busy_items(a, G, c, len0);
+    const int w = (int)blockIdx.x, grid = (int)gridDim.x;
+    if (w < busy) {
+        const WorkItem wi = busy_first_item(a, G, w, c, len0);
+        const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
+        split_mfma_item<D, PAGED, HG, NWH, KVT>(a, wi, c, Lb, smem, lds_ml);
+    }
+    const int empties = a.B * G * a.S - busy;
+    const int slots = grid * NW;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int e0 = ((w * NW + wave - busy * NW) % slots + slots) % slots;
+    if (e0 < empties) {
+        if (a.B <= 64) {
+            const EmptyItems em(a, G, c, len0);
+            for (int e = e0; e < empties; e += slots) wave_identity<D, HG>(a, em.item(e));
+        } else {
+            for (int e = e0; e < empties; e += slots) wave_identity<D, HG>(a, busy_first_item(a, G, busy + e, c, len0));
+        }
+    }
+}
+
 bool split_mfma_supported(int d, int kv_type, int group, int nq) {
     return (kv_type == kKvBF16 || kv_type == kKvE4M3 || kv_type == kKvE5M2) && group * nq >= 2 &&
            group * nq <= 16 && (d == 64 || d == 128);
@@ -507,8 +558,9 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
 // heads' waves read each key's adjacent rows together.  Ragged grouped-query
 // workload, 8 KV heads, 32768 keys: d = 128 126.6 -> 119.5 us on [B, Hkv, L, d] K/V
 // and 154.5 -> 120.9 us on [B, L, Hkv, d]; d = 64 57.6 -> 54.5 us and 78.8 -> 56.0 us.
-// One launch, with wg_slots = the work-groups of this kernel the device runs at once
-// (its occupancy per CU, queried once, times the CU count).
+// One launch.  wg_slots = the work-groups of this kernel the device runs at once (its
+// occupancy per CU, queried once, times the CU count); the grid is capped there when
+// the batch's (row, KV-head group) pairs fit in it.
 template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT>
 static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
     constexpr int THREADS = 64 * HG * NWH;
@@ -521,6 +573,7 @@ static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
         return nb;
     }();
     a.wg_slots = a.cus * per_cu;
+    if (a.wg_slots > 0 && (int64_t)a.B * (a.Hkv / HG) <= a.wg_slots && grid > a.wg_slots) grid = a.wg_slots;
     hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT>), dim3((unsigned)grid), dim3(THREADS), 0,
                        st, a);
 }

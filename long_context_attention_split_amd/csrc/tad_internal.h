@@ -97,10 +97,12 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
 
 // The chunk length for a kernel whose work-groups each serve G (row, chunk) units of
 // work: the finest length the S slots per row allow (c = batch_chunk_len) when its
-// non-empty chunks fit in the `slots` work-groups the device runs at once, else the
-// shortest longer length that fits (when even one chunk per row does not fit, one
-// chunk per row).  Chunks then never wait for a second round of work-groups, and a
-// ragged batch still spreads over the whole device.  Wave-uniform.
+// non-empty chunks fit in the `slots` work-groups the device runs at once, else a
+// longer length that fits, found by a few proportional steps, and failing those one
+// chunk per row (the longest row's length).  Chunks then never wait for a second round
+// of work-groups, and a ragged batch still spreads over the whole device.  With
+// B * G <= slots the busy work-groups G * sum_b ceil(L_b / c) never exceed slots.
+// Wave-uniform.
 __device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, int len0, int slots) {
     if (c <= 0 || slots <= 0) return c;
     int Lref = 0;
@@ -126,6 +128,7 @@ __device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, i
         c = max(min(cn, Lref), c + 1);
         busy = busy_of(c);
     }
+    if (busy > slots) c = Lref;
     return c;
 }
 
@@ -142,11 +145,9 @@ __device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int
     return chunk_of(row_len(a, b), s, batch_chunk_len(a));
 }
 
-// Work-group k of a grid of B * G * S, G work-groups per (row, chunk): the (row b,
-// index g < G, chunk s) it serves, with every non-empty chunk of the batch ahead of
-// every empty one -- row by row, g by g, chunk by chunk among the non-empty ones, then
-// the same among the empty ones.  A ragged batch's busy work-groups are thus all
-// dispatched first (and spread over the XCDs in turn) instead of waiting behind
+// Item k of the B * G * S items (row b, index g < G, chunk s) with chunk length c, in
+// busy-first order: every non-empty chunk of the batch ahead of every empty one -- row
+// by row, g by g, chunk by chunk among the non-empty ones, then the same among the
 // empty ones.  Wave-uniform; must be called by whole waves.
 struct WorkItem {
     int b, g, s;
@@ -161,6 +162,45 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     }
     return x;
 }
+
+// The number of non-empty items, G * sum_b min(ceil(L_b / c), S).  Wave-uniform.
+__device__ __forceinline__ int busy_items(const SplitArgs &a, int G, int c, int len0) {
+    if (c <= 0) return 0;
+    int n = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+        const int L = b0 == 0 ? len0 : lane_row_len(a, b0);
+        n += min((L + c - 1) / c, a.S);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
+    return __builtin_amdgcn_readfirstlane(n) * G;
+}
+
+// The empty items of a batch of at most 64 rows (one row per lane), numbered e = 0, 1,
+// ... in the order busy_first_item gives them after the busy ones.  The per-row counts
+// and their prefix sum are worked out once; item(e) is then one ballot.  Built and used
+// by whole waves.
+struct EmptyItems {
+    int G, S, nb, cnt, incl;   // per lane: non-empty chunks of the row, its empty items, prefix sum
+
+    __device__ __forceinline__ EmptyItems(const SplitArgs &a, int G_, int c, int len0) : G(G_), S(a.S) {
+        const bool row = (int)(threadIdx.x & 63) < a.B;
+        nb = c > 0 ? min((len0 + c - 1) / c, S) : 0;
+        cnt = row ? (S - nb) * G : 0;
+        incl = wave_incl_scan(cnt);
+    }
+    __device__ __forceinline__ WorkItem item(int e) const {
+        const uint64_t hit = __ballot(incl > e);
+        const int r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+        const int ne = S - __builtin_amdgcn_readlane(nb, r);          // empty chunks per index g
+        const int off = e - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(cnt, r));
+        WorkItem w;
+        w.b = r;
+        w.g = off / ne;
+        w.s = S - ne + off % ne;
+        return w;
+    }
+};
 
 __device__ __forceinline__ WorkItem busy_first_item(const SplitArgs &a, int G, int k, int c, int len0) {
     const int lane = (int)(threadIdx.x & 63);

@@ -464,6 +464,47 @@ def test_grouped_split_partials_ragged(lib, kv):
                 np.testing.assert_allclose(o[b, h, s] * fix, num, rtol=2e-3, atol=2e-3 * np.abs(num).max())
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L,d,kv,S", [
+    (1100, 4, 2, 64, 128, torch.bfloat16, 2),      # one KV head per work-group
+    (300, 16, 4, 40, 128, torch.bfloat16, 2),      # 4 KV heads per work-group, d 128
+    (600, 16, 4, 48, 64, torch.float8_e4m3fn, 3),  # 4 KV heads per work-group, d 64, FP8
+])
+def test_more_busy_items_than_work_groups(lib, B, Hq, Hkv, L, d, kv, S):
+    """The matrix-core grid holds at most one work-group per resident slot.  With more
+    (row, KV-head group) pairs than slots even the longest chunk length leaves more
+    busy items than work-groups, and work-groups run several busy items in turn."""
+    g = torch.Generator().manual_seed(B + d)
+    lens = torch.randint(0, L + 1, (B,), generator=g).tolist()
+    lens[0], lens[-1], lens[B // 2] = 0, L, 1
+    run_case(lib, 480 + B + d, B, Hq, Hkv, L, d, kv=kv, seq_lens=lens, n_splits=S)
+
+
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
+def test_empty_items_beyond_the_grid(lib, kv):
+    """Many more chunks than resident work-groups on a ragged batch: the empty chunks
+    are written by work-groups that already ran a busy one.  The workspace starts as
+    NaN, so every (row, head, chunk) partial must be written; the merge matches the
+    oracle."""
+    B, Hq, Hkv, L, d, S = 8, 32, 8, 3000, 128, 96
+    lens = [3000, 17, 0, 1204, 2999, 300, 1, 2048]
+    note("empty items beyond the grid kv=%s S=%d" % (kv, S))
+    c = W.random_case(490, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], k_scale=c["k_scale"],
+                            v_scale=c["v_scale"])
+    gd = to_dev(c)
+    ws = lib.workspace(gd["q"], gd["k"], S)
+    n = B * Hq * S
+    al = lambda x: (x + 255) // 256 * 256
+    mlo = ws[:al(4 * n) * 2 + 4 * n * d].view(torch.float32)
+    mlo.fill_(float("nan"))
+    lib.tad_split(gd["q"], gd["k"], gd["v"], gd["seq_lens"], None, S, ws, None, gd["k_scale"], gd["v_scale"])
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    lib.tad_combine(ws, B, Hq, 1, S, d, out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(mlo).any()
+    assert_parity(out.cpu().numpy(), ref, kv, vmax_real(c), "empty items")
+
+
 def test_empty_chunk_partials(lib):
     """Chunks past the sequence end are the merge identity: m = -inf, l = 0, o = 0."""
     c = to_dev(W.random_case(220, 1, 2, 2, 9, 64))
@@ -503,3 +544,14 @@ def test_dominant_key_and_value_shift(lib):
     shifted = gpu_decode(lib, c, 0)
     assert_parity(shifted, ref2, torch.bfloat16, vmax_valid(c["v"], None), "v+2")
     assert np.abs(shifted.mean() - base.mean() - 2.0) < 1e-2
+
+
+@pytest.mark.parametrize("B,Hkv,Lmax", [(1, 32, 131072), (8, 8, 32768), (4, 16, 65536), (1, 8, 1 << 20),
+                                        (2, 1, 300), (64, 32, 4096), (1, 1, 100)])
+def test_auto_splits_rule(lib, B, Hkv, Lmax):
+    """The documented automatic chunk count: ceil(4 CUs / (B Hkv)) for one row,
+    ceil(6 CUs / (B Hkv)) for several, no chunk under 256 keys, at least 1."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    per_cu = 4 if B == 1 else 6
+    want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax // 256, 4096))
+    assert lib.tad_auto_splits(B, Hkv, Lmax, 0) == want
