@@ -65,6 +65,35 @@ struct ChunkRange {
 };
 
 // Row b's length, clamped to [0, Lmax].
+// Inclusive prefix sum / maximum over the 64 lanes of a wave, in registers (DPP):
+// shifts by 1, 2, 4 and 8 lanes within each 16-lane row, then row_bcast:15 and
+// row_bcast:31 add row 0's total into row 1 and rows 0-1's into rows 2-3.  Lanes
+// before a row's start read as 0, so the maximum needs non-negative values.  One
+// VALU operation per step where shuffles take an LDS round trip each.  Whole waves.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_max(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));
+    return x;
+}
+
+// Sum and maximum (of non-negative values) over a wave, as scalars.
+__device__ __forceinline__ int wave_total(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); }
+__device__ __forceinline__ int wave_top(int x) { return __builtin_amdgcn_readlane(wave_incl_max(x), 63); }
+
 __device__ __forceinline__ int row_len(const SplitArgs &a, int b) {
     return a.seq_lens ? min(max(a.seq_lens[b], 0), a.Lmax) : a.Lmax;
 }
@@ -82,9 +111,7 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a, int len0) {
     if (a.seq_lens) {
         int mx = len0;
         for (int b0 = 64; b0 < a.B; b0 += 64) mx = max(mx, lane_row_len(a, b0));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-        Lref = __builtin_amdgcn_readfirstlane(mx);   // equal in every lane: keep it scalar
+        Lref = wave_top(mx);
     }
     int c = (Lref + a.S - 1) / a.S;
     if (a.block_table) c = (c + a.page_size - 1) / a.page_size * a.page_size;   // whole pages
@@ -113,13 +140,8 @@ __device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, i
             n += (L + cc - 1) / cc;
             mx = max(mx, L);
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            n += __shfl_xor(n, off, 64);
-            mx = max(mx, __shfl_xor(mx, off, 64));
-        }
-        Lref = __builtin_amdgcn_readfirstlane(mx);
-        return __builtin_amdgcn_readfirstlane(n) * G;
+        Lref = wave_top(mx);
+        return wave_total(n) * G;
     };
     int busy = busy_of(c);
     for (int it = 0; it < 16 && busy > slots && c < Lref; ++it) {
@@ -153,16 +175,6 @@ struct WorkItem {
     int b, g, s;
 };
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = (int)(threadIdx.x & 63);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
 // The number of non-empty items, G * sum_b min(ceil(L_b / c), S).  Wave-uniform.
 __device__ __forceinline__ int busy_items(const SplitArgs &a, int G, int c, int len0) {
     if (c <= 0) return 0;
@@ -171,9 +183,7 @@ __device__ __forceinline__ int busy_items(const SplitArgs &a, int G, int c, int 
         const int L = b0 == 0 ? len0 : lane_row_len(a, b0);
         n += min((L + c - 1) / c, a.S);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
-    return __builtin_amdgcn_readfirstlane(n) * G;
+    return wave_total(n) * G;
 }
 
 // The empty items of a batch of at most 64 rows (one row per lane), numbered e = 0, 1,
