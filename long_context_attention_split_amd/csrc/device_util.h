@@ -105,16 +105,34 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Maximum / sum over the 64 lanes of a wave, returned to every lane: an inclusive scan
+// in registers (DPP shifts by 1, 2, 4 and 8 lanes within each 16-lane row, then
+// row_bcast:15 and row_bcast:31 across rows; lanes without a source read the
+// identity), whose total lane 63 holds.  Fixed order, so bit-reproducible.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or(float x, float identity) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
+                                                                 __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
+    x = fmaxf(x, dpp_or<0x111, 0xF>(x, kNegInf));
+    x = fmaxf(x, dpp_or<0x112, 0xF>(x, kNegInf));
+    x = fmaxf(x, dpp_or<0x114, 0xF>(x, kNegInf));
+    x = fmaxf(x, dpp_or<0x118, 0xF>(x, kNegInf));
+    x = fmaxf(x, dpp_or<0x142, 0xA>(x, kNegInf));
+    x = fmaxf(x, dpp_or<0x143, 0xC>(x, kNegInf));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x += dpp_or<0x111, 0xF>(x, 0.f);
+    x += dpp_or<0x112, 0xF>(x, 0.f);
+    x += dpp_or<0x114, 0xF>(x, 0.f);
+    x += dpp_or<0x118, 0xF>(x, 0.f);
+    x += dpp_or<0x142, 0xA>(x, 0.f);
+    x += dpp_or<0x143, 0xC>(x, 0.f);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 __device__ __forceinline__ int wave_max_int(int x) {

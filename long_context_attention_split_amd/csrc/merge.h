@@ -47,16 +47,38 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
     float *w = lds;           // [S] weights
     float *part = lds + S;    // [NC] partial sums
 
+    // One round of loads up front: the first 64 chunks' m and l, and (D <= NC) the first
+    // PF partial outputs each computing thread will weigh -- the loads do not depend on
+    // the weights, so they need not wait for them.
+    constexpr int R = D <= NC ? NC / D : 1;     // thread rows sharing each output element
+    constexpr int PF = 16;
+    const int e = tid % D, rr = tid / D;
+    float pre[PF];
+    if constexpr (D <= NC) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            const int s = rr + i * R;
+            pre[i] = (tid < NC && s < S) ? load_partial<COHERENT>(o + (int64_t)s * D + e) : 0.f;
+        }
+    }
+    const float m0 = lane < S ? load_partial<COHERENT>(m + lane) : kNegInf;
+    const float l0 = lane < S ? load_partial<COHERENT>(l + lane) : 0.f;
+
     // global max: every wave reduces all S (lane-strided, then a butterfly), so every
     // wave holds the same value without a barrier
-    float mx = kNegInf;
-    for (int s = lane; s < S; s += 64) mx = fmaxf(mx, load_partial<COHERENT>(m + s));
+    float mx = m0;
+    for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, load_partial<COHERENT>(m + s));
     mx = wave_max(mx);
     const float Mu = (mx == kNegInf) ? 0.f : mx;
 
     // weights (stored by wave 0) and the denominator (every wave, same order)
     float ls = 0.f;
-    for (int s = lane; s < S; s += 64) {
+    if (lane < S) {
+        const float ws = exp2_fast(m0 - Mu);
+        if (tid < 64) w[lane] = ws;
+        ls = fmaf(ws, l0, ls);
+    }
+    for (int s = lane + 64; s < S; s += 64) {
         const float ws = exp2_fast(load_partial<COHERENT>(m + s) - Mu);
         if (tid < 64) w[s] = ws;
         ls = fmaf(ws, load_partial<COHERENT>(l + s), ls);
@@ -66,12 +88,15 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
     __syncthreads();
 
     if constexpr (D <= NC) {
-        constexpr int R = NC / D;              // thread rows sharing each output element
         if (tid < NC) {
-            const int e = tid % D, rr = tid / D;
             float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                const int s = rr + i * R;
+                if (s < S) acc = fmaf(w[s], pre[i], acc);
+            }
 #pragma unroll 8
-            for (int s = rr; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);
+            for (int s = rr + PF * R; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);
             part[tid] = acc;
         }
         __syncthreads();
