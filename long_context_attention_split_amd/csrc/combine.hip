@@ -1,7 +1,10 @@
 // combine.hip -- merge step of split-KV decoding as its own kernel.
 //
-// One work-group per (b, h, query token) row merges that row's S chunk partials with merge_row
-// (merge.h): a max tree, weights 2^(m_s - M), a fixed-order sum tree, one divide.
+// Work-group (row, g) merges column groups g, g + gridDim.y, ... of one (b, h, query
+// token) row's S chunk partials with merge_row (merge.h): the global max, weights
+// 2^(m_s - M), fixed-order sums, one divide.  The column groups of a row go to
+// separate work-groups, so a row with many chunks (one head cut into hundreds of
+// chunks) is merged by many CUs at once.
 // This is the global max / renormalise / sum / divide sequence that tree_attn_decode
 // ("Tree Attention Decoding") performs with one max all-reduce and two sum
 // all-reduces across machines; here the chunks live in one GPU's memory.  The split
@@ -22,18 +25,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
     const int t = row % a.nq, bh = row / a.nq;
     const int b = bh / a.Hq, h = bh % a.Hq;
     merge_row<D>(a.ws_m + (int64_t)row * S, a.ws_l + (int64_t)row * S, a.ws_o + (int64_t)row * S * D, S,
-                 a.out + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)t * a.sot, lds);
+                 a.out + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)t * a.sot, lds, (int)blockIdx.y,
+                 (int)gridDim.y);
 }
 
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
     if (rows <= 0) return hipSuccess;
+    if (d != 64 && d != 128 && d != 256 && d != 512) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)rows, (unsigned)merge_column_groups(a.S, d));
     switch (d) {
-        case 64: hipLaunchKernelGGL(combine_kernel<64>, dim3((unsigned)rows), dim3(kCombineThreads), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, dim3((unsigned)rows), dim3(kCombineThreads), 0, st, a); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, dim3((unsigned)rows), dim3(kCombineThreads), 0, st, a); break;
-        case 512: hipLaunchKernelGGL(combine_kernel<512>, dim3((unsigned)rows), dim3(kCombineThreads), 0, st, a); break;
-        default: return hipErrorInvalidValue;
+        case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kCombineThreads), 0, st, a); break;
+        case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kCombineThreads), 0, st, a); break;
+        case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(kCombineThreads), 0, st, a); break;
+        default: hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(kCombineThreads), 0, st, a); break;
     }
     return hipGetLastError();
 }

@@ -34,37 +34,59 @@ __device__ __forceinline__ void store_partial(float *p, float x) {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Thread rows per output column in the weighted sum over the chunks: row rr of R takes
+// the chunks s = rr, rr + R, ... in order and the R row sums are added in order, so the
+// bits depend on (S, D) only -- whichever kernel merges, however many work-groups share
+// the row's columns.  About 8 chunks per thread row, at least NC / D rows (every
+// thread busy), at most 64.
+__host__ __device__ constexpr int merge_thread_rows(int S, int D) {
+    int r = 1;
+    while (r < 64 && r * 8 < S) r *= 2;
+    const int min_r = kMergeThreads / D;
+    return r > min_r ? r : (min_r > 0 ? min_r : 1);
+}
+
+// Column groups of a row: NC / R columns each.
+__host__ __device__ constexpr int merge_column_groups(int S, int D) {
+    return D / (kMergeThreads / merge_thread_rows(S, D));
+}
+
 // Merge of one row, called by all NT threads of a work-group (NT a multiple of 64, at
-// least kMergeThreads).  The arithmetic runs on the first kMergeThreads threads in a
-// fixed order, so the result does not depend on the work-group size; the others only
-// join the barriers.  `lds` must hold S + kMergeThreads floats.
+// least kMergeThreads): column groups g0, g0 + gstep, ... of the output (all of them
+// with g0 = 0, gstep = 1).  The arithmetic runs on the first kMergeThreads threads in a
+// fixed order, so the result does not depend on the work-group size or on how the
+// column groups are shared out; the other threads only join the barriers.  `lds` must
+// hold S + kMergeThreads floats.
 template <int D, bool COHERENT = false, int NT = kMergeThreads>
 __device__ __forceinline__ void merge_row(const float *m, const float *l, const float *o, int S,
-                                          float *out_row, float *lds) {
+                                          float *out_row, float *lds, int g0 = 0, int gstep = 1) {
     constexpr int NC = kMergeThreads;           // threads that compute
-    static_assert(NT % 64 == 0 && NT >= NC && (D > NC || NC % D == 0), "work-group shape");
+    static_assert(NT % 64 == 0 && NT >= NC && (D & (D - 1)) == 0 && D >= 64, "work-group shape");
     const int tid = threadIdx.x, lane = tid & 63;
     float *w = lds;           // [S] weights
     float *part = lds + S;    // [NC] partial sums
+    const int R = merge_thread_rows(S, D);
+    const int CW = NC / R;                      // columns per group (divides D)
+    const int groups = D / CW;
+    const int cc = tid % CW, rr = tid / CW;     // this thread's column in a group, thread row
 
-    // One round of loads up front: the first 64 chunks' m and l, and (D <= NC) the first
-    // PF partial outputs each computing thread will weigh -- the loads do not depend on
-    // the weights, so they need not wait for them.
-    constexpr int R = D <= NC ? NC / D : 1;     // thread rows sharing each output element
+    // One round of loads up front: the first 64 chunks' m and l, and the first PF
+    // partial outputs of this thread's first column -- they do not depend on the
+    // weights, so they need not wait for them.
     constexpr int PF = 16;
-    const int e = tid % D, rr = tid / D;
     float pre[PF];
-    if constexpr (D <= NC) {
+    {
+        const int col = g0 * CW + cc;
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             const int s = rr + i * R;
-            pre[i] = (tid < NC && s < S) ? load_partial<COHERENT>(o + (int64_t)s * D + e) : 0.f;
+            pre[i] = (tid < NC && g0 < groups && s < S) ? load_partial<COHERENT>(o + (int64_t)s * D + col) : 0.f;
         }
     }
     const float m0 = lane < S ? load_partial<COHERENT>(m + lane) : kNegInf;
     const float l0 = lane < S ? load_partial<COHERENT>(l + lane) : 0.f;
 
-    // global max: every wave reduces all S (lane-strided, then a butterfly), so every
+    // global max: every wave reduces all S (lane-strided, then a wave scan), so every
     // wave holds the same value without a barrier
     float mx = m0;
     for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, load_partial<COHERENT>(m + s));
@@ -87,34 +109,28 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
     const float inv = (ls > 0.f) ? 1.f / ls : 0.f;
     __syncthreads();
 
-    if constexpr (D <= NC) {
+    for (int gi = g0; gi < groups; gi += gstep) {
+        const int col = gi * CW + cc;
         if (tid < NC) {
             float acc = 0.f;
+            int s = rr;
+            if (gi == g0) {
 #pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                const int s = rr + i * R;
-                if (s < S) acc = fmaf(w[s], pre[i], acc);
+                for (int i = 0; i < PF; ++i, s += R)
+                    if (s < S) acc = fmaf(w[s], pre[i], acc);
             }
 #pragma unroll 8
-            for (int s = rr + PF * R; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);
+            for (; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + col), acc);
             part[tid] = acc;
         }
         __syncthreads();
-        if (tid < D) {
+        if (tid < CW) {
             float sum = 0.f;
-#pragma unroll
-            for (int i = 0; i < R; ++i) sum += part[i * D + tid];
-            out_row[tid] = sum * inv;
+            for (int i = 0; i < R; ++i) sum += part[i * CW + tid];
+            out_row[col] = sum * inv;
         }
-    } else if (tid < NC) {
-        for (int e = tid; e < D; e += NC) {
-            float acc = 0.f;
-#pragma unroll 8
-            for (int s = 0; s < S; ++s) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + e), acc);
-            out_row[e] = acc * inv;
-        }
+        __syncthreads();                        // part and (after the last group) lds reusable
     }
-    __syncthreads();                            // lds may be reused after the return
 }
 
 }  // namespace tad
