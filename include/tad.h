@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10500 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10600 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -105,13 +105,16 @@ const char *tad_last_error(void);
 
 /*
  * Chunks per (b, head) chosen when n_splits <= 0, for a batch of B rows with Hkv KV
- * heads and Lmax keys on `device` (-1: the current device): ceil(4 * CUs / (B * Hkv))
- * for one row, i.e. four (row, KV head, chunk) units per compute unit, and
- * ceil(6 * CUs / (B * Hkv)) for several rows, whose lengths may differ (seq_lens), so
- * that a ragged batch's non-empty chunks still cover the device; no chunk shorter than
- * 256 keys and at least one.  Returns the count (>= 1) or a negative TAD_E* code.
+ * heads, Lmax keys, head dimension d and K/V dtype kv_dtype on `device` (-1: the
+ * current device): ceil(4 * CUs / (B * Hkv)) for one row, i.e. four (row, KV head,
+ * chunk) units per compute unit, and ceil(6 * CUs / (B * Hkv)) for several rows,
+ * whose lengths may differ (seq_lens), so that a ragged batch's non-empty chunks
+ * still cover the device; but no chunk under 128 KiB of K and V per KV head
+ * (Lmax * 2 * d * element size / 131072 chunks at most), and at least one.  Returns
+ * the count (>= 1) or a negative TAD_E* code (TAD_EUNSUPPORTED for d, TAD_EDTYPE for
+ * kv_dtype).
  */
-int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device);
+int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t d, int32_t kv_dtype, int32_t device);
 
 /*
  * Bytes of device workspace tad_decode_ws / tad_split / tad_combine need for
@@ -154,7 +157,7 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
 
 /*
  * Split + merge with a caller-provided workspace (no allocation).  Small problems
- * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 1024)
+ * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 8)
  * read by the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d]
  * caches, and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512,
  * more than 16 query rows per KV head) run as ONE launch: each split work-group

@@ -8,7 +8,7 @@ streams.  The functions carry the C names:
 - ``tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits, out, ws, stream=None)``
 - ``tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream=None)``
 - ``tad_combine(ws, B, Hq, nq, n_splits, d, out, stream=None)``
-- ``tad_auto_splits(B, Hkv, Lmax, device=-1)``, ``tad_workspace_bytes(B, Hq, nq, n_splits, d)``
+- ``tad_auto_splits(B, Hkv, Lmax, d, kv_dtype, device=-1)``, ``tad_workspace_bytes(B, Hq, nq, n_splits, d)``
 - ``tad_workspace_clear(ws, stream=None)``, ``tad_version()``, ``tad_last_error()``
 - ``tad_split_paged``, ``tad_decode_paged_ws``, ``tad_decode_paged``: the same with a
   paged K/V cache (k_cache, v_cache [num_pages, page_size, Hkv, d] and an int32
@@ -75,7 +75,7 @@ def load():
     lib.tad_last_error.restype = ctypes.c_char_p
     lib.tad_last_error.argtypes = []
     lib.tad_auto_splits.restype = i32
-    lib.tad_auto_splits.argtypes = [i32, i32, i64, i32]
+    lib.tad_auto_splits.argtypes = [i32, i32, i64, i32, i32, i32]
     lib.tad_workspace_bytes.restype = sz
     lib.tad_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.tad_workspace_clear.restype = ctypes.c_int
@@ -106,20 +106,17 @@ def _torch():
     return torch
 
 
+def dtype_code(dtype) -> int:
+    """TAD_* code of a torch dtype (-1 for one the library does not take)."""
+    torch = _torch()
+    return {torch.float32: TAD_F32, torch.bfloat16: TAD_BF16, torch.float8_e4m3fn: TAD_FP8_E4M3,
+            torch.float8_e5m2: TAD_FP8_E5M2}.get(dtype, -1)
+
+
 def describe(t, scale=None) -> TadTensor:
     """tad_tensor for a torch tensor (no copy; the tensor must outlive the call's work).
     ``scale``: fp32 [B, Hkv] dequantisation scales of an FP8 k or v, or None."""
-    torch = _torch()
-    if t.dtype == torch.float32:
-        dt = TAD_F32
-    elif t.dtype == torch.bfloat16:
-        dt = TAD_BF16
-    elif t.dtype == torch.float8_e4m3fn:
-        dt = TAD_FP8_E4M3
-    elif t.dtype == torch.float8_e5m2:
-        dt = TAD_FP8_E5M2
-    else:
-        dt = -1
+    dt = dtype_code(t.dtype)
     if t.dim() > 4:
         raise ValueError("tensors have at most 4 dims")
     d = TadTensor()
@@ -160,8 +157,10 @@ def tad_last_error() -> str:
     return load().tad_last_error().decode()
 
 
-def tad_auto_splits(B: int, Hkv: int, Lmax: int, device: int = -1) -> int:
-    r = load().tad_auto_splits(B, Hkv, Lmax, device)
+def tad_auto_splits(B: int, Hkv: int, Lmax: int, d: int, kv_dtype, device: int = -1) -> int:
+    """kv_dtype: a TAD_* code or a torch dtype."""
+    code = kv_dtype if isinstance(kv_dtype, int) else dtype_code(kv_dtype)
+    r = load().tad_auto_splits(B, Hkv, Lmax, d, code, device)
     if r < 0:
         _check(r)
     return r
@@ -254,7 +253,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens=None, alibi_slopes=N
     torch = _torch()
     B, Hq, d = q.shape[0], q.shape[1], q.shape[-1]
     Hkv, Lmax = k_cache.shape[2], block_table.shape[1] * k_cache.shape[1]
-    S = n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, q.device.index or 0)
+    S = n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, d, k_cache.dtype, q.device.index or 0)
     nbytes = tad_workspace_bytes(B, Hq, tokens_of(q), S, d)
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -276,7 +275,7 @@ def shape_of(q, k):
 def resolve_splits(q, k, n_splits: int = 0) -> int:
     """n_splits if positive, else the library's automatic choice."""
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
-    return n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, q.device.index or 0)
+    return n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, d, k.dtype, q.device.index or 0)
 
 
 def tokens_of(q) -> int:

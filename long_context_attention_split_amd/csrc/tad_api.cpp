@@ -237,12 +237,19 @@ int device_cus(int32_t device, int *cus) {
 // differ: then part of the chunks are empty, and the matrix-core kernel, which fits
 // the chunk length to the busy ones, gets room to spread a ragged batch over the
 // device (grouped-query decode, 8 rows of 4653..26803 keys, FP8 K/V: 58.0 -> 49.9 us
-// per step; uniform multi-row batches pay about 1% for the longer merge).
-int32_t auto_splits_for(int64_t B, int64_t Hkv, int64_t Lmax, int cus) {
+// per step; uniform multi-row batches pay about 1% for the longer merge).  No chunk
+// holds less than 128 KiB of K and V per KV head (256 keys at d = 128 in bf16, 32 at
+// d = 512 in fp32), since shorter chunks cost work-group start-up and merge time: 32
+// bf16 heads of 1024 keys decode in 13.5 us with 4 chunks (128 KiB) and 15.4 us with
+// 8; one fp32 d = 512 head of 4096 keys in 15.8 us with 128 chunks against ~40 us with
+// the 16 that a fixed 256-key minimum gave.
+constexpr int64_t kMinChunkBytes = 128 << 10;
+
+int32_t auto_splits_for(int64_t B, int64_t Hkv, int64_t Lmax, int64_t key_bytes, int cus) {
     const int64_t units = B * Hkv > 0 ? B * Hkv : 1;
     const int64_t per_cu = B > 1 ? 6 : 4;
     int64_t S = (per_cu * (int64_t)cus + units - 1) / units;
-    const int64_t by_len = Lmax / 256;                 // no chunk shorter than 256 keys
+    const int64_t by_len = Lmax * key_bytes / kMinChunkBytes;
     if (S > by_len) S = by_len;
     if (S > tad::kMaxSplits) S = tad::kMaxSplits;
     if (S < 1) S = 1;
@@ -374,7 +381,7 @@ int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v
     if (n_splits <= 0) {
         int cus = 0;
         if ((rc = device_cus(-1, &cus))) return rc;
-        *S = auto_splits_for(P->B, P->Hkv, P->Lmax, cus);
+        *S = auto_splits_for(P->B, P->Hkv, P->Lmax, 2 * P->d * elem_size(P->kv_dtype), cus);
     } else {
         *S = n_splits;
     }
@@ -448,13 +455,16 @@ int tad_version(void) { return TAD_VERSION; }
 
 const char *tad_last_error(void) { return g_last_error.c_str(); }
 
-int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t device) {
+int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t d, int32_t kv_dtype, int32_t device) {
     if (B < 1 || Hkv < 1 || Lmax < 0) return fail(TAD_EINVAL, "tad_auto_splits: bad sizes");
+    if (d != 64 && d != 128 && d != 256 && d != 512) return fail(TAD_EUNSUPPORTED, "tad_auto_splits: d = %d", d);
+    if (kv_dtype != TAD_F32 && kv_dtype != TAD_BF16 && !is_fp8(kv_dtype))
+        return fail(TAD_EDTYPE, "tad_auto_splits: K/V dtype %d", kv_dtype);
     int cus = 0;
     int rc = device_cus(device, &cus);
     if (rc) return rc;
     ok();
-    return auto_splits_for(B, Hkv, Lmax, cus);
+    return auto_splits_for(B, Hkv, Lmax, 2 * (int64_t)d * elem_size(kv_dtype), cus);
 }
 
 size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t nq, int32_t n_splits, int32_t d) {

@@ -330,6 +330,11 @@ hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);
 constexpr int kSplitThreads = 256;
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSplits = 4096;
-constexpr int kMaxFusedSplits = 1024;   // the fused merge keeps S weights in the kernel's LDS
+// Chunk counts up to which small problems merge in the vector kernel's last work-group
+// per row: one work-group merges the whole row there, which beyond a few chunks costs
+// more than the combine kernel's many (one fp32 d = 512 head of 4096 keys: 16 chunks
+// 43 vs 38 us, 64 chunks 55 vs 16 us; 32 bf16 heads of 1024 keys: 4 chunks 13.5 vs
+// 15.8 us, 8 chunks about even).
+constexpr int kMaxFusedSplits = 8;
 
 }  // namespace tad

@@ -294,8 +294,11 @@ def test_auto_splits_without_device_reports_hip_error(lib):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    assert lib.load().tad_auto_splits(1, 32, 131072, -1) == tad.TAD_EHIP
-    assert lib.load().tad_auto_splits(0, 32, 131072, -1) == tad.TAD_EINVAL
+    so = lib.load()
+    assert so.tad_auto_splits(1, 32, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EHIP
+    assert so.tad_auto_splits(0, 32, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EINVAL
+    assert so.tad_auto_splits(1, 32, 131072, 96, tad.TAD_BF16, -1) == tad.TAD_EUNSUPPORTED
+    assert so.tad_auto_splits(1, 32, 131072, 128, 7, -1) == tad.TAD_EDTYPE
 
 
 def test_product_does_not_reach_the_oracle():

@@ -546,12 +546,17 @@ def test_dominant_key_and_value_shift(lib):
     assert np.abs(shifted.mean() - base.mean() - 2.0) < 1e-2
 
 
-@pytest.mark.parametrize("B,Hkv,Lmax", [(1, 32, 131072), (8, 8, 32768), (4, 16, 65536), (1, 8, 1 << 20),
-                                        (2, 1, 300), (64, 32, 4096), (1, 1, 100)])
-def test_auto_splits_rule(lib, B, Hkv, Lmax):
+@pytest.mark.parametrize("B,Hkv,Lmax,d,kv", [
+    (1, 32, 131072, 128, torch.bfloat16), (8, 8, 32768, 128, torch.bfloat16), (8, 8, 32768, 128, torch.float8_e4m3fn),
+    (4, 16, 65536, 128, torch.bfloat16), (1, 8, 1 << 20, 128, torch.bfloat16), (1, 1, 4096, 512, torch.float32),
+    (2, 1, 300, 64, torch.bfloat16), (64, 32, 4096, 128, torch.bfloat16), (1, 1, 100, 128, torch.float32),
+    (1, 32, 1024, 128, torch.bfloat16), (2, 2, 16384, 128, torch.float8_e5m2)])
+def test_auto_splits_rule(lib, B, Hkv, Lmax, d, kv):
     """The documented automatic chunk count: ceil(4 CUs / (B Hkv)) for one row,
-    ceil(6 CUs / (B Hkv)) for several, no chunk under 256 keys, at least 1."""
+    ceil(6 CUs / (B Hkv)) for several, no chunk under 128 KiB of K and V per KV head,
+    at least 1."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     per_cu = 4 if B == 1 else 6
-    want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax // 256, 4096))
-    assert lib.tad_auto_splits(B, Hkv, Lmax, 0) == want
+    elem = torch.empty((), dtype=kv).element_size()
+    want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax * 2 * d * elem // (128 << 10), 4096))
+    assert lib.tad_auto_splits(B, Hkv, Lmax, d, kv, 0) == want
