@@ -279,6 +279,7 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo,
     // scaled into base-2 units and by the K dequantisation scale of the KV head (FP8).
     const float qs = a.qscale * ((F8 && a.k_scale) ? a.k_scale[b * a.Hkv + kvh] : 1.f);
+    const float vs = (F8 && a.v_scale) ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // applied to this wave's O
     uint4 qhi[NKK], qlo[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -453,13 +454,18 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     else run(std::false_type{});
 
     // ---- merge the NW wave states per head through LDS (reusing the tile buffers).
+    // Each wave's gq columns are rows of D floats in its own MAXG * D slot; with fewer
+    // than 16 columns the rows are padded by 16 bytes, so that the 16-byte stores of
+    // one column-block of a wave (one per column) land in different banks.
     __syncthreads();
-    float(*lds_o)[MAXG][D] = reinterpret_cast<float(*)[MAXG][D]>(smem);
+    const int RS = gq < MAXG ? D + 4 : D;                  // row stride, floats
+    float *const lds_o = reinterpret_cast<float *>(smem);  // [NW][MAXG * D], rows RS apart
     if (head_ok) {
+        float *const orow = lds_o + wave * (MAXG * D) + j16 * RS;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) lds_o[wave][j16][16 * nb + 4 * c4 + r] = O[nb][r];
+            for (int r = 0; r < 4; ++r) orow[16 * nb + 4 * c4 + r] = F8 ? O[nb][r] * vs : O[nb][r];
         if (c4 == 0) {
             lds_ml[0][wave][j16] = m;
             lds_ml[1][wave][j16] = l;
@@ -467,28 +473,33 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
-        const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
-        float M = kNegInf;                   // the exact chunk maximum of the column
+    // Per column (head x, column hh), one thread: the exact chunk maximum M, each wave's
+    // weight 2^(m_w - M) (written over its reference m_w) and the denominator.
+    if (threadIdx.x < HG * gq) {
+        const int x = threadIdx.x / gq, hh = threadIdx.x % gq;
+        float M = kNegInf;
 #pragma unroll
         for (int w = x * NWH; w < x * NWH + NWH; ++w) M = fmaxf(M, lds_ml[2][w][hh]);
         const float Mu = (M == kNegInf) ? 0.f : M;
-        float acc = 0.f, lsum = 0.f;
+        float lsum = 0.f;
 #pragma unroll
         for (int w = x * NWH; w < x * NWH + NWH; ++w) {
             const float sw = exp2_fast(lds_ml[0][w][hh] - Mu);
-            acc = fmaf(sw, lds_o[w][hh][e], acc);
+            lds_ml[0][w][hh] = sw;
             lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
         }
-        if constexpr (F8) {
-            if (a.v_scale) acc *= a.v_scale[b * a.Hkv + kvh0 + x];       // V dequantisation
-        }
         const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;   // hh: column
+        a.ws_m[r] = M;
+        a.ws_l[r] = lsum;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
+        const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = x * NWH; w < x * NWH + NWH; ++w) acc = fmaf(lds_ml[0][w][hh], lds_o[w * (MAXG * D) + hh * RS + e], acc);
+        const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
         a.ws_o[r * D + e] = acc;
-        if (e == 0) {
-            a.ws_m[r] = M;
-            a.ws_l[r] = lsum;
-        }
     }
 }
 
