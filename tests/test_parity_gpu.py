@@ -560,3 +560,33 @@ def test_auto_splits_rule(lib, B, Hkv, Lmax, d, kv):
     elem = torch.empty((), dtype=kv).element_size()
     want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax * 2 * d * elem // (128 << 10), 4096))
     assert lib.tad_auto_splits(B, Hkv, Lmax, d, kv, 0) == want
+
+
+@pytest.mark.parametrize("d,kv,L", [(512, torch.float32, 4096), (256, torch.bfloat16, 6000)])
+@pytest.mark.parametrize("S", [8, 64, 256, 0])
+def test_one_head_many_chunks(lib, d, kv, L, S):
+    """One head cut into many chunks (the automatic count gives a single fp32 d = 512
+    head of 4096 keys 128 of them): the combine spreads the row's columns over
+    work-groups, each column summed by several thread rows; S = 8 merges in the split
+    kernel's last work-group instead."""
+    run_case(lib, 500 + d + S, 1, 1, 1, L, d, kv=kv, n_splits=S)
+
+
+@pytest.mark.parametrize("d", [64, 256, 512])
+def test_fused_merge_equals_combine_wide_heads(lib, d):
+    """The fused merge (small grid, <= 8 chunks) and the combine kernel run the same
+    fixed-order merge, also where a row's columns form several groups: tad_decode_ws
+    equals tad_split + tad_combine bit for bit."""
+    c = to_dev(W.random_case(510 + d, 1, 2, 2, 2500, d, kv_dtype=torch.float32, seq_lens=[1999]))
+    S = 7
+    ws = lib.workspace(c["q"], c["k"], S)
+    a = torch.empty((1, 2, d), dtype=torch.float32, device=DEV)
+    lib.tad_decode_ws(c["q"], c["k"], c["v"], c["seq_lens"], None, S, a, ws)
+    ws2 = lib.workspace(c["q"], c["k"], S)
+    lib.tad_split(c["q"], c["k"], c["v"], c["seq_lens"], None, S, ws2)
+    b = torch.empty_like(a)
+    lib.tad_combine(ws2, 1, 2, 1, S, d, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = oracle.decode_f64(c["q"].cpu(), c["k"].cpu(), c["v"].cpu(), seq_lens=c["seq_lens"].cpu())
+    assert_parity(a.cpu().numpy(), ref, torch.float32, 0.0, "fused d=%d" % d)
