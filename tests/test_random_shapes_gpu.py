@@ -1,0 +1,62 @@
+"""GPU parity on seeded random shapes: batch sizes across 64-row blocks, query-head
+groups from 1 to 16, every head dimension and K/V dtype, ragged lengths with zeros,
+1-3 query tokens, ALiBi, automatic and explicit chunk counts from 1 to 300.  Each
+case goes through tad_decode_ws (whichever kernel and merge form the library picks)
+and is compared with the fp64 oracle under the same bars as the other parity tests.
+"""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from test_parity_gpu import DEV, assert_parity, note, vmax_real
+
+pytestmark = pytest.mark.gpu
+
+KV = [torch.float32, torch.bfloat16, torch.float8_e4m3fn, torch.float8_e5m2]
+
+
+def draw_cases(n, seed=2024):
+    rnd = random.Random(seed)
+    cases = []
+    for i in range(n):
+        d = rnd.choice([64, 128, 128, 256, 512])
+        kv = rnd.choice(KV)
+        Hkv = rnd.choice([1, 2, 3, 4, 8])
+        group = rnd.choice([1, 1, 2, 4, 8, 16])
+        B = rnd.choice([1, 2, 3, 5, 8, 17, 70])
+        nq = rnd.choice([1, 1, 1, 2, 3])
+        L = rnd.choice([1, 7, 63, 300, 1000, 2500, 5000])
+        if B * Hkv * group * L * d > 40_000_000:           # keep the oracle to a second or so
+            L = max(1, 40_000_000 // (B * Hkv * group * d))
+        ragged = B > 1 and rnd.random() < 0.7
+        S = rnd.choice([0, 0, 1, 2, 3, 7, 16, 24, 64, 300])
+        alibi = rnd.random() < 0.3
+        cases.append((i, B, Hkv * group, Hkv, L, d, kv, nq, ragged, S, alibi))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_cases(40), ids=lambda c: "c%d" % c[0])
+def test_random_shape(lib, case):
+    i, B, Hq, Hkv, L, d, kv, nq, ragged, S, alibi = case
+    g = torch.Generator().manual_seed(700 + i)
+    lens = None
+    if ragged:
+        lens = torch.randint(0, L + 1, (B,), generator=g).tolist()
+        lens[0] = L
+        lens[-1] = 0
+    note("random case %d: B=%d Hq=%d Hkv=%d L=%d d=%d kv=%s nq=%d lens=%s S=%d alibi=%s" %
+         (i, B, Hq, Hkv, L, d, kv, nq, "ragged" if ragged else "none", S, alibi))
+    c = W.random_case(800 + i, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi)
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(900 + i))
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
+    gd = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in c.items()}
+    out = lib.decode(gd["q"], gd["k"], gd["v"], gd["seq_lens"], gd["slopes"], S,
+                     k_scale=gd["k_scale"], v_scale=gd["v_scale"])
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), ref, kv, vmax_real(c), "random case %d" % i)
