@@ -1,8 +1,9 @@
 """GPU parity on seeded random shapes: batch sizes across 64-row blocks, query-head
 groups from 1 to 16, every head dimension and K/V dtype, ragged lengths with zeros,
-1-3 query tokens, ALiBi, automatic and explicit chunk counts from 1 to 300.  Each
-case goes through tad_decode_ws (whichever kernel and merge form the library picks)
-and is compared with the fp64 oracle under the same bars as the other parity tests.
+1-3 query tokens, ALiBi, automatic and explicit chunk counts from 1 to 300, on
+contiguous, token-major strided and paged caches.  Each case goes through the
+workspace entry points (whichever kernel and merge form the library picks) and is
+compared with the fp64 oracle under the same bars as the other parity tests.
 """
 import random
 
@@ -60,3 +61,65 @@ def test_random_shape(lib, case):
                      k_scale=gd["k_scale"], v_scale=gd["v_scale"])
     torch.cuda.synchronize()
     assert_parity(out.cpu().numpy(), ref, kv, vmax_real(c), "random case %d" % i)
+
+
+def draw_layout_cases(n, seed=2025):
+    """Random shapes on token-major strided caches ([B, L, Hkv, d] storage seen as
+    [B, Hkv, L, d]) and on paged caches (page sizes 16-128, pages stored token-major or
+    head-major)."""
+    rnd = random.Random(seed)
+    cases = []
+    for i in range(n):
+        layout = rnd.choice(["tokmajor", "paged"])
+        d = rnd.choice([64, 128, 128, 256] + ([512] if layout == "tokmajor" else []))
+        kv = rnd.choice(KV if layout == "tokmajor" else KV[1:])
+        Hkv = rnd.choice([1, 2, 3, 4, 8])
+        group = rnd.choice([1, 1, 2, 4, 8, 16])
+        B = rnd.choice([1, 2, 3, 5, 8, 17, 70])
+        nq = rnd.choice([1, 1, 1, 2, 3])
+        L = rnd.choice([1, 7, 16, 63, 300, 1000, 2500, 5000])
+        if B * Hkv * group * L * d > 40_000_000:
+            L = max(1, 40_000_000 // (B * Hkv * group * d))
+        ragged = B > 1 and rnd.random() < 0.7
+        S = rnd.choice([0, 0, 1, 2, 3, 7, 8, 9, 16, 24, 64, 300])
+        alibi = rnd.random() < 0.3
+        ps = rnd.choice([16, 32, 64, 128])
+        head_major = rnd.random() < 0.5
+        cases.append((i, layout, B, Hkv * group, Hkv, L, d, kv, nq, ragged, S, alibi, ps, head_major))
+    return cases
+
+
+def token_major(t):
+    """The same values stored [B, L, Hkv, d], viewed as [B, Hkv, L, d] (byte-wise for FP8)."""
+    if t.element_size() == 1:
+        return t.view(torch.uint8).transpose(1, 2).contiguous().transpose(1, 2).view(t.dtype)
+    return t.transpose(1, 2).contiguous().transpose(1, 2)
+
+
+@pytest.mark.parametrize("case", draw_layout_cases(30), ids=lambda c: "l%d-%s" % (c[0], c[1]))
+def test_random_layout(lib, case):
+    i, layout, B, Hq, Hkv, L, d, kv, nq, ragged, S, alibi, ps, head_major = case
+    g = torch.Generator().manual_seed(1700 + i)
+    lens = None
+    if ragged:
+        lens = torch.randint(0, L + 1, (B,), generator=g).tolist()
+        lens[0] = L
+        lens[-1] = 0
+    elif layout == "paged":
+        lens = [L] * B                 # without seq_lens a paged row spans all its pages
+    note("random layout case %d: %s B=%d Hq=%d Hkv=%d L=%d d=%d kv=%s nq=%d ragged=%s S=%d alibi=%s ps=%d hm=%s" %
+         (i, layout, B, Hq, Hkv, L, d, kv, nq, ragged, S, alibi, ps, head_major))
+    c = W.random_case(1800 + i, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi)
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(1900 + i))
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
+    dv = lambda x: None if x is None else x.to(DEV)
+    q, sl, sp, ks, vs = dv(c["q"]), dv(c["seq_lens"]), dv(c["slopes"]), dv(c["k_scale"]), dv(c["v_scale"])
+    if layout == "paged":
+        kc, vc, table = W.page_kv(c["k"], c["v"], ps, 1800 + i, head_major=head_major)
+        out = lib.decode_paged(q, dv(kc), dv(vc), dv(table), sl, sp, S, k_scale=ks, v_scale=vs)
+    else:
+        out = lib.decode(q, dv(token_major(c["k"])), dv(token_major(c["v"])), sl, sp, S, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), ref, kv, vmax_real(c), "random layout case %d" % i)
