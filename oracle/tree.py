@@ -15,7 +15,7 @@ function replaced by a chunk index:
    ``exp(local_max - global_max)``;
 5. sum ``den`` and ``num`` over the chunks and divide.
 
-Readings where the gist is silent (each is also listed in the design doc):
+Readings where the gist is silent:
 - an empty chunk (the gist would fail on it) is the identity of the merge:
   local_max = -inf, den = 0, num = 0;
 - an optional additive bias (ALiBi, see ``oracle_alibi_bias`` in decode_f64.c) is
