@@ -267,7 +267,7 @@ def main(argv=None) -> int:
     elif c["n_splits"] > 0:
         S = c["n_splits"]
     else:                                  # what tad_decode_ws picks
-        S = tad.tad_auto_splits(B, Hkv, Lmax, d, w.kv_dtype)
+        S = tad.tad_auto_splits(B, Hq, Hkv, 1, Lmax, d, w.kv_dtype)
     ws = tad.workspace(q, c["k"], S)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     kv_bytes = w.kv_bytes(c["seq_lens"])

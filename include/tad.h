@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10600 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10700 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -104,17 +104,20 @@ int tad_version(void);
 const char *tad_last_error(void);
 
 /*
- * Chunks per (b, head) chosen when n_splits <= 0, for a batch of B rows with Hkv KV
- * heads, Lmax keys, head dimension d and K/V dtype kv_dtype on `device` (-1: the
- * current device): ceil(4 * CUs / (B * Hkv)) for one row, i.e. four (row, KV head,
- * chunk) units per compute unit, and ceil(6 * CUs / (B * Hkv)) for several rows,
- * whose lengths may differ (seq_lens), so that a ragged batch's non-empty chunks
- * still cover the device; but no chunk under 128 KiB of K and V per KV head
- * (Lmax * 2 * d * element size / 131072 chunks at most), and at least one.  Returns
- * the count (>= 1) or a negative TAD_E* code (TAD_EUNSUPPORTED for d, TAD_EDTYPE for
- * kv_dtype).
+ * Chunks per (b, head) chosen when n_splits <= 0, for a batch of B rows with Hq query
+ * heads over Hkv KV heads, nq query tokens, Lmax keys, head dimension d and K/V dtype
+ * kv_dtype on `device` (-1: the current device): ceil(4 * CUs / (B * Hkv)) for one
+ * row, i.e. four (row, KV head, chunk) units per compute unit, and
+ * ceil(6 * CUs / (B * Hkv)) for several rows, whose lengths may differ (seq_lens), so
+ * that a ragged batch's non-empty chunks still cover the device; but no work-group's
+ * chunk under 128 KiB of K and V -- per KV head 128 KiB, or 32 KiB where the
+ * matrix-core kernel serves 4 KV heads per work-group (bf16 or FP8 K/V, d 64 or 128,
+ * 2..16 query rows per KV head, Hkv a multiple of 4) -- and at least one.  Returns the
+ * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
+ * d, TAD_EDTYPE for kv_dtype).
  */
-int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t d, int32_t kv_dtype, int32_t device);
+int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t Lmax, int32_t d, int32_t kv_dtype,
+                        int32_t device);
 
 /*
  * Bytes of device workspace tad_decode_ws / tad_split / tad_combine need for

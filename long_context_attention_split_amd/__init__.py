@@ -8,7 +8,7 @@ streams.  The functions carry the C names:
 - ``tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits, out, ws, stream=None)``
 - ``tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream=None)``
 - ``tad_combine(ws, B, Hq, nq, n_splits, d, out, stream=None)``
-- ``tad_auto_splits(B, Hkv, Lmax, d, kv_dtype, device=-1)``, ``tad_workspace_bytes(B, Hq, nq, n_splits, d)``
+- ``tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, kv_dtype, device=-1)``, ``tad_workspace_bytes(B, Hq, nq, n_splits, d)``
 - ``tad_workspace_clear(ws, stream=None)``, ``tad_version()``, ``tad_last_error()``
 - ``tad_split_paged``, ``tad_decode_paged_ws``, ``tad_decode_paged``: the same with a
   paged K/V cache (k_cache, v_cache [num_pages, page_size, Hkv, d] and an int32
@@ -75,7 +75,7 @@ def load():
     lib.tad_last_error.restype = ctypes.c_char_p
     lib.tad_last_error.argtypes = []
     lib.tad_auto_splits.restype = i32
-    lib.tad_auto_splits.argtypes = [i32, i32, i64, i32, i32, i32]
+    lib.tad_auto_splits.argtypes = [i32, i32, i32, i32, i64, i32, i32, i32]
     lib.tad_workspace_bytes.restype = sz
     lib.tad_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.tad_workspace_clear.restype = ctypes.c_int
@@ -157,10 +157,10 @@ def tad_last_error() -> str:
     return load().tad_last_error().decode()
 
 
-def tad_auto_splits(B: int, Hkv: int, Lmax: int, d: int, kv_dtype, device: int = -1) -> int:
+def tad_auto_splits(B: int, Hq: int, Hkv: int, nq: int, Lmax: int, d: int, kv_dtype, device: int = -1) -> int:
     """kv_dtype: a TAD_* code or a torch dtype."""
     code = kv_dtype if isinstance(kv_dtype, int) else dtype_code(kv_dtype)
-    r = load().tad_auto_splits(B, Hkv, Lmax, d, code, device)
+    r = load().tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, code, device)
     if r < 0:
         _check(r)
     return r
@@ -253,7 +253,8 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens=None, alibi_slopes=N
     torch = _torch()
     B, Hq, d = q.shape[0], q.shape[1], q.shape[-1]
     Hkv, Lmax = k_cache.shape[2], block_table.shape[1] * k_cache.shape[1]
-    S = n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, d, k_cache.dtype, q.device.index or 0)
+    S = n_splits if n_splits > 0 else tad_auto_splits(B, Hq, Hkv, tokens_of(q), Lmax, d, k_cache.dtype,
+                                                      q.device.index or 0)
     nbytes = tad_workspace_bytes(B, Hq, tokens_of(q), S, d)
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -275,7 +276,8 @@ def shape_of(q, k):
 def resolve_splits(q, k, n_splits: int = 0) -> int:
     """n_splits if positive, else the library's automatic choice."""
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
-    return n_splits if n_splits > 0 else tad_auto_splits(B, Hkv, Lmax, d, k.dtype, q.device.index or 0)
+    return n_splits if n_splits > 0 else tad_auto_splits(B, Hq, Hkv, tokens_of(q), Lmax, d, k.dtype,
+                                                         q.device.index or 0)
 
 
 def tokens_of(q) -> int:

@@ -39,6 +39,13 @@ int elem_size(int32_t dtype) {
 
 bool is_fp8(int32_t dtype) { return dtype == TAD_FP8_E4M3 || dtype == TAD_FP8_E5M2; }
 
+// The kernels' K/V element type for a (validated) tad_dtype.
+int kv_type_of(int32_t dtype) {
+    return dtype == TAD_F32 ? tad::kKvF32
+         : dtype == TAD_BF16 ? tad::kKvBF16
+         : dtype == TAD_FP8_E4M3 ? tad::kKvE4M3 : tad::kKvE5M2;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Shapes and strides of one decode call, normalised to 4-D [B, H, L, d] views.
@@ -237,19 +244,25 @@ int device_cus(int32_t device, int *cus) {
 // differ: then part of the chunks are empty, and the matrix-core kernel, which fits
 // the chunk length to the busy ones, gets room to spread a ragged batch over the
 // device (grouped-query decode, 8 rows of 4653..26803 keys, FP8 K/V: 58.0 -> 49.9 us
-// per step; uniform multi-row batches pay about 1% for the longer merge).  No chunk
-// holds less than 128 KiB of K and V per KV head (256 keys at d = 128 in bf16, 32 at
-// d = 512 in fp32), since shorter chunks cost work-group start-up and merge time: 32
-// bf16 heads of 1024 keys decode in 13.5 us with 4 chunks (128 KiB) and 15.4 us with
-// 8; one fp32 d = 512 head of 4096 keys in 15.8 us with 128 chunks against ~40 us with
-// the 16 that a fixed 256-key minimum gave.
+// per step; uniform multi-row batches pay about 1% for the longer merge).  No
+// work-group's chunk holds less than 128 KiB of K and V (per KV head: 128 KiB, or
+// 32 KiB where the matrix-core kernel serves 4 KV heads per work-group), since shorter
+// chunks cost work-group start-up and merge time: 32 bf16 heads of 1024 keys decode
+// in 13.5 us with 4 chunks (128 KiB) and 15.4 us with 8; one fp32 d = 512 head of
+// 4096 keys in 15.8 us with 128 chunks against ~40 us with the 16 that a fixed
+// 256-key minimum gave; 32 query heads over 8 KV heads of 4096 bf16 keys in 15.6 us
+// with 64 chunks against 18.0 us with 16.
 constexpr int64_t kMinChunkBytes = 128 << 10;
 
-int32_t auto_splits_for(int64_t B, int64_t Hkv, int64_t Lmax, int64_t key_bytes, int cus) {
+int32_t auto_splits_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t nq, int64_t Lmax, int64_t d,
+                        int32_t kv_dtype, int cus) {
     const int64_t units = B * Hkv > 0 ? B * Hkv : 1;
     const int64_t per_cu = B > 1 ? 6 : 4;
     int64_t S = (per_cu * (int64_t)cus + units - 1) / units;
-    const int64_t by_len = Lmax * key_bytes / kMinChunkBytes;
+    const int32_t group = (int32_t)(Hq / (Hkv > 0 ? Hkv : 1));
+    const int64_t heads_per_wg =
+        (Hkv % 4 == 0 && tad::split_mfma_supported((int)d, kv_type_of(kv_dtype), group, (int)nq)) ? 4 : 1;
+    const int64_t by_len = Lmax * 2 * d * elem_size(kv_dtype) * heads_per_wg / kMinChunkBytes;
     if (S > by_len) S = by_len;
     if (S > tad::kMaxSplits) S = tad::kMaxSplits;
     if (S < 1) S = 1;
@@ -290,9 +303,7 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
     a.q = q->data; a.sqb = P.sqb; a.sqh = P.sqh; a.sqt = P.sqt; a.q_bf16 = P.q_dtype == TAD_BF16;
     a.nq = (int32_t)P.nq;
     a.k = k->data; a.v = v->data;
-    a.kv_type = P.kv_dtype == TAD_F32 ? tad::kKvF32
-              : P.kv_dtype == TAD_BF16 ? tad::kKvBF16
-              : P.kv_dtype == TAD_FP8_E4M3 ? tad::kKvE4M3 : tad::kKvE5M2;
+    a.kv_type = kv_type_of(P.kv_dtype);
     a.k_scale = P.k_scale; a.v_scale = P.v_scale;
     a.skb = P.skb; a.skh = P.skh; a.skj = P.skj;
     a.svb = P.svb; a.svh = P.svh; a.svj = P.svj;
@@ -381,7 +392,7 @@ int prepare_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v
     if (n_splits <= 0) {
         int cus = 0;
         if ((rc = device_cus(-1, &cus))) return rc;
-        *S = auto_splits_for(P->B, P->Hkv, P->Lmax, 2 * P->d * elem_size(P->kv_dtype), cus);
+        *S = auto_splits_for(P->B, P->Hq, P->Hkv, P->nq, P->Lmax, P->d, P->kv_dtype, cus);
     } else {
         *S = n_splits;
     }
@@ -455,8 +466,10 @@ int tad_version(void) { return TAD_VERSION; }
 
 const char *tad_last_error(void) { return g_last_error.c_str(); }
 
-int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t d, int32_t kv_dtype, int32_t device) {
-    if (B < 1 || Hkv < 1 || Lmax < 0) return fail(TAD_EINVAL, "tad_auto_splits: bad sizes");
+int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t Lmax, int32_t d, int32_t kv_dtype,
+                        int32_t device) {
+    if (B < 1 || Hkv < 1 || Hq < Hkv || Hq % Hkv != 0 || nq < 1 || nq > 256 || Lmax < 0)
+        return fail(TAD_EINVAL, "tad_auto_splits: bad sizes");
     if (d != 64 && d != 128 && d != 256 && d != 512) return fail(TAD_EUNSUPPORTED, "tad_auto_splits: d = %d", d);
     if (kv_dtype != TAD_F32 && kv_dtype != TAD_BF16 && !is_fp8(kv_dtype))
         return fail(TAD_EDTYPE, "tad_auto_splits: K/V dtype %d", kv_dtype);
@@ -464,7 +477,7 @@ int32_t tad_auto_splits(int32_t B, int32_t Hkv, int64_t Lmax, int32_t d, int32_t
     int rc = device_cus(device, &cus);
     if (rc) return rc;
     ok();
-    return auto_splits_for(B, Hkv, Lmax, 2 * (int64_t)d * elem_size(kv_dtype), cus);
+    return auto_splits_for(B, Hq, Hkv, nq, Lmax, d, kv_dtype, cus);
 }
 
 size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t nq, int32_t n_splits, int32_t d) {

@@ -295,10 +295,12 @@ def test_auto_splits_without_device_reports_hip_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     so = lib.load()
-    assert so.tad_auto_splits(1, 32, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EHIP
-    assert so.tad_auto_splits(0, 32, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EINVAL
-    assert so.tad_auto_splits(1, 32, 131072, 96, tad.TAD_BF16, -1) == tad.TAD_EUNSUPPORTED
-    assert so.tad_auto_splits(1, 32, 131072, 128, 7, -1) == tad.TAD_EDTYPE
+    assert so.tad_auto_splits(1, 32, 32, 1, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EHIP
+    assert so.tad_auto_splits(0, 32, 32, 1, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EINVAL
+    assert so.tad_auto_splits(1, 12, 8, 1, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EINVAL   # Hq % Hkv
+    assert so.tad_auto_splits(1, 32, 8, 0, 131072, 128, tad.TAD_BF16, -1) == tad.TAD_EINVAL   # nq
+    assert so.tad_auto_splits(1, 32, 32, 1, 131072, 96, tad.TAD_BF16, -1) == tad.TAD_EUNSUPPORTED
+    assert so.tad_auto_splits(1, 32, 32, 1, 131072, 128, 7, -1) == tad.TAD_EDTYPE
 
 
 def test_product_does_not_reach_the_oracle():

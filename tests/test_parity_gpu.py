@@ -546,20 +546,28 @@ def test_dominant_key_and_value_shift(lib):
     assert np.abs(shifted.mean() - base.mean() - 2.0) < 1e-2
 
 
-@pytest.mark.parametrize("B,Hkv,Lmax,d,kv", [
-    (1, 32, 131072, 128, torch.bfloat16), (8, 8, 32768, 128, torch.bfloat16), (8, 8, 32768, 128, torch.float8_e4m3fn),
-    (4, 16, 65536, 128, torch.bfloat16), (1, 8, 1 << 20, 128, torch.bfloat16), (1, 1, 4096, 512, torch.float32),
-    (2, 1, 300, 64, torch.bfloat16), (64, 32, 4096, 128, torch.bfloat16), (1, 1, 100, 128, torch.float32),
-    (1, 32, 1024, 128, torch.bfloat16), (2, 2, 16384, 128, torch.float8_e5m2)])
-def test_auto_splits_rule(lib, B, Hkv, Lmax, d, kv):
+@pytest.mark.parametrize("B,Hq,Hkv,nq,Lmax,d,kv", [
+    (1, 32, 32, 1, 131072, 128, torch.bfloat16), (8, 32, 8, 1, 32768, 128, torch.bfloat16),
+    (8, 32, 8, 1, 32768, 128, torch.float8_e4m3fn), (4, 16, 16, 1, 65536, 128, torch.bfloat16),
+    (1, 8, 8, 1, 1 << 20, 128, torch.bfloat16), (1, 1, 1, 1, 4096, 512, torch.float32),
+    (2, 1, 1, 1, 300, 64, torch.bfloat16), (64, 32, 32, 1, 4096, 128, torch.bfloat16),
+    (1, 1, 1, 1, 100, 128, torch.float32), (1, 32, 32, 1, 1024, 128, torch.bfloat16),
+    (2, 16, 2, 1, 16384, 128, torch.float8_e5m2), (1, 32, 8, 1, 4096, 128, torch.bfloat16),
+    (1, 8, 8, 2, 4096, 64, torch.bfloat16), (1, 32, 8, 1, 4096, 256, torch.bfloat16),
+    (1, 128, 8, 2, 4096, 128, torch.bfloat16)])
+def test_auto_splits_rule(lib, B, Hq, Hkv, nq, Lmax, d, kv):
     """The documented automatic chunk count: ceil(4 CUs / (B Hkv)) for one row,
-    ceil(6 CUs / (B Hkv)) for several, no chunk under 128 KiB of K and V per KV head,
+    ceil(6 CUs / (B Hkv)) for several, no work-group chunk under 128 KiB of K and V
+    (32 KiB per KV head where the matrix-core kernel takes 4 KV heads per work-group),
     at least 1."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     per_cu = 4 if B == 1 else 6
     elem = torch.empty((), dtype=kv).element_size()
-    want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax * 2 * d * elem // (128 << 10), 4096))
-    assert lib.tad_auto_splits(B, Hkv, Lmax, d, kv, 0) == want
+    gq = Hq // Hkv * nq
+    matrix = d in (64, 128) and kv != torch.float32 and 2 <= gq <= 16
+    heads_per_wg = 4 if matrix and Hkv % 4 == 0 else 1
+    want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax * 2 * d * elem * heads_per_wg // (128 << 10), 4096))
+    assert lib.tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, kv, 0) == want
 
 
 @pytest.mark.parametrize("d,kv,L", [(512, torch.float32, 4096), (256, torch.bfloat16, 6000)])
