@@ -40,6 +40,13 @@
 //    lane's 8 reduction slots are the 8 keys whose probabilities it already holds;
 //    it is widened to bf16 in registers.
 //
+// Work distribution: the (row, KV-head group, chunk) items are numbered busy-first
+// (every non-empty chunk of the batch first); work-group i runs busy item i, the grid
+// holds at most one work-group per resident slot, and the empty chunks' merge
+// identities are written afterwards by single waves.  The chunk length is one per
+// batch, lengthened on the device when the non-empty chunks would not fit the
+// resident work-groups.
+//
 // Softmax per head: lane l owns head l%16 and 4 keys of each 16-key block; the lanes
 // l, l^16, l^32, l^48 exchange their max and sum (row swaps, no LDS).  The running
 // (m, l) and the rescale of O follow the online softmax of the "Flash Aandacht"
