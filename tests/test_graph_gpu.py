@@ -18,7 +18,8 @@ def dev(x):
     return None if x is None else x.to(DEV)
 
 
-@pytest.mark.parametrize("case", ["fused-mha", "gqa", "split-combine-mha", "paged-interleaved", "tokens"])
+@pytest.mark.parametrize("case", ["fused-mha", "gqa", "split-combine-mha", "paged-interleaved", "tokens",
+                                  "gqa-many-chunks"])
 def test_decode_ws_replays_in_a_graph(lib, case):
     print("[case] graph %s" % case, flush=True)
     paged = case == "paged-interleaved"
@@ -28,6 +29,8 @@ def test_decode_ws_replays_in_a_graph(lib, case):
         c, S = W.random_case(906, 2, 8, 2, 2500, 128, seq_lens=[2500, 1700]), 5
     elif case == "split-combine-mha":  # large grid: split then combine
         c, S = W.random_case(901, 2, 32, 32, 4000, 128, seq_lens=[4000, 3333]), 16
+    elif case == "gqa-many-chunks":   # more chunks than resident work-groups: waves write empty chunks
+        c, S = W.random_case(907, 8, 32, 8, 3000, 128, seq_lens=[3000, 17, 0, 1204, 2999, 300, 1, 2048]), 96
     elif case == "tokens":
         c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
         c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
@@ -63,8 +66,13 @@ def test_decode_ws_replays_in_a_graph(lib, case):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         call(out, ws)
+    n_part = q.shape[0] * q.shape[1] * (q.shape[2] if q.dim() == 4 else 1) * S
+    al = lambda x: (x + 255) // 256 * 256
+    partials = ws[:2 * al(4 * n_part) + 4 * n_part * q.shape[-1]].view(torch.float32)
     for i in range(3):
         out.fill_(float("nan"))                       # eager work between replays
+        if case == "gqa-many-chunks":
+            partials.fill_(float("nan"))              # every partial must be written again
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), "replay %d" % i
