@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark: split-KV exact decode on one MI355X, 128k-token MHA workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S] [--page-size P]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S] [--page-size P] [--tokens N]
 
 One step = one full decode over the workload's inputs, already resident in HBM:
 the split kernel then the combine kernel (tad_split + tad_combine, which is what
@@ -48,13 +48,14 @@ def kernel_source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: int, page_size: int = 0):
+def read_traffic(workload: int, page_size: int = 0, tokens: int = 1):
     """HBM bytes per split-kernel launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
+    tag = "workload%d" % workload + ("_tokens%d" % tokens if tokens > 1 else "")
     if page_size:
-        names = ["split_paged%d_workload%d_traffic.txt" % (page_size, workload)]
+        names = ["split_paged%d_%s_traffic.txt" % (page_size, tag)]
     else:
-        names = ["split_kernel_workload%d_traffic.txt" % workload, "split_mfma_workload%d_traffic.txt" % workload]
+        names = ["split_kernel_%s_traffic.txt" % tag, "split_mfma_%s_traffic.txt" % tag]
     paths = [os.path.join(ROOT, "profiles", n) for n in names if os.path.exists(os.path.join(ROOT, "profiles", n))]
     if not paths:
         return None
@@ -217,6 +218,9 @@ def main(argv=None) -> int:
                     help="store each page as [Hkv, page_size, d] instead of [page_size, Hkv, d]")
     ap.add_argument("--token-major", action="store_true",
                     help="contiguous K/V stored [B, L, Hkv, d] (described as [B, Hkv, L, d] by strides)")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="query tokens per row (several: the rows' last positions, as in "
+                         "speculative decoding; K/V are read once for all of them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for HBM byte counters)")
@@ -245,6 +249,10 @@ def main(argv=None) -> int:
     c = W.make_workload(args.workload)
     print("[bench] workload %d generated in %.1fs" % (args.workload, time.perf_counter() - t_gen),
           file=sys.stderr, flush=True)
+    if args.tokens > 1:                    # same K/V, nq query tokens per (row, head)
+        B0, Hq0, d0 = c["q"].shape
+        c["q"] = W.draw_q(1000 * args.workload + 6, B0, Hq0 * args.tokens, d0).view(B0, Hq0, args.tokens, d0)
+    nq = args.tokens
     q = c["q"].to(dev)
     if args.page_size:
         kc, vc, table = W.page_kv(c["k"], c["v"], args.page_size, 1000 * args.workload,
@@ -267,9 +275,9 @@ def main(argv=None) -> int:
     elif c["n_splits"] > 0:
         S = c["n_splits"]
     else:                                  # what tad_decode_ws picks
-        S = tad.tad_auto_splits(B, Hq, Hkv, 1, Lmax, d, w.kv_dtype)
+        S = tad.tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, w.kv_dtype)
     ws = tad.workspace(q, c["k"], S)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     kv_bytes = w.kv_bytes(c["seq_lens"])
     stream = torch.cuda.current_stream()
 
@@ -284,7 +292,7 @@ def main(argv=None) -> int:
             tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
         if ev is not None:
             ev[1].record(stream)
-        tad.tad_combine(ws, B, Hq, 1, S, d, out, stream)
+        tad.tad_combine(ws, B, Hq, nq, S, d, out, stream)
 
     scratch = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) if args.flush_mib else None
     for i in range(args.warmup):
@@ -321,7 +329,7 @@ def main(argv=None) -> int:
     print("[bench] step %.1f us (split kernel %.1f us, combine + gaps %.1f us), %.0f GB/s" %
           (ms_per_step * 1e3, split_avg * 1e3, comb_avg * 1e3, gbs), file=sys.stderr, flush=True)
 
-    traffic = read_traffic(args.workload, args.page_size)
+    traffic = read_traffic(args.workload, args.page_size, nq)
     kv_name = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8-e4m3",
                torch.float8_e5m2: "fp8-e5m2"}[w.kv_dtype]
     result = {
@@ -341,7 +349,8 @@ def main(argv=None) -> int:
         "kv_dtype": kv_name,
         "data": "synthetic",
         "config": {
-            "workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax,
+            "workload": w.name + (", %d query tokens per row" % nq if nq > 1 else ""),
+            "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax, "tokens": nq,
             "n_splits": S, "kv_bytes_per_step": kv_bytes,
             "timing": ("per-step events, %d MiB scratch written between steps" % args.flush_mib
                        if args.flush_mib else "steps back to back, wall clock"),
