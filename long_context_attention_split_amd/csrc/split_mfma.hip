@@ -461,18 +461,18 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     else run(std::false_type{});
 
     // ---- merge the NW wave states per head through LDS (reusing the tile buffers).
-    // Each wave's gq columns are rows of D floats in its own MAXG * D slot; with fewer
-    // than 16 columns the rows are padded by 16 bytes, so that the 16-byte stores of
-    // one column-block of a wave (one per column) land in different banks.
+    // Each wave's columns are rows of D floats in its own MAXG * D slot; the 16-byte
+    // chunk k of row j is stored at chunk k ^ j (j < 16), so that the 16-byte stores of
+    // one column block (one per column, rows 512 bytes apart) land in 16 different
+    // bank groups, and the merge's reads of a row (64 consecutive floats) too.
     __syncthreads();
-    const int RS = gq < MAXG ? D + 4 : D;                  // row stride, floats
-    float *const lds_o = reinterpret_cast<float *>(smem);  // [NW][MAXG * D], rows RS apart
+    float *const lds_o = reinterpret_cast<float *>(smem);  // [NW][MAXG][D], chunks swizzled per row
     if (head_ok) {
-        float *const orow = lds_o + wave * (MAXG * D) + j16 * RS;
+        float *const orow = lds_o + wave * (MAXG * D) + j16 * D;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) orow[16 * nb + 4 * c4 + r] = F8 ? O[nb][r] * vs : O[nb][r];
+            for (int r = 0; r < 4; ++r) orow[4 * ((4 * nb + c4) ^ j16) + r] = F8 ? O[nb][r] * vs : O[nb][r];
         if (c4 == 0) {
             lds_ml[0][wave][j16] = m;
             lds_ml[1][wave][j16] = l;
@@ -503,8 +503,9 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
         const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
         float acc = 0.f;
+        const int ecol = 4 * ((e >> 2) ^ hh) + (e & 3);         // swizzled position of element e in row hh
 #pragma unroll
-        for (int w = x * NWH; w < x * NWH + NWH; ++w) acc = fmaf(lds_ml[0][w][hh], lds_o[w * (MAXG * D) + hh * RS + e], acc);
+        for (int w = x * NWH; w < x * NWH + NWH; ++w) acc = fmaf(lds_ml[0][w][hh], lds_o[w * (MAXG * D) + hh * D + ecol], acc);
         const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
         a.ws_o[r * D + e] = acc;
     }
