@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10700 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 10800 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -127,7 +127,9 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  *     m[r]        fp32: chunk maximum of the scores, in base-2 units (score * log2 e);
  *                 -inf for an empty chunk
  *     l[r]        fp32: sum over the chunk of 2^(score*log2 e - m[r])
- *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e]
+ *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e];
+ *                 left unwritten for an empty chunk (tad_combine ignores the o of a
+ *                 chunk whose weight is 0, whatever it holds)
  *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws)
  * m, l, o are the per-chunk (local max, denominator, numerator) of tree_attn_decode,
  * with the maximum kept in base 2.

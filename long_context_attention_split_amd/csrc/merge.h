@@ -5,7 +5,9 @@
 //   M = max_s m_s,  w_s = 2^(m_s - M),  L = sum_s w_s l_s,  out = sum_s w_s o_s / L
 // -- the global max / renormalise / sum / divide steps that tree_attn_decode ("Tree
 // Attention Decoding") performs with one max all-reduce and two sum all-reduces.
-// Empty chunks (m = -inf) get weight 0; a row whose chunks are all empty gets out = 0.
+// Empty chunks (m = -inf) get weight 0, and a chunk of weight 0 adds nothing to the
+// sums whatever its o holds (so a producer need not write o for an empty chunk); a
+// row whose chunks are all empty gets out = 0.
 // Every sum runs in a fixed order, so the result is bit-reproducible and identical
 // whichever kernel performs the merge.
 #pragma once
@@ -18,6 +20,11 @@ namespace tad {
 // device coherence point (agent-scope atomic loads), for partials that other
 // work-groups of the same kernel wrote with agent-scope atomic stores.
 constexpr int kMergeThreads = 256;
+
+// acc + w * o, or acc unchanged for a weight of 0 (o may then be anything, NaN included).
+__device__ __forceinline__ float add_weighted(float w, float o, float acc) {
+    return w != 0.f ? fmaf(w, o, acc) : acc;
+}
 
 template <bool COHERENT>
 __device__ __forceinline__ float load_partial(const float *p) {
@@ -117,10 +124,10 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
             if (gi == g0) {
 #pragma unroll
                 for (int i = 0; i < PF; ++i, s += R)
-                    if (s < S) acc = fmaf(w[s], pre[i], acc);
+                    if (s < S) acc = add_weighted(w[s], pre[i], acc);
             }
 #pragma unroll 8
-            for (; s < S; s += R) acc = fmaf(w[s], load_partial<COHERENT>(o + (int64_t)s * D + col), acc);
+            for (; s < S; s += R) acc = add_weighted(w[s], load_partial<COHERENT>(o + (int64_t)s * D + col), acc);
             part[tid] = acc;
         }
         __syncthreads();
