@@ -498,14 +498,24 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
         a.ws_l[r] = lsum;
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < HG * gq * D; idx += THREADS) {
-        const int x = idx / (gq * D), hh = (idx / D) % gq, e = idx % D;
+    // Thread t handles element t % D of rows t / D, t / D + THREADS / D, ... (row = x * gq
+    // + hh); THREADS is a multiple of D >= 64, so a wave's row is uniform and (x, hh)
+    // advance by subtraction instead of a division per row.
+    static_assert(THREADS % D == 0, "a thread keeps one element of its rows");
+    constexpr int RSTEP = THREADS / D;
+    const int e = (int)threadIdx.x % D;
+    int row = __builtin_amdgcn_readfirstlane((int)threadIdx.x / D);
+    int x = 0, hh = row;
+    while (hh >= gq) { hh -= gq; ++x; }
+    for (; row < HG * gq; row += RSTEP) {
         float acc = 0.f;
         const int ecol = 4 * ((e >> 2) ^ hh) + (e & 3);         // swizzled position of element e in row hh
 #pragma unroll
         for (int w = x * NWH; w < x * NWH + NWH; ++w) acc = fmaf(lds_ml[0][w][hh], lds_o[w * (MAXG * D) + hh * D + ecol], acc);
         const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
         a.ws_o[r * D + e] = acc;
+        hh += RSTEP;
+        while (hh >= gq) { hh -= gq; ++x; }
     }
 }
 
