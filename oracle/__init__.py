@@ -11,9 +11,10 @@ package imports nothing from the product.
   values, fp8 with per-(batch, KV head) dequantisation scales.
 - ``alibi_bias``: the bias term that definition adds ("ALiBi with causal=True
   unexpected bias?", causal bias vector example).
-- ``tree``: numpy fp64 split-and-merge decoding in the steps of the tree-attention
-  gist, used to pin the definition by chunk-count and merge-order invariance and to
-  check per-chunk partials.
+- ``tree``: numpy fp64 split-and-merge decoding (per-chunk peak / mass / value sum,
+  then their combination), derived from the softmax over a union of key chunks that
+  the tree-attention gist computes; used to pin the definition by chunk-count and
+  merge-order invariance and to check per-chunk partials.
 """
 from __future__ import annotations
 
