@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 10800 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 20000 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -130,9 +130,24 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e];
  *                 left unwritten for an empty chunk (tad_combine ignores the o of a
  *                 chunk whose weight is 0, whatever it holds)
- *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws)
+ *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws),
+ *                 followed, when B * Hq * nq * n_splits < 256, by ccnt[r], int32
+ *                 arrival counters of the chunks' pieces (below)
+ *     sub_m, sub_l, sub_o: when B * Hq * nq * n_splits < 256, the partials of up to
+ *                 Pmax = min(512 / (B * Hq * nq * n_splits), 16384 / d, 64) pieces per
+ *                 chunk, same meaning as m, l, o for a piece of the chunk
  * m, l, o are the per-chunk (local max, denominator, numerator) of tree_attn_decode,
  * with the maximum kept in base 2.
+ *
+ * Pieces.  A call with few (row, chunk) pairs would leave most compute units idle
+ * (one head cut into 8 chunks is 8 work-groups), so where the vector kernel serves one
+ * query row per KV head, each chunk of at least 256 KiB of K+V is read by up to Pmax
+ * work-groups, each a contiguous piece of ceil(c / P) keys (whole pages for a paged
+ * cache) with P = min(Pmax, chunk bytes / 128 KiB), and the last of them to finish
+ * merges the pieces' partials into the chunk's (m, l, o) by the same rescale-and-sum.
+ * The chunks themselves, and so the partials tad_split reports, are those n_splits
+ * asks for; only their rounding differs from an uncut chunk.  P depends on the call's
+ * sizes only, so every entry point cuts a call the same way.
  */
 size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t nq, int32_t n_splits, int32_t d);
 
@@ -145,7 +160,9 @@ int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
 /*
  * Split step: every (b, query head, chunk) partial (m, l, o) into `ws` (layout above).
  * n_splits must be >= 1 here (use tad_auto_splits to pick one).  `ws` is a device
- * buffer of at least tad_workspace_bytes(B, Hq, nq, n_splits, d) bytes, 256-byte aligned.
+ * buffer of at least tad_workspace_bytes(B, Hq, nq, n_splits, d) bytes, 256-byte aligned,
+ * whose counters are zero (as for tad_decode_ws: chunks cut into pieces count their
+ * pieces there; every call that completes leaves them zero).
  */
 int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
               const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,

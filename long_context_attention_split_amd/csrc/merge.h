@@ -41,6 +41,95 @@ __device__ __forceinline__ void store_partial(float *p, float x) {
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Arrival ticket of a work-group on a counter shared by `total` work-groups that each
+// publish partials for one merge: true in the last one to arrive.  Called by every
+// thread of the work-group.  Ordering (HIP's scoped memory model): the barrier puts
+// every thread's earlier partial stores before thread 0's agent-scope release in the
+// counter update; the last arrival's update acquires at agent scope, so after the
+// second barrier every thread of that work-group sees all the other work-groups'
+// partials (the counter updates form one release sequence).  `flag` is a word of LDS.
+__device__ __forceinline__ bool arrive_last(int32_t *cnt, int total, int *flag) {
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+    __syncthreads();
+    return *flag != 0;
+}
+
+// Return an arrival counter to zero once its merge is done (the next use is in a later
+// kernel, ordered by the stream).
+__device__ __forceinline__ void reset_counter(int32_t *cnt) {
+    if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Pre-merge of one chunk's P pieces (m_p in base 2, l_p, o_p[D], written by P
+// work-groups) into the chunk's own partial: M = max_p m_p, w_p = 2^(m_p - M),
+// l = sum_p w_p l_p, o = sum_p w_p o_p -- the same rescale-and-sum as the row merge,
+// without the division, since the result is a partial again.  Fixed order: each of
+// the TPC thread parts of a column sums its pieces p in order, and the parts are added
+// in order; l is a wave sum over the pieces.  All P * D values are loaded in one round
+// (at most 64 per thread).  Called by all NT threads; `lds` holds 64 + NT floats.
+// Results are stored with store_partial (another work-group may merge them next).
+template <int D, int NT>
+__device__ __forceinline__ void merge_pieces(const float *m, const float *l, const float *o, int P, float *cm,
+                                             float *cl, float *co, float *lds) {
+    constexpr int TPC = D >= NT ? 1 : NT / D;      // threads per column
+    constexpr int CPT = D >= NT ? D / NT : 1;      // columns per thread
+    constexpr int PCAP = 16384 / D < 64 ? 16384 / D : 64;   // most pieces (max_sub_splits)
+    constexpr int PPT = PCAP / TPC;                // pieces per thread part: CPT * PPT <= 64 loads
+    static_assert(NT % 64 == 0 && (TPC == 1 || NT % D == 0), "work-group shape");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int part = TPC > 1 ? tid / D : 0;
+    const int col0 = TPC > 1 ? tid % D : tid;
+    float *w = lds;            // [64] weights
+    float *sums = lds + 64;    // [NT] part sums
+
+    // every load up front: this thread's pieces of its columns, then m and l
+    float v[CPT][PPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = part * PPT + i;
+            v[c][i] = p < P ? load_partial<true>(o + (int64_t)p * D + col0 + c * NT) : 0.f;
+        }
+    const float mp = lane < P ? load_partial<true>(m + lane) : kNegInf;
+    const float lp = lane < P ? load_partial<true>(l + lane) : 0.f;
+    const float M = wave_max(mp);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    const float wp = lane < P ? exp2_fast(mp - Mu) : 0.f;
+    if (tid < 64) w[lane] = wp;
+    const float lsum = wave_sum(wp * lp);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = part * PPT + i;
+            if (p < P) acc = add_weighted(w[p], v[c][i], acc);
+        }
+        if constexpr (TPC == 1) {
+            store_partial(co + col0 + c * NT, acc);
+        } else {
+            sums[tid] = acc;
+        }
+    }
+    if constexpr (TPC > 1) {
+        __syncthreads();
+        if (tid < D) {
+            float t = 0.f;
+#pragma unroll
+            for (int k = 0; k < TPC; ++k) t += sums[k * D + tid];
+            store_partial(co + tid, t);
+        }
+    }
+    if (tid == 0) {
+        store_partial(cm, M);
+        store_partial(cl, lsum);
+    }
+}
+
 // Thread rows per output column in the weighted sum over the chunks: row rr of R takes
 // the chunks s = rr, rr + R, ... in order and the R row sums are added in order, so the
 // bits depend on (S, D) only -- whichever kernel merges, however many work-groups share

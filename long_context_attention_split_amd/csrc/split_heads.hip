@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
 }
 
 bool split_heads_supported(const SplitArgs &a, int d) {
-    if (a.fused || a.group != 1 || a.nq != 1 || a.Hkv < 2 || a.Hq % kHeadsPerWave) return false;
+    if (a.fused || a.P > 1 || a.group != 1 || a.nq != 1 || a.Hkv < 2 || a.Hq % kHeadsPerWave) return false;
     if (d != 64 && d != 128 && d != 256) return false;
     if (a.skh != d || a.svh != d) return false;              // heads of a key adjacent
     return a.skj >= (int64_t)kHeadsPerWave * d && a.svj >= (int64_t)kHeadsPerWave * d;

@@ -543,7 +543,11 @@ void split_mfma_kernel(SplitArgs a) {
 
     const int G = a.Hkv / HG;
     const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
-    const int c = fit_chunk_len(a, G, batch_chunk_len(a, len0), len0, a.wg_slots);
+    // The fit applies where the launcher capped the grid at the resident slots (B * G
+    // <= slots); with more (row, KV-head group) pairs than slots no chunk length fits,
+    // and the grid holds every item, so the finest chunking stays.
+    const int fit_slots = (int64_t)a.B * G <= a.wg_slots ? a.wg_slots : 0;
+    const int c = fit_chunk_len(a, G, batch_chunk_len(a, len0), len0, fit_slots);
     const int busy = busy_items(a, G, c, len0);
     const int w = (int)blockIdx.x, grid = (int)gridDim.x;
     if (w < busy) {

@@ -44,7 +44,11 @@ namespace tad {
 // PAGED: K/V rows come from a paged cache through the block table; every wave tile
 // then lies inside one page (tile length divides the page size) and gets its own
 // buffer resource.
-template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PAGED = false>
+// TAIL: the variant whose work-groups may also merge -- the pieces of a chunk (a.P > 1)
+// and/or a whole row (a.fused) -- kept apart so that the plain kernel carries none of
+// that code or its registers.
+template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PAGED = false,
+          bool TAIL = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
     using Row = RowChunk<KVT, POLICY>;
     constexpr int EPL = Row::EPL;                // elements per lane per key
@@ -62,15 +66,20 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const int grp = lane / G;
     const int sub = lane % G;
 
-    // ---- work-group -> (b, h, t, s): query head h, query token t, chunk s.  When
-    // several (head, token) rows read the same KV chunk (query-head groups, several
-    // tokens), their gq work-groups get ids that are equal modulo 8, so they land on
-    // the same XCD and share its L2.
-    int b, h, t, s;
+    // ---- work-group -> (b, h, t, s, p): query head h, query token t, chunk s, piece p
+    // of the chunk (pieces: one query row per KV head only).  When several (head,
+    // token) rows read the same KV chunk (query-head groups, several tokens), their gq
+    // work-groups get ids that are equal modulo 8, so they land on the same XCD and
+    // share its L2.
+    int b, h, t, s, p = 0;
     const int S = a.S;
     const int gq = a.group * a.nq;                        // rows per KV head
     if (gq == 1) {
-        const int id = blockIdx.x;
+        int id = blockIdx.x;
+        if constexpr (TAIL) {
+            p = id % a.P;
+            id /= a.P;
+        }
         s = id % S;
         const int row = id / S;
         b = row / a.Hq;
@@ -91,9 +100,16 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     }
     const int kvh = h / a.group;
 
-    // The chunk of the KV row, clipped to the keys this token sees; from here on the
-    // row is single-token decode over its first L keys.
-    const ChunkRange cr = chunk_range(a, b, s);
+    // The chunk (or its piece p) of the KV row, clipped to the keys this token sees;
+    // from here on the row is single-token decode over its first L keys.
+    const int cfull = batch_chunk_len(a);
+    ChunkRange cr = chunk_of(row_len(a, b), s, cfull);
+    if (TAIL && a.P > 1) {
+        const int cs = sub_chunk_len(a, cfull);
+        const int pj0 = (int)min((int64_t)cr.j0 + (int64_t)p * cs, (int64_t)cr.j1);
+        cr.j1 = min(pj0 + cs, cr.j1);
+        cr.j0 = pj0;
+    }
     const int L = visible_keys(cr.L, a.nq, t);
     const int j1 = min(cr.j1, L), j0 = min(cr.j0, j1);
     const int n = j1 - j0;
@@ -228,76 +244,98 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const int64_t row = ((int64_t)b * a.Hq + h) * a.nq + t;
     const int64_t r = row * S + s;
     const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // V dequantisation
-    // Partials are written through to the device coherence point when this kernel also
-    // merges (fused), so the merging work-group can read them without cache maintenance.
+    // Where this work-group's partial goes: the chunk's slot, or piece p's slot.  A
+    // partial that another work-group of this kernel merges is written through to the
+    // device coherence point (store_partial).
+    const bool piece = TAIL && a.P > 1;
+    const int64_t rp = r * a.P + p;
+    float *const pm = piece ? a.sub_m + rp : a.ws_m + r;
+    float *const pl = piece ? a.sub_l + rp : a.ws_l + r;
+    float *const po = piece ? a.sub_o + rp * D : a.ws_o + r * D;
     for (int e = threadIdx.x; e < D; e += kSplitThreads) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_o[i][e], acc);
         acc *= vsc;
-        if (a.fused) store_partial(&a.ws_o[r * D + e], acc);
-        else a.ws_o[r * D + e] = acc;
+        if constexpr (TAIL) store_partial(po + e, acc);
+        else po[e] = acc;
     }
     if (threadIdx.x == 0) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) acc = fmaf(exp2_fast(lds_m[i] - Mu), lds_l[i], acc);
-        if (a.fused) {
-            store_partial(&a.ws_m[r], M);
-            store_partial(&a.ws_l[r], acc);
+        if constexpr (TAIL) {
+            store_partial(pm, M);
+            store_partial(pl, acc);
         } else {
-            a.ws_m[r] = M;
-            a.ws_l[r] = acc;
+            *pm = M;
+            *pl = acc;
         }
     }
 
-    // ---- fused merge: the last of the row's S work-groups to arrive merges the row.
-    if (a.fused) {
-        static_assert(SLOTS * D >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in lds_o");
+    if constexpr (TAIL) {
+        static_assert(SLOTS * D >= kMaxFusedSplits + kMergeThreads && SLOTS * D >= 64 + kSplitThreads,
+                      "merge scratch fits in lds_o");
         __shared__ int last;
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial stores are done
-        __syncthreads();
-        if (threadIdx.x == 0) last = atomicAdd(&a.cnt[row], 1) == S - 1;
-        __syncthreads();
-        if (last) {
+        // ---- pieces: the last of the chunk's P work-groups merges them into the chunk's
+        // partial.
+        if (piece) {
+            if (!arrive_last(&a.ccnt[r], a.P, &last)) return;
+            merge_pieces<D, kSplitThreads>(a.sub_m + r * a.P, a.sub_l + r * a.P, a.sub_o + r * a.P * D, a.P,
+                                           a.ws_m + r, a.ws_l + r, a.ws_o + r * D, &lds_o[0][0]);
+            reset_counter(&a.ccnt[r]);
+        }
+        // ---- fused merge: the last of the row's S chunks to be complete merges the row.
+        if (a.fused && arrive_last(&a.cnt[row], S, &last)) {
             merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
                                a.out + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)t * a.sot,
                                &lds_o[0][0]);
-            if (threadIdx.x == 0) a.cnt[row] = 0;
+            reset_counter(&a.cnt[row]);
         }
     }
 }
 
-template <int D, int KVT>
-static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
+template <int D, int KVT, bool TAIL>
+static hipError_t launch_tail(const SplitArgs &a, int64_t grid, hipStream_t st) {
     // paged caches: 16-key wave tiles (page sizes are multiples of 16)
     constexpr int KPW = 64 * RowChunk<KVT, kPolicyNT>::EPL / D;
     constexpr int UP = 16 / KPW > 0 ? 16 / KPW : 1;
+    constexpr int UD = 128 / RowChunk<KVT, kPolicyNT>::kBytes;
+    const int gq = a.group * a.nq;
+    if (a.block_table) {
+        if constexpr (KVT == kKvF32 || D > 256) {
+            return hipErrorInvalidValue;                  // not offered for paged caches
+        } else if (gq == 1) {
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, true, TAIL>), dim3((unsigned)grid),
+                               dim3(kSplitThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, true, TAIL>), dim3((unsigned)grid),
+                               dim3(kSplitThreads), 0, st, a);
+        }
+    } else if (gq == 1) {
+        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UD, false, TAIL>), dim3((unsigned)grid),
+                           dim3(kSplitThreads), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UD, false, TAIL>), dim3((unsigned)grid),
+                           dim3(kSplitThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int KVT>
+static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
     int64_t grid;
     const int gq = a.group * a.nq;
+    if (a.P > 1 && gq != 1) return hipErrorInvalidValue;   // pieces: one query row per KV head only
     if (gq == 1) {
-        grid = (int64_t)a.B * a.Hq * a.S;
+        grid = (int64_t)a.B * a.Hq * a.S * a.P;
     } else {
         const int64_t units = (int64_t)a.B * a.Hkv * a.S;
         grid = (units + 7) / 8 * 8 * gq;
     }
     if (grid <= 0) return hipSuccess;
-    if (a.block_table) {
-        if constexpr (KVT == kKvF32 || D > 256) {
-            return hipErrorInvalidValue;                  // not offered for paged caches
-        } else if (gq == 1) {
-            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, true>), dim3((unsigned)grid),
-                               dim3(kSplitThreads), 0, st, a);
-        } else {
-            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, true>), dim3((unsigned)grid),
-                               dim3(kSplitThreads), 0, st, a);
-        }
-    } else if (gq == 1) {
-        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-    } else {
-        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault>), dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
-    }
-    return hipGetLastError();
+    if (a.fused || a.P > 1) return launch_tail<D, KVT, true>(a, grid, st);
+    return launch_tail<D, KVT, false>(a, grid, st);
 }
 
 template <int D>

@@ -251,8 +251,8 @@ int device_cus(int32_t device, int *cus) {
 // in 13.5 us with 4 chunks (128 KiB) and 15.4 us with 8; one fp32 d = 512 head of
 // 4096 keys in 15.8 us with 128 chunks against ~40 us with the 16 that a fixed
 // 256-key minimum gave; 32 query heads over 8 KV heads of 4096 bf16 keys in 15.6 us
-// with 64 chunks against 18.0 us with 16.
-constexpr int64_t kMinChunkBytes = 128 << 10;
+// with 64 chunks against 18.0 us with 16.  (tad::kMinChunkBytes = 128 KiB.)
+using tad::kMinChunkBytes;
 
 int32_t auto_splits_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t nq, int64_t Lmax, int64_t d,
                         int32_t kv_dtype, int cus) {
@@ -269,10 +269,30 @@ int32_t auto_splits_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t nq, int64_t 
     return (int32_t)S;
 }
 
+// Device arrays of one call: the partials (m, l, o), the arrival counters (cnt per row,
+// ccnt per chunk), and the pieces' partials (sub_*), which exist when Pmax > 1.
 struct WsPtrs {
     float *m, *l, *o;
-    int32_t *cnt;
+    int32_t *cnt, *ccnt;
+    float *sm, *sl, *so;
+    int Pmax;
 };
+
+// Pointers into a workspace laid out by tad::ws_layout.  `counters`, when non-null,
+// replaces the workspace's own counter region (the no-allocation entry point keeps its
+// counters at a fixed place).
+void carve_at(char *base, int64_t rows, int64_t S, int64_t d, int32_t *counters, WsPtrs *p) {
+    const tad::WsLayout L = tad::ws_layout(rows, S, d);
+    p->m = (float *)(base + L.off_m);
+    p->l = (float *)(base + L.off_l);
+    p->o = (float *)(base + L.off_o);
+    p->cnt = counters ? counters : (int32_t *)(base + L.off_cnt);
+    p->ccnt = p->cnt + rows;
+    p->sm = (float *)(base + L.off_sm);
+    p->sl = (float *)(base + L.off_sl);
+    p->so = (float *)(base + L.off_so);
+    p->Pmax = L.Pmax;
+}
 
 int carve_ws(void *ws, size_t ws_bytes, int64_t rows, int64_t S, int64_t d, WsPtrs *p) {
     const tad::WsLayout L = tad::ws_layout(rows, S, d);
@@ -280,11 +300,20 @@ int carve_ws(void *ws, size_t ws_bytes, int64_t rows, int64_t S, int64_t d, WsPt
     if ((uintptr_t)ws & 255u) return fail(TAD_EWORKSPACE, "workspace must be 256-byte aligned");
     if (ws_bytes < L.total)
         return fail(TAD_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
-    p->m = (float *)((char *)ws + L.off_m);
-    p->l = (float *)((char *)ws + L.off_l);
-    p->o = (float *)((char *)ws + L.off_o);
-    p->cnt = (int32_t *)((char *)ws + L.off_cnt);
+    carve_at((char *)ws, rows, S, d, nullptr, p);
     return TAD_OK;
+}
+
+// Pieces per chunk (SplitArgs::P) for a call the vector kernel serves with one query
+// row per KV head: up to the workspace's Pmax (which brings the (row, chunk) pairs to
+// about kSubSplitTarget work-groups), and no piece under kMinChunkBytes of K and V, the
+// shortest chunk the automatic count gives.  A function of the call's sizes only, so
+// tad_split and the decode entry points cut a call the same way.
+int pieces_for(const Problem &P, int32_t S, int Pmax) {
+    if (Pmax <= 1) return 1;
+    const int64_t c = (P.Lmax + S - 1) / S;
+    const int64_t n = c * 2 * P.d * elem_size(P.kv_dtype) / kMinChunkBytes;
+    return (int)(n < 1 ? 1 : (n > Pmax ? Pmax : n));
 }
 
 // Output of a decode: fp32 [B, Hq, nq, d] with element strides.
@@ -318,10 +347,18 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
     a.wg_slots = 0;
     a.qscale = (float)(1.4426950408889634 / sqrt((double)P.d));
     a.ws_m = w.m; a.ws_l = w.l; a.ws_o = w.o;
-    a.fused = out.data != nullptr;
+    a.fused = 0;
     a.cnt = w.cnt;
     a.out = out.data;
     a.sob = out.sob; a.soh = out.soh; a.sot = out.sot;
+    a.P = 1;
+    a.ccnt = w.ccnt;
+    a.sub_m = w.sm; a.sub_l = w.sl; a.sub_o = w.so;
+    // pieces: only where the vector kernel runs with one query row per KV head
+    if (a.group * a.nq == 1 && !tad::split_mfma_supported((int)P.d, a.kv_type, a.group, a.nq) &&
+        !tad::split_heads_supported(a, (int)P.d))
+        a.P = pieces_for(P, S, w.Pmax);
+    a.fused = out.data != nullptr;
     return a;
 }
 
@@ -448,7 +485,7 @@ int decode_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, c
     WsPtrs w;
     rc = carve_ws(ws, bytes, rows, S, P.d, &w);
     if (!rc) {
-        hipError_t ez = tad::launch_fill_zero(w.cnt, rows, stream);
+        hipError_t ez = tad::launch_fill_zero(w.cnt, tad::ws_counters(rows, S, P.d), stream);
         if (ez != hipSuccess) rc = fail(TAD_EHIP, "counter clear launch: %s", hipGetErrorString(ez));
     }
     if (!rc) rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream);

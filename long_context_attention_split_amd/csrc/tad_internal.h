@@ -39,6 +39,14 @@ struct SplitArgs {
     int32_t *cnt;           // [B * Hq * nq] arrival counters
     float *out;             // [B, Hq, nq, d] fp32
     int64_t sob, soh, sot;  // out element strides
+    // Sub-chunks (vector kernel, one query row per KV head): with P > 1 every chunk is
+    // read by P work-groups, piece p holding keys [p * cs, (p + 1) * cs) of the chunk
+    // (cs = sub_chunk_len), and the last of the P to finish (counted in ccnt) merges
+    // their partials (sub_m, sub_l, sub_o) into the chunk's (m, l, o).  ccnt must be
+    // zero on entry and is left zero.
+    int32_t P;
+    int32_t *ccnt;          // [B * Hq * nq * S] arrival counters per chunk
+    float *sub_m, *sub_l, *sub_o;   // [rows * S * P], the same, [rows * S * P * d]
 };
 
 struct CombineArgs {
@@ -298,22 +306,66 @@ struct TilePages {
     }
 };
 
+// Sub-chunk length: chunk length c cut into P pieces (whole pages for a paged cache).
+__device__ __forceinline__ int sub_chunk_len(const SplitArgs &a, int c) {
+    int cs = (c + a.P - 1) / a.P;
+    if (a.block_table) cs = (cs + a.page_size - 1) / a.page_size * a.page_size;
+    return cs;
+}
+
 // Workspace carving (same arithmetic as tad_workspace_bytes).
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Sub-chunks: problems with fewer than kSubSplitBelow (row, chunk) pairs may cut every
+// chunk into up to max_sub_splits pieces, each its own work-group, to reach about
+// kSubSplitTarget work-groups (a chunk count the caller fixed can leave most compute
+// units idle: one fp32 d = 512 head of 4096 keys in 8 chunks ran as 8 work-groups).
+// At most 64 pieces, and at most 64 partial values per thread in the pre-merge
+// (pieces * d / 256): one round of loads.  A pure function of the sizes, so every
+// entry point that sees the same call cuts it the same way.
+constexpr int64_t kSubSplitBelow = 256;
+constexpr int64_t kSubSplitTarget = 512;
+// Shortest chunk (K and V bytes per KV head) worth a work-group of its own; the
+// automatic chunk count never goes below it either.
+constexpr int64_t kMinChunkBytes = 128 << 10;
+
+inline int max_sub_splits(int64_t rows, int64_t S, int64_t d) {
+    const int64_t pairs = rows * S;
+    if (pairs <= 0 || pairs >= kSubSplitBelow || d <= 0) return 1;
+    int64_t P = kSubSplitTarget / pairs;
+    const int64_t cap = 16384 / d < 64 ? 16384 / d : 64;
+    if (P > cap) P = cap;
+    return P < 1 ? 1 : (int)P;
+}
+
+// m, l, o (tad.h), then the arrival counters -- cnt [rows], followed, when chunks may be
+// cut into pieces, by ccnt [rows * S] -- then the pieces' partials sub_m, sub_l
+// [rows * S * Pmax] and sub_o [rows * S * Pmax * d].
 struct WsLayout {
-    size_t off_m, off_l, off_o, off_cnt, total;
+    size_t off_m, off_l, off_o, off_cnt, off_ccnt, off_sm, off_sl, off_so, total;
+    int Pmax;
 };
 
 inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
     WsLayout w;
-    size_t n = size_t(rows) * size_t(S);
+    const size_t n = size_t(rows) * size_t(S);
+    w.Pmax = max_sub_splits(rows, S, d);
+    const size_t np = w.Pmax > 1 ? n * size_t(w.Pmax) : 0;
     w.off_m = 0;
     w.off_l = align256(n * sizeof(float));
     w.off_o = w.off_l + align256(n * sizeof(float));
     w.off_cnt = w.off_o + align256(n * size_t(d) * sizeof(float));
-    w.total = w.off_cnt + align256(size_t(rows) * sizeof(int32_t));
+    w.off_ccnt = w.off_cnt + size_t(rows) * sizeof(int32_t);
+    w.off_sm = w.off_cnt + align256((size_t(rows) + (np ? n : 0)) * sizeof(int32_t));
+    w.off_sl = w.off_sm + align256(np * sizeof(float));
+    w.off_so = w.off_sl + align256(np * sizeof(float));
+    w.total = w.off_so + align256(np * size_t(d) * sizeof(float));
     return w;
+}
+
+// Arrival counters of a workspace: cnt and ccnt, contiguous from off_cnt.
+inline int64_t ws_counters(int64_t rows, int64_t S, int64_t d) {
+    return rows + (max_sub_splits(rows, S, d) > 1 ? rows * S : 0);
 }
 
 // Launchers (defined next to their kernels).  Return the hipError_t of the launch.

@@ -19,7 +19,7 @@ def dev(x):
 
 
 @pytest.mark.parametrize("case", ["fused-mha", "gqa", "split-combine-mha", "paged-interleaved", "tokens",
-                                  "gqa-many-chunks"])
+                                  "gqa-many-chunks", "pieces", "pieces-combine"])
 def test_decode_ws_replays_in_a_graph(lib, case):
     print("[case] graph %s" % case, flush=True)
     paged = case == "paged-interleaved"
@@ -31,6 +31,10 @@ def test_decode_ws_replays_in_a_graph(lib, case):
         c, S = W.random_case(901, 2, 32, 32, 4000, 128, seq_lens=[4000, 3333]), 16
     elif case == "gqa-many-chunks":   # more chunks than resident work-groups: waves write empty chunks
         c, S = W.random_case(907, 8, 32, 8, 3000, 128, seq_lens=[3000, 17, 0, 1204, 2999, 300, 1, 2048]), 96
+    elif case == "pieces":            # one head, 8 chunks read as pieces, then the fused row merge
+        c, S = W.random_case(908, 1, 1, 1, 4096, 512, kv_dtype=torch.float32), 8
+    elif case == "pieces-combine":    # 40 chunks read as pieces, then the combine kernel
+        c, S = W.random_case(909, 1, 2, 2, 60000, 128), 40
     elif case == "tokens":
         c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
         c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
