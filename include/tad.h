@@ -208,6 +208,23 @@ int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                tad_tensor *out, hipStream_t stream);
 
 /*
+ * Split + merge without a workspace argument and without allocating: for callers that
+ * cannot allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid it).  Arguments, result and errors as tad_decode; the output
+ * is bit-identical to tad_decode_ws with the same n_splits.  The partials and counters
+ * live in a 16 MiB device array inside the library, one copy per device, held until
+ * the process ends; its counters are cleared by a kernel on `stream` at the first call
+ * on a device.  A call whose partials need more than 16 MiB - 256 KiB
+ * (tad_workspace_bytes) or more than 65536 counters fails with TAD_EWORKSPACE before
+ * anything is launched.  Every call on a device shares that array: calls that overlap
+ * on one device (different streams without ordering between them, or host threads)
+ * race and give wrong results.
+ */
+int tad_decode_noalloc(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
+                       const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
+                       tad_tensor *out, hipStream_t stream);
+
+/*
  * Paged K/V cache.  The pages leave the K/V cache to the caller (SwitchHead README,
  * forward signature: the caller keeps the cache and hands it back each step); a
  * paged cache is the layout serving engines use for it: a shared pool of

@@ -5,6 +5,7 @@ behind the C ABI declared in ``include/tad.h``.  PyTorch supplies device memory 
 streams.  The functions carry the C names:
 
 - ``tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits, out, stream=None)``
+- ``tad_decode_noalloc(q, k, v, seq_lens, alibi_slopes, n_splits, out, stream=None)``
 - ``tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits, out, ws, stream=None)``
 - ``tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream=None)``
 - ``tad_combine(ws, B, Hq, nq, n_splits, d, out, stream=None)``
@@ -38,7 +39,7 @@ TAD_OK, TAD_EINVAL, TAD_EDTYPE, TAD_ELAYOUT, TAD_EUNSUPPORTED, TAD_EWORKSPACE, T
 
 EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_bytes",
            "tad_workspace_clear", "tad_split", "tad_combine", "tad_decode_ws", "tad_decode",
-           "tad_split_paged", "tad_decode_paged_ws", "tad_decode_paged")
+           "tad_decode_noalloc", "tad_split_paged", "tad_decode_paged_ws", "tad_decode_paged")
 
 
 class TadTensor(ctypes.Structure):
@@ -88,6 +89,8 @@ def load():
     lib.tad_decode_ws.argtypes = [P, P, P, vp, vp, i32, P, vp, sz, vp]
     lib.tad_decode.restype = ctypes.c_int
     lib.tad_decode.argtypes = [P, P, P, vp, vp, i32, P, vp]
+    lib.tad_decode_noalloc.restype = ctypes.c_int
+    lib.tad_decode_noalloc.argtypes = [P, P, P, vp, vp, i32, P, vp]
     PG = ctypes.POINTER(TadPagedKv)
     lib.tad_split_paged.restype = ctypes.c_int
     lib.tad_split_paged.argtypes = [P, P, P, PG, vp, vp, i32, vp, sz, vp]
@@ -205,6 +208,14 @@ def tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None,
     dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
     return _check(lib.tad_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                  _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
+
+
+def tad_decode_noalloc(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None, k_scale=None,
+                       v_scale=None) -> int:
+    lib = load()
+    dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
+    return _check(lib.tad_decode_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
+                                         _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
 
 
 def paged(block_table) -> TadPagedKv:

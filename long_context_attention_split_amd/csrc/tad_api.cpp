@@ -495,6 +495,75 @@ int decode_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, c
     return ok();
 }
 
+// ---- Scratch of tad_decode_noalloc: a file-scope device array, one copy per device
+// (HIP places a module's __device__ variables on every device that loads it; each
+// copy lives until the process ends).  Its first kScratchCounterBytes hold the arrival
+// counters, which must start at zero: they are cleared once per device, and every
+// call that completes leaves them zero.  The rest holds one call's partials, laid out
+// as a workspace (tad::ws_layout).  In host code `scratch` names a host-side stand-in,
+// not the device memory: only the address hipGetSymbolAddress returns for the current
+// device is ever passed on.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchCounterBytes = size_t(256) << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[64] = {nullptr};
+bool g_scratch_zeroed[64] = {false};
+
+// The current device's copy of `scratch` (looked up once per device), with its counters
+// cleared by a kernel on `stream` the first time.  A clear recorded into a stream that
+// is being captured only runs when the graph does, so it is repeated until one is
+// issued outside a capture.
+int scratch_of_device(hipStream_t stream, char **base) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TAD_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(TAD_EINVAL, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(TAD_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = (char *)p;
+    }
+    if (!g_scratch_zeroed[dev]) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return fail(TAD_EHIP, "hipStreamIsCapturing: %s", hipGetErrorString(e));
+        e = tad::launch_fill_zero((int32_t *)g_scratch_ptr[dev], (int64_t)(kScratchCounterBytes / 4), stream);
+        if (e != hipSuccess) return fail(TAD_EHIP, "scratch counter clear launch: %s", hipGetErrorString(e));
+        if (cs == hipStreamCaptureStatusNone) g_scratch_zeroed[dev] = true;
+    }
+    *base = g_scratch_ptr[dev];
+    return TAD_OK;
+}
+
+int decode_noalloc_impl(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
+                        const float *alibi_slopes, int32_t n_splits, tad_tensor *out, hipStream_t stream) {
+    Problem P;
+    int32_t S;
+    OutDesc od;
+    int rc;
+    if ((rc = prepare_decode(q, k, v, nullptr, n_splits, out, &P, &S, &od))) return rc;
+    const int64_t rows = P.B * P.Hq * P.nq;
+    const size_t need = tad::ws_layout(rows, S, P.d).total;
+    const int64_t counters = tad::ws_counters(rows, S, P.d);
+    if (need > kScratchBytes - kScratchCounterBytes || counters > (int64_t)(kScratchCounterBytes / 4))
+        return fail(TAD_EWORKSPACE,
+                    "tad_decode_noalloc: this call needs %zu bytes of partials and %lld counters; the scratch "
+                    "holds %zu bytes and %zu counters (use tad_decode_ws with a workspace)",
+                    need, (long long)counters, kScratchBytes - kScratchCounterBytes, kScratchCounterBytes / 4);
+    if (P.B == 0) return ok();
+    char *base = nullptr;
+    if ((rc = scratch_of_device(stream, &base))) return rc;
+    WsPtrs w;
+    carve_at(base + kScratchCounterBytes, rows, S, P.d, (int32_t *)base, &w);
+    if ((rc = run_decode(P, q, k, v, seq_lens, alibi_slopes, S, w, od, stream))) return rc;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -570,6 +639,11 @@ int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
 int tad_decode(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
                const float *alibi_slopes, int32_t n_splits, tad_tensor *out, hipStream_t stream) {
     return decode_impl(q, k, v, nullptr, seq_lens, alibi_slopes, n_splits, out, stream);
+}
+
+int tad_decode_noalloc(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v, const int32_t *seq_lens,
+                       const float *alibi_slopes, int32_t n_splits, tad_tensor *out, hipStream_t stream) {
+    return decode_noalloc_impl(q, k, v, seq_lens, alibi_slopes, n_splits, out, stream);
 }
 
 int tad_decode_paged_ws(const tad_tensor *q, const tad_tensor *k_cache, const tad_tensor *v_cache,

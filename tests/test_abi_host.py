@@ -319,3 +319,21 @@ def test_product_does_not_reach_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
 
+
+def test_noalloc_refuses_calls_beyond_its_scratch(lib):
+    """tad_decode_noalloc holds at most 16 MiB - 256 KiB of partials: a call needing more
+    fails with TAD_EWORKSPACE before any device work (64 heads x 100 chunks x d 512 is
+    about 26 MB of partials).  Bad arguments get the codes tad_decode gives."""
+    so = lib.load()
+    big = good(B=2, Hq=64, Hkv=64, L=1000, d=512)
+    call = lambda a, S: so.tad_decode_noalloc(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                                              None, None, S, ctypes.byref(a["out"]), None)
+    assert call(big, 100) == tad.TAD_EWORKSPACE
+    assert "16" in lib.tad_last_error() or "scratch" in lib.tad_last_error()
+    bad = good()
+    bad["k"] = desc([2, 2, 100, 128], addr=0)
+    assert call(bad, 4) == tad.TAD_EINVAL
+    bad = good()
+    bad["out"] = desc([2, 8, 128], tad.TAD_BF16)
+    assert call(bad, 4) == tad.TAD_EDTYPE
+    assert call(good(), 5000) == tad.TAD_EINVAL                         # n_splits beyond the maximum
