@@ -130,9 +130,7 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e];
  *                 left unwritten for an empty chunk (tad_combine ignores the o of a
  *                 chunk whose weight is 0, whatever it holds)
- *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws),
- *                 followed, when B * Hq * nq * n_splits < 256, by ccnt[r], int32
- *                 arrival counters of the chunks' pieces (below)
+ *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws)
  *     sub_m, sub_l, sub_o: when B * Hq * nq * n_splits < 256, the partials of up to
  *                 Pmax = min(512 / (B * Hq * nq * n_splits), 16384 / d, 64) pieces per
  *                 chunk, same meaning as m, l, o for a piece of the chunk
@@ -143,11 +141,11 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  * (one head cut into 8 chunks is 8 work-groups), so where the vector kernel serves one
  * query row per KV head, each chunk of at least 256 KiB of K+V is read by up to Pmax
  * work-groups, each a contiguous piece of ceil(c / P) keys (whole pages for a paged
- * cache) with P = min(Pmax, chunk bytes / 128 KiB), and the last of them to finish
- * merges the pieces' partials into the chunk's (m, l, o) by the same rescale-and-sum.
- * The chunks themselves, and so the partials tad_split reports, are those n_splits
- * asks for; only their rounding differs from an uncut chunk.  P depends on the call's
- * sizes only, so every entry point cuts a call the same way.
+ * cache) with P = min(Pmax, chunk bytes / 128 KiB); a second kernel then merges each
+ * chunk's pieces into the chunk's (m, l, o) by the same rescale-and-sum.  The chunks
+ * themselves, and so the partials tad_split reports, are those n_splits asks for; only
+ * their rounding differs from an uncut chunk.  P depends on the call's sizes only, so
+ * every entry point cuts a call the same way.
  */
 size_t tad_workspace_bytes(int32_t B, int32_t Hq, int32_t nq, int32_t n_splits, int32_t d);
 
@@ -160,9 +158,8 @@ int tad_workspace_clear(void *ws, size_t ws_bytes, hipStream_t stream);
 /*
  * Split step: every (b, query head, chunk) partial (m, l, o) into `ws` (layout above).
  * n_splits must be >= 1 here (use tad_auto_splits to pick one).  `ws` is a device
- * buffer of at least tad_workspace_bytes(B, Hq, nq, n_splits, d) bytes, 256-byte aligned,
- * whose counters are zero (as for tad_decode_ws: chunks cut into pieces count their
- * pieces there; every call that completes leaves them zero).
+ * buffer of at least tad_workspace_bytes(B, Hq, nq, n_splits, d) bytes, 256-byte aligned.
+ * Chunks read as pieces (above) take a second launch that merges them.
  */
 int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
               const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
@@ -179,20 +176,20 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
 
 /*
  * Split + merge with a caller-provided workspace (no allocation).  Small problems
- * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 8)
- * read by the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d]
- * caches, and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512,
- * more than 16 query rows per KV head) run as ONE launch: each split work-group
- * writes its partial, and the last one of a row to finish (counted in the
- * workspace's cnt array) merges the row, then returns its counter to zero.  Larger
- * problems, grouped-query heads on the matrix cores and caches whose KV heads are
- * interleaved per key with one query head per KV head run the split and combine
- * kernels back to back (the counters are then unused).
- * Either way the output is bit-identical to
+ * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 8) read
+ * by the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d] caches,
+ * and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512, more than
+ * 16 query rows per KV head) and not cut into pieces run as ONE launch: each split
+ * work-group writes its partial, and the last one of a row to finish (counted in the
+ * workspace's cnt array with agent-scope acquire-release updates) merges the row, then
+ * returns its counter to zero.  Larger problems, grouped-query heads on the matrix
+ * cores, chunks read as pieces and caches whose KV heads are interleaved per key with
+ * one query head per KV head run the split (and pieces) and combine kernels back to
+ * back (the counters are then unused).  Either way the output is bit-identical to
  * tad_split followed by tad_combine.  The counters must be zero the first time a
- * workspace is used (tad_workspace_clear, or memory allocated zeroed); every call
- * that runs to completion leaves them zero, so a workspace can be reused call after
- * call.  Calls that share one workspace must not overlap.
+ * workspace is used (tad_workspace_clear, or memory allocated zeroed); every call that
+ * runs to completion leaves them zero, so a workspace can be reused call after call.
+ * Calls that share one workspace must not overlap.
  */
 int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                   const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,

@@ -43,6 +43,31 @@ hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Pre-merge of chunks read as pieces: work-group r merges chunk r's P piece partials
+// into the chunk's (m, l, o) with merge_pieces (merge.h), so that the workspace then
+// holds exactly the n_splits chunk partials the caller asked for.  A kernel of its own
+// after the split kernel: the pieces' partials are complete and visible when it starts.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void pieces_kernel(PiecesArgs a) {
+    __shared__ float lds[64 + kCombineThreads];
+    const int64_t r = blockIdx.x;                // (row, chunk)
+    merge_pieces<D, kCombineThreads>(a.sub_m + r * a.P, a.sub_l + r * a.P, a.sub_o + r * a.P * D, a.P,
+                                     a.ws_m + r, a.ws_l + r, a.ws_o + r * D, lds);
+}
+
+hipError_t launch_pieces(const PiecesArgs &a, int d, hipStream_t st) {
+    if (a.chunks <= 0) return hipSuccess;
+    if (a.P < 1 || a.P > 64 || a.P * d > 16384) return hipErrorInvalidValue;
+    switch (d) {
+        case 64: hipLaunchKernelGGL(pieces_kernel<64>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
+        case 128: hipLaunchKernelGGL(pieces_kernel<128>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
+        case 256: hipLaunchKernelGGL(pieces_kernel<256>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
+        case 512: hipLaunchKernelGGL(pieces_kernel<512>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // Zero-fill of the workspace's arrival counters (a kernel rather than a memset so that
 // it can sit inside a captured graph).
 __global__ void fill_zero_kernel(int32_t *p, int64_t n) {

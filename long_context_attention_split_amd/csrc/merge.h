@@ -63,13 +63,13 @@ __device__ __forceinline__ void reset_counter(int32_t *cnt) {
 }
 
 // Pre-merge of one chunk's P pieces (m_p in base 2, l_p, o_p[D], written by P
-// work-groups) into the chunk's own partial: M = max_p m_p, w_p = 2^(m_p - M),
+// work-groups of the split kernel, read here in a later kernel) into the chunk's own
+// partial: M = max_p m_p, w_p = 2^(m_p - M),
 // l = sum_p w_p l_p, o = sum_p w_p o_p -- the same rescale-and-sum as the row merge,
 // without the division, since the result is a partial again.  Fixed order: each of
 // the TPC thread parts of a column sums its pieces p in order, and the parts are added
 // in order; l is a wave sum over the pieces.  All P * D values are loaded in one round
 // (at most 64 per thread).  Called by all NT threads; `lds` holds 64 + NT floats.
-// Results are stored with store_partial (another work-group may merge them next).
 template <int D, int NT>
 __device__ __forceinline__ void merge_pieces(const float *m, const float *l, const float *o, int P, float *cm,
                                              float *cl, float *co, float *lds) {
@@ -91,10 +91,10 @@ __device__ __forceinline__ void merge_pieces(const float *m, const float *l, con
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = part * PPT + i;
-            v[c][i] = p < P ? load_partial<true>(o + (int64_t)p * D + col0 + c * NT) : 0.f;
+            v[c][i] = p < P ? o[(int64_t)p * D + col0 + c * NT] : 0.f;
         }
-    const float mp = lane < P ? load_partial<true>(m + lane) : kNegInf;
-    const float lp = lane < P ? load_partial<true>(l + lane) : 0.f;
+    const float mp = lane < P ? m[lane] : kNegInf;
+    const float lp = lane < P ? l[lane] : 0.f;
     const float M = wave_max(mp);
     const float Mu = (M == kNegInf) ? 0.f : M;
     const float wp = lane < P ? exp2_fast(mp - Mu) : 0.f;
@@ -110,7 +110,7 @@ __device__ __forceinline__ void merge_pieces(const float *m, const float *l, con
             if (p < P) acc = add_weighted(w[p], v[c][i], acc);
         }
         if constexpr (TPC == 1) {
-            store_partial(co + col0 + c * NT, acc);
+            co[col0 + c * NT] = acc;
         } else {
             sums[tid] = acc;
         }
@@ -121,12 +121,12 @@ __device__ __forceinline__ void merge_pieces(const float *m, const float *l, con
             float t = 0.f;
 #pragma unroll
             for (int k = 0; k < TPC; ++k) t += sums[k * D + tid];
-            store_partial(co + tid, t);
+            co[tid] = t;
         }
     }
     if (tid == 0) {
-        store_partial(cm, M);
-        store_partial(cl, lsum);
+        *cm = M;
+        *cl = lsum;
     }
 }
 

@@ -44,9 +44,8 @@ namespace tad {
 // PAGED: K/V rows come from a paged cache through the block table; every wave tile
 // then lies inside one page (tile length divides the page size) and gets its own
 // buffer resource.
-// TAIL: the variant whose work-groups may also merge -- the pieces of a chunk (a.P > 1)
-// and/or a whole row (a.fused) -- kept apart so that the plain kernel carries none of
-// that code or its registers.
+// TAIL: the variant whose last work-group of a row also merges the row (a.fused), kept
+// apart so that the plain kernel carries none of that code or its registers.
 template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PAGED = false,
           bool TAIL = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
@@ -76,10 +75,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const int gq = a.group * a.nq;                        // rows per KV head
     if (gq == 1) {
         int id = blockIdx.x;
-        if constexpr (TAIL) {
-            p = id % a.P;
-            id /= a.P;
-        }
+        p = id % a.P;
+        id /= a.P;
         s = id % S;
         const int row = id / S;
         b = row / a.Hq;
@@ -104,7 +101,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     // from here on the row is single-token decode over its first L keys.
     const int cfull = batch_chunk_len(a);
     ChunkRange cr = chunk_of(row_len(a, b), s, cfull);
-    if (TAIL && a.P > 1) {
+    if (a.P > 1) {
         const int cs = sub_chunk_len(a, cfull);
         const int pj0 = (int)min((int64_t)cr.j0 + (int64_t)p * cs, (int64_t)cr.j1);
         cr.j1 = min(pj0 + cs, cr.j1);
@@ -244,10 +241,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const int64_t row = ((int64_t)b * a.Hq + h) * a.nq + t;
     const int64_t r = row * S + s;
     const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // V dequantisation
-    // Where this work-group's partial goes: the chunk's slot, or piece p's slot.  A
-    // partial that another work-group of this kernel merges is written through to the
-    // device coherence point (store_partial).
-    const bool piece = TAIL && a.P > 1;
+    // Where this work-group's partial goes: the chunk's slot, or piece p's slot (a later
+    // kernel merges the pieces).  A partial that another work-group of this kernel
+    // merges (fused) is written through to the device coherence point (store_partial).
+    const bool piece = a.P > 1;
     const int64_t rp = r * a.P + p;
     float *const pm = piece ? a.sub_m + rp : a.ws_m + r;
     float *const pl = piece ? a.sub_l + rp : a.ws_l + r;
@@ -274,19 +271,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     }
 
     if constexpr (TAIL) {
-        static_assert(SLOTS * D >= kMaxFusedSplits + kMergeThreads && SLOTS * D >= 64 + kSplitThreads,
-                      "merge scratch fits in lds_o");
+        static_assert(SLOTS * D >= kMaxFusedSplits + kMergeThreads, "merge scratch fits in lds_o");
         __shared__ int last;
-        // ---- pieces: the last of the chunk's P work-groups merges them into the chunk's
-        // partial.
-        if (piece) {
-            if (!arrive_last(&a.ccnt[r], a.P, &last)) return;
-            merge_pieces<D, kSplitThreads>(a.sub_m + r * a.P, a.sub_l + r * a.P, a.sub_o + r * a.P * D, a.P,
-                                           a.ws_m + r, a.ws_l + r, a.ws_o + r * D, &lds_o[0][0]);
-            reset_counter(&a.ccnt[r]);
-        }
-        // ---- fused merge: the last of the row's S chunks to be complete merges the row.
-        if (a.fused && arrive_last(&a.cnt[row], S, &last)) {
+        // ---- fused merge: the last of the row's S work-groups to finish merges the row.
+        if (arrive_last(&a.cnt[row], S, &last)) {
             merge_row<D, true>(a.ws_m + row * S, a.ws_l + row * S, a.ws_o + row * S * D, S,
                                a.out + (int64_t)b * a.sob + (int64_t)h * a.soh + (int64_t)t * a.sot,
                                &lds_o[0][0]);
@@ -334,7 +322,8 @@ static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
         grid = (units + 7) / 8 * 8 * gq;
     }
     if (grid <= 0) return hipSuccess;
-    if (a.fused || a.P > 1) return launch_tail<D, KVT, true>(a, grid, st);
+    if (a.fused && a.P > 1) return hipErrorInvalidValue;   // pieces merge in their own kernel
+    if (a.fused) return launch_tail<D, KVT, true>(a, grid, st);
     return launch_tail<D, KVT, false>(a, grid, st);
 }
 

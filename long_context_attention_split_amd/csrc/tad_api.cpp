@@ -269,11 +269,11 @@ int32_t auto_splits_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t nq, int64_t 
     return (int32_t)S;
 }
 
-// Device arrays of one call: the partials (m, l, o), the arrival counters (cnt per row,
-// ccnt per chunk), and the pieces' partials (sub_*), which exist when Pmax > 1.
+// Device arrays of one call: the partials (m, l, o), the arrival counters of the fused
+// merge (cnt, one per row), and the pieces' partials (sub_*), which exist when Pmax > 1.
 struct WsPtrs {
     float *m, *l, *o;
-    int32_t *cnt, *ccnt;
+    int32_t *cnt;
     float *sm, *sl, *so;
     int Pmax;
 };
@@ -287,7 +287,6 @@ void carve_at(char *base, int64_t rows, int64_t S, int64_t d, int32_t *counters,
     p->l = (float *)(base + L.off_l);
     p->o = (float *)(base + L.off_o);
     p->cnt = counters ? counters : (int32_t *)(base + L.off_cnt);
-    p->ccnt = p->cnt + rows;
     p->sm = (float *)(base + L.off_sm);
     p->sl = (float *)(base + L.off_sl);
     p->so = (float *)(base + L.off_so);
@@ -352,7 +351,6 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
     a.out = out.data;
     a.sob = out.sob; a.soh = out.soh; a.sot = out.sot;
     a.P = 1;
-    a.ccnt = w.ccnt;
     a.sub_m = w.sm; a.sub_l = w.sl; a.sub_o = w.so;
     // pieces: only where the vector kernel runs with one query row per KV head
     if (a.group * a.nq == 1 && !tad::split_mfma_supported((int)P.d, a.kv_type, a.group, a.nq) &&
@@ -365,7 +363,8 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
 // Launch the split kernel.  Kernel choice: query-head groups and several tokens on the
 // matrix cores; caches whose heads are interleaved per key (one query head per KV
 // head, unfused) on the head-packed vector kernel; everything else on the vector
-// kernel.
+// kernel.  Chunks read as pieces (a.P > 1) are then pre-merged by pieces_kernel, so the
+// workspace holds the chunk partials when the launches are done.
 int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream) {
     hipError_t e;
     if (tad::split_mfma_supported((int)d, a.kv_type, a.group, a.nq))
@@ -375,6 +374,15 @@ int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream) {
     else
         e = tad::launch_split_valu(a, (int)d, stream);
     if (e != hipSuccess) return fail(TAD_EHIP, "split kernel launch: %s", hipGetErrorString(e));
+    if (a.P > 1) {
+        tad::PiecesArgs pa;
+        pa.sub_m = a.sub_m; pa.sub_l = a.sub_l; pa.sub_o = a.sub_o;
+        pa.ws_m = a.ws_m; pa.ws_l = a.ws_l; pa.ws_o = a.ws_o;
+        pa.chunks = (int64_t)a.B * a.Hq * a.nq * a.S;
+        pa.P = a.P;
+        e = tad::launch_pieces(pa, (int)d, stream);
+        if (e != hipSuccess) return fail(TAD_EHIP, "pieces kernel launch: %s", hipGetErrorString(e));
+    }
     return TAD_OK;
 }
 
@@ -412,7 +420,7 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
     const tad::SplitArgs unfused = split_args(P, q, k, v, seq_lens, slopes, S, w, OutDesc());
     const bool vector_kernel = !tad::split_mfma_supported((int)P.d, unfused.kv_type, unfused.group, unfused.nq) &&
                                !tad::split_heads_supported(unfused, (int)P.d);
-    if (vector_kernel && S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus)
+    if (vector_kernel && unfused.P == 1 && S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus)
         return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
     if ((rc = launch_split(unfused, P.d, stream))) return rc;
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);

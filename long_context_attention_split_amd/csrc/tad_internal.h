@@ -39,14 +39,20 @@ struct SplitArgs {
     int32_t *cnt;           // [B * Hq * nq] arrival counters
     float *out;             // [B, Hq, nq, d] fp32
     int64_t sob, soh, sot;  // out element strides
-    // Sub-chunks (vector kernel, one query row per KV head): with P > 1 every chunk is
-    // read by P work-groups, piece p holding keys [p * cs, (p + 1) * cs) of the chunk
-    // (cs = sub_chunk_len), and the last of the P to finish (counted in ccnt) merges
-    // their partials (sub_m, sub_l, sub_o) into the chunk's (m, l, o).  ccnt must be
-    // zero on entry and is left zero.
+    // Pieces (vector kernel, one query row per KV head): with P > 1 every chunk is read
+    // by P work-groups, piece p holding keys [p * cs, (p + 1) * cs) of the chunk (cs =
+    // sub_chunk_len), each writing its partial to sub_m, sub_l, sub_o at index
+    // (row * S + s) * P + p; pieces_kernel then merges them into the chunk's (m, l, o).
     int32_t P;
-    int32_t *ccnt;          // [B * Hq * nq * S] arrival counters per chunk
     float *sub_m, *sub_l, *sub_o;   // [rows * S * P], the same, [rows * S * P * d]
+};
+
+// Pre-merge of the pieces of `chunks` chunks, P pieces each (see SplitArgs).
+struct PiecesArgs {
+    const float *sub_m, *sub_l, *sub_o;
+    float *ws_m, *ws_l, *ws_o;
+    int64_t chunks;
+    int32_t P;
 };
 
 struct CombineArgs {
@@ -338,11 +344,11 @@ inline int max_sub_splits(int64_t rows, int64_t S, int64_t d) {
     return P < 1 ? 1 : (int)P;
 }
 
-// m, l, o (tad.h), then the arrival counters -- cnt [rows], followed, when chunks may be
-// cut into pieces, by ccnt [rows * S] -- then the pieces' partials sub_m, sub_l
-// [rows * S * Pmax] and sub_o [rows * S * Pmax * d].
+// m, l, o (tad.h), then the arrival counters cnt [rows], then, when chunks may be cut
+// into pieces, the pieces' partials sub_m, sub_l [rows * S * Pmax] and sub_o
+// [rows * S * Pmax * d].
 struct WsLayout {
-    size_t off_m, off_l, off_o, off_cnt, off_ccnt, off_sm, off_sl, off_so, total;
+    size_t off_m, off_l, off_o, off_cnt, off_sm, off_sl, off_so, total;
     int Pmax;
 };
 
@@ -355,18 +361,15 @@ inline WsLayout ws_layout(int64_t rows, int64_t S, int64_t d) {
     w.off_l = align256(n * sizeof(float));
     w.off_o = w.off_l + align256(n * sizeof(float));
     w.off_cnt = w.off_o + align256(n * size_t(d) * sizeof(float));
-    w.off_ccnt = w.off_cnt + size_t(rows) * sizeof(int32_t);
-    w.off_sm = w.off_cnt + align256((size_t(rows) + (np ? n : 0)) * sizeof(int32_t));
+    w.off_sm = w.off_cnt + align256(size_t(rows) * sizeof(int32_t));
     w.off_sl = w.off_sm + align256(np * sizeof(float));
     w.off_so = w.off_sl + align256(np * sizeof(float));
     w.total = w.off_so + align256(np * size_t(d) * sizeof(float));
     return w;
 }
 
-// Arrival counters of a workspace: cnt and ccnt, contiguous from off_cnt.
-inline int64_t ws_counters(int64_t rows, int64_t S, int64_t d) {
-    return rows + (max_sub_splits(rows, S, d) > 1 ? rows * S : 0);
-}
+// Arrival counters of a workspace (cnt, from off_cnt).
+inline int64_t ws_counters(int64_t rows, int64_t, int64_t) { return rows; }
 
 // Launchers (defined next to their kernels).  Return the hipError_t of the launch.
 hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t s);
@@ -376,6 +379,7 @@ hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 bool split_heads_supported(const SplitArgs &a, int d);
 hipError_t launch_split_heads(const SplitArgs &a, int d, hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
+hipError_t launch_pieces(const PiecesArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);
 
 // Keys per work-group tile of the VALU split kernel (for tests of the host logic).

@@ -43,13 +43,13 @@ def test_workspace_bytes_layout(lib):
     assert lib.tad_workspace_bytes(1, 32, 1, 32, 128) == 2 * 4096 + 1024 * 128 * 4 + 256
     assert lib.tad_workspace_bytes(8, 32, 1, 16, 128) == 2 * 16384 + 4096 * 128 * 4 + 1024
     assert lib.tad_workspace_bytes(1, 32, 4, 32, 128) == 2 * 16384 + 4096 * 128 * 4 + 512   # 4 tokens
-    # fewer than 256 (row, chunk) pairs: chunk counters after cnt, then the partials of
+    # fewer than 256 (row, chunk) pairs: after cnt, the partials of
     # Pmax = min(512 / pairs, 16384 / d, 64) pieces per chunk
     # one d = 512 head in 8 chunks: Pmax 32
     assert lib.tad_workspace_bytes(1, 1, 1, 8, 512) == (2 * 256 + 8 * 512 * 4 + 256 + 2 * 1024
                                                         + 8 * 32 * 512 * 4)
-    # 32 heads in 4 chunks (128 pairs): Pmax 4; 32 + 128 counters
-    assert lib.tad_workspace_bytes(1, 32, 1, 4, 128) == (2 * 512 + 128 * 128 * 4 + 768 + 2 * 2048
+    # 32 heads in 4 chunks (128 pairs): Pmax 4
+    assert lib.tad_workspace_bytes(1, 32, 1, 4, 128) == (2 * 512 + 128 * 128 * 4 + 256 + 2 * 2048
                                                          + 512 * 128 * 4)
     assert lib.tad_workspace_bytes(0, 1, 1, 1, 64) == 0
     assert lib.tad_workspace_bytes(1, 1, 1, 0, 64) == 0
