@@ -2,22 +2,29 @@
 """Benchmark: split-KV exact decode on one MI355X, 128k-token MHA workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--splits S] [--page-size P] [--tokens N]
+    python bench.py --all [--steps K]
 
-One step = one full decode over the workload's inputs, already resident in HBM:
-the split kernel then the combine kernel (tad_split + tad_combine, which is what
-tad_decode_ws runs at this size); with --page-size the K/V are first copied into
-a paged cache (a permuted page pool, workloads.page_kv) and the split step is
-tad_split_paged.  W untimed steps, then K timed steps between two
-device synchronisations.  Rank 0 prints one JSON line with:
+One step = one full decode over the workload's inputs, already resident in HBM,
+through the public entry point tad_decode_ws (which runs the split kernel and then
+the combine kernel at this size, or one fused launch on small problems); with
+--page-size the K/V are first copied into a paged cache (a permuted page pool,
+workloads.page_kv) and the step is tad_decode_paged_ws.  W untimed steps, then K
+timed steps between two device synchronisations.  Rank 0 prints one JSON line with:
 
 - value: KV-read throughput in GB/s (algorithmic K+V bytes / step time),
 - ms_per_step and decode_step_us,
 - roofline: the split kernel's algorithmic bytes per launch / its mean duration,
-  timed with events recorded on the launch stream around every timed launch,
-  against the 8 TB/s HBM peak; traffic = HBM bytes per launch measured by
+  from K more split launches (tad_split) each bracketed by events on the launch
+  stream, against the 8 TB/s HBM peak; traffic = HBM bytes per launch measured by
   rocprofv3 counters when the committed measurement matches the current kernel
   source (else null),
 - cpu_baseline: the fp64 oracle timed on this host's cores over the same workload.
+
+--all instead prints one record per workload (1-7): the median over K steps of
+tad_decode_ws, each timed with events after 512 MiB of scratch has been written
+(so no K/V stays in the caches), the split kernel's median the same way, parity
+against the fp64 oracle (max-abs, rel-L2, the acceptance bar), the oracle's time,
+the host's CPU model and cores, the device's compute units and the seed.
 
 Only one GPU is used: the decode of one sequence is split across the compute units
 of a single device, so --gpus above 1 is refused.
@@ -205,12 +212,162 @@ def read_stream_probe(k, v, stream, reps: int = 10):
     return total / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def host_info():
+    """CPU model and usable cores of this host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def load_inputs(args, wid, dev):
+    """Workload ``wid`` on the device, with its step functions.  Returns a dict."""
+    import torch
+    import long_context_attention_split_amd as tad
+    import workloads as W
+    w = W.WORKLOADS[wid]
+    t_gen = time.perf_counter()
+    c = W.make_workload(wid)
+    print("[bench] workload %d generated in %.1fs" % (wid, time.perf_counter() - t_gen), file=sys.stderr, flush=True)
+    if args.tokens > 1:                    # same K/V, nq query tokens per (row, head)
+        B0, Hq0, d0 = c["q"].shape
+        c["q"] = W.draw_q(1000 * wid + 6, B0, Hq0 * args.tokens, d0).view(B0, Hq0, args.tokens, d0)
+    nq = args.tokens
+    q = c["q"].to(dev)
+    table = None
+    if args.page_size:
+        kc, vc, table = W.page_kv(c["k"], c["v"], args.page_size, 1000 * wid, head_major=args.head_major_pages)
+        k, v, table = kc.to(dev), vc.to(dev), table.to(dev)
+        del kc, vc
+    elif args.token_major:
+        k = c["k"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+        v = c["v"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    else:
+        k = c["k"].to(dev)
+        v = c["v"].to(dev)
+    sl = c["seq_lens"].to(dev) if c["seq_lens"] is not None else None
+    sp = c["slopes"].to(dev) if c["slopes"] is not None else None
+    ks = c["k_scale"].to(dev) if c["k_scale"] is not None else None
+    vs = c["v_scale"].to(dev) if c["v_scale"] is not None else None
+    B, Hq, Hkv, Lmax, d = tad.shape_of(c["q"], c["k"])
+    if args.splits > 0:
+        S = args.splits
+    elif c["n_splits"] > 0:
+        S = c["n_splits"]
+    else:                                  # what tad_decode_ws picks
+        S = tad.tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, w.kv_dtype)
+    ws = tad.workspace(q, c["k"], S)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def decode():
+        if table is not None:
+            tad.tad_decode_paged_ws(q, k, v, table, sl, sp, S, out, ws, stream, ks, vs)
+        else:
+            tad.tad_decode_ws(q, k, v, sl, sp, S, out, ws, stream, ks, vs)
+
+    def split():
+        if table is not None:
+            tad.tad_split_paged(q, k, v, table, sl, sp, S, ws, stream, ks, vs)
+        else:
+            tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
+
+    return dict(w=w, c=c, q=q, k=k, v=v, out=out, ws=ws, S=S, nq=nq, B=B, Hq=Hq, Hkv=Hkv, Lmax=Lmax, d=d,
+                stream=stream, decode=decode, split=split, kv_bytes=w.kv_bytes(c["seq_lens"]))
+
+
+def time_flushed(fn, stream, reps, scratch):
+    """Per-call milliseconds of fn (events on `stream`), scratch written before each call."""
+    import torch
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+    for i in range(reps):
+        if scratch is not None:
+            scratch.fill_(float(i))
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def run_all(args, dev) -> int:
+    """One JSON record per workload: flushed median step and split times, parity."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    cpu_model, cores = host_info()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev)     # 512 MiB
+    oracle.build(force=False)
+    for wid in sorted(W.WORKLOADS):
+        x = load_inputs(args, wid, dev)
+        for _ in range(args.warmup):
+            x["decode"]()
+        torch.cuda.synchronize()
+        step_ms = time_flushed(x["decode"], x["stream"], args.steps, scratch)
+        split_ms = time_flushed(x["split"], x["stream"], args.steps, scratch)
+        x["decode"]()
+        torch.cuda.synchronize()
+        got = x["out"].cpu().double().numpy()
+        c = x["c"]
+        threads = min(cores, x["B"] * x["Hq"])
+        t0 = time.perf_counter()
+        ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                                n_threads=threads, k_scale=c["k_scale"], v_scale=c["v_scale"])
+        oracle_s = time.perf_counter() - t0
+        # max |V| over the valid keys, in real units, one (b, KV head) slab at a time
+        vmax = 0.0
+        for b in range(x["B"]):
+            Lb = int(c["seq_lens"][b]) if c["seq_lens"] is not None else x["Lmax"]
+            for h in range(x["Hkv"]):
+                if Lb > 0:
+                    a = float(c["v"][b, h, :Lb].float().abs().max())
+                    vmax = max(vmax, a * (float(c["v_scale"][b, h]) if c["v_scale"] is not None else 1.0))
+        tol = 1e-5 if x["w"].kv_dtype == torch.float32 else 2e-3 * vmax
+        err = np.abs(got - ref)
+        rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        us = float(np.median(step_ms)) * 1e3
+        sus = float(np.median(split_ms)) * 1e3
+        rec = {
+            "metric": METRIC, "record": "per-workload",
+            "workload": wid, "config": {"workload": x["w"].name, "B": x["B"], "Hq": x["Hq"], "Hkv": x["Hkv"],
+                                         "d": x["d"], "L": x["Lmax"], "tokens": x["nq"], "n_splits": x["S"],
+                                         "kv_bytes_per_step": x["kv_bytes"]},
+            "decode_step_us_median": round(us, 2),
+            "decode_step_us_min": round(min(step_ms) * 1e3, 2),
+            "gbs": round(x["kv_bytes"] / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100.0 * x["kv_bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "split_kernel_us_median": round(sus, 2),
+            "roofline_frac_split_events": round(x["kv_bytes"] / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "tad_decode_ws and tad_split each timed with events, median of %d calls, 512 MiB "
+                      "written before each call" % args.steps,
+            "parity": {"max_abs": float(err.max()), "rel_l2": rel, "tolerance_max_abs": tol,
+                       "ok": bool(err.max() <= tol)},
+            "oracle": {"seconds": round(oracle_s, 3), "threads": threads, "kind": "fp64 C oracle, whole workload"},
+            "host": {"cpu_model": cpu_model, "cores": cores}, "device": {"compute_units": cus},
+            "seed": 1000 * wid,
+            "roofline_claim": wid != 1,
+        }
+        print(json.dumps(rec), flush=True)
+        del x, got, ref, c
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--all", action="store_true", help="one record per workload (1-7) instead of the bench line")
     ap.add_argument("--splits", type=int, default=0, help="chunks per head (0: automatic)")
     ap.add_argument("--page-size", type=int, default=0,
                     help="read K/V from a paged cache with pages of this many rows (0: contiguous)")
@@ -238,96 +395,42 @@ def main(argv=None) -> int:
 
     import torch
     import long_context_attention_split_amd as tad
-    import workloads as W
 
     tad.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.all:
+        return run_all(args, dev)
     probe = copy_probe(dev) if args.copy_probe else None
-    w = W.WORKLOADS[args.workload]
-    t_gen = time.perf_counter()
-    c = W.make_workload(args.workload)
-    print("[bench] workload %d generated in %.1fs" % (args.workload, time.perf_counter() - t_gen),
-          file=sys.stderr, flush=True)
-    if args.tokens > 1:                    # same K/V, nq query tokens per (row, head)
-        B0, Hq0, d0 = c["q"].shape
-        c["q"] = W.draw_q(1000 * args.workload + 6, B0, Hq0 * args.tokens, d0).view(B0, Hq0, args.tokens, d0)
-    nq = args.tokens
-    q = c["q"].to(dev)
-    if args.page_size:
-        kc, vc, table = W.page_kv(c["k"], c["v"], args.page_size, 1000 * args.workload,
-                                  head_major=args.head_major_pages)
-        k, v, table = kc.to(dev), vc.to(dev), table.to(dev)
-        del kc, vc
-    elif args.token_major:
-        k = c["k"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
-        v = c["v"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
-    else:
-        k = c["k"].to(dev)
-        v = c["v"].to(dev)
-    sl = c["seq_lens"].to(dev) if c["seq_lens"] is not None else None
-    sp = c["slopes"].to(dev) if c["slopes"] is not None else None
-    ks = c["k_scale"].to(dev) if c["k_scale"] is not None else None
-    vs = c["v_scale"].to(dev) if c["v_scale"] is not None else None
-    B, Hq, Hkv, Lmax, d = tad.shape_of(c["q"], c["k"])
-    if args.splits > 0:
-        S = args.splits
-    elif c["n_splits"] > 0:
-        S = c["n_splits"]
-    else:                                  # what tad_decode_ws picks
-        S = tad.tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, w.kv_dtype)
-    ws = tad.workspace(q, c["k"], S)
-    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    kv_bytes = w.kv_bytes(c["seq_lens"])
-    stream = torch.cuda.current_stream()
+    x = load_inputs(args, args.workload, dev)
+    w, c, q, k, v, out, stream = x["w"], x["c"], x["q"], x["k"], x["v"], x["out"], x["stream"]
+    B, Hq, Hkv, Lmax, d, S, nq, kv_bytes = x["B"], x["Hq"], x["Hkv"], x["Lmax"], x["d"], x["S"], x["nq"], x["kv_bytes"]
 
-    # One step = tad_split then tad_combine (what tad_decode_ws runs at this size);
-    # events bracket the split launch, the dominant kernel.
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        if args.page_size:
-            tad.tad_split_paged(q, k, v, table, sl, sp, S, ws, stream, ks, vs)
-        else:
-            tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
-        if ev is not None:
-            ev[1].record(stream)
-        tad.tad_combine(ws, B, Hq, nq, S, d, out, stream)
-
+    # The step: tad_decode_ws (tad_decode_paged_ws), the entry point a caller uses.
     scratch = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) if args.flush_mib else None
     for i in range(args.warmup):
         if scratch is not None:
             scratch.fill_(-1.0 - i)
-        step()
+        x["decode"]()
     torch.cuda.synchronize()
-    evs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     if args.flush_mib:
-        # flushed steps: each step bracketed by its own events, a scratch write between
-        ends = [TimingEvent() for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            scratch.fill_(float(i))
-            step(evs[i])
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = sum(evs[i][0].elapsed_time(ends[i]) for i in range(args.steps)) / args.steps
+        ms_per_step = sum(time_flushed(x["decode"], stream, args.steps, scratch)) / args.steps
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(evs[i])
+            x["decode"]()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms_per_step = wall * 1e3 / args.steps
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # The dominant kernel alone: K more split launches (tad_split), each bracketed by
+    # events on the launch stream (flushed like the steps when --flush-mib is given).
+    split_ms = time_flushed(x["split"], stream, args.steps, scratch)
     del scratch
-    split_ms = [e[0].elapsed_time(e[1]) for e in evs]
     split_avg = sum(split_ms) / len(split_ms)
-    # outside the split brackets: the combine kernel and launch gaps
-    comb_avg = ms_per_step - split_avg
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     split_gbs = kv_bytes / (split_avg * 1e-3) / 1e9
-    print("[bench] step %.1f us (split kernel %.1f us, combine + gaps %.1f us), %.0f GB/s" %
-          (ms_per_step * 1e3, split_avg * 1e3, comb_avg * 1e3, gbs), file=sys.stderr, flush=True)
+    print("[bench] step %.1f us (split kernel alone %.1f us), %.0f GB/s" %
+          (ms_per_step * 1e3, split_avg * 1e3, gbs), file=sys.stderr, flush=True)
 
     traffic = read_traffic(args.workload, args.page_size, nq)
     kv_name = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8-e4m3",
@@ -352,6 +455,7 @@ def main(argv=None) -> int:
             "workload": w.name + (", %d query tokens per row" % nq if nq > 1 else ""),
             "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax, "tokens": nq,
             "n_splits": S, "kv_bytes_per_step": kv_bytes,
+            "step": "tad_decode_paged_ws" if args.page_size else "tad_decode_ws",
             "timing": ("per-step events, %d MiB scratch written between steps" % args.flush_mib
                        if args.flush_mib else "steps back to back, wall clock"),
             "kv_layout": ("paged, %d-row pages%s" % (args.page_size, ", head-major" if args.head_major_pages else ""))
@@ -359,7 +463,6 @@ def main(argv=None) -> int:
                                                  else "contiguous [B, H, L, d]"),
         },
         "split_kernel_us": round(split_avg * 1e3, 2),
-        "combine_and_gaps_us": round(comb_avg * 1e3, 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(split_gbs, 1),
@@ -369,6 +472,7 @@ def main(argv=None) -> int:
             "traffic": traffic,
             "kernel": "split (tad_split_paged)" if args.page_size else "split (tad_split)",
             "algorithmic_bytes_per_launch": kv_bytes,
+            "timing": "%d split launches after the steps, each bracketed by events on the launch stream" % args.steps,
         },
     }
     probe_gbs = read_stream_probe(k, v, stream)
@@ -380,13 +484,15 @@ def main(argv=None) -> int:
         result["roofline"]["frac_of_read_probe"] = round(split_gbs / probe_gbs, 4)
 
     if not args.no_cpu_baseline:
+        x["decode"]()
         torch.cuda.synchronize()
         gpu_out = out.cpu().double().numpy()
-        del q, k, v
+        del q, k, v, x
         torch.cuda.empty_cache()
         ref, dt, threads, n_rows, passes = cpu_baseline(c)
         import numpy as np
         err = float(np.abs(gpu_out - ref).max())
+        cpu_model, _ = host_info()
         result["cpu_baseline"] = {
             "value": round(kv_bytes / dt / 1e9, 3),
             "unit": "GB/s",
@@ -395,6 +501,7 @@ def main(argv=None) -> int:
             "sample": ("the whole workload (all %d (b, head) rows) per pass, fp64 C oracle, %d passes, "
                        "%.3f s wall per pass" % (n_rows, passes, dt)),
             "seconds_per_pass": round(dt, 4),
+            "cpu_model": cpu_model,
         }
         result["parity_max_abs_vs_oracle"] = err
     if probe is not None:
