@@ -158,7 +158,7 @@ __device__ __forceinline__ void wave_identity(const SplitArgs &a, const WorkItem
 // v_mfma_f32_16x16x32_bf16 over the 32 keys.
 template <int D, bool PAGED, int HG, int NWH, int KVT>
 __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int c, const int Lb,
-                                                uint4 *smem, float (*lds_ml)[HG * NWH][16]) {
+                                                uint4 *smem, float (*lds_ml)[HG * NWH][16], int *lds_cnt) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr bool F8 = KVT != kKvBF16;
     constexpr int ELEM = F8 ? 1 : 2;     // bytes per K/V element
@@ -172,9 +172,8 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     constexpr int TILE = TK * CH;        // 16-byte LDS slots per tile and tensor
     constexpr int NW = HG * NWH;         // waves per work-group
     constexpr int THREADS = 64 * NW;
-    constexpr int MAXG = 16;
     static_assert(RPI <= 16 && NLD % NSB == 0, "a load instruction stays inside one 16-row piece of a tile");
-    static_assert(NW * MAXG * D * 4 <= NW * 2 * TILE * 16, "merge area fits in the tile buffers");
+    static_assert(NB * 64 * 16 <= 2 * TILE * 16, "a wave's O fits in its tile buffers");
 
 
     const int lane = threadIdx.x & 63;
@@ -458,64 +457,66 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     if (alibi) run(std::true_type{});
     else run(std::false_type{});
 
-    // ---- merge the NW wave states per head through LDS (reusing the tile buffers).
-    // Each wave's columns are rows of D floats in its own MAXG * D slot; the 16-byte
-    // chunk k of row j is stored at chunk k ^ j (j < 16), so that the 16-byte stores of
-    // one column block (one per column, rows 512 bytes apart) land in 16 different
-    // bank groups, and the merge's reads of a row (64 consecutive floats) too.
-    __syncthreads();
-    float *const lds_o = reinterpret_cast<float *>(smem);  // [NW][MAXG][D], chunks swizzled per row
-    if (head_ok) {
-        float *const orow = lds_o + wave * (MAXG * D) + j16 * D;
+    // ---- merge the NWH wave states of each head.  Waves of rank > 0 put their state in
+    // LDS -- O in their own tile buffer, free now, as 16-byte pieces in lane order (no
+    // bank conflicts), and (m, l, mx) per column -- and every lane then adds 1 to
+    // lds_cnt[hx] with workgroup-scope release, publishing its own stores.  The rank-0
+    // wave of the head waits (acquire) until all 64 (NWH - 1) lanes have counted, not
+    // for the other heads' waves, merges the states in registers in rank order and
+    // stores the partial straight from its registers: per column, M = the largest
+    // running maximum, each wave's weight 2^(m_w - M) against its reference maximum m_w,
+    // l = sum_w weight_w l_w, o = sum_w weight_w O_w.
+    float4 *const mine = reinterpret_cast<float4 *>(bufA);   // NB * 64 pieces
+    if (wr > 0) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) orow[4 * ((4 * nb + c4) ^ j16) + r] = F8 ? O[nb][r] * vs : O[nb][r];
+        for (int nb = 0; nb < NB; ++nb) mine[nb * 64 + lane] = make_float4(O[nb][0], O[nb][1], O[nb][2], O[nb][3]);
         if (c4 == 0) {
             lds_ml[0][wave][j16] = m;
             lds_ml[1][wave][j16] = l;
             lds_ml[2][wave][j16] = mx;
         }
+        __hip_atomic_fetch_add(&lds_cnt[hx], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return;
     }
-    __syncthreads();
-    // Per column (head x, column hh), one thread: the exact chunk maximum M, each wave's
-    // weight 2^(m_w - M) (written over its reference m_w) and the denominator.
-    if (threadIdx.x < HG * gq) {
-        const int x = threadIdx.x / gq, hh = threadIdx.x % gq;
-        float M = kNegInf;
+    while (__hip_atomic_load(&lds_cnt[hx], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 64 * (NWH - 1))
+        __builtin_amdgcn_s_sleep(1);
+    float M = mx;
 #pragma unroll
-        for (int w = x * NWH; w < x * NWH + NWH; ++w) M = fmaxf(M, lds_ml[2][w][hh]);
-        const float Mu = (M == kNegInf) ? 0.f : M;
-        float lsum = 0.f;
+    for (int k = 1; k < NWH; ++k) M = fmaxf(M, lds_ml[2][wave + k][j16]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    const float w0 = exp2_fast(m - Mu);
+    float lsum = w0 * l;
 #pragma unroll
-        for (int w = x * NWH; w < x * NWH + NWH; ++w) {
-            const float sw = exp2_fast(lds_ml[0][w][hh] - Mu);
-            lds_ml[0][w][hh] = sw;
-            lsum = fmaf(sw, lds_ml[1][w][hh], lsum);
+    for (int nb = 0; nb < NB; ++nb) O[nb] *= w0;
+#pragma unroll
+    for (int k = 1; k < NWH; ++k) {
+        const float wk = exp2_fast(lds_ml[0][wave + k][j16] - Mu);
+        lsum = fmaf(wk, lds_ml[1][wave + k][j16], lsum);
+        const float4 *const other = reinterpret_cast<const float4 *>(bufA + k * 2 * TILE);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float4 t = other[nb * 64 + lane];
+            O[nb][0] = fmaf(wk, t.x, O[nb][0]);
+            O[nb][1] = fmaf(wk, t.y, O[nb][1]);
+            O[nb][2] = fmaf(wk, t.z, O[nb][2]);
+            O[nb][3] = fmaf(wk, t.w, O[nb][3]);
         }
-        const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;   // hh: column
-        a.ws_m[r] = M;
-        a.ws_l[r] = lsum;
     }
-    __syncthreads();
-    // Thread t handles element t % D of rows t / D, t / D + THREADS / D, ... (row = x * gq
-    // + hh); THREADS is a multiple of D >= 64, so a wave's row is uniform and (x, hh)
-    // advance by subtraction instead of a division per row.
-    static_assert(THREADS % D == 0, "a thread keeps one element of its rows");
-    constexpr int RSTEP = THREADS / D;
-    const int e = (int)threadIdx.x % D;
-    int row = __builtin_amdgcn_readfirstlane((int)threadIdx.x / D);
-    int x = 0, hh = row;
-    while (hh >= gq) { hh -= gq; ++x; }
-    for (; row < HG * gq; row += RSTEP) {
-        float acc = 0.f;
-        const int ecol = 4 * ((e >> 2) ^ hh) + (e & 3);         // swizzled position of element e in row hh
+    if (head_ok) {
+        // column j16 is workspace row (b * Hq + kvh * g) * nq + j16; lane (c4, j16) holds
+        // elements 16 nb + 4 c4 .. + 3
+        const int64_t r = (((int64_t)b * a.Hq + (int64_t)kvh * g) * nq + j16) * S + s;
+        float *const orow = a.ws_o + r * D + 4 * c4;
 #pragma unroll
-        for (int w = x * NWH; w < x * NWH + NWH; ++w) acc = fmaf(lds_ml[0][w][hh], lds_o[w * (MAXG * D) + hh * D + ecol], acc);
-        const int64_t r = (((int64_t)b * a.Hq + (kvh0 + x) * g) * nq + hh) * S + s;
-        a.ws_o[r * D + e] = acc;
-        hh += RSTEP;
-        while (hh >= gq) { hh -= gq; ++x; }
+        for (int nb = 0; nb < NB; ++nb) {
+            const float sc = F8 ? vs : 1.f;
+            *reinterpret_cast<float4 *>(orow + 16 * nb) =
+                make_float4(O[nb][0] * sc, O[nb][1] * sc, O[nb][2] * sc, O[nb][3] * sc);
+        }
+        if (c4 == 0) {
+            a.ws_m[r] = M;
+            a.ws_l[r] = lsum;
+        }
     }
 }
 
@@ -540,6 +541,9 @@ void split_mfma_kernel(SplitArgs a) {
     // Per wave: a (K tile, V tile) pair, reused for the merge.
     __shared__ uint4 smem[NW * 2 * TILE];
     __shared__ float lds_ml[3][NW][16];
+    __shared__ int lds_cnt[HG];                            // lanes of each head's waves done with their loop
+    if (threadIdx.x < HG) lds_cnt[threadIdx.x] = 0;
+    __syncthreads();
 
     const int G = a.Hkv / HG;
     const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
@@ -553,7 +557,7 @@ void split_mfma_kernel(SplitArgs a) {
     if (w < busy) {
         const WorkItem wi = busy_first_item(a, G, w, c, len0);
         const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
-        split_mfma_item<D, PAGED, HG, NWH, KVT>(a, wi, c, Lb, smem, lds_ml);
+        split_mfma_item<D, PAGED, HG, NWH, KVT>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
     }
     const int empties = a.B * G * a.S - busy;
     const int slots = grid * NW;
