@@ -552,10 +552,16 @@ void split_mfma_kernel(SplitArgs a) {
     // and the grid holds every item, so the finest chunking stays.
     const int fit_slots = (int64_t)a.B * G <= a.wg_slots ? a.wg_slots : 0;
     const int c = fit_chunk_len(a, G, batch_chunk_len(a, len0), len0, fit_slots);
-    const int busy = busy_items(a, G, c, len0);
     const int w = (int)blockIdx.x, grid = (int)gridDim.x;
+    WorkItem wi{0, 0, 0};
+    int busy;
+    if (a.B <= 64) {
+        busy = busy_first_small(a, G, w, c, len0, &wi);
+    } else {
+        busy = busy_items(a, G, c, len0);
+        if (w < busy) wi = busy_first_item(a, G, w, c, len0);
+    }
     if (w < busy) {
-        const WorkItem wi = busy_first_item(a, G, w, c, len0);
         const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
         split_mfma_item<D, PAGED, HG, NWH, KVT>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
     }

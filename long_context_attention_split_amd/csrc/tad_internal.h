@@ -136,6 +136,14 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
     return batch_chunk_len(a, a.seq_lens ? lane_row_len(a, 0) : 0);
 }
 
+// ceil(x / y) for 0 <= x < 2^31, 0 < y < 2^31, through a correctly rounded double
+// division: the quotient is exact when it is an integer and cannot round across one
+// otherwise, so this is exact -- a few instructions where a 32-bit integer division by a
+// run-time divisor costs several dozen.
+__device__ __forceinline__ int ceil_div(int x, int y) {
+    return (int)__builtin_ceil((double)x / (double)y);
+}
+
 // The chunk length for a kernel whose work-groups each serve G (row, chunk) units of
 // work: the finest length the S slots per row allow (c = batch_chunk_len) when its
 // non-empty chunks fit in the `slots` work-groups the device runs at once, else a
@@ -146,21 +154,19 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a) {
 // Wave-uniform.
 __device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, int len0, int slots) {
     if (c <= 0 || slots <= 0) return c;
-    int Lref = 0;
     auto busy_of = [&](int cc) {                 // G * sum_b ceil(L_b / cc)
-        int n = 0, mx = 0;
-        for (int b0 = 0; b0 < a.B; b0 += 64) {
-            const int L = b0 == 0 ? len0 : lane_row_len(a, b0);
-            n += (L + cc - 1) / cc;
-            mx = max(mx, L);
-        }
-        Lref = wave_top(mx);
+        int n = 0;
+        for (int b0 = 0; b0 < a.B; b0 += 64) n += ceil_div(b0 == 0 ? len0 : lane_row_len(a, b0), cc);
         return wave_total(n) * G;
     };
     int busy = busy_of(c);
+    if (busy <= slots) return c;
+    int mx = len0;
+    for (int b0 = 64; b0 < a.B; b0 += 64) mx = max(mx, lane_row_len(a, b0));
+    const int Lref = wave_top(mx);
     for (int it = 0; it < 16 && busy > slots && c < Lref; ++it) {
-        int cn = (int)(((int64_t)c * busy + slots - 1) / slots);   // busy scales about as 1/c
-        if (a.block_table) cn = (cn + a.page_size - 1) / a.page_size * a.page_size;
+        int cn = (int)__builtin_ceil((double)c * busy / slots);     // busy scales about as 1/c
+        if (a.block_table) cn = ceil_div(cn, a.page_size) * a.page_size;
         c = max(min(cn, Lref), c + 1);
         busy = busy_of(c);
     }
@@ -193,11 +199,28 @@ struct WorkItem {
 __device__ __forceinline__ int busy_items(const SplitArgs &a, int G, int c, int len0) {
     if (c <= 0) return 0;
     int n = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
-        const int L = b0 == 0 ? len0 : lane_row_len(a, b0);
-        n += min((L + c - 1) / c, a.S);
-    }
+    for (int b0 = 0; b0 < a.B; b0 += 64) n += min(ceil_div(b0 == 0 ? len0 : lane_row_len(a, b0), c), a.S);
     return wave_total(n) * G;
+}
+
+// Batches of at most 64 rows (one row per lane): the number of busy items and, for
+// k < busy, busy item k (busy_items and busy_first_item from one scan).  len0 =
+// lane_row_len(a, 0).  Wave-uniform; whole waves.
+__device__ __forceinline__ int busy_first_small(const SplitArgs &a, int G, int k, int c, int len0, WorkItem *wi) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int nb = (lane < a.B && c > 0) ? min(ceil_div(len0, c), a.S) : 0;   // busy chunks of row `lane`
+    const int incl = wave_incl_scan(nb * G);
+    const int busy = __builtin_amdgcn_readlane(incl, 63);
+    if (k < busy) {
+        const uint64_t hit = __ballot(incl > k);
+        const int r = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+        const int nr = __builtin_amdgcn_readlane(nb, r);
+        const int off = k - (__builtin_amdgcn_readlane(incl, r) - nr * G);
+        wi->b = r;
+        wi->g = off / nr;
+        wi->s = off - wi->g * nr;
+    }
+    return busy;
 }
 
 // The empty items of a batch of at most 64 rows (one row per lane), numbered e = 0, 1,
@@ -209,7 +232,7 @@ struct EmptyItems {
 
     __device__ __forceinline__ EmptyItems(const SplitArgs &a, int G_, int c, int len0) : G(G_), S(a.S) {
         const bool row = (int)(threadIdx.x & 63) < a.B;
-        nb = c > 0 ? min((len0 + c - 1) / c, S) : 0;
+        nb = c > 0 ? min(ceil_div(len0, c), S) : 0;
         cnt = row ? (S - nb) * G : 0;
         incl = wave_incl_scan(cnt);
     }
@@ -234,7 +257,7 @@ __device__ __forceinline__ WorkItem busy_first_item(const SplitArgs &a, int G, i
             int cnt = 0;                         // this row's chunks of the pass
             if (bb < a.B) {
                 const int L = b0 == 0 ? len0 : row_len(a, bb);
-                const int busy = c > 0 ? min((L + c - 1) / c, a.S) : 0;
+                const int busy = c > 0 ? min(ceil_div(L, c), a.S) : 0;
                 cnt = pass == 0 ? busy : a.S - busy;
             }
             const int incl = wave_incl_scan(cnt * G);
