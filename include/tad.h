@@ -94,7 +94,9 @@ typedef struct tad_tensor {
     int32_t ndim;       /* 3 or 4 */
     int64_t shape[4];
     int64_t stride[4];  /* elements */
-    const float *scale; /* FP8 k/v only: device fp32 [B * Hkv] dequantisation scales, or NULL */
+    const float *scale; /* FP8 k/v only: device fp32 [B * Hkv] dequantisation scales, or NULL
+                           (a field beyond data/dtype/ndim/shape/stride because FP8 K/V need a
+                           per-(b, KV head) scale, folded into q and into the partials) */
 } tad_tensor;
 
 /* Library version, TAD_VERSION of the build. */
@@ -114,7 +116,8 @@ const char *tad_last_error(void);
  * matrix-core kernel serves 4 KV heads per work-group (bf16 or FP8 K/V, d 64 or 128,
  * 2..16 query rows per KV head, Hkv a multiple of 4) -- and at least one.  Returns the
  * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
- * d, TAD_EDTYPE for kv_dtype).
+ * d, TAD_EDTYPE for kv_dtype).  (Hq, nq, d and kv_dtype are arguments because the count
+ * mirrors the kernel choice and the byte-sized minimum chunk, which depend on them.)
  */
 int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t Lmax, int32_t d, int32_t kv_dtype,
                         int32_t device);
@@ -122,6 +125,7 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
 /*
  * Bytes of device workspace tad_decode_ws / tad_split / tad_combine need for
  * B * Hq * nq rows, n_splits chunks and head dimension d (0 if an argument is < 1).
+ * (nq is an argument because every query token has its own partials.)
  * Layout (each array starting at a 256-byte boundary), with row = (b * Hq + h) * nq
  * + t and r = row * n_splits + s:
  *     m[r]        fp32: chunk maximum of the scores, in base-2 units (score * log2 e);

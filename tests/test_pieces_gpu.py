@@ -147,3 +147,49 @@ def test_grouped_batch_beyond_resident_slots_keeps_its_chunks(lib, kv):
         busy = -(-lens[bb] // clen)
         assert np.isfinite(m[bb, :, :busy]).all(), bb
         assert np.isinf(m[bb, :, busy:]).all(), bb
+
+
+def piece_cases(n=14, seed=4242):
+    """Seeded random calls that cut their chunks into pieces: fewer than 256 (row, chunk)
+    pairs, chunks of at least 256 KiB of K+V, any head dim and K/V dtype, ALiBi, ragged
+    rows (a zero-length one included), one query row per KV head."""
+    import random
+    rnd = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rnd.choice([64, 128, 256, 512])
+        kv = rnd.choice([torch.float32, torch.bfloat16, torch.float8_e4m3fn, torch.float8_e5m2])
+        if d == 512 and kv != torch.float32 and kv != torch.bfloat16:
+            kv = torch.bfloat16
+        elem = {torch.float32: 4, torch.bfloat16: 2}.get(kv, 1)
+        B, H = rnd.choice([1, 2, 3]), rnd.choice([1, 2, 4])
+        S = rnd.randint(1, max(1, 40 // (B * H)))
+        keys = max(1, (256 << 10) // (2 * d * elem))          # one 256 KiB chunk
+        L = S * keys * rnd.randint(1, 4) + rnd.randint(0, keys)
+        L = min(L, 120000)
+        lens = None
+        if B > 1 and rnd.random() < 0.6:
+            lens = [L] + [rnd.randint(0, L) for _ in range(B - 1)]
+            if rnd.random() < 0.5:
+                lens[-1] = 0
+        out.append((i, B, H, L, d, kv, S, lens, rnd.random() < 0.4))
+    return out
+
+
+@pytest.mark.parametrize("case", piece_cases(), ids=lambda c: "c%d" % c[0])
+def test_random_piece_cases(lib, case):
+    i, B, H, L, d, kv, S, lens, alibi = case
+    note("random pieces case %d: B=%d H=%d L=%d d=%d kv=%s S=%d lens=%s alibi=%s" % (i, B, H, L, d, kv, S, lens, alibi))
+    c = W.random_case(700 + i, B, H, H, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"])
+    g = to_dev(c)
+    a, b, _ = decode_both_ways(lib, g, S, (B, H, d))
+    assert torch.equal(a, b)
+    # the allocating entry point cuts the call the same way
+    e = torch.empty_like(a)
+    lib.tad_decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], S, e, k_scale=g["k_scale"],
+                   v_scale=g["v_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, e)
+    assert_parity(a.cpu().numpy(), ref, kv, vmax_real(c), "random pieces %d" % i)
