@@ -111,10 +111,11 @@ const char *tad_last_error(void);
  * kv_dtype on `device` (-1: the current device): ceil(4 * CUs / (B * Hkv)) for one
  * row, i.e. four (row, KV head, chunk) units per compute unit, and
  * ceil(6 * CUs / (B * Hkv)) for several rows, whose lengths may differ (seq_lens), so
- * that a ragged batch's non-empty chunks still cover the device; but no work-group's
- * chunk under 128 KiB of K and V -- per KV head 128 KiB, or 32 KiB where the
- * matrix-core kernel serves 4 KV heads per work-group (bf16 or FP8 K/V, d 64 or 128,
- * 2..16 query rows per KV head, Hkv a multiple of 4) -- and at least one.  Returns the
+ * that a ragged batch's non-empty chunks still cover the device; but no chunk under
+ * 128 KiB of K and V per KV head -- or 32 KiB per KV head for grouped-query calls on the
+ * matrix-core kernel (bf16 or FP8 K/V, d 64 or 128, 2..16 query rows per KV head) with
+ * Hkv a multiple of 4, which it serves 4 KV heads to a work-group when there are at
+ * least 128 (row, 4-KV-head group, chunk) items -- and at least one.  Returns the
  * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
  * d, TAD_EDTYPE for kv_dtype).  (Hq, nq, d and kv_dtype are arguments because the count
  * mirrors the kernel choice and the byte-sized minimum chunk, which depend on them.)

@@ -584,6 +584,14 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
            group * nq <= 16 && (d == 64 || d == 128);
 }
 
+// Fewest (row, 4-KV-head group, chunk) items for which a work-group serves 4 KV heads;
+// below it one KV head per work-group gives 4x the work-groups (one row of 32 query
+// heads over 8 KV heads, 4096 keys at 8 chunks: 16 twelve-wave work-groups 20.7 us,
+// 64 four-wave ones 12.7 us; two rows of 16384 keys at 4 chunks 152.5 -> 50.9 us; at
+// the automatic chunk counts 8.1-9.0 us instead of 10.2-10.7 us on small calls, and
+// the same from 128 items on; graph replay).
+constexpr int64_t kGroupedHeadsMinItems = 128;
+
 // The 4-KV-heads-per-work-group variant: a KV head count divisible by 4.
 bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
     return a.Hkv % 4 == 0 && split_mfma_supported(d, a.kv_type, a.group, a.nq);
@@ -622,7 +630,7 @@ static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
 template <int D, int KVT>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
-    if (split_mfma_grouped_heads(a, D)) {
+    if (split_mfma_grouped_heads(a, D) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems) {
         constexpr int NWH = WAVES;                         // one work-group fills a CU
         const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
         if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT>(a, grid, st);

@@ -246,7 +246,8 @@ int device_cus(int32_t device, int *cus) {
 // device (grouped-query decode, 8 rows of 4653..26803 keys, FP8 K/V: 58.0 -> 49.9 us
 // per step; uniform multi-row batches pay about 1% for the longer merge).  No
 // work-group's chunk holds less than 128 KiB of K and V (per KV head: 128 KiB, or
-// 32 KiB where the matrix-core kernel serves 4 KV heads per work-group), since shorter
+// 32 KiB for grouped-query calls on the matrix-core kernel, which serves them 4 KV heads
+// to a work-group when items are many and one KV head otherwise), since shorter
 // chunks cost work-group start-up and merge time: 32 bf16 heads of 1024 keys decode
 // in 13.5 us with 4 chunks (128 KiB) and 15.4 us with 8; one fp32 d = 512 head of
 // 4096 keys in 15.8 us with 128 chunks against ~40 us with the 16 that a fixed

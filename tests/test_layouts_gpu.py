@@ -79,7 +79,8 @@ def test_interleaved_bf16_query_and_large_logits(lib):
 @pytest.mark.parametrize("alibi", [False, True])
 def test_interleaved_grouped_query_heads(lib, B, Hq, Hkv, nq, S, alibi):
     """Grouped-query heads over a [B, L, Hkv, d] cache with a KV-head count divisible by
-    4: the matrix-core kernel serves 4 adjacent KV heads per work-group."""
+    4, on calls with few (row, KV-head group, chunk) items: the matrix-core kernel then
+    serves one KV head per work-group (4 adjacent ones from 128 items on, below)."""
     note("interleaved gqa B=%d Hq=%d Hkv=%d nq=%d S=%d alibi=%s" % (B, Hq, Hkv, nq, S, alibi))
     lens = [1300, 777, 5][:B]
     c = W.random_case(880 + Hkv + nq + S, B, Hq, Hkv, 1300, 128, seq_lens=lens, alibi=alibi)
@@ -92,8 +93,8 @@ def test_interleaved_grouped_query_heads(lib, B, Hq, Hkv, nq, S, alibi):
 @pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
 @pytest.mark.parametrize("B,Hq,Hkv,nq,S", [(2, 32, 8, 1, 5), (3, 16, 4, 2, 9), (2, 16, 8, 1, 16)])
 def test_interleaved_grouped_query_heads_d64(lib, kv, B, Hq, Hkv, nq, S):
-    """d = 64 grouped-query heads over a [B, L, Hkv, d] cache: 4 adjacent KV heads x 4
-    waves per work-group, ragged lengths, ALiBi, one and several tokens."""
+    """d = 64 grouped-query heads over a [B, L, Hkv, d] cache, few items (one KV head
+    per work-group), ragged lengths, ALiBi, one and several tokens."""
     note("interleaved gqa d64 kv=%s B=%d Hq=%d Hkv=%d nq=%d S=%d" % (kv, B, Hq, Hkv, nq, S))
     c = W.random_case(960 + Hkv + nq + S, B, Hq, Hkv, 1250, 64, kv_dtype=kv, seq_lens=[1250, 701, 3][:B],
                       alibi=True)
@@ -105,10 +106,25 @@ def test_interleaved_grouped_query_heads_d64(lib, kv, B, Hq, Hkv, nq, S):
 @pytest.mark.parametrize("kv", [torch.float8_e4m3fn, torch.float8_e5m2])
 @pytest.mark.parametrize("S", [3, 16])
 def test_interleaved_fp8_grouped_query_heads(lib, kv, S):
-    """FP8 K/V in a [B, L, Hkv, d] cache with 4 adjacent KV heads per work-group."""
+    """FP8 K/V in a [B, L, Hkv, d] cache with grouped-query heads (one KV head per
+    work-group at these item counts)."""
     note("interleaved fp8 gqa kv=%s S=%d" % (kv, S))
     c = W.random_case(890 + S, 2, 32, 8, 1400, 128, kv_dtype=kv, seq_lens=[1400, 611], alibi=True)
     assert_parity(run_interleaved(lib, c, S), oracle_of(c), kv, vmax_real(c), "interleaved fp8 gqa S=%d" % S)
+
+
+@pytest.mark.parametrize("kv,d,nq,S", [(torch.bfloat16, 128, 1, 16), (torch.float8_e4m3fn, 128, 1, 24),
+                                       (torch.bfloat16, 64, 2, 16), (torch.float8_e5m2, 64, 1, 20)])
+def test_interleaved_four_heads_per_work_group(lib, kv, d, nq, S):
+    """Enough (row, 4-KV-head group, chunk) items (8 rows x 2 groups x S >= 128) for the
+    matrix-core kernel to serve 4 adjacent KV heads per work-group on a [B, L, Hkv, d]
+    cache: ragged lengths with an empty row, ALiBi, one and two tokens."""
+    note("interleaved 4 heads per work-group kv=%s d=%d nq=%d S=%d" % (kv, d, nq, S))
+    lens = [1500, 0, 733, 1499, 1, 1024, 640, 1200]
+    c = W.random_case(970 + d + nq + S, 8, 32, 8, 1500, d, kv_dtype=kv, seq_lens=lens, alibi=True)
+    if nq > 1:
+        c["q"] = torch.randn((8, 32, nq, d), generator=torch.Generator().manual_seed(971))
+    assert_parity(run_interleaved(lib, c, S), oracle_of(c), kv, vmax_real(c), "interleaved 4 heads S=%d" % S)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(6, 6), (2, 2), (8, 2)])

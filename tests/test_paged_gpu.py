@@ -50,18 +50,18 @@ def oracle_of(c):
 @pytest.mark.parametrize("B,Hq,Hkv,L,d,ps,kv,S", [
     (2, 4, 4, 1000, 128, 16, torch.bfloat16, 5),           # MHA, vector path, fused merge
     (4, 32, 32, 1500, 128, 16, torch.bfloat16, 8),         # larger grid: split + combine
-    (2, 16, 4, 1300, 128, 32, torch.bfloat16, 7),          # GQA 4: matrix-core path
+    (2, 16, 4, 1300, 128, 32, torch.bfloat16, 7),          # GQA 4: matrix-core path (one KV head per work-group)
     (2, 8, 4, 900, 64, 64, torch.bfloat16, 3),             # GQA 2, d 64, 64-row pages
     (2, 4, 2, 700, 256, 16, torch.bfloat16, 4),            # d 256 (vector path, GQA)
     (2, 4, 4, 1000, 128, 16, torch.float8_e4m3fn, 5),      # FP8 with scales, MHA
     (2, 8, 2, 1000, 128, 48, torch.float8_e5m2, 6),        # FP8 E5M2, GQA 4, 48-row pages
     (2, 4, 4, 600, 64, 16, torch.float8_e4m3fn, 3),        # FP8, d 64
     (1, 8, 8, 4096, 128, 256, torch.bfloat16, 0),          # 256-row pages, automatic splits
-    (2, 32, 8, 1200, 128, 16, torch.float8_e4m3fn, 5),     # FP8 GQA, 4 KV heads per work-group
-    (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 12),       # FP8 E5M2 GQA, 4 KV heads, split + combine
-    (2, 32, 8, 1100, 64, 16, torch.bfloat16, 6),           # d 64 GQA, 4 KV heads per work-group
-    (3, 16, 8, 1000, 64, 32, torch.float8_e4m3fn, 11),     # d 64 FP8 GQA, 4 KV heads, split + combine
-    (2, 16, 4, 900, 64, 16, torch.float8_e5m2, 7),         # d 64 FP8: 32-key tiles over two 16-row pages
+    (2, 32, 8, 1200, 128, 16, torch.float8_e4m3fn, 32),    # FP8 GQA, 4 KV heads per work-group (128 items)
+    (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 48),       # FP8 E5M2 GQA, 4 KV heads, split + combine
+    (2, 32, 8, 1100, 64, 16, torch.bfloat16, 40),          # d 64 GQA, 4 KV heads per work-group
+    (3, 16, 8, 1000, 64, 32, torch.float8_e4m3fn, 24),     # d 64 FP8 GQA, 4 KV heads, split + combine
+    (2, 16, 4, 900, 64, 16, torch.float8_e5m2, 7),         # d 64 FP8: 32-key tiles over two 16-row pages, few items
     (2, 8, 2, 777, 128, 16, torch.float8_e4m3fn, 9),       # FP8, one KV head per work-group, 16-row pages
 ])
 def test_paged_matches_oracle(lib, B, Hq, Hkv, L, d, ps, kv, S):
