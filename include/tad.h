@@ -135,7 +135,8 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  *     o[r * d + e] fp32: sum over the chunk of 2^(score*log2 e - m[r]) * v[., e];
  *                 left unwritten for an empty chunk (tad_combine ignores the o of a
  *                 chunk whose weight is 0, whatever it holds)
- *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws)
+ *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws; the
+ *                 matrix-core form uses the first B * Hkv, one per (b, KV head))
  *     sub_m, sub_l, sub_o: when B * Hq * nq * n_splits < 256, the partials of up to
  *                 Pmax = min(512 / (B * Hq * nq * n_splits), 16384 / d, 64) pieces per
  *                 chunk, same meaning as m, l, o for a piece of the chunk
@@ -180,21 +181,29 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
                 int32_t d, tad_tensor *out, hipStream_t stream);
 
 /*
- * Split + merge with a caller-provided workspace (no allocation).  Small problems
- * (B * Hq * nq * n_splits below the device's compute-unit count, n_splits <= 8) read
- * by the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d] caches,
- * and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512, more than
- * 16 query rows per KV head) and not cut into pieces run as ONE launch: each split
- * work-group writes its partial, and the last one of a row to finish (counted in the
- * workspace's cnt array with agent-scope acquire-release updates) merges the row, then
- * returns its counter to zero.  Larger problems, grouped-query heads on the matrix
- * cores, chunks read as pieces and caches whose KV heads are interleaved per key with
- * one query head per KV head run the split (and pieces) and combine kernels back to
- * back (the counters are then unused).  Either way the output is bit-identical to
- * tad_split followed by tad_combine.  The counters must be zero the first time a
- * workspace is used (tad_workspace_clear, or memory allocated zeroed); every call that
- * runs to completion leaves them zero, so a workspace can be reused call after call.
- * Calls that share one workspace must not overlap.
+ * Split + merge with a caller-provided workspace (no allocation).  Small problems run
+ * as ONE launch, the merge done by the split kernel itself: each work-group writes its
+ * partial, and the last one to finish (counted in the workspace's cnt array with
+ * agent-scope acquire-release updates) merges, then returns its counter to zero.  Two
+ * kernels do this:
+ *   - the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d] caches,
+ *     and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512, more
+ *     than 16 query rows per KV head), when B * Hq * nq * n_splits is below the
+ *     device's compute-unit count, n_splits <= 8 and no chunk is cut into pieces: the
+ *     last work-group of a row merges the row;
+ *   - the matrix-core kernel (grouped-query heads, several tokens), when it serves one
+ *     KV head per work-group, n_splits <= 8 and B * Hkv * n_splits is at most the
+ *     compute-unit count: the last work-group of a (b, KV head) merges that KV head's
+ *     (head, token) rows side by side.
+ * Larger problems, chunks read as pieces and caches whose KV heads are interleaved per
+ * key with one query head per KV head run the split (and pieces) and combine kernels
+ * back to back (the counters are then unused).  Either way the output is bit-identical
+ * to tad_split followed by tad_combine.  The one-launch form saves a launch where the
+ * host's launch rate sets the pace; replayed in a graph it is about as fast as the two
+ * kernels, or up to about a microsecond slower.  The counters must be zero the first
+ * time a workspace is used (tad_workspace_clear, or memory allocated zeroed); every
+ * call that runs to completion leaves them zero, so a workspace can be reused call
+ * after call.  Calls that share one workspace must not overlap.
  */
 int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                   const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,

@@ -130,6 +130,11 @@ __device__ __forceinline__ void merge_pieces(const float *m, const float *l, con
     }
 }
 
+// 1 / L, or 0 for a row whose chunks are all empty (L = 0).
+__device__ __forceinline__ float merge_inverse(float ls) {
+    return (ls > 0.f) ? 1.f / ls : 0.f;
+}
+
 // Thread rows per output column in the weighted sum over the chunks: row rr of R takes
 // the chunks s = rr, rr + R, ... in order and the R row sums are added in order, so the
 // bits depend on (S, D) only -- whichever kernel merges, however many work-groups share
@@ -202,7 +207,7 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
         ls = fmaf(ws, load_partial<COHERENT>(l + s), ls);
     }
     ls = wave_sum(ls);
-    const float inv = (ls > 0.f) ? 1.f / ls : 0.f;
+    const float inv = merge_inverse(ls);
     __syncthreads();
 
     for (int gi = g0; gi < groups; gi += gstep) {
@@ -226,6 +231,128 @@ __device__ __forceinline__ void merge_row(const float *m, const float *l, const 
             out_row[col] = sum * inv;
         }
         __syncthreads();                        // part and (after the last group) lds reusable
+    }
+}
+
+// LDS floats merge_rows needs for R rows of S chunks at head dim D: the weights [R][S],
+// the rows' 1 / L [R], then (from a multiple of 4) the thread-row sums [R][rows][D].
+__host__ __device__ constexpr int merge_rows_lds_floats(int R, int S, int D) {
+    return (R * S + R + 3) / 4 * 4 + R * merge_thread_rows(S, D) * D;
+}
+
+// Merge of R consecutive workspace rows (row j: m + j S, l + j S, o + j S D) by one
+// work-group of NT threads, every row to the same bits as merge_row gives it: the
+// weights and the denominator from the same lane order (one wave per row), the same
+// thread-row sums of the weighted o (thread row rr adds chunks rr, rr + Rt, ... in
+// order, Rt = merge_thread_rows(S, D)), then those sums in order, times 1 / L.  Rows are
+// merged side by side, so a work-group merging many rows pays the load latency about
+// once per round of KU (row, thread row, 4 columns) units per thread instead of once per
+// row.  Chunks s >= busy of every row are empty: their m and l are taken as -inf and 0
+// (what the merge identity holds) without loading them, and their o, which weight 0
+// leaves out of the sums, is not loaded either.  Needs S <= 64, R <= 4 NT / 64 and
+// merge_rows_lds_floats(R, S, D) floats of lds; out_of(j) is row j's output.
+// Called by all NT threads; plain loads (the caller orders them after the partials'
+// stores).
+template <int D, int NT, typename OutOf>
+__device__ __forceinline__ void merge_rows(const float *m, const float *l, const float *o, int S, int busy, int R,
+                                           OutOf out_of, float *lds) {
+    constexpr int NWV = NT / 64;                // waves
+    constexpr int RPW = 4;                      // rows per wave at most
+    constexpr int KU = 2;                       // units per thread and round
+    constexpr int QD = D / 4;                   // column quads per row
+    static_assert(NT % 64 == 0 && D % 4 == 0, "work-group shape");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Rt = merge_thread_rows(S, D);
+    const int SPT = (S + Rt - 1) / Rt;          // chunks per thread row (at most 8 for S <= 64)
+    float *const wl = lds;                      // [R][S] weights
+    float *const il = lds + R * S;              // [R] 1 / L
+    float4 *const part = reinterpret_cast<float4 *>(lds + (R * S + R + 3) / 4 * 4);   // [R][Rt][QD]
+    const int U = R * Rt * QD;                  // (row, thread row, quad) units
+
+    // the first round's o loads and every row's m, l -- none depends on another
+    auto load_units = [&](int u0, float4 (&v)[KU][8]) {
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int u = u0 + k * NT + tid;
+            const int j = u / (Rt * QD), rr = (u / QD) % Rt, q = u % QD;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int s = rr + i * Rt;
+                v[k][i] = (u < U && i < SPT && s < busy)
+                              ? *reinterpret_cast<const float4 *>(o + ((int64_t)j * S + s) * D + 4 * q)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    };
+    float4 v[KU][8];
+    load_units(0, v);
+    float mv[RPW], lv[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int j = wave + i * NWV;
+        mv[i] = (j < R && lane < busy) ? m[j * S + lane] : kNegInf;
+        lv[i] = (j < R && lane < busy) ? l[j * S + lane] : 0.f;
+    }
+    // weights and 1 / L of each row: merge_row's arithmetic on one wave
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int j = wave + i * NWV;
+        if (j < R) {
+            const float mx = wave_max(mv[i]);
+            const float Mu = (mx == kNegInf) ? 0.f : mx;
+            float ls = 0.f;
+            if (lane < S) {
+                const float ws = exp2_fast(mv[i] - Mu);
+                wl[j * S + lane] = ws;
+                ls = fmaf(ws, lv[i], ls);
+            }
+            ls = wave_sum(ls);
+            if (lane == 0) il[j] = merge_inverse(ls);
+        }
+    }
+    __syncthreads();
+    // thread-row sums over the chunks, in merge_row's order
+    for (int u0 = 0; u0 < U; u0 += KU * NT) {
+        if (u0 > 0) load_units(u0, v);
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int u = u0 + k * NT + tid;
+            if (u < U) {
+                const int j = u / (Rt * QD), rr = (u / QD) % Rt;
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int s = rr + i * Rt;
+                    if (i < SPT && s < S) {
+                        const float w = wl[j * S + s];
+                        acc.x = add_weighted(w, v[k][i].x, acc.x);
+                        acc.y = add_weighted(w, v[k][i].y, acc.y);
+                        acc.z = add_weighted(w, v[k][i].z, acc.z);
+                        acc.w = add_weighted(w, v[k][i].w, acc.w);
+                    }
+                }
+                part[u] = acc;
+            }
+        }
+    }
+    __syncthreads();
+    // the thread-row sums of each column in order, times 1 / L
+    for (int u = tid; u < R * QD; u += NT) {
+        const int j = u / QD, q = u % QD;
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < Rt; ++i) {
+            const float4 p = part[(j * Rt + i) * QD + q];
+            sum.x += p.x;
+            sum.y += p.y;
+            sum.z += p.z;
+            sum.w += p.w;
+        }
+        const float inv = il[j];
+        float *const dst = out_of(j) + 4 * q;
+        dst[0] = sum.x * inv;
+        dst[1] = sum.y * inv;
+        dst[2] = sum.z * inv;
+        dst[3] = sum.w * inv;
     }
 }
 

@@ -56,6 +56,7 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "merge.h"
 #include "tad_internal.h"
 
 namespace tad {
@@ -140,6 +141,21 @@ __device__ __forceinline__ void wave_identity(const SplitArgs &a, const WorkItem
     }
 }
 
+// Fused form: the output of the g * nq (head, token) rows of KV head wi.g of row wi.b,
+// written as 0 by one wave when the row has no keys -- no chunk of it arrives at a
+// counter, so no merge writes it (the merge of such a row gives 0).  Called for the
+// row's chunk 0, which is empty exactly then.
+template <int D>
+__device__ __forceinline__ void wave_zero_rows(const SplitArgs &a, const WorkItem wi) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int rows = a.group * a.nq;
+    for (int i = lane; i < rows * D; i += 64) {
+        const int j = i / D, e = i % D;
+        a.out[(int64_t)wi.b * a.sob + (int64_t)(wi.g * a.group + j / a.nq) * a.soh + (int64_t)(j % a.nq) * a.sot + e] =
+            0.f;
+    }
+}
+
 // One work item of the matrix-core split kernel: row wi.b, KV heads wi.g * HG ..
 // + HG - 1, chunk wi.s of the row's Lb keys cut with chunk length c.  smem and lds_ml
 // are the work-group's LDS.
@@ -156,7 +172,9 @@ __device__ __forceinline__ void wave_identity(const SplitArgs &a, const WorkItem
 // (ds_read_b64_tr_b8), and both are widened to bf16 in registers (exact: every E4M3
 // and E5M2 value is a bf16 number).  The value product then runs on
 // v_mfma_f32_16x16x32_bf16 over the 32 keys.
-template <int D, bool PAGED, int HG, int NWH, int KVT>
+// WT: the partial is written through to the device coherence point (store_partial),
+// for a merge in another work-group of the same launch (the fused form).
+template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false>
 __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int c, const int Lb,
                                                 uint4 *smem, float (*lds_ml)[HG * NWH][16], int *lds_cnt) {
     static_assert(D == 64 || D == 128, "head dim");
@@ -510,12 +528,22 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const float sc = F8 ? vs : 1.f;
-            *reinterpret_cast<float4 *>(orow + 16 * nb) =
-                make_float4(O[nb][0] * sc, O[nb][1] * sc, O[nb][2] * sc, O[nb][3] * sc);
+            if constexpr (WT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store_partial(orow + 16 * nb + i, O[nb][i] * sc);
+            } else {
+                *reinterpret_cast<float4 *>(orow + 16 * nb) =
+                    make_float4(O[nb][0] * sc, O[nb][1] * sc, O[nb][2] * sc, O[nb][3] * sc);
+            }
         }
         if (c4 == 0) {
-            a.ws_m[r] = M;
-            a.ws_l[r] = lsum;
+            if constexpr (WT) {
+                store_partial(a.ws_m + r, M);
+                store_partial(a.ws_l + r, lsum);
+            } else {
+                a.ws_m[r] = M;
+                a.ws_l[r] = lsum;
+            }
         }
     }
 }
@@ -532,9 +560,19 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 // as work-groups of their own, empty chunks queued behind the busy ones (one 12-wave
 // work-group fills a CU's LDS) and each paid the prologue again.
 // WAVES: occupancy target (waves per SIMD) the register allocator must meet.
-template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16>
+// TAIL (one KV head per work-group): the one-launch form.  The last of a (row, KV head)
+// pair's busy chunks to finish merges the pair's g * nq (head, token) rows into out
+// with merge_rows, behind the arrival ticket of arrive_last (agent-scope acq_rel), and
+// returns the counter to zero; the rows' empty chunks are taken as the merge identity,
+// and a row with no keys gets 0 from the wave that writes its chunk 0's identity.  Same
+// bits as split + combine.  The partials are written through to the device coherence
+// point, which leaves the release little to write back: one row of 32 query heads
+// over 8 KV heads, 4096 keys at 32 chunks, 16.2 us with plain stores, 13.1 us written
+// through, 12.8 us with a relaxed ticket (graph replay).
+template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16, bool TAIL = false>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
+    static_assert(!TAIL || HG == 1, "the fused merge serves one KV head per work-group");
     constexpr bool F8 = KVT != kKvBF16;
     constexpr int TILE = (F8 ? 32 : 16) * (D * (F8 ? 1 : 2) / 16);   // 16-byte slots per tile and tensor
     constexpr int NW = HG * NWH;
@@ -563,7 +601,20 @@ void split_mfma_kernel(SplitArgs a) {
     }
     if (w < busy) {
         const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
-        split_mfma_item<D, PAGED, HG, NWH, KVT>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
+        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
+        if constexpr (TAIL) {
+            __shared__ int last;
+            int32_t *const cnt = a.cnt + (int64_t)wi.b * a.Hkv + wi.g;
+            if (arrive_last(cnt, min(ceil_div(Lb, c), a.S), &last)) {
+                const int gq = a.group * a.nq;
+                const int64_t R0 = ((int64_t)wi.b * a.Hq + (int64_t)wi.g * a.group) * a.nq;   // first workspace row
+                float *const ob = a.out + (int64_t)wi.b * a.sob + (int64_t)wi.g * a.group * a.soh;
+                auto out_of = [&](int j) { return ob + (int64_t)(j / a.nq) * a.soh + (int64_t)(j % a.nq) * a.sot; };
+                merge_rows<D, 64 * NW>(a.ws_m + R0 * a.S, a.ws_l + R0 * a.S, a.ws_o + R0 * a.S * D, a.S,
+                                       min(ceil_div(Lb, c), a.S), gq, out_of, reinterpret_cast<float *>(smem));
+                reset_counter(cnt);
+            }
+        }
     }
     const int empties = a.B * G * a.S - busy;
     const int slots = grid * NW;
@@ -572,9 +623,17 @@ void split_mfma_kernel(SplitArgs a) {
     if (e0 < empties) {
         if (a.B <= 64) {
             const EmptyItems em(a, G, c, len0);
-            for (int e = e0; e < empties; e += slots) wave_identity<D, HG>(a, em.item(e));
+            for (int e = e0; e < empties; e += slots) {
+                const WorkItem ei = em.item(e);
+                wave_identity<D, HG>(a, ei);
+                if constexpr (TAIL) if (ei.s == 0) wave_zero_rows<D>(a, ei);
+            }
         } else {
-            for (int e = e0; e < empties; e += slots) wave_identity<D, HG>(a, busy_first_item(a, G, busy + e, c, len0));
+            for (int e = e0; e < empties; e += slots) {
+                const WorkItem ei = busy_first_item(a, G, busy + e, c, len0);
+                wave_identity<D, HG>(a, ei);
+                if constexpr (TAIL) if (ei.s == 0) wave_zero_rows<D>(a, ei);
+            }
         }
     }
 }
@@ -597,6 +656,19 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
     return a.Hkv % 4 == 0 && split_mfma_supported(d, a.kv_type, a.group, a.nq);
 }
 
+// Whether a call runs the variant with 4 KV heads per work-group.
+static bool runs_grouped_heads(const SplitArgs &a, int d) {
+    return split_mfma_grouped_heads(a, d) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems;
+}
+
+// Whether the one-launch form (TAIL) serves a call: one KV head per work-group, at most
+// 64 chunks, and the merge's weights and thread-row sums of the g * nq rows fit in the
+// work-group's tile buffers (4 waves x 2 tiles of 2 d 16-byte slots: 64 d floats).
+bool split_mfma_fusable(const SplitArgs &a, int d) {
+    if (!split_mfma_supported(d, a.kv_type, a.group, a.nq) || runs_grouped_heads(a, d)) return false;
+    return a.S >= 1 && a.S <= 64 && merge_rows_lds_floats(a.group * a.nq, a.S, d) <= 64 * d;
+}
+
 // Launched variants: loads overlapped with compute.  The tile held in registers
 // costs d/4 + 8 VGPRs per lane; at d = 128 that needs 3 waves per SIMD (152 VGPRs;
 // 4 waves would spill), which measured faster than 4 waves without the overlap
@@ -610,36 +682,41 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
 // One launch.  wg_slots = the work-groups of this kernel the device runs at once (its
 // occupancy per CU, queried once, times the CU count); the grid is capped there when
 // the batch's (row, KV-head group) pairs fit in it.
-template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT>
+template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT, bool TAIL = false>
 static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
     constexpr int THREADS = 64 * HG * NWH;
     static const int per_cu = [] {
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT>), THREADS,
-                0) != hipSuccess || nb < 1)
+                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL>),
+                THREADS, 0) != hipSuccess || nb < 1)
             nb = 1;
         return nb;
     }();
     a.wg_slots = a.cus * per_cu;
     if (a.wg_slots > 0 && (int64_t)a.B * (a.Hkv / HG) <= a.wg_slots && grid > a.wg_slots) grid = a.wg_slots;
-    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT>), dim3((unsigned)grid), dim3(THREADS), 0,
-                       st, a);
+    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL>), dim3((unsigned)grid),
+                       dim3(THREADS), 0, st, a);
 }
 
 template <int D, int KVT>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
-    if (split_mfma_grouped_heads(a, D) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems) {
+    const int64_t items = (int64_t)a.B * a.Hkv * a.S;
+    if (a.fused) {                                     // split_mfma_fusable holds
+        if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, true>(a, items, st);
+        else launch_k<D, WAVES, false, 1, 4, KVT, true>(a, items, st);
+        return;
+    }
+    if (runs_grouped_heads(a, D)) {
         constexpr int NWH = WAVES;                         // one work-group fills a CU
         const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
         if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT>(a, grid, st);
         else launch_k<D, WAVES, false, 4, NWH, KVT>(a, grid, st);
         return;
     }
-    const int64_t grid = (int64_t)a.B * a.Hkv * a.S;
-    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT>(a, grid, st);
-    else launch_k<D, WAVES, false, 1, 4, KVT>(a, grid, st);
+    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT>(a, items, st);
+    else launch_k<D, WAVES, false, 1, 4, KVT>(a, items, st);
 }
 
 template <int D>
@@ -653,6 +730,7 @@ static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
 
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {
     if ((int64_t)a.B * a.Hkv * a.S <= 0) return hipSuccess;
+    if (a.fused && !split_mfma_fusable(a, d)) return hipErrorInvalidValue;
     switch (d) {
         case 64: launch_mfma_d<64>(a, st); break;
         case 128: launch_mfma_d<128>(a, st); break;

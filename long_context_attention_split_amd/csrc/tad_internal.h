@@ -398,6 +398,7 @@ inline int64_t ws_counters(int64_t rows, int64_t, int64_t) { return rows; }
 hipError_t launch_split_valu(const SplitArgs &a, int d, hipStream_t s);
 bool split_mfma_supported(int d, int kv_type, int group, int nq);
 bool split_mfma_grouped_heads(const SplitArgs &a, int d);
+bool split_mfma_fusable(const SplitArgs &a, int d);
 hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t s);
 bool split_heads_supported(const SplitArgs &a, int d);
 hipError_t launch_split_heads(const SplitArgs &a, int d, hipStream_t s);

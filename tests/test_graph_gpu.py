@@ -25,7 +25,7 @@ def test_decode_ws_replays_in_a_graph(lib, case):
     paged = case == "paged-interleaved"
     if case == "fused-mha":           # small grid: one launch, merge in the last work-group
         c, S = W.random_case(900, 2, 8, 8, 2500, 128, seq_lens=[2500, 1700]), 5
-    elif case == "gqa":               # matrix-core split, then combine
+    elif case == "gqa":               # matrix-core split, merge in its last work-group per KV head
         c, S = W.random_case(906, 2, 8, 2, 2500, 128, seq_lens=[2500, 1700]), 5
     elif case == "split-combine-mha":  # large grid: split then combine
         c, S = W.random_case(901, 2, 32, 32, 4000, 128, seq_lens=[4000, 3333]), 16

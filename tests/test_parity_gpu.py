@@ -316,16 +316,17 @@ def test_several_tokens_entry_points_agree(lib):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv,nq", [(16, 4, 1), (32, 8, 1), (8, 8, 2)])
 def test_grouped_kv_heads_decode_equals_split_combine(lib, Hq, Hkv, nq, d):
-    """Grouped-query heads (4 KV heads per work-group when the KV head count allows)
-    always run split + combine, also on small grids: tad_decode_ws equals tad_split +
-    tad_combine bit for bit, call after call, and is within the bar of the oracle."""
+    """Grouped-query heads on the matrix cores, here a small grid at 3 chunks, where
+    tad_decode_ws merges in the split kernel's last work-group per (row, KV head): it
+    equals tad_split + tad_combine bit for bit, call after call, and is within the bar
+    of the oracle."""
     note("grouped kv heads Hq=%d Hkv=%d nq=%d d=%d" % (Hq, Hkv, nq, d))
     c = W.random_case(460 + Hq + nq + d, 2, Hq, Hkv, 1800, d, seq_lens=[1800, 1001])
     if nq > 1:
         c["q"] = torch.randn((2, Hq, nq, d), generator=torch.Generator().manual_seed(461))
     ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"])
     g = to_dev(c)
-    S = 3                                              # 2 * Hq * nq * 3 < CU count: fused
+    S = 3                                              # 2 * Hkv * 3 items <= CU count: fused
     a = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], None, S)
     again = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], None, S)
     ws = lib.workspace(g["q"], g["k"], S)
