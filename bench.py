@@ -175,12 +175,9 @@ class TimingEvent:
             self._hip.hipEventDestroy(self.h)
 
 
-def read_stream_probe(k, v, stream, reps: int = 10):
-    """GB/s of a plain read stream over the K and V allocations (libtad_probe.so, built
-    beside libtad.so), timed with events on `stream`; None when the probe library is
-    missing."""
+def probe_library():
+    """tad_probe_read_stream from libtad_probe.so (built beside libtad.so), or None."""
     import ctypes
-    import torch
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_attention_split_amd",
                         "libtad_probe.so")
     if not os.path.exists(path):
@@ -188,6 +185,16 @@ def read_stream_probe(k, v, stream, reps: int = 10):
     lib = ctypes.CDLL(path)
     lib.tad_probe_read_stream.restype = ctypes.c_int
     lib.tad_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def read_stream_probe(k, v, stream, reps: int = 10):
+    """GB/s of a plain read stream over the K and V allocations, timed with events on
+    `stream`, back to back; None when the probe library is missing."""
+    import torch
+    lib = probe_library()
+    if lib is None:
+        return None
     sink = torch.zeros(4096, dtype=torch.int32, device=k.device)
     bufs = []
     for t in (k, v):
@@ -335,6 +342,25 @@ def run_all(args, dev) -> int:
         rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
         us = float(np.median(step_ms)) * 1e3
         sus = float(np.median(split_ms)) * 1e3
+        # the same number of bytes read by a plain stream, timed the same way (cold)
+        probe = None
+        plib = probe_library()
+        if plib is not None:
+            nbytes = int(x["kv_bytes"])
+            pbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+            stream = x["stream"]
+
+            def read_once():
+                if plib.tad_probe_read_stream(pbuf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream) != 0:
+                    raise RuntimeError("read-stream probe launch failed")
+            read_once()
+            pus = float(np.median(time_flushed(read_once, stream, args.steps, scratch))) * 1e3
+            probe = {"us_median": round(pus, 2), "gbs": round(nbytes / (pus * 1e-6) / 1e9, 1),
+                     "split_rate_over_probe_rate": round(pus / sus, 4),
+                     "what": "plain read of the workload's K/V byte count from one contiguous buffer "
+                             "(libtad_probe.so), timed like the split"}
+            del pbuf
         rec = {
             "metric": METRIC, "record": "per-workload",
             "workload": wid, "config": {"workload": x["w"].name, "B": x["B"], "Hq": x["Hq"], "Hkv": x["Hkv"],
@@ -346,6 +372,7 @@ def run_all(args, dev) -> int:
             "pct_of_hbm_peak": round(100.0 * x["kv_bytes"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "split_kernel_us_median": round(sus, 2),
             "roofline_frac_split_events": round(x["kv_bytes"] / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "read_probe_cold": probe,
             "timing": "tad_decode_ws and tad_split each timed with events, median of %d calls, 512 MiB "
                       "written before each call" % args.steps,
             "parity": {"max_abs": float(err.max()), "rel_l2": rel, "tolerance_max_abs": tol,

@@ -288,7 +288,12 @@ static hipError_t launch_tail(const SplitArgs &a, int64_t grid, hipStream_t st) 
     // paged caches: 16-key wave tiles (page sizes are multiples of 16)
     constexpr int KPW = 64 * RowChunk<KVT, kPolicyNT>::EPL / D;
     constexpr int UP = 16 / KPW > 0 ? 16 / KPW : 1;
-    constexpr int UD = 128 / RowChunk<KVT, kPolicyNT>::kBytes;
+    // contiguous caches: 128 bytes of each row per lane and tensor in flight (8 loads),
+    // except FP8, whose rows take twice the arithmetic per byte: 4 loads (one row of 32
+    // heads x 131072 keys of E4M3: 164.0-164.4 us per step against 168.0-168.2 us with
+    // 8, 170-171 with 2, 172-173 with 3)
+    constexpr bool F8 = KVT == kKvE4M3 || KVT == kKvE5M2;
+    constexpr int UD = F8 ? 4 : 128 / RowChunk<KVT, kPolicyNT>::kBytes;
     const int gq = a.group * a.nq;
     if (a.block_table) {
         if constexpr (KVT == kKvF32 || D > 256) {
