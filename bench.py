@@ -185,6 +185,9 @@ def probe_library():
     lib = ctypes.CDLL(path)
     lib.tad_probe_read_stream.restype = ctypes.c_int
     lib.tad_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tad_probe_read_stream_static.restype = ctypes.c_int
+    lib.tad_probe_read_stream_static.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                                 ctypes.c_void_p]
     return lib
 
 
@@ -354,12 +357,22 @@ def run_all(args, dev) -> int:
             def read_once():
                 if plib.tad_probe_read_stream(pbuf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream) != 0:
                     raise RuntimeError("read-stream probe launch failed")
+
+            def read_static():
+                if plib.tad_probe_read_stream_static(pbuf.data_ptr(), nbytes, sink.data_ptr(), cus,
+                                                     stream.cuda_stream) != 0:
+                    raise RuntimeError("read-stream probe launch failed")
             read_once()
+            read_static()
             pus = float(np.median(time_flushed(read_once, stream, args.steps, scratch))) * 1e3
+            qus = float(np.median(time_flushed(read_static, stream, args.steps, scratch))) * 1e3
             probe = {"us_median": round(pus, 2), "gbs": round(nbytes / (pus * 1e-6) / 1e9, 1),
                      "split_rate_over_probe_rate": round(pus / sus, 4),
-                     "what": "plain read of the workload's K/V byte count from one contiguous buffer "
-                             "(libtad_probe.so), timed like the split"}
+                     "one_group_per_cu_us_median": round(qus, 2),
+                     "split_rate_over_one_group_per_cu_rate": round(qus / sus, 4),
+                     "what": "plain reads of the workload's K/V byte count from one contiguous buffer "
+                             "(libtad_probe.so), timed like the split: 4096 four-wave work-groups handed "
+                             "out by the dispatcher, and one twelve-wave work-group per CU with a fixed slice"}
             del pbuf
         rec = {
             "metric": METRIC, "record": "per-workload",

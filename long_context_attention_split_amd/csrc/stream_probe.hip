@@ -2,22 +2,22 @@
 // K/V streams are compared with (a measurement aid; not part of the decode library).
 //
 // Every work-group reads one contiguous slice of the buffer with 16-byte
-// non-temporal buffer loads, 4 waves x 8 loads in flight per wave, each load
-// instruction covering 1 KiB of consecutive bytes -- the access pattern of the split
-// kernels' K and V rows -- and folds the data into one word it writes to `sink`, so
-// that no load can be dropped.
+// non-temporal buffer loads, 8 loads in flight per wave, each load instruction
+// covering 1 KiB of consecutive bytes -- the access pattern of the split kernels' K
+// and V rows -- and folds the data into one word it writes to `sink`, so that no load
+// can be dropped.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
-constexpr uint32_t kStep = kThreads * 16 * kUnroll;   // bytes per work-group iteration
 
-__global__ __launch_bounds__(kThreads) void stream_probe_kernel(const char *base, uint64_t slice,
-                                                                  uint64_t bytes, uint32_t *sink) {
+template <int NT>
+__global__ __launch_bounds__(NT) void stream_probe_kernel(const char *base, uint64_t slice, uint64_t bytes,
+                                                          uint32_t *sink) {
+    constexpr uint32_t kStep = NT * 16 * kUnroll;    // bytes per work-group iteration
     const uint64_t start = (uint64_t)blockIdx.x * slice;
     const uint64_t len = start < bytes ? (bytes - start < slice ? bytes - start : slice) : 0;
     const __amdgpu_buffer_rsrc_t r =
@@ -29,24 +29,39 @@ __global__ __launch_bounds__(kThreads) void stream_probe_kernel(const char *base
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
             v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  r, (int)(off + (uint32_t)u * kThreads * 16u + lane_off), 0, 2));
+                                                  r, (int)(off + (uint32_t)u * NT * 16u + lane_off), 0, 2));
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;   // practically never taken; keeps the loads
 }
 
-}  // namespace
-
-// Read `bytes` bytes at `src` (device memory, 16-byte aligned) once, as fast as the
-// pattern above allows, on `stream`.  `sink`: device uint32 [4096], written at most.
-// Returns 0, or a hipError_t value if the launch failed.
-extern "C" int tad_probe_read_stream(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream) {
-    const int groups = 4096;                           // 16 per CU: every CU streams
+template <int NT>
+int launch_probe(const void *src, uint64_t bytes, uint32_t *sink, int groups, hipStream_t stream) {
+    constexpr uint64_t kStep = NT * 16 * kUnroll;
     uint64_t slice = (bytes + groups - 1) / groups;
     slice = (slice + kStep - 1) / kStep * kStep;       // whole iterations per work-group
     if (slice > 0x7fffffffull) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(stream_probe_kernel, dim3(groups), dim3(kThreads), 0, stream, (const char *)src, slice, bytes,
+    hipLaunchKernelGGL(stream_probe_kernel<NT>, dim3(groups), dim3(NT), 0, stream, (const char *)src, slice, bytes,
                        sink);
     return (int)hipGetLastError();
+}
+
+}  // namespace
+
+// Read `bytes` bytes at `src` (device memory, 16-byte aligned) once, as fast as the
+// pattern above allows, on `stream`: 4096 work-groups of 4 waves (16 per CU), which
+// the dispatcher hands to the CUs as they free up.  `sink`: device uint32 [4096],
+// written at most.  Returns 0, or a hipError_t value if the launch failed.
+extern "C" int tad_probe_read_stream(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t stream) {
+    return launch_probe<256>(src, bytes, sink, 4096, stream);
+}
+
+// The same read in the matrix-core split kernel's launch shape: `groups` work-groups
+// of 12 waves (at most 4096; one per CU when groups is the CU count), each reading one
+// slice of bytes / groups with 96 KiB in flight, so that no work moves between CUs.
+extern "C" int tad_probe_read_stream_static(const void *src, uint64_t bytes, uint32_t *sink, int groups,
+                                            hipStream_t stream) {
+    if (groups < 1 || groups > 4096) return (int)hipErrorInvalidValue;
+    return launch_probe<768>(src, bytes, sink, groups, stream);
 }
