@@ -192,9 +192,10 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  *     device's compute-unit count, n_splits <= 8 and no chunk is cut into pieces: the
  *     last work-group of a row merges the row;
  *   - the matrix-core kernel (grouped-query heads, several tokens), when it serves one
- *     KV head per work-group, n_splits <= 8 and B * Hkv * n_splits is at most the
- *     compute-unit count: the last work-group of a (b, KV head) merges that KV head's
- *     (head, token) rows side by side.
+ *     KV head per work-group, n_splits <= 8, B * Hkv * n_splits is at most the
+ *     compute-unit count and the merge fits the work-group's LDS (all cases but d = 64
+ *     with 16 (head, token) rows per KV head): the last work-group of a (b, KV head)
+ *     merges that KV head's (head, token) rows side by side.
  * Larger problems, chunks read as pieces and caches whose KV heads are interleaved per
  * key with one query head per KV head run the split (and pieces) and combine kernels
  * back to back (the counters are then unused).  Either way the output is bit-identical
