@@ -136,7 +136,8 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  *                 left unwritten for an empty chunk (tad_combine ignores the o of a
  *                 chunk whose weight is 0, whatever it holds)
  *     cnt[row]    int32: arrival counters of the fused merge (see tad_decode_ws; the
- *                 matrix-core form uses the first B * Hkv, one per (b, KV head))
+ *                 matrix-core form uses the first B * Hkv, one per (b, KV head), the
+ *                 head-packed form the first B * Hq / 4)
  *     sub_m, sub_l, sub_o: when B * Hq * nq * n_splits < 256, the partials of up to
  *                 Pmax = min(512 / (B * Hq * nq * n_splits), 16384 / d, 64) pieces per
  *                 chunk, same meaning as m, l, o for a piece of the chunk
@@ -195,10 +196,12 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  *     KV head per work-group, n_splits <= 8, B * Hkv * n_splits is at most the
  *     compute-unit count and the merge fits the work-group's LDS (all cases but d = 64
  *     with 16 (head, token) rows per KV head): the last work-group of a (b, KV head)
- *     merges that KV head's (head, token) rows side by side.
- * Larger problems, chunks read as pieces and caches whose KV heads are interleaved per
- * key with one query head per KV head run the split (and pieces) and combine kernels
- * back to back (the counters are then unused).  Either way the output is bit-identical
+ *     merges that KV head's (head, token) rows side by side;
+ *   - the head-packed kernel (caches whose KV heads are interleaved per key, one query
+ *     head per KV head), when n_splits <= 8 and B * Hq / 4 * n_splits is at most the
+ *     compute-unit count: the last work-group of a (b, 4-head group) merges its 4 rows.
+ * Larger problems and chunks read as pieces run the split (and pieces) and combine
+ * kernels back to back (the counters are then unused).  Either way the output is bit-identical
  * to tad_split followed by tad_combine.  The one-launch form saves a launch where the
  * host's launch rate sets the pace; replayed in a graph it is about as fast as the two
  * kernels, or up to about a microsecond slower.  The counters must be zero the first

@@ -18,9 +18,11 @@
 // has as many waves as split_valu's for the same chunk count.
 //
 // Every K and V byte of a chunk is read once, with 16-byte buffer loads; loads past
-// the chunk end return zero.  No fused merge: the combine kernel merges.
+// the chunk end return zero.  Every chunk has its work-group, so an empty chunk writes
+// the merge identity (m = -inf, l = 0, o = 0) itself.
 
 #include "device_util.h"
+#include "merge.h"
 #include "tad_internal.h"
 
 namespace tad {
@@ -83,7 +85,12 @@ constexpr int kHeadsPerWave = 64 / kHeadLanes;   // 4
 constexpr int kHeadsWaves = 16;                  // waves per work-group
 constexpr int kHeadsThreads = 64 * kHeadsWaves;
 
-template <int D, int KVT, bool PAGED>
+// TAIL: the one-launch form (a.fused).  The work-groups write their partials through to
+// the device coherence point, and the last of a (b, 4-head group)'s S chunks to arrive
+// (arrive_last: agent-scope acq_rel ticket on the group's counter) merges the group's 4
+// rows with merge_rows -- the combine's arithmetic, so the same bits -- and returns
+// the counter to zero.
+template <int D, int KVT, bool PAGED, bool TAIL = false>
 __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a) {
     constexpr int G = kHeadLanes, HPW = kHeadsPerWave, NW = kHeadsWaves;
     constexpr int EPL = D / G;
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
     }
 
     // ---- merge the NW wave states of each head (fixed order) and write the partials.
-    __shared__ float lds_o[NW][HPW * D];
+    __shared__ __align__(16) float lds_o[NW][HPW * D];     // also the fused merge's scratch
     __shared__ float lds_m[NW][HPW], lds_l[NW][HPW], lds_w[NW][HPW], lds_M[HPW];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) lds_o[wave][lane * EPL + e] = o[e];
@@ -228,8 +235,13 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
         }
         lds_M[g] = M;
         const int64_t r = ((int64_t)b * a.Hq + h0 + g) * S + s;
-        a.ws_m[r] = M;
-        a.ws_l[r] = lsum;
+        if constexpr (TAIL) {
+            store_partial(a.ws_m + r, M);
+            store_partial(a.ws_l + r, lsum);
+        } else {
+            a.ws_m[r] = M;
+            a.ws_l[r] = lsum;
+        }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < HPW * D; i += kHeadsThreads) {
@@ -239,12 +251,30 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
         for (int w = 0; w < NW; ++w) acc = fmaf(lds_w[w][g], lds_o[w][i], acc);
         const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + h0 + g] : 1.f;
         const int64_t r = ((int64_t)b * a.Hq + h0 + g) * S + s;
-        a.ws_o[r * D + e] = acc * vsc;
+        if constexpr (TAIL) store_partial(a.ws_o + r * D + e, acc * vsc);
+        else a.ws_o[r * D + e] = acc * vsc;
+    }
+
+    if constexpr (TAIL) {
+        static_assert(merge_rows_lds_floats(HPW, kMaxFusedSplits, D) <= NW * HPW * D, "merge scratch fits");
+        __shared__ int last;
+        int32_t *const cnt = a.cnt + bh;                   // one counter per (b, 4-head group)
+        if (arrive_last(cnt, S, &last)) {
+            const int64_t row0 = (int64_t)b * a.Hq + h0;   // the group's first workspace row
+            float *const ob = a.out + (int64_t)b * a.sob + (int64_t)h0 * a.soh;
+            auto out_of = [&](int j) { return ob + (int64_t)j * a.soh; };
+            merge_rows<D, kHeadsThreads>(a.ws_m + row0 * S, a.ws_l + row0 * S, a.ws_o + row0 * S * D, S, S, HPW,
+                                         out_of, &lds_o[0][0]);
+            reset_counter(cnt);
+        }
     }
 }
 
+// The fused form (a.fused) takes at most kMaxFusedSplits chunks.
 bool split_heads_supported(const SplitArgs &a, int d) {
-    if (a.fused || a.P > 1 || a.group != 1 || a.nq != 1 || a.Hkv < 2 || a.Hq % kHeadsPerWave) return false;
+    if ((a.fused && a.S > kMaxFusedSplits) || a.P > 1 || a.group != 1 || a.nq != 1 || a.Hkv < 2 ||
+        a.Hq % kHeadsPerWave)
+        return false;
     if (d != 64 && d != 128 && d != 256) return false;
     if (a.skh != d || a.svh != d) return false;              // heads of a key adjacent
     return a.skj >= (int64_t)kHeadsPerWave * d && a.svj >= (int64_t)kHeadsPerWave * d;
@@ -254,10 +284,22 @@ template <int D, int KVT>
 static hipError_t launch_ht(const SplitArgs &a, hipStream_t st) {
     const int64_t grid = (int64_t)a.B * (a.Hq / kHeadsPerWave) * a.S;
     if (grid <= 0) return hipSuccess;
-    if (a.block_table)
-        hipLaunchKernelGGL((split_heads_kernel<D, KVT, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((split_heads_kernel<D, KVT, false>), dim3((unsigned)grid), dim3(kHeadsThreads), 0, st, a);
+    if (a.fused && a.S > kMaxFusedSplits) return hipErrorInvalidValue;
+    if (a.block_table) {
+        if (a.fused)
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, true, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0,
+                               st, a);
+        else
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0, st,
+                               a);
+    } else {
+        if (a.fused)
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, false, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0,
+                               st, a);
+        else
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, false>), dim3((unsigned)grid), dim3(kHeadsThreads), 0, st,
+                               a);
+    }
     return hipGetLastError();
 }
 

@@ -410,11 +410,12 @@ int check_splits(int32_t S) {
 // per row merges the row (13.6 vs 15.5 us for 32 heads x 1024 keys), the matrix-core
 // kernel's last work-group per (row, KV head) merges that KV head's rows side by side
 // (one row of 32 query heads over 8 KV heads, 4096 keys at 8 chunks: 15.6 vs 18.4 us
-// per call through the Python binding; in a replayed graph 13.3 vs 13.0-13.2 us).  With
-// more chunks one work-group's merge costs more than the combine kernel (graph replay,
-// the same call at 32 chunks: 13.1 vs 9.9 us).  The head-packed kernel (4 heads per
-// wave) and larger grids run split and combine.  Both forms give bit-identical
-// outputs (the merges keep the combine's summation order).
+// per call through the Python binding; in a replayed graph 13.3 vs 13.0-13.2 us), and
+// the head-packed kernel's last work-group per (row, 4-head group) merges those 4
+// rows.  With more chunks one work-group's merge costs more than the combine kernel
+// (graph replay, the grouped-query call at 32 chunks: 13.1 vs 9.9 us), so larger grids
+// run split and combine.  Both forms give bit-identical outputs (the merges keep the
+// combine's summation order).
 int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
                const OutDesc &out, hipStream_t stream) {
@@ -423,11 +424,12 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
     if (rc) return rc;
     const tad::SplitArgs unfused = split_args(P, q, k, v, seq_lens, slopes, S, w, OutDesc());
     const bool mfma = tad::split_mfma_supported((int)P.d, unfused.kv_type, unfused.group, unfused.nq);
-    const bool vector_kernel = !mfma && !tad::split_heads_supported(unfused, (int)P.d);
-    if (vector_kernel && unfused.P == 1 && S <= tad::kMaxFusedSplits && P.B * P.Hq * P.nq * (int64_t)S < cus)
-        return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
-    if (mfma && S <= tad::kMaxFusedSplits && P.B * P.Hkv * (int64_t)S <= cus &&
-        tad::split_mfma_fusable(unfused, (int)P.d))
+    const bool heads = !mfma && tad::split_heads_supported(unfused, (int)P.d);
+    const bool vector_kernel = !mfma && !heads;
+    const bool small = S <= tad::kMaxFusedSplits;
+    if ((vector_kernel && unfused.P == 1 && small && P.B * P.Hq * P.nq * (int64_t)S < cus) ||
+        (mfma && small && P.B * P.Hkv * (int64_t)S <= cus && tad::split_mfma_fusable(unfused, (int)P.d)) ||
+        (heads && small && P.B * (P.Hq / 4) * (int64_t)S <= cus))
         return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
     if ((rc = launch_split(unfused, P.d, stream))) return rc;
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);

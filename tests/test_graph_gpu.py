@@ -38,7 +38,7 @@ def test_decode_ws_replays_in_a_graph(lib, case):
     elif case == "tokens":
         c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
         c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
-    else:
+    else:                             # token-major pages: head-packed split, merge in its last work-groups
         c, S = W.random_case(904, 2, 16, 16, 2000, 128, seq_lens=[2000, 1111]), 8
     q, k, v, sl = dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["seq_lens"])
     if paged:

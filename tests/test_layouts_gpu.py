@@ -136,8 +136,8 @@ def test_interleaved_fallbacks(lib, Hq, Hkv):
 
 
 def test_interleaved_entry_points_agree(lib):
-    """For interleaved caches tad_decode_ws never fuses: tad_decode_ws, tad_decode and
-    tad_split + tad_combine are bit-identical on small and large grids."""
+    """tad_decode_ws (one launch on the small grid, split + combine on the large one),
+    tad_decode and tad_split + tad_combine are bit-identical for interleaved caches."""
     for B, H, S in ((1, 4, 2), (2, 32, 16)):
         c = W.random_case(850 + B, B, H, H, 2000, 128, seq_lens=[2000, 1234][:B])
         q, sl = c["q"].to(DEV), c["seq_lens"].to(DEV)
@@ -178,3 +178,71 @@ def test_paged_interleaved_heads(lib, kv, d):
     ref = oracle_of(c)
     for S in (3, 12):
         assert_parity(run_paged(lib, c, S), ref, kv, vmax_real(c), "paged interleaved S=%d" % S)
+
+
+def counters_of(ws, rows, S, d):
+    """The workspace's arrival counters (after m, l and o, each 256-byte aligned)."""
+    al = lambda x: (x + 255) // 256 * 256
+    off = 2 * al(4 * rows * S) + al(4 * rows * S * d)
+    return ws[off:off + 4 * rows].view(torch.int32)
+
+
+@pytest.mark.parametrize("kv,d,B,H,L,S,lens,alibi", [
+    (torch.bfloat16, 128, 1, 4, 3000, 1, None, False),               # one group of 4 heads, one chunk
+    (torch.bfloat16, 128, 2, 16, 2500, 8, [2500, 0], True),          # an empty row, ALiBi, 8 chunks
+    (torch.float8_e4m3fn, 128, 3, 8, 4000, 5, [4000, 17, 2222], False),
+    (torch.float32, 64, 2, 8, 1500, 3, [1500, 1], False),             # fp32 d 64, a row of one key
+    (torch.float8_e5m2, 256, 1, 12, 2048, 7, None, True),             # d 256, 3 groups
+    (torch.bfloat16, 64, 4, 32, 1000, 8, [1000, 640, 0, 999], False),  # 256 work-groups
+])
+def test_interleaved_one_launch_equals_split_combine(lib, kv, d, B, H, L, S, lens, alibi):
+    """Small grids on interleaved caches run the head-packed kernel with the merge in its
+    last work-group per (row, 4-head group): bit-identical to tad_split + tad_combine,
+    call after call through one workspace whose counters it leaves at zero, and within
+    the bars of the oracle."""
+    note("interleaved one launch kv=%s d=%d B=%d H=%d S=%d lens=%s" % (kv, d, B, H, S, lens))
+    c = W.random_case(880 + d + S, B, H, H, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi)
+    g = lambda key: None if c.get(key) is None else c[key].to(DEV)
+    q, sl, sp = c["q"].to(DEV), g("seq_lens"), g("slopes")
+    kw = dict(k_scale=g("k_scale"), v_scale=g("v_scale"))
+    k, v = interleave(c["k"]), interleave(c["v"])
+    ws = lib.workspace(q, k, S)
+    outs = []
+    for _ in range(3):
+        o = torch.full((B, H, d), float("nan"), dtype=torch.float32, device=DEV)
+        lib.tad_decode_ws(q, k, v, sl, sp, S, o, ws, **kw)
+        outs.append(o)
+    ws2 = lib.workspace(q, k, S)
+    lib.tad_split(q, k, v, sl, sp, S, ws2, **kw)
+    sc = torch.full((B, H, d), float("nan"), dtype=torch.float32, device=DEV)
+    lib.tad_combine(ws2, B, H, 1, S, d, sc)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, sc)
+    assert (counters_of(ws, B * H, S, d) == 0).all()
+    out = outs[0].cpu().numpy()
+    assert_parity(out, oracle_of(c), kv, vmax_real(c), "interleaved one launch")
+    for b in range(B):
+        if lens is not None and lens[b] == 0:
+            assert (out[b] == 0).all()
+
+
+def test_paged_interleaved_one_launch(lib):
+    """Token-major pages with one query head per KV head on a small grid: one launch,
+    equal to tad_split_paged + tad_combine bit for bit."""
+    from test_paged_gpu import paged_case
+    B, H, L, d, S, ps = 2, 16, 1100, 128, 4, 16
+    c = paged_case(895, B, H, H, L, d, ps, torch.bfloat16, lens=[1100, 555])
+    g = lambda key: None if c.get(key) is None else c[key].to(DEV)
+    q, sl = c["q"].to(DEV), g("seq_lens")
+    kc, vc, tb = c["k_cache"].to(DEV), c["v_cache"].to(DEV), c["table"].to(DEV)
+    out = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    ws = lib.workspace(q, c["k"], S)
+    lib.tad_decode_paged_ws(q, kc, vc, tb, sl, None, S, out, ws)
+    ws2 = lib.workspace(q, c["k"], S)
+    lib.tad_split_paged(q, kc, vc, tb, sl, None, S, ws2)
+    out2 = torch.empty_like(out)
+    lib.tad_combine(ws2, B, H, 1, S, d, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert_parity(out.cpu().numpy(), oracle_of(c), torch.bfloat16, vmax_real(c), "paged interleaved one launch")
