@@ -2,8 +2,10 @@
 groups from 1 to 16, every head dimension and K/V dtype, ragged lengths with zeros,
 1-3 query tokens, ALiBi, automatic and explicit chunk counts from 1 to 300, on
 contiguous, token-major strided and paged caches.  Each case goes through the
-workspace entry points (whichever kernel and merge form the library picks) and is
-compared with the fp64 oracle under the same bars as the other parity tests.
+workspace entry points (whichever kernel and merge form the library picks), is
+compared with the fp64 oracle under the same bars as the other parity tests, and must
+equal tad_split + tad_combine on the same inputs bit for bit (one launch or two, the
+merge keeps the combine's arithmetic).
 """
 import random
 
@@ -40,7 +42,7 @@ def draw_cases(n, seed=2024):
     return cases
 
 
-@pytest.mark.parametrize("case", draw_cases(40), ids=lambda c: "c%d" % c[0])
+@pytest.mark.parametrize("case", draw_cases(80), ids=lambda c: "c%d" % c[0])
 def test_random_shape(lib, case):
     i, B, Hq, Hkv, L, d, kv, nq, ragged, S, alibi = case
     g = torch.Generator().manual_seed(700 + i)
@@ -59,7 +61,14 @@ def test_random_shape(lib, case):
     gd = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in c.items()}
     out = lib.decode(gd["q"], gd["k"], gd["v"], gd["seq_lens"], gd["slopes"], S,
                      k_scale=gd["k_scale"], v_scale=gd["v_scale"])
+    SS = lib.resolve_splits(gd["q"], gd["k"], S)
+    ws = lib.workspace(gd["q"], gd["k"], SS)
+    lib.tad_split(gd["q"], gd["k"], gd["v"], gd["seq_lens"], gd["slopes"], SS, ws, k_scale=gd["k_scale"],
+                  v_scale=gd["v_scale"])
+    sc = torch.full_like(out, float("nan"))
+    lib.tad_combine(ws, B, Hq, nq, SS, d, sc)
     torch.cuda.synchronize()
+    assert torch.equal(out, sc), "random case %d: decode differs from split + combine" % i
     assert_parity(out.cpu().numpy(), ref, kv, vmax_real(c), "random case %d" % i)
 
 
@@ -96,7 +105,7 @@ def token_major(t):
     return t.transpose(1, 2).contiguous().transpose(1, 2)
 
 
-@pytest.mark.parametrize("case", draw_layout_cases(30), ids=lambda c: "l%d-%s" % (c[0], c[1]))
+@pytest.mark.parametrize("case", draw_layout_cases(60), ids=lambda c: "l%d-%s" % (c[0], c[1]))
 def test_random_layout(lib, case):
     i, layout, B, Hq, Hkv, L, d, kv, nq, ragged, S, alibi, ps, head_major = case
     g = torch.Generator().manual_seed(1700 + i)
@@ -118,8 +127,20 @@ def test_random_layout(lib, case):
     q, sl, sp, ks, vs = dv(c["q"]), dv(c["seq_lens"]), dv(c["slopes"]), dv(c["k_scale"]), dv(c["v_scale"])
     if layout == "paged":
         kc, vc, table = W.page_kv(c["k"], c["v"], ps, 1800 + i, head_major=head_major)
-        out = lib.decode_paged(q, dv(kc), dv(vc), dv(table), sl, sp, S, k_scale=ks, v_scale=vs)
+        kc, vc, table = dv(kc), dv(vc), dv(table)
+        out = lib.decode_paged(q, kc, vc, table, sl, sp, S, k_scale=ks, v_scale=vs)
+        # the paged entry point's automatic count sees whole pages: table width x page size
+        SS = S if S > 0 else lib.tad_auto_splits(B, Hq, Hkv, nq, table.shape[1] * kc.shape[1], d, kc.dtype, 0)
+        ws = lib.workspace(q, c["k"], SS)
+        lib.tad_split_paged(q, kc, vc, table, sl, sp, SS, ws, k_scale=ks, v_scale=vs)
     else:
-        out = lib.decode(q, dv(token_major(c["k"])), dv(token_major(c["v"])), sl, sp, S, k_scale=ks, v_scale=vs)
+        k, v = dv(token_major(c["k"])), dv(token_major(c["v"]))
+        out = lib.decode(q, k, v, sl, sp, S, k_scale=ks, v_scale=vs)
+        SS = lib.resolve_splits(q, k, S)
+        ws = lib.workspace(q, k, SS)
+        lib.tad_split(q, k, v, sl, sp, SS, ws, k_scale=ks, v_scale=vs)
+    sc = torch.full_like(out, float("nan"))
+    lib.tad_combine(ws, B, Hq, nq, SS, d, sc)
     torch.cuda.synchronize()
+    assert torch.equal(out, sc), "random layout case %d: decode differs from split + combine" % i
     assert_parity(out.cpu().numpy(), ref, kv, vmax_real(c), "random layout case %d" % i)
