@@ -4,7 +4,8 @@
 // token) row's S chunk partials with merge_row (merge.h): the global max, weights
 // 2^(m_s - M), fixed-order sums, one divide.  The column groups of a row go to
 // separate work-groups, so a row with many chunks (one head cut into hundreds of
-// chunks) is merged by many CUs at once.
+// chunks) is merged by many CUs at once.  Calls with many rows merge 4 rows per
+// work-group instead (combine_rows_kernel), to the same bits.
 // This is the global max / renormalise / sum / divide sequence that tree_attn_decode
 // ("Tree Attention Decoding") performs with one max all-reduce and two sum
 // all-reduces across machines; here the chunks live in one GPU's memory.  The split
@@ -29,16 +30,47 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
                  (int)gridDim.y);
 }
 
+// Many rows of up to 64 chunks (several query tokens per head): work-group r merges
+// rows [R r, R r + R) side by side with merge_rows (merge.h) -- each row to merge_row's
+// bits, every o value loaded in one round of 16-byte loads.  1024 rows of 24 chunks
+// (d = 128): 4.8 us against 6.8 us for one row per work-group with column groups
+// (graph replay); with few rows the column groups' many work-groups are faster (32
+// rows of 32 chunks: 3.5 us against 3.9 us with one row per work-group).
+template <int D, int R>
+__global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(CombineArgs a) {
+    __shared__ __align__(16) float lds[merge_rows_lds_floats(R, 64, D)];
+    const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    const int nr = (int)(rows - r0 < R ? rows - r0 : R);
+    const int S = a.S;
+    auto out_of = [&](int j) {
+        const int64_t row = r0 + j;                // (b * Hq + h) * nq + t
+        const int64_t t = row % a.nq, bh = row / a.nq;
+        return a.out + (bh / a.Hq) * a.sob + (bh % a.Hq) * a.soh + t * a.sot;
+    };
+    merge_rows<D, kCombineThreads>(a.ws_m + r0 * S, a.ws_l + r0 * S, a.ws_o + r0 * S * D, S, S, nr, out_of, lds);
+}
+
+template <int D>
+static void launch_combine_d(const CombineArgs &a, int64_t rows, hipStream_t st) {
+    if (a.S <= 64 && rows >= 1024) {
+        hipLaunchKernelGGL((combine_rows_kernel<D, 4>), dim3((unsigned)((rows + 3) / 4)), dim3(kCombineThreads), 0, st,
+                           a);
+        return;
+    }
+    const dim3 grid((unsigned)rows, (unsigned)merge_column_groups(a.S, D));
+    hipLaunchKernelGGL(combine_kernel<D>, grid, dim3(kCombineThreads), 0, st, a);
+}
+
 hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
     if (rows <= 0) return hipSuccess;
-    if (d != 64 && d != 128 && d != 256 && d != 512) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)rows, (unsigned)merge_column_groups(a.S, d));
     switch (d) {
-        case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kCombineThreads), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kCombineThreads), 0, st, a); break;
-        case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(kCombineThreads), 0, st, a); break;
-        default: hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(kCombineThreads), 0, st, a); break;
+        case 64: launch_combine_d<64>(a, rows, st); break;
+        case 128: launch_combine_d<128>(a, rows, st); break;
+        case 256: launch_combine_d<256>(a, rows, st); break;
+        case 512: launch_combine_d<512>(a, rows, st); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
