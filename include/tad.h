@@ -115,7 +115,7 @@ const char *tad_last_error(void);
  * 128 KiB of K and V per KV head -- or 32 KiB per KV head for grouped-query calls on the
  * matrix-core kernel (bf16 or FP8 K/V, d 64 or 128, 2..16 query rows per KV head) with
  * Hkv a multiple of 4, which it serves 4 KV heads to a work-group when there are at
- * least 128 (row, 4-KV-head group, chunk) items -- and at least one.  Returns the
+ * least 256 (row, 4-KV-head group, chunk) items -- and at least one.  Returns the
  * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
  * d, TAD_EDTYPE for kv_dtype).  (Hq, nq, d and kv_dtype are arguments because the count
  * mirrors the kernel choice and the byte-sized minimum chunk, which depend on them.)

@@ -647,9 +647,10 @@ bool split_mfma_supported(int d, int kv_type, int group, int nq) {
 // below it one KV head per work-group gives 4x the work-groups (one row of 32 query
 // heads over 8 KV heads, 4096 keys at 8 chunks: 16 twelve-wave work-groups 20.7 us,
 // 64 four-wave ones 12.7 us; two rows of 16384 keys at 4 chunks 152.5 -> 50.9 us; at
-// the automatic chunk counts 8.1-9.0 us instead of 10.2-10.7 us on small calls, and
-// the same from 128 items on; graph replay).
-constexpr int64_t kGroupedHeadsMinItems = 128;
+// 128 items still 11.3 -> 10.3 us (4096 keys, 64 chunks), 19.6 -> 15.9 us (16384 keys,
+// 64 chunks), 13.7 -> 11.7 us (two rows, 32 chunks); about even from 256 items on;
+// graph replay).
+constexpr int64_t kGroupedHeadsMinItems = 256;
 
 // The 4-KV-heads-per-work-group variant: a KV head count divisible by 4.
 bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
