@@ -200,8 +200,9 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  *   - the head-packed kernel (caches whose KV heads are interleaved per key, one query
  *     head per KV head), when n_splits <= 8 and B * Hq / 4 * n_splits is at most the
  *     compute-unit count: the last work-group of a (b, 4-head group) merges its 4 rows.
- * Larger problems and chunks read as pieces run the split (and pieces) and combine
- * kernels back to back (the counters are then unused).  Either way the output is bit-identical
+ * Chunks read as pieces (below) on such small grids take two launches: the pieces
+ * kernel's last work-group per row merges the row.  Larger problems run the split
+ * (and pieces) and combine kernels back to back (the counters are then unused).  Either way the output is bit-identical
  * to tad_split followed by tad_combine.  The one-launch form saves a launch where the
  * host's launch rate sets the pace; replayed in a graph it is about as fast as the two
  * kernels, or up to about a microsecond slower.  The counters must be zero the first

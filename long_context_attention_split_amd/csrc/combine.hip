@@ -79,22 +79,45 @@ hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t st) {
 // into the chunk's (m, l, o) with merge_pieces (merge.h), so that the workspace then
 // holds exactly the n_splits chunk partials the caller asked for.  A kernel of its own
 // after the split kernel: the pieces' partials are complete and visible when it starts.
-template <int D>
+// TAIL (a.out non-null, at most kMaxFusedSplits chunks): the chunk partials are written
+// through, and the last of a row's S work-groups to arrive (arrive_last) merges the
+// row with merge_rows -- the combine's bits -- and returns the counter to zero.
+template <int D, bool TAIL>
 __global__ __launch_bounds__(kCombineThreads) void pieces_kernel(PiecesArgs a) {
     __shared__ float lds[64 + kCombineThreads];
     const int64_t r = blockIdx.x;                // (row, chunk)
-    merge_pieces<D, kCombineThreads>(a.sub_m + r * a.P, a.sub_l + r * a.P, a.sub_o + r * a.P * D, a.P,
-                                     a.ws_m + r, a.ws_l + r, a.ws_o + r * D, lds);
+    merge_pieces<D, kCombineThreads, TAIL>(a.sub_m + r * a.P, a.sub_l + r * a.P, a.sub_o + r * a.P * D, a.P,
+                                           a.ws_m + r, a.ws_l + r, a.ws_o + r * D, lds);
+    if constexpr (TAIL) {
+        __shared__ __align__(16) float mlds[merge_rows_lds_floats(1, kMaxFusedSplits, D)];
+        __shared__ int last;
+        const int64_t row = r / a.S;             // b * Hq + h
+        if (arrive_last(a.cnt + row, a.S, &last)) {
+            float *const orow = a.out + (row / a.Hq) * a.sob + (row % a.Hq) * a.soh;
+            merge_rows<D, kCombineThreads>(a.ws_m + row * a.S, a.ws_l + row * a.S, a.ws_o + row * a.S * D, a.S, a.S, 1,
+                                           [&](int) { return orow; }, mlds);
+            reset_counter(a.cnt + row);
+        }
+    }
+}
+
+template <int D>
+static void launch_pieces_d(const PiecesArgs &a, hipStream_t st) {
+    if (a.out)
+        hipLaunchKernelGGL((pieces_kernel<D, true>), dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((pieces_kernel<D, false>), dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a);
 }
 
 hipError_t launch_pieces(const PiecesArgs &a, int d, hipStream_t st) {
     if (a.chunks <= 0) return hipSuccess;
     if (a.P < 1 || a.P > 64 || a.P * d > 16384) return hipErrorInvalidValue;
+    if (a.out && (a.S < 1 || a.S > kMaxFusedSplits || !a.cnt || a.Hq < 1)) return hipErrorInvalidValue;
     switch (d) {
-        case 64: hipLaunchKernelGGL(pieces_kernel<64>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(pieces_kernel<128>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
-        case 256: hipLaunchKernelGGL(pieces_kernel<256>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
-        case 512: hipLaunchKernelGGL(pieces_kernel<512>, dim3((unsigned)a.chunks), dim3(kCombineThreads), 0, st, a); break;
+        case 64: launch_pieces_d<64>(a, st); break;
+        case 128: launch_pieces_d<128>(a, st); break;
+        case 256: launch_pieces_d<256>(a, st); break;
+        case 512: launch_pieces_d<512>(a, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -70,7 +70,9 @@ __device__ __forceinline__ void reset_counter(int32_t *cnt) {
 // the TPC thread parts of a column sums its pieces p in order, and the parts are added
 // in order; l is a wave sum over the pieces.  All P * D values are loaded in one round
 // (at most 64 per thread).  Called by all NT threads; `lds` holds 64 + NT floats.
-template <int D, int NT>
+// WT: write the chunk's partial through to the device coherence point (store_partial),
+// for a row merge in another work-group of the same kernel.
+template <int D, int NT, bool WT = false>
 __device__ __forceinline__ void merge_pieces(const float *m, const float *l, const float *o, int P, float *cm,
                                              float *cl, float *co, float *lds) {
     constexpr int TPC = D >= NT ? 1 : NT / D;      // threads per column
@@ -110,7 +112,8 @@ __device__ __forceinline__ void merge_pieces(const float *m, const float *l, con
             if (p < P) acc = add_weighted(w[p], v[c][i], acc);
         }
         if constexpr (TPC == 1) {
-            co[col0 + c * NT] = acc;
+            if constexpr (WT) store_partial(co + col0 + c * NT, acc);
+            else co[col0 + c * NT] = acc;
         } else {
             sums[tid] = acc;
         }
@@ -121,12 +124,18 @@ __device__ __forceinline__ void merge_pieces(const float *m, const float *l, con
             float t = 0.f;
 #pragma unroll
             for (int k = 0; k < TPC; ++k) t += sums[k * D + tid];
-            co[tid] = t;
+            if constexpr (WT) store_partial(co + tid, t);
+            else co[tid] = t;
         }
     }
     if (tid == 0) {
-        *cm = M;
-        *cl = lsum;
+        if constexpr (WT) {
+            store_partial(cm, M);
+            store_partial(cl, lsum);
+        } else {
+            *cm = M;
+            *cl = lsum;
+        }
     }
 }
 

@@ -365,8 +365,9 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
 // matrix cores; caches whose heads are interleaved per key (one query head per KV
 // head, unfused) on the head-packed vector kernel; everything else on the vector
 // kernel.  Chunks read as pieces (a.P > 1) are then pre-merged by pieces_kernel, so the
-// workspace holds the chunk partials when the launches are done.
-int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream) {
+// workspace holds the chunk partials when the launches are done; with merge_out the
+// pieces kernel also merges each row into merge_out (its last work-group per row).
+int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream, const OutDesc *merge_out = nullptr) {
     hipError_t e;
     if (tad::split_mfma_supported((int)d, a.kv_type, a.group, a.nq))
         e = tad::launch_split_mfma(a, (int)d, stream);
@@ -381,6 +382,11 @@ int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream) {
         pa.ws_m = a.ws_m; pa.ws_l = a.ws_l; pa.ws_o = a.ws_o;
         pa.chunks = (int64_t)a.B * a.Hq * a.nq * a.S;
         pa.P = a.P;
+        pa.S = a.S; pa.Hq = a.Hq;
+        pa.cnt = a.cnt;
+        pa.out = merge_out ? merge_out->data : nullptr;
+        pa.sob = merge_out ? merge_out->sob : 0;
+        pa.soh = merge_out ? merge_out->soh : 0;
         e = tad::launch_pieces(pa, (int)d, stream);
         if (e != hipSuccess) return fail(TAD_EHIP, "pieces kernel launch: %s", hipGetErrorString(e));
     }
@@ -431,6 +437,9 @@ int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const
         (mfma && small && P.B * P.Hkv * (int64_t)S <= cus && tad::split_mfma_fusable(unfused, (int)P.d)) ||
         (heads && small && P.B * (P.Hq / 4) * (int64_t)S <= cus))
         return launch_split(split_args(P, q, k, v, seq_lens, slopes, S, w, out), P.d, stream);
+    // chunks read as pieces: the pieces kernel's last work-group per row merges it
+    if (vector_kernel && unfused.P > 1 && small && P.B * P.Hq * P.nq * (int64_t)S <= cus)
+        return launch_split(unfused, P.d, stream, &out);
     if ((rc = launch_split(unfused, P.d, stream))) return rc;
     return launch_merge(P.B, P.Hq, P.nq, S, P.d, w, out, stream);
 }

@@ -47,12 +47,19 @@ struct SplitArgs {
     float *sub_m, *sub_l, *sub_o;   // [rows * S * P], the same, [rows * S * P * d]
 };
 
-// Pre-merge of the pieces of `chunks` chunks, P pieces each (see SplitArgs).
+// Pre-merge of the pieces of `chunks` chunks, P pieces each (see SplitArgs).  With out
+// non-null (one query row per head), the last chunk of each row to be pre-merged also
+// merges the row's S chunk partials into out (arrival counters cnt [rows], zero on
+// entry and left zero).
 struct PiecesArgs {
     const float *sub_m, *sub_l, *sub_o;
     float *ws_m, *ws_l, *ws_o;
     int64_t chunks;
     int32_t P;
+    int32_t S, Hq;
+    int32_t *cnt;
+    float *out;             // [B, Hq, d] fp32, or null
+    int64_t sob, soh;       // out element strides
 };
 
 struct CombineArgs {
