@@ -5,8 +5,8 @@ on a device.  Each call is checked against tad_decode_ws with the same n_splits 
 for bit: the same kernels, the same chunking) and against the fp64 oracle, on calls in
 a row whose sizes shrink, so that what an earlier call left in the array cannot leak
 into a later one: a large grouped-query decode (matrix cores, split + combine), then a
-one-head decode whose chunks are cut into pieces (chunk and row counters), then a
-small multi-head decode merged in the split kernel.
+one-head decode whose chunks are cut into pieces (merged in the pieces kernel's last
+work-group: row counters), then a small multi-head decode merged in the split kernel.
 """
 import pytest
 import torch
