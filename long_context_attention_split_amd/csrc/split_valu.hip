@@ -41,9 +41,9 @@ namespace tad {
 // re-read the same chunk and should find it in L2.
 // UK: keys per lane group per tile (K and V tiles of UK*16 bytes per lane for bf16).
 // KVT: element type of K and V (kKvF32, kKvBF16, kKvE4M3, kKvE5M2).
-// PAGED: K/V rows come from a paged cache through the block table; every wave tile
-// then lies inside one page (tile length divides the page size) and gets its own
-// buffer resource.
+// PAGED: K/V rows come from a paged cache through the block table; a wave tile is one
+// or two pieces of 16 rows, each inside one page (page sizes are multiples of 16) with
+// its own buffer resource.
 // TAIL: the variant whose last work-group of a row also merges the row (a.fused), kept
 // apart so that the plain kernel carries none of that code or its registers.
 template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PAGED = false,
@@ -58,7 +58,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     constexpr int T = KPW * U;                   // keys per wave tile
     constexpr int NW = kSplitThreads / 64;       // waves per work-group
     constexpr int SLOTS = NW * KPW;              // lane-group states to merge
-    static_assert(!PAGED || T == 16, "paged tiles are 16 keys: page sizes are multiples of 16");
+    // paged: a tile is 1 or 2 pieces of 16 rows, each inside one page (page sizes are
+    // multiples of 16), each with its own block-table lookup
+    constexpr int NSUB = PAGED ? T / 16 : 1;
+    static_assert(!PAGED || ((T == 16 || T == 32) && 16 % KPW == 0), "paged tiles: 16-row pieces");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const uint32_t krow = kvk.row_bytes, vrow = kvv.row_bytes;
     const __amdgpu_buffer_rsrc_t kr = PAGED ? make_rsrc(nullptr, 0u) : kvk.rows(j0, n);
     const __amdgpu_buffer_rsrc_t vr = PAGED ? make_rsrc(nullptr, 0u) : kvv.rows(j0, n);
-    TilePages pages;                                       // paged: this wave's tile pages
+    TilePages pages[NSUB];                                 // paged: this wave's tile pages
 
     // ---- this lane's EPL query elements, pre-scaled into base-2 units (and by the
     // K dequantisation scale, which multiplies every score of this KV head).
@@ -159,19 +162,36 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const uint32_t lane_off = (uint32_t)(sub * EPL * ELEM);
     using Tile = Row[U];
     auto load_tile = [&](Tile &kk, Tile &vv, int t0) {
-        __amdgpu_buffer_rsrc_t krs = kr, vrs = vr;
-        int tb = t0;                                       // first row, relative to the resource
         if constexpr (PAGED) {
-            const int nt = min(T, n - t0);
-            const int page = pages.get(kvk, j0, n, wave * T, NW * T, (t0 - wave * T) / (NW * T));
-            krs = kvk.page_rows(page, j0 + t0, nt);
-            vrs = kvv.page_rows(page, j0 + t0, nt);
-            tb = 0;
+            // piece h: rows [16 h, 16 h + 16) of the tile, from its own page
+            __amdgpu_buffer_rsrc_t krs[NSUB], vrs[NSUB];
+            const int k = (t0 - wave * T) / (NW * T);      // this wave's tile number
+#pragma unroll
+            for (int h = 0; h < NSUB; ++h) {
+                const int th = t0 + 16 * h;
+                const int nt = max(0, min(16, n - th));
+                const int page = pages[h].get(kvk, j0, n, wave * T + 16 * h, NW * T, k);
+                krs[h] = kvk.page_rows(page, j0 + th, nt);
+                vrs[h] = kvv.page_rows(page, j0 + th, nt);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                constexpr int RPP = 16 / KPW;               // load instructions per piece
+                const int h = u / RPP, r = (u % RPP) * KPW + grp;
+                kk[u].load(krs[h], (uint32_t)r * krow + lane_off);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                constexpr int RPP = 16 / KPW;
+                const int h = u / RPP, r = (u % RPP) * KPW + grp;
+                vv[u].load(vrs[h], (uint32_t)r * vrow + lane_off);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) kk[u].load(kr, (uint32_t)(t0 + u * KPW + grp) * krow + lane_off);
+#pragma unroll
+            for (int u = 0; u < U; ++u) vv[u].load(vr, (uint32_t)(t0 + u * KPW + grp) * vrow + lane_off);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) kk[u].load(krs, (uint32_t)(tb + u * KPW + grp) * krow + lane_off);
-#pragma unroll
-        for (int u = 0; u < U; ++u) vv[u].load(vrs, (uint32_t)(tb + u * KPW + grp) * vrow + lane_off);
     };
     // One tile: scores, online max/sum update, value accumulation.
     auto consume = [&](const Tile &kk, const Tile &vv, int t0) {
@@ -285,14 +305,18 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
 
 template <int D, int KVT, bool TAIL>
 static hipError_t launch_tail(const SplitArgs &a, int64_t grid, hipStream_t st) {
-    // paged caches: 16-key wave tiles (page sizes are multiples of 16)
+    // paged caches: 32-key wave tiles of two 16-row pieces, each from its own page (page
+    // sizes are multiples of 16), or 16 keys where 32 would take more than 8 loads per
+    // lane and tensor (4 for FP8, as on contiguous caches).  32 heads x 131072 bf16 keys
+    // in head-major pages, per step: 16-row pages 335.7-336.4 -> 330.2-332.4 us, 64-row
+    // pages 332.5-334.9 -> 324.3-324.8 us against 16-key tiles.
     constexpr int KPW = 64 * RowChunk<KVT, kPolicyNT>::EPL / D;
-    constexpr int UP = 16 / KPW > 0 ? 16 / KPW : 1;
+    constexpr bool F8 = KVT == kKvE4M3 || KVT == kKvE5M2;
+    constexpr int UP = 32 / KPW <= (F8 ? 4 : 8) ? 32 / KPW : 16 / KPW;
     // contiguous caches: 128 bytes of each row per lane and tensor in flight (8 loads),
     // except FP8, whose rows take twice the arithmetic per byte: 4 loads (one row of 32
     // heads x 131072 keys of E4M3: 164.0-164.4 us per step against 168.0-168.2 us with
     // 8, 170-171 with 2, 172-173 with 3)
-    constexpr bool F8 = KVT == kKvE4M3 || KVT == kKvE5M2;
     constexpr int UD = F8 ? 4 : 128 / RowChunk<KVT, kPolicyNT>::kBytes;
     const int gq = a.group * a.nq;
     if (a.block_table) {

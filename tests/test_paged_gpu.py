@@ -57,10 +57,10 @@ def oracle_of(c):
     (2, 8, 2, 1000, 128, 48, torch.float8_e5m2, 6),        # FP8 E5M2, GQA 4, 48-row pages
     (2, 4, 4, 600, 64, 16, torch.float8_e4m3fn, 3),        # FP8, d 64
     (1, 8, 8, 4096, 128, 256, torch.bfloat16, 0),          # 256-row pages, automatic splits
-    (2, 32, 8, 1200, 128, 16, torch.float8_e4m3fn, 32),    # FP8 GQA, 4 KV heads per work-group (128 items)
-    (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 48),       # FP8 E5M2 GQA, 4 KV heads, split + combine
-    (2, 32, 8, 1100, 64, 16, torch.bfloat16, 40),          # d 64 GQA, 4 KV heads per work-group
-    (3, 16, 8, 1000, 64, 32, torch.float8_e4m3fn, 24),     # d 64 FP8 GQA, 4 KV heads, split + combine
+    (2, 32, 8, 1200, 128, 16, torch.float8_e4m3fn, 64),    # FP8 GQA, 4 KV heads per work-group (256 items)
+    (3, 16, 4, 900, 128, 32, torch.float8_e5m2, 96),       # FP8 E5M2 GQA, 4 KV heads, split + combine
+    (2, 32, 8, 1100, 64, 16, torch.bfloat16, 64),          # d 64 GQA, 4 KV heads per work-group
+    (3, 16, 8, 1000, 64, 32, torch.float8_e4m3fn, 48),     # d 64 FP8 GQA, 4 KV heads, split + combine
     (2, 16, 4, 900, 64, 16, torch.float8_e5m2, 7),         # d 64 FP8: 32-key tiles over two 16-row pages, few items
     (2, 8, 2, 777, 128, 16, torch.float8_e4m3fn, 9),       # FP8, one KV head per work-group, 16-row pages
 ])
@@ -95,6 +95,23 @@ def test_paged_head_major_pages(lib, kv, Hq):
     assert c["k_cache"].stride(2) == 32 * 128
     ref = oracle_of(c)
     assert_parity(run_paged(lib, c, 4), ref, kv, vmax_real(c), "head-major")
+
+
+@pytest.mark.parametrize("ps,d,kv", [(16, 128, torch.bfloat16), (48, 128, torch.bfloat16), (32, 64, torch.bfloat16),
+                                     (48, 256, torch.bfloat16), (16, 64, torch.float8_e4m3fn),
+                                     (48, 128, torch.float8_e5m2), (16, 256, torch.float8_e4m3fn)])
+def test_paged_head_major_tiles_across_pages(lib, ps, d, kv):
+    """One query head per KV head on head-major pages (the vector kernel's paged form):
+    its 32-key wave tiles are two 16-row pieces, each looked up in the block table on
+    its own, so a tile may straddle two pages (16- and 48-row pages); ragged lengths
+    that end inside a piece, an empty row, one and several chunks."""
+    note("paged head-major tiles ps=%d d=%d kv=%s" % (ps, d, kv))
+    c = paged_case(700 + ps + d, 3, 4, 4, 1000, d, ps, kv, lens=[1000, 333, 0], head_major=True)
+    ref = oracle_of(c)
+    for S in (1, 3, 0):
+        out = run_paged(lib, c, S)
+        assert_parity(out, ref, kv, vmax_real(c), "head-major tiles ps=%d S=%d" % (ps, S))
+        assert (out[2] == 0).all()
 
 
 def test_paged_entry_points_agree(lib):
