@@ -363,8 +363,7 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
 
 // Launch the split kernel.  Kernel choice: query-head groups and several tokens on the
 // matrix cores; caches whose heads are interleaved per key (one query head per KV
-// head, unfused) on the head-packed vector kernel; everything else on the vector
-// kernel.  Chunks read as pieces (a.P > 1) are then pre-merged by pieces_kernel, so the
+// head) on the head-packed vector kernel; everything else on the vector kernel.  Chunks read as pieces (a.P > 1) are then pre-merged by pieces_kernel, so the
 // workspace holds the chunk partials when the launches are done; with merge_out the
 // pieces kernel also merges each row into merge_out (its last work-group per row).
 int launch_split(const tad::SplitArgs &a, int64_t d, hipStream_t stream, const OutDesc *merge_out = nullptr) {
@@ -418,10 +417,11 @@ int check_splits(int32_t S) {
 // (one row of 32 query heads over 8 KV heads, 4096 keys at 8 chunks: 15.6 vs 18.4 us
 // per call through the Python binding; in a replayed graph 13.3 vs 13.0-13.2 us), and
 // the head-packed kernel's last work-group per (row, 4-head group) merges those 4
-// rows.  With more chunks one work-group's merge costs more than the combine kernel
-// (graph replay, the grouped-query call at 32 chunks: 13.1 vs 9.9 us), so larger grids
-// run split and combine.  Both forms give bit-identical outputs (the merges keep the
-// combine's summation order).
+// rows; a call whose chunks are read as pieces takes two launches, the pieces kernel's
+// last work-group per row merging it.  With more chunks one work-group's merge costs
+// more than the combine kernel (graph replay, the grouped-query call at 32 chunks: 13.1
+// vs 9.9 us), so larger grids run split and combine.  Both forms give bit-identical
+// outputs (the merges keep the combine's summation order).
 int run_decode(const Problem &P, const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                const int32_t *seq_lens, const float *slopes, int32_t S, const WsPtrs &w,
                const OutDesc &out, hipStream_t stream) {
