@@ -80,7 +80,7 @@ def test_interleaved_bf16_query_and_large_logits(lib):
 def test_interleaved_grouped_query_heads(lib, B, Hq, Hkv, nq, S, alibi):
     """Grouped-query heads over a [B, L, Hkv, d] cache with a KV-head count divisible by
     4, on calls with few (row, KV-head group, chunk) items: the matrix-core kernel then
-    serves one KV head per work-group (4 adjacent ones from 128 items on, below)."""
+    serves one KV head per work-group (4 adjacent ones from 256 items on, below)."""
     note("interleaved gqa B=%d Hq=%d Hkv=%d nq=%d S=%d alibi=%s" % (B, Hq, Hkv, nq, S, alibi))
     lens = [1300, 777, 5][:B]
     c = W.random_case(880 + Hkv + nq + S, B, Hq, Hkv, 1300, 128, seq_lens=lens, alibi=alibi)
@@ -116,7 +116,7 @@ def test_interleaved_fp8_grouped_query_heads(lib, kv, S):
 @pytest.mark.parametrize("kv,d,nq,S", [(torch.bfloat16, 128, 1, 16), (torch.float8_e4m3fn, 128, 1, 24),
                                        (torch.bfloat16, 64, 2, 16), (torch.float8_e5m2, 64, 1, 20)])
 def test_interleaved_four_heads_per_work_group(lib, kv, d, nq, S):
-    """Enough (row, 4-KV-head group, chunk) items (8 rows x 2 groups x S >= 128) for the
+    """Enough (row, 4-KV-head group, chunk) items (8 rows x 2 groups x S >= 256) for the
     matrix-core kernel to serve 4 adjacent KV heads per work-group on a [B, L, Hkv, d]
     cache: ragged lengths with an empty row, ALiBi, one and two tokens."""
     note("interleaved 4 heads per work-group kv=%s d=%d nq=%d S=%d" % (kv, d, nq, S))

@@ -238,9 +238,9 @@ def test_fp8_ragged_gqa_alibi(lib, kv):
 @pytest.mark.parametrize("B,Hq,Hkv,d,nq,S", [
     (2, 8, 2, 128, 1, 5),        # 4 heads per KV head, one KV head per work-group
     (2, 32, 8, 128, 1, 3),       # few items: one KV head per work-group
-    (3, 32, 8, 128, 1, 24),      # 4 KV heads per work-group (144 items), many chunks
+    (3, 32, 8, 128, 1, 48),      # 4 KV heads per work-group (288 items), many chunks
     (2, 16, 4, 64, 1, 7),        # d 64
-    (2, 8, 8, 128, 2, 32),       # several tokens, 4 KV heads per work-group (128 items)
+    (2, 8, 8, 128, 2, 64),       # several tokens, 4 KV heads per work-group (256 items)
     (3, 16, 4, 128, 3, 9),       # 4 heads x 3 tokens = 12 columns
     (2, 4, 4, 128, 16, 4),       # 16 tokens fill the 16 columns
     (3, 8, 4, 64, 4, 5),         # d 64, 2 heads x 4 tokens
@@ -423,7 +423,7 @@ def test_split_partials_ragged_batch(lib):
 
 @pytest.mark.parametrize("B,Hq,Hkv,S", [(80, 16, 4, 5), (70, 32, 8, 3), (3, 32, 8, 64), (2, 8, 4, 12)])
 def test_grouped_ragged_rows_busy_first(lib, B, Hq, Hkv, S):
-    """Matrix-core kernel (4 KV heads per work-group from 128 items on): more rows than a
+    """Matrix-core kernel (4 KV heads per work-group from 256 items on): more rows than a
     wave has lanes, zero lengths and many empty chunks.  Work-group k serves the k-th chunk in
     busy-first order; every (row, head, chunk) partial must still be produced exactly
     once."""
