@@ -39,6 +39,8 @@ CASES = [
     (9, 32, 8, 1, 1, 1500, 128, torch.bfloat16, 8, "random", False),   # 32 rows of one KV head, 256 work-groups
     (10, 1, 16, 1, 1, 3000, 64, torch.bfloat16, 2, None, True),        # 16 query heads on one KV head
     (11, 1, 16, 2, 1, 4096, 64, torch.bfloat16, 0, None, False),       # automatic chunk count
+    (12, 100, 4, 1, 1, 300, 128, torch.bfloat16, 2, "random", True),   # more than 64 rows: the other plan path
+    (13, 80, 8, 2, 1, 500, 64, torch.float8_e4m3fn, 1, "random", False),  # 80 rows, one chunk each
 ]
 
 
