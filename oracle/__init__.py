@@ -8,7 +8,8 @@ package imports nothing from the product.
 - ``decode_f64``: the plain definition softmax(q K^T d^-1/2 + bias) V, evaluated
   row by row in double precision by ``decode_f64.c`` (see its header for the
   formula and the pages it follows); fp32, bf16 and OCP fp8 (E4M3, E5M2) keys and
-  values, fp8 with per-(batch, KV head) dequantisation scales.
+  values, fp8 with dequantisation scales per (batch, KV head) or per (batch, KV head,
+  block of key positions).
 - ``alibi_bias``: the bias term that definition adds ("ALiBi with causal=True
   unexpected bias?", causal bias vector example).
 - ``tree``: numpy fp64 split-and-merge decoding (per-chunk peak / mass / value sum,
@@ -55,7 +56,8 @@ def _load():
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_decode_f64.restype = i32
         lib.oracle_decode_f64.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, i64, i64, i64, i64, i64,
-                                          i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32]
+                                          i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, i64, i32, i64,
+                                          vp, i32, vp, i32]
         lib.oracle_alibi_bias.restype = ctypes.c_double
         lib.oracle_alibi_bias.argtypes = [i64, i64, ctypes.c_double]
         lib.oracle_fp8_e4m3.restype = ctypes.c_double
@@ -99,14 +101,16 @@ def _strides(a: np.ndarray):
 
 
 def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]] = None,
-               n_threads: Optional[int] = None, k_scale=None, v_scale=None) -> np.ndarray:
+               n_threads: Optional[int] = None, k_scale=None, v_scale=None, k_scale_block: int = 0,
+               v_scale_block: int = 0) -> np.ndarray:
     """Oracle output (float64).
 
     q [B, Hq, d] or [B, Hq, nq, d] (nq query tokens, the last nq positions of each row,
     causal among themselves); k, v [B, Hkv, Lmax, d] (fp32, bf16 or fp8 torch tensors,
     or numpy float32 / uint16 bf16 bits); seq_lens int32 [B] or None; slopes fp32 [Hq]
     or None; k_scale, v_scale fp32 [B, Hkv] dequantisation scales (real = stored *
-    scale) or None.  ``rows``: flat (b*Hq+h)*nq+t indices to compute (result
+    scale) or None -- or, with k_scale_block / v_scale_block > 0, [B, Hkv, nblk]: key j
+    uses block j // block.  ``rows``: flat (b*Hq+h)*nq+t indices to compute (result
     [len(rows), d]); None for all (result shaped like q).
     """
     lib = _load()
@@ -131,13 +135,22 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
     if slopes is not None:
         sp = np.ascontiguousarray(np.asarray(slopes.cpu() if hasattr(slopes, "cpu") else slopes,
                                              dtype=np.float32))
-    ksc = vsc = None
-    if k_scale is not None:
-        ksc = np.ascontiguousarray(np.asarray(k_scale.cpu() if hasattr(k_scale, "cpu") else k_scale,
-                                              dtype=np.float32)).reshape(-1)
-    if v_scale is not None:
-        vsc = np.ascontiguousarray(np.asarray(v_scale.cpu() if hasattr(v_scale, "cpu") else v_scale,
-                                              dtype=np.float32)).reshape(-1)
+    def scales(x, block, name):
+        if x is None:
+            if block:
+                raise ValueError("%s_scale_block given without %s_scale" % (name, name))
+            return None, 0
+        a = np.ascontiguousarray(np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.float32))
+        if block:
+            if a.ndim != 3 or a.shape[:2] != (B, Hkv) or a.shape[2] * block < Lmax:
+                raise ValueError("%s_scale must be [B, Hkv, >= ceil(Lmax / block)]" % name)
+            return a.reshape(-1), a.shape[2]
+        if a.size != B * Hkv:
+            raise ValueError("%s_scale must hold B * Hkv values" % name)
+        return a.reshape(-1), 0
+
+    ksc, knb = scales(k_scale, k_scale_block, "k")
+    vsc, vnb = scales(v_scale, v_scale_block, "v")
     rw = None
     n_rows = B * Hq * nq
     if rows is not None:
@@ -149,7 +162,8 @@ def decode_f64(q, k, v, seq_lens=None, slopes=None, rows: Optional[Sequence[int]
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
     rc = lib.oracle_decode_f64(ptr(qn), qt, sq[0], sq[1], sq[2], nq, ptr(kn), ptr(vn), kt,
                                sk[0], sk[1], sk[2], sv[0], sv[1], sv[2],
-                               B, Hq, Hkv, Lmax, d, ptr(sl), ptr(sp), ptr(ksc), ptr(vsc), ptr(rw), n_rows,
+                               B, Hq, Hkv, Lmax, d, ptr(sl), ptr(sp), ptr(ksc), ptr(vsc),
+                               int(k_scale_block), int(knb), int(v_scale_block), int(vnb), ptr(rw), n_rows,
                                ptr(out), int(n_threads))
     if rc != 0:
         raise RuntimeError("oracle_decode_f64 failed (%d)" % rc)

@@ -33,10 +33,11 @@
  *     the causal reading (each new token sees the cache up to its own position) is ours,
  *     the usual one for verifying several drafted tokens at once.
  *
- * FP8 keys and values (OCP E4M3 "fn" and E5M2 formats) carry a dequantisation scale per
- * (batch row, KV head): the stored value times the scale is the real value; the scores
- * and the weighted sum use those real values.  (The pages name FP8 attention only; the
- * scale granularity is our reading.)
+ * FP8 keys and values (OCP E4M3 "fn" and E5M2 formats) carry dequantisation scales: one
+ * per (batch row, KV head), or one per (batch row, KV head, block of `block` consecutive
+ * key positions) -- key j uses block j / block.  The stored value times its scale is
+ * the real value; the scores and the weighted sum use those real values.  (The pages
+ * name FP8 attention only; both scale granularities are our reading.)
  *
  * All arithmetic is double precision on exactly widened inputs (bf16 -> fp32 -> fp64
  * and fp8 -> fp64 are exact).  Rows are independent, so rows are spread over POSIX threads; each row
@@ -111,7 +112,10 @@ typedef struct {
     int B, Hq, Hkv, Lmax, d;
     const int32_t *seq_lens;     /* [B] or NULL */
     const float *slopes;         /* [Hq] or NULL */
-    const float *k_scale, *v_scale; /* [B * Hkv] dequantisation scales, or NULL (= 1) */
+    const float *k_scale, *v_scale; /* dequantisation scales, or NULL (= 1): [B * Hkv] when the
+                                       block is 0, else [B * Hkv * nblk] */
+    int k_block, v_block;        /* keys per scale block, or 0 (one scale per (b, KV head)) */
+    int64_t k_nblk, v_nblk;      /* scale blocks per (b, KV head) */
     const int32_t *rows;         /* flat (b*Hq+h)*nq+t indices to compute, or NULL for all */
     int n_rows;
     double *out;                 /* [n_rows, d] */
@@ -135,17 +139,19 @@ static void decode_row(const oracle_job *J, int b, int h, int t, double *s, doub
 
     const int kh = h / (J->Hq / J->Hkv);
     const double scale = 1.0 / sqrt((double)d);
-    const double ks = J->k_scale ? (double)J->k_scale[b * J->Hkv + kh] : 1.0;
-    const double vs = J->v_scale ? (double)J->v_scale[b * J->Hkv + kh] : 1.0;
+    const int64_t bk = (int64_t)b * J->Hkv + kh;
+    const double ks = (J->k_scale && !J->k_block) ? (double)J->k_scale[bk] : 1.0;
+    const double vs = (J->v_scale && !J->v_block) ? (double)J->v_scale[bk] : 1.0;
     const int64_t qoff = (int64_t)b * J->sqb + (int64_t)h * J->sqh + (int64_t)t * J->sqt;
     const int64_t koff = (int64_t)b * J->skb + (int64_t)kh * J->skh;
     const int64_t voff = (int64_t)b * J->svb + (int64_t)kh * J->svh;
 
     /* scores s_j = (q . k_j) / sqrt(d) + beta_j */
     for (int64_t j = 0; j < L; ++j) {
+        const double ksj = J->k_block ? (double)J->k_scale[bk * J->k_nblk + j / J->k_block] : ks;
         double dot = 0.0;
         for (int i = 0; i < d; ++i)
-            dot += widen(J->q, J->q_dtype, qoff + i) * (ks * widen(J->k, J->kv_dtype, koff + j * J->skj + i));
+            dot += widen(J->q, J->q_dtype, qoff + i) * (ksj * widen(J->k, J->kv_dtype, koff + j * J->skj + i));
         s[j] = dot * scale;
         if (J->slopes) s[j] += oracle_alibi_bias(L, j, (double)J->slopes[h]);
     }
@@ -156,9 +162,10 @@ static void decode_row(const oracle_job *J, int b, int h, int t, double *s, doub
     double z = 0.0;
     for (int64_t j = 0; j < L; ++j) {
         double w = exp(s[j] - m);
+        const double vsj = J->v_block ? (double)J->v_scale[bk * J->v_nblk + j / J->v_block] : vs;
         z += w;
         for (int e = 0; e < d; ++e)
-            out[e] += w * (vs * widen(J->v, J->kv_dtype, voff + j * J->svj + e));
+            out[e] += w * (vsj * widen(J->v, J->kv_dtype, voff + j * J->svj + e));
     }
     for (int e = 0; e < d; ++e) out[e] /= z;
 }
@@ -190,7 +197,11 @@ static void *worker(void *p)
  *   q      : [B, Hq, nq, d] with element strides (sqb, sqh, sqt, 1); dtype OR_F32 or OR_BF16
  *   k, v   : [B, Hkv, Lmax, d] with element strides (s?b, s?h, s?j, 1); same dtype
  *            (OR_F32, OR_BF16, OR_FP8_E4M3, OR_FP8_E5M2)
- *   k_scale, v_scale: [B * Hkv] scales (real = stored * scale), or NULL
+ *   k_scale, v_scale: scales (real = stored * scale), or NULL: [B * Hkv] with block 0,
+ *            else [B * Hkv * nblk], key j of (b, kv head kh) using entry
+ *            (b * Hkv + kh) * nblk + j / block
+ *   k_block, v_block: keys per scale block (0: one scale per (b, kv head))
+ *   k_nblk, v_nblk: scale blocks per (b, kv head), at least ceil(Lmax / block)
  *   rows   : flat indices (b*Hq + h)*nq + t to compute (n_rows of them), or NULL for all
  *   out    : [n_rows, d] doubles, row r for rows[r]
  *   n_threads: POSIX threads to use (>= 1)
@@ -203,14 +214,19 @@ int oracle_decode_f64(const void *q, int q_dtype, int64_t sqb, int64_t sqh, int6
                       int B, int Hq, int Hkv, int Lmax, int d,
                       const int32_t *seq_lens, const float *slopes,
                       const float *k_scale, const float *v_scale,
+                      int k_block, int64_t k_nblk, int v_block, int64_t v_nblk,
                       const int32_t *rows, int n_rows, double *out, int n_threads)
 {
     if (!q || !k || !v || !out || B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lmax < 0 || d <= 0 || nq < 1)
         return -1;
     if ((q_dtype != OR_F32 && q_dtype != OR_BF16) || kv_dtype < OR_F32 || kv_dtype > OR_FP8_E5M2)
         return -1;
+    if (k_block < 0 || v_block < 0) return -1;
+    if (k_block && (!k_scale || k_nblk * k_block < (int64_t)Lmax)) return -1;
+    if (v_block && (!v_scale || v_nblk * v_block < (int64_t)Lmax)) return -1;
     oracle_job J = {q, q_dtype, sqb, sqh, sqt, nq, k, v, kv_dtype, skb, skh, skj, svb, svh, svj,
                     B, Hq, Hkv, Lmax, d, seq_lens, slopes, k_scale, v_scale,
+                    k_block, v_block, k_nblk, v_nblk,
                     rows, rows ? n_rows : B * Hq * nq, out, n_threads < 1 ? 1 : n_threads};
     for (int r = 0; rows && r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= B * Hq * nq) return -1;

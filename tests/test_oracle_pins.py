@@ -389,6 +389,73 @@ def test_fp8_scaled_equals_dequantised_fp32(tdt):
     assert not np.allclose(oracle.decode_f64(c["q"], c["k"], c["v"]), out)
 
 
+def block_dequantised(codes, scales, block):
+    """fp64 real values of FP8 codes [B, H, L, d] under block scales [B, H, nblk]: each
+    scale repeated over its block's key positions (numpy's repeat, then cut to L)."""
+    L = codes.shape[2]
+    rep = np.repeat(scales.double().numpy(), block, axis=2)[:, :, :L]
+    return np.nan_to_num(oracle.widen(codes)) * rep[:, :, :, None]
+
+
+@pytest.mark.parametrize("alibi", [False, True])
+@pytest.mark.parametrize("tdt", [torch.float8_e4m3fn, torch.float8_e5m2])
+def test_fp8_block_scales_match_sdpa_on_dequantised(tdt, alibi):
+    """FP8 K/V with one scale per block of key positions (K blocks of 16, V blocks of 32;
+    75 keys, so both last blocks are partial; ragged lengths, GQA) give torch's fp64
+    scaled_dot_product_attention over the dequantised values."""
+    B, Hq, Hkv, L, d, kb, vb = 3, 8, 2, 75, 32, 16, 32
+    lens = [75, 17, 40]
+    c = W.random_case(23, B, Hq, Hkv, L, d, kv_dtype=tdt, seq_lens=lens, alibi=alibi)
+    k, ks = W.draw_kv_fp8_blocks(24, B, Hkv, L, d, kb, tdt)
+    v, vs = W.draw_kv_fp8_blocks(25, B, Hkv, L, d, vb, tdt)
+    out = oracle.decode_f64(c["q"], k, v, seq_lens=c["seq_lens"], slopes=c["slopes"], k_scale=ks, v_scale=vs,
+                            k_scale_block=kb, v_scale_block=vb)
+    q = torch.from_numpy(f64(c["q"])).unsqueeze(2)
+    kd = torch.from_numpy(block_dequantised(k, ks, kb)).repeat_interleave(Hq // Hkv, dim=1)
+    vd = torch.from_numpy(block_dequantised(v, vs, vb)).repeat_interleave(Hq // Hkv, dim=1)
+    mask = torch.full((B, Hq, 1, L), -math.inf, dtype=torch.float64)
+    for b, Lb in enumerate(lens):
+        j = torch.arange(Lb, dtype=torch.float64)
+        bias = torch.zeros(Hq, Lb, dtype=torch.float64)
+        if alibi:
+            bias = -c["slopes"].double().view(Hq, 1) * (Lb - 1 - j).view(1, Lb)
+        mask[b, :, 0, :Lb] = bias
+    ref = torch.nn.functional.scaled_dot_product_attention(q, kd, vd, attn_mask=mask).squeeze(2)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # the block index matters: one block off, or K and V blocks swapped, differ
+    ks_shift = torch.roll(ks, 1, dims=2)
+    assert not np.allclose(oracle.decode_f64(c["q"], k, v, seq_lens=c["seq_lens"], slopes=c["slopes"],
+                                             k_scale=ks_shift, v_scale=vs, k_scale_block=kb,
+                                             v_scale_block=vb), out)
+
+
+def test_fp8_block_scales_zero_query_closed_form():
+    """q = 0: every visible key weighs the same, so the output is the mean of the
+    dequantised value rows of the row's first L_b keys (V blocks of 64 over 150 keys)."""
+    B, Hkv, L, d, vb = 2, 2, 150, 16, 64
+    lens = [150, 70]
+    c = W.random_case(26, B, 2 * Hkv, Hkv, L, d, kv_dtype=torch.float8_e4m3fn, seq_lens=lens,
+                      scale_block=vb)
+    q = torch.zeros_like(c["q"])
+    out = oracle.decode_f64(q, c["k"], c["v"], seq_lens=c["seq_lens"], k_scale=c["k_scale"],
+                            v_scale=c["v_scale"], k_scale_block=vb, v_scale_block=vb)
+    vd = block_dequantised(c["v"], c["v_scale"], vb)
+    for b, Lb in enumerate(lens):
+        for h in range(2 * Hkv):
+            np.testing.assert_allclose(out[b, h], vd[b, h // 2, :Lb].mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_fp8_block_scales_constant_equal_head_scales():
+    """Block scales that repeat the (b, head) scale in every block give exactly the
+    per-(b, head) result."""
+    c = W.random_case(27, B=2, Hq=4, Hkv=2, L=50, d=16, kv_dtype=torch.float8_e4m3fn)
+    out = oracle.decode_f64(c["q"], c["k"], c["v"], k_scale=c["k_scale"], v_scale=c["v_scale"])
+    kb = c["k_scale"][:, :, None].repeat(1, 1, 4).contiguous()
+    vb = c["v_scale"][:, :, None].repeat(1, 1, 2).contiguous()
+    blk = oracle.decode_f64(c["q"], c["k"], c["v"], k_scale=kb, v_scale=vb, k_scale_block=16, v_scale_block=32)
+    np.testing.assert_array_equal(out, blk)
+
+
 # ----------------------------------------------------------------------------- several query tokens
 
 def multi_case(seed, B, Hq, Hkv, nq, L, d, lens=None, alibi=False):

@@ -148,6 +148,30 @@ def draw_kv_fp8(seed: int, B: int, Hkv: int, L: int, d: int, dtype=torch.float8_
     return out, scale
 
 
+def draw_kv_fp8_blocks(seed: int, B: int, Hkv: int, L: int, d: int, block: int, dtype=torch.float8_e4m3fn):
+    """N(0,1) K or V quantised to FP8 with one scale per (b, kv-head, block of ``block`` keys).
+
+    Each block's rows are N(0,1) draws times a seeded amplitude 2^u, u uniform on
+    [-2, 2] (so neighbouring blocks differ in range), divided by the block's
+    amax / (largest finite value of the format) and rounded by Tensor.to.  Returns
+    (stored [B, Hkv, L, d] fp8, scales [B, Hkv, ceil(L / block)] fp32) -- key j's real
+    value is stored * scale[..., j // block]."""
+    g = _gen(seed)
+    nblk = (L + block - 1) // block
+    out = torch.empty((B, Hkv, L, d), dtype=dtype)
+    scale = torch.empty((B, Hkv, nblk), dtype=F32)
+    for b in range(B):
+        for h in range(Hkv):
+            slab = torch.randn((L, d), generator=g, dtype=F32)
+            amp = torch.exp2(torch.rand((nblk,), generator=g, dtype=F32) * 4 - 2)
+            for i in range(nblk):
+                rows = slab[i * block:(i + 1) * block]
+                rows.mul_(amp[i])
+                scale[b, h, i] = float(rows.abs().max()) / FP8_MAX[dtype]
+                out[b, h, i * block:(i + 1) * block].copy_((rows / scale[b, h, i]).to(dtype))
+    return out, scale
+
+
 def draw_seq_lens(seed: int, B: int, lo: int, hi: int) -> torch.Tensor:
     """Integers uniform on [lo, hi] inclusive, int32."""
     return torch.randint(lo, hi + 1, (B,), generator=_gen(seed), dtype=torch.int64).to(torch.int32)
@@ -207,14 +231,22 @@ def plant_dominant_keys(seed: int, q: torch.Tensor, k: torch.Tensor, logit: floa
 
 
 def random_case(seed: int, B: int, Hq: int, Hkv: int, L: int, d: int, q_dtype=F32, kv_dtype=BF16,
-                seq_lens=None, alibi: bool = False, k_scale: float = 1.0, poison_tail: bool = True):
+                seq_lens=None, alibi: bool = False, k_scale: float = 1.0, poison_tail: bool = True,
+                scale_block: int = 0):
     """A small seeded case of arbitrary shape for parity tests (same recipe as the workloads).
 
     FP8 K/V (kv_dtype float8_e4m3fn / float8_e5m2) come with per-(b, kv-head) scales in
-    the returned k_scale / v_scale (None otherwise)."""
+    the returned k_scale / v_scale (None otherwise), or, with ``scale_block`` > 0, with
+    per-(b, kv-head, key block) scales [B, Hkv, ceil(L / scale_block)] from
+    ``draw_kv_fp8_blocks``."""
     q = draw_q(seed, B, Hq, d, q_dtype)
     ks = vs = None
-    if kv_dtype in FP8_MAX:
+    if kv_dtype in FP8_MAX and scale_block > 0:
+        k, ks = draw_kv_fp8_blocks(seed + 1, B, Hkv, L, d, scale_block, kv_dtype)
+        v, vs = draw_kv_fp8_blocks(seed + 2, B, Hkv, L, d, scale_block, kv_dtype)
+        if k_scale != 1.0:
+            ks = ks * k_scale
+    elif kv_dtype in FP8_MAX:
         k, ks = draw_kv_fp8(seed + 1, B, Hkv, L, d, kv_dtype)
         v, vs = draw_kv_fp8(seed + 2, B, Hkv, L, d, kv_dtype)
         if k_scale != 1.0:
