@@ -55,10 +55,11 @@ def kernel_source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: int, page_size: int = 0, tokens: int = 1):
+def read_traffic(workload: int, page_size: int = 0, tokens: int = 1, scale_block: int = 0):
     """HBM bytes per split-kernel launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    tag = "workload%d" % workload + ("_tokens%d" % tokens if tokens > 1 else "")
+    tag = ("workload%d" % workload + ("_tokens%d" % tokens if tokens > 1 else "")
+           + ("_block%d" % scale_block if scale_block else ""))
     if page_size:
         names = ["split_paged%d_%s_traffic.txt" % (page_size, tag)]
     else:
@@ -96,7 +97,8 @@ def cpu_baseline(c, cpu_seconds_target: float = 10.0):
     while passes == 0 or (total * threads < cpu_seconds_target and passes < 1000):
         t0 = time.perf_counter()
         o = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
-                              n_threads=threads, k_scale=c["k_scale"], v_scale=c["v_scale"])
+                              n_threads=threads, k_scale=c["k_scale"], v_scale=c["v_scale"],
+                              k_scale_block=c.get("scale_block", 0), v_scale_block=c.get("scale_block", 0))
         total += time.perf_counter() - t0
         passes += 1
         if out is None:
@@ -243,7 +245,11 @@ def load_inputs(args, wid, dev):
     import workloads as W
     w = W.WORKLOADS[wid]
     t_gen = time.perf_counter()
-    c = W.make_workload(wid)
+    sb = getattr(args, "scale_block", 0)
+    if sb and w.kv_dtype not in W.FP8_MAX:
+        raise SystemExit("--scale-block needs an FP8 workload (6 or 7)")
+    c = W.make_workload(wid, sb)
+    c["scale_block"] = sb
     print("[bench] workload %d generated in %.1fs" % (wid, time.perf_counter() - t_gen), file=sys.stderr, flush=True)
     if args.tokens > 1:                    # same K/V, nq query tokens per (row, head)
         B0, Hq0, d0 = c["q"].shape
@@ -276,17 +282,22 @@ def load_inputs(args, wid, dev):
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    if sb and table is not None:           # scales cover the paged cache's logical length
+        n = -(-table.shape[1] * args.page_size // sb)
+        pad = lambda s: torch.cat([s, torch.ones(s.shape[0], s.shape[1], n - s.shape[2], device=dev)], 2)
+        ks, vs = pad(ks), pad(vs)
+
     def decode():
         if table is not None:
-            tad.tad_decode_paged_ws(q, k, v, table, sl, sp, S, out, ws, stream, ks, vs)
+            tad.tad_decode_paged_ws(q, k, v, table, sl, sp, S, out, ws, stream, ks, vs, sb, sb)
         else:
-            tad.tad_decode_ws(q, k, v, sl, sp, S, out, ws, stream, ks, vs)
+            tad.tad_decode_ws(q, k, v, sl, sp, S, out, ws, stream, ks, vs, sb, sb)
 
     def split():
         if table is not None:
-            tad.tad_split_paged(q, k, v, table, sl, sp, S, ws, stream, ks, vs)
+            tad.tad_split_paged(q, k, v, table, sl, sp, S, ws, stream, ks, vs, sb, sb)
         else:
-            tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs)
+            tad.tad_split(q, k, v, sl, sp, S, ws, stream, ks, vs, sb, sb)
 
     return dict(w=w, c=c, q=q, k=k, v=v, out=out, ws=ws, S=S, nq=nq, B=B, Hq=Hq, Hkv=Hkv, Lmax=Lmax, d=d,
                 stream=stream, decode=decode, split=split, kv_bytes=w.kv_bytes(c["seq_lens"]))
@@ -418,6 +429,9 @@ def main(argv=None) -> int:
     ap.add_argument("--tokens", type=int, default=1,
                     help="query tokens per row (several: the rows' last positions, as in "
                          "speculative decoding; K/V are read once for all of them)")
+    ap.add_argument("--scale-block", type=int, default=0,
+                    help="FP8 workloads: quantise K and V with one scale per block of this many keys "
+                         "(a power of two, 16 to 65536) instead of one per (row, KV head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB elementwise copy (reference for HBM byte counters)")
@@ -472,7 +486,7 @@ def main(argv=None) -> int:
     print("[bench] step %.1f us (split kernel alone %.1f us), %.0f GB/s" %
           (ms_per_step * 1e3, split_avg * 1e3, gbs), file=sys.stderr, flush=True)
 
-    traffic = read_traffic(args.workload, args.page_size, nq)
+    traffic = read_traffic(args.workload, args.page_size, nq, args.scale_block)
     kv_name = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8-e4m3",
                torch.float8_e5m2: "fp8-e5m2"}[w.kv_dtype]
     result = {
@@ -492,7 +506,8 @@ def main(argv=None) -> int:
         "kv_dtype": kv_name,
         "data": "synthetic",
         "config": {
-            "workload": w.name + (", %d query tokens per row" % nq if nq > 1 else ""),
+            "workload": w.name + (", %d query tokens per row" % nq if nq > 1 else "")
+                        + (", K/V scales per %d-key block" % args.scale_block if args.scale_block else ""),
             "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": Lmax, "tokens": nq,
             "n_splits": S, "kv_bytes_per_step": kv_bytes,
             "step": "tad_decode_paged_ws" if args.page_size else "tad_decode_ws",

@@ -32,10 +32,15 @@
  *  - k, v: [B, Hkv, Lmax, d] or [B, Lmax, d] (then Hkv = 1); same dtype (TAD_F32,
  *          TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2) and shape; any outer strides (e.g.
  *          a [B, Lmax, Hkv, d] cache viewed as [B, Hkv, Lmax, d]).  Hq must be a
- *          multiple of Hkv.  FP8 tensors may carry a dequantisation scale (the
- *          tensor's `scale`: device fp32 [B * Hkv], index b * Hkv + kv_head; the real
- *          value is stored * scale; NULL means 1).  `scale` must be NULL for every
- *          other tensor.
+ *          multiple of Hkv.  FP8 tensors may carry dequantisation scales (the
+ *          tensor's `scale`; the real value is stored * scale; NULL means 1): with
+ *          `scale_block` = 0 one per (b, kv head), device fp32 [B * Hkv], index
+ *          b * Hkv + kv_head; with `scale_block` = n > 0 (a power of two, 16 to
+ *          65536) one per (b, kv head, block of n consecutive key positions), device
+ *          fp32 [B * Hkv * nblk] with nblk = ceil(Lcap / n) (Lcap: Lmax, or
+ *          max_pages * page_size for a paged cache), key j using index
+ *          (b * Hkv + kv_head) * nblk + j / n.  K and V choose independently.
+ *          `scale` must be NULL and `scale_block` 0 for every other tensor.
  *  - out : like q ([B, Hq, d] or [B, Hq, nq, d]), TAD_F32.
  *  - d (head dimension) must be 64, 128, 256 or 512.
  *  - seq_lens: DEVICE int32 [B] or NULL (every row uses Lmax).  Values are clamped
@@ -51,9 +56,9 @@
  *    tokens, bf16 or FP8 K/V, d 64 or 128) lengthens c when the batch's non-empty
  *    chunks would need more work-groups than the device runs at once, to the shortest
  *    length that fits (decided on the device from the row lengths); for it n_splits
- *    is the finest chunking.  (The result does not depend on the chunking; with one
- *    chunk length every non-empty work-group of a ragged batch has the same amount
- *    of work.)
+ *    is the finest chunking.  With block scales c is rounded up to whole blocks of
+ *    K and V.  (The result does not depend on the chunking; with one chunk length
+ *    every non-empty work-group of a ragged batch has the same amount of work.)
  *  - stream: HIP stream (0 = default stream).  All tensors are owned by the caller
  *    and must stay valid until the stream work completes.  The library never frees
  *    caller memory and keeps no state besides a per-device compute-unit count.
@@ -73,7 +78,7 @@
 extern "C" {
 #endif
 
-#define TAD_VERSION 20000 /* major*10000 + minor*100 + patch */
+#define TAD_VERSION 20100 /* major*10000 + minor*100 + patch */
 
 /* FP8 formats are the OCP ones: E4M3 "fn" (no infinities, max 448) and E5M2. */
 enum tad_dtype { TAD_F32 = 0, TAD_BF16 = 1, TAD_FP8_E4M3 = 2, TAD_FP8_E5M2 = 3 };
@@ -94,9 +99,12 @@ typedef struct tad_tensor {
     int32_t ndim;       /* 3 or 4 */
     int64_t shape[4];
     int64_t stride[4];  /* elements */
-    const float *scale; /* FP8 k/v only: device fp32 [B * Hkv] dequantisation scales, or NULL
+    const float *scale; /* FP8 k/v only: device fp32 dequantisation scales, or NULL
                            (a field beyond data/dtype/ndim/shape/stride because FP8 K/V need a
                            per-(b, KV head) scale, folded into q and into the partials) */
+    int32_t scale_block; /* FP8 k/v only: 0 = one scale per (b, KV head); n = one per block
+                            of n key positions (a power of two, 16..65536; the per-block
+                            form applies each key's scale to its score and value weight) */
 } tad_tensor;
 
 /* Library version, TAD_VERSION of the build. */
@@ -148,7 +156,7 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  * (one head cut into 8 chunks is 8 work-groups), so where the vector kernel serves one
  * query row per KV head, each chunk of at least 256 KiB of K+V is read by up to Pmax
  * work-groups, each a contiguous piece of ceil(c / P) keys (whole pages for a paged
- * cache) with P = min(Pmax, chunk bytes / 128 KiB); a second kernel then merges each
+ * cache, whole scale blocks with block scales) with P = min(Pmax, chunk bytes / 128 KiB); a second kernel then merges each
  * chunk's pieces into the chunk's (m, l, o) by the same rescale-and-sum.  The chunks
  * themselves, and so the partials tad_split reports, are those n_splits asks for; only
  * their rounding differs from an uncut chunk.  P depends on the call's sizes only, so
@@ -248,15 +256,17 @@ int tad_decode_noalloc(const tad_tensor *q, const tad_tensor *k, const tad_tenso
  * layout is not on the pages; it only changes where key j of row b is read:
  * page block_table[b * max_pages + j / page_size], row j % page_size of that page.
  *  - k_cache, v_cache: 4-D [num_pages, page_size, Hkv, d], same dtype and shape,
- *    TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2 (FP8 with the per-(b, kv head) `scale`
- *    described above); innermost stride 1, any outer strides, rows 16-byte aligned;
+ *    TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2 (FP8 with the `scale` and `scale_block`
+ *    described above, blocks counted in logical key positions); innermost stride 1,
+ *    any outer strides, rows 16-byte aligned;
  *    page_size a multiple of 16; d 64, 128 or 256.
  *  - pages->block_table: DEVICE int32 [B, max_pages], row-major, pages->max_pages
  *    >= 1.  The logical length is Lmax = max_pages * page_size; only the entries
  *    covering the first L_b keys of row b are read.  An entry outside [0, num_pages)
  *    is not checked on the host (the table lives on the device): its keys and
  *    values read as zeros, and no memory outside the cache is touched.
- *  - The chunk length c = ceil(Lref / n_splits) is rounded up to whole pages.
+ *  - The chunk length c = ceil(Lref / n_splits) is rounded up to whole pages (and
+ *    scale blocks).
  * q, out, seq_lens, alibi_slopes, n_splits, the workspace and the error codes are
  * as for tad_split / tad_decode_ws / tad_decode; the result equals theirs on the
  * gathered [B, Hkv, Lmax, d] K and V up to rounding (the chunk boundaries, and so

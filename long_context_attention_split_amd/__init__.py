@@ -19,7 +19,8 @@ and ``decode(...)`` allocates ``out`` and the workspace with torch and calls
 ``tad_decode_ws``.  Tensors: q [B, Hq, d] or [B, Hq, nq, d] (nq new tokens, causal)
 fp32/bf16; k, v [B, Hkv, Lmax, d]
 fp32/bf16/float8_e4m3fn/float8_e5m2 (innermost dim contiguous; FP8 with optional
-k_scale / v_scale fp32 [B, Hkv]); seq_lens int32 [B] or None; alibi_slopes fp32
+k_scale / v_scale fp32 [B, Hkv], or [B, Hkv, nblk] with k_scale_block / v_scale_block
+keys per scale block); seq_lens int32 [B] or None; alibi_slopes fp32
 [Hq] or None; out fp32 shaped like q.  All must live on the GPU.
 
 There is no fallback: if ``libtad.so`` has not been built, ``load()`` raises.
@@ -44,7 +45,8 @@ EXPORTS = ("tad_version", "tad_last_error", "tad_auto_splits", "tad_workspace_by
 
 class TadTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
-                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4), ("scale", ctypes.c_void_p)]
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4), ("scale", ctypes.c_void_p),
+                ("scale_block", ctypes.c_int32)]
 
 
 class TadPagedKv(ctypes.Structure):
@@ -116,9 +118,10 @@ def dtype_code(dtype) -> int:
             torch.float8_e5m2: TAD_FP8_E5M2}.get(dtype, -1)
 
 
-def describe(t, scale=None) -> TadTensor:
+def describe(t, scale=None, scale_block: int = 0) -> TadTensor:
     """tad_tensor for a torch tensor (no copy; the tensor must outlive the call's work).
-    ``scale``: fp32 [B, Hkv] dequantisation scales of an FP8 k or v, or None."""
+    ``scale``: fp32 dequantisation scales of an FP8 k or v ([B, Hkv], or [B, Hkv, nblk]
+    with ``scale_block`` keys per block), or None."""
     dt = dtype_code(t.dtype)
     if t.dim() > 4:
         raise ValueError("tensors have at most 4 dims")
@@ -130,6 +133,7 @@ def describe(t, scale=None) -> TadTensor:
         d.shape[i] = t.shape[i]
         d.stride[i] = t.stride(i)
     d.scale = None if scale is None else scale.data_ptr()
+    d.scale_block = int(scale_block)
     return d
 
 
@@ -178,9 +182,9 @@ def tad_workspace_clear(ws, stream=None) -> int:
 
 
 def tad_split(q, k, v, seq_lens, alibi_slopes, n_splits: int, ws, stream=None, k_scale=None,
-              v_scale=None) -> int:
+              v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv = describe(q), describe(k, k_scale), describe(v, v_scale)
+    dq, dk, dv = describe(q), describe(k, k_scale, k_scale_block), describe(v, v_scale, v_scale_block)
     return _check(lib.tad_split(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                 _ptr(alibi_slopes), n_splits, ws.data_ptr(), ws.numel() * ws.element_size(),
                                 _stream(stream)))
@@ -194,26 +198,29 @@ def tad_combine(ws, B: int, Hq: int, nq: int, n_splits: int, d: int, out, stream
 
 
 def tad_decode_ws(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, ws, stream=None, k_scale=None,
-                  v_scale=None) -> int:
+                  v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
+    dq, do = describe(q), describe(out)
+    dk, dv = describe(k, k_scale, k_scale_block), describe(v, v_scale, v_scale_block)
     return _check(lib.tad_decode_ws(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                     _ptr(alibi_slopes), n_splits, ctypes.byref(do), ws.data_ptr(),
                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def tad_decode(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None, k_scale=None,
-               v_scale=None) -> int:
+               v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
+    dq, do = describe(q), describe(out)
+    dk, dv = describe(k, k_scale, k_scale_block), describe(v, v_scale, v_scale_block)
     return _check(lib.tad_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                  _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
 
 
 def tad_decode_noalloc(q, k, v, seq_lens, alibi_slopes, n_splits: int, out, stream=None, k_scale=None,
-                       v_scale=None) -> int:
+                       v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k, k_scale), describe(v, v_scale), describe(out)
+    dq, do = describe(q), describe(out)
+    dk, dv = describe(k, k_scale, k_scale_block), describe(v, v_scale, v_scale_block)
     return _check(lib.tad_decode_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(seq_lens),
                                          _ptr(alibi_slopes), n_splits, ctypes.byref(do), _stream(stream)))
 
@@ -230,18 +237,21 @@ def paged(block_table) -> TadPagedKv:
 
 
 def tad_split_paged(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n_splits: int, ws, stream=None,
-                    k_scale=None, v_scale=None) -> int:
+                    k_scale=None, v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv, pg = describe(q), describe(k_cache, k_scale), describe(v_cache, v_scale), paged(block_table)
+    dq, pg = describe(q), paged(block_table)
+    dk, dv = describe(k_cache, k_scale, k_scale_block), describe(v_cache, v_scale, v_scale_block)
     return _check(lib.tad_split_paged(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(pg),
                                       _ptr(seq_lens), _ptr(alibi_slopes), n_splits, ws.data_ptr(),
                                       ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def tad_decode_paged_ws(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n_splits: int, out, ws,
-                        stream=None, k_scale=None, v_scale=None) -> int:
+                        stream=None, k_scale=None, v_scale=None, k_scale_block: int = 0,
+                        v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k_cache, k_scale), describe(v_cache, v_scale), describe(out)
+    dq, do = describe(q), describe(out)
+    dk, dv = describe(k_cache, k_scale, k_scale_block), describe(v_cache, v_scale, v_scale_block)
     pg = paged(block_table)
     return _check(lib.tad_decode_paged_ws(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(pg),
                                           _ptr(seq_lens), _ptr(alibi_slopes), n_splits, ctypes.byref(do),
@@ -249,9 +259,10 @@ def tad_decode_paged_ws(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes
 
 
 def tad_decode_paged(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n_splits: int, out, stream=None,
-                     k_scale=None, v_scale=None) -> int:
+                     k_scale=None, v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0) -> int:
     lib = load()
-    dq, dk, dv, do = describe(q), describe(k_cache, k_scale), describe(v_cache, v_scale), describe(out)
+    dq, do = describe(q), describe(out)
+    dk, dv = describe(k_cache, k_scale, k_scale_block), describe(v_cache, v_scale, v_scale_block)
     pg = paged(block_table)
     return _check(lib.tad_decode_paged(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(pg),
                                        _ptr(seq_lens), _ptr(alibi_slopes), n_splits, ctypes.byref(do),
@@ -259,7 +270,7 @@ def tad_decode_paged(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, n
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens=None, alibi_slopes=None, n_splits: int = 0,
-                 stream=None, k_scale=None, v_scale=None):
+                 stream=None, k_scale=None, v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0):
     """out = tad_decode_paged_ws(...) with torch-allocated out and workspace."""
     torch = _torch()
     B, Hq, d = q.shape[0], q.shape[1], q.shape[-1]
@@ -270,7 +281,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens=None, alibi_slopes=N
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     tad_decode_paged_ws(q, k_cache, v_cache, block_table, seq_lens, alibi_slopes, S, out, ws, stream,
-                        k_scale, v_scale)
+                        k_scale, v_scale, k_scale_block, v_scale_block)
     return out
 
 
@@ -306,23 +317,25 @@ def workspace(q, k, n_splits: int):
 
 
 def decode(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 0, stream=None, k_scale=None,
-           v_scale=None):
+           v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0):
     """out = tad_decode_ws(...) with torch-allocated out [B, Hq, d] fp32 and workspace."""
     torch = _torch()
     S = resolve_splits(q, k, n_splits)
     ws = workspace(q, k, S)
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    tad_decode_ws(q, k, v, seq_lens, alibi_slopes, S, out, ws, stream, k_scale, v_scale)
+    tad_decode_ws(q, k, v, seq_lens, alibi_slopes, S, out, ws, stream, k_scale, v_scale, k_scale_block,
+                  v_scale_block)
     return out
 
 
 def split_partials(q, k, v, seq_lens=None, alibi_slopes=None, n_splits: int = 1, stream=None,
-                   k_scale=None, v_scale=None):
+                   k_scale=None, v_scale=None, k_scale_block: int = 0, v_scale_block: int = 0):
     """Run tad_split only; returns (m, l, o) views of the workspace:
     m, l [B, Hq, S] (m in base-2 units), o [B, Hq, S, d]."""
     torch = _torch()
     ws = workspace(q, k, n_splits)
-    tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream, k_scale, v_scale)
+    tad_split(q, k, v, seq_lens, alibi_slopes, n_splits, ws, stream, k_scale, v_scale, k_scale_block,
+              v_scale_block)
     B, Hq, Hkv, Lmax, d = shape_of(q, k)
     nq = tokens_of(q)
     n = B * Hq * nq * n_splits

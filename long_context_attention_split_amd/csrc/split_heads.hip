@@ -17,6 +17,10 @@
 // per head through LDS at the end.  A launch (B * Hq / 4 * S work-groups of 16 waves)
 // has as many waves as split_valu's for the same chunk count.
 //
+// FP8 block scales: a tile's U keys (a power of two, at most 16) lie in one block, since
+// blocks hold at least 16 keys and chunks start on block boundaries, so each lane group
+// loads its head's K and V scale once per tile.
+//
 // Every K and V byte of a chunk is read once, with 16-byte buffer loads; loads past
 // the chunk end return zero.  Every chunk has its work-group, so an empty chunk writes
 // the merge identity (m = -inf, l = 0, o = 0) itself.
@@ -90,11 +94,15 @@ constexpr int kHeadsThreads = 64 * kHeadsWaves;
 // (arrive_last: agent-scope acq_rel ticket on the group's counter) merges the group's 4
 // rows with merge_rows -- the combine's arithmetic, so the same bits -- and returns
 // the counter to zero.
-template <int D, int KVT, bool PAGED, bool TAIL = false>
+// BLK: FP8 K/V with block scales (kernels of their own, so that the per-(b, KV head)
+// kernels keep their registers and schedule).
+template <int D, int KVT, bool PAGED, bool TAIL = false, bool BLK = false>
 __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a) {
     constexpr int G = kHeadLanes, HPW = kHeadsPerWave, NW = kHeadsWaves;
     constexpr int EPL = D / G;
     using Row = HeadSlice<KVT, EPL>;
+    constexpr bool F8 = KVT == kKvE4M3 || KVT == kKvE5M2;
+    static_assert(!BLK || F8, "block scales are for FP8 K/V");
     // keys per wave tile (a power of two <= 16, so it divides every page size): K and
     // V tiles of 16 KiB per wave for bf16 slices up to 16 bytes, 8 KiB otherwise --
     // FP8 widening and 16-element slices need the registers
@@ -132,7 +140,8 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
     // dequantisation scale of the head.
     float qv[EPL];
     {
-        const float qs = a.qscale * (a.k_scale ? a.k_scale[b * a.Hkv + h] : 1.f);
+        const bool k_head = a.k_scale && (!BLK || !a.k_blk_lg);   // one K scale per (b, KV head)
+        const float qs = a.qscale * (k_head ? a.k_scale[b * a.Hkv + h] : 1.f);
         const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + sub * EPL;
         if (a.q_bf16) {
             const uint16_t *qp = (const uint16_t *)a.q + qoff;
@@ -169,6 +178,13 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
         for (int u = 0; u < U; ++u) kk[u].load(krs, (uint32_t)(tb + u) * krow + lane_off);
 #pragma unroll
         for (int u = 0; u < U; ++u) vv[u].load(vrs, (uint32_t)(tb + u) * vrow + lane_off);
+        // FP8 block scales of the tile, loaded behind its K and V rows
+        float kst = 1.f, vst = 1.f;
+        if constexpr (BLK) {
+            const int jt = __builtin_amdgcn_readfirstlane(j0 + t0);
+            if (a.k_blk_lg) kst = block_scale(a.k_scale, a.k_blk_lg, a.k_nblk, b * a.Hkv + h, jt);
+            if (a.v_blk_lg) vst = block_scale(a.v_scale, a.v_blk_lg, a.v_nblk, b * a.Hkv + h, jt);
+        }
 
         float sc[U];
 #pragma unroll
@@ -179,6 +195,10 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc = fmaf(qv[e], kf[e], acc);
             sc[u] = group_sum<G>(acc);
+        }
+        if constexpr (BLK) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) sc[u] *= kst;
         }
         if (alibi) {
 #pragma unroll
@@ -202,10 +222,12 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
         for (int u = 0; u < U; ++u) {
             const float p = exp2_fast(sc[u] - m_use);
             l += p;
+            float pv = p;
+            if constexpr (BLK) pv = p * vst;
             float vf[EPL];
             vv[u].widen(vf);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
+            for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
         }
         m = m_new;
     }
@@ -249,7 +271,8 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
         float acc = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) acc = fmaf(lds_w[w][g], lds_o[w][i], acc);
-        const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + h0 + g] : 1.f;
+        const bool v_head = a.v_scale && (!BLK || !a.v_blk_lg);
+        const float vsc = v_head ? a.v_scale[b * a.Hkv + h0 + g] : 1.f;
         const int64_t r = ((int64_t)b * a.Hq + h0 + g) * S + s;
         if constexpr (TAIL) store_partial(a.ws_o + r * D + e, acc * vsc);
         else a.ws_o[r * D + e] = acc * vsc;
@@ -280,36 +303,37 @@ bool split_heads_supported(const SplitArgs &a, int d) {
     return a.skj >= (int64_t)kHeadsPerWave * d && a.svj >= (int64_t)kHeadsPerWave * d;
 }
 
-template <int D, int KVT>
+template <int D, int KVT, bool BLK = false>
 static hipError_t launch_ht(const SplitArgs &a, hipStream_t st) {
     const int64_t grid = (int64_t)a.B * (a.Hq / kHeadsPerWave) * a.S;
     if (grid <= 0) return hipSuccess;
     if (a.fused && a.S > kMaxFusedSplits) return hipErrorInvalidValue;
     if (a.block_table) {
         if (a.fused)
-            hipLaunchKernelGGL((split_heads_kernel<D, KVT, true, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0,
-                               st, a);
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, true, true, BLK>), dim3((unsigned)grid),
+                               dim3(kHeadsThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((split_heads_kernel<D, KVT, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0, st,
-                               a);
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, true, false, BLK>), dim3((unsigned)grid),
+                               dim3(kHeadsThreads), 0, st, a);
     } else {
         if (a.fused)
-            hipLaunchKernelGGL((split_heads_kernel<D, KVT, false, true>), dim3((unsigned)grid), dim3(kHeadsThreads), 0,
-                               st, a);
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, false, true, BLK>), dim3((unsigned)grid),
+                               dim3(kHeadsThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((split_heads_kernel<D, KVT, false>), dim3((unsigned)grid), dim3(kHeadsThreads), 0, st,
-                               a);
+            hipLaunchKernelGGL((split_heads_kernel<D, KVT, false, false, BLK>), dim3((unsigned)grid),
+                               dim3(kHeadsThreads), 0, st, a);
     }
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_hd(const SplitArgs &a, hipStream_t st) {
+    const bool blk = a.k_blk_lg || a.v_blk_lg;         // FP8 block scales: kernels of their own
     switch (a.kv_type) {
         case kKvF32: return launch_ht<D, kKvF32>(a, st);
         case kKvBF16: return launch_ht<D, kKvBF16>(a, st);
-        case kKvE4M3: return launch_ht<D, kKvE4M3>(a, st);
-        case kKvE5M2: return launch_ht<D, kKvE5M2>(a, st);
+        case kKvE4M3: return blk ? launch_ht<D, kKvE4M3, true>(a, st) : launch_ht<D, kKvE4M3>(a, st);
+        case kKvE5M2: return blk ? launch_ht<D, kKvE5M2, true>(a, st) : launch_ht<D, kKvE5M2>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -171,14 +171,20 @@ __device__ __forceinline__ void wave_zero_rows(const SplitArgs &a, const WorkIte
 // as they are, the V^T operands through gfx950's 8-bit transposing LDS read
 // (ds_read_b64_tr_b8), and both are widened to bf16 in registers (exact: every E4M3
 // and E5M2 value is a bf16 number).  The value product then runs on
-// v_mfma_f32_16x16x32_bf16 over the 32 keys.
+// v_mfma_f32_16x16x32_bf16 over the 32 keys.  Dequantisation scales per (b, KV head)
+// are folded into q (K) and into the wave's O (V); scales per block of key positions
+// multiply each 16-key score block (K) and each probability before it becomes the
+// value product's operand (V), while l sums the unscaled probabilities.
 // WT: the partial is written through to the device coherence point (store_partial),
 // for a merge in another work-group of the same launch (the fused form).
-template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false>
+// BLK: FP8 K/V with block scales (kernels of their own, so that the per-(b, KV head)
+// kernels keep their registers and schedule).
+template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false, bool BLK = false>
 __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int c, const int Lb,
                                                 uint4 *smem, float (*lds_ml)[HG * NWH][16], int *lds_cnt) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr bool F8 = KVT != kKvBF16;
+    static_assert(!BLK || F8, "block scales are for FP8 K/V");
     constexpr int ELEM = F8 ? 1 : 2;     // bytes per K/V element
     constexpr int NKK = D / 32;          // 32-wide slices of d (score reduction)
     constexpr int NB = D / 16;           // 16-wide column blocks of the output
@@ -300,8 +306,10 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 
     // ---- B operands of the score product: q of head j16, dims 32kk + 8c4 + t, as hi/lo,
     // scaled into base-2 units and by the K dequantisation scale of the KV head (FP8).
-    const float qs = a.qscale * ((F8 && a.k_scale) ? a.k_scale[b * a.Hkv + kvh] : 1.f);
-    const float vs = (F8 && a.v_scale) ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // applied to this wave's O
+    const bool k_head = F8 && a.k_scale && (!BLK || !a.k_blk_lg);   // one K scale per (b, KV head)
+    const bool v_head = F8 && a.v_scale && (!BLK || !a.v_blk_lg);
+    const float qs = a.qscale * (k_head ? a.k_scale[b * a.Hkv + kvh] : 1.f);
+    const float vs = v_head ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // applied to this wave's O
     uint4 qhi[NKK], qlo[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -374,7 +382,22 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 
     // ALIBI: add the per-head linear bias (wave-uniform: its own loop body).  Only tiles
     // reaching past some column's visible limit run the masking.
-    auto consume = [&](const TileOps &ops, int t0, auto alibi_c) {
+    // FP8 block scales of the tile at t0: a 16-key score block lies in one block (blocks
+    // hold at least 16 keys; chunks start on block boundaries), so each takes one K and
+    // one V scale (scalar loads, issued with the tile's own loads).
+    struct TileScales {
+        float k[NSB], v[NSB];
+    };
+    auto load_scales = [&](int t0, TileScales &ts) {
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int jb = __builtin_amdgcn_readfirstlane(j0 + t0 + 16 * sb);
+            ts.k[sb] = a.k_blk_lg ? block_scale(a.k_scale, a.k_blk_lg, a.k_nblk, b * a.Hkv + kvh, jb) : 1.f;
+            ts.v[sb] = a.v_blk_lg ? block_scale(a.v_scale, a.v_blk_lg, a.v_nblk, b * a.Hkv + kvh, jb) : 1.f;
+        }
+    };
+
+    auto consume = [&](const TileOps &ops, int t0, const TileScales &ts, auto alibi_c) {
         constexpr bool ALIBI = decltype(alibi_c)::value;
         // scores: p[4 sb + r] is key t0 + 16 sb + 4 c4 + r, head j16
         float p[4 * NSB];
@@ -393,6 +416,7 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float x = sc[r];
+                if constexpr (BLK) x *= ts.k[sb];
                 if constexpr (ALIBI) x = fmaf(slope2, (float)(j0 + t0 + 16 * sb + 4 * c4 + r - (Lc - 1)), x);
                 p[4 * sb + r] = x;
             }
@@ -431,7 +455,11 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
         // t0 + 4 c4 + t; FP8: the slot order of the V^T read above
         uint32_t ph[4 * NSB], pl[4 * NSB];
 #pragma unroll
-        for (int i = 0; i < 4 * NSB; ++i) split_bf16(p[i], ph[i], pl[i]);
+        for (int i = 0; i < 4 * NSB; ++i) {
+            float pv = p[i];                           // weight of the value row: V block scale
+            if constexpr (BLK) pv *= ts.v[i / 4];
+            split_bf16(pv, ph[i], pl[i]);
+        }
         if constexpr (F8) {
             const uint4 phi = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16, ph[4] | ph[5] << 16,
                                          ph[6] | ph[7] << 16);
@@ -461,14 +489,20 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     // reads have returned), and the tile is consumed while the next one loads.
     auto run = [&](auto alibi_c) {
         int t0 = wr * TK;                          // its loads were issued above
+        TileScales ts, tsn;                        // BLK: scales of this tile and the next
+        if constexpr (BLK) load_scales(t0, ts);
         while (t0 < n) {
             __builtin_amdgcn_s_waitcnt(VM_ALL);
             TileOps ops;
             read_tile(bufA, ops);
             __builtin_amdgcn_s_waitcnt(LGKM_ALL);
             const int tn = t0 + STRIDE;
-            if (tn < n) issue_tile(bufA, tn);
-            consume(ops, t0, alibi_c);
+            if (tn < n) {
+                issue_tile(bufA, tn);
+                if constexpr (BLK) load_scales(tn, tsn);
+            }
+            consume(ops, t0, ts, alibi_c);
+            if constexpr (BLK) ts = tsn;
             t0 = tn;
         }
     };
@@ -569,7 +603,8 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 // point, which leaves the release little to write back: one row of 32 query heads
 // over 8 KV heads, 4096 keys at 32 chunks, 16.2 us with plain stores, 13.1 us written
 // through, 12.8 us with a relaxed ticket (graph replay).
-template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16, bool TAIL = false>
+template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16, bool TAIL = false,
+          bool BLK = false>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
     static_assert(!TAIL || HG == 1, "the fused merge serves one KV head per work-group");
@@ -601,7 +636,7 @@ void split_mfma_kernel(SplitArgs a) {
     }
     if (w < busy) {
         const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
-        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
+        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL, BLK>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
         if constexpr (TAIL) {
             __shared__ int last;
             int32_t *const cnt = a.cnt + (int64_t)wi.b * a.Hkv + wi.g;
@@ -683,48 +718,55 @@ bool split_mfma_fusable(const SplitArgs &a, int d) {
 // One launch.  wg_slots = the work-groups of this kernel the device runs at once (its
 // occupancy per CU, queried once, times the CU count); the grid is capped there when
 // the batch's (row, KV-head group) pairs fit in it.
-template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT, bool TAIL = false>
+template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT, bool TAIL = false, bool BLK = false>
 static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
     constexpr int THREADS = 64 * HG * NWH;
     static const int per_cu = [] {
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL>),
+                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK>),
                 THREADS, 0) != hipSuccess || nb < 1)
             nb = 1;
         return nb;
     }();
     a.wg_slots = a.cus * per_cu;
     if (a.wg_slots > 0 && (int64_t)a.B * (a.Hkv / HG) <= a.wg_slots && grid > a.wg_slots) grid = a.wg_slots;
-    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK>), dim3((unsigned)grid),
                        dim3(THREADS), 0, st, a);
 }
 
-template <int D, int KVT>
+template <int D, int KVT, bool BLK = false>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
     const int64_t items = (int64_t)a.B * a.Hkv * a.S;
     if (a.fused) {                                     // split_mfma_fusable holds
-        if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, true>(a, items, st);
-        else launch_k<D, WAVES, false, 1, 4, KVT, true>(a, items, st);
+        if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, true, BLK>(a, items, st);
+        else launch_k<D, WAVES, false, 1, 4, KVT, true, BLK>(a, items, st);
         return;
     }
     if (runs_grouped_heads(a, D)) {
         constexpr int NWH = WAVES;                         // one work-group fills a CU
         const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
-        if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT>(a, grid, st);
-        else launch_k<D, WAVES, false, 4, NWH, KVT>(a, grid, st);
+        if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT, false, BLK>(a, grid, st);
+        else launch_k<D, WAVES, false, 4, NWH, KVT, false, BLK>(a, grid, st);
         return;
     }
-    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT>(a, items, st);
-    else launch_k<D, WAVES, false, 1, 4, KVT>(a, items, st);
+    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, false, BLK>(a, items, st);
+    else launch_k<D, WAVES, false, 1, 4, KVT, false, BLK>(a, items, st);
 }
 
 template <int D>
 static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
+    const bool blk = a.k_blk_lg || a.v_blk_lg;         // FP8 block scales: kernels of their own
     switch (a.kv_type) {
-        case kKvE4M3: launch_mfma_t<D, kKvE4M3>(a, st); break;
-        case kKvE5M2: launch_mfma_t<D, kKvE5M2>(a, st); break;
+        case kKvE4M3:
+            if (blk) launch_mfma_t<D, kKvE4M3, true>(a, st);
+            else launch_mfma_t<D, kKvE4M3>(a, st);
+            break;
+        case kKvE5M2:
+            if (blk) launch_mfma_t<D, kKvE5M2, true>(a, st);
+            else launch_mfma_t<D, kKvE5M2>(a, st);
+            break;
         default: launch_mfma_t<D, kKvBF16>(a, st); break;
     }
 }

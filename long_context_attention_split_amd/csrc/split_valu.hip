@@ -21,8 +21,11 @@
 // EPL consecutive elements (8 for fp32 and bf16, 16 for FP8: one 16-byte load, two
 // for fp32).  A wave therefore covers 64/G keys per load instruction; the q.k dot
 // product is EPL FMAs per lane followed by a log2(G)-step DPP butterfly inside the
-// lane group.  FP8 K/V carry a dequantisation scale per (b, kv head): the K scale
-// is folded into q, the V scale into the chunk's output.  Each lane group
+// lane group.  FP8 K/V carry a dequantisation scale per (b, kv head) -- the K scale
+// folded into q, the V scale into the chunk's output -- or per block of key positions:
+// then a load's KPW keys share one block (blocks hold at least 16 keys and chunks and
+// pieces start on block boundaries), whose K scale multiplies their scores and whose
+// V scale their value weights, one scalar load each per tile and load.  Each lane group
 // runs its own online softmax over the keys it sees (no cross-group traffic in the
 // loop); the 4*64/G group states of a work-group are merged through LDS at the end.
 //
@@ -46,10 +49,13 @@ namespace tad {
 // its own buffer resource.
 // TAIL: the variant whose last work-group of a row also merges the row (a.fused), kept
 // apart so that the plain kernel carries none of that code or its registers.
+// BLK: FP8 K/V with block scales (likewise kernels of their own).
 template <int D, int KVT, int POLICY, int UK = 128 / RowChunk<KVT, POLICY>::kBytes, bool PAGED = false,
-          bool TAIL = false>
+          bool TAIL = false, bool BLK = false>
 __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) {
     using Row = RowChunk<KVT, POLICY>;
+    constexpr bool F8 = KVT == kKvE4M3 || KVT == kKvE5M2;
+    static_assert(!BLK || F8, "block scales are for FP8 K/V");
     constexpr int EPL = Row::EPL;                // elements per lane per key
     constexpr int G = D / EPL;                   // lanes per key row
     constexpr int KPW = 64 / G;                  // keys per wave load instruction
@@ -127,7 +133,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     // K dequantisation scale, which multiplies every score of this KV head).
     float qv[EPL];
     {
-        const float qs = a.qscale * (a.k_scale ? a.k_scale[b * a.Hkv + kvh] : 1.f);
+        const bool k_head = a.k_scale && (!BLK || !a.k_blk_lg);   // one K scale per (b, KV head)
+        const float qs = a.qscale * (k_head ? a.k_scale[b * a.Hkv + kvh] : 1.f);
         const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)t * a.sqt + sub * EPL;
 #pragma unroll
         for (int c8 = 0; c8 < EPL / 8; ++c8) {
@@ -205,6 +212,16 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
             for (int e = 0; e < EPL; ++e) acc = fmaf(qv[e], kf[e], acc);
             sc[u] = group_sum<G>(acc);
         }
+        float vsu[U];                                       // V block scales of the tile's loads
+        if constexpr (BLK) {
+            const int bkv = b * a.Hkv + kvh;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int ju = __builtin_amdgcn_readfirstlane(j0 + t0 + u * KPW);
+                if (a.k_blk_lg) sc[u] *= block_scale(a.k_scale, a.k_blk_lg, a.k_nblk, bkv, ju);
+                vsu[u] = a.v_blk_lg ? block_scale(a.v_scale, a.v_blk_lg, a.v_nblk, bkv, ju) : 1.f;
+            }
+        }
         if (alibi) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -228,10 +245,12 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
         for (int u = 0; u < U; ++u) {
             const float p = exp2_fast(sc[u] - m_use);
             l += p;
+            float pv = p;
+            if constexpr (BLK) pv = p * vsu[u];
             float vf[EPL];
             vv[u].widen(vf);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, vf[e], o[e]);
+            for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
         }
         m = m_new;
     };
@@ -260,7 +279,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     const float Mu = (M == kNegInf) ? 0.f : M;
     const int64_t row = ((int64_t)b * a.Hq + h) * a.nq + t;
     const int64_t r = row * S + s;
-    const float vsc = a.v_scale ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // V dequantisation
+    const bool v_head = a.v_scale && (!BLK || !a.v_blk_lg);
+    const float vsc = v_head ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // V dequantisation
     // Where this work-group's partial goes: the chunk's slot, or piece p's slot (a later
     // kernel merges the pieces).  A partial that another work-group of this kernel
     // merges (fused) is written through to the device coherence point (store_partial).
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_valu_kernel(SplitArgs a) 
     }
 }
 
-template <int D, int KVT, bool TAIL>
+template <int D, int KVT, bool TAIL, bool BLK>
 static hipError_t launch_tail(const SplitArgs &a, int64_t grid, hipStream_t st) {
     // paged caches: 32-key wave tiles of two 16-row pieces, each from its own page (page
     // sizes are multiples of 16), or 16 keys where 32 would take more than 8 loads per
@@ -323,23 +343,23 @@ static hipError_t launch_tail(const SplitArgs &a, int64_t grid, hipStream_t st) 
         if constexpr (KVT == kKvF32 || D > 256) {
             return hipErrorInvalidValue;                  // not offered for paged caches
         } else if (gq == 1) {
-            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, true, TAIL>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UP, true, TAIL, BLK>), dim3((unsigned)grid),
                                dim3(kSplitThreads), 0, st, a);
         } else {
-            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, true, TAIL>), dim3((unsigned)grid),
-                               dim3(kSplitThreads), 0, st, a);
+            hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UP, true, TAIL, BLK>),
+                               dim3((unsigned)grid), dim3(kSplitThreads), 0, st, a);
         }
     } else if (gq == 1) {
-        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UD, false, TAIL>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyNT, UD, false, TAIL, BLK>), dim3((unsigned)grid),
                            dim3(kSplitThreads), 0, st, a);
     } else {
-        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UD, false, TAIL>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((split_valu_kernel<D, KVT, kPolicyDefault, UD, false, TAIL, BLK>), dim3((unsigned)grid),
                            dim3(kSplitThreads), 0, st, a);
     }
     return hipGetLastError();
 }
 
-template <int D, int KVT>
+template <int D, int KVT, bool BLK = false>
 static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
     int64_t grid;
     const int gq = a.group * a.nq;
@@ -352,17 +372,18 @@ static hipError_t launch_t(const SplitArgs &a, hipStream_t st) {
     }
     if (grid <= 0) return hipSuccess;
     if (a.fused && a.P > 1) return hipErrorInvalidValue;   // pieces merge in their own kernel
-    if (a.fused) return launch_tail<D, KVT, true>(a, grid, st);
-    return launch_tail<D, KVT, false>(a, grid, st);
+    if (a.fused) return launch_tail<D, KVT, true, BLK>(a, grid, st);
+    return launch_tail<D, KVT, false, BLK>(a, grid, st);
 }
 
 template <int D>
 static hipError_t launch_d(const SplitArgs &a, hipStream_t st) {
+    const bool blk = a.k_blk_lg || a.v_blk_lg;         // FP8 block scales: kernels of their own
     switch (a.kv_type) {
         case kKvF32: return launch_t<D, kKvF32>(a, st);
         case kKvBF16: return launch_t<D, kKvBF16>(a, st);
-        case kKvE4M3: return launch_t<D, kKvE4M3>(a, st);
-        case kKvE5M2: return launch_t<D, kKvE5M2>(a, st);
+        case kKvE4M3: return blk ? launch_t<D, kKvE4M3, true>(a, st) : launch_t<D, kKvE4M3>(a, st);
+        case kKvE5M2: return blk ? launch_t<D, kKvE5M2, true>(a, st) : launch_t<D, kKvE5M2>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

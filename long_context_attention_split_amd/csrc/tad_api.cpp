@@ -48,6 +48,42 @@ int kv_type_of(int32_t dtype) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// scale / scale_block of a k or v tensor (dtype already checked).
+int check_scales(const tad_tensor *t, const char *name) {
+    if (t->scale && !is_fp8(t->dtype))
+        return fail(TAD_EINVAL, "%s: a dequantisation scale is only allowed for FP8 tensors", name);
+    const int32_t n = t->scale_block;
+    if (n == 0) return TAD_OK;
+    if (!is_fp8(t->dtype)) return fail(TAD_EINVAL, "%s: scale_block is only allowed for FP8 tensors", name);
+    if (!t->scale) return fail(TAD_EINVAL, "%s: scale_block %d without a scale array", name, n);
+    if (n < 16 || n > 65536 || (n & (n - 1)))
+        return fail(TAD_EUNSUPPORTED, "%s: scale_block must be a power of two from 16 to 65536 (got %d)", name, n);
+    return TAD_OK;
+}
+
+int log2_of(int32_t n) {
+    int lg = 0;
+    while ((1 << lg) < n) ++lg;
+    return lg;
+}
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+// Chunk and piece lengths are multiples of this: whole pages, whole K and V scale blocks.
+int64_t chunk_align(int64_t page_size, int32_t k_blk, int32_t v_blk) {
+    int64_t a = page_size > 1 ? page_size : 1;
+    for (int64_t n : {(int64_t)k_blk, (int64_t)v_blk})
+        if (n > 1) a = a / gcd64(a, n) * n;
+    return a;
+}
+
 // Shapes and strides of one decode call, normalised to 4-D [B, H, L, d] views.
 struct Problem {
     int64_t B = 0, Hq = 0, Hkv = 0, Lmax = 0, d = 0, nq = 1;
@@ -56,6 +92,7 @@ struct Problem {
     int64_t skb = 0, skh = 0, skj = 0;
     int64_t svb = 0, svh = 0, svj = 0;
     const float *k_scale = nullptr, *v_scale = nullptr;
+    int32_t k_blk = 0, v_blk = 0;      // keys per scale block (0: one scale per (b, KV head))
     // paged cache (block_table non-null): skh/skj are the head/row strides inside a page
     const int32_t *block_table = nullptr;
     int64_t max_pages = 0, page_size = 0, num_pages = 0, skp = 0, svp = 0;
@@ -101,8 +138,8 @@ int parse_kv(const tad_tensor *t, const char *name, int64_t *B, int64_t *H, int6
     if (*B < 0 || *H < 1 || *L < 0 || *d < 1) return fail(TAD_EINVAL, "%s: bad shape", name);
     if (t->dtype != TAD_F32 && t->dtype != TAD_BF16 && !is_fp8(t->dtype))
         return fail(TAD_EDTYPE, "%s: dtype must be TAD_F32, TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2", name);
-    if (t->scale && !is_fp8(t->dtype))
-        return fail(TAD_EINVAL, "%s: a dequantisation scale is only allowed for FP8 tensors", name);
+    int rc = check_scales(t, name);
+    if (rc) return rc;
     const int64_t es = elem_size(t->dtype);
     if (!aligned16(t->data) || (*sb * es) % 16 || (*sh * es) % 16 || (*sj * es) % 16)
         return fail(TAD_ELAYOUT, "%s: rows must start on 16-byte boundaries", name);
@@ -135,6 +172,7 @@ int parse_problem(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
     P->B = Bq; P->Hq = Hq; P->Hkv = Hk; P->Lmax = Lk; P->d = dq; P->nq = nq;
     P->q_dtype = q->dtype; P->kv_dtype = k->dtype;
     P->k_scale = k->scale; P->v_scale = v->scale;
+    P->k_blk = k->scale_block; P->v_blk = v->scale_block;
     return TAD_OK;
 }
 
@@ -152,8 +190,8 @@ int parse_paged_kv(const tad_tensor *t, const char *name, int64_t *NP, int64_t *
                               (long long)*PS);
     if (t->dtype != TAD_BF16 && !is_fp8(t->dtype))
         return fail(TAD_EDTYPE, "%s: a paged cache must be TAD_BF16, TAD_FP8_E4M3 or TAD_FP8_E5M2", name);
-    if (t->scale && !is_fp8(t->dtype))
-        return fail(TAD_EINVAL, "%s: a dequantisation scale is only allowed for FP8 tensors", name);
+    int rc = check_scales(t, name);
+    if (rc) return rc;
     const int64_t es = elem_size(t->dtype);
     if (!aligned16(t->data) || (*sp * es) % 16 || (*sj * es) % 16 || (*sh * es) % 16)
         return fail(TAD_ELAYOUT, "%s: rows must start on 16-byte boundaries", name);
@@ -192,6 +230,7 @@ int parse_paged_problem(const tad_tensor *q, const tad_tensor *k, const tad_tens
     P->skb = P->svb = 0;
     P->q_dtype = q->dtype; P->kv_dtype = k->dtype;
     P->k_scale = k->scale; P->v_scale = v->scale;
+    P->k_blk = k->scale_block; P->v_blk = v->scale_block;
     P->block_table = pages->block_table;
     P->max_pages = pages->max_pages; P->page_size = PSk; P->num_pages = NPk;
     return TAD_OK;
@@ -210,9 +249,12 @@ int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *so
 
 // 32-bit buffer offsets: one chunk plus a tile of overrun must span < 4 GiB.
 int check_offsets(const Problem &P, int64_t S) {
+    const int64_t al = chunk_align(P.block_table ? P.page_size : 1, P.k_blk, P.v_blk);
+    if (al > (int64_t(1) << 30))
+        return fail(TAD_EUNSUPPORTED, "pages and scale blocks would need chunks of %lld keys", (long long)al);
     if (P.block_table) return TAD_OK;    // paged: one resource per 16-key tile (checked in parse_paged_kv)
     const int64_t es = elem_size(P.kv_dtype);
-    const int64_t c = (P.Lmax + S - 1) / S;
+    const int64_t c = ((P.Lmax + S - 1) / S + al - 1) / al * al;
     const int64_t span_k = (c + 64) * P.skj * es, span_v = (c + 64) * P.svj * es;
     if (span_k >= (int64_t(1) << 32) || span_v >= (int64_t(1) << 32))
         return fail(TAD_EUNSUPPORTED, "chunk spans >= 4 GiB; use more splits");
@@ -334,6 +376,11 @@ tad::SplitArgs split_args(const Problem &P, const tad_tensor *q, const tad_tenso
     a.k = k->data; a.v = v->data;
     a.kv_type = kv_type_of(P.kv_dtype);
     a.k_scale = P.k_scale; a.v_scale = P.v_scale;
+    a.k_blk_lg = P.k_blk ? log2_of(P.k_blk) : 0;
+    a.v_blk_lg = P.v_blk ? log2_of(P.v_blk) : 0;
+    a.k_nblk = P.k_blk ? (int32_t)((P.Lmax + P.k_blk - 1) / P.k_blk) : 0;
+    a.v_nblk = P.v_blk ? (int32_t)((P.Lmax + P.v_blk - 1) / P.v_blk) : 0;
+    a.align = (int32_t)chunk_align(P.block_table ? P.page_size : 1, P.k_blk, P.v_blk);
     a.skb = P.skb; a.skh = P.skh; a.skj = P.skj;
     a.svb = P.svb; a.svh = P.svh; a.svj = P.svj;
     a.seq_lens = seq_lens; a.slopes = slopes;

@@ -17,7 +17,14 @@ struct SplitArgs {
     int32_t nq;             // query tokens per (b, h): the row's last nq positions, causal
     const void *k, *v;      // [B, Hkv, Lmax, d], innermost contiguous
     int32_t kv_type;        // kKvF32, kKvBF16, kKvE4M3, kKvE5M2 (device_util.h)
-    const float *k_scale, *v_scale;  // [B * Hkv] dequantisation scales, or null (1)
+    const float *k_scale, *v_scale;  // FP8 dequantisation scales, or null (1): [B * Hkv], or
+                                     // [B * Hkv * nblk] when the tensor has block scales
+    // Block scales: key j of (b, KV head h) has scale k_scale[(b * Hkv + h) * k_nblk +
+    // (j >> k_blk_lg)]; k_blk_lg = 0 means one scale per (b, KV head).  Blocks hold at
+    // least 16 keys, and chunks and pieces start on block boundaries (align).
+    int32_t k_blk_lg, v_blk_lg;
+    int32_t k_nblk, v_nblk;
+    int32_t align;          // chunk and piece lengths are multiples of this (pages, scale blocks)
     int64_t skb, skh, skj;  // k element strides
     int64_t svb, svh, svj;  // v element strides
     const int32_t *seq_lens;  // [B] or null
@@ -135,7 +142,7 @@ __device__ __forceinline__ int batch_chunk_len(const SplitArgs &a, int len0) {
         Lref = wave_top(mx);
     }
     int c = (Lref + a.S - 1) / a.S;
-    if (a.block_table) c = (c + a.page_size - 1) / a.page_size * a.page_size;   // whole pages
+    if (a.align > 1) c = (c + a.align - 1) / a.align * a.align;   // whole pages and scale blocks
     return c;
 }
 
@@ -173,7 +180,7 @@ __device__ __forceinline__ int fit_chunk_len(const SplitArgs &a, int G, int c, i
     const int Lref = wave_top(mx);
     for (int it = 0; it < 16 && busy > slots && c < Lref; ++it) {
         int cn = (int)__builtin_ceil((double)c * busy / slots);     // busy scales about as 1/c
-        if (a.block_table) cn = ceil_div(cn, a.page_size) * a.page_size;
+        if (a.align > 1) cn = ceil_div(cn, a.align) * a.align;
         c = max(min(cn, Lref), c + 1);
         busy = busy_of(c);
     }
@@ -192,6 +199,13 @@ __device__ __forceinline__ ChunkRange chunk_of(int L, int s, int c) {
 
 __device__ __forceinline__ ChunkRange chunk_range(const SplitArgs &a, int b, int s) {
     return chunk_of(row_len(a, b), s, batch_chunk_len(a));
+}
+
+// Block scale of key j of the (b, KV head) pair bh = b * Hkv + h (lg = log2 of the block
+// length, nblk blocks per pair).  The block index is capped at the last block: keys past
+// a row's end are masked, but a tile may still look one up.
+__device__ __forceinline__ float block_scale(const float *sc, int lg, int nblk, int bh, int j) {
+    return sc[(int64_t)bh * nblk + min(j >> lg, nblk - 1)];
 }
 
 // Item k of the B * G * S items (row b, index g < G, chunk s) with chunk length c, in
@@ -345,7 +359,7 @@ struct TilePages {
 // Sub-chunk length: chunk length c cut into P pieces (whole pages for a paged cache).
 __device__ __forceinline__ int sub_chunk_len(const SplitArgs &a, int c) {
     int cs = (c + a.P - 1) / a.P;
-    if (a.block_table) cs = (cs + a.page_size - 1) / a.page_size * a.page_size;
+    if (a.align > 1) cs = (cs + a.align - 1) / a.align * a.align;
     return cs;
 }
 

@@ -143,6 +143,32 @@ def test_fp8_and_scale_rules(lib):
     assert call_split(so, e, ws_bytes=0) == tad.TAD_EWORKSPACE
 
 
+def test_block_scale_rules(lib):
+    """scale_block: 0 (one scale per (b, KV head)) or a power of two from 16 to 65536,
+    on FP8 tensors with a scale array only; K and V choose independently."""
+    so = lib.load()
+
+    def fp8(kb, vb):
+        a = good()
+        a["k"] = desc([2, 2, 100, 128], tad.TAD_FP8_E4M3)
+        a["v"] = desc([2, 2, 100, 128], tad.TAD_FP8_E4M3)
+        a["k"].scale, a["v"].scale = FAKE, FAKE
+        a["k"].scale_block, a["v"].scale_block = kb, vb
+        return a
+
+    for kb, vb in ((16, 0), (0, 64), (65536, 256), (32, 32)):
+        assert call_split(so, fp8(kb, vb), ws_bytes=0) == tad.TAD_EWORKSPACE   # validated up to the workspace
+    for n in (8, 48, 100, 131072, -16):
+        assert call_split(so, fp8(0, n)) == tad.TAD_EUNSUPPORTED
+        assert "scale_block" in lib.tad_last_error()
+    a = fp8(16, 0)
+    a["k"].scale = None                                               # blocks without scales
+    assert call_split(so, a) == tad.TAD_EINVAL
+    b = good()
+    b["v"].scale_block = 16                                           # bf16 values
+    assert call_split(so, b) == tad.TAD_EINVAL
+
+
 def test_split_rejects_bad_splits_and_workspace(lib):
     so = lib.load()
     a = good()

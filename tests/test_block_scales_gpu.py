@@ -1,0 +1,169 @@
+"""GPU: FP8 K/V with one dequantisation scale per block of key positions.
+
+A tensor's ``scale_block`` = n gives key j of (b, KV head) the scale
+scale[b, h, j // n] (a power of two n from 16 to 65536; K and V choose apart).  The
+chunk length is rounded up to whole blocks, so every kernel's key tiles see one block
+at a time.  Each case runs one kernel form -- the vector kernel (with pieces and
+fused), the head-packed kernel, the matrix-core kernel (4 KV heads or 1 per
+work-group, fused), each on a paged cache too -- and must match the fp64 oracle on
+the dequantised values within the FP8 bar, and tad_decode_ws must equal tad_split +
+tad_combine bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle import tree
+from test_parity_gpu import DEV, assert_parity, note, vmax_valid
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = torch.float8_e4m3fn, torch.float8_e5m2
+
+
+def dequantised(codes, scales, block):
+    """fp64 values of FP8 codes [B, H, L, d] under block scales [B, H, >= ceil(L / block)]."""
+    L = codes.shape[2]
+    rep = np.repeat(scales.double().numpy(), block, axis=2)[:, :, :L]
+    return np.nan_to_num(oracle.widen(codes)) * rep[:, :, :, None]
+
+
+def block_case(seed, B, Hq, Hkv, nq, L, d, kv, lens, alibi, kb, vb):
+    """Seeded inputs; K quantised in blocks of kb keys, V in blocks of vb keys."""
+    c = W.random_case(seed, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi, scale_block=kb)
+    v, vs = W.draw_kv_fp8_blocks(seed + 50, B, Hkv, L, d, vb, kv)
+    if lens is not None:
+        nan_bits = 0x7F if kv == E4 else 0x7E
+        for b, Lb in enumerate(lens):
+            v.view(torch.uint8)[b, :, Lb:, :] = nan_bits
+    c["v"], c["v_scale"] = v, vs
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(seed + 9))
+    return c
+
+
+def padded(scales, block, Lcap):
+    """Scales [B, H, n] widened to ceil(Lcap / block) blocks (a paged cache's logical
+    length may exceed the drawn one); the extra blocks cover no key and hold 1."""
+    n = -(-Lcap // block)
+    out = torch.ones(scales.shape[0], scales.shape[1], n, dtype=torch.float32)
+    out[:, :, :scales.shape[2]] = scales
+    return out
+
+
+# (seed, B, Hq, Hkv, nq, L, d, kv, S, lens, alibi, k block, v block, layout, kernel form)
+CASES = [
+    (1, 2, 4, 4, 1, 3000, 128, E4, 8, [3000, 1777], True, 16, 64, "contig", "vector"),
+    (2, 1, 6, 6, 1, 5000, 64, E5, 0, None, False, 32, 32, "contig", "vector, automatic chunks"),
+    (3, 1, 1, 1, 1, 20000, 256, E4, 4, None, False, 128, 256, "contig", "vector, pieces"),
+    (4, 1, 2, 2, 1, 4096, 512, E4, 8, None, True, 16, 16, "contig", "vector d 512, pieces"),
+    (5, 1, 4, 4, 1, 600, 128, E4, 4, None, False, 16, 32, "contig", "vector, one launch"),
+    (6, 2, 4, 2, 1, 2500, 256, E5, 6, [2500, 999], False, 64, 16, "contig", "vector, query-head groups"),
+    (7, 1, 2, 2, 3, 1500, 512, E4, 5, None, False, 16, 16, "contig", "vector, 3 tokens"),
+    (8, 2, 8, 8, 1, 4000, 128, E4, 8, [4000, 2100], True, 32, 128, "tokmajor", "head-packed"),
+    (9, 1, 8, 8, 1, 1200, 64, E5, 4, None, False, 16, 16, "tokmajor", "head-packed, one launch"),
+    (10, 8, 32, 8, 1, 6000, 128, E4, 24, "random", False, 64, 16, "contig", "matrix cores, 4 KV heads/WG"),
+    (11, 2, 16, 4, 4, 3000, 64, E5, 8, [3000, 1500], True, 32, 32, "contig", "matrix cores, 4 tokens"),
+    (12, 1, 32, 8, 1, 4096, 128, E4, 8, None, False, 16, 64, "contig", "matrix cores, one launch"),
+    (13, 4, 16, 2, 1, 8000, 128, E4, 0, None, False, 256, 256, "contig", "matrix cores, automatic chunks"),
+    (14, 2, 32, 8, 1, 3000, 128, E4, 8, [3000, 1111], False, 64, 32, "paged16", "matrix cores, paged"),
+    (15, 2, 8, 8, 1, 2500, 64, E5, 6, [2500, 801], True, 16, 128, "paged32", "head-packed, paged"),
+    (16, 2, 2, 2, 1, 2000, 128, E4, 5, [2000, 1300], False, 64, 64, "paged16hm", "vector, paged"),
+    (17, 2, 8, 2, 1, 2000, 128, E4, 6, [2000, 700], False, 64, 16, "paged48", "matrix cores, 48-row pages"),
+]
+
+
+def run_layout(lib, c, layout, S, kb, vb, entry):
+    """One call through `entry` ("ws": tad_decode_ws, "alloc": tad_decode, "split":
+    tad_split + tad_combine) on the case's layout; returns out on the GPU."""
+    q = c["q"].to(DEV)
+    dev = lambda key: None if c.get(key) is None else c[key].to(DEV)
+    shape = q.shape
+    out = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+    B, Hq, d = q.shape[0], q.shape[1], q.shape[-1]
+    nq = q.shape[2] if q.dim() == 4 else 1
+    kw = dict(k_scale_block=kb, v_scale_block=vb)
+    if layout.startswith("paged"):
+        ps = int(layout[5:7])
+        kc, vc, table = W.page_kv(c["k"], c["v"], ps, 900 + S, head_major=layout.endswith("hm"))
+        Lcap = table.shape[1] * ps
+        ks, vs = padded(c["k_scale"], kb, Lcap).to(DEV), padded(c["v_scale"], vb, Lcap).to(DEV)
+        kc, vc, table = kc.to(DEV), vc.to(DEV), table.to(DEV)
+        ws = lib.workspace(q, c["k"].to(DEV), S)
+        args = (q, kc, vc, table, dev("seq_lens"), dev("slopes"), S)
+        if entry == "ws":
+            lib.tad_decode_paged_ws(*args, out, ws, k_scale=ks, v_scale=vs, **kw)
+        elif entry == "alloc":
+            lib.tad_decode_paged(*args, out, k_scale=ks, v_scale=vs, **kw)
+        else:
+            lib.tad_split_paged(*args, ws, k_scale=ks, v_scale=vs, **kw)
+            lib.tad_combine(ws, B, Hq, nq, S, d, out)
+        return out
+    if layout == "tokmajor":
+        k = c["k"].transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        v = c["v"].transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+        assert k.stride(1) == d
+    else:
+        k, v = c["k"].to(DEV), c["v"].to(DEV)
+    ks, vs = dev("k_scale"), dev("v_scale")
+    ws = lib.workspace(q, k, S)
+    args = (q, k, v, dev("seq_lens"), dev("slopes"), S)
+    if entry == "ws":
+        lib.tad_decode_ws(*args, out, ws, k_scale=ks, v_scale=vs, **kw)
+    elif entry == "alloc":
+        lib.tad_decode(*args, out, k_scale=ks, v_scale=vs, **kw)
+    else:
+        lib.tad_split(*args, ws, k_scale=ks, v_scale=vs, **kw)
+        lib.tad_combine(ws, B, Hq, nq, S, d, out)
+    return out
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d" % c[0])
+def test_block_scaled_fp8_decode(lib, case):
+    seed, B, Hq, Hkv, nq, L, d, kv, S, lens, alibi, kb, vb, layout, form = case
+    if lens == "random":
+        lens = torch.randint(1, L + 1, (B,), generator=torch.Generator().manual_seed(960 + seed)).tolist()
+        lens[0] = L
+    note("block scales seed=%d %s B=%d Hq=%d Hkv=%d nq=%d L=%d d=%d kv=%s S=%d lens=%s alibi=%s kb=%d vb=%d %s" %
+         (seed, form, B, Hq, Hkv, nq, L, d, kv, S, lens, alibi, kb, vb, layout))
+    c = block_case(940 + seed, B, Hq, Hkv, nq, L, d, kv, lens, alibi, kb, vb)
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"], k_scale_block=kb, v_scale_block=vb)
+    S = lib.resolve_splits(c["q"].to(DEV), c["k"].to(DEV), S)
+    out = run_layout(lib, c, layout, S, kb, vb, "ws")
+    two = run_layout(lib, c, layout, S, kb, vb, "split")
+    alloc = run_layout(lib, c, layout, S, kb, vb, "alloc")
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    assert torch.equal(out, alloc)
+    vmax = vmax_valid(torch.from_numpy(dequantised(c["v"], c["v_scale"], vb)), c["seq_lens"])
+    assert_parity(out.cpu().numpy(), ref, kv, vmax, "block scales %s" % form)
+
+
+def test_block_scaled_partials_use_whole_blocks(lib):
+    """With block scales the chunk length ceil(L / S) is rounded up to whole blocks
+    (here 1000 keys, S = 7: 143 -> 256 with K blocks of 256, so chunks 4..6 are empty),
+    and tad_split's partials are the chunk statistics of the dequantised values."""
+    B, H, L, d, S, kb, vb = 1, 2, 1000, 128, 7, 256, 64
+    c = block_case(990, B, H, H, 1, L, d, E4, None, False, kb, vb)
+    g = {k: (x.to(DEV) if torch.is_tensor(x) else x) for k, x in c.items()}
+    m, l, o = lib.split_partials(g["q"], g["k"], g["v"], None, None, S, k_scale=g["k_scale"],
+                                 v_scale=g["v_scale"], k_scale_block=kb, v_scale_block=vb)
+    torch.cuda.synchronize()
+    m, l, o = m.cpu().double().numpy(), l.cpu().double().numpy(), o.cpu().double().numpy()
+    kd, vd = dequantised(c["k"], c["k_scale"], kb), dequantised(c["v"], c["v_scale"], vb)
+    clen = 256
+    for h in range(H):
+        parts = tree.chunk_partials(oracle.widen(c["q"])[0, h], kd[0, h], vd[0, h], S, None, clen)
+        for s, (lm, den, num) in enumerate(parts):
+            if den == 0.0:
+                assert s >= 4 and m[0, h, s] == -np.inf and l[0, h, s] == 0
+                continue
+            assert m[0, h, s] * math.log(2) == pytest.approx(lm, rel=1e-5, abs=1e-5)
+            fix = math.exp(m[0, h, s] * math.log(2) - lm)
+            assert l[0, h, s] * fix == pytest.approx(den, rel=1e-4)
+            np.testing.assert_allclose(o[0, h, s] * fix, num, rtol=2e-4, atol=2e-4 * np.abs(num).max())

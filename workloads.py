@@ -160,15 +160,15 @@ def draw_kv_fp8_blocks(seed: int, B: int, Hkv: int, L: int, d: int, block: int, 
     nblk = (L + block - 1) // block
     out = torch.empty((B, Hkv, L, d), dtype=dtype)
     scale = torch.empty((B, Hkv, nblk), dtype=F32)
+    pad = nblk * block - L
     for b in range(B):
         for h in range(Hkv):
             slab = torch.randn((L, d), generator=g, dtype=F32)
             amp = torch.exp2(torch.rand((nblk,), generator=g, dtype=F32) * 4 - 2)
-            for i in range(nblk):
-                rows = slab[i * block:(i + 1) * block]
-                rows.mul_(amp[i])
-                scale[b, h, i] = float(rows.abs().max()) / FP8_MAX[dtype]
-                out[b, h, i * block:(i + 1) * block].copy_((rows / scale[b, h, i]).to(dtype))
+            slab.mul_(amp.repeat_interleave(block)[:L, None])
+            amax = torch.nn.functional.pad(slab.abs(), (0, 0, 0, pad)).view(nblk, block * d).amax(dim=1)
+            scale[b, h] = (amax.double() / FP8_MAX[dtype]).float()
+            out[b, h].copy_((slab / scale[b, h].repeat_interleave(block)[:L, None]).to(dtype))
     return out, scale
 
 
@@ -177,17 +177,22 @@ def draw_seq_lens(seed: int, B: int, lo: int, hi: int) -> torch.Tensor:
     return torch.randint(lo, hi + 1, (B,), generator=_gen(seed), dtype=torch.int64).to(torch.int32)
 
 
-def make_workload(wid: int):
+def make_workload(wid: int, scale_block: int = 0):
     """All inputs of workload ``wid`` as CPU tensors.
 
     Returns a dict with q, k, v, seq_lens (int32 or None), slopes (fp32 or None),
     n_splits (int, <= 0 for automatic) and, for workload 5, planted (int64 [B, Hkv]).
+    ``scale_block`` > 0 (FP8 workloads): K and V quantised per block of that many keys
+    by ``draw_kv_fp8_blocks`` (same seeds), scales [B, Hkv, ceil(Lmax / scale_block)].
     """
     w = WORKLOADS[wid]
     base = 1000 * wid
     q = draw_q(base + 0, w.B, w.Hq, w.d, w.q_dtype)
     ks = vs = None
-    if w.kv_dtype in FP8_MAX:
+    if w.kv_dtype in FP8_MAX and scale_block > 0:
+        k, ks = draw_kv_fp8_blocks(base + 1, w.B, w.Hkv, w.Lmax, w.d, scale_block, w.kv_dtype)
+        v, vs = draw_kv_fp8_blocks(base + 2, w.B, w.Hkv, w.Lmax, w.d, scale_block, w.kv_dtype)
+    elif w.kv_dtype in FP8_MAX:
         k, ks = draw_kv_fp8(base + 1, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype)
         v, vs = draw_kv_fp8(base + 2, w.B, w.Hkv, w.Lmax, w.d, w.kv_dtype)
     else:
