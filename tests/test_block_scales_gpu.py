@@ -167,3 +167,19 @@ def test_block_scaled_partials_use_whole_blocks(lib):
             fix = math.exp(m[0, h, s] * math.log(2) - lm)
             assert l[0, h, s] * fix == pytest.approx(den, rel=1e-4)
             np.testing.assert_allclose(o[0, h, s] * fix, num, rtol=2e-4, atol=2e-4 * np.abs(num).max())
+
+
+def test_block_scaled_noalloc_shrinking(lib):
+    """The allocation-free entry point with block scales: two calls in a row, the second
+    smaller, each equal to tad_decode_ws bit for bit."""
+    for seed, B, L, S in ((995, 2, 5000, 8), (996, 1, 1800, 4)):
+        c = {k: (x.to(DEV) if torch.is_tensor(x) else x)
+             for k, x in block_case(seed, B, 32, 8, 1, L, 128, E4, [L, L // 3][:B], False, 32, 64).items()}
+        kw = dict(k_scale=c["k_scale"], v_scale=c["v_scale"], k_scale_block=32, v_scale_block=64)
+        a = torch.empty((B, 32, 128), dtype=torch.float32, device=DEV)
+        lib.tad_decode_noalloc(c["q"], c["k"], c["v"], c["seq_lens"], None, S, a, **kw)
+        ws = lib.workspace(c["q"], c["k"], S)
+        b = torch.empty_like(a)
+        lib.tad_decode_ws(c["q"], c["k"], c["v"], c["seq_lens"], None, S, b, ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)

@@ -19,7 +19,8 @@ def dev(x):
 
 
 @pytest.mark.parametrize("case", ["fused-mha", "gqa", "split-combine-mha", "paged-interleaved", "tokens",
-                                  "gqa-many-chunks", "pieces", "pieces-combine"])
+                                  "gqa-many-chunks", "pieces", "pieces-combine", "fp8-block-gqa",
+                                  "fp8-block-split-combine"])
 def test_decode_ws_replays_in_a_graph(lib, case):
     print("[case] graph %s" % case, flush=True)
     paged = case == "paged-interleaved"
@@ -35,12 +36,20 @@ def test_decode_ws_replays_in_a_graph(lib, case):
         c, S = W.random_case(908, 1, 1, 1, 4096, 512, kv_dtype=torch.float32), 8
     elif case == "pieces-combine":    # 40 chunks read as pieces, then the combine kernel
         c, S = W.random_case(909, 1, 2, 2, 60000, 128), 40
+    elif case == "fp8-block-gqa":     # FP8 with 32-key scale blocks, matrix-core one-launch form
+        c, S = W.random_case(910, 2, 8, 2, 2500, 128, kv_dtype=torch.float8_e4m3fn, seq_lens=[2500, 1700],
+                             scale_block=32), 5
+    elif case == "fp8-block-split-combine":   # FP8 with 64-key scale blocks, vector split then combine
+        c, S = W.random_case(911, 2, 32, 32, 4000, 128, kv_dtype=torch.float8_e5m2, seq_lens=[4000, 3333],
+                             scale_block=64), 16
     elif case == "tokens":
         c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
         c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
     else:                             # token-major pages: head-packed split, merge in its last work-groups
         c, S = W.random_case(904, 2, 16, 16, 2000, 128, seq_lens=[2000, 1111]), 8
     q, k, v, sl = dev(c["q"]), dev(c["k"]), dev(c["v"]), dev(c["seq_lens"])
+    blk = {"fp8-block-gqa": 32, "fp8-block-split-combine": 64}.get(case, 0)
+    kw = dict(k_scale=dev(c["k_scale"]), v_scale=dev(c["v_scale"]), k_scale_block=blk, v_scale_block=blk)
     if paged:
         kc, vc, tb = W.page_kv(c["k"], c["v"], 16, 904)
         kc, vc, tb = dev(kc), dev(vc), dev(tb)
@@ -49,7 +58,7 @@ def test_decode_ws_replays_in_a_graph(lib, case):
         if paged:
             lib.tad_decode_paged_ws(q, kc, vc, tb, sl, None, S, out, ws)
         else:
-            lib.tad_decode_ws(q, k, v, sl, None, S, out, ws)
+            lib.tad_decode_ws(q, k, v, sl, None, S, out, ws, **kw)
 
     def eager():
         out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
