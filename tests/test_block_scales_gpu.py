@@ -10,6 +10,7 @@ the dequantised values within the FP8 bar, and tad_decode_ws must equal tad_spli
 tad_combine bit for bit.
 """
 import math
+import random
 
 import numpy as np
 import pytest
@@ -183,3 +184,90 @@ def test_block_scaled_noalloc_shrinking(lib):
         lib.tad_decode_ws(c["q"], c["k"], c["v"], c["seq_lens"], None, S, b, ws, **kw)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
+
+
+def draw_block_cases(n, seed=2026):
+    """Random FP8 shapes with block scales on K, V or both (the other tensor then has one
+    scale per (row, KV head)), on contiguous, token-major and paged caches."""
+    rnd = random.Random(seed)
+    cases = []
+    for i in range(n):
+        layout = rnd.choice(["contig", "tokmajor", "paged"])
+        d = rnd.choice([64, 128, 128, 256] + ([512] if layout != "paged" else []))
+        kv = rnd.choice([E4, E5])
+        Hkv = rnd.choice([1, 2, 4, 8])
+        group = rnd.choice([1, 1, 2, 4, 8])
+        B = rnd.choice([1, 2, 3, 5, 8, 70])
+        nq = rnd.choice([1, 1, 1, 2, 4])
+        L = rnd.choice([1, 17, 300, 1000, 2500, 5000])
+        if B * Hkv * group * L * d > 40_000_000:
+            L = max(1, 40_000_000 // (B * Hkv * group * d))
+        ragged = B > 1 and rnd.random() < 0.7
+        S = rnd.choice([0, 0, 1, 3, 7, 8, 16, 24, 64])
+        alibi = rnd.random() < 0.3
+        blocks = [16, 32, 64, 128, 256, 1024]
+        kb, vb = rnd.choice([0] + blocks), rnd.choice([0] + blocks)
+        if kb == 0 and vb == 0:
+            vb = rnd.choice(blocks)
+        ps = rnd.choice([16, 32, 48, 64])
+        cases.append((i, layout, B, Hkv * group, Hkv, nq, L, d, kv, ragged, S, alibi, kb, vb, ps))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_block_cases(40), ids=lambda c: "r%d-%s" % (c[0], c[1]))
+def test_random_block_scaled(lib, case):
+    i, layout, B, Hq, Hkv, nq, L, d, kv, ragged, S, alibi, kb, vb, ps = case
+    lens = None
+    if ragged:
+        lens = torch.randint(0, L + 1, (B,), generator=torch.Generator().manual_seed(2700 + i)).tolist()
+        lens[0], lens[-1] = L, 0
+    elif layout == "paged":
+        lens = [L] * B
+    note("random block case %d: %s B=%d Hq=%d Hkv=%d nq=%d L=%d d=%d kv=%s lens=%s S=%d alibi=%s kb=%d vb=%d ps=%d"
+         % (i, layout, B, Hq, Hkv, nq, L, d, kv, lens, S, alibi, kb, vb, ps))
+    c = W.random_case(2800 + i, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi, scale_block=kb)
+    if vb != kb:                                   # V in its own mode
+        if vb:
+            v, vs = W.draw_kv_fp8_blocks(2850 + i, B, Hkv, L, d, vb, kv)
+        else:
+            v, vs = W.draw_kv_fp8(2850 + i, B, Hkv, L, d, kv)
+        if lens is not None:
+            for b, Lb in enumerate(lens):
+                v.view(torch.uint8)[b, :, Lb:, :] = 0x7F if kv == E4 else 0x7E
+        c["v"], c["v_scale"] = v, vs
+    if nq > 1:
+        c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(2900 + i))
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                            k_scale=c["k_scale"], v_scale=c["v_scale"], k_scale_block=kb, v_scale_block=vb)
+    dv = lambda x: None if x is None else x.to(DEV)
+    q, sl, sp = dv(c["q"]), dv(c["seq_lens"]), dv(c["slopes"])
+    kw = dict(k_scale_block=kb, v_scale_block=vb)
+    if layout == "paged":
+        kc, vc, table = W.page_kv(c["k"], c["v"], ps, 2800 + i)
+        Lcap = table.shape[1] * ps
+        ks = dv(padded(c["k_scale"], kb, Lcap) if kb else c["k_scale"])
+        vs = dv(padded(c["v_scale"], vb, Lcap) if vb else c["v_scale"])
+        kc, vc, table = dv(kc), dv(vc), dv(table)
+        out = lib.decode_paged(q, kc, vc, table, sl, sp, S, k_scale=ks, v_scale=vs, **kw)
+        SS = S if S > 0 else lib.tad_auto_splits(B, Hq, Hkv, nq, Lcap, d, kc.dtype, 0)
+        ws = lib.workspace(q, c["k"], SS)
+        lib.tad_split_paged(q, kc, vc, table, sl, sp, SS, ws, k_scale=ks, v_scale=vs, **kw)
+    else:
+        if layout == "tokmajor":
+            k = c["k"].view(torch.uint8).transpose(1, 2).contiguous().transpose(1, 2).view(kv).to(DEV)
+            v = c["v"].view(torch.uint8).transpose(1, 2).contiguous().transpose(1, 2).view(kv).to(DEV)
+        else:
+            k, v = dv(c["k"]), dv(c["v"])
+        ks, vs = dv(c["k_scale"]), dv(c["v_scale"])
+        out = lib.decode(q, k, v, sl, sp, S, k_scale=ks, v_scale=vs, **kw)
+        SS = lib.resolve_splits(q, k, S)
+        ws = lib.workspace(q, k, SS)
+        lib.tad_split(q, k, v, sl, sp, SS, ws, k_scale=ks, v_scale=vs, **kw)
+    two = torch.full_like(out, float("nan"))
+    lib.tad_combine(ws, B, Hq, nq, SS, d, two)
+    torch.cuda.synchronize()
+    assert torch.equal(out, two), "random block case %d: decode differs from split + combine" % i
+    vd = dequantised(c["v"], c["v_scale"], vb) if vb else \
+        np.nan_to_num(oracle.widen(c["v"])) * c["v_scale"].double().numpy()[:, :, None, None]
+    assert_parity(out.cpu().numpy(), ref, kv, vmax_valid(torch.from_numpy(vd), c["seq_lens"]),
+                  "random block case %d" % i)
