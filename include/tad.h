@@ -11,11 +11,11 @@
  * ALiBi bias -slope_h * (L_t - 1 - j).  With one query token (the usual decode
  * step) L_t = L_b.  With nq tokens they are the row's last nq positions and token t
  * sees the keys up to its own position: L_t = clamp(L_b - nq + t + 1, 0, L_b)
- * (causal among the new tokens, as when several drafted tokens are verified).  Sources: "Tree Attention Decoding"
- * (tree_attn_decode.py gist), functions regular_decode (the definition) and
- * tree_attn_decode (chunk the keys, keep a local max, a sum of exponentials and an
- * exponential-weighted value sum per chunk, then take the global max, rescale and
- * sum); "ALiBi with causal=True unexpected bias?" (llm-foundry issue 186: the causal
+ * (causal among the new tokens, as when several drafted tokens are verified).
+ * Sources: "Tree Attention Decoding" (tree_attn_decode.py gist), functions
+ * regular_decode (the definition) and tree_attn_decode (chunk the keys, keep a local
+ * max, a sum of exponentials and an exponential-weighted value sum per chunk, then
+ * take the global max, rescale and sum); "ALiBi with causal=True unexpected bias?" (llm-foundry issue 186: the causal
  * bias row and passing a per-head vector instead of a full bias matrix);
  * "Flash Aandacht: Revolutie in Transformer Efficientie", section on the mathematics
  * (softmax decomposition and fusion).
@@ -156,8 +156,9 @@ int32_t tad_auto_splits(int32_t B, int32_t Hq, int32_t Hkv, int32_t nq, int64_t 
  * (one head cut into 8 chunks is 8 work-groups), so where the vector kernel serves one
  * query row per KV head, each chunk of at least 256 KiB of K+V is read by up to Pmax
  * work-groups, each a contiguous piece of ceil(c / P) keys (whole pages for a paged
- * cache, whole scale blocks with block scales) with P = min(Pmax, chunk bytes / 128 KiB); a second kernel then merges each
- * chunk's pieces into the chunk's (m, l, o) by the same rescale-and-sum.  The chunks
+ * cache, whole scale blocks with block scales) with P = min(Pmax, chunk bytes /
+ * 128 KiB); a second kernel then merges each chunk's pieces into the chunk's (m, l, o)
+ * by the same rescale-and-sum.  The chunks
  * themselves, and so the partials tad_split reports, are those n_splits asks for; only
  * their rounding differs from an uncut chunk.  P depends on the call's sizes only, so
  * every entry point cuts a call the same way.
@@ -193,7 +194,7 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  * Split + merge with a caller-provided workspace (no allocation).  Small problems run
  * as ONE launch, the merge done by the split kernel itself: each work-group writes its
  * partial, and the last one to finish (counted in the workspace's cnt array with
- * agent-scope acquire-release updates) merges, then returns its counter to zero.  Two
+ * agent-scope acquire-release updates) merges, then returns its counter to zero.  Three
  * kernels do this:
  *   - the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d] caches,
  *     and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512, more
@@ -210,13 +211,14 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  *     compute-unit count: the last work-group of a (b, 4-head group) merges its 4 rows.
  * Chunks read as pieces (below) on such small grids take two launches: the pieces
  * kernel's last work-group per row merges the row.  Larger problems run the split
- * (and pieces) and combine kernels back to back (the counters are then unused).  Either way the output is bit-identical
- * to tad_split followed by tad_combine.  The one-launch form saves a launch where the
- * host's launch rate sets the pace; replayed in a graph it is about as fast as the two
- * kernels, or up to about a microsecond slower.  The counters must be zero the first
- * time a workspace is used (tad_workspace_clear, or memory allocated zeroed); every
- * call that runs to completion leaves them zero, so a workspace can be reused call
- * after call.  Calls that share one workspace must not overlap.
+ * (and pieces) and combine kernels back to back (the counters are then unused).
+ * Either way the output is bit-identical to tad_split followed by tad_combine.  The
+ * one-launch form saves a launch where the host's launch rate sets the pace; replayed
+ * in a graph it is about as fast as the two kernels, or up to about a microsecond
+ * slower.  The counters must be zero the first time a workspace is used
+ * (tad_workspace_clear, or memory allocated zeroed); every call that runs to
+ * completion leaves them zero, so a workspace can be reused call after call.  Calls
+ * that share one workspace must not overlap.
  */
 int tad_decode_ws(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
                   const int32_t *seq_lens, const float *alibi_slopes, int32_t n_splits,
