@@ -12,17 +12,17 @@ import torch
 
 import oracle
 import workloads as W
-from test_parity_gpu import assert_parity, note, vmax_real
+from test_parity_gpu import assert_parity, note, vmax_real, vmax_valid
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 
 
-def run_workload(lib, wid):
+def run_workload(lib, wid, scale_block=0):
     w = W.WORKLOADS[wid]
-    note("workload %d: %s" % (wid, w.name))
-    c = W.make_workload(wid)
+    note("workload %d: %s%s" % (wid, w.name, ", scale blocks of %d keys" % scale_block if scale_block else ""))
+    c = W.make_workload(wid, scale_block)
     q = c["q"].to(DEV)
     k = c["k"].to(DEV)
     v = c["v"].to(DEV)
@@ -32,14 +32,22 @@ def run_workload(lib, wid):
     vs = c["v_scale"].to(DEV) if c["v_scale"] is not None else None
     S = lib.resolve_splits(q, k, c["n_splits"])
     note("workload %d: n_splits=%d" % (wid, S))
-    out = lib.decode(q, k, v, sl, sp, S, k_scale=ks, v_scale=vs)
+    out = lib.decode(q, k, v, sl, sp, S, k_scale=ks, v_scale=vs, k_scale_block=scale_block,
+                     v_scale_block=scale_block)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     del q, k, v
     torch.cuda.empty_cache()
     ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
-                            k_scale=c["k_scale"], v_scale=c["v_scale"])
-    assert_parity(out, ref, w.kv_dtype, vmax_real(c), "workload %d" % wid)
+                            k_scale=c["k_scale"], v_scale=c["v_scale"], k_scale_block=scale_block,
+                            v_scale_block=scale_block)
+    if scale_block:                        # max |V| of the dequantised values, block by block
+        vd = np.repeat(c["v_scale"].double().numpy(), scale_block, axis=2)[:, :, :c["v"].shape[2]]
+        vmax = vmax_valid(torch.from_numpy(np.nan_to_num(oracle.widen(c["v"])) * vd[:, :, :, None]),
+                          c["seq_lens"])
+    else:
+        vmax = vmax_real(c)
+    assert_parity(out, ref, w.kv_dtype, vmax, "workload %d" % wid)
     return out, ref, c
 
 
@@ -67,6 +75,13 @@ def test_workload6_fp8_mha(lib):
 def test_workload7_fp8_gqa_ragged(lib):
     out, ref, c = run_workload(lib, 7)
     assert c["seq_lens"].min() >= 1024
+
+
+@pytest.mark.parametrize("wid", [6, 7])
+def test_fp8_workloads_with_block_scales(lib, wid):
+    """Workloads 6 and 7 quantised with one scale per 64-key block (the bench's
+    --scale-block 64), at full size."""
+    run_workload(lib, wid, 64)
 
 
 def test_workload5_million_keys(lib):
