@@ -75,6 +75,7 @@ CASES = [
     (15, 2, 8, 8, 1, 2500, 64, E5, 6, [2500, 801], True, 16, 128, "paged32", "head-packed, paged"),
     (16, 2, 2, 2, 1, 2000, 128, E4, 5, [2000, 1300], False, 64, 64, "paged16hm", "vector, paged"),
     (17, 2, 8, 2, 1, 2000, 128, E4, 6, [2000, 700], False, 64, 16, "paged48", "matrix cores, 48-row pages"),
+    (18, 1, 2, 2, 1, 20000, 128, E5, 2, None, False, 64, 128, "paged16hm", "vector, paged, pieces"),
 ]
 
 
