@@ -19,7 +19,7 @@
 //
 // FP8 block scales: a tile's U keys (a power of two, at most 16) lie in one block, since
 // blocks hold at least 16 keys and chunks start on block boundaries, so each lane group
-// loads its head's K and V scale once per tile.
+// loads its head's K and V scale once per tile, one tile ahead.
 //
 // Every K and V byte of a chunk is read once, with 16-byte buffer loads; loads past
 // the chunk end return zero.  Every chunk has its work-group, so an empty chunk writes
@@ -163,6 +163,16 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
 
     const uint32_t lane_off = (uint32_t)(lane * Row::BYTES);
     TilePages pages;                                       // paged: this wave's tile pages
+    // BLK: the block scales of the tile at t (its U keys lie in one block), for this
+    // lane group's head; each tile's are loaded one tile ahead, behind the K and V rows
+    // of the tile before.
+    float kst = 1.f, vst = 1.f;
+    auto tile_scales = [&](int t, float &ks, float &vs) {
+        const int jt = __builtin_amdgcn_readfirstlane(j0 + t);
+        if (a.k_blk_lg) ks = block_scale(a.k_scale, a.k_blk_lg, a.k_nblk, b * a.Hkv + h, jt);
+        if (a.v_blk_lg) vs = block_scale(a.v_scale, a.v_blk_lg, a.v_nblk, b * a.Hkv + h, jt);
+    };
+    if constexpr (BLK) tile_scales(wave * U, kst, vst);
     for (int t0 = wave * U, k = 0; t0 < n; t0 += STRIDE, ++k) {
         __amdgpu_buffer_rsrc_t krs = kr, vrs = vr;
         int tb = t0;                                       // first key, relative to the resource
@@ -178,13 +188,8 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
         for (int u = 0; u < U; ++u) kk[u].load(krs, (uint32_t)(tb + u) * krow + lane_off);
 #pragma unroll
         for (int u = 0; u < U; ++u) vv[u].load(vrs, (uint32_t)(tb + u) * vrow + lane_off);
-        // FP8 block scales of the tile, loaded behind its K and V rows
-        float kst = 1.f, vst = 1.f;
-        if constexpr (BLK) {
-            const int jt = __builtin_amdgcn_readfirstlane(j0 + t0);
-            if (a.k_blk_lg) kst = block_scale(a.k_scale, a.k_blk_lg, a.k_nblk, b * a.Hkv + h, jt);
-            if (a.v_blk_lg) vst = block_scale(a.v_scale, a.v_blk_lg, a.v_nblk, b * a.Hkv + h, jt);
-        }
+        float kstn = 1.f, vstn = 1.f;                      // BLK: the next tile's scales
+        if constexpr (BLK) tile_scales(t0 + STRIDE, kstn, vstn);
 
         float sc[U];
 #pragma unroll
@@ -230,6 +235,10 @@ __global__ __launch_bounds__(kHeadsThreads) void split_heads_kernel(SplitArgs a)
             for (int e = 0; e < EPL; ++e) o[e] = fmaf(pv, vf[e], o[e]);
         }
         m = m_new;
+        if constexpr (BLK) {
+            kst = kstn;
+            vst = vstn;
+        }
     }
 
     // ---- merge the NW wave states of each head (fixed order) and write the partials.
