@@ -70,6 +70,11 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libtad.so is not built (%s); run __graft_entry__.build() or "
                            "python -m long_context_attention_split_amd.build" % LIB_PATH)
+    # torch first: its HIP runtime is then the one libtad.so binds to (same soname), so
+    # the process has one runtime and the tensors' device pointers and streams are
+    # valid in the library.  Loaded first, the library would bring the system runtime
+    # and torch would share that one instead of its own.
+    _torch()
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(TadTensor)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t

@@ -363,3 +363,18 @@ def test_noalloc_refuses_calls_beyond_its_scratch(lib):
     bad["out"] = desc([2, 8, 128], tad.TAD_BF16)
     assert call(bad, 4) == tad.TAD_EDTYPE
     assert call(good(), 5000) == tad.TAD_EINVAL                         # n_splits beyond the maximum
+
+
+def test_one_hip_runtime_in_the_process():
+    """Loading the binding before anything else leaves one HIP runtime in the process
+    (torch's, which libtad.so then shares), so torch tensors and streams are valid in
+    the library."""
+    import subprocess
+    import sys
+    code = ("import long_context_attention_split_amd as t; t.load(); "
+            "m = open('/proc/self/maps').read().splitlines(); "
+            "print('\\n'.join(sorted({l.split()[-1] for l in m if 'libamdhip64' in l})))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert out.returncode == 0, out.stderr[-2000:]
+    paths = [p for p in out.stdout.split("\n") if p.strip()]
+    assert len(paths) == 1, paths
