@@ -272,3 +272,32 @@ def test_random_block_scaled(lib, case):
         np.nan_to_num(oracle.widen(c["v"])) * c["v_scale"].double().numpy()[:, :, None, None]
     assert_parity(out.cpu().numpy(), ref, kv, vmax_valid(torch.from_numpy(vd), c["seq_lens"]),
                   "random block case %d" % i)
+
+
+@pytest.mark.parametrize("form", ["vector", "head-packed", "matrix cores"])
+def test_block_scales_extreme_values(lib, form):
+    """Block scales spanning 2^-30 .. 2^30, some exactly 0 (an all-zero block) and some
+    negative (sign-flipped codes): scores reach ~1e10 and value rows ~1e11, and the
+    result still matches the oracle (max-abs bar relative to the largest real |V|, and
+    the rel-L2 gate)."""
+    B, L, d, kb, vb = 2, 3000, 128, 32, 64
+    Hq, Hkv = {"vector": (4, 4), "head-packed": (8, 8), "matrix cores": (16, 4)}[form]
+    c = block_case(1100 + len(form), B, Hq, Hkv, 1, L, d, E4, [L, 1777], False, kb, vb)
+    g = torch.Generator().manual_seed(1200 + len(form))
+    for key in ("k_scale", "v_scale"):
+        s = c[key]
+        mag = torch.exp2(torch.randint(-30, 31, s.shape, generator=g).float())
+        sign = torch.where(torch.rand(s.shape, generator=g) < 0.15, -1.0, 1.0)
+        zero = torch.rand(s.shape, generator=g) < 0.05
+        c[key] = torch.where(zero, torch.zeros_like(s), s * mag * sign).contiguous()
+    note("extreme block scales %s: |scale| in [%g, %g]" % (form, c["v_scale"].abs()[c["v_scale"] != 0].min(),
+                                                           c["v_scale"].abs().max()))
+    ref = oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], k_scale=c["k_scale"],
+                            v_scale=c["v_scale"], k_scale_block=kb, v_scale_block=vb)
+    layout = "tokmajor" if form == "head-packed" else "contig"
+    out = run_layout(lib, c, layout, 6, kb, vb, "ws")
+    two = run_layout(lib, c, layout, 6, kb, vb, "split")
+    torch.cuda.synchronize()
+    assert torch.equal(out, two)
+    vmax = vmax_valid(torch.from_numpy(np.abs(dequantised(c["v"], c["v_scale"], vb))), c["seq_lens"])
+    assert_parity(out.cpu().numpy(), ref, E4, vmax, "extreme block scales %s" % form)
