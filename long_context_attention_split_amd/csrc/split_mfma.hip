@@ -45,7 +45,10 @@
 // holds at most one work-group per resident slot, and the empty chunks' merge
 // identities are written afterwards by single waves.  The chunk length is one per
 // batch, lengthened on the device when the non-empty chunks would not fit the
-// resident work-groups.
+// resident work-groups.  A KV head with more than 16 (head, token) columns (g * nq up
+// to 256) has them cut into blocks of 16, the product width: each (item, column block)
+// is a work-group of its own, the blocks of one item on one XCD one after another
+// (column_block_of), so that the later blocks read the chunk's K and V from its L2.
 //
 // Softmax per head: lane l owns head l%16 and 4 keys of each 16-key block; the lanes
 // l, l^16, l^32, l^48 exchange their max and sum (row swaps, no LDS).  The running
@@ -123,21 +126,44 @@ __device__ __forceinline__ f32x4_t mfma16x16x16(uint2 a, uint2 b, f32x4_t c) {
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // The merge identity (m = -inf, l = 0), written by one wave, for the query columns of
-// an empty item: row wi.b, KV heads wi.g * HG .. + HG - 1, chunk wi.s.  Those are the
-// HG * g * nq (head, token) rows R0, R0 + 1, ... of the workspace (at most 64).  The
-// merge gives such a chunk weight 0 and leaves its o out of the sums, so o is not
-// written: with 64 rows of d = 128 that is 32 KB per empty item, and on a ragged
-// batch of 8 rows with 4 tokens each those stores took about a seventh of the
+// an empty item: row wi.b, KV heads wi.g * HG .. + HG - 1, chunk wi.s, every column
+// block.  Those are the HG * g * nq (head, token) rows R0, R0 + 1, ... of the
+// workspace.  The merge gives such a chunk weight 0 and leaves its o out of the sums,
+// so o is not written: with 64 rows of d = 128 that is 32 KB per empty item, and on a
+// ragged batch of 8 rows with 4 tokens each those stores took about a seventh of the
 // kernel's time.
 template <int D, int HG>
 __device__ __forceinline__ void wave_identity(const SplitArgs &a, const WorkItem wi) {
     const int lane = (int)(threadIdx.x & 63);
     const int rows = HG * a.group * a.nq;
     const int64_t R0 = ((int64_t)wi.b * a.Hq + (int64_t)wi.g * HG * a.group) * a.nq;
-    if (lane < rows) {
-        const int64_t r = (R0 + lane) * a.S + wi.s;
+    for (int i = lane; i < rows; i += 64) {
+        const int64_t r = (R0 + i) * a.S + wi.s;
         a.ws_m[r] = kNegInf;
         a.ws_l[r] = 0.f;
+    }
+}
+
+// Column blocks: a KV head's g * nq (head, token) columns are cut into blocks of 16, one
+// product width, and each (busy item, column block) pair is a work-group of its own that
+// streams the item's K and V.  Work-group w of the busy ones -> (busy item, block): the
+// ncb blocks of item i run on work-groups 8 apart, all on one XCD (the dispatcher sends
+// work-group w to XCD w mod 8) and dispatched one after another, so the later blocks
+// find the chunk's K and V in that XCD's L2; items go in groups of 8, and a last group
+// of fewer items in order.  The identity map for ncb = 1.  Wave-uniform.
+__device__ __forceinline__ void column_block_of(int w, int busy, int ncb, int *item, int *cb) {
+    const int grp = 8 * ncb;
+    const int full = busy / 8;                   // complete groups of 8 items
+    const int q = w / grp;
+    if (q < full) {
+        const int r = w - q * grp;
+        *item = 8 * q + (r & 7);
+        *cb = r >> 3;
+    } else {
+        const int rem = max(busy - 8 * full, 1); // items of the last group (w < busy * ncb)
+        const int j = w - grp * full;
+        *item = 8 * full + j % rem;
+        *cb = j / rem;
     }
 }
 
@@ -179,9 +205,11 @@ __device__ __forceinline__ void wave_zero_rows(const SplitArgs &a, const WorkIte
 // for a merge in another work-group of the same launch (the fused form).
 // BLK: FP8 K/V with block scales (kernels of their own, so that the per-(b, KV head)
 // kernels keep their registers and schedule).
+// cb: the column block (16 of the KV head's g * nq columns, from column 16 cb).
 template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false, bool BLK = false>
-__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int c, const int Lb,
-                                                uint4 *smem, float (*lds_ml)[HG * NWH][16], int *lds_cnt) {
+__device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int cb, const int c,
+                                                const int Lb, uint4 *smem, float (*lds_ml)[HG * NWH][16],
+                                                int *lds_cnt) {
     static_assert(D == 64 || D == 128, "head dim");
     constexpr bool F8 = KVT != kKvBF16;
     static_assert(!BLK || F8, "block scales are for FP8 K/V");
@@ -205,17 +233,19 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     const int c4 = lane >> 4;            // 8-wide (4-wide) reduction block of this lane
     const int j16 = lane & 15;           // column (head) / row (key, value column)
 
-    // Columns of the products are (query head, query token) pairs: column j16 < g*nq is
-    // head kvh*g + j16/nq, token j16%nq; with one token this is one head per column.
+    // Columns of the products are (query head, query token) pairs: product column j16 is
+    // the KV head's column jc = 16 cb + j16, which for jc < g*nq is head kvh*g + jc/nq,
+    // token jc%nq; with one token this is one head per column.
     const int S = a.S, g = a.group, nq = a.nq;
     const int gq = g * nq;
     const int b = wi.b, s = wi.s;
     const int kvh0 = wi.g * HG;                            // first KV head of the work-group
     const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
     const int kvh = kvh0 + hx;
-    const bool head_ok = j16 < gq;
-    const int tok = head_ok ? j16 % nq : 0;
-    const int h = kvh * g + (head_ok ? j16 / nq : 0);
+    const int jc = 16 * cb + j16;
+    const bool head_ok = jc < gq;
+    const int tok = head_ok ? jc % nq : 0;
+    const int h = kvh * g + (head_ok ? jc / nq : 0);
 
     const ChunkRange cr = chunk_of(Lb, s, c);
     const int j0 = cr.j0, j1 = cr.j1;
@@ -554,10 +584,15 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
             O[nb][3] = fmaf(wk, t.w, O[nb][3]);
         }
     }
-    if (head_ok) {
-        // column j16 is workspace row (b * Hq + kvh * g) * nq + j16; lane (c4, j16) holds
+    // The column again, from the lane index: the prologue's jc is not kept live through
+    // the loop (one register, which the paged FP8 block-scale kernels do not have).
+    int j16e = (int)(threadIdx.x & 15);
+    asm volatile("" : "+v"(j16e));
+    const int jce = 16 * cb + j16e;
+    if (jce < gq) {
+        // column jce is workspace row (b * Hq + kvh * g) * nq + jce; lane (c4, j16) holds
         // elements 16 nb + 4 c4 .. + 3
-        const int64_t r = (((int64_t)b * a.Hq + (int64_t)kvh * g) * nq + j16) * S + s;
+        const int64_t r = (((int64_t)b * a.Hq + (int64_t)kvh * g) * nq + jce) * S + s;
         float *const orow = a.ws_o + r * D + 4 * c4;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -619,24 +654,30 @@ void split_mfma_kernel(SplitArgs a) {
     __syncthreads();
 
     const int G = a.Hkv / HG;
+    const int ncb = (a.group * a.nq + 15) >> 4;            // 16-column blocks per KV head
     const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
-    // The fit applies where the launcher capped the grid at the resident slots (B * G
-    // <= slots); with more (row, KV-head group) pairs than slots no chunk length fits,
-    // and the grid holds every item, so the finest chunking stays.
-    const int fit_slots = (int64_t)a.B * G <= a.wg_slots ? a.wg_slots : 0;
-    const int c = fit_chunk_len(a, G, batch_chunk_len(a, len0), len0, fit_slots);
+    // The fit applies where the launcher capped the grid at the resident slots (B * G *
+    // ncb <= slots); with more (row, KV-head group, column block) triples than slots no
+    // chunk length fits, and the grid holds every item, so the finest chunking stays.
+    const int fit_slots = (int64_t)a.B * G * ncb <= a.wg_slots ? a.wg_slots : 0;
+    const int c = fit_chunk_len(a, G * ncb, batch_chunk_len(a, len0), len0, fit_slots);
     const int w = (int)blockIdx.x, grid = (int)gridDim.x;
     WorkItem wi{0, 0, 0};
-    int busy;
+    int busy, item = w, cb = 0;                            // busy items; this work-group's item and block
+    if (ncb > 1) {
+        busy = busy_items(a, G, c, len0);
+        if (w < busy * ncb) column_block_of(w, busy, ncb, &item, &cb);
+    }
     if (a.B <= 64) {
-        busy = busy_first_small(a, G, w, c, len0, &wi);
+        busy = busy_first_small(a, G, item, c, len0, &wi);
     } else {
         busy = busy_items(a, G, c, len0);
-        if (w < busy) wi = busy_first_item(a, G, w, c, len0);
+        if (item < busy) wi = busy_first_item(a, G, item, c, len0);
     }
-    if (w < busy) {
+    const int busy_wgs = busy * ncb;
+    if (w < busy_wgs) {
         const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
-        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL, BLK>(a, wi, c, Lb, smem, lds_ml, lds_cnt);
+        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL, BLK>(a, wi, cb, c, Lb, smem, lds_ml, lds_cnt);
         if constexpr (TAIL) {
             __shared__ int last;
             int32_t *const cnt = a.cnt + (int64_t)wi.b * a.Hkv + wi.g;
@@ -654,7 +695,7 @@ void split_mfma_kernel(SplitArgs a) {
     const int empties = a.B * G * a.S - busy;
     const int slots = grid * NW;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int e0 = ((w * NW + wave - busy * NW) % slots + slots) % slots;
+    const int e0 = ((w * NW + wave - busy_wgs * NW) % slots + slots) % slots;
     if (e0 < empties) {
         if (a.B <= 64) {
             const EmptyItems em(a, G, c, len0);
@@ -674,8 +715,8 @@ void split_mfma_kernel(SplitArgs a) {
 }
 
 bool split_mfma_supported(int d, int kv_type, int group, int nq) {
-    return (kv_type == kKvBF16 || kv_type == kKvE4M3 || kv_type == kKvE5M2) && group * nq >= 2 &&
-           group * nq <= 16 && (d == 64 || d == 128);
+    return (kv_type == kKvBF16 || kv_type == kKvE4M3 || kv_type == kKvE5M2) && (int64_t)group * nq >= 2 &&
+           (int64_t)group * nq <= kMaxMfmaColumns && (d == 64 || d == 128);
 }
 
 // Fewest (row, 4-KV-head group, chunk) items for which a work-group serves 4 KV heads;
@@ -702,6 +743,8 @@ static bool runs_grouped_heads(const SplitArgs &a, int d) {
 // work-group's tile buffers (4 waves x 2 tiles of 2 d 16-byte slots: 64 d floats).
 bool split_mfma_fusable(const SplitArgs &a, int d) {
     if (!split_mfma_supported(d, a.kv_type, a.group, a.nq) || runs_grouped_heads(a, d)) return false;
+    if (a.group * a.nq > 16) return false;             // one column block: the merge takes <= 16 rows
+
     return a.S >= 1 && a.S <= 64 && merge_rows_lds_floats(a.group * a.nq, a.S, d) <= 64 * d;
 }
 
@@ -730,7 +773,8 @@ static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
         return nb;
     }();
     a.wg_slots = a.cus * per_cu;
-    if (a.wg_slots > 0 && (int64_t)a.B * (a.Hkv / HG) <= a.wg_slots && grid > a.wg_slots) grid = a.wg_slots;
+    const int64_t ncb = (a.group * a.nq + 15) / 16;
+    if (a.wg_slots > 0 && (int64_t)a.B * (a.Hkv / HG) * ncb <= a.wg_slots && grid > a.wg_slots) grid = a.wg_slots;
     hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK>), dim3((unsigned)grid),
                        dim3(THREADS), 0, st, a);
 }
@@ -738,7 +782,8 @@ static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
 template <int D, int KVT, bool BLK = false>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     constexpr int WAVES = D == 128 ? 3 : 4;
-    const int64_t items = (int64_t)a.B * a.Hkv * a.S;
+    const int64_t ncb = (a.group * a.nq + 15) / 16;    // column blocks: a work-group each
+    const int64_t items = (int64_t)a.B * a.Hkv * a.S * ncb;
     if (a.fused) {                                     // split_mfma_fusable holds
         if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, true, BLK>(a, items, st);
         else launch_k<D, WAVES, false, 1, 4, KVT, true, BLK>(a, items, st);
@@ -746,7 +791,7 @@ static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
     }
     if (runs_grouped_heads(a, D)) {
         constexpr int NWH = WAVES;                         // one work-group fills a CU
-        const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S;
+        const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S * ncb;
         if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT, false, BLK>(a, grid, st);
         else launch_k<D, WAVES, false, 4, NWH, KVT, false, BLK>(a, grid, st);
         return;

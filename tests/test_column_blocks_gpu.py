@@ -1,0 +1,103 @@
+"""GPU parity of grouped-query decode with more than 16 (head, token) columns per KV
+head (query-head groups times query tokens, g * nq up to 256).
+
+The matrix-core kernel cuts a KV head's g * nq columns into blocks of 16 (one product
+width); each (chunk, column block) pair is a work-group of its own that streams the
+chunk's K and V, and the blocks of one chunk run on one XCD, one after another.  Every
+case is held to the oracle's bars (fp64 definition: softmax over each token's visible
+keys, times V), checked bit for bit against tad_split + tad_combine on a workspace
+poisoned with NaN (a partial row no work-group wrote would surface), and repeated
+(bit-identical calls).  The cases cover one and four KV heads per work-group, a last
+group of fewer than 8 busy chunks, d 64 and 128, bf16, FP8 with per-head and per-block
+scales, ALiBi, ragged rows shorter than nq, a paged cache, and 256 columns (16 blocks,
+the most) next to 258 (the vector kernel).
+"""
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from test_block_scales_gpu import dequantised
+from test_parity_gpu import DEV, assert_parity, note, to_dev, vmax_real, vmax_valid
+from test_paged_gpu import paged_case, run_paged, oracle_of
+
+pytestmark = pytest.mark.gpu
+
+BF16, E4M3, E5M2 = torch.bfloat16, torch.float8_e4m3fn, torch.float8_e5m2
+
+
+def tokens_case(seed, B, Hq, Hkv, nq, L, d, kv, lens, alibi, scale_block=0):
+    c = W.random_case(seed, B, Hq, Hkv, L, d, kv_dtype=kv, seq_lens=lens, alibi=alibi, scale_block=scale_block)
+    c["q"] = torch.randn((B, Hq, nq, d), generator=torch.Generator().manual_seed(seed + 9))
+    return c
+
+
+def oracle_ref(c, blk=0):
+    return oracle.decode_f64(c["q"], c["k"], c["v"], seq_lens=c["seq_lens"], slopes=c["slopes"],
+                             k_scale=c["k_scale"], v_scale=c["v_scale"], k_scale_block=blk, v_scale_block=blk)
+
+
+def vmax_of(c, blk):
+    """max |V| over the valid keys, dequantised (per-head or per-block scales)."""
+    if not blk:
+        return vmax_real(c)
+    v = dequantised(c["v"], c["v_scale"], blk)
+    return vmax_valid(torch.from_numpy(v), c["seq_lens"])
+
+
+def split_combine_poisoned(lib, g, S, blk):
+    """tad_split into a workspace whose every byte is 0xFF (NaN partials; tad_split with
+    several columns per KV head leaves the arrival counters alone), then tad_combine."""
+    B, Hq, nq, d = g["q"].shape
+    ws = lib.workspace(g["q"], g["k"], S)
+    ws.fill_(0xFF)
+    lib.tad_split(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], S, ws, k_scale=g.get("k_scale"),
+                  v_scale=g.get("v_scale"), k_scale_block=blk, v_scale_block=blk)
+    out = torch.empty((B, Hq, nq, d), dtype=torch.float32, device=DEV)
+    lib.tad_combine(ws, B, Hq, nq, S, d, out)
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,nq,d,kv,lens,S,alibi,blk", [
+    (2, 4, 4, 17, 128, BF16, [700, 15], 3, False, 0),        # 17 columns: 2 blocks, one KV head per WG
+    (2, 8, 2, 5, 128, BF16, [900, 333], 5, True, 0),         # 4 heads x 5 tokens = 20
+    (2, 8, 4, 9, 64, BF16, [1000, 7], 4, True, 0),           # 18 columns, d 64, a row shorter than nq
+    (2, 32, 4, 4, 128, BF16, [1500, 1100], 4, False, 0),     # 8 heads x 4 tokens = 32, few items
+    (2, 32, 4, 4, 128, BF16, [1500, 1100], 160, True, 0),    # 4 KV heads per WG; 125 busy chunks (8 q + 5)
+    (3, 16, 1, 3, 64, E4M3, [800, 2, 1200], 6, False, 0),    # 16 heads x 3 tokens = 48, FP8
+    (2, 16, 4, 8, 128, E5M2, [1300, 640], 96, True, 64),     # 32 columns, 4 KV heads per WG, 64-key scale blocks
+    (1, 4, 2, 100, 64, BF16, [1000], 4, True, 0),            # 200 columns: 13 blocks
+    (2, 64, 4, 16, 128, BF16, [640, 900], 7, False, 0),      # 256 columns: 16 blocks (the most)
+    (1, 2, 1, 129, 64, BF16, [600], 3, False, 0),            # 258 columns: the vector kernel
+])
+def test_column_blocks_against_oracle(lib, B, Hq, Hkv, nq, d, kv, lens, S, alibi, blk):
+    gq = Hq // Hkv * nq
+    note("column blocks B=%d Hq=%d Hkv=%d nq=%d (g*nq=%d) d=%d kv=%s lens=%s S=%d alibi=%s blk=%d" %
+         (B, Hq, Hkv, nq, gq, d, kv, lens, S, alibi, blk))
+    c = tokens_case(900 + gq + d + S, B, Hq, Hkv, nq, max(lens), d, kv, lens, alibi, blk)
+    ref = oracle_ref(c, blk)
+    g = to_dev(c)
+    a = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], S, k_scale=g.get("k_scale"),
+                   v_scale=g.get("v_scale"), k_scale_block=blk, v_scale_block=blk)
+    again = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], S, k_scale=g.get("k_scale"),
+                       v_scale=g.get("v_scale"), k_scale_block=blk, v_scale_block=blk)
+    b = split_combine_poisoned(lib, g, S, blk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(b).all()
+    assert torch.equal(a, again) and torch.equal(a, b)
+    assert_parity(a.cpu().numpy(), ref, kv, vmax_of(c, blk), "column blocks g*nq=%d" % gq)
+    for bb, L in enumerate(lens):
+        if L < nq:                                   # tokens before the row's first key
+            assert (a[bb, :, :nq - L] == 0).all()
+
+
+@pytest.mark.parametrize("nq,ps,kv", [(6, 16, BF16), (12, 32, E4M3)])
+def test_column_blocks_paged(lib, nq, ps, kv):
+    """Paged cache (block table, 16- and 32-row pages), 4 query heads per KV head times
+    nq tokens = 24 or 48 columns, ragged rows, ALiBi."""
+    note("column blocks paged nq=%d ps=%d kv=%s" % (nq, ps, kv))
+    c = paged_case(960 + nq, 2, 8, 2, 1100, 128, ps, kv, lens=[1100, 517], alibi=True, nq=nq)
+    ref = oracle_of(c)
+    for S in (5, 0):
+        out = run_paged(lib, c, S)
+        assert_parity(out, ref, kv, vmax_real(c), "paged column blocks S=%d" % S)

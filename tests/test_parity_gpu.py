@@ -277,8 +277,8 @@ def multi_case(seed, B, Hq, Hkv, nq, L, d, kv=torch.bfloat16, lens=None, alibi=F
     (2, 4, 4, 2, torch.bfloat16, 128),      # matrix-core path: 2 tokens per head
     (1, 8, 8, 16, torch.bfloat16, 128),     # 16 tokens fill the 16 columns
     (2, 8, 2, 4, torch.bfloat16, 64),       # 4 heads x 4 tokens
-    (2, 4, 4, 17, torch.bfloat16, 128),     # more columns than 16: vector path
-    (2, 8, 2, 5, torch.bfloat16, 128),      # 4 heads x 5 tokens: vector path
+    (2, 4, 4, 17, torch.bfloat16, 128),     # 17 columns: matrix cores, 2 column blocks
+    (2, 8, 2, 5, torch.bfloat16, 128),      # 4 heads x 5 tokens: 2 column blocks
     (2, 4, 4, 3, torch.float32, 128),       # fp32: vector path
     (2, 4, 2, 3, torch.float8_e4m3fn, 256),
 ])
@@ -584,7 +584,7 @@ def test_auto_splits_rule(lib, B, Hq, Hkv, nq, Lmax, d, kv):
     per_cu = 4 if B == 1 else 6
     elem = torch.empty((), dtype=kv).element_size()
     gq = Hq // Hkv * nq
-    matrix = d in (64, 128) and kv != torch.float32 and 2 <= gq <= 16
+    matrix = d in (64, 128) and kv != torch.float32 and 2 <= gq <= 256
     heads_per_wg = 4 if matrix and Hkv % 4 == 0 else 1
     want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax * 2 * d * elem * heads_per_wg // (128 << 10), 4096))
     assert lib.tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, kv, 0) == want
