@@ -205,12 +205,17 @@ __device__ __forceinline__ void wave_zero_rows(const SplitArgs &a, const WorkIte
 // for a merge in another work-group of the same launch (the fused form).
 // BLK: FP8 K/V with block scales (kernels of their own, so that the per-(b, KV head)
 // kernels keep their registers and schedule).
-// cb: the column block (16 of the KV head's g * nq columns, from column 16 cb).
-template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false, bool BLK = false>
+// CB: column blocks per wave (1 or 2); cb: the work-group's first column block is
+// cb * CB (16 of the KV head's g * nq columns each, from column 16 cb CB).  With CB = 2
+// a wave keeps two blocks' q operands and states and runs both blocks' products on
+// each tile it loads, so the chunk's K and V are read once for 32 columns.
+// ox: LDS for the merge of blocks 1 .. CB - 1 ((CB - 1) * NW * NB * 64 float4).
+template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false, bool BLK = false, int CB = 1>
 __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int cb, const int c,
-                                                const int Lb, uint4 *smem, float (*lds_ml)[HG * NWH][16],
-                                                int *lds_cnt) {
+                                                const int Lb, uint4 *smem, float (*lds_ml)[3][HG * NWH][16],
+                                                float4 *ox, int *lds_cnt) {
     static_assert(D == 64 || D == 128, "head dim");
+    static_assert(CB == 1 || CB == 2, "column blocks per wave");
     constexpr bool F8 = KVT != kKvBF16;
     static_assert(!BLK || F8, "block scales are for FP8 K/V");
     constexpr int ELEM = F8 ? 1 : 2;     // bytes per K/V element
@@ -233,19 +238,24 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     const int c4 = lane >> 4;            // 8-wide (4-wide) reduction block of this lane
     const int j16 = lane & 15;           // column (head) / row (key, value column)
 
-    // Columns of the products are (query head, query token) pairs: product column j16 is
-    // the KV head's column jc = 16 cb + j16, which for jc < g*nq is head kvh*g + jc/nq,
-    // token jc%nq; with one token this is one head per column.
+    // Columns of the products are (query head, query token) pairs: product column j16 of
+    // block k is the KV head's column jc = 16 (cb CB + k) + j16, which for jc < g*nq is
+    // head kvh*g + jc/nq, token jc%nq; with one token this is one head per column.
     const int S = a.S, g = a.group, nq = a.nq;
     const int gq = g * nq;
     const int b = wi.b, s = wi.s;
     const int kvh0 = wi.g * HG;                            // first KV head of the work-group
     const int hx = wave / NWH, wr = wave % NWH;            // this wave's head and rank in it
     const int kvh = kvh0 + hx;
-    const int jc = 16 * cb + j16;
-    const bool head_ok = jc < gq;
-    const int tok = head_ok ? jc % nq : 0;
-    const int h = kvh * g + (head_ok ? jc / nq : 0);
+    bool head_ok[CB];
+    int tok[CB], h[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+        const int jc = 16 * (cb * CB + k) + j16;
+        head_ok[k] = jc < gq;
+        tok[k] = head_ok[k] ? jc % nq : 0;
+        h[k] = kvh * g + (head_ok[k] ? jc / nq : 0);
+    }
 
     const ChunkRange cr = chunk_of(Lb, s, c);
     const int j0 = cr.j0, j1 = cr.j1;
@@ -255,8 +265,12 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
         return;
     }
     // keys this column's token sees, and that limit relative to the chunk start
-    const int Lc = visible_keys(cr.L, nq, tok);
-    const int lim = min(n, Lc - j0);
+    int Lc[CB], lim[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+        Lc[k] = visible_keys(cr.L, nq, tok[k]);
+        lim[k] = min(n, Lc[k] - j0);
+    }
     // tiles ending at or before lim_all are seen in full by every column
     const int lim_all = __builtin_amdgcn_readfirstlane(min(n, visible_keys(cr.L, nq, 0) - j0));
 
@@ -340,11 +354,13 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     const bool v_head = F8 && a.v_scale && (!BLK || !a.v_blk_lg);
     const float qs = a.qscale * (k_head ? a.k_scale[b * a.Hkv + kvh] : 1.f);
     const float vs = v_head ? a.v_scale[b * a.Hkv + kvh] : 1.f;   // applied to this wave's O
-    uint4 qhi[NKK], qlo[NKK];
+    uint4 qhi[CB][NKK], qlo[CB][NKK];
+#pragma unroll
+    for (int k = 0; k < CB; ++k)
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         float x[8];
-        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h * a.sqh + (int64_t)tok * a.sqt + 32 * kk + 8 * c4;
+        const int64_t qoff = (int64_t)b * a.sqb + (int64_t)h[k] * a.sqh + (int64_t)tok[k] * a.sqt + 32 * kk + 8 * c4;
         if (a.q_bf16) {
             const uint4 w = *(const uint4 *)((const uint16_t *)a.q + qoff);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
@@ -358,11 +374,13 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
         }
         uint32_t hw[8], lw[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) split_bf16(head_ok ? x[t] * qs : 0.f, hw[t], lw[t]);
-        qhi[kk] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
-        qlo[kk] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
+        for (int t = 0; t < 8; ++t) split_bf16(head_ok[k] ? x[t] * qs : 0.f, hw[t], lw[t]);
+        qhi[k][kk] = make_uint4(hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16);
+        qlo[k][kk] = make_uint4(lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16);
     }
-    const float slope2 = (a.slopes && head_ok) ? a.slopes[h] * 1.4426950408889634f : 0.f;
+    float slope2[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) slope2[k] = (a.slopes && head_ok[k]) ? a.slopes[h[k]] * 1.4426950408889634f : 0.f;
     const bool alibi = a.slopes != nullptr;
 
     // Column state: O and l are sums of 2^(s - m) for a reference m that is moved up to
@@ -370,10 +388,15 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     // weights are at most 2^kSlack and the rescale of O is rare); the epilogue
     // re-expresses every wave's sums against the exact chunk maximum.
     constexpr float kSlack = 8.f;
-    float m = kNegInf, mx = kNegInf, l = 0.f;
-    f32x4_t O[NB];
+    float m[CB], mx[CB], l[CB];
+    f32x4_t O[CB][NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < CB; ++k) {
+        m[k] = mx[k] = kNegInf;
+        l[k] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) O[k][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // The matrix operands of one tile, as each lane holds them: K rows for the score
@@ -429,85 +452,108 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 
     auto consume = [&](const TileOps &ops, int t0, const TileScales &ts, auto alibi_c) {
         constexpr bool ALIBI = decltype(alibi_c)::value;
-        // scores: p[4 sb + r] is key t0 + 16 sb + 4 c4 + r, head j16
-        float p[4 * NSB];
+        // scores: p[k][4 sb + r] is key t0 + 16 sb + 4 c4 + r, column j16 of block k; each
+        // K operand is widened (FP8) once and serves every block
+        float p[CB][4 * NSB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-            f32x4_t sh = zero4, sl = zero4;                // q hi and lo: two independent chains
+            f32x4_t sh[CB], sl[CB];                        // q hi and lo: independent chains
+#pragma unroll
+            for (int k = 0; k < CB; ++k) sh[k] = sl[k] = zero4;
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 uint4 kop;
                 if constexpr (F8) kop = widen8(ops.k[sb][kk]);
                 else kop = ops.k[sb][kk];
-                sh = mfma16x16x32(kop, qhi[kk], sh);
-                sl = mfma16x16x32(kop, qlo[kk], sl);
-            }
-            const f32x4_t sc = sh + sl;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = sc[r];
-                if constexpr (BLK) x *= ts.k[sb];
-                if constexpr (ALIBI) x = fmaf(slope2, (float)(j0 + t0 + 16 * sb + 4 * c4 + r - (Lc - 1)), x);
-                p[4 * sb + r] = x;
+                for (int k = 0; k < CB; ++k) {
+                    sh[k] = mfma16x16x32(kop, qhi[k][kk], sh[k]);
+                    sl[k] = mfma16x16x32(kop, qlo[k][kk], sl[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < CB; ++k) {
+                const f32x4_t sc = sh[k] + sl[k];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = sc[r];
+                    if constexpr (BLK) x *= ts.k[sb];
+                    if constexpr (ALIBI)
+                        x = fmaf(slope2[k], (float)(j0 + t0 + 16 * sb + 4 * c4 + r - (Lc[k] - 1)), x);
+                    p[k][4 * sb + r] = x;
+                }
             }
         }
         if (t0 + TK > lim_all) {
 #pragma unroll
-            for (int i = 0; i < 4 * NSB; ++i) p[i] = (t0 + 16 * (i / 4) + 4 * c4 + i % 4 < lim) ? p[i] : kNegInf;
-        }
-        float mt = p[0];
+            for (int k = 0; k < CB; ++k)
 #pragma unroll
-        for (int i = 1; i < 4 * NSB; ++i) mt = fmaxf(mt, p[i]);
-        mt = rows_max(mt);
-        mx = fmaxf(mx, mt);
-        // some column's maximum passed its reference by more than the slack (or its
-        // first key arrived): every column's reference moves up to its running maximum
-        const bool up = __any(mt > m + kSlack);
-        const float m_new = up ? mx : m;
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4 * NSB; ++i) {
-            p[i] = exp2_fast(p[i] - m_use);
-            ps += p[i];
+                for (int i = 0; i < 4 * NSB; ++i)
+                    p[k][i] = (t0 + 16 * (i / 4) + 4 * c4 + i % 4 < lim[k]) ? p[k][i] : kNegInf;
         }
-        ps = rows_sum(ps);
-        if (up) {
-            const float alpha = exp2_fast(m - m_use);
-            l *= alpha;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) O[nb] *= alpha;
-        }
-        l += ps;
-        m = m_new;
-
-        // P^T operands: reduction slot t of this lane holds p[t] -- bf16: key
+        // P^T operands per block: reduction slot t of this lane holds p[k][t] -- bf16: key
         // t0 + 4 c4 + t; FP8: the slot order of the V^T read above
-        uint32_t ph[4 * NSB], pl[4 * NSB];
+        typedef typename std::conditional<F8, uint4, uint2>::type POp;
+        POp phi[CB], plo[CB];
 #pragma unroll
-        for (int i = 0; i < 4 * NSB; ++i) {
-            float pv = p[i];                           // weight of the value row: V block scale
-            if constexpr (BLK) pv *= ts.v[i / 4];
-            split_bf16(pv, ph[i], pl[i]);
-        }
-        if constexpr (F8) {
-            const uint4 phi = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16, ph[4] | ph[5] << 16,
-                                         ph[6] | ph[7] << 16);
-            const uint4 plo = make_uint4(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16, pl[4] | pl[5] << 16,
-                                         pl[6] | pl[7] << 16);
+        for (int k = 0; k < CB; ++k) {
+            float mt = p[k][0];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const uint4 vt = widen8(ops.v[nb]);
-                O[nb] = mfma16x16x32(vt, phi, O[nb]);
-                O[nb] = mfma16x16x32(vt, plo, O[nb]);
+            for (int i = 1; i < 4 * NSB; ++i) mt = fmaxf(mt, p[k][i]);
+            mt = rows_max(mt);
+            mx[k] = fmaxf(mx[k], mt);
+            // some column's maximum passed its reference by more than the slack (or its
+            // first key arrived): every column's reference moves up to its running maximum
+            const bool up = __any(mt > m[k] + kSlack);
+            const float m_new = up ? mx[k] : m[k];
+            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4 * NSB; ++i) {
+                p[k][i] = exp2_fast(p[k][i] - m_use);
+                ps += p[k][i];
             }
-        } else {
-            const uint2 phi = make_uint2(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16);
-            const uint2 plo = make_uint2(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16);
+            ps = rows_sum(ps);
+            if (up) {
+                const float alpha = exp2_fast(m[k] - m_use);
+                l[k] *= alpha;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                O[nb] = mfma16x16x16(ops.v[nb], phi, O[nb]);
-                O[nb] = mfma16x16x16(ops.v[nb], plo, O[nb]);
+                for (int nb = 0; nb < NB; ++nb) O[k][nb] *= alpha;
+            }
+            l[k] += ps;
+            m[k] = m_new;
+
+            uint32_t ph[4 * NSB], pl[4 * NSB];
+#pragma unroll
+            for (int i = 0; i < 4 * NSB; ++i) {
+                float pv = p[k][i];                    // weight of the value row: V block scale
+                if constexpr (BLK) pv *= ts.v[i / 4];
+                split_bf16(pv, ph[i], pl[i]);
+            }
+            if constexpr (F8) {
+                phi[k] = make_uint4(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16, ph[4] | ph[5] << 16, ph[6] | ph[7] << 16);
+                plo[k] = make_uint4(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16, pl[4] | pl[5] << 16, pl[6] | pl[7] << 16);
+            } else {
+                phi[k] = make_uint2(ph[0] | ph[1] << 16, ph[2] | ph[3] << 16);
+                plo[k] = make_uint2(pl[0] | pl[1] << 16, pl[2] | pl[3] << 16);
+            }
+        }
+        // value products: each V^T operand is widened (FP8) once and serves every block
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if constexpr (F8) {
+                const uint4 vt = widen8(ops.v[nb]);
+#pragma unroll
+                for (int k = 0; k < CB; ++k) {
+                    O[k][nb] = mfma16x16x32(vt, phi[k], O[k][nb]);
+                    O[k][nb] = mfma16x16x32(vt, plo[k], O[k][nb]);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < CB; ++k) {
+                    O[k][nb] = mfma16x16x16(ops.v[nb], phi[k], O[k][nb]);
+                    O[k][nb] = mfma16x16x16(ops.v[nb], plo[k], O[k][nb]);
+                }
             }
         }
     };
@@ -548,70 +594,83 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
     // stores the partial straight from its registers: per column, M = the largest
     // running maximum, each wave's weight 2^(m_w - M) against its reference maximum m_w,
     // l = sum_w weight_w l_w, o = sum_w weight_w O_w.
-    float4 *const mine = reinterpret_cast<float4 *>(bufA);   // NB * 64 pieces
+    // With CB = 2 the second block's O goes to the wave's piece of ox, and its
+    // (m, l, mx) to lds_ml[1].
+    auto o_area = [&](int k, int wv) -> float4 * {             // NB * 64 pieces
+        return k == 0 ? reinterpret_cast<float4 *>(smem + wv * 2 * TILE) : ox + ((k - 1) * NW + wv) * NB * 64;
+    };
     if (wr > 0) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) mine[nb * 64 + lane] = make_float4(O[nb][0], O[nb][1], O[nb][2], O[nb][3]);
-        if (c4 == 0) {
-            lds_ml[0][wave][j16] = m;
-            lds_ml[1][wave][j16] = l;
-            lds_ml[2][wave][j16] = mx;
+        for (int k = 0; k < CB; ++k) {
+            float4 *const mine = o_area(k, wave);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                mine[nb * 64 + lane] = make_float4(O[k][nb][0], O[k][nb][1], O[k][nb][2], O[k][nb][3]);
+            if (c4 == 0) {
+                lds_ml[k][0][wave][j16] = m[k];
+                lds_ml[k][1][wave][j16] = l[k];
+                lds_ml[k][2][wave][j16] = mx[k];
+            }
         }
         __hip_atomic_fetch_add(&lds_cnt[hx], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         return;
     }
     while (__hip_atomic_load(&lds_cnt[hx], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 64 * (NWH - 1))
         __builtin_amdgcn_s_sleep(1);
-    float M = mx;
 #pragma unroll
-    for (int k = 1; k < NWH; ++k) M = fmaxf(M, lds_ml[2][wave + k][j16]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    const float w0 = exp2_fast(m - Mu);
-    float lsum = w0 * l;
+    for (int k = 0; k < CB; ++k) {
+        float M = mx[k];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) O[nb] *= w0;
+        for (int w = 1; w < NWH; ++w) M = fmaxf(M, lds_ml[k][2][wave + w][j16]);
+        const float Mu = (M == kNegInf) ? 0.f : M;
+        const float w0 = exp2_fast(m[k] - Mu);
+        float lsum = w0 * l[k];
 #pragma unroll
-    for (int k = 1; k < NWH; ++k) {
-        const float wk = exp2_fast(lds_ml[0][wave + k][j16] - Mu);
-        lsum = fmaf(wk, lds_ml[1][wave + k][j16], lsum);
-        const float4 *const other = reinterpret_cast<const float4 *>(bufA + k * 2 * TILE);
+        for (int nb = 0; nb < NB; ++nb) O[k][nb] *= w0;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const float4 t = other[nb * 64 + lane];
-            O[nb][0] = fmaf(wk, t.x, O[nb][0]);
-            O[nb][1] = fmaf(wk, t.y, O[nb][1]);
-            O[nb][2] = fmaf(wk, t.z, O[nb][2]);
-            O[nb][3] = fmaf(wk, t.w, O[nb][3]);
-        }
-    }
-    // The column again, from the lane index: the prologue's jc is not kept live through
-    // the loop (one register, which the paged FP8 block-scale kernels do not have).
-    int j16e = (int)(threadIdx.x & 15);
-    asm volatile("" : "+v"(j16e));
-    const int jce = 16 * cb + j16e;
-    if (jce < gq) {
-        // column jce is workspace row (b * Hq + kvh * g) * nq + jce; lane (c4, j16) holds
-        // elements 16 nb + 4 c4 .. + 3
-        const int64_t r = (((int64_t)b * a.Hq + (int64_t)kvh * g) * nq + jce) * S + s;
-        float *const orow = a.ws_o + r * D + 4 * c4;
+        for (int w = 1; w < NWH; ++w) {
+            const float wk = exp2_fast(lds_ml[k][0][wave + w][j16] - Mu);
+            lsum = fmaf(wk, lds_ml[k][1][wave + w][j16], lsum);
+            const float4 *const other = o_area(k, wave + w);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const float sc = F8 ? vs : 1.f;
-            if constexpr (WT) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) store_partial(orow + 16 * nb + i, O[nb][i] * sc);
-            } else {
-                *reinterpret_cast<float4 *>(orow + 16 * nb) =
-                    make_float4(O[nb][0] * sc, O[nb][1] * sc, O[nb][2] * sc, O[nb][3] * sc);
+            for (int nb = 0; nb < NB; ++nb) {
+                const float4 t = other[nb * 64 + lane];
+                O[k][nb][0] = fmaf(wk, t.x, O[k][nb][0]);
+                O[k][nb][1] = fmaf(wk, t.y, O[k][nb][1]);
+                O[k][nb][2] = fmaf(wk, t.z, O[k][nb][2]);
+                O[k][nb][3] = fmaf(wk, t.w, O[k][nb][3]);
             }
         }
-        if (c4 == 0) {
-            if constexpr (WT) {
-                store_partial(a.ws_m + r, M);
-                store_partial(a.ws_l + r, lsum);
-            } else {
-                a.ws_m[r] = M;
-                a.ws_l[r] = lsum;
+        // The column again, from the lane index: the prologue's column is not kept live
+        // through the loop (one register, which the paged FP8 block-scale kernels do not
+        // have).
+        int j16e = (int)(threadIdx.x & 15);
+        asm volatile("" : "+v"(j16e));
+        const int jce = 16 * (cb * CB + k) + j16e;
+        if (jce < gq) {
+            // column jce is workspace row (b * Hq + kvh * g) * nq + jce; lane (c4, j16)
+            // holds elements 16 nb + 4 c4 .. + 3
+            const int64_t r = (((int64_t)b * a.Hq + (int64_t)kvh * g) * nq + jce) * S + s;
+            float *const orow = a.ws_o + r * D + 4 * c4;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float sc = F8 ? vs : 1.f;
+                if constexpr (WT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) store_partial(orow + 16 * nb + i, O[k][nb][i] * sc);
+                } else {
+                    *reinterpret_cast<float4 *>(orow + 16 * nb) =
+                        make_float4(O[k][nb][0] * sc, O[k][nb][1] * sc, O[k][nb][2] * sc, O[k][nb][3] * sc);
+                }
+            }
+            if (c4 == 0) {
+                if constexpr (WT) {
+                    store_partial(a.ws_m + r, M);
+                    store_partial(a.ws_l + r, lsum);
+                } else {
+                    a.ws_m[r] = M;
+                    a.ws_l[r] = lsum;
+                }
             }
         }
     }
@@ -638,23 +697,28 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 // point, which leaves the release little to write back: one row of 32 query heads
 // over 8 KV heads, 4096 keys at 32 chunks, 16.2 us with plain stores, 13.1 us written
 // through, 12.8 us with a relaxed ticket (graph replay).
+// CB: 16-column blocks per wave (2: a work-group serves 32 (head, token) columns of
+// each of its KV heads from one read of the chunk).
 template <int D, int WAVES, bool PAGED, int HG = 1, int NWH = 4, int KVT = kKvBF16, bool TAIL = false,
-          bool BLK = false>
+          bool BLK = false, int CB = 1>
 __global__ __launch_bounds__(64 * HG * NWH) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void split_mfma_kernel(SplitArgs a) {
-    static_assert(!TAIL || HG == 1, "the fused merge serves one KV head per work-group");
+    static_assert(!TAIL || (HG == 1 && CB == 1), "the fused merge serves one KV head and 16 columns per work-group");
     constexpr bool F8 = KVT != kKvBF16;
     constexpr int TILE = (F8 ? 32 : 16) * (D * (F8 ? 1 : 2) / 16);   // 16-byte slots per tile and tensor
     constexpr int NW = HG * NWH;
-    // Per wave: a (K tile, V tile) pair, reused for the merge.
+    // Per wave: a (K tile, V tile) pair, reused for the merge (and, with CB = 2, the
+    // second block's O in ox).
     __shared__ uint4 smem[NW * 2 * TILE];
-    __shared__ float lds_ml[3][NW][16];
+    __shared__ float4 ox[CB > 1 ? (CB - 1) * NW * (D / 16) * 64 : 1];
+    __shared__ float lds_ml[CB][3][NW][16];
     __shared__ int lds_cnt[HG];                            // lanes of each head's waves done with their loop
     if (threadIdx.x < HG) lds_cnt[threadIdx.x] = 0;
     __syncthreads();
 
     const int G = a.Hkv / HG;
-    const int ncb = (a.group * a.nq + 15) >> 4;            // 16-column blocks per KV head
+    // work-group column blocks per KV head: CB blocks of 16 columns each
+    const int ncb = (((a.group * a.nq + 15) >> 4) + CB - 1) / CB;
     const int len0 = lane_row_len(a, 0);                   // rows 0..63: one load, reused
     // The fit applies where the launcher capped the grid at the resident slots (B * G *
     // ncb <= slots); with more (row, KV-head group, column block) triples than slots no
@@ -677,7 +741,7 @@ void split_mfma_kernel(SplitArgs a) {
     const int busy_wgs = busy * ncb;
     if (w < busy_wgs) {
         const int Lb = wi.b < 64 ? __builtin_amdgcn_readlane(len0, wi.b) : row_len(a, wi.b);
-        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL, BLK>(a, wi, cb, c, Lb, smem, lds_ml, lds_cnt);
+        split_mfma_item<D, PAGED, HG, NWH, KVT, TAIL, BLK, CB>(a, wi, cb, c, Lb, smem, lds_ml, ox, lds_cnt);
         if constexpr (TAIL) {
             __shared__ int last;
             int32_t *const cnt = a.cnt + (int64_t)wi.b * a.Hkv + wi.g;
@@ -761,43 +825,57 @@ bool split_mfma_fusable(const SplitArgs &a, int d) {
 // One launch.  wg_slots = the work-groups of this kernel the device runs at once (its
 // occupancy per CU, queried once, times the CU count); the grid is capped there when
 // the batch's (row, KV-head group) pairs fit in it.
-template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT, bool TAIL = false, bool BLK = false>
+// grid: every (item, work-group column block); capped as above.
+template <int D, int WAVES, bool PAGED, int HG, int NWH, int KVT, bool TAIL = false, bool BLK = false, int CB = 1>
 static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
     constexpr int THREADS = 64 * HG * NWH;
     static const int per_cu = [] {
         int nb = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK>),
+                &nb, reinterpret_cast<const void *>(&split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK, CB>),
                 THREADS, 0) != hipSuccess || nb < 1)
             nb = 1;
         return nb;
     }();
     a.wg_slots = a.cus * per_cu;
-    const int64_t ncb = (a.group * a.nq + 15) / 16;
+    const int64_t ncb = ((a.group * a.nq + 15) / 16 + CB - 1) / CB;
     if (a.wg_slots > 0 && (int64_t)a.B * (a.Hkv / HG) * ncb <= a.wg_slots && grid > a.wg_slots) grid = a.wg_slots;
-    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((split_mfma_kernel<D, WAVES, PAGED, HG, NWH, KVT, TAIL, BLK, CB>), dim3((unsigned)grid),
                        dim3(THREADS), 0, st, a);
 }
 
-template <int D, int KVT, bool BLK = false>
+// CB: 16-column blocks per wave.  Two (more than 16 columns, per-(b, KV head) scales)
+// cost 2 x (q operands + O) registers: d = 128 then runs 2 waves per SIMD (8-wave
+// work-groups for 4 KV heads), d = 64 3.
+template <int D, int KVT, bool BLK = false, int CB = 1>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
-    constexpr int WAVES = D == 128 ? 3 : 4;
-    const int64_t ncb = (a.group * a.nq + 15) / 16;    // column blocks: a work-group each
+    constexpr int WAVES = CB == 1 ? (D == 128 ? 3 : 4) : (D == 128 ? 2 : 3);
+    const int64_t ncb = ((a.group * a.nq + 15) / 16 + CB - 1) / CB;   // work-group column blocks
     const int64_t items = (int64_t)a.B * a.Hkv * a.S * ncb;
-    if (a.fused) {                                     // split_mfma_fusable holds
-        if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, true, BLK>(a, items, st);
-        else launch_k<D, WAVES, false, 1, 4, KVT, true, BLK>(a, items, st);
-        return;
+    if constexpr (CB == 1) {
+        if (a.fused) {                                 // split_mfma_fusable holds
+            if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, true, BLK>(a, items, st);
+            else launch_k<D, WAVES, false, 1, 4, KVT, true, BLK>(a, items, st);
+            return;
+        }
     }
     if (runs_grouped_heads(a, D)) {
         constexpr int NWH = WAVES;                         // one work-group fills a CU
         const int64_t grid = (int64_t)a.B * (a.Hkv / 4) * a.S * ncb;
-        if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT, false, BLK>(a, grid, st);
-        else launch_k<D, WAVES, false, 4, NWH, KVT, false, BLK>(a, grid, st);
+        if (a.block_table) launch_k<D, WAVES, true, 4, NWH, KVT, false, BLK, CB>(a, grid, st);
+        else launch_k<D, WAVES, false, 4, NWH, KVT, false, BLK, CB>(a, grid, st);
         return;
     }
-    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, false, BLK>(a, items, st);
-    else launch_k<D, WAVES, false, 1, 4, KVT, false, BLK>(a, items, st);
+    if (a.block_table) launch_k<D, WAVES, true, 1, 4, KVT, false, BLK, CB>(a, items, st);
+    else launch_k<D, WAVES, false, 1, 4, KVT, false, BLK, CB>(a, items, st);
+}
+
+// Per-(b, KV head) scales and more than 16 columns per KV head: two column blocks per
+// wave.
+template <int D, int KVT>
+static void launch_mfma_cols(const SplitArgs &a, hipStream_t st) {
+    if (a.group * a.nq > 16) launch_mfma_t<D, KVT, false, 2>(a, st);
+    else launch_mfma_t<D, KVT>(a, st);
 }
 
 template <int D>
@@ -806,13 +884,13 @@ static void launch_mfma_d(const SplitArgs &a, hipStream_t st) {
     switch (a.kv_type) {
         case kKvE4M3:
             if (blk) launch_mfma_t<D, kKvE4M3, true>(a, st);
-            else launch_mfma_t<D, kKvE4M3>(a, st);
+            else launch_mfma_cols<D, kKvE4M3>(a, st);
             break;
         case kKvE5M2:
             if (blk) launch_mfma_t<D, kKvE5M2, true>(a, st);
-            else launch_mfma_t<D, kKvE5M2>(a, st);
+            else launch_mfma_cols<D, kKvE5M2>(a, st);
             break;
-        default: launch_mfma_t<D, kKvBF16>(a, st); break;
+        default: launch_mfma_cols<D, kKvBF16>(a, st); break;
     }
 }
 

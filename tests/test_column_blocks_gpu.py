@@ -2,8 +2,10 @@
 head (query-head groups times query tokens, g * nq up to 256).
 
 The matrix-core kernel cuts a KV head's g * nq columns into blocks of 16 (one product
-width); each (chunk, column block) pair is a work-group of its own that streams the
-chunk's K and V, and the blocks of one chunk run on one XCD, one after another.  Every
+width).  With per-(b, KV head) scales each wave runs two blocks on every tile it loads
+(32 columns per read of the chunk); with FP8 block scales each block is a work-group of
+its own.  A call with more blocks than a work-group takes gives each (chunk, group of
+blocks) a work-group, those of one chunk on one XCD, one after another.  Every
 case is held to the oracle's bars (fp64 definition: softmax over each token's visible
 keys, times V), checked bit for bit against tad_split + tad_combine on a workspace
 poisoned with NaN (a partial row no work-group wrote would surface), and repeated
@@ -64,8 +66,8 @@ def split_combine_poisoned(lib, g, S, blk):
     (2, 8, 4, 9, 64, BF16, [1000, 7], 4, True, 0),           # 18 columns, d 64, a row shorter than nq
     (2, 32, 4, 4, 128, BF16, [1500, 1100], 4, False, 0),     # 8 heads x 4 tokens = 32, few items
     (2, 32, 4, 4, 128, BF16, [1500, 1100], 160, True, 0),    # 4 KV heads per WG; 125 busy chunks (8 q + 5)
-    (3, 16, 1, 3, 64, E4M3, [800, 2, 1200], 6, False, 0),    # 16 heads x 3 tokens = 48, FP8
-    (2, 16, 4, 8, 128, E5M2, [1300, 640], 96, True, 64),     # 32 columns, 4 KV heads per WG, 64-key scale blocks
+    (3, 16, 1, 3, 64, E4M3, [800, 2, 1200], 6, False, 0),    # 16 heads x 3 tokens = 48, FP8 (2 WGs, one block empty)
+    (2, 16, 4, 8, 128, E5M2, [1300, 640], 96, True, 64),     # 32 columns, 4 KV heads per WG, 64-key scale blocks (one block per WG)
     (1, 4, 2, 100, 64, BF16, [1000], 4, True, 0),            # 200 columns: 13 blocks
     (2, 64, 4, 16, 128, BF16, [640, 900], 7, False, 0),      # 256 columns: 16 blocks (the most)
     (1, 2, 1, 129, 64, BF16, [600], 3, False, 0),            # 258 columns: the vector kernel
