@@ -46,9 +46,11 @@
 // identities are written afterwards by single waves.  The chunk length is one per
 // batch, lengthened on the device when the non-empty chunks would not fit the
 // resident work-groups.  A KV head with more than 16 (head, token) columns (g * nq up
-// to 256) has them cut into blocks of 16, the product width: each (item, column block)
-// is a work-group of its own, the blocks of one item on one XCD one after another
-// (column_block_of), so that the later blocks read the chunk's K and V from its L2.
+// to 256) has them cut into blocks of 16, the product width.  Each wave runs two
+// blocks on every tile it loads (CB = 2: the chunk is read once for 32 columns; FP8
+// block-scale kernels keep one); a call with more blocks than that gives each (item,
+// group of blocks) a work-group of its own, those of one item on one XCD one after
+// another (column_block_of), so that the later ones find the chunk's K and V in its L2.
 //
 // Softmax per head: lane l owns head l%16 and 4 keys of each 16-key block; the lanes
 // l, l^16, l^32, l^48 exchange their max and sum (row swaps, no LDS).  The running
@@ -145,12 +147,13 @@ __device__ __forceinline__ void wave_identity(const SplitArgs &a, const WorkItem
 }
 
 // Column blocks: a KV head's g * nq (head, token) columns are cut into blocks of 16, one
-// product width, and each (busy item, column block) pair is a work-group of its own that
-// streams the item's K and V.  Work-group w of the busy ones -> (busy item, block): the
-// ncb blocks of item i run on work-groups 8 apart, all on one XCD (the dispatcher sends
-// work-group w to XCD w mod 8) and dispatched one after another, so the later blocks
-// find the chunk's K and V in that XCD's L2; items go in groups of 8, and a last group
-// of fewer items in order.  The identity map for ncb = 1.  Wave-uniform.
+// product width, and a work-group serves CB of them; with more, each (busy item, group
+// of CB blocks) pair is a work-group of its own that streams the item's K and V.
+// Work-group w of the busy ones -> (busy item, block group): the ncb groups of item i
+// run on work-groups 8 apart, all on one XCD (the dispatcher sends work-group w to XCD
+// w mod 8) and dispatched one after another, so the later ones find the chunk's K and
+// V in that XCD's L2; items go in groups of 8, and a last group of fewer items in
+// order.  The identity map for ncb = 1.  Wave-uniform.
 __device__ __forceinline__ void column_block_of(int w, int busy, int ncb, int *item, int *cb) {
     const int grp = 8 * ncb;
     const int full = busy / 8;                   // complete groups of 8 items
@@ -777,6 +780,10 @@ void split_mfma_kernel(SplitArgs a) {
         }
     }
 }
+
+// Most (head, token) columns per KV head the matrix-core kernel takes (g * nq): 16
+// blocks of 16; wider calls run the vector kernel.
+constexpr int kMaxMfmaColumns = 256;
 
 bool split_mfma_supported(int d, int kv_type, int group, int nq) {
     return (kv_type == kKvBF16 || kv_type == kKvE4M3 || kv_type == kKvE5M2) && (int64_t)group * nq >= 2 &&

@@ -427,10 +427,6 @@ hipError_t launch_combine(const CombineArgs &a, int d, hipStream_t s);
 hipError_t launch_pieces(const PiecesArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero(int32_t *p, int64_t n, hipStream_t s);
 
-// Most (head, token) columns per KV head the matrix-core kernel takes (g * nq): 16
-// blocks of 16, each a work-group of its own; wider calls run the vector kernel.
-constexpr int kMaxMfmaColumns = 256;
-
 // Keys per work-group tile of the VALU split kernel (for tests of the host logic).
 constexpr int kSplitThreads = 256;
 constexpr int kCombineThreads = 256;
