@@ -14,6 +14,8 @@ group of fewer than 8 busy chunks, d 64 and 128, bf16, FP8 with per-head and per
 scales, ALiBi, ragged rows shorter than nq, a paged cache, and 256 columns (16 blocks,
 the most) next to 258 (the vector kernel).
 """
+import random
+
 import pytest
 import torch
 
@@ -103,3 +105,51 @@ def test_column_blocks_paged(lib, nq, ps, kv):
     for S in (5, 0):
         out = run_paged(lib, c, S)
         assert_parity(out, ref, kv, vmax_real(c), "paged column blocks S=%d" % S)
+
+
+def draw_wide_cases(n, seed=2026):
+    """Random calls with 17..256 (head, token) columns per KV head: batches across the
+    64-row blocks of the work plan (70 rows), one to 8 KV heads, ragged lengths with
+    zeros and rows shorter than nq, automatic and explicit chunk counts, ALiBi."""
+    rnd = random.Random(seed)
+    cases = []
+    while len(cases) < n:
+        d = rnd.choice([64, 128])
+        kv = rnd.choice([BF16, BF16, E4M3, E5M2])
+        Hkv = rnd.choice([1, 2, 4, 8])
+        group = rnd.choice([1, 2, 4, 8, 16])
+        nq = rnd.choice([2, 3, 4, 5, 8, 12, 16, 33])
+        if not 16 < group * nq <= 256:
+            continue
+        B = rnd.choice([1, 2, 3, 8, 70])
+        L = rnd.choice([17, 300, 1000, 2500, 6000])
+        if B * Hkv * group * nq * L * d > 60_000_000:      # keep the oracle to a second or so
+            L = max(nq + 1, 60_000_000 // (B * Hkv * group * nq * d))
+        S = rnd.choice([0, 0, 1, 3, 8, 24, 100])
+        cases.append((len(cases), B, Hkv * group, Hkv, nq, L, d, kv, B > 1 and rnd.random() < 0.8, S,
+                      rnd.random() < 0.3))
+    return cases
+
+
+@pytest.mark.parametrize("case", draw_wide_cases(24), ids=lambda c: "w%d" % c[0])
+def test_column_blocks_random(lib, case):
+    i, B, Hq, Hkv, nq, L, d, kv, ragged, S, alibi = case
+    lens = None
+    if ragged:
+        lens = torch.randint(0, L + 1, (B,), generator=torch.Generator().manual_seed(980 + i)).tolist()
+        lens[0] = L
+        lens[-1] = 0
+        if B > 2:
+            lens[1] = min(L, max(0, nq - 2))             # a row shorter than the tokens
+    note("wide random %d: B=%d Hq=%d Hkv=%d nq=%d (g*nq=%d) L=%d d=%d kv=%s lens=%s S=%d alibi=%s" %
+         (i, B, Hq, Hkv, nq, Hq // Hkv * nq, L, d, kv, "ragged" if ragged else "none", S, alibi))
+    c = tokens_case(990 + i, B, Hq, Hkv, nq, L, d, kv, lens, alibi)
+    ref = oracle_ref(c)
+    g = to_dev(c)
+    a = lib.decode(g["q"], g["k"], g["v"], g["seq_lens"], g["slopes"], S, k_scale=g.get("k_scale"),
+                   v_scale=g.get("v_scale"))
+    SS = lib.resolve_splits(g["q"], g["k"], S)
+    b = split_combine_poisoned(lib, g, SS, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "wide random case %d: decode differs from split + combine" % i
+    assert_parity(a.cpu().numpy(), ref, kv, vmax_real(c), "wide random %d" % i)
