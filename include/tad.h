@@ -53,7 +53,7 @@
  *    seq_lens): torch.chunk(n_splits) when all rows have the same length.  The last
  *    chunk of a row may be shorter; shorter rows end with empty chunks, which
  *    contribute nothing.  The matrix-core kernel (query-head groups or several
- *    tokens, 2..256 (head, token) rows per KV head, bf16 or FP8 K/V, d 64 or 128;
+ *    tokens, 2..256 (head, token) rows per KV head, bf16 or FP8 K/V, d 64, 128 or 256;
  *    more than 16 such rows are served in blocks of 16, each block of a chunk a
  *    work-group of its own that reads the chunk's K and V) lengthens c when the batch's non-empty
  *    chunks would need more work-groups than the device runs at once, to the shortest
@@ -123,7 +123,7 @@ const char *tad_last_error(void);
  * ceil(6 * CUs / (B * Hkv)) for several rows, whose lengths may differ (seq_lens), so
  * that a ragged batch's non-empty chunks still cover the device; but no chunk under
  * 128 KiB of K and V per KV head -- or 32 KiB per KV head for grouped-query calls on the
- * matrix-core kernel (bf16 or FP8 K/V, d 64 or 128, 2..256 (head, token) rows per KV head) with
+ * matrix-core kernel (bf16 or FP8 K/V, d 64, 128 or 256, 2..256 (head, token) rows per KV head) with
  * Hkv a multiple of 4, which it serves 4 KV heads to a work-group when there are at
  * least 256 (row, 4-KV-head group, chunk) items -- and at least one.  Returns the
  * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
@@ -199,7 +199,7 @@ int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t 
  * agent-scope acquire-release updates) merges, then returns its counter to zero.  Three
  * kernels do this:
  *   - the vector kernel (one query head per work-group: MHA on [B, Hkv, L, d] caches,
- *     and the cases the matrix-core kernel does not take -- fp32 K/V, d 256/512, more
+ *     and the cases the matrix-core kernel does not take -- fp32 K/V, d 512, more
  *     than 256 (head, token) rows per KV head), when B * Hq * nq * n_splits is below the
  *     device's compute-unit count, n_splits <= 8 and no chunk is cut into pieces: the
  *     last work-group of a row merges the row;

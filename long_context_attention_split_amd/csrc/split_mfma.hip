@@ -14,7 +14,8 @@
 // Decoding").
 //
 // Data path: each wave streams tiles of K and V (16 keys for bf16, 32 keys for FP8:
-// 8 KiB at d = 128 either way) straight from HBM into its own LDS buffers with
+// 8 KiB at d = 128 either way, 16 KiB at d = 256) straight from HBM into its own LDS
+// buffers with
 // buffer_load_dwordx4 ... lds.  Every load instruction covers whole consecutive rows
 // -- the pattern that streams at full HBM rate -- and the lanes of a row fetch its
 // 16-byte chunks in an XOR-swizzled order, so that the matrix-core operand reads
@@ -217,7 +218,7 @@ template <int D, bool PAGED, int HG, int NWH, int KVT, bool WT = false, bool BLK
 __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkItem wi, const int cb, const int c,
                                                 const int Lb, uint4 *smem, float (*lds_ml)[3][HG * NWH][16],
                                                 float4 *ox, int *lds_cnt) {
-    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(D == 64 || D == 128 || D == 256, "head dim");
     static_assert(CB == 1 || CB == 2, "column blocks per wave");
     constexpr bool F8 = KVT != kKvBF16;
     static_assert(!BLK || F8, "block scales are for FP8 K/V");
@@ -287,11 +288,13 @@ __device__ __forceinline__ void split_mfma_item(const SplitArgs &a, const WorkIt
 
     // LDS slot (row r, position p) holds chunk p ^ swz(r) of row r.  Within a 16-row
     // score block the 16 rows of an operand read land in distinct 16-byte bank groups
-    // (CH = 16: swz(r) = r; CH = 8: the row parity plus r/2; CH = 4: the row's place in
-    // the 256-byte bank space plus r/4).  Rows 16..31 of an FP8 tile are rotated by
-    // CH/2 more, so that the transposing V read, which takes rows from both halves,
+    // (CH = 16 or 32: swz(r) = r, the low 4 bits of the position, since a row is a
+    // multiple of the 256-byte bank space; CH = 8: the row parity plus r/2; CH = 4: the
+    // row's place in the bank space plus r/4).  Rows 16..31 of an FP8 tile are rotated
+    // by CH/2 more, so that the transposing V read, which takes rows from both halves,
     // spreads too.
-    auto swz = [](int r) { return (r / (16 / CH) + (r / 16) * (CH / 2)) % CH; };
+    constexpr int RD = CH >= 16 ? 1 : 16 / CH;
+    auto swz = [](int r) { return (r / RD + (r / 16) * (CH / 2)) % CH; };
     uint4 *const bufA = smem + wave * 2 * TILE;
     const int ld_r = lane / CH, ld_p = lane % CH;
     // A operand of the value product for value columns [16 nb, 16 nb + 16): lane l needs
@@ -787,7 +790,7 @@ constexpr int kMaxMfmaColumns = 256;
 
 bool split_mfma_supported(int d, int kv_type, int group, int nq) {
     return (kv_type == kKvBF16 || kv_type == kKvE4M3 || kv_type == kKvE5M2) && (int64_t)group * nq >= 2 &&
-           (int64_t)group * nq <= kMaxMfmaColumns && (d == 64 || d == 128);
+           (int64_t)group * nq <= kMaxMfmaColumns && (d == 64 || d == 128 || d == 256);
 }
 
 // Fewest (row, 4-KV-head group, chunk) items for which a work-group serves 4 KV heads;
@@ -822,7 +825,8 @@ bool split_mfma_fusable(const SplitArgs &a, int d) {
 // Launched variants: loads overlapped with compute.  The tile held in registers
 // costs d/4 + 8 VGPRs per lane; at d = 128 that needs 3 waves per SIMD (152 VGPRs;
 // 4 waves would spill), which measured faster than 4 waves without the overlap
-// (grouped-query decode, 8 KV heads, 131072 keys: 87.0 vs 93.8 us).  d = 64 keeps 4.
+// (grouped-query decode, 8 KV heads, 131072 keys: 87.0 vs 93.8 us).  d = 64 keeps 4,
+// d = 256 (q operands and O twice d = 128's) runs 2.
 // With a KV head count divisible by 4, a work-group runs 4 KV heads x WAVES waves
 // (12 waves at d = 128, 16 at d = 64): one work-group per CU at the usual chunk
 // count, all resident at once, and for caches with the heads of a key adjacent the 4
@@ -856,7 +860,7 @@ static void launch_k(SplitArgs a, int64_t grid, hipStream_t st) {
 // work-groups for 4 KV heads), d = 64 3.
 template <int D, int KVT, bool BLK = false, int CB = 1>
 static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
-    constexpr int WAVES = CB == 1 ? (D == 128 ? 3 : 4) : (D == 128 ? 2 : 3);
+    constexpr int WAVES = CB == 1 ? (D == 256 ? 1 : D == 128 ? 3 : 4) : (D == 128 ? 2 : 3);
     const int64_t ncb = ((a.group * a.nq + 15) / 16 + CB - 1) / CB;   // work-group column blocks
     const int64_t items = (int64_t)a.B * a.Hkv * a.S * ncb;
     if constexpr (CB == 1) {
@@ -878,11 +882,16 @@ static void launch_mfma_t(const SplitArgs &a, hipStream_t st) {
 }
 
 // Per-(b, KV head) scales and more than 16 columns per KV head: two column blocks per
-// wave.
+// wave (d 64 and 128; at d = 256 one block's q and O already take half the registers).
 template <int D, int KVT>
 static void launch_mfma_cols(const SplitArgs &a, hipStream_t st) {
-    if (a.group * a.nq > 16) launch_mfma_t<D, KVT, false, 2>(a, st);
-    else launch_mfma_t<D, KVT>(a, st);
+    if constexpr (D != 256) {
+        if (a.group * a.nq > 16) {
+            launch_mfma_t<D, KVT, false, 2>(a, st);
+            return;
+        }
+    }
+    launch_mfma_t<D, KVT>(a, st);
 }
 
 template <int D>
@@ -907,6 +916,7 @@ hipError_t launch_split_mfma(const SplitArgs &a, int d, hipStream_t st) {
     switch (d) {
         case 64: launch_mfma_d<64>(a, st); break;
         case 128: launch_mfma_d<128>(a, st); break;
+        case 256: launch_mfma_d<256>(a, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -63,7 +63,7 @@ CASES = [
     (3, 1, 1, 1, 1, 20000, 256, E4, 4, None, False, 128, 256, "contig", "vector, pieces"),
     (4, 1, 2, 2, 1, 4096, 512, E4, 8, None, True, 16, 16, "contig", "vector d 512, pieces"),
     (5, 1, 4, 4, 1, 600, 128, E4, 4, None, False, 16, 32, "contig", "vector, one launch"),
-    (6, 2, 4, 2, 1, 2500, 256, E5, 6, [2500, 999], False, 64, 16, "contig", "vector, query-head groups"),
+    (6, 2, 4, 2, 1, 2500, 256, E5, 6, [2500, 999], False, 64, 16, "contig", "matrix cores, d 256"),
     (7, 1, 2, 2, 3, 1500, 512, E4, 5, None, False, 16, 16, "contig", "vector, 3 tokens"),
     (8, 2, 8, 8, 1, 4000, 128, E4, 8, [4000, 2100], True, 32, 128, "tokmajor", "head-packed"),
     (9, 1, 8, 8, 1, 1200, 64, E5, 4, None, False, 16, 16, "tokmajor", "head-packed, one launch"),
@@ -76,6 +76,7 @@ CASES = [
     (16, 2, 2, 2, 1, 2000, 128, E4, 5, [2000, 1300], False, 64, 64, "paged16hm", "vector, paged"),
     (17, 2, 8, 2, 1, 2000, 128, E4, 6, [2000, 700], False, 64, 16, "paged48", "matrix cores, 48-row pages"),
     (18, 1, 2, 2, 1, 20000, 128, E5, 2, None, False, 64, 128, "paged16hm", "vector, paged, pieces"),
+    (19, 2, 4, 2, 1, 2500, 512, E5, 6, [2500, 999], False, 64, 16, "contig", "vector, query-head groups"),
 ]
 
 

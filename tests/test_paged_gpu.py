@@ -52,7 +52,7 @@ def oracle_of(c):
     (4, 32, 32, 1500, 128, 16, torch.bfloat16, 8),         # larger grid: split + combine
     (2, 16, 4, 1300, 128, 32, torch.bfloat16, 7),          # GQA 4: matrix-core path (one KV head per work-group)
     (2, 8, 4, 900, 64, 64, torch.bfloat16, 3),             # GQA 2, d 64, 64-row pages
-    (2, 4, 2, 700, 256, 16, torch.bfloat16, 4),            # d 256 (vector path, GQA)
+    (2, 4, 2, 700, 256, 16, torch.bfloat16, 4),            # d 256, GQA 2: matrix cores (one wave per SIMD)
     (2, 4, 4, 1000, 128, 16, torch.float8_e4m3fn, 5),      # FP8 with scales, MHA
     (2, 8, 2, 1000, 128, 48, torch.float8_e5m2, 6),        # FP8 E5M2, GQA 4, 48-row pages
     (2, 4, 4, 600, 64, 16, torch.float8_e4m3fn, 3),        # FP8, d 64
