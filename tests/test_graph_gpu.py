@@ -20,7 +20,7 @@ def dev(x):
 
 @pytest.mark.parametrize("case", ["fused-mha", "gqa", "split-combine-mha", "paged-interleaved", "tokens",
                                   "gqa-many-chunks", "pieces", "pieces-combine", "fp8-block-gqa",
-                                  "fp8-block-split-combine"])
+                                  "fp8-block-split-combine", "wide-columns", "d256-fused", "d256-many-chunks"])
 def test_decode_ws_replays_in_a_graph(lib, case):
     print("[case] graph %s" % case, flush=True)
     paged = case == "paged-interleaved"
@@ -42,6 +42,13 @@ def test_decode_ws_replays_in_a_graph(lib, case):
     elif case == "fp8-block-split-combine":   # FP8 with 64-key scale blocks, vector split then combine
         c, S = W.random_case(911, 2, 32, 32, 4000, 128, kv_dtype=torch.float8_e5m2, seq_lens=[4000, 3333],
                              scale_block=64), 16
+    elif case == "wide-columns":      # 8 heads x 4 tokens = 32 columns per KV head: two blocks per wave
+        c, S = W.random_case(912, 2, 8, 1, 2000, 128, seq_lens=[2000, 900]), 6
+        c["q"] = torch.randn((2, 8, 4, 128), generator=torch.Generator().manual_seed(915))
+    elif case == "d256-fused":        # d 256 on the matrix cores, merge in its last work-group per KV head
+        c, S = W.random_case(913, 2, 8, 4, 1500, 256, seq_lens=[1500, 800]), 4
+    elif case == "d256-many-chunks":  # d 256, 4 KV heads per work-group, more chunks than resident work-groups
+        c, S = W.random_case(914, 8, 16, 8, 2000, 256, seq_lens=[2000, 17, 0, 1204, 1999, 300, 1, 1024]), 96
     elif case == "tokens":
         c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
         c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
@@ -84,7 +91,7 @@ def test_decode_ws_replays_in_a_graph(lib, case):
     partials = ws[:2 * al(4 * n_part) + 4 * n_part * q.shape[-1]].view(torch.float32)
     for i in range(3):
         out.fill_(float("nan"))                       # eager work between replays
-        if case == "gqa-many-chunks":
+        if case in ("gqa-many-chunks", "d256-many-chunks"):
             partials.fill_(float("nan"))              # every partial must be written again
         g.replay()
         torch.cuda.synchronize()

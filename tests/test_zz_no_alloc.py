@@ -4,9 +4,10 @@ Its partials and counters live in the library's own device array, shared by ever
 on a device.  Each call is checked against tad_decode_ws with the same n_splits (bit
 for bit: the same kernels, the same chunking) and against the fp64 oracle, on calls in
 a row whose sizes shrink, so that what an earlier call left in the array cannot leak
-into a later one: a large grouped-query decode (matrix cores, split + combine), then a
-one-head decode whose chunks are cut into pieces (merged in the pieces kernel's last
-work-group: row counters), then a small multi-head decode merged in the split kernel.
+into a later one: a large grouped-query decode (matrix cores, split + combine), a d = 256
+grouped-query decode (matrix cores at one wave per SIMD), then a one-head decode whose
+chunks are cut into pieces (merged in the pieces kernel's last work-group: row
+counters), then a small multi-head decode merged in the split kernel.
 """
 import pytest
 import torch
@@ -35,6 +36,8 @@ def run_pair(lib, c, S):
 CASES = [
     ("grouped-query, 8 rows, ragged, automatic chunks", dict(seed=950, B=8, Hq=32, Hkv=8, L=6000, d=128,
                                                             seq_lens=[6000, 17, 0, 3001, 5999, 640, 1, 2048]), 0),
+    ("d 256 grouped-query, 4 rows, ragged, automatic chunks", dict(seed=953, B=4, Hq=16, Hkv=4, L=3000, d=256,
+                                                                   seq_lens=[3000, 1, 2999, 1500]), 0),
     ("one fp32 d=512 head, 8 chunks cut into pieces", dict(seed=951, B=1, Hq=1, Hkv=1, L=4096, d=512,
                                                           kv_dtype=torch.float32), 8),
     ("4 heads, 3 chunks, merged in the split kernel", dict(seed=952, B=1, Hq=4, Hkv=4, L=1000, d=64,
