@@ -124,8 +124,9 @@ const char *tad_last_error(void);
  * that a ragged batch's non-empty chunks still cover the device; but no chunk under
  * 128 KiB of K and V per KV head -- or 32 KiB per KV head for grouped-query calls on the
  * matrix-core kernel (bf16 or FP8 K/V, d 64, 128 or 256, 2..256 (head, token) rows per KV head) with
- * Hkv a multiple of 4, which it serves 4 KV heads to a work-group when there are at
- * least 256 (row, 4-KV-head group, chunk) items -- and at least one.  Returns the
+ * Hkv a multiple of 4 and at most 16 such rows (any number at d = 256), which it serves
+ * 4 KV heads to a work-group when there are at least 256 (row, 4-KV-head group, chunk)
+ * items -- and at least one.  Returns the
  * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
  * d, TAD_EDTYPE for kv_dtype).  (Hq, nq, d and kv_dtype are arguments because the count
  * mirrors the kernel choice and the byte-sized minimum chunk, which depend on them.)

@@ -807,9 +807,14 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
     return a.Hkv % 4 == 0 && split_mfma_supported(d, a.kv_type, a.group, a.nq);
 }
 
-// Whether a call runs the variant with 4 KV heads per work-group.
+// Whether a call runs the variant with 4 KV heads per work-group.  Not with two column
+// blocks per wave (more than 16 columns at d 64/128): with 2 waves per SIMD the 4-head
+// form has only 2 waves per KV head, and one KV head per 4-wave work-group measured
+// faster (8 query tokens per row, cold steps: ragged FP8 grouped-query batch 60.5-61.8
+// -> 54.5-55.3 us, bf16 134.3-134.4 -> 132.1-132.5 us).
 static bool runs_grouped_heads(const SplitArgs &a, int d) {
-    return split_mfma_grouped_heads(a, d) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems;
+    return split_mfma_grouped_heads(a, d) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems &&
+           (a.group * a.nq <= 16 || d == 256);
 }
 
 // Whether the one-launch form (TAIL) serves a call: one KV head per work-group, at most

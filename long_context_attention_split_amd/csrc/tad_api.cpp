@@ -303,8 +303,10 @@ int32_t auto_splits_for(int64_t B, int64_t Hq, int64_t Hkv, int64_t nq, int64_t 
     const int64_t per_cu = B > 1 ? 6 : 4;
     int64_t S = (per_cu * (int64_t)cus + units - 1) / units;
     const int32_t group = (int32_t)(Hq / (Hkv > 0 ? Hkv : 1));
-    const int64_t heads_per_wg =
-        (Hkv % 4 == 0 && tad::split_mfma_supported((int)d, kv_type_of(kv_dtype), group, (int)nq)) ? 4 : 1;
+    // mirrors the matrix-core kernel's choice: 4 KV heads per work-group only with one
+    // column block per wave (at most 16 (head, token) columns, or d = 256)
+    const int64_t heads_per_wg = (Hkv % 4 == 0 && tad::split_mfma_supported((int)d, kv_type_of(kv_dtype), group, (int)nq) &&
+                                  ((int64_t)group * nq <= 16 || d == 256)) ? 4 : 1;
     const int64_t by_len = Lmax * 2 * d * elem_size(kv_dtype) * heads_per_wg / kMinChunkBytes;
     if (S > by_len) S = by_len;
     if (S > tad::kMaxSplits) S = tad::kMaxSplits;

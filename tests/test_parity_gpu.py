@@ -585,7 +585,7 @@ def test_auto_splits_rule(lib, B, Hq, Hkv, nq, Lmax, d, kv):
     elem = torch.empty((), dtype=kv).element_size()
     gq = Hq // Hkv * nq
     matrix = d in (64, 128, 256) and kv != torch.float32 and 2 <= gq <= 256
-    heads_per_wg = 4 if matrix and Hkv % 4 == 0 else 1
+    heads_per_wg = 4 if matrix and Hkv % 4 == 0 and (gq <= 16 or d == 256) else 1
     want = max(1, min(-(-per_cu * cus // (B * Hkv)), Lmax * 2 * d * elem * heads_per_wg // (128 << 10), 4096))
     assert lib.tad_auto_splits(B, Hq, Hkv, nq, Lmax, d, kv, 0) == want
 
