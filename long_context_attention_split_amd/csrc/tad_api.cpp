@@ -247,8 +247,15 @@ int check_out(const tad_tensor *out, const Problem &P, int64_t *sob, int64_t *so
     return TAD_OK;
 }
 
-// 32-bit buffer offsets: one chunk plus a tile of overrun must span < 4 GiB.
+// 32-bit buffer offsets: one chunk plus a tile of overrun must span < 4 GiB.  And 32-bit
+// work counts: no split or pieces kernel launches more than B * Hq * nq * n_splits
+// work-groups (the matrix-core kernel B * Hkv * n_splits * column blocks, fewer), which
+// the kernels index with 32-bit integers.
 int check_offsets(const Problem &P, int64_t S) {
+    const int64_t rows = P.B * P.Hq * P.nq;
+    if (rows > 0 && S > int64_t(0x7fffffff) / rows)
+        return fail(TAD_EUNSUPPORTED, "B * Hq * nq * n_splits = %lld * %lld exceeds 2^31 - 1", (long long)rows,
+                    (long long)S);
     const int64_t al = chunk_align(P.block_table ? P.page_size : 1, P.k_blk, P.v_blk);
     if (al > (int64_t(1) << 30))
         return fail(TAD_EUNSUPPORTED, "pages and scale blocks would need chunks of %lld keys", (long long)al);

@@ -240,6 +240,16 @@ def test_chunk_span_limit(lib):
     assert call_split(so, a, n_splits=4, ws_bytes=0) == tad.TAD_EWORKSPACE   # passes the span check
 
 
+def test_work_count_limit(lib):
+    """Calls whose B * Hq * nq * n_splits exceeds 2^31 - 1 are refused before any launch
+    (the kernels count work-groups in 32 bits); one under the limit passes that check."""
+    so = lib.load()
+    a = good(B=65536, Hq=64, Hkv=64, L=100)              # 2^22 rows
+    assert call_split(so, a, n_splits=512) == tad.TAD_EUNSUPPORTED          # 2^31
+    assert "exceeds" in lib.tad_last_error()
+    assert call_split(so, a, n_splits=511, ws_bytes=0) == tad.TAD_EWORKSPACE  # passes the count check
+
+
 def paged_good(B=2, Hq=8, Hkv=2, NP=20, PS=16, d=128, max_pages=7):
     return dict(q=desc([B, Hq, d], tad.TAD_F32), k=desc([NP, PS, Hkv, d]), v=desc([NP, PS, Hkv, d]),
                 out=desc([B, Hq, d], tad.TAD_F32), pages=tad.TadPagedKv(FAKE, max_pages))
