@@ -811,10 +811,16 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
 // blocks per wave (more than 16 columns at d 64/128): with 2 waves per SIMD the 4-head
 // form has only 2 waves per KV head, and one KV head per 4-wave work-group measured
 // faster (8 query tokens per row, cold steps: ragged FP8 grouped-query batch 60.5-61.8
-// -> 54.5-55.3 us, bf16 134.3-134.4 -> 132.1-132.5 us).
+// -> 54.5-55.3 us, bf16 134.3-134.4 -> 132.1-132.5 us).  Nor for FP8 K/V stored head
+// by head ([B, Hkv, L, d]): its 4 heads' rows lie far apart, and one KV head per
+// work-group, three work-groups per CU, measured faster (ragged FP8 batch, cold steps,
+// three runs each: one token 41.8-41.9 -> 40.6-41.0 us, 4 tokens 47.2-47.3 -> 45.8-46.8
+// us, 64-key block scales 44.7-45.2 -> 42.4-42.6 us); bf16 and caches with the heads of
+// a key adjacent (strides or pages) keep the 4-head form, which reads each key's
+// adjacent rows together.
 static bool runs_grouped_heads(const SplitArgs &a, int d) {
     return split_mfma_grouped_heads(a, d) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems &&
-           (a.group * a.nq <= 16 || d == 256);
+           (a.group * a.nq <= 16 || d == 256) && (a.kv_type == kKvBF16 || a.block_table || a.skh < a.skj);
 }
 
 // Whether the one-launch form (TAIL) serves a call: one KV head per work-group, at most
