@@ -36,26 +36,48 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
 // (d = 128): 4.8 us against 6.8 us for one row per work-group with column groups
 // (graph replay); with few rows the column groups' many work-groups are faster (32
 // rows of 32 chunks: 3.5 us against 3.9 us with one row per work-group).
-template <int D, int R>
+// SCAN: the rows' m are read first: chunks past the last one with a finite m in any of
+// the R rows are empty (the split kernels write m = -inf there and leave o unwritten),
+// and merge_rows takes them as the merge identity without reading their o -- on ragged
+// batches about a third to a half of the o a row would otherwise read.  Same bits.  It
+// costs a dependent round trip, which pays only on large partial sets: 2048 rows x 24
+// chunks (8 query tokens on the ragged grouped-query batches, 25 MB of o), cold steps
+// 133.1-133.3 -> 128.8-129.6 us (bf16) and 55.3-55.7 -> 52.2-52.7 us (FP8); 1024 rows
+// (13 MB) 46.1-46.4 -> 46.7-46.9 us and 127.1-127.6 -> 127.7-127.9 us.
+template <int D, int R, bool SCAN>
 __global__ __launch_bounds__(kCombineThreads) void combine_rows_kernel(CombineArgs a) {
+    static_assert(R * 64 <= kCombineThreads, "one m per thread");
     __shared__ __align__(16) float lds[merge_rows_lds_floats(R, 64, D)];
+    __shared__ int busy_all;
     const int64_t rows = (int64_t)a.B * a.Hq * a.nq;
     const int64_t r0 = (int64_t)blockIdx.x * R;
     const int nr = (int)(rows - r0 < R ? rows - r0 : R);
     const int S = a.S;
+    int busy = S;
+    if constexpr (SCAN) {
+        const int tid = threadIdx.x;
+        if (tid == 0) busy_all = 0;
+        __syncthreads();
+        if (tid < nr * S && a.ws_m[r0 * S + tid] != kNegInf) atomicMax(&busy_all, tid % S + 1);
+        __syncthreads();
+        busy = busy_all;
+    }
     auto out_of = [&](int j) {
         const int64_t row = r0 + j;                // (b * Hq + h) * nq + t
         const int64_t t = row % a.nq, bh = row / a.nq;
         return a.out + (bh / a.Hq) * a.sob + (bh % a.Hq) * a.soh + t * a.sot;
     };
-    merge_rows<D, kCombineThreads>(a.ws_m + r0 * S, a.ws_l + r0 * S, a.ws_o + r0 * S * D, S, S, nr, out_of, lds);
+    merge_rows<D, kCombineThreads>(a.ws_m + r0 * S, a.ws_l + r0 * S, a.ws_o + r0 * S * D, S, busy, nr, out_of, lds);
 }
 
 template <int D>
 static void launch_combine_d(const CombineArgs &a, int64_t rows, hipStream_t st) {
     if (a.S <= 64 && rows >= 1024) {
-        hipLaunchKernelGGL((combine_rows_kernel<D, 4>), dim3((unsigned)((rows + 3) / 4)), dim3(kCombineThreads), 0, st,
-                           a);
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        if (rows * a.S * D >= (int64_t(4) << 20))          // 16 MB of o partials or more
+            hipLaunchKernelGGL((combine_rows_kernel<D, 4, true>), grid, dim3(kCombineThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((combine_rows_kernel<D, 4, false>), grid, dim3(kCombineThreads), 0, st, a);
         return;
     }
     const dim3 grid((unsigned)rows, (unsigned)merge_column_groups(a.S, D));

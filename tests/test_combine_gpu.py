@@ -22,9 +22,11 @@ def layout(rows, S, d):
     return 0, al(4 * n), 2 * al(4 * n), n
 
 
-def fill_partials(lib, rows_shape, S, d, seed):
+def fill_partials(lib, rows_shape, S, d, seed, tail=0):
     """A workspace for B x Hq x nq rows holding seeded partials: maxima spread over 40
-    (base 2), some empty chunks (m = -inf, l = 0, o left as garbage), one row empty."""
+    (base 2), some empty chunks (m = -inf, l = 0, o left as garbage), one row empty;
+    with tail > 0 the rows of even batch rows end with `tail` empty chunks (as a ragged
+    batch's shorter rows do)."""
     B, Hq, nq = rows_shape
     rows = B * Hq * nq
     q = torch.zeros((B, Hq, nq, d), device=DEV)
@@ -36,6 +38,10 @@ def fill_partials(lib, rows_shape, S, d, seed):
     o = torch.randn((rows, S, d), generator=g, dtype=torch.float64) * 20
     empty = torch.rand((rows, S), generator=g) < 0.25
     empty[3] = True                                   # a row with no keys at all
+    if tail:
+        per_b = Hq * nq
+        for b in range(0, B, 2):
+            empty[b * per_b:(b + 1) * per_b, S - tail:] = True
     m[empty] = -np.inf
     l[empty] = 0.0
     o[empty] = float("nan")                           # never read with weight 0
@@ -57,16 +63,20 @@ def merge_f64(m, l, o):
     return torch.where(L[:, None] > 0, O / L[:, None], torch.zeros_like(O))
 
 
-@pytest.mark.parametrize("d,S,nq", [(128, 24, 4), (64, 64, 2), (256, 7, 1), (128, 1, 8)])
-def test_row_batched_combine_matches_column_split(lib, d, S, nq):
+@pytest.mark.parametrize("d,S,nq,tail", [(128, 24, 4, 0), (64, 64, 2, 0), (256, 7, 1, 0), (128, 1, 8, 0),
+                                         (128, 48, 8, 10), (64, 64, 4, 63)])
+def test_row_batched_combine_matches_column_split(lib, d, S, nq, tail):
+    """The last two cases hold 16 MB of o partials or more, where the combine first reads
+    the rows' m and skips the o of chunks past the last non-empty one; their trailing
+    empty chunks hold NaN o, which must not be read with a nonzero weight."""
     B, Hq = 1024 // (31 * nq) + 1, 31                  # more than 1024 rows (not a multiple of 4 for nq < 4)
     rows = B * Hq * nq
-    note("combine rows=%d S=%d d=%d" % (rows, S, d))
-    ws, m, l, o = fill_partials(lib, (B, Hq, nq), S, d, 40 + S + d)
+    note("combine rows=%d S=%d d=%d tail=%d" % (rows, S, d, tail))
+    ws, m, l, o = fill_partials(lib, (B, Hq, nq), S, d, 40 + S + d, tail)
     big = torch.empty((B, Hq, nq, d), dtype=torch.float32, device=DEV)
     lib.tad_combine(ws, B, Hq, nq, S, d, big)
     # the first batch row alone (Hq * nq < 1024 rows): the column-split form
-    ws1, _, _, _ = fill_partials(lib, (1, Hq, nq), S, d, 40 + S + d)
+    ws1, _, _, _ = fill_partials(lib, (1, Hq, nq), S, d, 40 + S + d, tail)
     om, ol, oo, n = layout(rows, S, d)
     om1, ol1, oo1, n1 = layout(Hq * nq, S, d)
     ws1[om1:om1 + 4 * n1].copy_(ws[om:om + 4 * n1])
