@@ -153,3 +153,17 @@ def test_column_blocks_random(lib, case):
     torch.cuda.synchronize()
     assert torch.equal(a, b), "wide random case %d: decode differs from split + combine" % i
     assert_parity(a.cpu().numpy(), ref, kv, vmax_real(c), "wide random %d" % i)
+
+
+@pytest.mark.parametrize("kv,d,nq", [(BF16, 128, 8), (E4M3, 64, 5), (BF16, 256, 3), (E5M2, 128, 2)])
+def test_token_major_caches(lib, kv, d, nq):
+    """K/V stored [B, L, Hkv, d] (the heads of a key next to each other), seen as
+    [B, Hkv, L, d] through strides: 32 and 20 columns per KV head (two blocks per wave),
+    d 256, and FP8 with 8 columns (4 KV heads per work-group from 256 items on, which
+    such caches keep); small and large chunk counts."""
+    from test_layouts_gpu import run_interleaved
+    note("token-major kv=%s d=%d nq=%d" % (kv, d, nq))
+    c = tokens_case(1400 + d + nq, 2, 16, 4, nq, 1500, d, kv, [1500, 777], True)
+    ref = oracle_ref(c)
+    for S in (5, 160):
+        assert_parity(run_interleaved(lib, c, S), ref, kv, vmax_real(c), "token-major S=%d" % S)
