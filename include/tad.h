@@ -126,9 +126,10 @@ const char *tad_last_error(void);
  * matrix-core kernel (bf16 or FP8 K/V, d 64, 128 or 256, 2..256 (head, token) rows per KV head) with
  * Hkv a multiple of 4 and at most 16 such rows (any number at d = 256), which it serves
  * 4 KV heads to a work-group when there are at least 256 (row, 4-KV-head group, chunk)
- * items and K/V are bf16 or store the KV heads of a key next to each other -- and at
- * least one.  (The count sees no strides: FP8 K/V stored head by head get the 32 KiB
- * minimum though their kernel serves one KV head per work-group.)  Returns the
+ * items and K/V store the KV heads of a key next to each other or are bf16 with
+ * query-head groups -- and at least one.  (The count sees no strides: FP8 K/V, and bf16
+ * with one query head per KV head, stored head by head get the 32 KiB minimum though
+ * their kernel serves one KV head per work-group.)  Returns the
  * count (>= 1) or a negative TAD_E* code (TAD_EINVAL for sizes, TAD_EUNSUPPORTED for
  * d, TAD_EDTYPE for kv_dtype).  (Hq, nq, d and kv_dtype are arguments because the count
  * mirrors the kernel choice and the byte-sized minimum chunk, which depend on them.)

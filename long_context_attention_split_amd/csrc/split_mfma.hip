@@ -815,12 +815,17 @@ bool split_mfma_grouped_heads(const SplitArgs &a, int d) {
 // by head ([B, Hkv, L, d]): its 4 heads' rows lie far apart, and one KV head per
 // work-group, three work-groups per CU, measured faster (ragged FP8 batch, cold steps,
 // three runs each: one token 41.8-41.9 -> 40.6-41.0 us, 4 tokens 47.2-47.3 -> 45.8-46.8
-// us, 64-key block scales 44.7-45.2 -> 42.4-42.6 us); bf16 and caches with the heads of
-// a key adjacent (strides or pages) keep the 4-head form, which reads each key's
-// adjacent rows together.
+// us, 64-key block scales 44.7-45.2 -> 42.4-42.6 us).  Nor, stored head by head, for
+// bf16 K/V with one query head per KV head (several tokens): 2 and 4 tokens on the
+// 32-head 131072-key MHA workload 331.7-333.6 -> 317.5-320.0 us per step, 4 tokens on
+// the ALiBi workload 323.0-323.4 -> 318.8-320.2 us; bf16 query-head groups keep it
+// (ragged grouped-query batch 117.0-117.4 against 118.4-119.8 us).  Caches with the
+// heads of a key adjacent (strides or pages) keep the 4-head form, which reads each
+// key's adjacent rows together.
 static bool runs_grouped_heads(const SplitArgs &a, int d) {
     return split_mfma_grouped_heads(a, d) && (int64_t)a.B * (a.Hkv / 4) * a.S >= kGroupedHeadsMinItems &&
-           (a.group * a.nq <= 16 || d == 256) && (a.kv_type == kKvBF16 || a.block_table || a.skh < a.skj);
+           (a.group * a.nq <= 16 || d == 256) &&
+           ((a.kv_type == kKvBF16 && a.group > 1) || a.block_table || a.skh < a.skj);
 }
 
 // Whether the one-launch form (TAIL) serves a call: one KV head per work-group, at most
