@@ -20,7 +20,8 @@ def dev(x):
 
 @pytest.mark.parametrize("case", ["fused-mha", "gqa", "split-combine-mha", "paged-interleaved", "tokens",
                                   "gqa-many-chunks", "pieces", "pieces-combine", "fp8-block-gqa",
-                                  "fp8-block-split-combine", "wide-columns", "d256-fused", "d256-many-chunks"])
+                                  "fp8-block-split-combine", "wide-columns", "d256-fused", "d256-many-chunks",
+                                  "combine-scan"])
 def test_decode_ws_replays_in_a_graph(lib, case):
     print("[case] graph %s" % case, flush=True)
     paged = case == "paged-interleaved"
@@ -49,6 +50,9 @@ def test_decode_ws_replays_in_a_graph(lib, case):
         c, S = W.random_case(913, 2, 8, 4, 1500, 256, seq_lens=[1500, 800]), 4
     elif case == "d256-many-chunks":  # d 256, 4 KV heads per work-group, more chunks than resident work-groups
         c, S = W.random_case(914, 8, 16, 8, 2000, 256, seq_lens=[2000, 17, 0, 1204, 1999, 300, 1, 1024]), 96
+    elif case == "combine-scan":      # 2048 (head, token) rows x 24 chunks: the combine reads m first
+        c, S = W.random_case(916, 8, 32, 8, 4000, 128, seq_lens=[4000, 17, 0, 1204, 3999, 300, 1, 2048]), 24
+        c["q"] = torch.randn((8, 32, 8, 128), generator=torch.Generator().manual_seed(917))
     elif case == "tokens":
         c, S = W.random_case(902, 2, 8, 2, 1500, 128, seq_lens=[1500, 900]), 6
         c["q"] = torch.randn((2, 8, 3, 128), generator=torch.Generator().manual_seed(903))
@@ -91,7 +95,7 @@ def test_decode_ws_replays_in_a_graph(lib, case):
     partials = ws[:2 * al(4 * n_part) + 4 * n_part * q.shape[-1]].view(torch.float32)
     for i in range(3):
         out.fill_(float("nan"))                       # eager work between replays
-        if case in ("gqa-many-chunks", "d256-many-chunks"):
+        if case in ("gqa-many-chunks", "d256-many-chunks", "combine-scan"):
             partials.fill_(float("nan"))              # every partial must be written again
         g.replay()
         torch.cuda.synchronize()
