@@ -191,7 +191,10 @@ int tad_split(const tad_tensor *q, const tad_tensor *k, const tad_tensor *v,
  * Merge step: for each (b, h, t) row, M = max_s m, w_s = 2^(m_s - M), L = sum_s w_s
  * l_s, out = sum_s w_s o_s / L, summed in a fixed order (bit-reproducible).  Rows
  * whose chunks are all empty get out = 0.  `out` is fp32 [B, Hq, d] (nq = 1) or
- * [B, Hq, nq, d].
+ * [B, Hq, nq, d].  An empty chunk must hold m = -inf (as tad_split writes it): its o is
+ * never read with a nonzero weight, and with 16 MB of o or more (many (head, token)
+ * rows, at most 64 chunks) the merge reads the rows' m first and skips the o of
+ * chunks past each group of 4 rows' last non-empty one.
  */
 int tad_combine(const void *ws, size_t ws_bytes, int32_t B, int32_t Hq, int32_t nq, int32_t n_splits,
                 int32_t d, tad_tensor *out, hipStream_t stream);
